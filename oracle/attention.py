@@ -1,0 +1,314 @@
+"""NumPy oracle: gated GQA causal attention written out as its definition.
+
+TEST INFRASTRUCTURE (see the package docstring): only tests, the smoke check
+and the bench's CPU-baseline leg may use this module.
+
+Notation follows the pages. For batch b, query token i, query head h, with
+group = H/G query heads per key/value head and g = floor(h / group):
+
+    q_hat = RoPE(RMSNorm(q[b,i,h], w_q), pos[b,i])
+    k_hat_j = RoPE(RMSNorm(k[b,j,g], w_k), pos[b,j])          for j <= i
+    s_j = (q_hat . k_hat_j) * scale,   scale = 1/sqrt(d)
+    a_j = exp(s_j - max s) / sum_j exp(s_j - max s)           (causal: j <= i)
+    y = sum_j a_j v[b,j,g]
+    out[b,i,h*d:(h+1)*d] = y * sigmoid(z)                      (z: gate logits)
+
+Sources:
+* "Transformer by Hand · 6. Gated attention": section "The formula"
+  (softmax(QK^T/sqrt(d) + M) V with the causal mask M); section "Four things
+  Qwen3.5 adds to the textbook" (GQA sharing, QK-Norm before RoPE, RoPE on the
+  first quarter of the head, the output gate); the forward code and its shape
+  table in "The code: qwen/attention.py" (norm then RoPE, repeat_interleave
+  for GQA, mask above the diagonal, gate multiplied after the head concat).
+* "Gated Attention：算完注意力，再决定用多少", section "门放在哪里？"
+  (Y = Concat_h(G_h ⊙ O_h) W_O, headwise vs elementwise gate) and the
+  two-branch sigmoid in "两个 head，手算一次".
+* "多头注意力与 GQA", section "分组查询注意力（GQA）" (head h reads KV group
+  floor(h / group_size)).
+* "Attention, worked all the way through": "Why scaling and stable softmax
+  matter" (subtract the row max before exp; a masked -inf gets weight 0) and
+  "Qwen3's exact order" (norm q and k, not v; then RoPE; then attention).
+* "Gated Attention for Large Language Models ... 论文阅读", section
+  "从标准注意力走到门控，计算流程有什么变化" (S, Y, g = sigmoid(X W_theta),
+  Y~ = Y ⊙ g, concat then W_O).
+
+Readings where the pages are silent (each is also listed in the design notes):
+* RMSNorm: x / sqrt(mean(x^2) + eps) * w, eps inside the root, w the
+  effective multiplier (parity with a real checkpoint's norm: unpinned).
+* RoPE: rotate-half pairs (t, t + r/2) inside the first r = rot_dim dims, angle
+  pos * base^(-2t/r); dims >= r untouched (checkpoint convention: unpinned).
+* The causal mask is by token index inside the call (j <= i); positions only
+  feed RoPE.
+* Decode: the new token at position L attends to the L cached keys and to
+  itself; cached K-hat is used as stored (already normed and rotated).
+"""
+from __future__ import annotations
+
+import math
+from typing import Iterable, Optional, Sequence
+
+import numpy as np
+
+GATE_NONE = "none"
+GATE_HEADWISE = "headwise"
+GATE_ELEMENTWISE = "elementwise"
+
+
+def _check_finite(name: str, x) -> None:
+    # The headwise gate helper on "Gated Attention：算完注意力，再决定用多少"
+    # rejects empty and non-finite inputs with ValueError; the oracle keeps
+    # that convention for every input it is given.
+    if x is None:
+        return
+    a = np.asarray(x)
+    if a.size == 0:
+        raise ValueError(f"{name}: expected a nonempty array")
+    if a.dtype.kind == "f" and not np.all(np.isfinite(a)):
+        raise ValueError(f"{name}: expected finite values")
+
+
+def rms_norm(x: np.ndarray, w: Optional[np.ndarray], eps: float, dtype=np.float64) -> np.ndarray:
+    """Per-vector RMSNorm over the last axis: x / sqrt(mean(x^2) + eps) * w.
+
+    QK-Norm of "Transformer by Hand · 6. Gated attention" (section "Four
+    things Qwen3.5 adds to the textbook": q and k each pass an RMSNorm, one
+    shared [d] weight per projection, before RoPE). ``w=None`` skips the norm.
+    Pinned by closed forms and scale invariance in the tests.
+    """
+    x = np.asarray(x, dtype=dtype)
+    if w is None:
+        return x
+    ms = np.mean(x * x, axis=-1, keepdims=True)
+    return x / np.sqrt(ms + dtype(eps)) * np.asarray(w, dtype=dtype)
+
+
+def rope_angles(positions: np.ndarray, rot_dim: int, base: float, dtype=np.float64) -> np.ndarray:
+    """Angles theta[..., t] = pos * base^(-2t/rot_dim) for t < rot_dim/2."""
+    half = rot_dim // 2
+    t = np.arange(half, dtype=np.float64)
+    inv_freq = np.power(np.float64(base), -2.0 * t / rot_dim)
+    return (np.asarray(positions, dtype=np.float64)[..., None] * inv_freq).astype(dtype)
+
+
+def rope(x: np.ndarray, positions: np.ndarray, rot_dim: int, base: float, dtype=np.float64) -> np.ndarray:
+    """Rotate the first ``rot_dim`` dims of x [..., T, heads, d] by position.
+
+    Partial RoPE of "Transformer by Hand · 6. Gated attention" (only the first
+    quarter of each head rotates; the rest stays position-free). Pair
+    convention (rotate-half within the rotated block) is a reading.
+    ``positions`` has shape [..., T]; ``rot_dim == 0`` returns x unchanged.
+    """
+    x = np.asarray(x, dtype=dtype)
+    if rot_dim == 0:
+        return x
+    half = rot_dim // 2
+    th = rope_angles(positions, rot_dim, base, dtype=np.float64)[..., None, :]  # [..., T, 1, half]
+    c = np.cos(th).astype(dtype)
+    s = np.sin(th).astype(dtype)
+    out = x.copy()
+    a = x[..., :half]
+    b = x[..., half:rot_dim]
+    out[..., :half] = a * c - b * s
+    out[..., half:rot_dim] = b * c + a * s
+    return out
+
+
+def sigmoid(z, dtype=np.float64):
+    """Two-branch stable logistic sigmoid.
+
+    As written on "Gated Attention：算完注意力，再决定用多少" (section
+    "两个 head，手算一次"): z >= 0 uses 1/(1+e^-z), z < 0 uses e^z/(1+e^z).
+    """
+    z = np.asarray(z, dtype=dtype)
+    out = np.empty_like(z)
+    pos = z >= 0
+    out[pos] = 1.0 / (1.0 + np.exp(-z[pos]))
+    ez = np.exp(z[~pos])
+    out[~pos] = ez / (1.0 + ez)
+    return out
+
+
+def apply_gate(y: np.ndarray, z: Optional[np.ndarray], gate_mode: str, dtype=np.float64) -> np.ndarray:
+    """Output gate on per-head attention outputs y [..., H, d].
+
+    Elementwise: y * sigmoid(z) with z [..., H, d]; headwise: one logit per
+    token per head, z [..., H]; none: y. Source: "Gated Attention：算完注意力，
+    再决定用多少", section "门放在哪里？" (G_h ⊙ O_h, headwise vs elementwise),
+    and "Transformer by Hand · 6. Gated attention", "How the gate is computed:
+    three steps" (g = sigmoid(z), multiplied dimension by dimension).
+    """
+    y = np.asarray(y, dtype=dtype)
+    if gate_mode == GATE_NONE:
+        return y
+    _check_finite("gate logits", z)
+    g = sigmoid(z, dtype=dtype)
+    if gate_mode == GATE_HEADWISE:
+        return y * g[..., None]
+    if gate_mode == GATE_ELEMENTWISE:
+        return y * g
+    raise ValueError(f"unknown gate mode {gate_mode!r}")
+
+
+def softmax_rows(s: np.ndarray, dtype=np.float64) -> np.ndarray:
+    """Stable row softmax: exp(x - max) / sum exp(x - max); -inf maps to 0.
+
+    "Attention, worked all the way through", section "Why scaling and stable
+    softmax matter".
+    """
+    s = np.asarray(s, dtype=dtype)
+    m = np.max(s, axis=-1, keepdims=True)
+    e = np.exp(s - m)
+    return e / np.sum(e, axis=-1, keepdims=True)
+
+
+def causal_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float,
+                     dtype=np.float64, return_weights: bool = False):
+    """One head: softmax(Q K^T * scale + M) V with M = -inf above the diagonal.
+
+    q [T,d], k [T,d], v [T,dv]. "Transformer by Hand · 6. Gated attention",
+    section "The formula"; "Attention, worked all the way through", section
+    "One head · explicit axes" (score, mask, row softmax, weighted read).
+    """
+    q = np.asarray(q, dtype=dtype)
+    k = np.asarray(k, dtype=dtype)
+    v = np.asarray(v, dtype=dtype)
+    T = q.shape[0]
+    s = (q @ k.T) * dtype(scale)
+    mask = np.triu(np.ones((T, k.shape[0]), dtype=bool), k=1)
+    s = np.where(mask, -np.inf, s)
+    a = softmax_rows(s, dtype=dtype)
+    o = a @ v
+    return (o, a) if return_weights else o
+
+
+def kv_group(h: int, n_q_heads: int, n_kv_heads: int) -> int:
+    """Query head h reads KV head floor(h / (H/G)) ("多头注意力与 GQA", GQA section)."""
+    return h // (n_q_heads // n_kv_heads)
+
+
+def _default_scale(d: int, scale: Optional[float]) -> float:
+    # 1/sqrt(head_dim): "The formula" on "Transformer by Hand · 6. Gated attention".
+    return 1.0 / math.sqrt(d) if not scale else float(scale)
+
+
+def prefill_keys(k, k_norm_w, positions, *, rms_eps: float, rope_base: float, rot_dim: int,
+                 dtype=np.float64) -> np.ndarray:
+    """K-hat = RoPE(RMSNorm(k)) for k [B,n,G,d]: what a prefill writes to a KV cache."""
+    kn = rms_norm(k, k_norm_w, rms_eps, dtype=dtype)
+    return rope(kn, positions, rot_dim, rope_base, dtype=dtype)
+
+
+def prefill(q, k, v, gate, *, gate_mode: str, q_norm_w, k_norm_w, positions,
+            rms_eps: float = 1e-6, rope_base: float = 10000.0, rot_dim: int = 0,
+            scale: Optional[float] = None, dtype=np.float64, block: int = 256) -> np.ndarray:
+    """Gated GQA causal attention over whole sequences.
+
+    q [B,n,H,d], k/v [B,n,G,d], gate [B,n,H,d] | [B,n,H] | None, norm weights
+    [d] or None, positions [B,n] int. Returns out [B,n,H*d] (the gated head
+    concat that W_O would consume). Query rows are processed in blocks of
+    ``block`` rows against all keys up to the block's last row; the blocking
+    does not change the result.
+    """
+    for name, x in (("q", q), ("k", k), ("v", v)):
+        _check_finite(name, x)
+    q = np.asarray(q)
+    B, n, H, d = q.shape
+    G = np.asarray(k).shape[2]
+    if H % G:
+        raise ValueError("n_q_heads must be a multiple of n_kv_heads")
+    sc = _default_scale(d, scale)
+    qh = rope(rms_norm(q, q_norm_w, rms_eps, dtype), positions, rot_dim, rope_base, dtype)
+    kh = prefill_keys(k, k_norm_w, positions, rms_eps=rms_eps, rope_base=rope_base,
+                      rot_dim=rot_dim, dtype=dtype)
+    vv = np.asarray(v, dtype=dtype)
+    y = np.empty((B, n, H, d), dtype=dtype)
+    for b in range(B):
+        for h in range(H):
+            g = kv_group(h, H, G)
+            for r0 in range(0, n, block):
+                r1 = min(n, r0 + block)
+                s = (qh[b, r0:r1, h] @ kh[b, :r1, g].T) * dtype(sc)       # [rows, r1]
+                rows = np.arange(r0, r1)[:, None]
+                s = np.where(np.arange(r1)[None, :] > rows, -np.inf, s)   # causal: j <= i
+                y[b, r0:r1, h] = softmax_rows(s, dtype) @ vv[b, :r1, g]
+    out = apply_gate(y, gate, gate_mode, dtype=dtype)
+    return out.reshape(B, n, H * d)
+
+
+def prefill_rows(q, k, v, gate, rows: Sequence[tuple], *, gate_mode: str, q_norm_w, k_norm_w,
+                 positions, rms_eps: float = 1e-6, rope_base: float = 10000.0, rot_dim: int = 0,
+                 scale: Optional[float] = None, dtype=np.float64) -> np.ndarray:
+    """The same computation for selected (b, i, h) rows only; returns [len(rows), d].
+
+    Used at sizes where the whole output is too expensive on the CPU.
+    """
+    q = np.asarray(q)
+    B, n, H, d = q.shape
+    G = np.asarray(k).shape[2]
+    sc = _default_scale(d, scale)
+    out = np.empty((len(rows), d), dtype=dtype)
+    khat_cache = {}
+    for r, (b, i, h) in enumerate(rows):
+        g = kv_group(h, H, G)
+        if (b, g) not in khat_cache:
+            khat_cache[(b, g)] = rope(rms_norm(np.asarray(k)[b, :, g][:, None, :], k_norm_w, rms_eps, dtype),
+                                      np.asarray(positions)[b], rot_dim, rope_base, dtype)[:, 0, :]
+        kh = khat_cache[(b, g)]
+        qv = rope(rms_norm(q[b, i, h][None, None, :], q_norm_w, rms_eps, dtype),
+                  np.asarray(positions)[b, i:i + 1], rot_dim, rope_base, dtype)[0, 0]
+        s = (kh[: i + 1] @ qv) * dtype(sc)
+        a = softmax_rows(s[None, :], dtype)[0]
+        y = a @ np.asarray(v, dtype=dtype)[b, : i + 1, g]
+        if gate_mode == GATE_ELEMENTWISE:
+            zz = np.asarray(gate)[b, i, h][None, :]          # [1 head, d]
+        elif gate_mode == GATE_HEADWISE:
+            zz = np.asarray(gate)[b, i, h:h + 1]             # [1 head]
+        else:
+            zz = None
+        out[r] = apply_gate(y[None, :], zz, gate_mode, dtype)[0]
+    return out
+
+
+def decode(q, k_new, v_new, gate, *, gate_mode: str, q_norm_w, k_norm_w, k_cache_rows: Iterable,
+           cache_lens, rms_eps: float = 1e-6, rope_base: float = 10000.0, rot_dim: int = 0,
+           scale: Optional[float] = None, dtype=np.float64, seqs: Optional[Sequence[int]] = None):
+    """One decode step per sequence.
+
+    q [B,H,d], k_new/v_new [B,G,d] (raw, before norm), gate [B,H,d] | [B,H].
+    ``k_cache_rows(b)`` returns (K-hat [L_b,G,d], V [L_b,G,d]) for sequence b:
+    the cached rows, used as stored. The new token sits at position L_b and
+    attends to the L_b cached keys and to itself (causal: a row sees j <= i).
+    Returns (out [len(seqs),H*d], k_hat_new [len(seqs),G,d]).
+
+    Source: "多头注意力与 GQA", section "标准多头注意力（MHA）" (a decode step
+    dots the new query with every cached key and mixes every cached value; Q
+    is never cached), with the prefill definition above for one row.
+    """
+    q = np.asarray(q)
+    B, H, d = q.shape
+    G = np.asarray(k_new).shape[1]
+    sc = _default_scale(d, scale)
+    lens = np.asarray(cache_lens)
+    seqs = list(range(B)) if seqs is None else list(seqs)
+    out = np.empty((len(seqs), H * d), dtype=dtype)
+    khn = np.empty((len(seqs), G, d), dtype=dtype)
+    for r, b in enumerate(seqs):
+        L = int(lens[b])
+        pos = np.array([L])
+        qh = rope(rms_norm(q[b][None], q_norm_w, rms_eps, dtype), pos, rot_dim, rope_base, dtype)[0]  # [H,d]
+        kn = rope(rms_norm(np.asarray(k_new)[b][None], k_norm_w, rms_eps, dtype), pos, rot_dim,
+                  rope_base, dtype)[0]                                                              # [G,d]
+        khn[r] = kn
+        kc, vc = k_cache_rows(b)
+        kc = np.asarray(kc, dtype=dtype)[:L]
+        vc = np.asarray(vc, dtype=dtype)[:L]
+        y = np.empty((H, d), dtype=dtype)
+        for h in range(H):
+            g = kv_group(h, H, G)
+            keys = np.concatenate([kc[:, g], kn[g][None]], axis=0)
+            vals = np.concatenate([vc[:, g], np.asarray(v_new, dtype=dtype)[b, g][None]], axis=0)
+            s = (keys @ qh[h]) * dtype(sc)
+            y[h] = softmax_rows(s[None], dtype)[0] @ vals
+        z = None if gate is None else np.asarray(gate)[b]
+        out[r] = apply_gate(y, z, gate_mode, dtype).reshape(H * d)
+    return out, khn

@@ -1,0 +1,162 @@
+"""Pins of the CPU oracle against an independent brute force, a library routine,
+closed forms and invariants of RMSNorm, RoPE, GQA and decode."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import attention as A
+from oracle import loops as L
+from gated_gqa_softmax_amd import accounting
+from tests.conftest import load_golden
+from tests.test_oracle_pins import _rand_case
+
+
+@pytest.mark.parametrize("seed,B,n,H,G,d,rot,mode", [
+    (0, 1, 5, 2, 1, 4, 4, "elementwise"),
+    (1, 2, 9, 4, 2, 8, 2, "headwise"),
+    (2, 1, 6, 4, 4, 8, 8, "none"),          # G = H: plain multi-head
+    (3, 2, 7, 8, 2, 2, 2, "elementwise"),   # group 4, d = 2
+    (4, 1, 9, 6, 3, 8, 0, "elementwise"),   # group 2 with 3 KV heads, no RoPE
+])
+def test_numpy_oracle_matches_bruteforce_loops(seed, B, n, H, G, d, rot, mode):
+    q, k, v, gate, wq, wk, pos = _rand_case(seed, B, n, H, G, d, rot, mode)
+    pos = pos + 3 * seed                                       # non-zero start positions
+    kw = dict(q_norm_w=wq, k_norm_w=wk, positions=pos, rms_eps=1e-6, rope_base=10000.0, rot_dim=rot)
+    got = A.prefill(q, k, v, gate, gate_mode=mode, **kw)
+    ref = L.gated_attention(q.tolist(), k.tolist(), v.tolist(),
+                            None if gate is None else gate.tolist(), mode, wq.tolist(), wk.tolist(),
+                            pos.tolist(), 1e-6, 10000.0, rot)
+    assert np.allclose(got, np.array(ref), atol=1e-12, rtol=0)
+
+
+def test_ungated_core_matches_torch_sdpa():
+    """Norm/RoPE off, gate off: the oracle equals torch's fp64 CPU SDPA with
+    K/V repeated per group (repeat_interleave, as the page's forward code does)."""
+    q, k, v, _, _, _, pos = _rand_case(11, B=2, n=13, H=6, G=2, d=16, rot=0)
+    got = A.prefill(q, k, v, None, gate_mode=A.GATE_NONE, q_norm_w=None, k_norm_w=None,
+                    positions=pos, rot_dim=0)
+    tq = torch.from_numpy(q).permute(0, 2, 1, 3)
+    tk = torch.from_numpy(k).permute(0, 2, 1, 3).repeat_interleave(3, dim=1)
+    tv = torch.from_numpy(v).permute(0, 2, 1, 3).repeat_interleave(3, dim=1)
+    ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, is_causal=True)
+    ref = ref.permute(0, 2, 1, 3).reshape(2, 13, 6 * 16).numpy()
+    assert np.allclose(got, ref, atol=1e-12, rtol=0)
+
+
+def test_gqa_mapping_is_contiguous_groups():
+    # floor(h / group), not h mod G: heads 0,1,2 -> KV 0; heads 3,4,5 -> KV 1.
+    assert [A.kv_group(h, 6, 2) for h in range(6)] == [0, 0, 0, 1, 1, 1]
+    q, k, v, _, _, _, pos = _rand_case(12, B=1, n=5, H=4, G=2, d=4, rot=0, gate_mode="none")
+    out = A.prefill(q, k, v, None, gate_mode="none", q_norm_w=None, k_norm_w=None, positions=pos)
+    # head 1 must equal single-head attention of q head 1 against KV head 0
+    o1 = A.causal_attention(q[0, :, 1], k[0, :, 0], v[0, :, 0], 0.5)
+    assert np.allclose(out[0, :, 4:8], o1, atol=1e-14)
+
+
+def test_rms_norm_closed_forms():
+    x = np.array([3.0, -4.0, 0.0, 0.0])                 # mean square = 25/4
+    y = A.rms_norm(x, np.ones(4), eps=0.0)
+    assert np.allclose(y, x / 2.5, atol=1e-15)
+    y = A.rms_norm(x, np.ones(4), eps=2.0)              # eps inside the root
+    assert np.allclose(y, x / math.sqrt(25 / 4 + 2.0), atol=1e-15)
+    w = np.array([1.0, 2.0, 3.0, 4.0])
+    assert np.allclose(A.rms_norm(x, w, eps=0.0), x / 2.5 * w, atol=1e-15)
+    rng = np.random.default_rng(0)
+    z = rng.standard_normal((5, 64))
+    assert np.allclose(A.rms_norm(7.5 * z, None, 0.0), 7.5 * z)         # None = no norm
+    assert np.allclose(A.rms_norm(7.5 * z, np.ones(64), 1e-9), A.rms_norm(z, np.ones(64), 1e-9), atol=1e-9)
+    r = A.rms_norm(z, np.ones(64), 0.1)
+    ms = np.mean(z * z, axis=-1)
+    assert np.allclose(np.sqrt(np.mean(r * r, -1)), (1 + 0.1 / ms) ** -0.5, atol=1e-14)
+
+
+def test_rope_closed_form_and_invariants():
+    # rot = 2: one pair (0, 1), theta = pos exactly
+    x = np.array([[[0.3, -1.2, 5.0, 7.0]]])           # [T=1, heads=1, d=4]
+    for p in (0, 1, 5, 1000):
+        y = A.rope(x, np.array([p]), 2, 10000.0)
+        c, s = math.cos(p), math.sin(p)
+        assert np.allclose(y[0, 0], [0.3 * c + 1.2 * s, -1.2 * c + 0.3 * s, 5.0, 7.0], atol=1e-12)
+    # rot = 4 on d = 6: pairs (0,2) and (1,3), second pair angle pos * base^(-1/2)
+    x = np.arange(1.0, 7.0)[None, None]
+    y = A.rope(x, np.array([3]), 4, 100.0)[0, 0]
+    t0, t1 = 3.0, 3.0 / 10.0
+    want = [1 * math.cos(t0) - 3 * math.sin(t0), 2 * math.cos(t1) - 4 * math.sin(t1),
+            3 * math.cos(t0) + 1 * math.sin(t0), 4 * math.cos(t1) + 2 * math.sin(t1), 5, 6]
+    assert np.allclose(y, want, atol=1e-12)
+    rng = np.random.default_rng(1)
+    q = rng.standard_normal((1, 1, 32))
+    k = rng.standard_normal((1, 1, 32))
+    assert np.array_equal(A.rope(q, np.array([0]), 8, 10000.0), q)          # pos 0 is identity
+    y = A.rope(q, np.array([77]), 8, 10000.0)
+    assert np.array_equal(y[..., 8:], q[..., 8:])                           # untouched tail
+    n_in = q[..., :4] ** 2 + q[..., 4:8] ** 2
+    n_out = y[..., :4] ** 2 + y[..., 4:8] ** 2
+    assert np.allclose(n_in, n_out, atol=1e-12)                             # pair norms kept
+    # <R_m q, R_n k> depends on m - n only
+    d1 = np.sum(A.rope(q, np.array([40]), 8, 10000.0) * A.rope(k, np.array([13]), 8, 10000.0))
+    d2 = np.sum(A.rope(q, np.array([140]), 8, 10000.0) * A.rope(k, np.array([113]), 8, 10000.0))
+    assert d1 == pytest.approx(d2, abs=1e-11)
+
+
+def test_prefill_rows_and_block_size_agree_with_full():
+    q, k, v, gate, wq, wk, pos = _rand_case(5, B=2, n=40, H=4, G=2, d=16, rot=4)
+    kw = dict(gate_mode="elementwise", q_norm_w=wq, k_norm_w=wk, positions=pos, rot_dim=4)
+    full = A.prefill(q, k, v, gate, **kw)
+    small_blocks = A.prefill(q, k, v, gate, block=7, **kw)
+    assert np.allclose(full, small_blocks, atol=1e-14)
+    rows = [(0, 0, 0), (1, 39, 3), (0, 17, 2), (1, 5, 1)]
+    got = A.prefill_rows(q, k, v, gate, rows, **kw)
+    for r, (b, i, h) in enumerate(rows):
+        assert np.allclose(got[r], full[b, i, h * 16:(h + 1) * 16], atol=1e-14)
+
+
+def test_decode_is_last_row_of_prefill():
+    q, k, v, gate, wq, wk, pos = _rand_case(6, B=2, n=12, H=4, G=2, d=16, rot=8)
+    kw = dict(q_norm_w=wq, k_norm_w=wk, rms_eps=1e-6, rope_base=10000.0, rot_dim=8)
+    full = A.prefill(q, k, v, gate, gate_mode="elementwise", positions=pos, **kw)
+    L0 = 11
+    khat = A.prefill_keys(k, wk, pos, rms_eps=1e-6, rope_base=10000.0, rot_dim=8)
+    out, khn = A.decode(q[:, L0], k[:, L0], v[:, L0], gate[:, L0], gate_mode="elementwise",
+                        k_cache_rows=lambda b: (khat[b, :L0], v[b, :L0]),
+                        cache_lens=np.array([L0, L0]), **kw)
+    assert np.allclose(out, full[:, L0], atol=1e-13)
+    assert np.allclose(khn, khat[:, L0], atol=1e-14)
+
+
+def test_decode_empty_cache_is_gated_value():
+    rng = np.random.default_rng(9)
+    q = rng.standard_normal((1, 2, 8))
+    kn = rng.standard_normal((1, 1, 8))
+    vn = rng.standard_normal((1, 1, 8))
+    z = rng.standard_normal((1, 2, 8))
+    out, _ = A.decode(q, kn, vn, z, gate_mode="elementwise", q_norm_w=None, k_norm_w=None,
+                      k_cache_rows=lambda b: (np.zeros((0, 1, 8)), np.zeros((0, 1, 8))),
+                      cache_lens=np.array([0]), rot_dim=0)
+    want = np.concatenate([vn[0, 0] * A.sigmoid(z[0, 0]), vn[0, 0] * A.sigmoid(z[0, 1])])
+    assert np.allclose(out[0], want, atol=1e-15)
+
+
+def test_kv_cache_size_closed_forms():
+    g = load_golden("kv_cache_sizes.json")
+    p = g["per_token"]
+    assert accounting.kv_numbers_per_token(p["n_kv_heads"], p["head_dim"]) == p["gqa_numbers"]
+    assert accounting.kv_numbers_per_token(p["n_q_heads"], p["head_dim"]) == p["mha_numbers"]
+    w = g["whole_model_8k"]
+    gqa = accounting.kv_cache_bytes(w["tokens"], w["layers"], 2, w["head_dim"], w["elem_bytes"])
+    mha = accounting.kv_cache_bytes(w["tokens"], w["layers"], 8, w["head_dim"], w["elem_bytes"])
+    assert gqa / w["mb_unit_bytes"] == w["gqa_mb"]
+    assert mha / w["mb_unit_bytes"] == w["mha_mb"]
+    # decode bytes: cache term plus per-sequence traffic
+    lens = [1024, 3]
+    got = accounting.decode_bytes(lens, 8, 2, 256)
+    assert got == 1027 * 1024 * 2 + 2 * (2048 + 2048 + 1024 + 2048 + 1024) * 2
+
+
+def test_causal_flop_count():
+    # brute count of visible pairs: n(n+1)/2 pairs, 4d flops each
+    n, d, H, B = 37, 8, 3, 2
+    pairs = sum(i + 1 for i in range(n))
+    assert accounting.causal_prefill_flops(B, H, d, n) == B * H * pairs * 4 * d
