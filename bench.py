@@ -1,0 +1,233 @@
+#!/usr/bin/env python3
+"""Throughput of gated GQA causal attention on one MI355X.
+
+One step is one prefill pass (ga_prefill: the K-hat kernel then the fused
+attention kernel) over the Qwen3.5-0.8B-shaped workload (B=1, n=4096, H=8,
+G=2, d=256, RoPE on 64 dims, elementwise gate, bf16). The decode half of the
+metric (ga_decode over 64 sequences with cache lengths ~U[1024, 32768]) is
+measured in the same run and reported under "decode".
+
+Printed: one JSON line. ``value`` is prefill TFLOP/s counting only the
+unmasked causal work 2*B*H*d*n*(n+1); ``roofline`` relates the attention
+kernel's own duration (HIP events around each launch, on its stream) to the
+bf16 dense MFMA peak; ``cpu_baseline`` times the CPU oracle on the host.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+MI355X_BF16_DENSE_TFLOPS = 2500.0
+MI355X_HBM_GBS = 8000.0
+METRIC = "gated GQA attn fwd TFLOP/s (prefill) + decode KV GB/s, % of MI355X roofline"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="qwen35_0p8b_prefill",
+                    help="prefill workload to time (default: the headline one)")
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--decode-steps", type=int, default=20)
+    return ap.parse_args()
+
+
+def time_prefill(torch, api, inputs, accounting, wname, steps, warmup):
+    w = inputs.WORKLOADS[wname]
+    x = inputs.make_prefill(w)
+    et = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    dv = lambda a, dt=None: torch.from_numpy(np.ascontiguousarray(a)).to("cuda", dtype=dt) if a is not None else None
+    q, k, v = dv(x["q"], et), dv(x["k"], et), dv(x["v"], et)
+    gate = dv(x["gate"], et)
+    wq, wk, pos = dv(x["q_norm_w"]), dv(x["k_norm_w"]), dv(x["positions"])
+    d = api.make_desc(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.rot_dim, w.rope_base, w.rms_eps, 0.0, et,
+                      w.gate_mode)
+    khat = torch.empty_like(k)
+    out = torch.empty((w.batch, w.seq_len, w.n_q_heads * w.head_dim), dtype=et, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step(ev0=None, ev1=None):
+        # exactly what ga_prefill does, with events around the attention kernel
+        api.ga_prefill_keys(d, k, None, wk, pos, k_hat=khat, stream=stream)
+        if ev0 is not None:
+            ev0.record(stream)
+        api.ga_prefill_attention(d, q, khat, v, gate, wq, pos, out=out, stream=stream)
+        if ev1 is not None:
+            ev1.record(stream)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(*ev[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    attn_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    # whole ga_prefill calls, for the step figure
+    ws = torch.empty(api.ga_prefill_workspace_bytes(d, w.seq_len), dtype=torch.uint8, device="cuda")
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(steps):
+        api.ga_prefill(d, q, k, v, gate, wq, wk, pos, out=out, workspace=ws, stream=stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    step_ms = e0.elapsed_time(e1) / steps
+    flops = accounting.causal_prefill_flops(w.batch, w.n_q_heads, w.head_dim, w.seq_len)
+    return dict(w=w, x=x, flops=flops, attn_ms=attn_ms, step_ms=step_ms, wall_s=wall)
+
+
+def time_decode(torch, api, inputs, accounting, steps, warmup):
+    w = inputs.WORKLOADS["decode_64seq"]
+    x = inputs.make_decode(w)
+    et = torch.bfloat16
+    lens = x["cache_lens"]
+    max_len = int(lens.max())
+    cap = max_len + 1
+    kc = torch.empty((w.batch, cap, w.n_kv_heads, w.head_dim), dtype=et, device="cuda")
+    vc = torch.empty_like(kc)
+
+    def put(b, kh, vv):
+        kc[b, : len(kh)] = torch.from_numpy(kh).to("cuda", dtype=et)
+        vc[b, : len(vv)] = torch.from_numpy(vv).to("cuda", dtype=et)
+
+    inputs.for_each_cache_rows(w, lens, put, threads=min(16, os.cpu_count() or 1))
+    dv = lambda a, dt=None: torch.from_numpy(np.ascontiguousarray(a)).to("cuda", dtype=dt)
+    q, kn, vn, gate = dv(x["q"], et), dv(x["k_new"], et), dv(x["v_new"], et), dv(x["gate"], et)
+    wq, wk, dl = dv(x["q_norm_w"]), dv(x["k_norm_w"]), dv(lens)
+    d = api.make_desc(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.rot_dim, w.rope_base, w.rms_eps, 0.0, et,
+                      w.gate_mode)
+    ws = torch.empty(api.ga_decode_workspace_bytes(d, max_len), dtype=torch.uint8, device="cuda")
+    out = torch.empty((w.batch, w.n_q_heads * w.head_dim), dtype=et, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step(ev0=None, ev1=None):
+        if ev0 is not None:
+            ev0.record(stream)
+        api.ga_decode_partials(d, q, kc, vc, dl, max_len, ws, q_norm_w=wq, stream=stream)
+        if ev1 is not None:
+            ev1.record(stream)
+        api.ga_decode_merge(d, q, kn, vn, kc, vc, dl, max_len, ws, gate=gate, q_norm_w=wq, k_norm_w=wk, out=out,
+                            stream=stream)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for i in range(steps):
+        step(*ev[i])
+    e1.record(stream)
+    torch.cuda.synchronize()
+    step_ms = e0.elapsed_time(e1) / steps
+    part_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    total_bytes = accounting.decode_bytes(lens, w.n_q_heads, w.n_kv_heads, w.head_dim, 2, w.gate_mode)
+    cache_bytes = int(lens.astype(np.int64).sum()) * 2 * w.n_kv_heads * w.head_dim * 2
+    part_bytes = cache_bytes + w.batch * w.n_q_heads * w.head_dim * 2          # cache + q
+    return {
+        "metric": "decode KV GB/s",
+        "value": total_bytes / (step_ms * 1e-3) / 1e9,
+        "unit": "GB/s",
+        "ms_per_step": step_ms,
+        "steps": steps,
+        "config": {"workload": w.name, "batch": w.batch, "cache_len_range": [w.cache_len_lo, w.cache_len_hi],
+                   "sum_cache_len": int(lens.sum()), "n_q_heads": w.n_q_heads, "n_kv_heads": w.n_kv_heads,
+                   "head_dim": w.head_dim, "rot_dim": w.rot_dim, "gate": w.gate_mode},
+        "bytes_per_step": total_bytes,
+        "roofline": {"bound": "hbm", "kernel": "decode_partials_kernel", "achieved": part_bytes / (part_ms * 1e-3) / 1e9,
+                     "peak": MI355X_HBM_GBS, "unit": "GB/s",
+                     "frac": part_bytes / (part_ms * 1e-3) / 1e9 / MI355X_HBM_GBS, "traffic": None,
+                     "kernel_ms": part_ms, "algorithmic_bytes": part_bytes},
+    }
+
+
+def cpu_baseline(w, x, flops, budget_s=12.0):
+    """The CPU oracle, as it stands, on the whole prefill workload, repeated
+    until about budget_s seconds of work (at least once)."""
+    from oracle import attention as oracle
+    try:
+        import threadpoolctl
+        threads = max((i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()), default=1)
+    except Exception:  # pragma: no cover
+        threads = 1
+    times = []
+    t_start = time.perf_counter()
+    while True:
+        t0 = time.perf_counter()
+        oracle.prefill(x["q"], x["k"], x["v"], x["gate"], gate_mode=w.gate_mode, q_norm_w=x["q_norm_w"],
+                       k_norm_w=x["k_norm_w"], positions=x["positions"], rms_eps=w.rms_eps, rope_base=w.rope_base,
+                       rot_dim=w.rot_dim)
+        times.append(time.perf_counter() - t0)
+        if time.perf_counter() - t_start > budget_s or len(times) >= 8:
+            break
+    t = float(np.median(times))
+    cpu = ""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                cpu = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"whole {w.name} workload, fp64 NumPy oracle, median of {len(times)} runs "
+                      f"({t:.2f} s each)", "cpu": cpu}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(multi-GPU sharding of this path is design-only)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    from gated_gqa_softmax_amd import accounting, api, inputs
+
+    pre = time_prefill(torch, api, inputs, accounting, args.workload, args.steps, args.warmup)
+    w = pre["w"]
+    achieved = pre["flops"] / (pre["attn_ms"] * 1e-3) / 1e12
+    rec = {
+        "metric": METRIC,
+        "value": pre["flops"] / (pre["step_ms"] * 1e-3) / 1e12,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": pre["step_ms"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "seq_len": w.seq_len, "n_q_heads": w.n_q_heads,
+                   "n_kv_heads": w.n_kv_heads, "head_dim": w.head_dim, "rot_dim": w.rot_dim, "gate": w.gate_mode,
+                   "parallelism": "single-gpu"},
+        "roofline": {"bound": "mfma", "kernel": "prefill_mfma_kernel", "achieved": achieved,
+                     "peak": MI355X_BF16_DENSE_TFLOPS, "unit": "TFLOP/s", "frac": achieved / MI355X_BF16_DENSE_TFLOPS,
+                     "traffic": None, "kernel_ms": pre["attn_ms"], "algorithmic_flops": pre["flops"]},
+    }
+    if not args.no_decode:
+        rec["decode"] = time_decode(torch, api, inputs, accounting, args.decode_steps, args.warmup)
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(w, pre["x"], pre["flops"])
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

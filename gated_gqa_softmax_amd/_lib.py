@@ -1,0 +1,91 @@
+"""ctypes loader for libga.so and the C declarations of include/ga.h.
+
+Loading fails loudly when the library has not been built: there is no
+fallback implementation anywhere in the package.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libga.so")
+
+GA_OK = 0
+GA_ERR_NULL_ARG = 1
+GA_ERR_BAD_SHAPE = 2
+GA_ERR_BAD_DTYPE = 3
+GA_ERR_UNSUPPORTED = 4
+GA_ERR_MISALIGNED = 5
+GA_ERR_WORKSPACE = 6
+GA_ERR_HIP = 7
+
+GA_BF16 = 0
+GA_F32 = 1
+GA_GATE_NONE = 0
+GA_GATE_HEADWISE = 1
+GA_GATE_ELEMENTWISE = 2
+
+
+class AttnDesc(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32),
+        ("n_q_heads", ctypes.c_int32),
+        ("n_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("rot_dim", ctypes.c_int32),
+        ("rope_base", ctypes.c_float),
+        ("rms_eps", ctypes.c_float),
+        ("softmax_scale", ctypes.c_float),
+        ("dtype", ctypes.c_int32),
+        ("gate_mode", ctypes.c_int32),
+    ]
+
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int32
+_S = ctypes.c_size_t
+_D = ctypes.POINTER(AttnDesc)
+
+SIGNATURES = {
+    "ga_prefill_workspace_bytes": (_S, [_D, _I]),
+    "ga_prefill": (_I, [_D, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _P, _S, _P, _P]),
+    "ga_prefill_keys": (_I, [_D, _I, _P, _P, _P, _P, _P, _P, _I, _P]),
+    "ga_prefill_attention": (_I, [_D, _I, _P, _P, _I, _P, _I, _P, _P, _P, _P, _P]),
+    "ga_decode_split_keys": (_I, []),
+    "ga_decode_workspace_bytes": (_S, [_D, _I]),
+    "ga_decode": (_I, [_D, _P, _P, _P, _P, _P, _P, _P, _P, _I, _P, _I, _P, _S, _P, _P]),
+    "ga_decode_partials": (_I, [_D, _P, _P, _P, _P, _I, _P, _I, _P, _S, _P]),
+    "ga_decode_merge": (_I, [_D, _P, _P, _P, _P, _P, _P, _P, _P, _I, _P, _I, _P, _S, _P, _P]),
+    "ga_status_string": (ctypes.c_char_p, [_I]),
+    "ga_last_error": (ctypes.c_char_p, []),
+    "ga_fast_path": (_I, [_I, _I, _I, _I]),
+    "ga_version": (_I, []),
+}
+
+_lock = threading.Lock()
+_lib = None
+
+
+class LibraryNotBuilt(RuntimeError):
+    pass
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libga.so once and attach the declared signatures."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(path):
+            raise LibraryNotBuilt(
+                f"{path} not found: build it with `python -m gated_gqa_softmax_amd.build` "
+                "(the package has no non-HIP implementation)")
+        lib = ctypes.CDLL(path)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = lib
+        return lib

@@ -1,0 +1,205 @@
+"""Python binding of the C ABI (include/ga.h), one function per entry point.
+
+Argument marshalling only: each function checks that tensors are on the
+GPU, contiguous and of the declared element type, fills the ``ga_attn_desc``,
+passes raw device pointers and the current HIP stream to libga.so, and
+raises ``GaError`` when the library returns a non-OK status. Every step of
+the computation runs in the library's HIP kernels. PyTorch supplies device
+memory and the stream; workspaces the caller does not pass are allocated
+here with torch.
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import Optional
+
+import torch
+
+from . import _lib
+from ._lib import AttnDesc
+
+_GATE = {"none": _lib.GA_GATE_NONE, "headwise": _lib.GA_GATE_HEADWISE,
+         "elementwise": _lib.GA_GATE_ELEMENTWISE}
+_DTYPE = {torch.bfloat16: _lib.GA_BF16, torch.float32: _lib.GA_F32}
+
+
+class GaError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        lib = _lib.load()
+        self.status = status
+        self.name = lib.ga_status_string(status).decode()
+        self.detail = lib.ga_last_error().decode()
+        super().__init__(f"{where}: {self.name}: {self.detail}")
+
+
+def make_desc(batch, n_q_heads, n_kv_heads, head_dim, rot_dim=0, rope_base=10000.0, rms_eps=1e-6,
+              softmax_scale=0.0, dtype=torch.bfloat16, gate_mode="none") -> AttnDesc:
+    return AttnDesc(int(batch), int(n_q_heads), int(n_kv_heads), int(head_dim), int(rot_dim),
+                    float(rope_base), float(rms_eps), float(softmax_scale),
+                    _DTYPE[dtype] if isinstance(dtype, torch.dtype) else int(dtype),
+                    _GATE[gate_mode] if isinstance(gate_mode, str) else int(gate_mode))
+
+
+def _ptr(t: Optional[torch.Tensor], name: str, dtype=None) -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    return t.data_ptr()
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _check(status: int, where: str):
+    if status != _lib.GA_OK:
+        raise GaError(status, where)
+
+
+def _elem_dtype(desc: AttnDesc):
+    return torch.bfloat16 if desc.dtype == _lib.GA_BF16 else torch.float32
+
+
+def ga_version() -> int:
+    return _lib.load().ga_version()
+
+
+def ga_status_string(status: int) -> str:
+    return _lib.load().ga_status_string(status).decode()
+
+
+def ga_last_error() -> str:
+    return _lib.load().ga_last_error().decode()
+
+
+def ga_fast_path(dtype, head_dim: int, rot_dim: int, group: int) -> int:
+    dt = _DTYPE[dtype] if isinstance(dtype, torch.dtype) else int(dtype)
+    return _lib.load().ga_fast_path(dt, head_dim, rot_dim, group)
+
+
+def ga_decode_split_keys() -> int:
+    return _lib.load().ga_decode_split_keys()
+
+
+def ga_prefill_workspace_bytes(desc: AttnDesc, seq_len: int) -> int:
+    return _lib.load().ga_prefill_workspace_bytes(ctypes.byref(desc), seq_len)
+
+
+def ga_decode_workspace_bytes(desc: AttnDesc, max_cache_len: int) -> int:
+    return _lib.load().ga_decode_workspace_bytes(ctypes.byref(desc), max_cache_len)
+
+
+def _workspace(nbytes: int, device, workspace: Optional[torch.Tensor]):
+    if workspace is not None:
+        return workspace
+    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+
+
+def ga_prefill(desc: AttnDesc, q, k, v, gate=None, q_norm_w=None, k_norm_w=None, positions=None,
+               k_cache=None, v_cache=None, out=None, workspace=None, stream=None) -> torch.Tensor:
+    """out [B,n,H*d] = gated GQA causal attention of q [B,n,H,d], k, v [B,n,G,d]."""
+    lib = _lib.load()
+    et = _elem_dtype(desc)
+    B, n = q.shape[0], q.shape[1]
+    if out is None:
+        out = torch.empty((B, n, desc.n_q_heads * desc.head_dim), dtype=et, device=q.device)
+    cap = 0
+    if k_cache is not None:
+        cap = k_cache.shape[1]
+        ws_bytes = 0
+    else:
+        ws_bytes = ga_prefill_workspace_bytes(desc, n)
+        workspace = _workspace(ws_bytes, q.device, workspace)
+    st = lib.ga_prefill(ctypes.byref(desc), n, _ptr(q, "q", et), _ptr(k, "k", et), _ptr(v, "v", et),
+                        _ptr(gate, "gate", et), _ptr(q_norm_w, "q_norm_w", torch.float32),
+                        _ptr(k_norm_w, "k_norm_w", torch.float32), _ptr(positions, "positions", torch.int32),
+                        _ptr(k_cache, "k_cache", et), _ptr(v_cache, "v_cache", et), cap,
+                        _ptr(workspace, "workspace"), workspace.numel() if workspace is not None else 0,
+                        _ptr(out, "out", et), _stream(stream))
+    _check(st, "ga_prefill")
+    return out
+
+
+def ga_prefill_keys(desc: AttnDesc, k, v=None, k_norm_w=None, positions=None, k_hat=None, v_out=None,
+                    stream=None) -> torch.Tensor:
+    lib = _lib.load()
+    et = _elem_dtype(desc)
+    n = k.shape[1]
+    if k_hat is None:
+        k_hat = torch.empty_like(k)
+    cap = k_hat.shape[1]
+    st = lib.ga_prefill_keys(ctypes.byref(desc), n, _ptr(k, "k", et), _ptr(v, "v", et),
+                             _ptr(k_norm_w, "k_norm_w", torch.float32), _ptr(positions, "positions", torch.int32),
+                             _ptr(k_hat, "k_hat", et), _ptr(v_out, "v_out", et), cap, _stream(stream))
+    _check(st, "ga_prefill_keys")
+    return k_hat
+
+
+def ga_prefill_attention(desc: AttnDesc, q, k_hat, v, gate=None, q_norm_w=None, positions=None, out=None,
+                         stream=None) -> torch.Tensor:
+    lib = _lib.load()
+    et = _elem_dtype(desc)
+    B, n = q.shape[0], q.shape[1]
+    if out is None:
+        out = torch.empty((B, n, desc.n_q_heads * desc.head_dim), dtype=et, device=q.device)
+    st = lib.ga_prefill_attention(ctypes.byref(desc), n, _ptr(q, "q", et), _ptr(k_hat, "k_hat", et), k_hat.shape[1],
+                                  _ptr(v, "v", et), v.shape[1], _ptr(gate, "gate", et),
+                                  _ptr(q_norm_w, "q_norm_w", torch.float32), _ptr(positions, "positions", torch.int32),
+                                  _ptr(out, "out", et), _stream(stream))
+    _check(st, "ga_prefill_attention")
+    return out
+
+
+def ga_decode(desc: AttnDesc, q, k_new, v_new, k_cache, v_cache, cache_lens, max_cache_len: int, gate=None,
+              q_norm_w=None, k_norm_w=None, out=None, workspace=None, stream=None) -> torch.Tensor:
+    """out [B,H*d] for one new token per sequence; appends K-hat/V at slot cache_lens[b]."""
+    lib = _lib.load()
+    et = _elem_dtype(desc)
+    B = q.shape[0]
+    if out is None:
+        out = torch.empty((B, desc.n_q_heads * desc.head_dim), dtype=et, device=q.device)
+    workspace = _workspace(ga_decode_workspace_bytes(desc, max_cache_len), q.device, workspace)
+    st = lib.ga_decode(ctypes.byref(desc), _ptr(q, "q", et), _ptr(k_new, "k_new", et), _ptr(v_new, "v_new", et),
+                       _ptr(gate, "gate", et), _ptr(q_norm_w, "q_norm_w", torch.float32),
+                       _ptr(k_norm_w, "k_norm_w", torch.float32), _ptr(k_cache, "k_cache", et),
+                       _ptr(v_cache, "v_cache", et), k_cache.shape[1], _ptr(cache_lens, "cache_lens", torch.int32),
+                       int(max_cache_len), _ptr(workspace, "workspace"), workspace.numel(), _ptr(out, "out", et),
+                       _stream(stream))
+    _check(st, "ga_decode")
+    return out
+
+
+def ga_decode_partials(desc: AttnDesc, q, k_cache, v_cache, cache_lens, max_cache_len: int, workspace,
+                       q_norm_w=None, stream=None) -> torch.Tensor:
+    lib = _lib.load()
+    et = _elem_dtype(desc)
+    st = lib.ga_decode_partials(ctypes.byref(desc), _ptr(q, "q", et), _ptr(q_norm_w, "q_norm_w", torch.float32),
+                                _ptr(k_cache, "k_cache", et), _ptr(v_cache, "v_cache", et), k_cache.shape[1],
+                                _ptr(cache_lens, "cache_lens", torch.int32), int(max_cache_len),
+                                _ptr(workspace, "workspace"), workspace.numel(), _stream(stream))
+    _check(st, "ga_decode_partials")
+    return workspace
+
+
+def ga_decode_merge(desc: AttnDesc, q, k_new, v_new, k_cache, v_cache, cache_lens, max_cache_len: int, workspace,
+                    gate=None, q_norm_w=None, k_norm_w=None, out=None, stream=None) -> torch.Tensor:
+    lib = _lib.load()
+    et = _elem_dtype(desc)
+    B = q.shape[0]
+    if out is None:
+        out = torch.empty((B, desc.n_q_heads * desc.head_dim), dtype=et, device=q.device)
+    st = lib.ga_decode_merge(ctypes.byref(desc), _ptr(q, "q", et), _ptr(k_new, "k_new", et), _ptr(v_new, "v_new", et),
+                             _ptr(gate, "gate", et), _ptr(q_norm_w, "q_norm_w", torch.float32),
+                             _ptr(k_norm_w, "k_norm_w", torch.float32), _ptr(k_cache, "k_cache", et),
+                             _ptr(v_cache, "v_cache", et), k_cache.shape[1],
+                             _ptr(cache_lens, "cache_lens", torch.int32), int(max_cache_len),
+                             _ptr(workspace, "workspace"), workspace.numel(), _ptr(out, "out", et), _stream(stream))
+    _check(st, "ga_decode_merge")
+    return out

@@ -1,0 +1,446 @@
+// C ABI: argument validation, dispatch to the fused or generic kernels.
+// Every check runs on the host before any launch; nothing is allocated.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "../../include/ga.h"
+#include "ga_internal.hpp"
+
+using namespace ga;
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+ga_status fail(ga_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+ga_status ok() {
+  g_last_error[0] = '\0';
+  return GA_OK;
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+int elem_bytes(const ga_attn_desc* d) { return d->dtype == GA_BF16 ? 2 : 4; }
+
+ga_status check_desc(const ga_attn_desc* d) {
+  if (!d) return fail(GA_ERR_NULL_ARG, "desc is NULL");
+  if (d->dtype != GA_BF16 && d->dtype != GA_F32) return fail(GA_ERR_BAD_DTYPE, "dtype %d out of range", d->dtype);
+  if (d->gate_mode < GA_GATE_NONE || d->gate_mode > GA_GATE_ELEMENTWISE)
+    return fail(GA_ERR_BAD_DTYPE, "gate_mode %d out of range", d->gate_mode);
+  if (d->batch < 0) return fail(GA_ERR_BAD_SHAPE, "batch %d < 0", d->batch);
+  if (d->n_q_heads < 1 || d->n_kv_heads < 1) return fail(GA_ERR_BAD_SHAPE, "head counts must be >= 1");
+  if (d->n_q_heads % d->n_kv_heads) return fail(GA_ERR_BAD_SHAPE, "n_q_heads %d not a multiple of n_kv_heads %d",
+                                                d->n_q_heads, d->n_kv_heads);
+  if (d->head_dim < 1) return fail(GA_ERR_BAD_SHAPE, "head_dim %d < 1", d->head_dim);
+  if (d->head_dim > 256) return fail(GA_ERR_UNSUPPORTED, "head_dim %d > 256", d->head_dim);
+  if (d->rot_dim < 0 || d->rot_dim > d->head_dim || (d->rot_dim & 1))
+    return fail(GA_ERR_BAD_SHAPE, "rot_dim %d must be even and in [0, head_dim]", d->rot_dim);
+  if (d->rot_dim > 0 && !(d->rope_base > 0.f && isfinite(d->rope_base)))
+    return fail(GA_ERR_BAD_SHAPE, "rope_base must be finite and > 0");
+  if (!(d->rms_eps >= 0.f && isfinite(d->rms_eps))) return fail(GA_ERR_BAD_SHAPE, "rms_eps must be finite, >= 0");
+  if (!(d->softmax_scale >= 0.f && isfinite(d->softmax_scale)))
+    return fail(GA_ERR_BAD_SHAPE, "softmax_scale must be finite, >= 0");
+  return GA_OK;
+}
+
+float scale_of(const ga_attn_desc* d) {
+  return d->softmax_scale > 0.f ? d->softmax_scale : (float)(1.0 / sqrt((double)d->head_dim));
+}
+
+// Angular frequencies base^(-2t/rot), computed in fp64 on the host.
+void fill_inv_freq(const ga_attn_desc* d, double* inv_freq) {
+  const int half = d->rot_dim / 2;
+  for (int t = 0; t < kMaxHalfRot; ++t)
+    inv_freq[t] = (t < half) ? pow((double)d->rope_base, -2.0 * t / (double)d->rot_dim) : 0.0;
+}
+
+bool prefill_fast(const ga_attn_desc* d) {
+  const int grp = d->n_q_heads / d->n_kv_heads;
+  const int hd = d->head_dim;
+  return d->dtype == GA_BF16 && (hd == 64 || hd == 128 || hd == 256) && d->rot_dim % 16 == 0 && grp <= 128;
+}
+
+bool decode_fast(const ga_attn_desc* d) {
+  const int grp = d->n_q_heads / d->n_kv_heads;
+  const int hd = d->head_dim;
+  return d->dtype == GA_BF16 && (hd == 64 || hd == 128 || hd == 256) && d->rot_dim % 16 == 0 &&
+         (grp == 1 || grp == 2 || grp == 4 || grp == 8 || grp == 16);
+}
+
+ga_status check_tensor(const void* p, const char* name, const ga_attn_desc* d, bool required = true) {
+  if (!p) return required ? fail(GA_ERR_NULL_ARG, "%s is NULL", name) : GA_OK;
+  const size_t a = d->dtype == GA_BF16 ? 16 : 4;
+  if (!aligned(p, a)) return fail(GA_ERR_MISALIGNED, "%s is not %zu-byte aligned", name, a);
+  return GA_OK;
+}
+
+ga_status check_gate(const void* gate, const ga_attn_desc* d) {
+  if (d->gate_mode == GA_GATE_NONE) return GA_OK;
+  if (!gate) return fail(GA_ERR_NULL_ARG, "gate is NULL but gate_mode is %d", d->gate_mode);
+  const size_t a = d->gate_mode == GA_GATE_ELEMENTWISE ? (d->dtype == GA_BF16 ? 16 : 4) : (size_t)elem_bytes(d);
+  if (!aligned(gate, a)) return fail(GA_ERR_MISALIGNED, "gate is not %zu-byte aligned", a);
+  return GA_OK;
+}
+
+ga_status hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(GA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+size_t decode_nsplit(int32_t max_len) {
+  size_t ns = ((size_t)(max_len > 0 ? max_len : 0) + kDecodeChunk - 1) / kDecodeChunk;
+  return ns < 1 ? 1 : ns;
+}
+
+ga_status prefill_keys_impl(const ga_attn_desc* desc, int32_t n, const void* k, const void* v,
+                            const float* k_norm_w, const int32_t* positions, void* k_hat, void* v_out,
+                            int32_t kv_cap, hipStream_t stream) {
+  PrepParams pp;
+  memset(&pp, 0, sizeof(pp));
+  pp.src = k;
+  pp.vsrc = v;
+  pp.dst = k_hat;
+  pp.vdst = v_out;
+  pp.src_bstride = (long)n * desc->n_kv_heads * desc->head_dim;
+  pp.vsrc_bstride = pp.src_bstride;
+  pp.dst_bstride = (long)kv_cap * desc->n_kv_heads * desc->head_dim;
+  pp.vdst_bstride = pp.dst_bstride;
+  pp.w = k_norm_w;
+  pp.positions = positions;
+  pp.B = desc->batch;
+  pp.n = n;
+  pp.G = desc->n_kv_heads;
+  pp.d = desc->head_dim;
+  pp.rot = desc->rot_dim;
+  pp.eps = desc->rms_eps;
+  fill_inv_freq(desc, pp.inv_freq);
+  return hip_status(launch_prep_keys(pp, desc->dtype == GA_BF16, stream), "prefill keys launch");
+}
+
+ga_status prefill_attn_impl(const ga_attn_desc* desc, int32_t n, const void* q, const void* k_hat,
+                            int32_t k_cap, const void* v, int32_t v_cap, const void* gate,
+                            const float* q_norm_w, const int32_t* positions, void* out, hipStream_t stream) {
+  const int H = desc->n_q_heads, G = desc->n_kv_heads, d = desc->head_dim;
+  const int grp = H / G;
+  if (prefill_fast(desc)) {
+    PrefillParams pp;
+    memset(&pp, 0, sizeof(pp));
+    pp.q = (const uint16_t*)q;
+    pp.khat = (const uint16_t*)k_hat;
+    pp.v = (const uint16_t*)v;
+    pp.gate = (const uint16_t*)gate;
+    pp.wq = q_norm_w;
+    pp.positions = positions;
+    pp.out = (uint16_t*)out;
+    pp.k_bstride = (long)k_cap * G * d;
+    pp.v_bstride = (long)v_cap * G * d;
+    pp.B = desc->batch;
+    pp.n = n;
+    pp.H = H;
+    pp.G = G;
+    pp.grp = grp;
+    pp.TB = 128 / grp;
+    pp.nblk = (n + pp.TB - 1) / pp.TB;
+    pp.rot = desc->rot_dim;
+    pp.half = desc->rot_dim / 2;
+    pp.use_table = (pp.TB * pp.half <= 1024) ? 1 : 0;
+    pp.eps = desc->rms_eps;
+    pp.scale_log2 = scale_of(desc) * 1.4426950408889634f;
+    fill_inv_freq(desc, pp.inv_freq);
+    if ((long long)pp.B * G * pp.nblk > 0x7fffffffLL) return fail(GA_ERR_UNSUPPORTED, "grid too large");
+    return hip_status(launch_prefill_mfma(pp, d, desc->gate_mode, stream), "prefill attention launch");
+  }
+  NaiveParams np;
+  memset(&np, 0, sizeof(np));
+  np.q = q;
+  np.khat = k_hat;
+  np.v = v;
+  np.gate = gate;
+  np.wq = q_norm_w;
+  np.positions = positions;
+  np.out = out;
+  np.k_bstride = (long)k_cap * G * d;
+  np.v_bstride = (long)v_cap * G * d;
+  np.B = desc->batch;
+  np.n = n;
+  np.H = H;
+  np.G = G;
+  np.d = d;
+  np.rot = desc->rot_dim;
+  np.gate_mode = desc->gate_mode;
+  np.decode = 0;
+  np.eps = desc->rms_eps;
+  np.scale = scale_of(desc);
+  fill_inv_freq(desc, np.inv_freq);
+  return hip_status(launch_naive(np, desc->dtype == GA_BF16, stream), "prefill attention launch");
+}
+
+ga_status check_decode_common(const ga_attn_desc* desc, const void* q, const void* k_cache, const void* v_cache,
+                              int32_t cache_cap, const int32_t* cache_lens, int32_t max_cache_len) {
+  ga_status st;
+  if ((st = check_tensor(q, "q", desc)) != GA_OK) return st;
+  if ((st = check_tensor(k_cache, "k_cache", desc)) != GA_OK) return st;
+  if ((st = check_tensor(v_cache, "v_cache", desc)) != GA_OK) return st;
+  if (!cache_lens) return fail(GA_ERR_NULL_ARG, "cache_lens is NULL");
+  if (max_cache_len < 0) return fail(GA_ERR_BAD_SHAPE, "max_cache_len %d < 0", max_cache_len);
+  if ((long long)cache_cap < (long long)max_cache_len + 1)
+    return fail(GA_ERR_BAD_SHAPE, "cache_cap %d < max_cache_len + 1 (%d)", cache_cap, max_cache_len + 1);
+  return GA_OK;
+}
+
+void fill_decode_params(DecodeParams& dp, const ga_attn_desc* desc, const void* q, const void* k_new,
+                        const void* v_new, const void* gate, const float* q_norm_w, const float* k_norm_w,
+                        const void* k_cache, const void* v_cache, int32_t cache_cap, const int32_t* cache_lens,
+                        int32_t max_cache_len, const void* workspace, const void* out) {
+  memset(&dp, 0, sizeof(dp));
+  const int H = desc->n_q_heads, G = desc->n_kv_heads, d = desc->head_dim;
+  dp.q = (const uint16_t*)q;
+  dp.k_new = (const uint16_t*)k_new;
+  dp.v_new = (const uint16_t*)v_new;
+  dp.gate = (const uint16_t*)gate;
+  dp.wq = q_norm_w;
+  dp.wk = k_norm_w;
+  dp.k_cache = (uint16_t*)k_cache;
+  dp.v_cache = (uint16_t*)v_cache;
+  dp.cache_lens = cache_lens;
+  dp.ws = (float*)workspace;
+  dp.out = (uint16_t*)out;
+  dp.cache_bstride = (long)cache_cap * G * d;
+  dp.B = desc->batch;
+  dp.H = H;
+  dp.G = G;
+  dp.grp = H / G;
+  dp.rot = desc->rot_dim;
+  dp.half = desc->rot_dim / 2;
+  dp.max_len = max_cache_len;
+  dp.nsplit = (int)decode_nsplit(max_cache_len);
+  dp.eps = desc->rms_eps;
+  dp.scale_log2 = scale_of(desc) * 1.4426950408889634f;
+  fill_inv_freq(desc, dp.inv_freq);
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t ga_prefill_workspace_bytes(const ga_attn_desc* desc, int32_t seq_len) {
+  if (check_desc(desc) != GA_OK || seq_len < 0) return 0;
+  const size_t elems = (size_t)desc->batch * seq_len * desc->n_kv_heads * desc->head_dim;
+  return round_up(elems * elem_bytes(desc), 256);
+}
+
+ga_status ga_prefill_keys(const ga_attn_desc* desc, int32_t seq_len, const void* k, const void* v,
+                          const float* k_norm_w, const int32_t* positions, void* k_hat, void* v_out,
+                          int32_t kv_cap, void* stream) {
+  ga_status st;
+  if ((st = check_desc(desc)) != GA_OK) return st;
+  if (seq_len < 0) return fail(GA_ERR_BAD_SHAPE, "seq_len %d < 0", seq_len);
+  if (desc->batch == 0 || seq_len == 0) return ok();
+  if ((st = check_tensor(k, "k", desc)) != GA_OK) return st;
+  if ((st = check_tensor(k_hat, "k_hat", desc)) != GA_OK) return st;
+  if (v_out) {
+    if ((st = check_tensor(v, "v", desc)) != GA_OK) return st;
+    if ((st = check_tensor(v_out, "v_out", desc)) != GA_OK) return st;
+  }
+  if (kv_cap < seq_len) return fail(GA_ERR_BAD_SHAPE, "kv_cap %d < seq_len %d", kv_cap, seq_len);
+  return prefill_keys_impl(desc, seq_len, k, v, k_norm_w, positions, k_hat, v_out, kv_cap, (hipStream_t)stream);
+}
+
+ga_status ga_prefill_attention(const ga_attn_desc* desc, int32_t seq_len, const void* q, const void* k_hat,
+                               int32_t k_cap, const void* v, int32_t v_cap, const void* gate,
+                               const float* q_norm_w, const int32_t* positions, void* out, void* stream) {
+  ga_status st;
+  if ((st = check_desc(desc)) != GA_OK) return st;
+  if (seq_len < 0) return fail(GA_ERR_BAD_SHAPE, "seq_len %d < 0", seq_len);
+  if (desc->batch == 0 || seq_len == 0) return ok();
+  if ((st = check_tensor(q, "q", desc)) != GA_OK) return st;
+  if ((st = check_tensor(k_hat, "k_hat", desc)) != GA_OK) return st;
+  if ((st = check_tensor(v, "v", desc)) != GA_OK) return st;
+  if ((st = check_tensor(out, "out", desc)) != GA_OK) return st;
+  if ((st = check_gate(gate, desc)) != GA_OK) return st;
+  if (k_cap < seq_len || v_cap < seq_len)
+    return fail(GA_ERR_BAD_SHAPE, "k_cap %d / v_cap %d < seq_len %d", k_cap, v_cap, seq_len);
+  return prefill_attn_impl(desc, seq_len, q, k_hat, k_cap, v, v_cap,
+                           desc->gate_mode == GA_GATE_NONE ? nullptr : gate, q_norm_w, positions, out,
+                           (hipStream_t)stream);
+}
+
+ga_status ga_prefill(const ga_attn_desc* desc, int32_t seq_len, const void* q, const void* k, const void* v,
+                     const void* gate, const float* q_norm_w, const float* k_norm_w, const int32_t* positions,
+                     void* k_cache, void* v_cache, int32_t cache_cap, void* workspace, size_t workspace_bytes,
+                     void* out, void* stream) {
+  ga_status st;
+  if ((st = check_desc(desc)) != GA_OK) return st;
+  if (seq_len < 0) return fail(GA_ERR_BAD_SHAPE, "seq_len %d < 0", seq_len);
+  if (desc->batch == 0 || seq_len == 0) return ok();
+  if ((st = check_tensor(q, "q", desc)) != GA_OK) return st;
+  if ((st = check_tensor(k, "k", desc)) != GA_OK) return st;
+  if ((st = check_tensor(v, "v", desc)) != GA_OK) return st;
+  if ((st = check_tensor(out, "out", desc)) != GA_OK) return st;
+  if ((st = check_gate(gate, desc)) != GA_OK) return st;
+  void* khat;
+  int32_t kcap;
+  if (k_cache) {
+    if ((st = check_tensor(k_cache, "k_cache", desc)) != GA_OK) return st;
+    if ((st = check_tensor(v_cache, "v_cache", desc)) != GA_OK) return st;
+    if (cache_cap < seq_len) return fail(GA_ERR_BAD_SHAPE, "cache_cap %d < seq_len %d", cache_cap, seq_len);
+    khat = k_cache;
+    kcap = cache_cap;
+  } else {
+    if (v_cache) return fail(GA_ERR_NULL_ARG, "v_cache given without k_cache");
+    const size_t need = ga_prefill_workspace_bytes(desc, seq_len);
+    if (!workspace || workspace_bytes < need)
+      return fail(GA_ERR_WORKSPACE, "workspace %zu bytes < %zu required", workspace ? workspace_bytes : 0, need);
+    if (!aligned(workspace, 16)) return fail(GA_ERR_MISALIGNED, "workspace is not 16-byte aligned");
+    khat = workspace;
+    kcap = seq_len;
+  }
+  hipStream_t s = (hipStream_t)stream;
+  if ((st = prefill_keys_impl(desc, seq_len, k, v, k_norm_w, positions, khat, v_cache, kcap, s)) != GA_OK) return st;
+  return prefill_attn_impl(desc, seq_len, q, khat, kcap, v, seq_len,
+                           desc->gate_mode == GA_GATE_NONE ? nullptr : gate, q_norm_w, positions, out, s);
+}
+
+int32_t ga_decode_split_keys(void) { return kDecodeChunk; }
+
+size_t ga_decode_workspace_bytes(const ga_attn_desc* desc, int32_t max_cache_len) {
+  if (check_desc(desc) != GA_OK || max_cache_len < 0) return 0;
+  const size_t per = (size_t)desc->batch * desc->n_q_heads * decode_nsplit(max_cache_len);
+  return round_up(per * (desc->head_dim + 2) * sizeof(float), 256);
+}
+
+ga_status ga_decode_partials(const ga_attn_desc* desc, const void* q, const float* q_norm_w, const void* k_cache,
+                             const void* v_cache, int32_t cache_cap, const int32_t* cache_lens,
+                             int32_t max_cache_len, void* workspace, size_t workspace_bytes, void* stream) {
+  ga_status st;
+  if ((st = check_desc(desc)) != GA_OK) return st;
+  if (desc->batch == 0) return ok();
+  if (!decode_fast(desc)) return fail(GA_ERR_UNSUPPORTED, "decode stages need the fused path (bf16, d in {64,128,256}, rot %% 16 == 0, group in {1,2,4,8,16})");
+  if ((st = check_decode_common(desc, q, k_cache, v_cache, cache_cap, cache_lens, max_cache_len)) != GA_OK) return st;
+  const size_t need = ga_decode_workspace_bytes(desc, max_cache_len);
+  if (!workspace || workspace_bytes < need)
+    return fail(GA_ERR_WORKSPACE, "workspace %zu bytes < %zu required", workspace ? workspace_bytes : 0, need);
+  if (!aligned(workspace, 16)) return fail(GA_ERR_MISALIGNED, "workspace is not 16-byte aligned");
+  DecodeParams dp;
+  fill_decode_params(dp, desc, q, nullptr, nullptr, nullptr, q_norm_w, nullptr, k_cache, v_cache, cache_cap,
+                     cache_lens, max_cache_len, workspace, nullptr);
+  return hip_status(launch_decode_partials(dp, desc->head_dim, (hipStream_t)stream), "decode partials launch");
+}
+
+ga_status ga_decode_merge(const ga_attn_desc* desc, const void* q, const void* k_new, const void* v_new,
+                          const void* gate, const float* q_norm_w, const float* k_norm_w, void* k_cache,
+                          void* v_cache, int32_t cache_cap, const int32_t* cache_lens, int32_t max_cache_len,
+                          const void* workspace, size_t workspace_bytes, void* out, void* stream) {
+  ga_status st;
+  if ((st = check_desc(desc)) != GA_OK) return st;
+  if (desc->batch == 0) return ok();
+  if (!decode_fast(desc)) return fail(GA_ERR_UNSUPPORTED, "decode stages need the fused path (bf16, d in {64,128,256}, rot %% 16 == 0, group in {1,2,4,8,16})");
+  if ((st = check_decode_common(desc, q, k_cache, v_cache, cache_cap, cache_lens, max_cache_len)) != GA_OK) return st;
+  if ((st = check_tensor(k_new, "k_new", desc)) != GA_OK) return st;
+  if ((st = check_tensor(v_new, "v_new", desc)) != GA_OK) return st;
+  if ((st = check_tensor(out, "out", desc)) != GA_OK) return st;
+  if ((st = check_gate(gate, desc)) != GA_OK) return st;
+  const size_t need = ga_decode_workspace_bytes(desc, max_cache_len);
+  if (!workspace || workspace_bytes < need)
+    return fail(GA_ERR_WORKSPACE, "workspace %zu bytes < %zu required", workspace ? workspace_bytes : 0, need);
+  if (!aligned(workspace, 16)) return fail(GA_ERR_MISALIGNED, "workspace is not 16-byte aligned");
+  DecodeParams dp;
+  fill_decode_params(dp, desc, q, k_new, v_new, desc->gate_mode == GA_GATE_NONE ? nullptr : gate, q_norm_w,
+                     k_norm_w, k_cache, v_cache, cache_cap, cache_lens, max_cache_len, workspace, out);
+  return hip_status(launch_decode_merge(dp, desc->head_dim, desc->gate_mode, (hipStream_t)stream),
+                    "decode merge launch");
+}
+
+ga_status ga_decode(const ga_attn_desc* desc, const void* q, const void* k_new, const void* v_new, const void* gate,
+                    const float* q_norm_w, const float* k_norm_w, void* k_cache, void* v_cache, int32_t cache_cap,
+                    const int32_t* cache_lens, int32_t max_cache_len, void* workspace, size_t workspace_bytes,
+                    void* out, void* stream) {
+  ga_status st;
+  if ((st = check_desc(desc)) != GA_OK) return st;
+  if (desc->batch == 0) return ok();
+  if ((st = check_decode_common(desc, q, k_cache, v_cache, cache_cap, cache_lens, max_cache_len)) != GA_OK) return st;
+  if ((st = check_tensor(k_new, "k_new", desc)) != GA_OK) return st;
+  if ((st = check_tensor(v_new, "v_new", desc)) != GA_OK) return st;
+  if ((st = check_tensor(out, "out", desc)) != GA_OK) return st;
+  if ((st = check_gate(gate, desc)) != GA_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  if (decode_fast(desc)) {
+    if ((st = ga_decode_partials(desc, q, q_norm_w, k_cache, v_cache, cache_cap, cache_lens, max_cache_len,
+                                 workspace, workspace_bytes, stream)) != GA_OK)
+      return st;
+    return ga_decode_merge(desc, q, k_new, v_new, gate, q_norm_w, k_norm_w, k_cache, v_cache, cache_cap, cache_lens,
+                           max_cache_len, workspace, workspace_bytes, out, stream);
+  }
+  NaiveParams np;
+  memset(&np, 0, sizeof(np));
+  const int G = desc->n_kv_heads, d = desc->head_dim;
+  np.q = q;
+  np.khat = k_cache;
+  np.v = v_cache;
+  np.gate = desc->gate_mode == GA_GATE_NONE ? nullptr : gate;
+  np.wq = q_norm_w;
+  np.wk = k_norm_w;
+  np.cache_lens = cache_lens;
+  np.k_new = k_new;
+  np.v_new = v_new;
+  np.k_cache_out = k_cache;
+  np.v_cache_out = v_cache;
+  np.out = out;
+  np.k_bstride = (long)cache_cap * G * d;
+  np.v_bstride = np.k_bstride;
+  np.B = desc->batch;
+  np.n = 1;
+  np.H = desc->n_q_heads;
+  np.G = G;
+  np.d = d;
+  np.rot = desc->rot_dim;
+  np.gate_mode = desc->gate_mode;
+  np.decode = 1;
+  np.max_len = max_cache_len;
+  np.eps = desc->rms_eps;
+  np.scale = scale_of(desc);
+  fill_inv_freq(desc, np.inv_freq);
+  return hip_status(launch_naive(np, desc->dtype == GA_BF16, s), "decode launch");
+}
+
+const char* ga_status_string(ga_status status) {
+  switch (status) {
+    case GA_OK: return "GA_OK";
+    case GA_ERR_NULL_ARG: return "GA_ERR_NULL_ARG";
+    case GA_ERR_BAD_SHAPE: return "GA_ERR_BAD_SHAPE";
+    case GA_ERR_BAD_DTYPE: return "GA_ERR_BAD_DTYPE";
+    case GA_ERR_UNSUPPORTED: return "GA_ERR_UNSUPPORTED";
+    case GA_ERR_MISALIGNED: return "GA_ERR_MISALIGNED";
+    case GA_ERR_WORKSPACE: return "GA_ERR_WORKSPACE";
+    case GA_ERR_HIP: return "GA_ERR_HIP";
+    default: return "GA_ERR_UNKNOWN";
+  }
+}
+
+const char* ga_last_error(void) { return g_last_error; }
+
+int32_t ga_fast_path(int32_t dtype, int32_t head_dim, int32_t rot_dim, int32_t group) {
+  ga_attn_desc d;
+  memset(&d, 0, sizeof(d));
+  d.dtype = dtype;
+  d.head_dim = head_dim;
+  d.rot_dim = rot_dim;
+  d.n_kv_heads = 1;
+  d.n_q_heads = group > 0 ? group : 1;
+  return (prefill_fast(&d) ? 1 : 0) | (decode_fast(&d) ? 2 : 0);
+}
+
+int32_t ga_version(void) { return 1; }
+
+}  // extern "C"

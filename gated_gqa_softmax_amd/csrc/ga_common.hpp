@@ -1,0 +1,158 @@
+// Device helpers shared by the gfx950 kernels: element conversion, wave
+// reductions, RMSNorm/RoPE arithmetic and the sigmoid gate.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ga {
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;  // MFMA operand
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kNegBig = -1.0e30f;  // finite floor for running maxima
+
+// ---- element conversion ----------------------------------------------------
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t h16) { return __uint_as_float(h16 << 16); }
+__device__ __forceinline__ float lo_bf16(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float hi_bf16(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Round-to-nearest-even pack of two floats into two bf16 (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  bf16x2_t v;
+  v.x = (__bf16)lo;
+  v.y = (__bf16)hi;
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float x) {
+  return (uint16_t)(pack_bf16x2(x, 0.f) & 0xffffu);
+}
+
+// Element access for the two storage types.
+template <typename T> struct Elem;
+template <> struct Elem<float> {
+  typedef float storage;
+  static __device__ __forceinline__ float load(const float* p, long i) { return p[i]; }
+  static __device__ __forceinline__ void store(float* p, long i, float x) { p[i] = x; }
+};
+template <> struct Elem<uint16_t> {  // bf16 bits
+  typedef uint16_t storage;
+  static __device__ __forceinline__ float load(const uint16_t* p, long i) { return bf16_bits_to_f32(p[i]); }
+  static __device__ __forceinline__ void store(uint16_t* p, long i, float x) { p[i] = f32_to_bf16_bits(x); }
+};
+
+// ---- arithmetic ------------------------------------------------------------
+
+// Logistic sigmoid in fp32: 1/(1 + 2^(-z*log2 e)). z = 0 gives exactly 0.5;
+// z >= 100 gives exactly 1; z <= -100 gives 0.
+__device__ __forceinline__ float sigmoid_f32(float z) {
+  return 1.0f / (1.0f + __builtin_amdgcn_exp2f(-z * kLog2e));
+}
+
+// cos/sin of pos * inv_freq: the product and the reduction to [-pi, pi] are
+// done in fp64 so that large positions keep full fp32 accuracy.
+__device__ __forceinline__ void rope_cos_sin(int pos, double inv_freq, float* c, float* s) {
+  const double two_pi = 6.283185307179586476925286766559;
+  double th = (double)pos * inv_freq;
+  double k = rint(th * (1.0 / two_pi));
+  double r = fma(-k, two_pi, th);
+  sincosf((float)r, s, c);
+}
+
+// ---- wave reductions (wave64) -----------------------------------------------
+
+template <int WIDTH>
+__device__ __forceinline__ float sum_xor(float x) {
+#pragma unroll
+  for (int m = WIDTH / 2; m >= 1; m >>= 1) x += __shfl_xor(x, m, 64);
+  return x;
+}
+
+template <int WIDTH>
+__device__ __forceinline__ float max_xor(float x) {
+#pragma unroll
+  for (int m = WIDTH / 2; m >= 1; m >>= 1) x = fmaxf(x, __shfl_xor(x, m, 64));
+  return x;
+}
+
+// Value of lane (l ^ 32) via v_permlane32_swap (gfx950).
+__device__ __forceinline__ float swap_half(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  // r[0]: lanes 0-31 keep x, lanes 32-63 get lanes 0-31's x.
+  // r[1]: lanes 0-31 get lanes 32-63's x, lanes 32-63 keep x.
+  const int upper = (threadIdx.x & 32) != 0;
+  return __uint_as_float(upper ? r[0] : r[1]);
+}
+
+}  // namespace ga
+
+namespace ga {
+
+// RMSNorm + partial RoPE of one row chunk held in registers. Rows occupy
+// aligned groups of LPR = D/8 lanes; lane c of a group holds elements
+// [8c, 8c+8) in x. ``w`` may be null (no norm); ``rot`` = 0 skips RoPE.
+// ``cs_row`` (optional) holds (cos, sin) for pair index t of this row's
+// position; otherwise they are computed from ``inv_freq``.
+template <int D, typename FreqT>
+__device__ __forceinline__ void norm_rope_chunk(float x[8], int c, const float* w, float eps, int rot,
+                                                int pos, const FreqT& inv_freq, const float2* cs_row) {
+  constexpr int LPR = D / 8;
+  float ss = 0.f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) ss += x[j] * x[j];
+  ss = sum_xor<LPR>(ss);
+  if (w) {
+    const float inv = 1.0f / sqrtf(ss / (float)D + eps);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) x[j] = x[j] * inv * w[c * 8 + j];
+  }
+  if (rot > 0) {
+    const int half = rot >> 1;
+    const bool first = c * 8 < half;
+    const bool rotated = c * 8 < rot;
+    const int lane = threadIdx.x & 63;
+    const int src = first ? lane + half / 8 : lane - half / 8;
+    float xp[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) xp[j] = __shfl(x[j], rotated ? src : lane, 64);
+    if (rotated) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int t = (first ? c * 8 : c * 8 - half) + j;
+        float cs, sn;
+        if (cs_row) {
+          const float2 e = cs_row[t];
+          cs = e.x;
+          sn = e.y;
+        } else {
+          rope_cos_sin(pos, inv_freq[t], &cs, &sn);
+        }
+        x[j] = first ? (x[j] * cs - xp[j] * sn) : (x[j] * cs + xp[j] * sn);
+      }
+    }
+  }
+}
+
+__device__ __forceinline__ void unpack8(const u32x4_t raw, float x[8]) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    x[2 * j] = lo_bf16(raw[j]);
+    x[2 * j + 1] = hi_bf16(raw[j]);
+  }
+}
+
+__device__ __forceinline__ u32x4_t pack8(const float x[8]) {
+  u32x4_t r;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) r[j] = pack_bf16x2(x[2 * j], x[2 * j + 1]);
+  return r;
+}
+
+}  // namespace ga

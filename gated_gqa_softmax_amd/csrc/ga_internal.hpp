@@ -1,0 +1,91 @@
+// Kernel parameter blocks and launchers shared between the kernel files and
+// the C ABI layer (ga_api.hip). Host-side declarations only.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ga {
+
+constexpr int kMaxHalfRot = 128;  // rot_dim <= 256
+
+// K-hat = RoPE(RMSNorm(k)) for [B,n,G,d] rows; optional copy of v.
+struct PrepParams {
+  const void* src;     // k rows, [B, *, G, d] with batch stride src_bstride
+  const void* vsrc;    // v rows or null
+  void* dst;           // K-hat rows
+  void* vdst;          // copy of v, or null
+  long src_bstride, vsrc_bstride, dst_bstride, vdst_bstride;  // elements per batch
+  const float* w;      // [d] or null
+  const int* positions;  // [B, n] or null (= token index)
+  int B, n, G, d, rot;
+  float eps;
+  double inv_freq[kMaxHalfRot];
+};
+
+// Fused MFMA prefill (bf16).
+struct PrefillParams {
+  const uint16_t* q;
+  const uint16_t* khat;
+  const uint16_t* v;
+  const uint16_t* gate;
+  const float* wq;
+  const int* positions;
+  uint16_t* out;
+  long k_bstride, v_bstride;
+  int B, n, H, G, grp, TB, nblk, rot, half, use_table;
+  float eps, scale_log2;
+  double inv_freq[kMaxHalfRot];
+};
+
+// Generic (any d <= 256) attention, one wave per query row. Used for fp32 and
+// for shapes without a fused kernel. For decode, rows attend to a cache plus
+// the new token.
+struct NaiveParams {
+  const void* q;        // prefill [B,n,H,d]; decode [B,H,d]
+  const void* khat;     // prepared keys [B, kcap, G, d] (prefill or cache)
+  const void* v;        // values [B, vcap, G, d]
+  const void* gate;
+  const float* wq;
+  const float* wk;      // decode: k_new norm weight
+  const int* positions; // prefill positions or null
+  const int* cache_lens;  // decode only
+  const void* k_new;    // decode only
+  const void* v_new;    // decode only
+  void* k_cache_out;    // decode: slot L written (k_cache base)
+  void* v_cache_out;
+  void* out;
+  long k_bstride, v_bstride;
+  int B, n, H, G, d, rot, gate_mode, decode, max_len;
+  float eps, scale;
+  double inv_freq[kMaxHalfRot];
+};
+
+// Fused decode (bf16): split kernel + merge kernel.
+struct DecodeParams {
+  const uint16_t* q;        // [B,H,D]
+  const uint16_t* k_new;    // [B,G,D]
+  const uint16_t* v_new;
+  const uint16_t* gate;
+  const float* wq;
+  const float* wk;
+  uint16_t* k_cache;        // [B,cap,G,D]
+  uint16_t* v_cache;
+  const int* cache_lens;
+  float* ws;                // partials
+  uint16_t* out;            // [B,H*D]
+  long cache_bstride;       // cap*G*D
+  int B, H, G, grp, rot, half, max_len, nsplit;
+  float eps, scale_log2;
+  double inv_freq[kMaxHalfRot];
+};
+
+constexpr int kDecodeChunk = 512;  // keys per decode split
+
+hipError_t launch_prep_keys(const PrepParams& p, int is_bf16, hipStream_t s);
+hipError_t launch_prefill_mfma(const PrefillParams& p, int D, int gate_mode, hipStream_t s);
+hipError_t launch_naive(const NaiveParams& p, int is_bf16, hipStream_t s);
+hipError_t launch_decode_partials(const DecodeParams& p, int D, hipStream_t s);
+hipError_t launch_decode_merge(const DecodeParams& p, int D, int gate_mode, hipStream_t s);
+
+}  // namespace ga

@@ -80,11 +80,20 @@ WORKLOADS = {
 
 
 def round_bf16(x: np.ndarray) -> np.ndarray:
-    """Round float32 values to the nearest bf16 value (ties to even); float32 out."""
-    x = np.ascontiguousarray(x, dtype=np.float32)
-    u = x.view(np.uint32).astype(np.uint64)
-    u = (u + 0x7FFF + ((u >> 16) & 1)) & 0xFFFF0000
-    return u.astype(np.uint32).view(np.float32).reshape(x.shape)
+    """Round float32 values to the nearest bf16 value (ties to even); float32 out.
+
+    NaN stays NaN; finite values beyond the bf16 range round to infinity.
+    """
+    x = np.array(x, dtype=np.float32, copy=True, order="C")
+    u = x.view(np.uint32)
+    nan = np.isnan(x)
+    lsb = (u >> np.uint32(16)) & np.uint32(1)
+    u += np.uint32(0x7FFF)
+    u += lsb
+    u &= np.uint32(0xFFFF0000)
+    if nan.any():
+        x[nan] = np.float32("nan")
+    return x
 
 
 def _store(x: np.ndarray, dtype: str) -> np.ndarray:
@@ -148,15 +157,14 @@ def decode_cache_rows(w: Workload, b: int, length: int) -> tuple:
     return _store(kh, w.dtype), _store(vv, w.dtype)
 
 
-def fill_decode_cache(w: Workload, cache_lens: np.ndarray, capacity: int,
-                      k_out: np.ndarray, v_out: np.ndarray) -> None:
-    """Write every sequence's rows into caller arrays of shape [B,capacity,G,d].
+def for_each_cache_rows(w: Workload, cache_lens, fn, threads: int = 8) -> None:
+    """Call ``fn(b, k_hat_rows, v_rows)`` for every sequence, drawing the
+    sequences' streams on a thread pool (the draws are independent)."""
+    from concurrent.futures import ThreadPoolExecutor
 
-    Slots at and beyond a sequence's length are left as the caller set them.
-    """
-    assert k_out.shape == (w.batch, capacity, w.n_kv_heads, w.head_dim)
-    for b in range(w.batch):
-        L = int(cache_lens[b])
-        kh, vv = decode_cache_rows(w, b, L)
-        k_out[b, :L] = kh
-        v_out[b, :L] = vv
+    def job(b):
+        return b, decode_cache_rows(w, b, int(cache_lens[b]))
+
+    with ThreadPoolExecutor(max_workers=max(1, threads)) as ex:
+        for b, (kh, vv) in ex.map(job, range(w.batch)):
+            fn(b, kh, vv)

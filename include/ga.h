@@ -1,0 +1,192 @@
+/*
+ * ga.h -- C ABI of the gated grouped-query causal attention library (gfx950).
+ *
+ * The library computes the forward pass of one full-attention layer of a
+ * Qwen3.5 / Qwen3-Next style model, from already-projected q, k, v and gate
+ * logits to the gated concat of the head outputs (the input of W_O):
+ *
+ *   q_hat = RoPE(RMSNorm(q[b,i,h], w_q), pos[b,i])
+ *   k_hat = RoPE(RMSNorm(k[b,j,g], w_k), pos[b,j])        g = floor(h / (H/G))
+ *   y     = softmax_j<=i(q_hat . k_hat_j * scale) V          scale = 1/sqrt(d)
+ *   out[b,i,h*d + e] = y_e * sigmoid(z)                     (elementwise z[b,i,h,e],
+ *                                                            headwise z[b,i,h], or none)
+ *
+ * Sources (page title, section): "Transformer by Hand · 6. Gated attention",
+ * "The formula" (causal softmax(QK^T/sqrt(d)) V), "Four things Qwen3.5 adds to
+ * the textbook" (GQA, QK-Norm before RoPE, RoPE on the first quarter of the
+ * head, output gate) and "The code: qwen/attention.py" (order of operations
+ * and shapes); "Gated Attention：算完注意力，再决定用多少", "门放在哪里？"
+ * (gate after SDPA and before W_O; headwise vs elementwise); "多头注意力与 GQA",
+ * "分组查询注意力（GQA）" (head h reads KV head floor(h/group)) and
+ * "标准多头注意力（MHA）" (decode reads every cached K and V; Q is not cached).
+ *
+ * Readings of points the pages leave open: RMSNorm is x/sqrt(mean(x^2)+eps)*w
+ * with w the effective weight; RoPE rotates pairs (t, t + rot/2) inside the
+ * first rot dims by pos * base^(-2t/rot); the causal mask is by token index
+ * inside a call; a decode token attends to the cache and to itself.
+ *
+ * Conventions for every entry point:
+ *  - Pointers named as tensors are DEVICE pointers; ``desc`` is a host pointer
+ *    read during the call only. ``stream`` is a hipStream_t (NULL = the null
+ *    stream). All launches are asynchronous on ``stream``.
+ *  - The caller owns every buffer. The library writes only ``out``, the
+ *    cache slots named below and the workspace. It keeps no state between
+ *    calls; calls on different streams with disjoint outputs may overlap.
+ *  - Layouts are dense, row-major, innermost index last:
+ *      q [B,n,H,d]  k,v [B,n,G,d]  gate [B,n,H,d] | [B,n,H]  out [B,n,H*d]
+ *      caches [B,cap,G,d]  norm weights [d] float32  positions [B,n] int32
+ *    Element type of q, k, v, gate, out and caches is ``desc->dtype``.
+ *    bf16 tensors must be 16-byte aligned.
+ *  - Errors: shapes, pointers, alignment, capacities and workspace size are
+ *    checked on the host before anything is launched; a failed check returns
+ *    its status and launches nothing. ``ga_last_error()`` gives a message for
+ *    the last failure on the calling thread. Data values are not checked:
+ *    NaN and Inf propagate through the arithmetic.
+ *  - Empty inputs (batch == 0, or seq_len == 0 for prefill) are a no-op
+ *    returning GA_OK.
+ */
+#ifndef GA_H
+#define GA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  GA_OK = 0,
+  GA_ERR_NULL_ARG = 1,     /* a required pointer is NULL */
+  GA_ERR_BAD_SHAPE = 2,    /* a size is negative or inconsistent (e.g. H % G != 0) */
+  GA_ERR_BAD_DTYPE = 3,    /* dtype or gate mode out of range */
+  GA_ERR_UNSUPPORTED = 4,  /* valid but not implemented (e.g. head_dim > 256) */
+  GA_ERR_MISALIGNED = 5,   /* a bf16 tensor is not 16-byte aligned */
+  GA_ERR_WORKSPACE = 6,    /* workspace missing or smaller than required */
+  GA_ERR_HIP = 7           /* the HIP runtime reported an error at launch */
+} ga_status;
+
+typedef enum { GA_BF16 = 0, GA_F32 = 1 } ga_dtype;
+typedef enum { GA_GATE_NONE = 0, GA_GATE_HEADWISE = 1, GA_GATE_ELEMENTWISE = 2 } ga_gate_mode;
+
+typedef struct {
+  int32_t batch;        /* B >= 0 */
+  int32_t n_q_heads;    /* H >= 1, a multiple of n_kv_heads */
+  int32_t n_kv_heads;   /* G >= 1 */
+  int32_t head_dim;     /* d, 1..256 */
+  int32_t rot_dim;      /* RoPE dims, even, 0..d; 0 = no RoPE (configs: d/4) */
+  float rope_base;      /* > 0 when rot_dim > 0 (configs: 10000) */
+  float rms_eps;        /* >= 0 (configs: 1e-6) */
+  float softmax_scale;  /* 0 = 1/sqrt(head_dim); else used as given (> 0) */
+  int32_t dtype;        /* ga_dtype: element type of q/k/v/gate/out/caches */
+  int32_t gate_mode;    /* ga_gate_mode */
+} ga_attn_desc;
+
+/* ---- prefill ------------------------------------------------------------ */
+
+/* Workspace ga_prefill needs when it is given no KV cache: room for K-hat
+ * (B*n*G*d elements, rounded up to 256 bytes). */
+size_t ga_prefill_workspace_bytes(const ga_attn_desc* desc, int32_t seq_len);
+
+/* Whole prefill: ga_prefill_keys, then ga_prefill_attention.
+ *  q, k, v       [B,n,H,d] / [B,n,G,d] / [B,n,G,d], raw projections.
+ *  gate          [B,n,H,d] (elementwise) | [B,n,H] (headwise) | NULL (none).
+ *  q_norm_w, k_norm_w  [d] float32 effective RMSNorm weights; NULL = no norm.
+ *  positions     [B,n] int32 RoPE positions; NULL = token index 0..n-1.
+ *  k_cache, v_cache  optional [B,cache_cap,G,d]: when k_cache is given, K-hat
+ *                (normed, rotated, rounded to dtype) is written to slots
+ *                [0,n) of k_cache and v to the same slots of v_cache (both
+ *                required, cache_cap >= n); the attention then reads K-hat
+ *                from the cache and the workspace may be NULL. Without a
+ *                cache, K-hat goes to ``workspace``.
+ *  out           [B,n,H*d]. */
+ga_status ga_prefill(const ga_attn_desc* desc, int32_t seq_len,
+                     const void* q, const void* k, const void* v, const void* gate,
+                     const float* q_norm_w, const float* k_norm_w, const int32_t* positions,
+                     void* k_cache, void* v_cache, int32_t cache_cap,
+                     void* workspace, size_t workspace_bytes,
+                     void* out, void* stream);
+
+/* First stage of ga_prefill (one kernel): k_hat[b,i,g,:] = RoPE(RMSNorm(k))
+ * for i < seq_len into k_hat [B,kv_cap,G,d]; when v_out is not NULL, also
+ * copies v into v_out [B,kv_cap,G,d]. kv_cap >= seq_len. */
+ga_status ga_prefill_keys(const ga_attn_desc* desc, int32_t seq_len,
+                          const void* k, const void* v, const float* k_norm_w,
+                          const int32_t* positions, void* k_hat, void* v_out, int32_t kv_cap,
+                          void* stream);
+
+/* Second stage of ga_prefill (one kernel): causal attention of the normed,
+ * rotated q against prepared keys, with the gate fused into the epilogue.
+ *  k_hat  [B,k_cap,G,d] as written by ga_prefill_keys (k_cap >= seq_len).
+ *  v      [B,v_cap,G,d] (v_cap >= seq_len; the raw v input has v_cap = n). */
+ga_status ga_prefill_attention(const ga_attn_desc* desc, int32_t seq_len,
+                               const void* q, const void* k_hat, int32_t k_cap,
+                               const void* v, int32_t v_cap, const void* gate,
+                               const float* q_norm_w, const int32_t* positions,
+                               void* out, void* stream);
+
+/* ---- decode ------------------------------------------------------------- */
+
+/* Key-chunk length of one decode split (keys per partial result). */
+int32_t ga_decode_split_keys(void);
+
+/* Workspace ga_decode needs for caches holding up to max_cache_len tokens:
+ * B*H*ceil(max_cache_len/split_keys) partial results of (d + 2) floats. */
+size_t ga_decode_workspace_bytes(const ga_attn_desc* desc, int32_t max_cache_len);
+
+/* One decode step for B sequences, each with one new token at position
+ * L_b = cache_lens[b]:
+ *  q [B,H,d], k_new, v_new [B,G,d]: raw projections of the new token.
+ *  gate [B,H,d] | [B,H] | NULL.
+ *  k_cache, v_cache [B,cache_cap,G,d]: slots [0,L_b) hold K-hat (already
+ *      normed and rotated) and V; they are read as stored. The call writes
+ *      the new token's K-hat and V to slot L_b; the caller advances
+ *      cache_lens afterwards. The new token attends to the L_b cached keys
+ *      and to itself.
+ *  cache_lens [B] int32 device array; max_cache_len is a host upper bound of
+ *      its values (cache_cap >= max_cache_len + 1). A sequence whose length
+ *      is outside [0, max_cache_len] gets NaN outputs and no cache write.
+ *  out [B,H*d]. Two kernels: ga_decode_partials then ga_decode_merge. */
+ga_status ga_decode(const ga_attn_desc* desc,
+                    const void* q, const void* k_new, const void* v_new, const void* gate,
+                    const float* q_norm_w, const float* k_norm_w,
+                    void* k_cache, void* v_cache, int32_t cache_cap,
+                    const int32_t* cache_lens, int32_t max_cache_len,
+                    void* workspace, size_t workspace_bytes,
+                    void* out, void* stream);
+
+/* First stage of ga_decode (one kernel): for every sequence, KV head and key
+ * chunk of the cache, the partial softmax state (row max, row sum, unnormed
+ * weighted V) of the group's query heads, into the workspace. Reads only
+ * slots [0, L_b). */
+ga_status ga_decode_partials(const ga_attn_desc* desc, const void* q, const float* q_norm_w,
+                             const void* k_cache, const void* v_cache, int32_t cache_cap,
+                             const int32_t* cache_lens, int32_t max_cache_len,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+/* Second stage of ga_decode (one kernel): adds the new token's own key and
+ * value, merges the partials, applies the gate, writes out and appends the
+ * new K-hat and V at slot L_b. */
+ga_status ga_decode_merge(const ga_attn_desc* desc, const void* q, const void* k_new,
+                          const void* v_new, const void* gate, const float* q_norm_w,
+                          const float* k_norm_w, void* k_cache, void* v_cache, int32_t cache_cap,
+                          const int32_t* cache_lens, int32_t max_cache_len,
+                          const void* workspace, size_t workspace_bytes, void* out, void* stream);
+
+/* ---- misc --------------------------------------------------------------- */
+
+const char* ga_status_string(ga_status status);
+/* Message for the last failed call on the calling thread ("" if none). */
+const char* ga_last_error(void);
+/* Which fused kernels serve (dtype, head_dim, rot_dim, group = H/G): bit 0 =
+ * the MFMA prefill (bf16, d in {64,128,256}, rot % 16 == 0, group <= 128),
+ * bit 1 = the split-K decode (same, group in {1,2,4,8,16}). Shapes without a
+ * fused kernel run on the generic one-wave-per-row kernel (any d <= 256,
+ * fp32 or bf16); ga_decode_partials/ga_decode_merge need bit 1. */
+int32_t ga_fast_path(int32_t dtype, int32_t head_dim, int32_t rot_dim, int32_t group);
+int32_t ga_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* GA_H */

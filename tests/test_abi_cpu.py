@@ -1,0 +1,129 @@
+"""Host-side checks of the C ABI: the library loads, exports every entry point
+include/ga.h declares, and rejects bad arguments before any GPU work (these
+calls never reach a kernel launch, so they run without a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from gated_gqa_softmax_amd import _lib
+from gated_gqa_softmax_amd._lib import AttnDesc
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _lib_or_build():
+    if not os.path.exists(_lib.LIB_PATH):
+        from gated_gqa_softmax_amd.build import build_library
+        build_library()
+    return _lib.load()
+
+
+def _declared():
+    names = set()
+    for fn in os.listdir(os.path.join(ROOT, "include")):
+        if fn.endswith(".h"):
+            src = open(os.path.join(ROOT, "include", fn)).read()
+            src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+            names |= set(re.findall(r"\b(ga_[a-z_0-9]+)\s*\(", src))
+    return names
+
+
+def test_library_exports_every_declared_entry_point():
+    lib = _lib_or_build()
+    declared = _declared()
+    assert declared == set(_lib.SIGNATURES), declared ^ set(_lib.SIGNATURES)
+    for name in declared:
+        assert getattr(lib, name) is not None
+    assert lib.ga_version() >= 1
+
+
+def _desc(**kw):
+    base = dict(batch=1, n_q_heads=8, n_kv_heads=2, head_dim=256, rot_dim=64, rope_base=10000.0,
+                rms_eps=1e-6, softmax_scale=0.0, dtype=_lib.GA_BF16, gate_mode=_lib.GA_GATE_ELEMENTWISE)
+    base.update(kw)
+    return AttnDesc(**base)
+
+
+def test_host_queries():
+    lib = _lib_or_build()
+    d = _desc()
+    assert lib.ga_prefill_workspace_bytes(ctypes.byref(d), 4096) == 4096 * 2 * 256 * 2
+    ck = lib.ga_decode_split_keys()
+    assert ck > 0
+    d5 = _desc(batch=64)
+    ns = -(-32768 // ck)
+    want = 64 * 8 * ns * (256 + 2) * 4
+    assert lib.ga_decode_workspace_bytes(ctypes.byref(d5), 32768) == (want + 255) // 256 * 256
+    assert lib.ga_fast_path(_lib.GA_BF16, 256, 64, 4) == 3
+    assert lib.ga_fast_path(_lib.GA_BF16, 128, 32, 8) == 3
+    assert lib.ga_fast_path(_lib.GA_BF16, 128, 32, 3) == 1       # decode: generic kernel
+    assert lib.ga_fast_path(_lib.GA_F32, 8, 2, 2) == 0
+    assert lib.ga_fast_path(_lib.GA_BF16, 96, 16, 2) == 0
+    assert lib.ga_status_string(_lib.GA_ERR_WORKSPACE) == b"GA_ERR_WORKSPACE"
+
+
+A16 = 1 << 20          # fake, 16-byte aligned "device" addresses: never dereferenced
+MIS = A16 + 2
+
+
+def _prefill(lib, d, n=16, q=A16, k=A16, v=A16, gate=A16, out=A16, ws=A16, ws_bytes=1 << 30,
+             k_cache=None, v_cache=None, cap=0):
+    return lib.ga_prefill(ctypes.byref(d) if d is not None else None, n, q, k, v, gate, None, None, None,
+                          k_cache, v_cache, cap, ws, ws_bytes, out, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(n_q_heads=8, n_kv_heads=3), _lib.GA_ERR_BAD_SHAPE),
+    (dict(head_dim=300), _lib.GA_ERR_UNSUPPORTED),
+    (dict(head_dim=0), _lib.GA_ERR_BAD_SHAPE),
+    (dict(rot_dim=3), _lib.GA_ERR_BAD_SHAPE),
+    (dict(rot_dim=258), _lib.GA_ERR_BAD_SHAPE),
+    (dict(rope_base=0.0), _lib.GA_ERR_BAD_SHAPE),
+    (dict(rms_eps=-1.0), _lib.GA_ERR_BAD_SHAPE),
+    (dict(softmax_scale=float("nan")), _lib.GA_ERR_BAD_SHAPE),
+    (dict(dtype=7), _lib.GA_ERR_BAD_DTYPE),
+    (dict(gate_mode=5), _lib.GA_ERR_BAD_DTYPE),
+    (dict(batch=-1), _lib.GA_ERR_BAD_SHAPE),
+])
+def test_prefill_rejects_bad_descriptors(kw, status):
+    lib = _lib_or_build()
+    assert _prefill(lib, _desc(**kw)) == status
+    assert lib.ga_last_error() != b""
+
+
+def test_prefill_rejects_bad_pointers_and_workspace():
+    lib = _lib_or_build()
+    d = _desc()
+    assert _prefill(lib, None) == _lib.GA_ERR_NULL_ARG
+    assert _prefill(lib, d, q=None) == _lib.GA_ERR_NULL_ARG
+    assert _prefill(lib, d, gate=None) == _lib.GA_ERR_NULL_ARG
+    assert _prefill(lib, d, out=MIS) == _lib.GA_ERR_MISALIGNED
+    assert _prefill(lib, d, k=MIS) == _lib.GA_ERR_MISALIGNED
+    assert _prefill(lib, d, ws=None) == _lib.GA_ERR_WORKSPACE
+    assert _prefill(lib, d, ws_bytes=10) == _lib.GA_ERR_WORKSPACE
+    assert _prefill(lib, d, k_cache=A16, v_cache=A16, cap=8) == _lib.GA_ERR_BAD_SHAPE   # cap < n
+    assert _prefill(lib, d, k_cache=A16, v_cache=None, cap=16) == _lib.GA_ERR_NULL_ARG
+    assert _prefill(lib, d, n=-1) == _lib.GA_ERR_BAD_SHAPE
+    # empty inputs are a no-op
+    assert _prefill(lib, d, n=0, q=None) == _lib.GA_OK
+    assert _prefill(lib, _desc(batch=0), q=None) == _lib.GA_OK
+
+
+def test_decode_rejects_bad_arguments():
+    lib = _lib_or_build()
+    d = _desc(batch=4)
+
+    def call(desc=d, cap=101, max_len=100, lens=A16, ws=A16, ws_bytes=1 << 30, q=A16, out=A16):
+        return lib.ga_decode(ctypes.byref(desc), q, A16, A16, A16, None, None, A16, A16, cap, lens, max_len,
+                             ws, ws_bytes, out, None)
+
+    assert call(cap=100) == _lib.GA_ERR_BAD_SHAPE            # no room for the appended slot
+    assert call(max_len=-1) == _lib.GA_ERR_BAD_SHAPE
+    assert call(lens=None) == _lib.GA_ERR_NULL_ARG
+    assert call(ws_bytes=16) == _lib.GA_ERR_WORKSPACE
+    assert call(q=MIS) == _lib.GA_ERR_MISALIGNED
+    assert call(desc=_desc(batch=0), q=None) == _lib.GA_OK
+    assert lib.ga_decode_partials(ctypes.byref(_desc(head_dim=96, rot_dim=16)), A16, None, A16, A16, 101, A16,
+                                  100, A16, 1 << 30, None) == _lib.GA_ERR_UNSUPPORTED
