@@ -82,6 +82,12 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
             raise LibraryNotBuilt(
                 f"{path} not found: build it with `python -m gated_gqa_softmax_amd.build` "
                 "(the package has no non-HIP implementation)")
+        # The library links libamdhip64; when the process also uses PyTorch,
+        # let torch load its HIP runtime first so that one runtime serves both.
+        try:
+            import torch  # noqa: F401
+        except ImportError:
+            pass
         lib = ctypes.CDLL(path)
         for name, (res, args) in SIGNATURES.items():
             fn = getattr(lib, name)

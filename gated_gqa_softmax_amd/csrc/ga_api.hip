@@ -65,6 +65,17 @@ void fill_inv_freq(const ga_attn_desc* d, double* inv_freq) {
     inv_freq[t] = (t < half) ? pow((double)d->rope_base, -2.0 * t / (double)d->rot_dim) : 0.0;
 }
 
+// Second fused prefill design (mirrored blocks, two key phases, direct-to-LDS
+// loads): d in {128, 256}, rot % 16 == 0, group <= 64, and every K/V byte
+// offset of one (batch, KV head) within a 31-bit buffer range.
+bool prefill_v2_ok(const ga_attn_desc* d, int32_t k_cap, int32_t v_cap) {
+  const int grp = d->n_q_heads / d->n_kv_heads;
+  const int hd = d->head_dim;
+  const long long row = 2LL * d->n_kv_heads * hd;
+  return d->dtype == GA_BF16 && (hd == 128 || hd == 256) && d->rot_dim % 16 == 0 && grp <= 64 &&
+         row * k_cap < (1LL << 31) && row * v_cap < (1LL << 31);
+}
+
 bool prefill_fast(const ga_attn_desc* d) {
   const int grp = d->n_q_heads / d->n_kv_heads;
   const int hd = d->head_dim;
@@ -133,7 +144,8 @@ ga_status prefill_attn_impl(const ga_attn_desc* desc, int32_t n, const void* q, 
                             const float* q_norm_w, const int32_t* positions, void* out, hipStream_t stream) {
   const int H = desc->n_q_heads, G = desc->n_kv_heads, d = desc->head_dim;
   const int grp = H / G;
-  if (prefill_fast(desc)) {
+  const bool v2 = prefill_v2_ok(desc, k_cap, v_cap);
+  if (v2 || prefill_fast(desc)) {
     PrefillParams pp;
     memset(&pp, 0, sizeof(pp));
     pp.q = (const uint16_t*)q;
@@ -150,15 +162,16 @@ ga_status prefill_attn_impl(const ga_attn_desc* desc, int32_t n, const void* q, 
     pp.H = H;
     pp.G = G;
     pp.grp = grp;
-    pp.TB = 128 / grp;
+    pp.TB = (v2 ? 64 : 128) / grp;  // tokens per block: 128 rows (v1) or 64 rows (v2) per block
     pp.nblk = (n + pp.TB - 1) / pp.TB;
     pp.rot = desc->rot_dim;
     pp.half = desc->rot_dim / 2;
-    pp.use_table = (pp.TB * pp.half <= 1024) ? 1 : 0;
+    pp.use_table = ((v2 ? 2 : 1) * pp.TB * pp.half <= 1024) ? 1 : 0;
     pp.eps = desc->rms_eps;
     pp.scale_log2 = scale_of(desc) * 1.4426950408889634f;
     fill_inv_freq(desc, pp.inv_freq);
     if ((long long)pp.B * G * pp.nblk > 0x7fffffffLL) return fail(GA_ERR_UNSUPPORTED, "grid too large");
+    if (v2) return hip_status(launch_prefill_v2(pp, d, desc->gate_mode, stream), "prefill attention launch");
     return hip_status(launch_prefill_mfma(pp, d, desc->gate_mode, stream), "prefill attention launch");
   }
   NaiveParams np;

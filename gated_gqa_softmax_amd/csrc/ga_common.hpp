@@ -66,6 +66,13 @@ __device__ __forceinline__ void rope_cos_sin(int pos, double inv_freq, float* c,
   sincosf((float)r, s, c);
 }
 
+// Out-of-line copy for paths that evaluate it per element (keeps kernels small).
+__device__ __noinline__ float2 rope_cos_sin_call(int pos, double inv_freq) {
+  float c, s;
+  rope_cos_sin(pos, inv_freq, &c, &s);
+  return make_float2(c, s);
+}
+
 // ---- wave reductions (wave64) -----------------------------------------------
 
 template <int WIDTH>
@@ -132,7 +139,9 @@ __device__ __forceinline__ void norm_rope_chunk(float x[8], int c, const float* 
           cs = e.x;
           sn = e.y;
         } else {
-          rope_cos_sin(pos, inv_freq[t], &cs, &sn);
+          const float2 e = rope_cos_sin_call(pos, inv_freq[t]);
+          cs = e.x;
+          sn = e.y;
         }
         x[j] = first ? (x[j] * cs - xp[j] * sn) : (x[j] * cs + xp[j] * sn);
       }

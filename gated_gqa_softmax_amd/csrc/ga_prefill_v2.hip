@@ -1,0 +1,389 @@
+// Fused flash-style prefill for gfx950, second design: balanced causal work,
+// two waves per SIMD, K/V streamed into LDS by direct-to-LDS loads.
+//
+// Definition (same as the first design): causal softmax(q_hat k_hat^T * scale) V
+// per query head, q_hat = RoPE(RMSNorm(q)), sigmoid output gate; sources:
+// "Transformer by Hand · 6. Gated attention" ("The formula", "Four things
+// Qwen3.5 adds to the textbook"), "Gated Attention：算完注意力，再决定用多少"
+// ("门放在哪里？"), "Attention, worked all the way through" ("Why scaling and
+// stable softmax matter", used here in its running-max form).
+//
+// Layout of the work:
+//  * A workgroup has 8 waves and 128 query rows in 4 row groups of 32. Rows
+//    are (query head of the GQA group, token) pairs, so each K/V tile in LDS
+//    serves every head of the group.
+//  * Row groups 0-1 come from token block p and row groups 2-3 from block
+//    nblk-1-p: the causal work of a light block and its mirror adds up to the
+//    same amount for every workgroup.
+//  * Each row group has two waves ("phases"); a stage holds 64 keys and phase
+//    f takes keys [32f, 32f+32) of it, so a row group's key range is split
+//    between two waves that are merged in LDS at the end. Waves are ordered
+//    so that every SIMD runs one light-block wave and one heavy-block wave.
+//  * S^T = K Q^T and O^T += V^T P^T use v_mfma_f32_32x32x16_bf16; the P
+//    fragments come straight from the S^T accumulators; V^T fragments come
+//    from row-major V in LDS through ds_read_b64_tr_b16 (16-bit transpose
+//    read), so V needs no transposition on its way in.
+//  * K and V tiles go from HBM/L2 to LDS with global_load_lds_dwordx4 (no
+//    register staging), XOR-swizzled per row so the MFMA operand reads are
+//    free of bank conflicts; stages are double (d = 256) or triple (d = 128)
+//    buffered.
+#include "ga_common.hpp"
+#include "ga_internal.hpp"
+
+namespace ga {
+
+typedef __attribute__((__vector_size__(4 * sizeof(short)))) short i16x4_t;
+typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
+
+template <int D>
+struct V2Shape {
+  static constexpr int ST = 64;                      // keys per stage
+  static constexpr int CPR = D / 8;                  // 16-byte chunks per row
+  static constexpr int ROW_BYTES = D * 2;
+  static constexpr int TILE_BYTES = ST * ROW_BYTES;  // K (or V) of one stage
+  static constexpr int STAGE_BYTES = 2 * TILE_BYTES;
+  static constexpr int NSTAGE = (D == 256) ? 2 : 3;
+  static constexpr int BUF_BYTES = NSTAGE * STAGE_BYTES;
+  static constexpr int QS_BYTES = 128 * ROW_BYTES;
+  static constexpr int LOADS_PER_TILE = TILE_BYTES / 1024;  // 1 KB per wave instruction
+  static constexpr int LOADS_PER_WAVE = LOADS_PER_TILE / 8;
+  static constexpr int ROWS_PER_LOAD = 1024 / ROW_BYTES;
+  static constexpr int XCHG_BYTES = 4 * (D / 32) * 16 * 64 * 4;  // phase-1 O of 4 row groups
+  static_assert(CPR >= 16, "swizzles need at least 16 chunks per row");
+  static_assert(QS_BYTES <= STAGE_BYTES, "Q staging must fit one stage");
+  static_assert(XCHG_BYTES <= BUF_BYTES, "merge buffer must fit the stages");
+  static_assert(LOADS_PER_WAVE >= 1, "tile too small");
+};
+
+__device__ __forceinline__ int swz_k(int row) { return row & 15; }
+__device__ __forceinline__ int swz_v(int row) { return (row & 3) << 2; }
+
+// Issue the direct-to-LDS loads of one stage (64 keys of K-hat and V) for this
+// wave: 1 KB of LDS per instruction, lane l's 16 bytes at slot l. The whole
+// byte offset goes in the VGPR operand so the buffer range check sees it.
+template <int D>
+__device__ __forceinline__ void v2_issue_stage(unsigned char* smem, __amdgpu_buffer_rsrc_t krs,
+                                               __amdgpu_buffer_rsrc_t vrs, const int* koff, const int* voff,
+                                               int w, int st, int kv_row_bytes) {
+  typedef V2Shape<D> S;
+  unsigned char* kt = smem + (st % S::NSTAGE) * S::STAGE_BYTES;
+  unsigned char* vt = kt + S::TILE_BYTES;
+  const int soff = st * S::ST * kv_row_bytes;
+#pragma unroll
+  for (int j = 0; j < S::LOADS_PER_WAVE; ++j) {
+    const int t = w + 8 * j;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (__attribute__((address_space(3))) void*)(kt + t * 1024), 16,
+                                             koff[j] + soff, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (__attribute__((address_space(3))) void*)(vt + t * 1024), 16,
+                                             voff[j] + soff, 0, 0, 0);
+  }
+}
+
+template <int D, int GATE>
+__global__ __launch_bounds__(512) void prefill_v2_kernel(const PrefillParams p) {
+  typedef V2Shape<D> S;
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[S::BUF_BYTES];
+  __shared__ float2 table[1024];
+  __shared__ float ml_x[4][64][2];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  const int l32 = lane & 31;
+  const int hi = lane >> 5;
+  // wave -> (row group, phase): each SIMD (w % 4) gets one light and one heavy wave
+  const int rg = (w < 4) ? w : ((w + 2) & 3);
+  const int phase = (w < 4) ? 0 : 1;
+
+  const int nBG = p.B * p.G;
+  const int u = blockIdx.x;
+  const int pair = u / nBG;
+  const int bg = u % nBG;
+  const int b = bg / p.G;
+  const int g = bg % p.G;
+  const int TB = p.TB;
+  const int n = p.n;
+  const int blk_heavy = p.nblk - 1 - pair;
+  const int blk_light = (pair < blk_heavy) ? pair : -1;   // -1: no light block (odd middle)
+  const int kend = min(n, blk_heavy * TB + TB);
+  const int nst = (kend + S::ST - 1) / S::ST;
+
+  // this lane's query row
+  const int my_blk = (rg < 2) ? blk_light : blk_heavy;
+  const int my_local = (rg & 1) * 32 + l32;
+  const int my_hh = my_local / TB;
+  const int my_tt = my_local - my_hh * TB;
+  const int my_tok0 = my_blk * TB + my_tt;
+  const bool my_valid = (my_blk >= 0) && (my_hh < p.grp) && (my_tok0 < n);
+  const int my_tok = my_valid ? my_tok0 : 0x3fffffff;
+  const int my_h = g * p.grp + my_hh;
+  int wave_max_tok = my_valid ? my_tok : -1;
+  int wave_min_tok = my_tok;
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) {
+    wave_max_tok = max(wave_max_tok, __shfl_xor(wave_max_tok, m, 64));
+    wave_min_tok = min(wave_min_tok, __shfl_xor(wave_min_tok, m, 64));
+  }
+
+  // ---- direct-to-LDS stage loads --------------------------------------------
+  // Buffer resources cover keys [0, n) of this (b, g): rows past the end read
+  // as zeros (out-of-range buffer loads return 0), which the mask then hides.
+  const int kv_row_bytes = p.G * D * 2;
+  const uint32_t valid_bytes = (uint32_t)((n - 1) * kv_row_bytes + D * 2);
+  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(p.khat + (long)b * p.k_bstride + (long)g * D), (short)0, (int)valid_bytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(p.v + (long)b * p.v_bstride + (long)g * D), (short)0, (int)valid_bytes, 0x00020000);
+  int koff[S::LOADS_PER_WAVE], voff[S::LOADS_PER_WAVE];
+#pragma unroll
+  for (int j = 0; j < S::LOADS_PER_WAVE; ++j) {
+    const int row = (w + 8 * j) * S::ROWS_PER_LOAD + lane / S::CPR;
+    const int ph = lane % S::CPR;
+    koff[j] = row * kv_row_bytes + ((ph ^ swz_k(row)) << 4);
+    voff[j] = row * kv_row_bytes + ((ph ^ swz_v(row)) << 4);
+  }
+  for (int s = 0; s < S::NSTAGE - 1; ++s)
+    if (s < nst) v2_issue_stage<D>(smem, krs, vrs, koff, voff, w, s, kv_row_bytes);
+
+  // ---- Q prologue: RMSNorm + RoPE of 128 rows into LDS (stage NSTAGE-1) ------
+  uint16_t* Qs = (uint16_t*)(smem + (S::NSTAGE - 1) * S::STAGE_BYTES);
+  const int half = p.half;
+  if (p.use_table) {
+    for (int e = tid; e < 2 * TB * half; e += 512) {
+      const int side = e / (TB * half);
+      const int rem = e - side * TB * half;
+      const int tt = rem / half;
+      const int t = rem - tt * half;
+      const int blk = side ? blk_heavy : blk_light;
+      const int tok = blk * TB + tt;
+      const int pos = (blk >= 0 && tok < n) ? (p.positions ? p.positions[(long)b * n + tok] : tok) : 0;
+      float c, s;
+      rope_cos_sin(pos, p.inv_freq[t], &c, &s);
+      table[e] = make_float2(c, s);
+    }
+    __syncthreads();
+  }
+  {
+    constexpr int LPR = D / 8;
+    constexpr int RPI = 64 / LPR;
+    const int c = lane % LPR;
+    const int rsub = lane / LPR;
+    for (int it = 0; it < 16 / RPI; ++it) {
+      const int r = w * 16 + it * RPI + rsub;      // 0..127
+      const int side = r >> 6;
+      const int blk = side ? blk_heavy : blk_light;
+      const int local = r & 63;
+      const int hh = local / TB;
+      const int tt = local - hh * TB;
+      const int tok = blk * TB + tt;
+      const bool valid = (blk >= 0) && (hh < p.grp) && (tok < n);
+      u32x4_t raw = {0, 0, 0, 0};
+      if (valid) raw = *(const u32x4_t*)(p.q + (((long)b * n + tok) * p.H + g * p.grp + hh) * D + c * 8);
+      float x[8];
+      unpack8(raw, x);
+      const int pos = valid ? (p.positions ? p.positions[(long)b * n + tok] : tok) : 0;
+      norm_rope_chunk<D>(x, c, p.wq, p.eps, p.rot, pos, p.inv_freq,
+                         p.use_table ? table + (side * TB + tt) * half : nullptr);
+      *(u32x4_t*)(Qs + r * D + c * 8) = pack8(x);
+    }
+  }
+  __syncthreads();
+  bf16x8_t qf[D / 16];
+  {
+    const int my_r = rg * 32 + l32;
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) qf[kk] = *(const bf16x8_t*)(Qs + my_r * D + kk * 16 + hi * 8);
+  }
+
+  // ---- main loop over stages ------------------------------------------------
+  f32x16_t o[D / 32];
+#pragma unroll
+  for (int mb = 0; mb < D / 32; ++mb)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) o[mb][i] = 0.f;
+  float m_run = kNegBig;
+  float l_run = 0.f;
+  const float sl2 = p.scale_log2;
+  const int i16 = lane & 15;
+  const int g16 = lane >> 4;
+  // Lane-constant parts of the swizzled LDS addresses (the loop adds immediates).
+  // K operand: row = 32*phase + l32, chunk (2kk + hi) ^ (row & 15).
+  int kofs[8];
+  {
+    const int y = lane & 15;
+#pragma unroll
+    for (int k7 = 0; k7 < 8; ++k7)
+      kofs[k7] = l32 * S::ROW_BYTES + ((k7 ^ (y >> 1)) << 5) + ((hi ^ (y & 1)) << 4);
+  }
+  // V^T operand: row = 32*phase + 16ks + 4*hi + i16/4 (+8), chunk (4mb + c) ^ 4x.
+  int vofs[4];
+  {
+    const int x = (i16 >> 2) & 3;
+    const int c = (g16 & 1) * 2 + ((i16 & 3) >> 1);
+#pragma unroll
+    for (int m3 = 0; m3 < 4; ++m3)
+      vofs[m3] = (hi * 4 + (i16 >> 2)) * S::ROW_BYTES + ((4 * (m3 ^ x) + c) << 4) + (i16 & 1) * 8;
+  }
+
+  for (int st = 0; st < nst; ++st) {
+    // stage st has landed once at most the younger stages' loads are outstanding
+    if (S::NSTAGE == 3 && st + 1 < nst)
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * S::LOADS_PER_WAVE) : "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (st + S::NSTAGE - 1 < nst) v2_issue_stage<D>(smem, krs, vrs, koff, voff, w, st + S::NSTAGE - 1, kv_row_bytes);
+
+    const int k0 = st * S::ST + phase * 32;
+    if (k0 > wave_max_tok) continue;
+    const unsigned char* kt = smem + (st % S::NSTAGE) * S::STAGE_BYTES;
+    const unsigned char* vt = kt + S::TILE_BYTES;
+
+    f32x16_t s;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) s[i] = 0.f;
+    {
+      const unsigned char* kr = kt + phase * 32 * S::ROW_BYTES;
+#pragma unroll
+      for (int kk = 0; kk < D / 16; ++kk) {
+        const bf16x8_t a = *(const bf16x8_t*)(kr + kofs[kk & 7] + ((kk & 8) << 5));
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], s, 0, 0, 0);
+      }
+    }
+    const bool need_mask = (k0 + 31 > wave_min_tok) || (k0 + 32 > n);
+    float mloc = kNegBig;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      float x = s[i] * sl2;
+      if (need_mask) {
+        const int key = k0 + (i >> 2) * 8 + hi * 4 + (i & 3);
+        if (key > my_tok || key >= n) x = -INFINITY;
+      }
+      s[i] = x;
+      mloc = fmaxf(mloc, x);
+    }
+    {
+      auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(mloc), __float_as_uint(mloc), false, false);
+      mloc = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+    }
+    const float m_new = fmaxf(m_run, mloc);
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    float lsum = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float pv = __builtin_amdgcn_exp2f(s[i] - m_new);
+      s[i] = pv;
+      lsum += pv;
+    }
+    l_run = l_run * alpha + lsum;
+    m_run = m_new;
+    if (!__all(alpha == 1.0f)) {
+#pragma unroll
+      for (int mb = 0; mb < D / 32; ++mb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) o[mb][i] *= alpha;
+    }
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      u32x4_t pk;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) pk[j] = pack_bf16x2(s[ks * 8 + 2 * j], s[ks * 8 + 2 * j + 1]);
+      const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, pk);
+      // V^T fragment rows: keys 16ks + 4(lane/32) + (lane%16)/4 (+8 for slots 4..7)
+      const unsigned char* vr = vt + (phase * 32 + ks * 16) * S::ROW_BYTES;
+#pragma unroll
+      for (int mb = 0; mb < D / 32; ++mb) {
+        const unsigned char* a1 = vr + vofs[mb & 3] + ((mb & 4) << 6);
+        const unsigned char* a2 = a1 + 8 * S::ROW_BYTES;
+        const i16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)a1);
+        const i16x4_t v2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)a2);
+        const u32x4_t av = {__builtin_bit_cast(u32x2_t, v1)[0], __builtin_bit_cast(u32x2_t, v1)[1],
+                            __builtin_bit_cast(u32x2_t, v2)[0], __builtin_bit_cast(u32x2_t, v2)[1]};
+        o[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, av), pb, o[mb], 0, 0, 0);
+      }
+    }
+  }
+
+  // ---- merge the two phases of each row group --------------------------------
+  __syncthreads();  // stage buffers are free
+  float* xo = (float*)smem;
+  if (phase == 1) {
+#pragma unroll
+    for (int mb = 0; mb < D / 32; ++mb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) xo[((rg * (D / 32) + mb) * 16 + i) * 64 + lane] = o[mb][i];
+    ml_x[rg][lane][0] = m_run;
+    ml_x[rg][lane][1] = l_run;
+  }
+  __syncthreads();
+  if (phase == 1) return;
+  {
+    const float m1 = ml_x[rg][lane][0];
+    const float l1 = ml_x[rg][lane][1];
+    const float mt = fmaxf(m_run, m1);
+    const float a0 = __builtin_amdgcn_exp2f(m_run - mt);
+    const float a1 = __builtin_amdgcn_exp2f(m1 - mt);
+    l_run = l_run * a0 + l1 * a1;
+#pragma unroll
+    for (int mb = 0; mb < D / 32; ++mb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) o[mb][i] = o[mb][i] * a0 + xo[((rg * (D / 32) + mb) * 16 + i) * 64 + lane] * a1;
+  }
+
+  // ---- epilogue: normalise, gate, store -------------------------------------
+  {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_run), __float_as_uint(l_run), false, false);
+    l_run = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  }
+  if (!my_valid) return;
+  const float inv_l = 1.0f / l_run;
+  const long row_off = ((long)b * n + my_tok) * p.H + my_h;
+  uint16_t* orow = p.out + row_off * D;
+  float hg = 1.0f;
+  if (GATE == 1) hg = sigmoid_f32(bf16_bits_to_f32(p.gate[row_off]));
+#pragma unroll
+  for (int mb = 0; mb < D / 32; ++mb) {
+#pragma unroll
+    for (int ig = 0; ig < 4; ++ig) {
+      const int dm = mb * 32 + ig * 8 + hi * 4;
+      float y[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) y[j] = o[mb][ig * 4 + j] * inv_l;
+      if (GATE == 2) {
+        const u32x2_t z = *(const u32x2_t*)(p.gate + row_off * D + dm);
+        y[0] *= sigmoid_f32(lo_bf16(z[0]));
+        y[1] *= sigmoid_f32(hi_bf16(z[0]));
+        y[2] *= sigmoid_f32(lo_bf16(z[1]));
+        y[3] *= sigmoid_f32(hi_bf16(z[1]));
+      } else if (GATE == 1) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) y[j] *= hg;
+      }
+      const u32x2_t ov = {pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
+      *(u32x2_t*)(orow + dm) = ov;
+    }
+  }
+}
+
+template <int D>
+static hipError_t launch_v2_d(const PrefillParams& p, int gate_mode, hipStream_t s) {
+  const int npairs = (p.nblk + 1) / 2;
+  const long grid = (long)p.B * p.G * npairs;
+  if (grid <= 0) return hipSuccess;
+  switch (gate_mode) {
+    case 0: hipLaunchKernelGGL((prefill_v2_kernel<D, 0>), dim3((unsigned)grid), dim3(512), 0, s, p); break;
+    case 1: hipLaunchKernelGGL((prefill_v2_kernel<D, 1>), dim3((unsigned)grid), dim3(512), 0, s, p); break;
+    default: hipLaunchKernelGGL((prefill_v2_kernel<D, 2>), dim3((unsigned)grid), dim3(512), 0, s, p); break;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_prefill_v2(const PrefillParams& p, int D, int gate_mode, hipStream_t s) {
+  switch (D) {
+    case 128: return launch_v2_d<128>(p, gate_mode, s);
+    case 256: return launch_v2_d<256>(p, gate_mode, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace ga

@@ -32,6 +32,8 @@ SMALL_CASES = [
     _case("d128_g16_full_rope", 1, 65, 16, 1, 128, 128, "elementwise", seed=107),
     _case("d128_g1_full_rope_no_table", 1, 150, 2, 2, 128, 128, "headwise", seed=108),
     _case("d256_g2_b3_n97", 3, 97, 4, 2, 256, 0, "headwise", seed=109),          # no RoPE
+    _case("d128_g128", 1, 20, 128, 1, 128, 32, "elementwise", seed=113),         # group > 64: first design
+    _case("d256_g64_n40", 1, 40, 64, 1, 256, 64, "headwise", seed=114),
     # generic kernel (fp32, or bf16 shapes without a fused kernel)
     _case("f32_d24_g2", 2, 33, 4, 2, 24, 8, "headwise", dtype="f32", seed=110),
     _case("bf16_d96_g2", 1, 40, 4, 2, 96, 24, "elementwise", seed=111),
