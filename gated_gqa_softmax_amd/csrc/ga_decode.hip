@@ -28,25 +28,32 @@ namespace ga {
 
 template <int D, int GRP>
 __global__ __launch_bounds__(256) void decode_partials_kernel(const DecodeParams p) {
-  constexpr int C = kDecodeChunk;
+  constexpr int C = kDecodeChunk;   // keys per workgroup
+  constexpr int KW = C / 4;         // keys per wave
   constexpr int SQ = D + 8;
-  constexpr int LPR = D / 8;
-  extern __shared__ __attribute__((aligned(16))) unsigned char dyn_smem[];
-  uint16_t* Qs = (uint16_t*)dyn_smem;                 // [16][SQ] bf16 q-hat (rows >= GRP are 0)
-  float* Ssc = (float*)(dyn_smem + 16 * SQ * 2);      // [C][GRP] scores, then probabilities
-  float* Red = Ssc;                                   // reused: [4][GRP][D] wave partials
+  constexpr int LPR = D / 8;        // lanes per row (8 dims each) in the value mix
+  constexpr int KPW = 64 / LPR;     // keys per value-mix step
+  constexpr int VSTEPS = 16 / KPW;  // value-mix steps per 16-key group
+  __shared__ __attribute__((aligned(16))) uint16_t Qs[16 * SQ];  // q-hat rows (>= GRP are 0)
+  __shared__ float Pw[4][16][GRP];                               // per wave: p of the current group
+  __shared__ float Aw[4][GRP];                                   // per wave: rescale of the current group
+  __shared__ float Xw[4][GRP][D];                                // cross-wave merge: unnormalised o
+  __shared__ float Mw[4][GRP], Lw[4][GRP];
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int split = blockIdx.x;
-  const int bg = blockIdx.y;
-  const int b = bg / p.G, g = bg % p.G;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // consecutive workgroups take the KV heads of one chunk, so the heads'
+  // halves of each cache row are read at the same time
+  const int u = blockIdx.x;
+  const int g = u % p.G;
+  const int split = (u / p.G) % p.nsplit;
+  const int b = u / (p.G * p.nsplit);
   int L = p.cache_lens[b];
   if (L < 0 || L > p.max_len) L = 0;
   const int start = split * C;
-  if (start >= L) return;
-  const int nk = min(C, L - start);
+  if (start >= L) return;  // whole workgroup: no keys in this chunk
 
-  // q-hat of the group's heads at position L (same rounding as prefill: bf16)
+  // q-hat of the group's heads at position L (bf16, the MFMA operand precision)
   for (int idx = tid; idx < 16 * LPR; idx += 256) {
     const int r = idx / LPR, c = idx % LPR;
     u32x4_t raw = {0, 0, 0, 0};
@@ -58,252 +65,270 @@ __global__ __launch_bounds__(256) void decode_partials_kernel(const DecodeParams
   }
   __syncthreads();
 
-  // ---- scores: S^T[key][head] = K-hat . q-hat, 16 keys per MFMA group -------
   const int l16 = lane & 15, q4 = lane >> 4;
   bf16x8_t qf[D / 32];
 #pragma unroll
   for (int c = 0; c < D / 32; ++c) qf[c] = *(const bf16x8_t*)(Qs + l16 * SQ + c * 32 + q4 * 8);
+  const long row = (long)p.G * D;
   const uint16_t* Kc = p.k_cache + (long)b * p.cache_bstride + (long)g * D;
   const uint16_t* Vc = p.v_cache + (long)b * p.cache_bstride + (long)g * D;
-  const long row = (long)p.G * D;
-  const int ngroups = (nk + 15) / 16;
-  for (int gi = w; gi < ngroups; gi += 4) {
-    const int key = start + gi * 16 + l16;
-    const bool kval = key < start + nk;
-    u32x4_t kr[D / 32];
-#pragma unroll
-    for (int c = 0; c < D / 32; ++c)
-      kr[c] = kval ? *(const u32x4_t*)(Kc + key * row + c * 32 + q4 * 8) : u32x4_t{0, 0, 0, 0};
-    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int c = 0; c < D / 32; ++c)
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kr[c]), qf[c], acc, 0, 0, 0);
-    // acc[i]: head l16, key gi*16 + 4*q4 + i
-    if (l16 < GRP) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int kl = gi * 16 + q4 * 4 + i;
-        if (kl < C) Ssc[kl * GRP + l16] = (kl < nk) ? acc[i] * p.scale_log2 : -INFINITY;
-      }
-    }
-  }
-  __syncthreads();
-
-  // ---- chunk softmax per head (exact within the chunk) ----------------------
-  float* ws_o = p.ws;
-  float* ws_ml = p.ws + (long)p.B * p.H * p.nsplit * D;
-  for (int h = w; h < GRP; h += 4) {
-    float mx = -INFINITY;
-    for (int k = lane; k < nk; k += 64) mx = fmaxf(mx, Ssc[k * GRP + h]);
-    mx = max_xor<64>(mx);
-    float sm = 0.f;
-    for (int k = lane; k < nk; k += 64) {
-      const float e = __builtin_amdgcn_exp2f(Ssc[k * GRP + h] - mx);
-      Ssc[k * GRP + h] = e;
-      sm += e;
-    }
-    sm = sum_xor<64>(sm);
-    if (lane == 0) {
-      const long idx = ((long)b * p.H + g * GRP + h) * p.nsplit + split;
-      ws_ml[idx * 2 + 0] = mx;
-      ws_ml[idx * 2 + 1] = sm;
-    }
-  }
-  __syncthreads();
-
-  // ---- value mix: lane owns 8 dims of one key slot ---------------------------
-  constexpr int KPW = 64 / LPR;  // key slots per wave
+  const int kbeg = start + w * KW;
+  const int kend = min(kbeg + KW, min(start + C, L));
+  const int ngroups = kend > kbeg ? (kend - kbeg + 15) / 16 : 0;
+  const float sl2 = p.scale_log2;
   const int dc = lane % LPR, ks = lane / LPR;
+
+  float m_lane = kNegBig;  // reference max of head l16 (same in the 4 lanes of that head)
+  float l_part = 0.f;      // this lane's share of head l16's row sum
   float acc[GRP][8];
 #pragma unroll
   for (int h = 0; h < GRP; ++h)
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
-  constexpr int STEP = 4 * KPW;
-  constexpr int UNROLL = 4;
-  for (int k0 = w * KPW + ks; k0 < nk; k0 += STEP * UNROLL) {
-    u32x4_t vr[UNROLL];
+
+  // K and V rows of the first group; each iteration prefetches the next group
+  u32x4_t kr[D / 32];
+  u32x4_t vr[VSTEPS];
+  // Loads are unconditional: keys past the slice end read the slice's last row
+  // (their scores are masked to -inf), so the compiler can track each load.
+  const int klast = max(kend - 1, 0);
+  {
+    const int key = min(kbeg + l16, klast);
 #pragma unroll
-    for (int u = 0; u < UNROLL; ++u) {
-      const int k = k0 + u * STEP;
-      vr[u] = (k < nk) ? *(const u32x4_t*)(Vc + (long)(start + k) * row + dc * 8) : u32x4_t{0, 0, 0, 0};
-    }
+    for (int c = 0; c < D / 32; ++c) kr[c] = *(const u32x4_t*)(Kc + key * row + c * 32 + q4 * 8);
 #pragma unroll
-    for (int u = 0; u < UNROLL; ++u) {
-      const int k = k0 + u * STEP;
-      if (k < nk) {
-        float v[8];
-        unpack8(vr[u], v);
-#pragma unroll
-        for (int h = 0; h < GRP; ++h) {
-          const float pw = Ssc[k * GRP + h];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) acc[h][e] += pw * v[e];
-        }
-      }
+    for (int t = 0; t < VSTEPS; ++t) {
+      const int vkey = min(kbeg + ks + KPW * t, klast);
+      vr[t] = *(const u32x4_t*)(Vc + vkey * row + dc * 8);
     }
   }
-  // reduce over key slots inside the wave
+  for (int gi = 0; gi < ngroups; ++gi) {
+    const int k0 = kbeg + gi * 16;
+    // scores of this group: S^T[key][head], v_mfma_f32_16x16x32_bf16 over d
+    f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < D / 32; ++c)
+      sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kr[c]), qf[c], sc, 0, 0, 0);
+    // K rows of the next group
+    {
+      const int key = min(k0 + 16 + l16, klast);
+#pragma unroll
+      for (int c = 0; c < D / 32; ++c) kr[c] = *(const u32x4_t*)(Kc + key * row + c * 32 + q4 * 8);
+    }
+    // online softmax of head l16 over the group's keys k0 + 4*q4 + i
+    float s[4];
+    float gm = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      s[i] = (k0 + q4 * 4 + i < kend) ? sc[i] * sl2 : -INFINITY;
+      gm = fmaxf(gm, s[i]);
+    }
+    gm = fmaxf(gm, __shfl_xor(gm, 16, 64));
+    gm = fmaxf(gm, __shfl_xor(gm, 32, 64));
+    const float m_new = fmaxf(m_lane, gm);
+    const float alpha = __builtin_amdgcn_exp2f(m_lane - m_new);
+    m_lane = m_new;
+    float ps = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      s[i] = __builtin_amdgcn_exp2f(s[i] - m_new);
+      ps += s[i];
+    }
+    l_part = l_part * alpha + ps;
+    if (l16 < GRP) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) Pw[w][q4 * 4 + i][l16] = s[i];
+      if (q4 == 0) Aw[w][l16] = alpha;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // value mix: lane owns dims [8dc, 8dc+8) of keys ks + KPW*t
+#pragma unroll
+    for (int h = 0; h < GRP; ++h) {
+      const float a = Aw[w][h];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[h][e] *= a;
+    }
+    u32x4_t vn[VSTEPS];
+#pragma unroll
+    for (int t = 0; t < VSTEPS; ++t) {
+      const int vkey = min(k0 + 16 + ks + KPW * t, klast);
+      vn[t] = *(const u32x4_t*)(Vc + vkey * row + dc * 8);
+    }
+#pragma unroll
+    for (int t = 0; t < VSTEPS; ++t) {
+      const int kl = ks + KPW * t;
+      float v[8];
+      unpack8(vr[t], v);
+#pragma unroll
+      for (int h = 0; h < GRP; ++h) {
+        const float pw = Pw[w][kl][h];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[h][e] += pw * v[e];
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < VSTEPS; ++t) vr[t] = vn[t];
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  }
+
+  // per-wave totals: row sums over the 4 lanes of each head, o over key slots
+  l_part += __shfl_xor(l_part, 16, 64);
+  l_part += __shfl_xor(l_part, 32, 64);
 #pragma unroll
   for (int m = LPR; m < 64; m <<= 1)
 #pragma unroll
     for (int h = 0; h < GRP; ++h)
 #pragma unroll
       for (int e = 0; e < 8; ++e) acc[h][e] += __shfl_xor(acc[h][e], m, 64);
-  __syncthreads();  // Ssc no longer needed: reuse as Red
+  if (lane < GRP) {
+    Mw[w][lane] = m_lane;
+    Lw[w][lane] = l_part;
+  }
   if (ks == 0) {
 #pragma unroll
     for (int h = 0; h < GRP; ++h)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) Red[(w * GRP + h) * D + dc * 8 + e] = acc[h][e];
+      for (int e = 0; e < 8; ++e) Xw[w][h][dc * 8 + e] = acc[h][e];
   }
   __syncthreads();
+
+  // merge the 4 waves and write this chunk's partial result
+  float* ws_o = p.ws;
+  float* ws_ml = p.ws + (long)p.B * p.H * p.nsplit * D;
   for (int idx = tid; idx < GRP * D; idx += 256) {
     const int h = idx / D, e = idx % D;
-    const float s = Red[(0 * GRP + h) * D + e] + Red[(1 * GRP + h) * D + e] + Red[(2 * GRP + h) * D + e] +
-                    Red[(3 * GRP + h) * D + e];
-    ws_o[(((long)b * p.H + g * GRP + h) * p.nsplit + split) * D + e] = s;
+    const float M = fmaxf(fmaxf(Mw[0][h], Mw[1][h]), fmaxf(Mw[2][h], Mw[3][h]));
+    float o = 0.f;
+#pragma unroll
+    for (int ww = 0; ww < 4; ++ww) o += Xw[ww][h][e] * __builtin_amdgcn_exp2f(Mw[ww][h] - M);
+    ws_o[(((long)b * p.H + g * GRP + h) * p.nsplit + split) * D + e] = o;
+    if (e == 0) {
+      float l = 0.f;
+#pragma unroll
+      for (int ww = 0; ww < 4; ++ww) l += Lw[ww][h] * __builtin_amdgcn_exp2f(Mw[ww][h] - M);
+      const long mi = ((long)b * p.H + g * GRP + h) * p.nsplit + split;
+      ws_ml[mi * 2 + 0] = M;
+      ws_ml[mi * 2 + 1] = l;
+    }
   }
 }
 
+// One workgroup per (sequence, query head): the new token's own key and value,
+// the chunk partials, the gate; the group's first head also appends the new
+// K-hat and V to the cache.
 template <int D, int GATE>
 __global__ __launch_bounds__(256) void decode_merge_kernel(const DecodeParams p) {
   constexpr int LPR = D / 8;
-  constexpr int SPLITS_PER_PASS = 256;
-  __shared__ float qk[17][D];       // rows 0..grp-1: q-hat (bf16-rounded); row 16: k-hat new
-  __shared__ float snew[16];
-  __shared__ float mtot[16], ltot[16];
-  __shared__ float wts[16][SPLITS_PER_PASS];
+  constexpr int SPASS = 256;
+  __shared__ float qk[2][D];  // row 0: q-hat (bf16-rounded); row 1: new k-hat (bf16-rounded)
+  __shared__ float red[8];
+  __shared__ float wts[SPASS];
+  __shared__ float sh_snew, sh_M, sh_L;
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int bg = blockIdx.x;
-  const int b = bg / p.G, g = bg % p.G;
+  const int bh = blockIdx.x;
+  const int b = bh / p.H, h = bh % p.H;
   const int grp = p.grp;
+  const int g = h / grp;
   const int L = p.cache_lens[b];
-  uint16_t* out = p.out + ((long)b * p.H + g * grp) * D;
+  uint16_t* out = p.out + ((long)b * p.H + h) * D;
   if (L < 0 || L > p.max_len) {
-    for (int idx = tid; idx < grp * D; idx += 256) out[idx] = 0x7fc0;  // NaN
+    for (int e = tid; e < D; e += 256) out[e] = 0x7fc0;  // NaN
     return;
   }
-
-  // q-hat rows and the new key row: norm + rope at position L, rounded to bf16
-  for (int idx = tid; idx < 17 * LPR; idx += 256) {
-    const int r = idx / LPR, c = idx % LPR;
-    const bool is_k = (r == 16);
-    u32x4_t raw = {0, 0, 0, 0};
-    if (is_k) raw = *(const u32x4_t*)(p.k_new + ((long)b * p.G + g) * D + c * 8);
-    else if (r < grp) raw = *(const u32x4_t*)(p.q + ((long)b * p.H + g * grp + r) * D + c * 8);
+  if (tid < 2 * LPR) {  // two rows, LPR lanes each (whole lane groups of one wave)
+    const int r = tid / LPR, c = tid % LPR;
+    const u32x4_t raw = (r == 0) ? *(const u32x4_t*)(p.q + ((long)b * p.H + h) * D + c * 8)
+                                 : *(const u32x4_t*)(p.k_new + ((long)b * p.G + g) * D + c * 8);
     float x[8];
     unpack8(raw, x);
-    norm_rope_chunk<D>(x, c, is_k ? p.wk : p.wq, p.eps, p.rot, L, p.inv_freq, nullptr);
+    norm_rope_chunk<D>(x, c, r == 0 ? p.wq : p.wk, p.eps, p.rot, L, p.inv_freq, nullptr);
     const u32x4_t pk = pack8(x);
     float xr[8];
     unpack8(pk, xr);
 #pragma unroll
     for (int j = 0; j < 8; ++j) qk[r][c * 8 + j] = xr[j];
-    if (is_k) {
+    if (r == 1 && h % grp == 0) {
       const long slot = (long)b * p.cache_bstride + ((long)L * p.G + g) * D + c * 8;
       *(u32x4_t*)(p.k_cache + slot) = pk;
       *(u32x4_t*)(p.v_cache + slot) = *(const u32x4_t*)(p.v_new + ((long)b * p.G + g) * D + c * 8);
     }
   }
   __syncthreads();
-  // the new token's own score, per head
-  for (int h = w; h < grp; h += 4) {
+  if (w == 0) {
     float s = 0.f;
-    for (int e = lane; e < D; e += 64) s += qk[h][e] * qk[16][e];
+    for (int e = lane; e < D; e += 64) s += qk[0][e] * qk[1][e];
     s = sum_xor<64>(s);
-    if (lane == 0) snew[h] = s * p.scale_log2;
+    if (lane == 0) sh_snew = s * p.scale_log2;
   }
   __syncthreads();
-
+  const float snew = sh_snew;
   const int ns = (L + kDecodeChunk - 1) / kDecodeChunk;
-  const float* ws_o = p.ws;
-  const float* ws_ml = p.ws + (long)p.B * p.H * p.nsplit * D;
-  // global max and sum per head
-  for (int h = w; h < grp; h += 4) {
-    const long base = ((long)b * p.H + g * grp + h) * p.nsplit;
-    float mx = snew[h];
-    for (int s = lane; s < ns; s += 64) mx = fmaxf(mx, ws_ml[(base + s) * 2]);
-    mx = max_xor<64>(mx);
-    float sm = 0.f;
-    for (int s = lane; s < ns; s += 64) sm += ws_ml[(base + s) * 2 + 1] * __builtin_amdgcn_exp2f(ws_ml[(base + s) * 2] - mx);
-    sm = sum_xor<64>(sm) + __builtin_amdgcn_exp2f(snew[h] - mx);
-    if (lane == 0) {
-      mtot[h] = mx;
-      ltot[h] = sm;
+  const long base = ((long)b * p.H + h) * p.nsplit;
+  const float* ws_o = p.ws + base * D;
+  const float* ws_ml = p.ws + (long)p.B * p.H * p.nsplit * D + base * 2;
+  // global max, then the row sum
+  float mx = snew;
+  for (int s = tid; s < ns; s += 256) mx = fmaxf(mx, ws_ml[s * 2]);
+  mx = max_xor<64>(mx);
+  if (lane == 0) red[w] = mx;
+  __syncthreads();
+  if (tid == 0) sh_M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  __syncthreads();
+  const float M = sh_M;
+  float sm = 0.f;
+  for (int s = tid; s < ns; s += 256) sm += ws_ml[s * 2 + 1] * __builtin_amdgcn_exp2f(ws_ml[s * 2] - M);
+  sm = sum_xor<64>(sm);
+  if (lane == 0) red[4 + w] = sm;
+  __syncthreads();
+  if (tid == 0) sh_L = red[4] + red[5] + red[6] + red[7] + __builtin_amdgcn_exp2f(snew - M);
+  // weighted sum of the chunk outputs, SPASS chunks at a time
+  float o0 = 0.f, o1 = 0.f;
+  for (int s0 = 0; s0 < ns; s0 += SPASS) {
+    __syncthreads();
+    if (s0 + tid < ns) wts[tid] = __builtin_amdgcn_exp2f(ws_ml[(s0 + tid) * 2] - M);
+    __syncthreads();
+    const int sn = min(SPASS, ns - s0);
+    if (tid < D) {
+      const float* src = ws_o + (long)s0 * D + tid;
+      int s = 0;
+      for (; s + 4 <= sn; s += 4) {
+        const float a0 = src[(long)(s + 0) * D], a1 = src[(long)(s + 1) * D];
+        const float a2 = src[(long)(s + 2) * D], a3 = src[(long)(s + 3) * D];
+        o0 += a0 * wts[s] + a2 * wts[s + 2];
+        o1 += a1 * wts[s + 1] + a3 * wts[s + 3];
+      }
+      for (; s < sn; ++s) o0 += src[(long)s * D] * wts[s];
     }
   }
   __syncthreads();
-
-  // outputs: thread owns (head, dim) pairs
-  constexpr int MAXO = 16 * D / 256;
-  float accv[MAXO];
-#pragma unroll
-  for (int j = 0; j < MAXO; ++j) accv[j] = 0.f;
-  for (int s0 = 0; s0 < ns; s0 += SPLITS_PER_PASS) {
-    for (int idx = tid; idx < grp * SPLITS_PER_PASS; idx += 256) {
-      const int h = idx / SPLITS_PER_PASS, s = idx % SPLITS_PER_PASS;
-      const long base = ((long)b * p.H + g * grp + h) * p.nsplit;
-      wts[h][s] = (s0 + s < ns) ? __builtin_amdgcn_exp2f(ws_ml[(base + s0 + s) * 2] - mtot[h]) : 0.f;
-    }
-    __syncthreads();
-    const int sn = min(SPLITS_PER_PASS, ns - s0);
-#pragma unroll
-    for (int j = 0; j < MAXO; ++j) {
-      const int idx = tid + 256 * j;
-      if (idx < grp * D) {
-        const int h = idx / D, e = idx % D;
-        const long base = ((long)b * p.H + g * grp + h) * p.nsplit + s0;
-        float a = accv[j];
-        for (int s = 0; s < sn; ++s) a += ws_o[(base + s) * D + e] * wts[h][s];
-        accv[j] = a;
-      }
-    }
-    __syncthreads();
-  }
-#pragma unroll
-  for (int j = 0; j < MAXO; ++j) {
-    const int idx = tid + 256 * j;
-    if (idx < grp * D) {
-      const int h = idx / D, e = idx % D;
-      const float vnew = bf16_bits_to_f32(p.v_new[((long)b * p.G + g) * D + e]);
-      float y = (accv[j] + vnew * __builtin_amdgcn_exp2f(snew[h] - mtot[h])) / ltot[h];
-      if (GATE == 2) y *= sigmoid_f32(bf16_bits_to_f32(p.gate[((long)b * p.H + g * grp + h) * D + e]));
-      if (GATE == 1) y *= sigmoid_f32(bf16_bits_to_f32(p.gate[(long)b * p.H + g * grp + h]));
-      out[idx] = f32_to_bf16_bits(y);
-    }
+  if (tid < D) {
+    const int e = tid;
+    const float vnew = bf16_bits_to_f32(p.v_new[((long)b * p.G + g) * D + e]);
+    float y = (o0 + o1 + vnew * __builtin_amdgcn_exp2f(snew - M)) / sh_L;
+    if (GATE == 2) y *= sigmoid_f32(bf16_bits_to_f32(p.gate[((long)b * p.H + h) * D + e]));
+    if (GATE == 1) y *= sigmoid_f32(bf16_bits_to_f32(p.gate[(long)b * p.H + h]));
+    out[e] = f32_to_bf16_bits(y);
   }
 }
 
 template <int D>
 static hipError_t launch_partials_d(const DecodeParams& p, hipStream_t s) {
-  const dim3 grid((unsigned)p.nsplit, (unsigned)(p.B * p.G));
-  if (grid.x == 0 || grid.y == 0) return hipSuccess;
-  const size_t sq = 16 * (D + 8) * 2;
-  size_t body = 0;
-#define GA_PARTIALS_CASE(GR)                                                                     \
-  case GR: {                                                                                     \
-    const size_t s1 = (size_t)kDecodeChunk * GR * 4, s2 = (size_t)4 * GR * D * 4;                \
-    body = s1 > s2 ? s1 : s2;                                                                    \
-    if (sq + body > 65536) {                                                                     \
-      hipError_t e = hipFuncSetAttribute((const void*)decode_partials_kernel<D, GR>,             \
-                                         hipFuncAttributeMaxDynamicSharedMemorySize,             \
-                                         (int)(sq + body));                                      \
-      if (e != hipSuccess) return e;                                                             \
-    }                                                                                            \
-    hipLaunchKernelGGL((decode_partials_kernel<D, GR>), grid, dim3(256), sq + body, s, p);       \
-    break;                                                                                       \
-  }
+  const long nwg = (long)p.nsplit * p.B * p.G;
+  if (nwg <= 0) return hipSuccess;
+  const dim3 grid((unsigned)nwg);
   switch (p.grp) {
-    GA_PARTIALS_CASE(1)
-    GA_PARTIALS_CASE(2)
-    GA_PARTIALS_CASE(4)
-    GA_PARTIALS_CASE(8)
-    GA_PARTIALS_CASE(16)
+    case 1: hipLaunchKernelGGL((decode_partials_kernel<D, 1>), grid, dim3(256), 0, s, p); break;
+    case 2: hipLaunchKernelGGL((decode_partials_kernel<D, 2>), grid, dim3(256), 0, s, p); break;
+    case 4: hipLaunchKernelGGL((decode_partials_kernel<D, 4>), grid, dim3(256), 0, s, p); break;
+    case 8: hipLaunchKernelGGL((decode_partials_kernel<D, 8>), grid, dim3(256), 0, s, p); break;
+    case 16: hipLaunchKernelGGL((decode_partials_kernel<D, 16>), grid, dim3(256), 0, s, p); break;
     default: return hipErrorInvalidValue;
   }
-#undef GA_PARTIALS_CASE
   return hipGetLastError();
 }
 
@@ -318,7 +343,7 @@ hipError_t launch_decode_partials(const DecodeParams& p, int D, hipStream_t s) {
 
 template <int D>
 static hipError_t launch_merge_d(const DecodeParams& p, int gate_mode, hipStream_t s) {
-  const dim3 grid((unsigned)(p.B * p.G));
+  const dim3 grid((unsigned)(p.B * p.H));
   if (grid.x == 0) return hipSuccess;
   switch (gate_mode) {
     case 0: hipLaunchKernelGGL((decode_merge_kernel<D, 0>), grid, dim3(256), 0, s, p); break;

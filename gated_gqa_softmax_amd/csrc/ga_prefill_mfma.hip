@@ -55,7 +55,7 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(const PrefillParams p
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int w = tid >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index (uniform)
   const int l32 = lane & 31;
   const int hi = lane >> 5;
 
@@ -86,6 +86,9 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(const PrefillParams p
     wave_max_tok = max(wave_max_tok, __shfl_xor(wave_max_tok, m, 64));
     wave_min_tok = min(wave_min_tok, __shfl_xor(wave_min_tok, m, 64));
   }
+  // wave-uniform: keep them in scalar registers so tile skips and masks branch uniformly
+  wave_max_tok = __builtin_amdgcn_readfirstlane(wave_max_tok);
+  wave_min_tok = __builtin_amdgcn_readfirstlane(wave_min_tok);
 
   const uint16_t* kbase_ptr = p.khat + (long)b * p.k_bstride + (long)g * D;
   const uint16_t* vbase_ptr = p.v + (long)b * p.v_bstride + (long)g * D;
@@ -224,21 +227,24 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(const PrefillParams p
           s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], s[kb], 0, 0, 0);
         }
       }
-      const bool need_mask = (k0 + KN - 1 > wave_min_tok) || (k0 + KN > n);
+      const bool need_mask = (k0 + KN - 1 > wave_min_tok) || (k0 + KN > n);  // wave-uniform
+#pragma unroll
+      for (int kb = 0; kb < KN / 32; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) s[kb][i] *= sl2;
+      if (need_mask) {
+        const int lim = min(my_tok, n - 1) - (k0 + hi * 4);
+#pragma unroll
+        for (int kb = 0; kb < KN / 32; ++kb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i)
+            s[kb][i] = (kb * 32 + (i >> 2) * 8 + (i & 3) <= lim) ? s[kb][i] : -INFINITY;
+      }
       float mloc = kNegBig;
 #pragma unroll
-      for (int kb = 0; kb < KN / 32; ++kb) {
+      for (int kb = 0; kb < KN / 32; ++kb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          float x = s[kb][i] * sl2;
-          if (need_mask) {
-            const int key = k0 + kb * 32 + (i >> 2) * 8 + hi * 4 + (i & 3);
-            if (key > my_tok || key >= n) x = -INFINITY;
-          }
-          s[kb][i] = x;
-          mloc = fmaxf(mloc, x);
-        }
-      }
+        for (int i = 0; i < 16; ++i) mloc = fmaxf(mloc, s[kb][i]);
       {
         auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(mloc), __float_as_uint(mloc), false, false);
         mloc = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));

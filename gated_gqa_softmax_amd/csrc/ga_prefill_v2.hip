@@ -23,10 +23,16 @@
 //    fragments come straight from the S^T accumulators; V^T fragments come
 //    from row-major V in LDS through ds_read_b64_tr_b16 (16-bit transpose
 //    read), so V needs no transposition on its way in.
-//  * K and V tiles go from HBM/L2 to LDS with global_load_lds_dwordx4 (no
+//  * K and V tiles go from HBM/L2 to LDS with buffer_load ... lds (no
 //    register staging), XOR-swizzled per row so the MFMA operand reads are
 //    free of bank conflicts; stages are double (d = 256) or triple (d = 128)
-//    buffered.
+//    buffered. LDS holds [K stage 0..S-1][V stage 0..S-1] and the stage loop
+//    is unrolled over the buffers, so every operand address is a lane
+//    register plus an immediate.
+//  * The reference row max is raised lazily: the output is rescaled only when
+//    a tile's max exceeds the reference by more than 2^8, so probabilities
+//    stay below 256 (exact in fp32, fine as bf16 operands) and most tiles
+//    skip the rescale.
 #include "ga_common.hpp"
 #include "ga_internal.hpp"
 
@@ -41,16 +47,14 @@ struct V2Shape {
   static constexpr int CPR = D / 8;                  // 16-byte chunks per row
   static constexpr int ROW_BYTES = D * 2;
   static constexpr int TILE_BYTES = ST * ROW_BYTES;  // K (or V) of one stage
-  static constexpr int STAGE_BYTES = 2 * TILE_BYTES;
   static constexpr int NSTAGE = (D == 256) ? 2 : 3;
-  static constexpr int BUF_BYTES = NSTAGE * STAGE_BYTES;
-  static constexpr int QS_BYTES = 128 * ROW_BYTES;
+  static constexpr int BUF_BYTES = 2 * NSTAGE * TILE_BYTES;
+  static constexpr int VBASE = NSTAGE * TILE_BYTES;  // start of the V stages
   static constexpr int LOADS_PER_TILE = TILE_BYTES / 1024;  // 1 KB per wave instruction
   static constexpr int LOADS_PER_WAVE = LOADS_PER_TILE / 8;
   static constexpr int ROWS_PER_LOAD = 1024 / ROW_BYTES;
   static constexpr int XCHG_BYTES = 4 * (D / 32) * 16 * 64 * 4;  // phase-1 O of 4 row groups
   static_assert(CPR >= 16, "swizzles need at least 16 chunks per row");
-  static_assert(QS_BYTES <= STAGE_BYTES, "Q staging must fit one stage");
   static_assert(XCHG_BYTES <= BUF_BYTES, "merge buffer must fit the stages");
   static_assert(LOADS_PER_WAVE >= 1, "tile too small");
 };
@@ -58,24 +62,131 @@ struct V2Shape {
 __device__ __forceinline__ int swz_k(int row) { return row & 15; }
 __device__ __forceinline__ int swz_v(int row) { return (row & 3) << 2; }
 
-// Issue the direct-to-LDS loads of one stage (64 keys of K-hat and V) for this
-// wave: 1 KB of LDS per instruction, lane l's 16 bytes at slot l. The whole
-// byte offset goes in the VGPR operand so the buffer range check sees it.
+constexpr float kLazyRescale = 8.0f;  // log2 headroom before the output is rescaled
+
+// Per-wave state of the main loop.
 template <int D>
-__device__ __forceinline__ void v2_issue_stage(unsigned char* smem, __amdgpu_buffer_rsrc_t krs,
-                                               __amdgpu_buffer_rsrc_t vrs, const int* koff, const int* voff,
-                                               int w, int st, int kv_row_bytes) {
+struct V2Wave {
+  bf16x8_t qf[D / 16];   // Q^T operand fragments of this wave's 32 rows
+  f32x16_t o[D / 32];    // O^T accumulators
+  float m_run, l_run;    // reference max (log2 domain) and lane-partial row sum
+  int kofs[8];           // K operand LDS addresses (lane part, phase included)
+  int vofs[4];           // V^T operand LDS addresses (lane part, phase and V base included)
+};
+
+// Q staging rows: 0-63 in K buffer NSTAGE-1, 64-127 in V buffer NSTAGE-1.
+template <int D>
+__device__ __forceinline__ uint16_t* v2_qrow(unsigned char* smem, int r) {
   typedef V2Shape<D> S;
-  unsigned char* kt = smem + (st % S::NSTAGE) * S::STAGE_BYTES;
-  unsigned char* vt = kt + S::TILE_BYTES;
+  return (uint16_t*)(smem + ((r < 64) ? (S::NSTAGE - 1) : (2 * S::NSTAGE - 1)) * S::TILE_BYTES +
+                     (r & 63) * S::ROW_BYTES);
+}
+
+// Direct-to-LDS loads of one stage (64 keys of K-hat and V) for this wave:
+// 1 KB of LDS per instruction, lane l's 16 bytes at slot l. The whole byte
+// offset goes in the VGPR operand so the buffer range check sees it.
+template <int D, int BUF>
+__device__ __forceinline__ void v2_issue(unsigned char* smem, __amdgpu_buffer_rsrc_t krs, __amdgpu_buffer_rsrc_t vrs,
+                                         int koff, int voff, int w, int st, int kv_row_bytes) {
+  typedef V2Shape<D> S;
+  unsigned char* kt = smem + BUF * S::TILE_BYTES;
+  unsigned char* vt = smem + S::VBASE + BUF * S::TILE_BYTES;
   const int soff = st * S::ST * kv_row_bytes;
+  const int jstep = 8 * S::ROWS_PER_LOAD * kv_row_bytes;
 #pragma unroll
   for (int j = 0; j < S::LOADS_PER_WAVE; ++j) {
     const int t = w + 8 * j;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (__attribute__((address_space(3))) void*)(kt + t * 1024), 16,
-                                             koff[j] + soff, 0, 0, 0);
+                                             koff + soff + j * jstep, 0, 0, 0);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (__attribute__((address_space(3))) void*)(vt + t * 1024), 16,
-                                             voff[j] + soff, 0, 0, 0);
+                                             voff + soff + j * jstep, 0, 0, 0);
+  }
+}
+
+// One 32-key tile (this wave's phase half of stage buffer BUF) for 32 rows.
+template <int D, int BUF>
+__device__ __forceinline__ void v2_tile(const unsigned char* smem, V2Wave<D>& ws, bool need_mask, int lim,
+                                        float sl2) {
+  typedef V2Shape<D> S;
+  f32x16_t s;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) s[i] = 0.f;
+#pragma unroll
+  for (int kk = 0; kk < D / 16; ++kk) {
+    const bf16x8_t a = *(const bf16x8_t*)(smem + ws.kofs[kk & 7] + (BUF * S::TILE_BYTES + ((kk & 8) << 5)));
+    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, ws.qf[kk], s, 0, 0, 0);
+  }
+  if (need_mask) {
+    // s[i] holds key k0 + 8(i/4) + 4hi + (i%4); visible iff 8(i/4) + (i%4) <= lim
+#pragma unroll
+    for (int i = 0; i < 16; ++i) s[i] = ((i >> 2) * 8 + (i & 3) <= lim) ? s[i] : -INFINITY;
+  }
+  float mloc = s[0];
+#pragma unroll
+  for (int i = 1; i < 16; ++i) mloc = fmaxf(mloc, s[i]);
+  {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(mloc), __float_as_uint(mloc), false, false);
+    mloc = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  }
+  const float mcand = mloc * sl2;
+  if (!__all(mcand <= ws.m_run + kLazyRescale)) {
+    const float m_new = fmaxf(ws.m_run, mcand);
+    const float alpha = __builtin_amdgcn_exp2f(ws.m_run - m_new);
+    ws.l_run *= alpha;
+#pragma unroll
+    for (int mb = 0; mb < D / 32; ++mb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) ws.o[mb][i] *= alpha;
+    ws.m_run = m_new;
+  }
+  const float nm = -ws.m_run;
+  float lsum = 0.f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], sl2, nm));
+    s[i] = pv;
+    lsum += pv;
+  }
+  ws.l_run += lsum;
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    u32x4_t pk;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) pk[j] = pack_bf16x2(s[ks * 8 + 2 * j], s[ks * 8 + 2 * j + 1]);
+    const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, pk);
+#pragma unroll
+    for (int mb = 0; mb < D / 32; ++mb) {
+      // V^T fragment rows: keys 16ks + 4(lane/32) + (lane%16)/4 (+8 for slots 4..7)
+      const unsigned char* a1 =
+          smem + ws.vofs[mb & 3] + (BUF * S::TILE_BYTES + ((mb & 4) << 6) + ks * 16 * S::ROW_BYTES);
+      const i16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)a1);
+      const i16x4_t v2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(a1 + 8 * S::ROW_BYTES));
+      const u32x4_t av = {__builtin_bit_cast(u32x2_t, v1)[0], __builtin_bit_cast(u32x2_t, v1)[1],
+                          __builtin_bit_cast(u32x2_t, v2)[0], __builtin_bit_cast(u32x2_t, v2)[1]};
+      ws.o[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, av), pb, ws.o[mb], 0, 0, 0);
+    }
+  }
+}
+
+// One pipeline step: wait for stage st (buffer BUF), refill the buffer freed
+// by the previous step, and run this wave's tile if it has visible keys.
+template <int D, int BUF>
+__device__ __forceinline__ void v2_step(unsigned char* smem, V2Wave<D>& ws, __amdgpu_buffer_rsrc_t krs,
+                                        __amdgpu_buffer_rsrc_t vrs, int koff, int voff, int w, int st, int nst,
+                                        int kv_row_bytes, int phase, int wave_min_tok, int wave_max_tok,
+                                        int my_lim_tok, int n, float sl2, int hi) {
+  typedef V2Shape<D> S;
+  if (S::NSTAGE == 3 && st + 1 < nst)
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * S::LOADS_PER_WAVE) : "memory");
+  else
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  if (st + S::NSTAGE - 1 < nst)
+    v2_issue<D, (BUF + S::NSTAGE - 1) % S::NSTAGE>(smem, krs, vrs, koff, voff, w, st + S::NSTAGE - 1, kv_row_bytes);
+  const int k0 = st * S::ST + phase * 32;
+  if (k0 <= wave_max_tok) {
+    const bool need_mask = (k0 + 31 > wave_min_tok) || (k0 + 32 > n);  // wave-uniform
+    v2_tile<D, BUF>(smem, ws, need_mask, my_lim_tok - (k0 + hi * 4), sl2);
   }
 }
 
@@ -88,7 +199,7 @@ __global__ __launch_bounds__(512) void prefill_v2_kernel(const PrefillParams p) 
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int w = tid >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index (uniform)
   const int l32 = lane & 31;
   const int hi = lane >> 5;
   // wave -> (row group, phase): each SIMD (w % 4) gets one light and one heavy wave
@@ -124,6 +235,10 @@ __global__ __launch_bounds__(512) void prefill_v2_kernel(const PrefillParams p) 
     wave_max_tok = max(wave_max_tok, __shfl_xor(wave_max_tok, m, 64));
     wave_min_tok = min(wave_min_tok, __shfl_xor(wave_min_tok, m, 64));
   }
+  // wave-uniform: keep them in scalar registers so tile skips and masks branch uniformly
+  wave_max_tok = __builtin_amdgcn_readfirstlane(wave_max_tok);
+  wave_min_tok = __builtin_amdgcn_readfirstlane(wave_min_tok);
+  const int my_lim_tok = min(my_tok, n - 1);
 
   // ---- direct-to-LDS stage loads --------------------------------------------
   // Buffer resources cover keys [0, n) of this (b, g): rows past the end read
@@ -134,19 +249,19 @@ __global__ __launch_bounds__(512) void prefill_v2_kernel(const PrefillParams p) 
       (void*)(p.khat + (long)b * p.k_bstride + (long)g * D), (short)0, (int)valid_bytes, 0x00020000);
   const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(p.v + (long)b * p.v_bstride + (long)g * D), (short)0, (int)valid_bytes, 0x00020000);
-  int koff[S::LOADS_PER_WAVE], voff[S::LOADS_PER_WAVE];
-#pragma unroll
-  for (int j = 0; j < S::LOADS_PER_WAVE; ++j) {
-    const int row = (w + 8 * j) * S::ROWS_PER_LOAD + lane / S::CPR;
+  int koff, voff;
+  {
+    // load j covers rows row0 + 8j*ROWS_PER_LOAD (multiples of 16 apart): same swizzle
+    const int row0 = w * S::ROWS_PER_LOAD + lane / S::CPR;
     const int ph = lane % S::CPR;
-    koff[j] = row * kv_row_bytes + ((ph ^ swz_k(row)) << 4);
-    voff[j] = row * kv_row_bytes + ((ph ^ swz_v(row)) << 4);
+    koff = row0 * kv_row_bytes + ((ph ^ swz_k(row0)) << 4);
+    voff = row0 * kv_row_bytes + ((ph ^ swz_v(row0)) << 4);
   }
-  for (int s = 0; s < S::NSTAGE - 1; ++s)
-    if (s < nst) v2_issue_stage<D>(smem, krs, vrs, koff, voff, w, s, kv_row_bytes);
 
-  // ---- Q prologue: RMSNorm + RoPE of 128 rows into LDS (stage NSTAGE-1) ------
-  uint16_t* Qs = (uint16_t*)(smem + (S::NSTAGE - 1) * S::STAGE_BYTES);
+  if (nst > 0) v2_issue<D, 0>(smem, krs, vrs, koff, voff, w, 0, kv_row_bytes);
+  if (S::NSTAGE == 3 && nst > 1) v2_issue<D, 1>(smem, krs, vrs, koff, voff, w, 1, kv_row_bytes);
+
+  // ---- Q prologue: RMSNorm + RoPE of 128 rows into LDS ------------------------
   const int half = p.half;
   if (p.use_table) {
     for (int e = tid; e < 2 * TB * half; e += 512) {
@@ -184,124 +299,52 @@ __global__ __launch_bounds__(512) void prefill_v2_kernel(const PrefillParams p) 
       const int pos = valid ? (p.positions ? p.positions[(long)b * n + tok] : tok) : 0;
       norm_rope_chunk<D>(x, c, p.wq, p.eps, p.rot, pos, p.inv_freq,
                          p.use_table ? table + (side * TB + tt) * half : nullptr);
-      *(u32x4_t*)(Qs + r * D + c * 8) = pack8(x);
+      *(u32x4_t*)(v2_qrow<D>(smem, r) + c * 8) = pack8(x);
     }
   }
   __syncthreads();
-  bf16x8_t qf[D / 16];
-  {
-    const int my_r = rg * 32 + l32;
-#pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) qf[kk] = *(const bf16x8_t*)(Qs + my_r * D + kk * 16 + hi * 8);
-  }
 
-  // ---- main loop over stages ------------------------------------------------
-  f32x16_t o[D / 32];
+  V2Wave<D> ws;
+  {
+    const uint16_t* qr = v2_qrow<D>(smem, rg * 32 + l32);
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) ws.qf[kk] = *(const bf16x8_t*)(qr + kk * 16 + hi * 8);
+  }
 #pragma unroll
   for (int mb = 0; mb < D / 32; ++mb)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) o[mb][i] = 0.f;
-  float m_run = kNegBig;
-  float l_run = 0.f;
+    for (int i = 0; i < 16; ++i) ws.o[mb][i] = 0.f;
+  ws.m_run = kNegBig;
+  ws.l_run = 0.f;
   const float sl2 = p.scale_log2;
-  const int i16 = lane & 15;
-  const int g16 = lane >> 4;
-  // Lane-constant parts of the swizzled LDS addresses (the loop adds immediates).
-  // K operand: row = 32*phase + l32, chunk (2kk + hi) ^ (row & 15).
-  int kofs[8];
   {
+    const int i16 = lane & 15;
+    const int g16 = lane >> 4;
+    const int pbase = phase * 32 * S::ROW_BYTES;
+    // K operand: row = 32*phase + l32, chunk (2kk + hi) ^ (row & 15)
     const int y = lane & 15;
 #pragma unroll
     for (int k7 = 0; k7 < 8; ++k7)
-      kofs[k7] = l32 * S::ROW_BYTES + ((k7 ^ (y >> 1)) << 5) + ((hi ^ (y & 1)) << 4);
-  }
-  // V^T operand: row = 32*phase + 16ks + 4*hi + i16/4 (+8), chunk (4mb + c) ^ 4x.
-  int vofs[4];
-  {
+      ws.kofs[k7] = pbase + l32 * S::ROW_BYTES + ((k7 ^ (y >> 1)) << 5) + ((hi ^ (y & 1)) << 4);
+    // V^T operand: row = 32*phase + 16ks + 4*hi + i16/4 (+8), chunk (4mb + c) ^ 4x
     const int x = (i16 >> 2) & 3;
     const int c = (g16 & 1) * 2 + ((i16 & 3) >> 1);
 #pragma unroll
     for (int m3 = 0; m3 < 4; ++m3)
-      vofs[m3] = (hi * 4 + (i16 >> 2)) * S::ROW_BYTES + ((4 * (m3 ^ x) + c) << 4) + (i16 & 1) * 8;
+      ws.vofs[m3] =
+          S::VBASE + pbase + (hi * 4 + (i16 >> 2)) * S::ROW_BYTES + ((4 * (m3 ^ x) + c) << 4) + (i16 & 1) * 8;
   }
 
-  for (int st = 0; st < nst; ++st) {
-    // stage st has landed once at most the younger stages' loads are outstanding
-    if (S::NSTAGE == 3 && st + 1 < nst)
-      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * S::LOADS_PER_WAVE) : "memory");
-    else
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    if (st + S::NSTAGE - 1 < nst) v2_issue_stage<D>(smem, krs, vrs, koff, voff, w, st + S::NSTAGE - 1, kv_row_bytes);
-
-    const int k0 = st * S::ST + phase * 32;
-    if (k0 > wave_max_tok) continue;
-    const unsigned char* kt = smem + (st % S::NSTAGE) * S::STAGE_BYTES;
-    const unsigned char* vt = kt + S::TILE_BYTES;
-
-    f32x16_t s;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) s[i] = 0.f;
-    {
-      const unsigned char* kr = kt + phase * 32 * S::ROW_BYTES;
-#pragma unroll
-      for (int kk = 0; kk < D / 16; ++kk) {
-        const bf16x8_t a = *(const bf16x8_t*)(kr + kofs[kk & 7] + ((kk & 8) << 5));
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], s, 0, 0, 0);
-      }
-    }
-    const bool need_mask = (k0 + 31 > wave_min_tok) || (k0 + 32 > n);
-    float mloc = kNegBig;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      float x = s[i] * sl2;
-      if (need_mask) {
-        const int key = k0 + (i >> 2) * 8 + hi * 4 + (i & 3);
-        if (key > my_tok || key >= n) x = -INFINITY;
-      }
-      s[i] = x;
-      mloc = fmaxf(mloc, x);
-    }
-    {
-      auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(mloc), __float_as_uint(mloc), false, false);
-      mloc = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-    }
-    const float m_new = fmaxf(m_run, mloc);
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-    float lsum = 0.f;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const float pv = __builtin_amdgcn_exp2f(s[i] - m_new);
-      s[i] = pv;
-      lsum += pv;
-    }
-    l_run = l_run * alpha + lsum;
-    m_run = m_new;
-    if (!__all(alpha == 1.0f)) {
-#pragma unroll
-      for (int mb = 0; mb < D / 32; ++mb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) o[mb][i] *= alpha;
-    }
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      u32x4_t pk;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) pk[j] = pack_bf16x2(s[ks * 8 + 2 * j], s[ks * 8 + 2 * j + 1]);
-      const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, pk);
-      // V^T fragment rows: keys 16ks + 4(lane/32) + (lane%16)/4 (+8 for slots 4..7)
-      const unsigned char* vr = vt + (phase * 32 + ks * 16) * S::ROW_BYTES;
-#pragma unroll
-      for (int mb = 0; mb < D / 32; ++mb) {
-        const unsigned char* a1 = vr + vofs[mb & 3] + ((mb & 4) << 6);
-        const unsigned char* a2 = a1 + 8 * S::ROW_BYTES;
-        const i16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)a1);
-        const i16x4_t v2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)a2);
-        const u32x4_t av = {__builtin_bit_cast(u32x2_t, v1)[0], __builtin_bit_cast(u32x2_t, v1)[1],
-                            __builtin_bit_cast(u32x2_t, v2)[0], __builtin_bit_cast(u32x2_t, v2)[1]};
-        o[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, av), pb, o[mb], 0, 0, 0);
-      }
-    }
+  // ---- main loop, unrolled over the stage buffers -----------------------------
+  for (int st0 = 0; st0 < nst; st0 += S::NSTAGE) {
+    v2_step<D, 0>(smem, ws, krs, vrs, koff, voff, w, st0, nst, kv_row_bytes, phase, wave_min_tok, wave_max_tok,
+                  my_lim_tok, n, sl2, hi);
+    if (st0 + 1 < nst)
+      v2_step<D, 1>(smem, ws, krs, vrs, koff, voff, w, st0 + 1, nst, kv_row_bytes, phase, wave_min_tok,
+                    wave_max_tok, my_lim_tok, n, sl2, hi);
+    if (S::NSTAGE == 3 && st0 + 2 < nst)
+      v2_step<D, (S::NSTAGE == 3 ? 2 : 0)>(smem, ws, krs, vrs, koff, voff, w, st0 + 2, nst, kv_row_bytes, phase,
+                                           wave_min_tok, wave_max_tok, my_lim_tok, n, sl2, hi);
   }
 
   // ---- merge the two phases of each row group --------------------------------
@@ -311,23 +354,25 @@ __global__ __launch_bounds__(512) void prefill_v2_kernel(const PrefillParams p) 
 #pragma unroll
     for (int mb = 0; mb < D / 32; ++mb)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) xo[((rg * (D / 32) + mb) * 16 + i) * 64 + lane] = o[mb][i];
-    ml_x[rg][lane][0] = m_run;
-    ml_x[rg][lane][1] = l_run;
+      for (int i = 0; i < 16; ++i) xo[((rg * (D / 32) + mb) * 16 + i) * 64 + lane] = ws.o[mb][i];
+    ml_x[rg][lane][0] = ws.m_run;
+    ml_x[rg][lane][1] = ws.l_run;
   }
   __syncthreads();
   if (phase == 1) return;
+  float l_run;
   {
     const float m1 = ml_x[rg][lane][0];
     const float l1 = ml_x[rg][lane][1];
-    const float mt = fmaxf(m_run, m1);
-    const float a0 = __builtin_amdgcn_exp2f(m_run - mt);
+    const float mt = fmaxf(ws.m_run, m1);
+    const float a0 = __builtin_amdgcn_exp2f(ws.m_run - mt);
     const float a1 = __builtin_amdgcn_exp2f(m1 - mt);
-    l_run = l_run * a0 + l1 * a1;
+    l_run = ws.l_run * a0 + l1 * a1;
 #pragma unroll
     for (int mb = 0; mb < D / 32; ++mb)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) o[mb][i] = o[mb][i] * a0 + xo[((rg * (D / 32) + mb) * 16 + i) * 64 + lane] * a1;
+      for (int i = 0; i < 16; ++i)
+        ws.o[mb][i] = ws.o[mb][i] * a0 + xo[((rg * (D / 32) + mb) * 16 + i) * 64 + lane] * a1;
   }
 
   // ---- epilogue: normalise, gate, store -------------------------------------
@@ -348,7 +393,7 @@ __global__ __launch_bounds__(512) void prefill_v2_kernel(const PrefillParams p) 
       const int dm = mb * 32 + ig * 8 + hi * 4;
       float y[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) y[j] = o[mb][ig * 4 + j] * inv_l;
+      for (int j = 0; j < 4; ++j) y[j] = ws.o[mb][ig * 4 + j] * inv_l;
       if (GATE == 2) {
         const u32x2_t z = *(const u32x2_t*)(p.gate + row_off * D + dm);
         y[0] *= sigmoid_f32(lo_bf16(z[0]));
