@@ -35,9 +35,100 @@ def parse():
     ap.add_argument("--workload", default="qwen35_0p8b_prefill",
                     help="prefill workload to time (default: the headline one)")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true", help="decode only (for counter runs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--decode-steps", type=int, default=20)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy (reference for HBM byte counters)")
+    ap.add_argument("--record-traffic", nargs=6,
+                    metavar=("KERNEL", "WORKLOAD", "FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
+                    help="write profiles/hbm_traffic.json from rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE "
+                         "counter_collection.csv files of a bench run and of a --copy-calibration run")
     return ap.parse_args()
+
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(ROOT, "gated_gqa_softmax_amd", "csrc")
+KERNEL_SOURCES = {
+    "prefill_v2_kernel": ["ga_prefill_v2.hip", "ga_common.hpp", "ga_internal.hpp"],
+    "decode_partials_kernel": ["ga_decode.hip", "ga_common.hpp", "ga_internal.hpp"],
+}
+
+
+def source_digest(kernel: str) -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from profiles/hbm_traffic.json (rocprofv3 FETCH_SIZE and
+    WRITE_SIZE scaled by a plain copy of known size), or None when the record is
+    missing or was measured on a different version of the kernel's source."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)[f"{kernel}@{workload}"]
+    except (OSError, KeyError, ValueError):
+        return None
+    if rec.get("source_sha256") != source_digest(kernel):
+        return None
+    return rec["fetch_kib"] * 1024 * rec["fetch_scale"] + rec["write_kib"] * 1024 * rec["write_scale"]
+
+
+COPY_BYTES = 1 << 30
+COPY_KERNEL = "neg_kernel"
+
+
+def copy_calibration(torch):
+    """A plain elementwise pass (y = -x, bf16) that reads and writes COPY_BYTES each."""
+    src = torch.empty(COPY_BYTES // 2, dtype=torch.bfloat16, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_read": COPY_BYTES, "copy_calibration_bytes_written": COPY_BYTES,
+                      "launches": 5}))
+
+
+def counter_per_dispatch(csv_path: str, kernel: str, counter: str) -> float:
+    """Mean over dispatches of one rocprofv3 counter (summed over its instances)
+    for the kernels whose name contains `kernel`."""
+    import csv
+    per = {}
+    with open(csv_path) as f:
+        for r in csv.DictReader(f):
+            if kernel in r["Kernel_Name"] and r["Counter_Name"] == counter:
+                per[r["Dispatch_Id"]] = per.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
+    if not per:
+        raise SystemExit(f"{csv_path}: no {counter} rows for a kernel named *{kernel}*")
+    return sum(per.values()) / len(per)
+
+
+def record_traffic(kernel, workload, fetch_csv, write_csv, copy_fetch_csv, copy_write_csv):
+    fetch = counter_per_dispatch(fetch_csv, kernel, "FETCH_SIZE")
+    write = counter_per_dispatch(write_csv, kernel, "WRITE_SIZE")
+    cf = counter_per_dispatch(copy_fetch_csv, COPY_KERNEL, "FETCH_SIZE")
+    cw = counter_per_dispatch(copy_write_csv, COPY_KERNEL, "WRITE_SIZE")
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    try:
+        with open(path) as f:
+            db = json.load(f)
+    except (OSError, ValueError):
+        db = {}
+    rec = {"source_sha256": source_digest(kernel), "fetch_kib": fetch, "write_kib": write,
+           "fetch_scale": COPY_BYTES / 1024 / cf, "write_scale": COPY_BYTES / 1024 / cw,
+           "copy_fetch_kib": cf, "copy_write_kib": cw, "copy_bytes": COPY_BYTES}
+    rec["bytes_per_launch"] = fetch * 1024 * rec["fetch_scale"] + write * 1024 * rec["write_scale"]
+    db[f"{kernel}@{workload}"] = rec
+    with open(path, "w") as f:
+        json.dump(db, f, indent=1, sort_keys=True)
+        f.write("\n")
+    print(json.dumps({f"{kernel}@{workload}": rec}))
 
 
 def time_prefill(torch, api, inputs, accounting, wname, steps, warmup):
@@ -149,12 +240,13 @@ def time_decode(torch, api, inputs, accounting, steps, warmup):
         "bytes_per_step": total_bytes,
         "roofline": {"bound": "hbm", "kernel": "decode_partials_kernel", "achieved": part_bytes / (part_ms * 1e-3) / 1e9,
                      "peak": MI355X_HBM_GBS, "unit": "GB/s",
-                     "frac": part_bytes / (part_ms * 1e-3) / 1e9 / MI355X_HBM_GBS, "traffic": None,
+                     "frac": part_bytes / (part_ms * 1e-3) / 1e9 / MI355X_HBM_GBS,
+                     "traffic": measured_traffic("decode_partials_kernel", w.name),
                      "kernel_ms": part_ms, "algorithmic_bytes": part_bytes},
     }
 
 
-def cpu_baseline(w, x, flops, budget_s=12.0):
+def cpu_baseline(w, x, flops, budget_s=15.0):
     """The CPU oracle, as it stands, on the whole prefill workload, repeated
     until about budget_s seconds of work (at least once)."""
     from oracle import attention as oracle
@@ -171,7 +263,7 @@ def cpu_baseline(w, x, flops, budget_s=12.0):
                        k_norm_w=x["k_norm_w"], positions=x["positions"], rms_eps=w.rms_eps, rope_base=w.rope_base,
                        rot_dim=w.rot_dim)
         times.append(time.perf_counter() - t0)
-        if time.perf_counter() - t_start > budget_s or len(times) >= 8:
+        if time.perf_counter() - t_start > budget_s:
             break
     t = float(np.median(times))
     cpu = ""
@@ -189,6 +281,9 @@ def cpu_baseline(w, x, flops, budget_s=12.0):
 
 def main():
     args = parse()
+    if args.record_traffic:
+        record_traffic(*args.record_traffic)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(multi-GPU sharding of this path is design-only)", file=sys.stderr)
@@ -199,6 +294,13 @@ def main():
         sys.exit(2)
     from gated_gqa_softmax_amd import accounting, api, inputs
 
+    if args.copy_calibration:
+        copy_calibration(torch)
+        return
+    if args.no_prefill:
+        dec = time_decode(torch, api, inputs, accounting, args.decode_steps, args.warmup)
+        print(json.dumps({"decode": dec}), flush=True)
+        return
     pre = time_prefill(torch, api, inputs, accounting, args.workload, args.steps, args.warmup)
     w = pre["w"]
     achieved = pre["flops"] / (pre["attn_ms"] * 1e-3) / 1e12
@@ -218,9 +320,10 @@ def main():
         "config": {"workload": w.name, "batch": w.batch, "seq_len": w.seq_len, "n_q_heads": w.n_q_heads,
                    "n_kv_heads": w.n_kv_heads, "head_dim": w.head_dim, "rot_dim": w.rot_dim, "gate": w.gate_mode,
                    "parallelism": "single-gpu"},
-        "roofline": {"bound": "mfma", "kernel": "prefill_mfma_kernel", "achieved": achieved,
+        "roofline": {"bound": "mfma", "kernel": "prefill_v2_kernel", "achieved": achieved,
                      "peak": MI355X_BF16_DENSE_TFLOPS, "unit": "TFLOP/s", "frac": achieved / MI355X_BF16_DENSE_TFLOPS,
-                     "traffic": None, "kernel_ms": pre["attn_ms"], "algorithmic_flops": pre["flops"]},
+                     "traffic": measured_traffic("prefill_v2_kernel", w.name), "kernel_ms": pre["attn_ms"],
+                     "algorithmic_flops": pre["flops"]},
     }
     if not args.no_decode:
         rec["decode"] = time_decode(torch, api, inputs, accounting, args.decode_steps, args.warmup)
