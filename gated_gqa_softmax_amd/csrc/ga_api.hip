@@ -72,8 +72,11 @@ bool prefill_v2_ok(const ga_attn_desc* d, int32_t k_cap, int32_t v_cap) {
   const int grp = d->n_q_heads / d->n_kv_heads;
   const int hd = d->head_dim;
   const long long row = 2LL * d->n_kv_heads * hd;
-  return d->dtype == GA_BF16 && (hd == 128 || hd == 256) && d->rot_dim % 16 == 0 && grp <= 64 &&
-         row * k_cap < (1LL << 31) && row * v_cap < (1LL << 31);
+  // the q prologue keeps every RoPE pair inside one quarter of the row and
+  // tables (cos, sin) for the 2 * (64 / grp) tokens of a workgroup
+  const int tb = grp <= 64 ? 64 / grp : 0;
+  return d->dtype == GA_BF16 && (hd == 128 || hd == 256) && d->rot_dim % 16 == 0 && d->rot_dim <= hd / 4 &&
+         grp <= 64 && 2 * tb * (d->rot_dim / 2) <= 2048 && row * k_cap < (1LL << 31) && row * v_cap < (1LL << 31);
 }
 
 bool prefill_fast(const ga_attn_desc* d) {

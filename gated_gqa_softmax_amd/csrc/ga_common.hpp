@@ -50,10 +50,11 @@ template <> struct Elem<uint16_t> {  // bf16 bits
 
 // ---- arithmetic ------------------------------------------------------------
 
-// Logistic sigmoid in fp32: 1/(1 + 2^(-z*log2 e)). z = 0 gives exactly 0.5;
-// z >= 100 gives exactly 1; z <= -100 gives 0.
+// Logistic sigmoid in fp32: 1/(1 + 2^(-z*log2 e)) with the hardware
+// reciprocal (about 1 ulp). z = 0 gives exactly 0.5; z >= 100 gives exactly
+// 1; z <= -100 gives 0.
 __device__ __forceinline__ float sigmoid_f32(float z) {
-  return 1.0f / (1.0f + __builtin_amdgcn_exp2f(-z * kLog2e));
+  return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-z * kLog2e));
 }
 
 // cos/sin of pos * inv_freq: the product and the reduction to [-pi, pi] are
@@ -89,6 +90,53 @@ __device__ __forceinline__ float max_xor(float x) {
   return x;
 }
 
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+
+// Raw buffer resource: 48-bit base, stride 0, num_bytes readable bytes (loads
+// at or past num_bytes return zeros), dword 3 = 0x00020000 as for the
+// library's other buffer loads. The values are wave-uniform (scalar).
+__device__ __forceinline__ i32x4_t buffer_desc(const void* base, uint32_t num_bytes) {
+  const unsigned long long a = (unsigned long long)base;
+  i32x4_t r;
+  r[0] = __builtin_amdgcn_readfirstlane((int)(a & 0xffffffffu));
+  r[1] = __builtin_amdgcn_readfirstlane((int)((a >> 32) & 0xffffu));
+  r[2] = __builtin_amdgcn_readfirstlane((int)num_bytes);
+  r[3] = 0x00020000;
+  return r;
+}
+
+// 16 bytes per lane from byte offset voffset of the buffer straight into LDS
+// at lds_base + 16 * lane (lds_base wave-uniform). Written as inline asm so
+// the compiler does not track it: a tracked LDS write of unknown extent makes
+// the compiler wait for it before every later LDS access, which would
+// serialise the loads with the compute they should overlap. The caller waits
+// with s_waitcnt vmcnt and a barrier before the data is read.
+__device__ __forceinline__ void buffer_load_lds16(i32x4_t rsrc, uint32_t lds_base, int voffset) {
+  asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+               :
+               : "v"(voffset), "s"(rsrc), "{m0}"(lds_base)
+               : "memory");
+}
+
+// LDS byte address of a pointer into a __shared__ array.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// Sum over the 4 lanes of a quad (lanes 4k..4k+3), all lanes active: two
+// DPP quad permutations (xor 1, xor 2), no LDS traffic.
+__device__ __forceinline__ float quad_sum(float x) {
+  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, true));
+  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, true));
+  return x;
+}
+
+// Workgroup barrier for LDS traffic only: the wave's LDS operations complete
+// before it, while its global loads (including loads into LDS, which the
+// caller waits for with an explicit vmcnt) stay in flight. __syncthreads()
+// would also wait for every outstanding global load.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 // Value of lane (l ^ 32) via v_permlane32_swap (gfx950).
 __device__ __forceinline__ float swap_half(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -104,7 +152,8 @@ namespace ga {
 
 // RMSNorm + partial RoPE of one row chunk held in registers. Rows occupy
 // aligned groups of LPR = D/8 lanes; lane c of a group holds elements
-// [8c, 8c+8) in x. ``w`` may be null (no norm); ``rot`` = 0 skips RoPE.
+// [8c, 8c+8) in x. ``w`` points at the 8 norm weights of that chunk, or is
+// null (no norm); ``rot`` = 0 skips RoPE.
 // ``cs_row`` (optional) holds (cos, sin) for pair index t of this row's
 // position; otherwise they are computed from ``inv_freq``.
 template <int D, typename FreqT>
@@ -118,7 +167,7 @@ __device__ __forceinline__ void norm_rope_chunk(float x[8], int c, const float* 
   if (w) {
     const float inv = 1.0f / sqrtf(ss / (float)D + eps);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) x[j] = x[j] * inv * w[c * 8 + j];
+    for (int j = 0; j < 8; ++j) x[j] = x[j] * inv * w[j];
   }
   if (rot > 0) {
     const int half = rot >> 1;

@@ -60,7 +60,7 @@ __global__ __launch_bounds__(256) void decode_partials_kernel(const DecodeParams
     if (r < GRP) raw = *(const u32x4_t*)(p.q + ((long)b * p.H + g * GRP + r) * D + c * 8);
     float x[8];
     unpack8(raw, x);
-    norm_rope_chunk<D>(x, c, p.wq, p.eps, p.rot, L, p.inv_freq, nullptr);
+    norm_rope_chunk<D>(x, c, p.wq ? p.wq + c * 8 : nullptr, p.eps, p.rot, L, p.inv_freq, nullptr);
     *(u32x4_t*)(Qs + r * SQ + c * 8) = pack8(x);
   }
   __syncthreads();
@@ -246,7 +246,8 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(const DecodeParams p)
                                  : *(const u32x4_t*)(p.k_new + ((long)b * p.G + g) * D + c * 8);
     float x[8];
     unpack8(raw, x);
-    norm_rope_chunk<D>(x, c, r == 0 ? p.wq : p.wk, p.eps, p.rot, L, p.inv_freq, nullptr);
+    const float* nw = (r == 0) ? p.wq : p.wk;
+    norm_rope_chunk<D>(x, c, nw ? nw + c * 8 : nullptr, p.eps, p.rot, L, p.inv_freq, nullptr);
     const u32x4_t pk = pack8(x);
     float xr[8];
     unpack8(pk, xr);

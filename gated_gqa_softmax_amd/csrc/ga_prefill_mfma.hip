@@ -182,7 +182,7 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(const PrefillParams p
       float x[8];
       unpack8(raw, x);
       const int pos = valid ? (p.positions ? p.positions[(long)b * n + tok] : tok) : 0;
-      norm_rope_chunk<D>(x, c, p.wq, p.eps, p.rot, pos, p.inv_freq,
+      norm_rope_chunk<D>(x, c, p.wq ? p.wq + c * 8 : nullptr, p.eps, p.rot, pos, p.inv_freq,
                          p.use_table ? table + tt * half : nullptr);
       *(u32x4_t*)(smem + r * S::SK + c * 8) = pack8(x);
     }

@@ -70,8 +70,10 @@ struct V2Wave {
   bf16x8_t qf[D / 16];   // Q^T operand fragments of this wave's 32 rows
   f32x16_t o[D / 32];    // O^T accumulators
   float m_run, l_run;    // reference max (log2 domain) and lane-partial row sum
-  int kofs[8];           // K operand LDS addresses (lane part, phase included)
-  int vofs[4];           // V^T operand LDS addresses (lane part, phase and V base included)
+  int kbase;             // K operand LDS address of step 0 (lane part, phase included);
+                         // step kk reads kbase ^ ((kk & 7) << 5), + 256 for kk >= 8
+  int vbase;             // V^T operand LDS address of dim block 0 (lane part, phase and
+                         // V base included); dim block mb reads vbase ^ ((mb & 3) << 6), + 256 for mb >= 4
 };
 
 // Q staging rows: 0-63 in K buffer NSTAGE-1, 64-127 in V buffer NSTAGE-1.
@@ -86,36 +88,81 @@ __device__ __forceinline__ uint16_t* v2_qrow(unsigned char* smem, int r) {
 // 1 KB of LDS per instruction, lane l's 16 bytes at slot l. The whole byte
 // offset goes in the VGPR operand so the buffer range check sees it.
 template <int D, int BUF>
-__device__ __forceinline__ void v2_issue(unsigned char* smem, __amdgpu_buffer_rsrc_t krs, __amdgpu_buffer_rsrc_t vrs,
-                                         int koff, int voff, int w, int st, int kv_row_bytes) {
+__device__ __forceinline__ void v2_issue(unsigned char* smem, i32x4_t krs, i32x4_t vrs, int koff, int voff, int w,
+                                         int st, int kv_row_bytes) {
   typedef V2Shape<D> S;
-  unsigned char* kt = smem + BUF * S::TILE_BYTES;
-  unsigned char* vt = smem + S::VBASE + BUF * S::TILE_BYTES;
+  const uint32_t kt = lds_addr(smem + BUF * S::TILE_BYTES);
+  const uint32_t vt = lds_addr(smem + S::VBASE + BUF * S::TILE_BYTES);
   const int soff = st * S::ST * kv_row_bytes;
   const int jstep = 8 * S::ROWS_PER_LOAD * kv_row_bytes;
+  // opaque per call: each load adds its scalar offset instead of keeping one
+  // loop-invariant VGPR per load
+  asm volatile("" : "+v"(koff), "+v"(voff));
 #pragma unroll
   for (int j = 0; j < S::LOADS_PER_WAVE; ++j) {
     const int t = w + 8 * j;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (__attribute__((address_space(3))) void*)(kt + t * 1024), 16,
-                                             koff + soff + j * jstep, 0, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (__attribute__((address_space(3))) void*)(vt + t * 1024), 16,
-                                             voff + soff + j * jstep, 0, 0, 0);
+    buffer_load_lds16(krs, kt + t * 1024, koff + soff + j * jstep);
+    buffer_load_lds16(vrs, vt + t * 1024, voff + soff + j * jstep);
   }
 }
 
 // One 32-key tile (this wave's phase half of stage buffer BUF) for 32 rows.
+// Operand reads run KPF (K) and VPF (V^T) MFMAs ahead of their use, so LDS
+// latency overlaps the matrix pipe instead of stalling each MFMA.
 template <int D, int BUF>
 __device__ __forceinline__ void v2_tile(const unsigned char* smem, V2Wave<D>& ws, bool need_mask, int lim,
                                         float sl2) {
   typedef V2Shape<D> S;
+  constexpr int NK = D / 16;   // QK steps (16 dims each)
+  constexpr int NV = D / 16;   // PV MFMAs: 2 key halves x D/32 dim blocks
+  constexpr int KPF = (D == 256) ? 3 : 4;  // bounded by the register budget of d = 256
+  constexpr int VPF = (D == 256) ? 2 : 3;
+  int kb = ws.kbase, vb = ws.vbase;
+  // opaque per tile: the per-step addresses stay short-lived temporaries
+  asm volatile("" : "+v"(kb), "+v"(vb));
+  // each address is its own opaque value, so none is kept alive across the
+  // loop (the K steps kk and kk + 8 would otherwise share one register)
+  auto kread = [&](int kk) {
+    int a = kb ^ ((kk & 7) << 5);
+    asm volatile("" : "+v"(a));
+    return *(const bf16x8_t*)(smem + a + (BUF * S::TILE_BYTES + ((kk >> 3) << 8)));
+  };
+  // V^T fragment rows: keys 16ks + 4(lane/32) + (lane%16)/4 (+8 for slots 4..7)
+  auto vread = [&](int t) {
+    const int ks = t / (D / 32), mb = t % (D / 32);
+    int a = vb ^ ((mb & 3) << 6);
+    asm volatile("" : "+v"(a));
+    const unsigned char* a1 = smem + a + (BUF * S::TILE_BYTES + ((mb & 4) << 6) + ks * 16 * S::ROW_BYTES);
+    const i16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)a1);
+    const i16x4_t v2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(a1 + 8 * S::ROW_BYTES));
+    const u32x4_t av = {__builtin_bit_cast(u32x2_t, v1)[0], __builtin_bit_cast(u32x2_t, v1)[1],
+                        __builtin_bit_cast(u32x2_t, v2)[0], __builtin_bit_cast(u32x2_t, v2)[1]};
+    return __builtin_bit_cast(bf16x8_t, av);
+  };
+
+  bf16x8_t ka[NK];
   f32x16_t s;
 #pragma unroll
   for (int i = 0; i < 16; ++i) s[i] = 0.f;
 #pragma unroll
-  for (int kk = 0; kk < D / 16; ++kk) {
-    const bf16x8_t a = *(const bf16x8_t*)(smem + ws.kofs[kk & 7] + (BUF * S::TILE_BYTES + ((kk & 8) << 5)));
-    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, ws.qf[kk], s, 0, 0, 0);
+  for (int kk = 0; kk < KPF; ++kk) ka[kk] = kread(kk);
+#pragma unroll
+  for (int kk = 0; kk < NK; ++kk) {
+    if (kk + KPF < NK) ka[kk + KPF] = kread(kk + KPF);
+    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[kk], ws.qf[kk], s, 0, 0, 0);
   }
+  // keep that order: KPF reads ahead, then one MFMA per read
+  __builtin_amdgcn_sched_group_barrier(0x100, KPF, 0);
+#pragma unroll
+  for (int kk = 0; kk < NK - KPF; ++kk) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, KPF, 0);
+  // the first V^T operands do not depend on the softmax
+  bf16x8_t va[NV];
+#pragma unroll
+  for (int t = 0; t < VPF; ++t) va[t] = vread(t);
   if (need_mask) {
     // s[i] holds key k0 + 8(i/4) + 4hi + (i%4); visible iff 8(i/4) + (i%4) <= lim
 #pragma unroll
@@ -148,31 +195,33 @@ __device__ __forceinline__ void v2_tile(const unsigned char* smem, V2Wave<D>& ws
     lsum += pv;
   }
   ws.l_run += lsum;
+  bf16x8_t pb[2];
 #pragma unroll
   for (int ks = 0; ks < 2; ++ks) {
     u32x4_t pk;
 #pragma unroll
     for (int j = 0; j < 4; ++j) pk[j] = pack_bf16x2(s[ks * 8 + 2 * j], s[ks * 8 + 2 * j + 1]);
-    const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, pk);
-#pragma unroll
-    for (int mb = 0; mb < D / 32; ++mb) {
-      // V^T fragment rows: keys 16ks + 4(lane/32) + (lane%16)/4 (+8 for slots 4..7)
-      const unsigned char* a1 =
-          smem + ws.vofs[mb & 3] + (BUF * S::TILE_BYTES + ((mb & 4) << 6) + ks * 16 * S::ROW_BYTES);
-      const i16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)a1);
-      const i16x4_t v2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(a1 + 8 * S::ROW_BYTES));
-      const u32x4_t av = {__builtin_bit_cast(u32x2_t, v1)[0], __builtin_bit_cast(u32x2_t, v1)[1],
-                          __builtin_bit_cast(u32x2_t, v2)[0], __builtin_bit_cast(u32x2_t, v2)[1]};
-      ws.o[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, av), pb, ws.o[mb], 0, 0, 0);
-    }
+    pb[ks] = __builtin_bit_cast(bf16x8_t, pk);
   }
+#pragma unroll
+  for (int t = 0; t < NV; ++t) {
+    if (t + VPF < NV) va[t + VPF] = vread(t + VPF);
+    const int ks = t / (D / 32), mb = t % (D / 32);
+    ws.o[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[t], pb[ks], ws.o[mb], 0, 0, 0);
+  }
+  // one MFMA, then the two transposed reads of the operand VPF steps ahead
+#pragma unroll
+  for (int t = 0; t < NV - VPF; ++t) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, VPF, 1);
 }
 
 // One pipeline step: wait for stage st (buffer BUF), refill the buffer freed
 // by the previous step, and run this wave's tile if it has visible keys.
 template <int D, int BUF>
-__device__ __forceinline__ void v2_step(unsigned char* smem, V2Wave<D>& ws, __amdgpu_buffer_rsrc_t krs,
-                                        __amdgpu_buffer_rsrc_t vrs, int koff, int voff, int w, int st, int nst,
+__device__ __forceinline__ void v2_step(unsigned char* smem, V2Wave<D>& ws, i32x4_t krs, i32x4_t vrs, int koff, int voff, int w, int st, int nst,
                                         int kv_row_bytes, int phase, int wave_min_tok, int wave_max_tok,
                                         int my_lim_tok, int n, float sl2, int hi) {
   typedef V2Shape<D> S;
@@ -180,7 +229,7 @@ __device__ __forceinline__ void v2_step(unsigned char* smem, V2Wave<D>& ws, __am
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * S::LOADS_PER_WAVE) : "memory");
   else
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
+  lds_barrier();
   if (st + S::NSTAGE - 1 < nst)
     v2_issue<D, (BUF + S::NSTAGE - 1) % S::NSTAGE>(smem, krs, vrs, koff, voff, w, st + S::NSTAGE - 1, kv_row_bytes);
   const int k0 = st * S::ST + phase * 32;
@@ -190,11 +239,25 @@ __device__ __forceinline__ void v2_step(unsigned char* smem, V2Wave<D>& ws, __am
   }
 }
 
+// RoPE of the first 2*HALF elements of a row held in x[0, N): pairs
+// (t, t + HALF) rotated by (cos, sin) = cs[t].
+template <int N, int HALF>
+__device__ __forceinline__ void rope_quarter(float* x, const float2* cs) {
+  static_assert(2 * HALF <= N, "rotated dims must lie in the lane's quarter");
+#pragma unroll
+  for (int t = 0; t < HALF; ++t) {
+    const float2 e = cs[t];
+    const float a = x[t], c = x[t + HALF];
+    x[t] = a * e.x - c * e.y;
+    x[t + HALF] = c * e.x + a * e.y;
+  }
+}
+
 template <int D, int GATE>
 __global__ __launch_bounds__(512) void prefill_v2_kernel(const PrefillParams p) {
   typedef V2Shape<D> S;
   __shared__ __attribute__((aligned(1024))) unsigned char smem[S::BUF_BYTES];
-  __shared__ float2 table[1024];
+  __shared__ float2 table[2048];
   __shared__ float ml_x[4][64][2];
 
   const int tid = threadIdx.x;
@@ -245,10 +308,8 @@ __global__ __launch_bounds__(512) void prefill_v2_kernel(const PrefillParams p) 
   // as zeros (out-of-range buffer loads return 0), which the mask then hides.
   const int kv_row_bytes = p.G * D * 2;
   const uint32_t valid_bytes = (uint32_t)((n - 1) * kv_row_bytes + D * 2);
-  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(p.khat + (long)b * p.k_bstride + (long)g * D), (short)0, (int)valid_bytes, 0x00020000);
-  const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(p.v + (long)b * p.v_bstride + (long)g * D), (short)0, (int)valid_bytes, 0x00020000);
+  const i32x4_t krs = buffer_desc(p.khat + (long)b * p.k_bstride + (long)g * D, valid_bytes);
+  const i32x4_t vrs = buffer_desc(p.v + (long)b * p.v_bstride + (long)g * D, valid_bytes);
   int koff, voff;
   {
     // load j covers rows row0 + 8j*ROWS_PER_LOAD (multiples of 16 apart): same swizzle
@@ -258,51 +319,102 @@ __global__ __launch_bounds__(512) void prefill_v2_kernel(const PrefillParams p) 
     voff = row0 * kv_row_bytes + ((ph ^ swz_v(row0)) << 4);
   }
 
-  if (nst > 0) v2_issue<D, 0>(smem, krs, vrs, koff, voff, w, 0, kv_row_bytes);
-  if (S::NSTAGE == 3 && nst > 1) v2_issue<D, 1>(smem, krs, vrs, koff, voff, w, 1, kv_row_bytes);
 
   // ---- Q prologue: RMSNorm + RoPE of 128 rows into LDS ------------------------
+  // Four adjacent lanes per row; lane quarter qq holds elements
+  // [qq*D/4, qq*D/4 + D/4). The RoPE pairs (t, t + rot/2) with rot <= D/4 all
+  // sit in quarter 0, and the row's sum of squares takes two quad shuffles.
+  // The q reads go out before the K/V stage loads, so waiting for them leaves
+  // the stage loads in flight (loads complete in issue order).
+  constexpr int QE = D / 4;
   const int half = p.half;
-  if (p.use_table) {
-    for (int e = tid; e < 2 * TB * half; e += 512) {
-      const int side = e / (TB * half);
-      const int rem = e - side * TB * half;
-      const int tt = rem / half;
-      const int t = rem - tt * half;
-      const int blk = side ? blk_heavy : blk_light;
-      const int tok = blk * TB + tt;
-      const int pos = (blk >= 0 && tok < n) ? (p.positions ? p.positions[(long)b * n + tok] : tok) : 0;
+  const int qrow = tid >> 2;  // 0..127
+  const int qq = tid & 3;
+  const int qside = qrow >> 6;
+  const int qtt = (qrow & 63) % TB;
+  u32x4_t qraw[QE / 8];
+  {
+    const int qblk = qside ? blk_heavy : blk_light;
+    const int qhh = (qrow & 63) / TB;
+    const int qtok = qblk * TB + qtt;
+    const bool qvalid = (qblk >= 0) && (qhh < p.grp) && (qtok < n);
+    // unconditional (a branch around the loads would make the wave wait for
+    // them at its join): rows outside the block read row 0 and are never stored
+    const uint16_t* src =
+        p.q + (((long)b * n + (qvalid ? qtok : 0)) * p.H + g * p.grp + (qvalid ? qhh : 0)) * D + qq * QE;
+#pragma unroll
+    for (int i = 0; i < QE / 8; ++i) qraw[i] = *(const u32x4_t*)(src + 8 * i);
+  }
+  f32x4_t qw[QE / 4];
+  if (p.wq) {
+#pragma unroll
+    for (int i = 0; i < QE / 4; ++i) qw[i] = *(const f32x4_t*)(p.wq + qq * QE + 4 * i);
+  }
+
+  // table inputs: up to 4 (token, pair) entries per thread
+  constexpr int TPT = 4;  // 2 * TB * half <= 2048 = TPT * 512 (checked on the host)
+  int tpos[TPT];
+  double tfreq[TPT];
+  // (loads unconditional, indices clamped; only entries e < 2 * TB * half are stored)
+#pragma unroll
+  for (int k = 0; k < TPT; ++k) {
+    const int e = half > 0 ? min(tid + 512 * k, 2 * TB * half - 1) : 0;
+    const int side = half > 0 ? e / (TB * half) : 0;
+    const int rem = e - side * TB * half;
+    const int tt = half > 0 ? rem / half : 0;
+    const int t = rem - tt * half;
+    const int blk = side ? blk_heavy : blk_light;
+    const int tok = (blk >= 0 && blk * TB + tt < n) ? blk * TB + tt : 0;
+    tpos[k] = p.positions ? p.positions[(long)b * n + tok] : tok;
+    tfreq[k] = p.inv_freq[t];
+  }
+
+  // (cos, sin) per (token of the two blocks, pair index), shared by the group's heads
+#pragma unroll
+  for (int k = 0; k < TPT; ++k) {
+    const int e = tid + 512 * k;
+    if (e < 2 * TB * half) {
       float c, s;
-      rope_cos_sin(pos, p.inv_freq[t], &c, &s);
+      rope_cos_sin(tpos[k], tfreq[k], &c, &s);
       table[e] = make_float2(c, s);
     }
-    __syncthreads();
   }
+  // The first stage loads go out only now: every load above has been consumed,
+  // so no later wait of the compiler (which does not count these loads) can
+  // end up waiting for them.
+  if (nst > 0) v2_issue<D, 0>(smem, krs, vrs, koff, voff, w, 0, kv_row_bytes);
+  if (S::NSTAGE == 3 && nst > 1) v2_issue<D, 1>(smem, krs, vrs, koff, voff, w, 1, kv_row_bytes);
+  lds_barrier();
   {
-    constexpr int LPR = D / 8;
-    constexpr int RPI = 64 / LPR;
-    const int c = lane % LPR;
-    const int rsub = lane / LPR;
-    for (int it = 0; it < 16 / RPI; ++it) {
-      const int r = w * 16 + it * RPI + rsub;      // 0..127
-      const int side = r >> 6;
-      const int blk = side ? blk_heavy : blk_light;
-      const int local = r & 63;
-      const int hh = local / TB;
-      const int tt = local - hh * TB;
-      const int tok = blk * TB + tt;
-      const bool valid = (blk >= 0) && (hh < p.grp) && (tok < n);
-      u32x4_t raw = {0, 0, 0, 0};
-      if (valid) raw = *(const u32x4_t*)(p.q + (((long)b * n + tok) * p.H + g * p.grp + hh) * D + c * 8);
-      float x[8];
-      unpack8(raw, x);
-      const int pos = valid ? (p.positions ? p.positions[(long)b * n + tok] : tok) : 0;
-      norm_rope_chunk<D>(x, c, p.wq, p.eps, p.rot, pos, p.inv_freq,
-                         p.use_table ? table + (side * TB + tt) * half : nullptr);
-      *(u32x4_t*)(v2_qrow<D>(smem, r) + c * 8) = pack8(x);
+    float x[QE];
+#pragma unroll
+    for (int i = 0; i < QE / 8; ++i) unpack8(qraw[i], x + 8 * i);
+    if (p.wq) {
+      float ss = 0.f;
+#pragma unroll
+      for (int e = 0; e < QE; ++e) ss += x[e] * x[e];
+      ss = quad_sum(ss);
+      const float inv = rsqrtf(ss * (1.0f / D) + p.eps);
+#pragma unroll
+      for (int e = 0; e < QE; ++e) x[e] *= inv * qw[e / 4][e % 4];
     }
+    if (qq == 0) {
+      const float2* cs = table + (qside * TB + qtt) * half;
+      // half % 8 == 0 and 2 * half <= D/4 (checked on the host)
+      if (half == 8) rope_quarter<QE, 8>(x, cs);
+      if (half == 16) rope_quarter<QE, 16>(x, cs);
+      if constexpr (QE >= 48) {
+        if (half == 24) rope_quarter<QE, 24>(x, cs);
+      }
+      if constexpr (QE >= 64) {
+        if (half == 32) rope_quarter<QE, 32>(x, cs);
+      }
+    }
+    uint16_t* dst = v2_qrow<D>(smem, qrow) + qq * QE;
+#pragma unroll
+    for (int i = 0; i < QE / 8; ++i) *(u32x4_t*)(dst + 8 * i) = pack8(x + 8 * i);
   }
-  __syncthreads();
+  lds_barrier();
 
   V2Wave<D> ws;
   {
@@ -323,16 +435,11 @@ __global__ __launch_bounds__(512) void prefill_v2_kernel(const PrefillParams p) 
     const int pbase = phase * 32 * S::ROW_BYTES;
     // K operand: row = 32*phase + l32, chunk (2kk + hi) ^ (row & 15)
     const int y = lane & 15;
-#pragma unroll
-    for (int k7 = 0; k7 < 8; ++k7)
-      ws.kofs[k7] = pbase + l32 * S::ROW_BYTES + ((k7 ^ (y >> 1)) << 5) + ((hi ^ (y & 1)) << 4);
+    ws.kbase = pbase + l32 * S::ROW_BYTES + ((y >> 1) << 5) + ((hi ^ (y & 1)) << 4);
     // V^T operand: row = 32*phase + 16ks + 4*hi + i16/4 (+8), chunk (4mb + c) ^ 4x
     const int x = (i16 >> 2) & 3;
     const int c = (g16 & 1) * 2 + ((i16 & 3) >> 1);
-#pragma unroll
-    for (int m3 = 0; m3 < 4; ++m3)
-      ws.vofs[m3] =
-          S::VBASE + pbase + (hi * 4 + (i16 >> 2)) * S::ROW_BYTES + ((4 * (m3 ^ x) + c) << 4) + (i16 & 1) * 8;
+    ws.vbase = S::VBASE + pbase + (hi * 4 + (i16 >> 2)) * S::ROW_BYTES + ((4 * x + c) << 4) + (i16 & 1) * 8;
   }
 
   // ---- main loop, unrolled over the stage buffers -----------------------------
@@ -347,66 +454,102 @@ __global__ __launch_bounds__(512) void prefill_v2_kernel(const PrefillParams p) 
                                            wave_min_tok, wave_max_tok, my_lim_tok, n, sl2, hi);
   }
 
-  // ---- merge the two phases of each row group --------------------------------
-  __syncthreads();  // stage buffers are free
+  // ---- epilogue: merge the two phases, normalise, gate, store ---------------
+  // Both waves of a row group finish it: phase f writes rows [16f, 16f + 16),
+  // RPI rows per instruction and LPR lanes of 8 elements per row, so gate
+  // reads and output writes are whole 16-byte pieces of each row. The gate
+  // is fetched before the merge so that its latency overlaps the merge.
+  constexpr int LPR = D / 8;     // lanes per row, 8 elements each
+  constexpr int RPI = 64 / LPR;  // rows per wave instruction
+  constexpr int NIT = 16 / RPI;  // instructions for the wave's 16 rows
+  const int qc = lane % LPR;
+  const int rsub = lane / LPR;
+  long erow[NIT];  // row index (b, token, head) of each row of this wave's share, -1 if none
+  u32x4_t graw[NIT];
+  uint16_t ghead[NIT];
+#pragma unroll
+  for (int it = 0; it < NIT; ++it) {
+    const int local = (rg & 1) * 32 + phase * 16 + it * RPI + rsub;  // row within the token block
+    const int blk = (rg < 2) ? blk_light : blk_heavy;
+    const int hh = local / TB;
+    const int tt = local - hh * TB;
+    const int tok = blk * TB + tt;
+    const bool valid = (blk >= 0) && (hh < p.grp) && (tok < n);
+    erow[it] = valid ? ((long)b * n + tok) * p.H + g * p.grp + hh : -1;
+    graw[it] = u32x4_t{0, 0, 0, 0};
+    ghead[it] = 0;
+    if (valid && GATE == 2) graw[it] = *(const u32x4_t*)(p.gate + erow[it] * D + qc * 8);
+    if (valid && GATE == 1) ghead[it] = p.gate[erow[it]];
+  }
+
+  lds_barrier();  // stage buffers are free; the gate reads stay in flight
   float* xo = (float*)smem;
   if (phase == 1) {
+    // 16 bytes per lane: accumulator elements 4ig..4ig+3 of block mb
 #pragma unroll
     for (int mb = 0; mb < D / 32; ++mb)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) xo[((rg * (D / 32) + mb) * 16 + i) * 64 + lane] = ws.o[mb][i];
+      for (int ig = 0; ig < 4; ++ig)
+        *(f32x4_t*)(xo + (((rg * (D / 32) + mb) * 4 + ig) * 64 + lane) * 4) =
+            f32x4_t{ws.o[mb][4 * ig], ws.o[mb][4 * ig + 1], ws.o[mb][4 * ig + 2], ws.o[mb][4 * ig + 3]};
     ml_x[rg][lane][0] = ws.m_run;
     ml_x[rg][lane][1] = ws.l_run;
   }
-  __syncthreads();
-  if (phase == 1) return;
-  float l_run;
-  {
+  lds_barrier();
+  // row group rg's region of xo: 32 rows x D floats, 16-byte chunk q of row r
+  // stored at chunk q ^ (r & 15)
+  float* xr = xo + rg * 32 * D;
+  if (phase == 0) {
     const float m1 = ml_x[rg][lane][0];
     const float l1 = ml_x[rg][lane][1];
     const float mt = fmaxf(ws.m_run, m1);
     const float a0 = __builtin_amdgcn_exp2f(ws.m_run - mt);
     const float a1 = __builtin_amdgcn_exp2f(m1 - mt);
-    l_run = ws.l_run * a0 + l1 * a1;
+    float l_run = ws.l_run * a0 + l1 * a1;
 #pragma unroll
     for (int mb = 0; mb < D / 32; ++mb)
 #pragma unroll
-      for (int i = 0; i < 16; ++i)
-        ws.o[mb][i] = ws.o[mb][i] * a0 + xo[((rg * (D / 32) + mb) * 16 + i) * 64 + lane] * a1;
-  }
-
-  // ---- epilogue: normalise, gate, store -------------------------------------
-  {
-    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_run), __float_as_uint(l_run), false, false);
-    l_run = __uint_as_float(r[0]) + __uint_as_float(r[1]);
-  }
-  if (!my_valid) return;
-  const float inv_l = 1.0f / l_run;
-  const long row_off = ((long)b * n + my_tok) * p.H + my_h;
-  uint16_t* orow = p.out + row_off * D;
-  float hg = 1.0f;
-  if (GATE == 1) hg = sigmoid_f32(bf16_bits_to_f32(p.gate[row_off]));
+      for (int ig = 0; ig < 4; ++ig) {
+        const f32x4_t o1 = *(const f32x4_t*)(xo + (((rg * (D / 32) + mb) * 4 + ig) * 64 + lane) * 4);
 #pragma unroll
-  for (int mb = 0; mb < D / 32; ++mb) {
-#pragma unroll
-    for (int ig = 0; ig < 4; ++ig) {
-      const int dm = mb * 32 + ig * 8 + hi * 4;
-      float y[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) y[j] = ws.o[mb][ig * 4 + j] * inv_l;
-      if (GATE == 2) {
-        const u32x2_t z = *(const u32x2_t*)(p.gate + row_off * D + dm);
-        y[0] *= sigmoid_f32(lo_bf16(z[0]));
-        y[1] *= sigmoid_f32(hi_bf16(z[0]));
-        y[2] *= sigmoid_f32(lo_bf16(z[1]));
-        y[3] *= sigmoid_f32(hi_bf16(z[1]));
-      } else if (GATE == 1) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) y[j] *= hg;
+        for (int jj = 0; jj < 4; ++jj) ws.o[mb][4 * ig + jj] = ws.o[mb][4 * ig + jj] * a0 + o1[jj] * a1;
       }
-      const u32x2_t ov = {pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
-      *(u32x2_t*)(orow + dm) = ov;
+    {
+      auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_run), __float_as_uint(l_run), false, false);
+      l_run = __uint_as_float(r[0]) + __uint_as_float(r[1]);
     }
+    const float inv_l = 1.0f / l_run;
+    // lane (l32, hi) holds row l32, elements mb*32 + ig*8 + hi*4 + [0, 4)
+#pragma unroll
+    for (int mb = 0; mb < D / 32; ++mb)
+#pragma unroll
+      for (int ig = 0; ig < 4; ++ig) {
+        const int q = mb * 8 + ig * 2 + hi;
+        f32x4_t y;
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) y[jj] = ws.o[mb][ig * 4 + jj] * inv_l;
+        *(f32x4_t*)(xr + l32 * D + ((q ^ (l32 & 15)) << 2)) = y;
+      }
+  }
+  lds_barrier();
+#pragma unroll
+  for (int it = 0; it < NIT; ++it) {
+    if (erow[it] < 0) continue;
+    const int lr = phase * 16 + it * RPI + rsub;
+    const f32x4_t y0 = *(const f32x4_t*)(xr + lr * D + (((2 * qc) ^ (lr & 15)) << 2));
+    const f32x4_t y1 = *(const f32x4_t*)(xr + lr * D + (((2 * qc + 1) ^ (lr & 15)) << 2));
+    float y[8] = {y0[0], y0[1], y0[2], y0[3], y1[0], y1[1], y1[2], y1[3]};
+    if (GATE == 2) {
+      float z[8];
+      unpack8(graw[it], z);
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) y[jj] *= sigmoid_f32(z[jj]);
+    } else if (GATE == 1) {
+      const float hg = sigmoid_f32(bf16_bits_to_f32(ghead[it]));
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) y[jj] *= hg;
+    }
+    *(u32x4_t*)(p.out + erow[it] * D + qc * 8) = pack8(y);
   }
 }
 
