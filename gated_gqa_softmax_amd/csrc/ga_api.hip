@@ -3,6 +3,7 @@
 #include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include "../../include/ga.h"
@@ -79,6 +80,34 @@ bool prefill_v2_ok(const ga_attn_desc* d, int32_t k_cap, int32_t v_cap) {
          grp <= 64 && 2 * tb * (d->rot_dim / 2) <= 2048 && row * k_cap < (1LL << 31) && row * v_cap < (1LL << 31);
 }
 
+// The wide kernel: 256 query rows per workgroup, one causal block each,
+// heaviest first; it needs enough blocks to balance the triangle (two or more
+// per compute unit). RoPE pairs must stay inside one lane: rot/2 % 16 == 0.
+bool prefill_wide_ok(const ga_attn_desc* d, int32_t n, int32_t k_cap, int32_t v_cap, bool require_large) {
+  const int grp = d->n_q_heads / d->n_kv_heads;
+  const int hd = d->head_dim;
+  const long long row = 2LL * d->n_kv_heads * hd;
+  if (!(d->dtype == GA_BF16 && hd == 128 && d->rot_dim % 32 == 0 && grp <= 256 && row * k_cap < (1LL << 31) &&
+        row * v_cap < (1LL << 31)))
+    return false;
+  const long long tb = 256 / grp;
+  const long long blocks = (long long)d->batch * d->n_kv_heads * ((n + tb - 1) / tb);
+  return !require_large || blocks >= 512;
+}
+
+// Kernel choice for prefill attention: automatic, or forced (when the forced
+// kernel serves the shape) by GA_PREFILL_KERNEL = wide | mirror | simple | generic.
+enum PrefillKernel { PK_AUTO, PK_WIDE, PK_MIRROR, PK_SIMPLE, PK_GENERIC };
+PrefillKernel prefill_kernel_request() {
+  const char* e = getenv("GA_PREFILL_KERNEL");
+  if (!e) return PK_AUTO;
+  if (!strcmp(e, "wide")) return PK_WIDE;
+  if (!strcmp(e, "mirror")) return PK_MIRROR;
+  if (!strcmp(e, "simple")) return PK_SIMPLE;
+  if (!strcmp(e, "generic")) return PK_GENERIC;
+  return PK_AUTO;
+}
+
 bool prefill_fast(const ga_attn_desc* d) {
   const int grp = d->n_q_heads / d->n_kv_heads;
   const int hd = d->head_dim;
@@ -147,8 +176,14 @@ ga_status prefill_attn_impl(const ga_attn_desc* desc, int32_t n, const void* q, 
                             const float* q_norm_w, const int32_t* positions, void* out, hipStream_t stream) {
   const int H = desc->n_q_heads, G = desc->n_kv_heads, d = desc->head_dim;
   const int grp = H / G;
-  const bool v2 = prefill_v2_ok(desc, k_cap, v_cap);
-  if (v2 || prefill_fast(desc)) {
+  const PrefillKernel req = prefill_kernel_request();
+  bool wide = prefill_wide_ok(desc, n, k_cap, v_cap, req != PK_WIDE);
+  bool v2 = !wide && prefill_v2_ok(desc, k_cap, v_cap);
+  bool v1 = !wide && !v2 && prefill_fast(desc);
+  if (req == PK_MIRROR && prefill_v2_ok(desc, k_cap, v_cap)) wide = false, v2 = true, v1 = false;
+  if (req == PK_SIMPLE && prefill_fast(desc)) wide = false, v2 = false, v1 = true;
+  if (req == PK_GENERIC) wide = false, v2 = false, v1 = false;
+  if (wide || v2 || v1) {
     PrefillParams pp;
     memset(&pp, 0, sizeof(pp));
     pp.q = (const uint16_t*)q;
@@ -165,7 +200,7 @@ ga_status prefill_attn_impl(const ga_attn_desc* desc, int32_t n, const void* q, 
     pp.H = H;
     pp.G = G;
     pp.grp = grp;
-    pp.TB = (v2 ? 64 : 128) / grp;  // tokens per block: 128 rows (v1) or 64 rows (v2) per block
+    pp.TB = (wide ? 256 : v2 ? 64 : 128) / grp;  // tokens per block: 256 (wide), 64 (mirror), 128 (simple) rows
     pp.nblk = (n + pp.TB - 1) / pp.TB;
     pp.rot = desc->rot_dim;
     pp.half = desc->rot_dim / 2;
@@ -174,6 +209,7 @@ ga_status prefill_attn_impl(const ga_attn_desc* desc, int32_t n, const void* q, 
     pp.scale_log2 = scale_of(desc) * 1.4426950408889634f;
     fill_inv_freq(desc, pp.inv_freq);
     if ((long long)pp.B * G * pp.nblk > 0x7fffffffLL) return fail(GA_ERR_UNSUPPORTED, "grid too large");
+    if (wide) return hip_status(launch_prefill_wide(pp, d, desc->gate_mode, stream), "prefill attention launch");
     if (v2) return hip_status(launch_prefill_v2(pp, d, desc->gate_mode, stream), "prefill attention launch");
     return hip_status(launch_prefill_mfma(pp, d, desc->gate_mode, stream), "prefill attention launch");
   }

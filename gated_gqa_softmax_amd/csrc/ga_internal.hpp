@@ -85,6 +85,7 @@ constexpr int kDecodeChunk = 512;  // keys per decode split
 hipError_t launch_prep_keys(const PrepParams& p, int is_bf16, hipStream_t s);
 hipError_t launch_prefill_mfma(const PrefillParams& p, int D, int gate_mode, hipStream_t s);
 hipError_t launch_prefill_v2(const PrefillParams& p, int D, int gate_mode, hipStream_t s);
+hipError_t launch_prefill_wide(const PrefillParams& p, int D, int gate_mode, hipStream_t s);
 hipError_t launch_naive(const NaiveParams& p, int is_bf16, hipStream_t s);
 hipError_t launch_decode_partials(const DecodeParams& p, int D, hipStream_t s);
 hipError_t launch_decode_merge(const DecodeParams& p, int D, int gate_mode, hipStream_t s);

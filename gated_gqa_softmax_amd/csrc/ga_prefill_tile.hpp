@@ -1,0 +1,198 @@
+// Building blocks of the fused prefill kernels (gfx950): the LDS stage ring
+// that K-hat and V tiles stream into, the per-wave state of a 32-row query
+// group, and one 32-key tile of flash attention on 32x32x16 bf16 MFMA.
+//
+// Definition: causal softmax(q_hat k_hat^T * scale) V per query head, as in
+// "Transformer by Hand · 6. Gated attention" ("The formula"), computed over key
+// tiles with a running max and row sum ("Attention, worked all the way
+// through", "Why scaling and stable softmax matter").
+//
+//  * S^T = K Q^T puts one query row per lane (lane l: row l % 32), so the row
+//    max needs one permlane32 swap and the probabilities are already in the
+//    B-operand layout of O^T += V^T P^T; V^T fragments come from row-major V
+//    in LDS through ds_read_b64_tr_b16.
+//  * K and V rows are XOR-swizzled in LDS per 16-byte chunk (K: chunk ^
+//    (row & 15); V: chunk ^ 4 (row & 3)) so those reads are conflict-free.
+//  * The running max is raised lazily: the output is rescaled only when a
+//    tile's max exceeds the reference by more than 2^8, so probabilities stay
+//    below 256 (exact in fp32, fine as bf16 operands).
+#pragma once
+
+#include "ga_common.hpp"
+#include "ga_internal.hpp"
+
+namespace ga {
+
+typedef __attribute__((__vector_size__(4 * sizeof(short)))) short i16x4_t;
+typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
+
+template <int D, int NS>
+struct TileShape {
+  static constexpr int ST = 64;                      // keys per stage
+  static constexpr int CPR = D / 8;                  // 16-byte chunks per row
+  static constexpr int ROW_BYTES = D * 2;
+  static constexpr int TILE_BYTES = ST * ROW_BYTES;  // K (or V) of one stage
+  static constexpr int NSTAGE = NS;                 // stage buffers in the ring
+  static constexpr int BUF_BYTES = 2 * NSTAGE * TILE_BYTES;
+  static constexpr int VBASE = NSTAGE * TILE_BYTES;  // start of the V stages
+  static constexpr int LOADS_PER_TILE = TILE_BYTES / 1024;  // 1 KB per wave instruction
+  static constexpr int LOADS_PER_WAVE = LOADS_PER_TILE / 8;
+  static constexpr int ROWS_PER_LOAD = 1024 / ROW_BYTES;
+  static_assert(CPR >= 16, "swizzles need at least 16 chunks per row");
+  static_assert(LOADS_PER_WAVE >= 1, "tile too small");
+};
+
+__device__ __forceinline__ int swz_k(int row) { return row & 15; }
+__device__ __forceinline__ int swz_v(int row) { return (row & 3) << 2; }
+
+constexpr float kLazyRescale = 8.0f;  // log2 headroom before the output is rescaled
+
+// Per-wave state of the main loop.
+template <int D>
+struct WaveState {
+  bf16x8_t qf[D / 16];   // Q^T operand fragments of this wave's 32 rows
+  f32x16_t o[D / 32];    // O^T accumulators
+  float m_run, l_run;    // reference max (log2 domain) and lane-partial row sum
+  int kbase;             // K operand LDS address of step 0 (lane part, phase included);
+                         // step kk reads kbase ^ ((kk & 7) << 5), + 256 for kk >= 8
+  int vbase;             // V^T operand LDS address of dim block 0 (lane part, phase and
+                         // V base included); dim block mb reads vbase ^ ((mb & 3) << 6), + 256 for mb >= 4
+};
+
+// Direct-to-LDS loads of one stage (64 keys of K-hat and V) for this wave:
+// 1 KB of LDS per instruction, lane l's 16 bytes at slot l. The whole byte
+// offset goes in the VGPR operand so the buffer range check sees it.
+template <int D, int NS, int BUF>
+__device__ __forceinline__ void stage_issue(unsigned char* smem, i32x4_t krs, i32x4_t vrs, int koff, int voff, int w,
+                                         int st, int kv_row_bytes) {
+  typedef TileShape<D, NS> S;
+  const uint32_t kt = lds_addr(smem + BUF * S::TILE_BYTES);
+  const uint32_t vt = lds_addr(smem + S::VBASE + BUF * S::TILE_BYTES);
+  const int soff = st * S::ST * kv_row_bytes;
+  const int jstep = 8 * S::ROWS_PER_LOAD * kv_row_bytes;
+  // opaque per call: each load adds its scalar offset instead of keeping one
+  // loop-invariant VGPR per load
+  asm volatile("" : "+v"(koff), "+v"(voff));
+#pragma unroll
+  for (int j = 0; j < S::LOADS_PER_WAVE; ++j) {
+    const int t = w + 8 * j;
+    buffer_load_lds16(krs, kt + t * 1024, koff + soff + j * jstep);
+    buffer_load_lds16(vrs, vt + t * 1024, voff + soff + j * jstep);
+  }
+}
+
+// One 32-key tile for the wave's 32 rows: keys [32 * HALF, 32 * HALF + 32) of
+// stage buffer BUF, past the lane part already in ws.kbase / ws.vbase.
+// Operand reads run KPF (K) and VPF (V^T) MFMAs ahead of their use, so LDS
+// latency overlaps the matrix pipe instead of stalling each MFMA.
+template <int D, int NS, int BUF, int HALF>
+__device__ __forceinline__ void attn_tile(const unsigned char* smem, WaveState<D>& ws, bool need_mask, int lim,
+                                        float sl2) {
+  typedef TileShape<D, NS> S;
+  constexpr int NK = D / 16;   // QK steps (16 dims each)
+  constexpr int NV = D / 16;   // PV MFMAs: 2 key halves x D/32 dim blocks
+  constexpr int KPF = (D == 256) ? 3 : 4;  // bounded by the register budget of d = 256
+  constexpr int VPF = (D == 256) ? 2 : 3;
+  int kb = ws.kbase, vb = ws.vbase;
+  // opaque per tile: the per-step addresses stay short-lived temporaries
+  asm volatile("" : "+v"(kb), "+v"(vb));
+  // each address is its own opaque value, so none is kept alive across the
+  // loop (the K steps kk and kk + 8 would otherwise share one register)
+  auto kread = [&](int kk) {
+    int a = kb ^ ((kk & 7) << 5);
+    asm volatile("" : "+v"(a));
+    return *(const bf16x8_t*)(smem + a + (BUF * S::TILE_BYTES + HALF * 32 * S::ROW_BYTES + ((kk >> 3) << 8)));
+  };
+  // V^T fragment rows: keys 16ks + 4(lane/32) + (lane%16)/4 (+8 for slots 4..7)
+  auto vread = [&](int t) {
+    const int ks = t / (D / 32), mb = t % (D / 32);
+    int a = vb ^ ((mb & 3) << 6);
+    asm volatile("" : "+v"(a));
+    const unsigned char* a1 =
+        smem + a + (BUF * S::TILE_BYTES + HALF * 32 * S::ROW_BYTES + ((mb & 4) << 6) + ks * 16 * S::ROW_BYTES);
+    const i16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)a1);
+    const i16x4_t v2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(a1 + 8 * S::ROW_BYTES));
+    const u32x4_t av = {__builtin_bit_cast(u32x2_t, v1)[0], __builtin_bit_cast(u32x2_t, v1)[1],
+                        __builtin_bit_cast(u32x2_t, v2)[0], __builtin_bit_cast(u32x2_t, v2)[1]};
+    return __builtin_bit_cast(bf16x8_t, av);
+  };
+
+  bf16x8_t ka[NK];
+  f32x16_t s;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) s[i] = 0.f;
+#pragma unroll
+  for (int kk = 0; kk < KPF; ++kk) ka[kk] = kread(kk);
+#pragma unroll
+  for (int kk = 0; kk < NK; ++kk) {
+    if (kk + KPF < NK) ka[kk + KPF] = kread(kk + KPF);
+    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[kk], ws.qf[kk], s, 0, 0, 0);
+  }
+  // keep that order: KPF reads ahead, then one MFMA per read
+  __builtin_amdgcn_sched_group_barrier(0x100, KPF, 0);
+#pragma unroll
+  for (int kk = 0; kk < NK - KPF; ++kk) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, KPF, 0);
+  // the first V^T operands do not depend on the softmax
+  bf16x8_t va[NV];
+#pragma unroll
+  for (int t = 0; t < VPF; ++t) va[t] = vread(t);
+  if (need_mask) {
+    // s[i] holds key k0 + 8(i/4) + 4hi + (i%4); visible iff 8(i/4) + (i%4) <= lim
+#pragma unroll
+    for (int i = 0; i < 16; ++i) s[i] = ((i >> 2) * 8 + (i & 3) <= lim) ? s[i] : -INFINITY;
+  }
+  float mloc = s[0];
+#pragma unroll
+  for (int i = 1; i < 16; ++i) mloc = fmaxf(mloc, s[i]);
+  {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(mloc), __float_as_uint(mloc), false, false);
+    mloc = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  }
+  const float mcand = mloc * sl2;
+  if (!__all(mcand <= ws.m_run + kLazyRescale)) {
+    const float m_new = fmaxf(ws.m_run, mcand);
+    const float alpha = __builtin_amdgcn_exp2f(ws.m_run - m_new);
+    ws.l_run *= alpha;
+#pragma unroll
+    for (int mb = 0; mb < D / 32; ++mb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) ws.o[mb][i] *= alpha;
+    ws.m_run = m_new;
+  }
+  const float nm = -ws.m_run;
+  float lsum = 0.f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], sl2, nm));
+    s[i] = pv;
+    lsum += pv;
+  }
+  ws.l_run += lsum;
+  bf16x8_t pb[2];
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    u32x4_t pk;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) pk[j] = pack_bf16x2(s[ks * 8 + 2 * j], s[ks * 8 + 2 * j + 1]);
+    pb[ks] = __builtin_bit_cast(bf16x8_t, pk);
+  }
+#pragma unroll
+  for (int t = 0; t < NV; ++t) {
+    if (t + VPF < NV) va[t + VPF] = vread(t + VPF);
+    const int ks = t / (D / 32), mb = t % (D / 32);
+    ws.o[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[t], pb[ks], ws.o[mb], 0, 0, 0);
+  }
+  // one MFMA, then the two transposed reads of the operand VPF steps ahead
+#pragma unroll
+  for (int t = 0; t < NV - VPF; ++t) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, VPF, 1);
+}
+
+}  // namespace ga

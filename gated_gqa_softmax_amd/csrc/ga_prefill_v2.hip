@@ -33,209 +33,41 @@
 //    a tile's max exceeds the reference by more than 2^8, so probabilities
 //    stay below 256 (exact in fp32, fine as bf16 operands) and most tiles
 //    skip the rescale.
-#include "ga_common.hpp"
-#include "ga_internal.hpp"
+#include "ga_prefill_tile.hpp"
 
 namespace ga {
 
-typedef __attribute__((__vector_size__(4 * sizeof(short)))) short i16x4_t;
-typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
-
 template <int D>
-struct V2Shape {
-  static constexpr int ST = 64;                      // keys per stage
-  static constexpr int CPR = D / 8;                  // 16-byte chunks per row
-  static constexpr int ROW_BYTES = D * 2;
-  static constexpr int TILE_BYTES = ST * ROW_BYTES;  // K (or V) of one stage
-  static constexpr int NSTAGE = (D == 256) ? 2 : 3;
-  static constexpr int BUF_BYTES = 2 * NSTAGE * TILE_BYTES;
-  static constexpr int VBASE = NSTAGE * TILE_BYTES;  // start of the V stages
-  static constexpr int LOADS_PER_TILE = TILE_BYTES / 1024;  // 1 KB per wave instruction
-  static constexpr int LOADS_PER_WAVE = LOADS_PER_TILE / 8;
-  static constexpr int ROWS_PER_LOAD = 1024 / ROW_BYTES;
-  static constexpr int XCHG_BYTES = 4 * (D / 32) * 16 * 64 * 4;  // phase-1 O of 4 row groups
-  static_assert(CPR >= 16, "swizzles need at least 16 chunks per row");
-  static_assert(XCHG_BYTES <= BUF_BYTES, "merge buffer must fit the stages");
-  static_assert(LOADS_PER_WAVE >= 1, "tile too small");
-};
-
-__device__ __forceinline__ int swz_k(int row) { return row & 15; }
-__device__ __forceinline__ int swz_v(int row) { return (row & 3) << 2; }
-
-constexpr float kLazyRescale = 8.0f;  // log2 headroom before the output is rescaled
-
-// Per-wave state of the main loop.
+constexpr int kMirrorStages = (D == 256) ? 2 : 3;
 template <int D>
-struct V2Wave {
-  bf16x8_t qf[D / 16];   // Q^T operand fragments of this wave's 32 rows
-  f32x16_t o[D / 32];    // O^T accumulators
-  float m_run, l_run;    // reference max (log2 domain) and lane-partial row sum
-  int kbase;             // K operand LDS address of step 0 (lane part, phase included);
-                         // step kk reads kbase ^ ((kk & 7) << 5), + 256 for kk >= 8
-  int vbase;             // V^T operand LDS address of dim block 0 (lane part, phase and
-                         // V base included); dim block mb reads vbase ^ ((mb & 3) << 6), + 256 for mb >= 4
-};
+using MirrorShape = TileShape<D, kMirrorStages<D>>;
 
 // Q staging rows: 0-63 in K buffer NSTAGE-1, 64-127 in V buffer NSTAGE-1.
 template <int D>
 __device__ __forceinline__ uint16_t* v2_qrow(unsigned char* smem, int r) {
-  typedef V2Shape<D> S;
+  typedef MirrorShape<D> S;
   return (uint16_t*)(smem + ((r < 64) ? (S::NSTAGE - 1) : (2 * S::NSTAGE - 1)) * S::TILE_BYTES +
                      (r & 63) * S::ROW_BYTES);
-}
-
-// Direct-to-LDS loads of one stage (64 keys of K-hat and V) for this wave:
-// 1 KB of LDS per instruction, lane l's 16 bytes at slot l. The whole byte
-// offset goes in the VGPR operand so the buffer range check sees it.
-template <int D, int BUF>
-__device__ __forceinline__ void v2_issue(unsigned char* smem, i32x4_t krs, i32x4_t vrs, int koff, int voff, int w,
-                                         int st, int kv_row_bytes) {
-  typedef V2Shape<D> S;
-  const uint32_t kt = lds_addr(smem + BUF * S::TILE_BYTES);
-  const uint32_t vt = lds_addr(smem + S::VBASE + BUF * S::TILE_BYTES);
-  const int soff = st * S::ST * kv_row_bytes;
-  const int jstep = 8 * S::ROWS_PER_LOAD * kv_row_bytes;
-  // opaque per call: each load adds its scalar offset instead of keeping one
-  // loop-invariant VGPR per load
-  asm volatile("" : "+v"(koff), "+v"(voff));
-#pragma unroll
-  for (int j = 0; j < S::LOADS_PER_WAVE; ++j) {
-    const int t = w + 8 * j;
-    buffer_load_lds16(krs, kt + t * 1024, koff + soff + j * jstep);
-    buffer_load_lds16(vrs, vt + t * 1024, voff + soff + j * jstep);
-  }
-}
-
-// One 32-key tile (this wave's phase half of stage buffer BUF) for 32 rows.
-// Operand reads run KPF (K) and VPF (V^T) MFMAs ahead of their use, so LDS
-// latency overlaps the matrix pipe instead of stalling each MFMA.
-template <int D, int BUF>
-__device__ __forceinline__ void v2_tile(const unsigned char* smem, V2Wave<D>& ws, bool need_mask, int lim,
-                                        float sl2) {
-  typedef V2Shape<D> S;
-  constexpr int NK = D / 16;   // QK steps (16 dims each)
-  constexpr int NV = D / 16;   // PV MFMAs: 2 key halves x D/32 dim blocks
-  constexpr int KPF = (D == 256) ? 3 : 4;  // bounded by the register budget of d = 256
-  constexpr int VPF = (D == 256) ? 2 : 3;
-  int kb = ws.kbase, vb = ws.vbase;
-  // opaque per tile: the per-step addresses stay short-lived temporaries
-  asm volatile("" : "+v"(kb), "+v"(vb));
-  // each address is its own opaque value, so none is kept alive across the
-  // loop (the K steps kk and kk + 8 would otherwise share one register)
-  auto kread = [&](int kk) {
-    int a = kb ^ ((kk & 7) << 5);
-    asm volatile("" : "+v"(a));
-    return *(const bf16x8_t*)(smem + a + (BUF * S::TILE_BYTES + ((kk >> 3) << 8)));
-  };
-  // V^T fragment rows: keys 16ks + 4(lane/32) + (lane%16)/4 (+8 for slots 4..7)
-  auto vread = [&](int t) {
-    const int ks = t / (D / 32), mb = t % (D / 32);
-    int a = vb ^ ((mb & 3) << 6);
-    asm volatile("" : "+v"(a));
-    const unsigned char* a1 = smem + a + (BUF * S::TILE_BYTES + ((mb & 4) << 6) + ks * 16 * S::ROW_BYTES);
-    const i16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)a1);
-    const i16x4_t v2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(a1 + 8 * S::ROW_BYTES));
-    const u32x4_t av = {__builtin_bit_cast(u32x2_t, v1)[0], __builtin_bit_cast(u32x2_t, v1)[1],
-                        __builtin_bit_cast(u32x2_t, v2)[0], __builtin_bit_cast(u32x2_t, v2)[1]};
-    return __builtin_bit_cast(bf16x8_t, av);
-  };
-
-  bf16x8_t ka[NK];
-  f32x16_t s;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) s[i] = 0.f;
-#pragma unroll
-  for (int kk = 0; kk < KPF; ++kk) ka[kk] = kread(kk);
-#pragma unroll
-  for (int kk = 0; kk < NK; ++kk) {
-    if (kk + KPF < NK) ka[kk + KPF] = kread(kk + KPF);
-    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[kk], ws.qf[kk], s, 0, 0, 0);
-  }
-  // keep that order: KPF reads ahead, then one MFMA per read
-  __builtin_amdgcn_sched_group_barrier(0x100, KPF, 0);
-#pragma unroll
-  for (int kk = 0; kk < NK - KPF; ++kk) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-  }
-  __builtin_amdgcn_sched_group_barrier(0x008, KPF, 0);
-  // the first V^T operands do not depend on the softmax
-  bf16x8_t va[NV];
-#pragma unroll
-  for (int t = 0; t < VPF; ++t) va[t] = vread(t);
-  if (need_mask) {
-    // s[i] holds key k0 + 8(i/4) + 4hi + (i%4); visible iff 8(i/4) + (i%4) <= lim
-#pragma unroll
-    for (int i = 0; i < 16; ++i) s[i] = ((i >> 2) * 8 + (i & 3) <= lim) ? s[i] : -INFINITY;
-  }
-  float mloc = s[0];
-#pragma unroll
-  for (int i = 1; i < 16; ++i) mloc = fmaxf(mloc, s[i]);
-  {
-    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(mloc), __float_as_uint(mloc), false, false);
-    mloc = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-  }
-  const float mcand = mloc * sl2;
-  if (!__all(mcand <= ws.m_run + kLazyRescale)) {
-    const float m_new = fmaxf(ws.m_run, mcand);
-    const float alpha = __builtin_amdgcn_exp2f(ws.m_run - m_new);
-    ws.l_run *= alpha;
-#pragma unroll
-    for (int mb = 0; mb < D / 32; ++mb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) ws.o[mb][i] *= alpha;
-    ws.m_run = m_new;
-  }
-  const float nm = -ws.m_run;
-  float lsum = 0.f;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], sl2, nm));
-    s[i] = pv;
-    lsum += pv;
-  }
-  ws.l_run += lsum;
-  bf16x8_t pb[2];
-#pragma unroll
-  for (int ks = 0; ks < 2; ++ks) {
-    u32x4_t pk;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) pk[j] = pack_bf16x2(s[ks * 8 + 2 * j], s[ks * 8 + 2 * j + 1]);
-    pb[ks] = __builtin_bit_cast(bf16x8_t, pk);
-  }
-#pragma unroll
-  for (int t = 0; t < NV; ++t) {
-    if (t + VPF < NV) va[t + VPF] = vread(t + VPF);
-    const int ks = t / (D / 32), mb = t % (D / 32);
-    ws.o[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[t], pb[ks], ws.o[mb], 0, 0, 0);
-  }
-  // one MFMA, then the two transposed reads of the operand VPF steps ahead
-#pragma unroll
-  for (int t = 0; t < NV - VPF; ++t) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
-    __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
-  }
-  __builtin_amdgcn_sched_group_barrier(0x008, VPF, 1);
 }
 
 // One pipeline step: wait for stage st (buffer BUF), refill the buffer freed
 // by the previous step, and run this wave's tile if it has visible keys.
 template <int D, int BUF>
-__device__ __forceinline__ void v2_step(unsigned char* smem, V2Wave<D>& ws, i32x4_t krs, i32x4_t vrs, int koff, int voff, int w, int st, int nst,
+__device__ __forceinline__ void v2_step(unsigned char* smem, WaveState<D>& ws, i32x4_t krs, i32x4_t vrs, int koff, int voff, int w, int st, int nst,
                                         int kv_row_bytes, int phase, int wave_min_tok, int wave_max_tok,
                                         int my_lim_tok, int n, float sl2, int hi) {
-  typedef V2Shape<D> S;
+  typedef MirrorShape<D> S;
   if (S::NSTAGE == 3 && st + 1 < nst)
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * S::LOADS_PER_WAVE) : "memory");
   else
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   lds_barrier();
   if (st + S::NSTAGE - 1 < nst)
-    v2_issue<D, (BUF + S::NSTAGE - 1) % S::NSTAGE>(smem, krs, vrs, koff, voff, w, st + S::NSTAGE - 1, kv_row_bytes);
+    stage_issue<D, kMirrorStages<D>, (BUF + S::NSTAGE - 1) % S::NSTAGE>(smem, krs, vrs, koff, voff, w, st + S::NSTAGE - 1, kv_row_bytes);
   const int k0 = st * S::ST + phase * 32;
   if (k0 <= wave_max_tok) {
     const bool need_mask = (k0 + 31 > wave_min_tok) || (k0 + 32 > n);  // wave-uniform
-    v2_tile<D, BUF>(smem, ws, need_mask, my_lim_tok - (k0 + hi * 4), sl2);
+    attn_tile<D, kMirrorStages<D>, BUF, 0>(smem, ws, need_mask, my_lim_tok - (k0 + hi * 4), sl2);
   }
 }
 
@@ -255,7 +87,8 @@ __device__ __forceinline__ void rope_quarter(float* x, const float2* cs) {
 
 template <int D, int GATE>
 __global__ __launch_bounds__(512) void prefill_v2_kernel(const PrefillParams p) {
-  typedef V2Shape<D> S;
+  typedef MirrorShape<D> S;
+  static_assert(4 * 32 * D * 4 <= S::BUF_BYTES, "the phase merge reuses the stage buffers");
   __shared__ __attribute__((aligned(1024))) unsigned char smem[S::BUF_BYTES];
   __shared__ float2 table[2048];
   __shared__ float ml_x[4][64][2];
@@ -382,8 +215,8 @@ __global__ __launch_bounds__(512) void prefill_v2_kernel(const PrefillParams p) 
   // The first stage loads go out only now: every load above has been consumed,
   // so no later wait of the compiler (which does not count these loads) can
   // end up waiting for them.
-  if (nst > 0) v2_issue<D, 0>(smem, krs, vrs, koff, voff, w, 0, kv_row_bytes);
-  if (S::NSTAGE == 3 && nst > 1) v2_issue<D, 1>(smem, krs, vrs, koff, voff, w, 1, kv_row_bytes);
+  if (nst > 0) stage_issue<D, kMirrorStages<D>, 0>(smem, krs, vrs, koff, voff, w, 0, kv_row_bytes);
+  if (S::NSTAGE == 3 && nst > 1) stage_issue<D, kMirrorStages<D>, 1>(smem, krs, vrs, koff, voff, w, 1, kv_row_bytes);
   lds_barrier();
   {
     float x[QE];
@@ -416,7 +249,7 @@ __global__ __launch_bounds__(512) void prefill_v2_kernel(const PrefillParams p) 
   }
   lds_barrier();
 
-  V2Wave<D> ws;
+  WaveState<D> ws;
   {
     const uint16_t* qr = v2_qrow<D>(smem, rg * 32 + l32);
 #pragma unroll

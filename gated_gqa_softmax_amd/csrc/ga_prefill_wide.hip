@@ -1,0 +1,304 @@
+// Fused flash-style prefill for gfx950, wide form for grids with many token
+// blocks (batched or long sequences), head_dim 128.
+//
+// Definition: causal softmax(q_hat k_hat^T * scale) V per query head with
+// q_hat = RoPE(RMSNorm(q)) and the sigmoid output gate; sources: "Transformer
+// by Hand · 6. Gated attention" ("The formula", "Four things Qwen3.5 adds to
+// the textbook"), "Gated Attention：算完注意力，再决定用多少" ("门放在哪里？").
+//
+// Layout of the work:
+//  * A workgroup takes one block of 256 query rows, (head of the GQA group,
+//    token) pairs in head-major order, and 8 waves of 32 rows. Every wave reads
+//    every K/V stage, so each K/V byte brought into LDS serves 256 rows.
+//  * Blocks are dispatched heaviest (latest tokens) first; with many blocks per
+//    compute unit the dispatcher then balances the causal triangle.
+//  * All waves of a workgroup span about the same key range, so the two waves
+//    sharing a SIMD stay equally loaded.
+//  * K-hat and V stream through a ring of 4 stages of 64 keys (3 in flight);
+//    each wave runs both 32-key tiles of a stage between barriers.
+//  * q is read straight into the MFMA operand layout: lane (r, h) holds 16-byte
+//    chunks 2kk + h of row r, so the row norm needs the partner lane (r, 1 - h)
+//    once and, with rot/2 a multiple of 16, both elements of every RoPE pair
+//    sit in the same lane.
+//  * The gated output leaves through LDS in row-major order: 16-byte gate
+//    reads and output writes.
+#include "ga_prefill_tile.hpp"
+
+namespace ga {
+
+constexpr int kWideStages = 4;
+template <int D>
+using WideShape = TileShape<D, kWideStages>;
+
+// Wait until stage st has landed in this wave's part of the ring: `ahead`
+// later stages (0 .. kWideStages - 2) may still be in flight.
+template <int LPS>
+__device__ __forceinline__ void wait_stage(int ahead) {
+  static_assert(2 * LPS < 64, "vmcnt range");
+  if (ahead >= 2)
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * LPS) : "memory");
+  else if (ahead == 1)
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LPS) : "memory");
+  else
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
+template <int D, int BUF>
+__device__ __forceinline__ void wide_step(unsigned char* smem, WaveState<D>& ws, i32x4_t krs, i32x4_t vrs,
+                                          int koff, int voff, int w, int st, int nst, int kv_row_bytes,
+                                          int wave_min_tok, int wave_max_tok, int my_lim_tok, int n, float sl2,
+                                          int hi) {
+  typedef WideShape<D> S;
+  wait_stage<2 * S::LOADS_PER_WAVE>(min(S::NSTAGE - 2, nst - 1 - st));
+  lds_barrier();
+  if (st + S::NSTAGE - 1 < nst)
+    stage_issue<D, S::NSTAGE, (BUF + S::NSTAGE - 1) % S::NSTAGE>(smem, krs, vrs, koff, voff, w,
+                                                                st + S::NSTAGE - 1, kv_row_bytes);
+  const int k0 = st * S::ST;
+  if (k0 <= wave_max_tok) {
+    const bool need_mask = (k0 + 31 > wave_min_tok) || (k0 + 32 > n);
+    attn_tile<D, S::NSTAGE, BUF, 0>(smem, ws, need_mask, my_lim_tok - (k0 + hi * 4), sl2);
+  }
+  if (k0 + 32 <= wave_max_tok) {
+    const bool need_mask = (k0 + 63 > wave_min_tok) || (k0 + 64 > n);
+    attn_tile<D, S::NSTAGE, BUF, 1>(smem, ws, need_mask, my_lim_tok - (k0 + 32 + hi * 4), sl2);
+  }
+}
+
+template <int D, int GATE>
+__global__ __launch_bounds__(512) void prefill_wide_kernel(const PrefillParams p) {
+  typedef WideShape<D> S;
+  static_assert(256 * D * 4 <= S::BUF_BYTES, "the output staging reuses the stage buffers");
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[S::BUF_BYTES];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31;
+  const int hi = lane >> 5;
+
+  const int nBG = p.B * p.G;
+  const int u = blockIdx.x;
+  const int blk = p.nblk - 1 - u / nBG;  // heaviest block first
+  const int bg = u % nBG;
+  const int b = bg / p.G;
+  const int g = bg % p.G;
+  const int TB = p.TB;
+  const int n = p.n;
+  const int kend = min(n, blk * TB + TB);
+  const int nst = (kend + S::ST - 1) / S::ST;
+
+  // this lane's query row (head-major inside the block)
+  const int my_r = w * 32 + l32;
+  const int my_hh = my_r / TB;
+  const int my_tt = my_r - my_hh * TB;
+  const int my_tok0 = blk * TB + my_tt;
+  const bool my_valid = (my_hh < p.grp) && (my_tok0 < n);
+  const int my_tok = my_valid ? my_tok0 : 0x3fffffff;
+  int wave_max_tok = my_valid ? my_tok : -1;
+  int wave_min_tok = my_tok;
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) {
+    wave_max_tok = max(wave_max_tok, __shfl_xor(wave_max_tok, m, 64));
+    wave_min_tok = min(wave_min_tok, __shfl_xor(wave_min_tok, m, 64));
+  }
+  wave_max_tok = __builtin_amdgcn_readfirstlane(wave_max_tok);
+  wave_min_tok = __builtin_amdgcn_readfirstlane(wave_min_tok);
+  const int my_lim_tok = min(my_tok, n - 1);
+
+  // ---- stage loads: the first NSTAGE - 1 stages go out before anything else
+  const int kv_row_bytes = p.G * D * 2;
+  const uint32_t valid_bytes = (uint32_t)((n - 1) * kv_row_bytes + D * 2);
+  const i32x4_t krs = buffer_desc(p.khat + (long)b * p.k_bstride + (long)g * D, valid_bytes);
+  const i32x4_t vrs = buffer_desc(p.v + (long)b * p.v_bstride + (long)g * D, valid_bytes);
+  int koff, voff;
+  {
+    const int row0 = w * S::ROWS_PER_LOAD + lane / S::CPR;
+    const int ph = lane % S::CPR;
+    koff = row0 * kv_row_bytes + ((ph ^ swz_k(row0)) << 4);
+    voff = row0 * kv_row_bytes + ((ph ^ swz_v(row0)) << 4);
+  }
+  if (nst > 0) stage_issue<D, S::NSTAGE, 0>(smem, krs, vrs, koff, voff, w, 0, kv_row_bytes);
+  if (nst > 1) stage_issue<D, S::NSTAGE, 1>(smem, krs, vrs, koff, voff, w, 1, kv_row_bytes);
+  if (nst > 2) stage_issue<D, S::NSTAGE, 2>(smem, krs, vrs, koff, voff, w, 2, kv_row_bytes);
+
+  // ---- q_hat of this lane's row, straight into the MFMA operand layout -------
+  // Lane (l32, hi) holds elements 16kk + 8hi + [0, 8) of row l32 for every kk.
+  WaveState<D> ws;
+  {
+    constexpr int NK = D / 16;
+    const int half = p.half;
+    const int hq = my_valid ? g * p.grp + my_hh : g * p.grp;  // rows outside the block read a real row
+    const int tq = my_valid ? my_tok0 : 0;
+    const uint16_t* qrow = p.q + (((long)b * n + tq) * p.H + hq) * D + hi * 8;
+    u32x4_t raw[NK];
+#pragma unroll
+    for (int kk = 0; kk < NK; ++kk) raw[kk] = *(const u32x4_t*)(qrow + kk * 16);
+    f32x4_t wv[NK][2];
+    if (p.wq) {
+#pragma unroll
+      for (int kk = 0; kk < NK; ++kk) {
+        wv[kk][0] = *(const f32x4_t*)(p.wq + kk * 16 + hi * 8);
+        wv[kk][1] = *(const f32x4_t*)(p.wq + kk * 16 + hi * 8 + 4);
+      }
+    }
+    const int pos = p.positions ? p.positions[(long)b * n + tq] : tq;
+    float x[NK][8];
+#pragma unroll
+    for (int kk = 0; kk < NK; ++kk) unpack8(raw[kk], x[kk]);
+    if (p.wq) {
+      float ss = 0.f;
+#pragma unroll
+      for (int kk = 0; kk < NK; ++kk)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) ss += x[kk][j] * x[kk][j];
+      ss += swap_half(ss);
+      const float inv = rsqrtf(ss * (1.0f / D) + p.eps);
+#pragma unroll
+      for (int kk = 0; kk < NK; ++kk)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) x[kk][j] *= inv * wv[kk][j >> 2][j & 3];
+    }
+    // RoPE: pair (t, t + half) with t = 16kk + 8hi + j, kk < half / 16
+#pragma unroll
+    for (int kk = 0; kk < NK / 2; ++kk) {
+      if (kk * 16 < half) {
+        const int kp = kk + (half >> 4);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          float c, s;
+          rope_cos_sin(pos, p.inv_freq[kk * 16 + hi * 8 + j], &c, &s);
+          float a = x[kk][j], e = 0.f;
+          // kp is lane-uniform; select its chunk without dynamic indexing
+#pragma unroll
+          for (int q2 = 0; q2 < NK; ++q2)
+            if (q2 == kp) e = x[q2][j];
+          const float ra = a * c - e * s, re = e * c + a * s;
+          x[kk][j] = ra;
+#pragma unroll
+          for (int q2 = 0; q2 < NK; ++q2)
+            if (q2 == kp) x[q2][j] = re;
+        }
+      }
+    }
+#pragma unroll
+    for (int kk = 0; kk < NK; ++kk) ws.qf[kk] = __builtin_bit_cast(bf16x8_t, pack8(x[kk]));
+  }
+#pragma unroll
+  for (int mb = 0; mb < D / 32; ++mb)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) ws.o[mb][i] = 0.f;
+  ws.m_run = kNegBig;
+  ws.l_run = 0.f;
+  const float sl2 = p.scale_log2;
+  {
+    const int i16 = lane & 15;
+    const int g16 = lane >> 4;
+    // K operand: row = l32 (+ 32 * HALF), chunk (2kk + hi) ^ (row & 15)
+    const int y = lane & 15;
+    ws.kbase = l32 * S::ROW_BYTES + ((y >> 1) << 5) + ((hi ^ (y & 1)) << 4);
+    // V^T operand: row = 16ks + 4*hi + i16/4 (+8) (+ 32 * HALF), chunk (4mb + c) ^ 4x
+    const int x = (i16 >> 2) & 3;
+    const int c = (g16 & 1) * 2 + ((i16 & 3) >> 1);
+    ws.vbase = S::VBASE + (hi * 4 + (i16 >> 2)) * S::ROW_BYTES + ((4 * x + c) << 4) + (i16 & 1) * 8;
+  }
+
+  // ---- main loop, unrolled over the ring --------------------------------------
+  for (int st0 = 0; st0 < nst; st0 += S::NSTAGE) {
+    wide_step<D, 0>(smem, ws, krs, vrs, koff, voff, w, st0, nst, kv_row_bytes, wave_min_tok, wave_max_tok,
+                    my_lim_tok, n, sl2, hi);
+    if (st0 + 1 < nst)
+      wide_step<D, 1>(smem, ws, krs, vrs, koff, voff, w, st0 + 1, nst, kv_row_bytes, wave_min_tok, wave_max_tok,
+                      my_lim_tok, n, sl2, hi);
+    if (st0 + 2 < nst)
+      wide_step<D, 2>(smem, ws, krs, vrs, koff, voff, w, st0 + 2, nst, kv_row_bytes, wave_min_tok, wave_max_tok,
+                      my_lim_tok, n, sl2, hi);
+    if (st0 + 3 < nst)
+      wide_step<D, 3>(smem, ws, krs, vrs, koff, voff, w, st0 + 3, nst, kv_row_bytes, wave_min_tok, wave_max_tok,
+                      my_lim_tok, n, sl2, hi);
+  }
+
+  // ---- epilogue: normalise, gate, store ----------------------------------------
+  // The wave's 32 rows, RPI rows per instruction and LPR lanes of 8 elements
+  // per row. The gate is fetched first so that its latency overlaps the rest.
+  constexpr int LPR = D / 8;
+  constexpr int RPI = 64 / LPR;
+  constexpr int NIT = 32 / RPI;
+  const int qc = lane % LPR;
+  const int rsub = lane / LPR;
+  long erow[NIT];
+  u32x4_t graw[NIT];
+  uint16_t ghead[NIT];
+#pragma unroll
+  for (int it = 0; it < NIT; ++it) {
+    const int r = w * 32 + it * RPI + rsub;
+    const int hh = r / TB;
+    const int tt = r - hh * TB;
+    const int tok = blk * TB + tt;
+    const bool valid = (hh < p.grp) && (tok < n);
+    erow[it] = valid ? ((long)b * n + tok) * p.H + g * p.grp + hh : -1;
+    const long grow = valid ? erow[it] : ((long)b * n) * p.H + g * p.grp;  // unconditional read
+    if (GATE == 2) graw[it] = *(const u32x4_t*)(p.gate + grow * D + qc * 8);
+    if (GATE == 1) ghead[it] = p.gate[grow];
+  }
+  float l_run = ws.l_run;
+  l_run += swap_half(l_run);
+  const float inv_l = 1.0f / l_run;
+  lds_barrier();  // every wave is done with the stage buffers
+  // the wave's region: 32 rows x D floats, 16-byte chunk q of row r at chunk q ^ (r & 15)
+  float* xr = (float*)smem + w * 32 * D;
+#pragma unroll
+  for (int mb = 0; mb < D / 32; ++mb)
+#pragma unroll
+    for (int ig = 0; ig < 4; ++ig) {
+      const int q = mb * 8 + ig * 2 + hi;
+      f32x4_t y;
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) y[jj] = ws.o[mb][ig * 4 + jj] * inv_l;
+      *(f32x4_t*)(xr + l32 * D + ((q ^ (l32 & 15)) << 2)) = y;
+    }
+  // the region is this wave's own: order its LDS writes before its reads
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+  for (int it = 0; it < NIT; ++it) {
+    if (erow[it] < 0) continue;
+    const int lr = it * RPI + rsub;
+    const f32x4_t y0 = *(const f32x4_t*)(xr + lr * D + (((2 * qc) ^ (lr & 15)) << 2));
+    const f32x4_t y1 = *(const f32x4_t*)(xr + lr * D + (((2 * qc + 1) ^ (lr & 15)) << 2));
+    float y[8] = {y0[0], y0[1], y0[2], y0[3], y1[0], y1[1], y1[2], y1[3]};
+    if (GATE == 2) {
+      float z[8];
+      unpack8(graw[it], z);
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) y[jj] *= sigmoid_f32(z[jj]);
+    } else if (GATE == 1) {
+      const float hg = sigmoid_f32(bf16_bits_to_f32(ghead[it]));
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) y[jj] *= hg;
+    }
+    *(u32x4_t*)(p.out + erow[it] * D + qc * 8) = pack8(y);
+  }
+}
+
+template <int D>
+static hipError_t launch_wide_d(const PrefillParams& p, int gate_mode, hipStream_t s) {
+  const long grid = (long)p.B * p.G * p.nblk;
+  if (grid <= 0) return hipSuccess;
+  switch (gate_mode) {
+    case 0: hipLaunchKernelGGL((prefill_wide_kernel<D, 0>), dim3((unsigned)grid), dim3(512), 0, s, p); break;
+    case 1: hipLaunchKernelGGL((prefill_wide_kernel<D, 1>), dim3((unsigned)grid), dim3(512), 0, s, p); break;
+    default: hipLaunchKernelGGL((prefill_wide_kernel<D, 2>), dim3((unsigned)grid), dim3(512), 0, s, p); break;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_prefill_wide(const PrefillParams& p, int D, int gate_mode, hipStream_t s) {
+  switch (D) {
+    case 128: return launch_wide_d<128>(p, gate_mode, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace ga

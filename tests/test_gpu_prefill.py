@@ -50,6 +50,35 @@ def test_prefill_small_shapes(w):
     assert_close(got, want, w, w.name)
 
 
+# Each fused kernel forced (GA_PREFILL_KERNEL) on the shapes it serves, so the
+# kernels that the automatic choice keeps for large grids are also checked on
+# small ragged ones: several blocks, partial last blocks and stages, groups that
+# do not divide the block, full-width RoPE, single tokens.
+KERNEL_CASES = [
+    ("wide", _case("d128_g2_b2_n130", 2, 130, 16, 8, 128, 32, "headwise", seed=102)),
+    ("wide", _case("d128_g8_n200", 1, 200, 32, 4, 128, 32, "elementwise", seed=103)),
+    ("wide", _case("d128_g3_n17", 1, 17, 6, 2, 128, 32, "elementwise", seed=106)),
+    ("wide", _case("d128_g16_full_rope", 1, 65, 16, 1, 128, 128, "elementwise", seed=107)),
+    ("wide", _case("d128_g1_n300_full_rope", 1, 300, 2, 2, 128, 128, "headwise", seed=108)),
+    ("wide", _case("d128_g128_n3", 1, 3, 128, 1, 128, 32, "elementwise", seed=113)),
+    ("wide", _case("d128_g4_n700", 1, 700, 8, 2, 128, 32, "elementwise", seed=115)),
+    ("wide", _case("d128_g2_n1_nogate", 2, 1, 4, 2, 128, 0, "none", seed=116)),
+    ("mirror", _case("d128_g8_n200", 1, 200, 32, 4, 128, 32, "elementwise", seed=103)),
+    ("mirror", _case("d128_g4_n700", 1, 700, 8, 2, 128, 32, "elementwise", seed=115)),
+    ("simple", _case("d128_g2_b2_n130", 2, 130, 16, 8, 128, 32, "headwise", seed=102)),
+    ("simple", _case("d256_g4_n300", 1, 300, 8, 2, 256, 64, "elementwise", seed=101)),
+]
+
+
+@pytest.mark.parametrize("kernel,w", KERNEL_CASES, ids=lambda v: v if isinstance(v, str) else v.name)
+def test_prefill_forced_kernel(kernel, w, monkeypatch):
+    print(f"[prefill:{kernel}] {w.name}", flush=True)
+    monkeypatch.setenv("GA_PREFILL_KERNEL", kernel)
+    x = inputs.make_prefill(w)
+    got = host(gpu_prefill(w, x))
+    assert_close(got, oracle_prefill(w, x), w, f"{kernel}:{w.name}")
+
+
 def test_prefill_peaky_rows():
     """Norm weight x4 makes softmax rows peaky, stressing the running-max rescale.
 
