@@ -57,18 +57,19 @@ __device__ __forceinline__ float sigmoid_f32(float z) {
   return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-z * kLog2e));
 }
 
-// cos/sin of pos * inv_freq: the product and the reduction to [-pi, pi] are
-// done in fp64 so that large positions keep full fp32 accuracy.
+// cos/sin of the RoPE angle pos * inv_freq. The angle is formed and reduced
+// in fp64, in revolutions (rev = pos * inv_freq / 2pi, reduced to [-1/2, 1/2]),
+// so large positions keep full fp32 accuracy; the hardware v_sin_f32 /
+// v_cos_f32 then take revolutions directly (measured on gfx950: absolute
+// error <= 1.3e-7 on [-1/2, 1/2]).
 __device__ __forceinline__ void rope_cos_sin(int pos, double inv_freq, float* c, float* s) {
-  const double two_pi = 6.283185307179586476925286766559;
-  double th = (double)pos * inv_freq;
-  double k = rint(th * (1.0 / two_pi));
-  double r = fma(-k, two_pi, th);
-  sincosf((float)r, s, c);
+  const double rev = (double)pos * inv_freq * 0.15915494309189533577;  // 1 / (2 pi)
+  const float r = (float)(rev - rint(rev));
+  *s = __builtin_amdgcn_sinf(r);
+  *c = __builtin_amdgcn_cosf(r);
 }
 
-// Out-of-line copy for paths that evaluate it per element (keeps kernels small).
-__device__ __noinline__ float2 rope_cos_sin_call(int pos, double inv_freq) {
+__device__ __forceinline__ float2 rope_cos_sin_call(int pos, double inv_freq) {
   float c, s;
   rope_cos_sin(pos, inv_freq, &c, &s);
   return make_float2(c, s);
@@ -131,6 +132,19 @@ __device__ __forceinline__ float quad_sum(float x) {
   return x;
 }
 
+// Sum over aligned groups of WIDTH lanes (4, 8, 16 or 32), every lane of a
+// group receiving the total, all lanes active: DPP quad permutations, then
+// half-row and row mirrors (VALU only), then one xor-16 shuffle for 32.
+template <int WIDTH>
+__device__ __forceinline__ float group_sum(float x) {
+  static_assert(WIDTH == 4 || WIDTH == 8 || WIDTH == 16 || WIDTH == 32, "group width");
+  x = quad_sum(x);
+  if (WIDTH >= 8) x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x141, 0xF, 0xF, true));
+  if (WIDTH >= 16) x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x140, 0xF, 0xF, true));
+  if (WIDTH >= 32) x += __shfl_xor(x, 16, 64);
+  return x;
+}
+
 // Workgroup barrier for LDS traffic only: the wave's LDS operations complete
 // before it, while its global loads (including loads into LDS, which the
 // caller waits for with an explicit vmcnt) stay in flight. __syncthreads()
@@ -163,9 +177,9 @@ __device__ __forceinline__ void norm_rope_chunk(float x[8], int c, const float* 
   float ss = 0.f;
 #pragma unroll
   for (int j = 0; j < 8; ++j) ss += x[j] * x[j];
-  ss = sum_xor<LPR>(ss);
+  ss = group_sum<LPR>(ss);
   if (w) {
-    const float inv = 1.0f / sqrtf(ss / (float)D + eps);
+    const float inv = rsqrtf(ss * (1.0f / D) + eps);
 #pragma unroll
     for (int j = 0; j < 8; ++j) x[j] = x[j] * inv * w[j];
   }
