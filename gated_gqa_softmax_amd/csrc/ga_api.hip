@@ -114,11 +114,14 @@ bool prefill_fast(const ga_attn_desc* d) {
   return d->dtype == GA_BF16 && (hd == 64 || hd == 128 || hd == 256) && d->rot_dim % 16 == 0 && grp <= 128;
 }
 
-bool decode_fast(const ga_attn_desc* d) {
+// The split decode kernels address one sequence's cache with 32-bit byte
+// offsets: cache_cap * G * d * 2 must stay below 2^31 (cache_cap 0: shape only).
+bool decode_fast(const ga_attn_desc* d, int32_t cache_cap) {
   const int grp = d->n_q_heads / d->n_kv_heads;
   const int hd = d->head_dim;
   return d->dtype == GA_BF16 && (hd == 64 || hd == 128 || hd == 256) && d->rot_dim % 16 == 0 &&
-         (grp == 1 || grp == 2 || grp == 4 || grp == 8 || grp == 16);
+         (grp == 1 || grp == 2 || grp == 4 || grp == 8 || grp == 16) &&
+         (long long)cache_cap * d->n_kv_heads * hd * 2 < (1LL << 31);
 }
 
 ga_status check_tensor(const void* p, const char* name, const ga_attn_desc* d, bool required = true) {
@@ -378,7 +381,9 @@ ga_status ga_decode_partials(const ga_attn_desc* desc, const void* q, const floa
   ga_status st;
   if ((st = check_desc(desc)) != GA_OK) return st;
   if (desc->batch == 0) return ok();
-  if (!decode_fast(desc)) return fail(GA_ERR_UNSUPPORTED, "decode stages need the fused path (bf16, d in {64,128,256}, rot %% 16 == 0, group in {1,2,4,8,16})");
+  if (!decode_fast(desc, cache_cap))
+    return fail(GA_ERR_UNSUPPORTED, "decode stages need the fused path (bf16, d in {64,128,256}, rot %% 16 == 0, "
+                                    "group in {1,2,4,8,16}, cache_cap * G * d * 2 < 2^31)");
   if ((st = check_decode_common(desc, q, k_cache, v_cache, cache_cap, cache_lens, max_cache_len)) != GA_OK) return st;
   const size_t need = ga_decode_workspace_bytes(desc, max_cache_len);
   if (!workspace || workspace_bytes < need)
@@ -397,7 +402,9 @@ ga_status ga_decode_merge(const ga_attn_desc* desc, const void* q, const void* k
   ga_status st;
   if ((st = check_desc(desc)) != GA_OK) return st;
   if (desc->batch == 0) return ok();
-  if (!decode_fast(desc)) return fail(GA_ERR_UNSUPPORTED, "decode stages need the fused path (bf16, d in {64,128,256}, rot %% 16 == 0, group in {1,2,4,8,16})");
+  if (!decode_fast(desc, cache_cap))
+    return fail(GA_ERR_UNSUPPORTED, "decode stages need the fused path (bf16, d in {64,128,256}, rot %% 16 == 0, "
+                                    "group in {1,2,4,8,16}, cache_cap * G * d * 2 < 2^31)");
   if ((st = check_decode_common(desc, q, k_cache, v_cache, cache_cap, cache_lens, max_cache_len)) != GA_OK) return st;
   if ((st = check_tensor(k_new, "k_new", desc)) != GA_OK) return st;
   if ((st = check_tensor(v_new, "v_new", desc)) != GA_OK) return st;
@@ -427,7 +434,7 @@ ga_status ga_decode(const ga_attn_desc* desc, const void* q, const void* k_new, 
   if ((st = check_tensor(out, "out", desc)) != GA_OK) return st;
   if ((st = check_gate(gate, desc)) != GA_OK) return st;
   hipStream_t s = (hipStream_t)stream;
-  if (decode_fast(desc)) {
+  if (decode_fast(desc, cache_cap)) {
     if ((st = ga_decode_partials(desc, q, q_norm_w, k_cache, v_cache, cache_cap, cache_lens, max_cache_len,
                                  workspace, workspace_bytes, stream)) != GA_OK)
       return st;
@@ -490,7 +497,7 @@ int32_t ga_fast_path(int32_t dtype, int32_t head_dim, int32_t rot_dim, int32_t g
   d.rot_dim = rot_dim;
   d.n_kv_heads = 1;
   d.n_q_heads = group > 0 ? group : 1;
-  return (prefill_fast(&d) ? 1 : 0) | (decode_fast(&d) ? 2 : 0);
+  return (prefill_fast(&d) ? 1 : 0) | (decode_fast(&d, 0) ? 2 : 0);
 }
 
 int32_t ga_version(void) { return 1; }

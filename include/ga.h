@@ -117,6 +117,12 @@ ga_status ga_prefill_keys(const ga_attn_desc* desc, int32_t seq_len,
 
 /* Second stage of ga_prefill (one kernel): causal attention of the normed,
  * rotated q against prepared keys, with the gate fused into the epilogue.
+ * Kernel choice (bf16): a wide kernel (256 query rows per workgroup; d = 128,
+ * rot % 32 == 0, at least 512 token blocks), a mirrored-block kernel (d in
+ * {128, 256}, rot <= d/4) or a simple one (d in {64, 128, 256}); otherwise the
+ * generic kernel. The environment variable GA_PREFILL_KERNEL = wide | mirror |
+ * simple | generic, read at each call, forces a kernel that serves the shape
+ * (for testing and tuning); results agree within the parity tolerance.
  *  k_hat  [B,k_cap,G,d] as written by ga_prefill_keys (k_cap >= seq_len).
  *  v      [B,v_cap,G,d] (v_cap >= seq_len; the raw v input has v_cap = n). */
 ga_status ga_prefill_attention(const ga_attn_desc* desc, int32_t seq_len,
