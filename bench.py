@@ -143,6 +143,8 @@ def time_prefill(torch, api, inputs, accounting, wname, steps, warmup):
                       w.gate_mode)
     khat = torch.empty_like(k)
     out = torch.empty((w.batch, w.seq_len, w.n_q_heads * w.head_dim), dtype=et, device="cuda")
+    ws_attn = torch.empty(max(1, api.ga_prefill_attention_workspace_bytes(d, w.seq_len)), dtype=torch.uint8,
+                          device="cuda")
     stream = torch.cuda.current_stream()
 
     def step(ev0=None, ev1=None):
@@ -150,7 +152,7 @@ def time_prefill(torch, api, inputs, accounting, wname, steps, warmup):
         api.ga_prefill_keys(d, k, None, wk, pos, k_hat=khat, stream=stream)
         if ev0 is not None:
             ev0.record(stream)
-        api.ga_prefill_attention(d, q, khat, v, gate, wq, pos, out=out, stream=stream)
+        api.ga_prefill_attention(d, q, khat, v, gate, wq, pos, out=out, workspace=ws_attn, stream=stream)
         if ev1 is not None:
             ev1.record(stream)
 

@@ -50,9 +50,10 @@ _D = ctypes.POINTER(AttnDesc)
 
 SIGNATURES = {
     "ga_prefill_workspace_bytes": (_S, [_D, _I]),
+    "ga_prefill_attention_workspace_bytes": (_S, [_D, _I]),
     "ga_prefill": (_I, [_D, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _P, _S, _P, _P]),
     "ga_prefill_keys": (_I, [_D, _I, _P, _P, _P, _P, _P, _P, _I, _P]),
-    "ga_prefill_attention": (_I, [_D, _I, _P, _P, _I, _P, _I, _P, _P, _P, _P, _P]),
+    "ga_prefill_attention": (_I, [_D, _I, _P, _P, _I, _P, _I, _P, _P, _P, _P, _S, _P, _P]),
     "ga_decode_split_keys": (_I, []),
     "ga_decode_workspace_bytes": (_S, [_D, _I]),
     "ga_decode": (_I, [_D, _P, _P, _P, _P, _P, _P, _P, _P, _I, _P, _I, _P, _S, _P, _P]),

@@ -92,6 +92,10 @@ def ga_prefill_workspace_bytes(desc: AttnDesc, seq_len: int) -> int:
     return _lib.load().ga_prefill_workspace_bytes(ctypes.byref(desc), seq_len)
 
 
+def ga_prefill_attention_workspace_bytes(desc: AttnDesc, seq_len: int) -> int:
+    return _lib.load().ga_prefill_attention_workspace_bytes(ctypes.byref(desc), seq_len)
+
+
 def ga_decode_workspace_bytes(desc: AttnDesc, max_cache_len: int) -> int:
     return _lib.load().ga_decode_workspace_bytes(ctypes.byref(desc), max_cache_len)
 
@@ -113,9 +117,10 @@ def ga_prefill(desc: AttnDesc, q, k, v, gate=None, q_norm_w=None, k_norm_w=None,
     cap = 0
     if k_cache is not None:
         cap = k_cache.shape[1]
-        ws_bytes = 0
+        ws_bytes = ga_prefill_attention_workspace_bytes(desc, n)
     else:
         ws_bytes = ga_prefill_workspace_bytes(desc, n)
+    if ws_bytes:
         workspace = _workspace(ws_bytes, q.device, workspace)
     st = lib.ga_prefill(ctypes.byref(desc), n, _ptr(q, "q", et), _ptr(k, "k", et), _ptr(v, "v", et),
                         _ptr(gate, "gate", et), _ptr(q_norm_w, "q_norm_w", torch.float32),
@@ -143,15 +148,19 @@ def ga_prefill_keys(desc: AttnDesc, k, v=None, k_norm_w=None, positions=None, k_
 
 
 def ga_prefill_attention(desc: AttnDesc, q, k_hat, v, gate=None, q_norm_w=None, positions=None, out=None,
-                         stream=None) -> torch.Tensor:
+                         workspace=None, stream=None) -> torch.Tensor:
     lib = _lib.load()
     et = _elem_dtype(desc)
     B, n = q.shape[0], q.shape[1]
     if out is None:
         out = torch.empty((B, n, desc.n_q_heads * desc.head_dim), dtype=et, device=q.device)
+    ws_bytes = ga_prefill_attention_workspace_bytes(desc, n)
+    if ws_bytes:
+        workspace = _workspace(ws_bytes, q.device, workspace)
     st = lib.ga_prefill_attention(ctypes.byref(desc), n, _ptr(q, "q", et), _ptr(k_hat, "k_hat", et), k_hat.shape[1],
                                   _ptr(v, "v", et), v.shape[1], _ptr(gate, "gate", et),
                                   _ptr(q_norm_w, "q_norm_w", torch.float32), _ptr(positions, "positions", torch.int32),
+                                  _ptr(workspace, "workspace"), workspace.numel() if workspace is not None else 0,
                                   _ptr(out, "out", et), _stream(stream))
     _check(st, "ga_prefill_attention")
     return out

@@ -96,22 +96,72 @@ bool prefill_wide_ok(const ga_attn_desc* d, int32_t n, int32_t k_cap, int32_t v_
 }
 
 // Kernel choice for prefill attention: automatic, or forced (when the forced
-// kernel serves the shape) by GA_PREFILL_KERNEL = wide | mirror | simple | generic.
-enum PrefillKernel { PK_AUTO, PK_WIDE, PK_MIRROR, PK_SIMPLE, PK_GENERIC };
+// kernel serves the shape) by GA_PREFILL_KERNEL = wide | split | mirror | simple | generic.
+enum PrefillKernel { PK_AUTO, PK_WIDE, PK_SPLIT, PK_MIRROR, PK_SIMPLE, PK_GENERIC };
 PrefillKernel prefill_kernel_request() {
   const char* e = getenv("GA_PREFILL_KERNEL");
   if (!e) return PK_AUTO;
   if (!strcmp(e, "wide")) return PK_WIDE;
+  if (!strcmp(e, "split")) return PK_SPLIT;
   if (!strcmp(e, "mirror")) return PK_MIRROR;
   if (!strcmp(e, "simple")) return PK_SIMPLE;
   if (!strcmp(e, "generic")) return PK_GENERIC;
   return PK_AUTO;
 }
 
+// Split-key balance: the second workgroup of a pair, which also runs the light
+// unit, gets this many fewer stages of the heavy unit, for its extra prologue
+// and epilogue (GA_PREFILL_SPLIT_BIAS overrides it, for tuning).
+int split_overhead_stages() {
+  const char* e = getenv("GA_PREFILL_SPLIT_BIAS");
+  if (e && *e) {
+    const int v = atoi(e);
+    return v < 0 ? 0 : (v > 64 ? 64 : v);
+  }
+  return 8;
+}
+
+// The kernel prefill attention runs for a shape (automatic choice: wide, then
+// mirrored, then simple, then generic; the split-key mode only on request).
+PrefillKernel prefill_choice(const ga_attn_desc* d, int32_t n, int32_t k_cap, int32_t v_cap);
+
+// Mirrored-kernel units (two blocks of 64 rows) and unit pairs per (batch, KV head).
+void split_shape(const ga_attn_desc* d, int32_t n, int* nunits, int* npairs) {
+  const int tb = 64 / (d->n_q_heads / d->n_kv_heads);
+  const int nblk = (n + tb - 1) / tb;
+  *nunits = (nblk + 1) / 2;
+  *npairs = (*nunits + 1) / 2;
+}
+
+// Workspace bytes of the attention stage (nonzero only for the split-key mode).
+size_t prefill_attn_ws_bytes(const ga_attn_desc* d, int32_t n, int32_t k_cap, int32_t v_cap) {
+  if (d->batch <= 0 || n <= 0 || prefill_choice(d, n, k_cap, v_cap) != PK_SPLIT) return 0;
+  int nunits, npairs;
+  split_shape(d, n, &nunits, &npairs);
+  return prefill_split_bytes((long)d->batch * d->n_kv_heads * npairs, d->head_dim);
+}
+
 bool prefill_fast(const ga_attn_desc* d) {
   const int grp = d->n_q_heads / d->n_kv_heads;
   const int hd = d->head_dim;
   return d->dtype == GA_BF16 && (hd == 64 || hd == 128 || hd == 256) && d->rot_dim % 16 == 0 && grp <= 128;
+}
+
+PrefillKernel prefill_choice(const ga_attn_desc* d, int32_t n, int32_t k_cap, int32_t v_cap) {
+  const PrefillKernel req = prefill_kernel_request();
+  // (the mirrored kernel numbers output rows (b, token, head) in 32 bits)
+  const bool v2 = prefill_v2_ok(d, k_cap, v_cap) && (long long)d->batch * n * d->n_q_heads < (1LL << 31);
+  if (req == PK_WIDE && prefill_wide_ok(d, n, k_cap, v_cap, false)) return PK_WIDE;
+  if (req == PK_SPLIT && v2) return PK_SPLIT;
+  if (req == PK_MIRROR && v2) return PK_MIRROR;
+  if (req == PK_SIMPLE && prefill_fast(d)) return PK_SIMPLE;
+  if (req == PK_GENERIC) return PK_GENERIC;
+  if (prefill_wide_ok(d, n, k_cap, v_cap, true)) return PK_WIDE;
+  // (the split-key mode is opt-in: on the measured shapes its extra
+  // workgroup prologues and epilogues cost more than the balance gains)
+  if (v2) return PK_MIRROR;
+  if (prefill_fast(d)) return PK_SIMPLE;
+  return PK_GENERIC;
 }
 
 // The split decode kernels address one sequence's cache with 32-bit byte
@@ -174,18 +224,19 @@ ga_status prefill_keys_impl(const ga_attn_desc* desc, int32_t n, const void* k, 
   return hip_status(launch_prep_keys(pp, desc->dtype == GA_BF16, stream), "prefill keys launch");
 }
 
+// workspace: at least prefill_attn_ws_bytes(desc, n, k_cap, v_cap) bytes
+// (checked by the callers), 16-byte aligned; may be NULL when that is 0.
 ga_status prefill_attn_impl(const ga_attn_desc* desc, int32_t n, const void* q, const void* k_hat,
                             int32_t k_cap, const void* v, int32_t v_cap, const void* gate,
-                            const float* q_norm_w, const int32_t* positions, void* out, hipStream_t stream) {
+                            const float* q_norm_w, const int32_t* positions, void* workspace, void* out,
+                            hipStream_t stream) {
   const int H = desc->n_q_heads, G = desc->n_kv_heads, d = desc->head_dim;
   const int grp = H / G;
-  const PrefillKernel req = prefill_kernel_request();
-  bool wide = prefill_wide_ok(desc, n, k_cap, v_cap, req != PK_WIDE);
-  bool v2 = !wide && prefill_v2_ok(desc, k_cap, v_cap);
-  bool v1 = !wide && !v2 && prefill_fast(desc);
-  if (req == PK_MIRROR && prefill_v2_ok(desc, k_cap, v_cap)) wide = false, v2 = true, v1 = false;
-  if (req == PK_SIMPLE && prefill_fast(desc)) wide = false, v2 = false, v1 = true;
-  if (req == PK_GENERIC) wide = false, v2 = false, v1 = false;
+  const PrefillKernel choice = prefill_choice(desc, n, k_cap, v_cap);
+  const bool wide = choice == PK_WIDE;
+  const bool split = choice == PK_SPLIT;
+  const bool v2 = split || choice == PK_MIRROR;
+  const bool v1 = choice == PK_SIMPLE;
   if (wide || v2 || v1) {
     PrefillParams pp;
     memset(&pp, 0, sizeof(pp));
@@ -212,6 +263,17 @@ ga_status prefill_attn_impl(const ga_attn_desc* desc, int32_t n, const void* q, 
     pp.scale_log2 = scale_of(desc) * 1.4426950408889634f;
     fill_inv_freq(desc, pp.inv_freq);
     if ((long long)pp.B * G * pp.nblk > 0x7fffffffLL) return fail(GA_ERR_UNSUPPORTED, "grid too large");
+    if (split) {
+      split_shape(desc, n, &pp.nunits, &pp.npairs);
+      const size_t slots = (size_t)pp.B * G * pp.npairs;
+      auto r256 = [](size_t x) { return (x + 255) / 256 * 256; };
+      char* base = (char*)workspace;
+      pp.part = (float*)base;
+      pp.part_lse = (float*)(base + r256(slots * 128 * d * 4));
+      pp.sync = (unsigned*)(base + r256(slots * 128 * d * 4) + r256(slots * 128 * 4));
+      pp.split = 1;
+      pp.split_ovh = split_overhead_stages();
+    }
     if (wide) return hip_status(launch_prefill_wide(pp, d, desc->gate_mode, stream), "prefill attention launch");
     if (v2) return hip_status(launch_prefill_v2(pp, d, desc->gate_mode, stream), "prefill attention launch");
     return hip_status(launch_prefill_mfma(pp, d, desc->gate_mode, stream), "prefill attention launch");
@@ -289,10 +351,15 @@ void fill_decode_params(DecodeParams& dp, const ga_attn_desc* desc, const void* 
 
 extern "C" {
 
+size_t ga_prefill_attention_workspace_bytes(const ga_attn_desc* desc, int32_t seq_len) {
+  if (check_desc(desc) != GA_OK || seq_len < 0) return 0;
+  return prefill_attn_ws_bytes(desc, seq_len, seq_len, seq_len);
+}
+
 size_t ga_prefill_workspace_bytes(const ga_attn_desc* desc, int32_t seq_len) {
   if (check_desc(desc) != GA_OK || seq_len < 0) return 0;
   const size_t elems = (size_t)desc->batch * seq_len * desc->n_kv_heads * desc->head_dim;
-  return round_up(elems * elem_bytes(desc), 256);
+  return round_up(elems * elem_bytes(desc), 256) + prefill_attn_ws_bytes(desc, seq_len, seq_len, seq_len);
 }
 
 ga_status ga_prefill_keys(const ga_attn_desc* desc, int32_t seq_len, const void* k, const void* v,
@@ -314,7 +381,8 @@ ga_status ga_prefill_keys(const ga_attn_desc* desc, int32_t seq_len, const void*
 
 ga_status ga_prefill_attention(const ga_attn_desc* desc, int32_t seq_len, const void* q, const void* k_hat,
                                int32_t k_cap, const void* v, int32_t v_cap, const void* gate,
-                               const float* q_norm_w, const int32_t* positions, void* out, void* stream) {
+                               const float* q_norm_w, const int32_t* positions, void* workspace,
+                               size_t workspace_bytes, void* out, void* stream) {
   ga_status st;
   if ((st = check_desc(desc)) != GA_OK) return st;
   if (seq_len < 0) return fail(GA_ERR_BAD_SHAPE, "seq_len %d < 0", seq_len);
@@ -326,8 +394,12 @@ ga_status ga_prefill_attention(const ga_attn_desc* desc, int32_t seq_len, const 
   if ((st = check_gate(gate, desc)) != GA_OK) return st;
   if (k_cap < seq_len || v_cap < seq_len)
     return fail(GA_ERR_BAD_SHAPE, "k_cap %d / v_cap %d < seq_len %d", k_cap, v_cap, seq_len);
+  const size_t need = prefill_attn_ws_bytes(desc, seq_len, k_cap, v_cap);
+  if (need && (!workspace || workspace_bytes < need))
+    return fail(GA_ERR_WORKSPACE, "workspace %zu bytes < %zu required", workspace ? workspace_bytes : 0, need);
+  if (need && !aligned(workspace, 16)) return fail(GA_ERR_MISALIGNED, "workspace is not 16-byte aligned");
   return prefill_attn_impl(desc, seq_len, q, k_hat, k_cap, v, v_cap,
-                           desc->gate_mode == GA_GATE_NONE ? nullptr : gate, q_norm_w, positions, out,
+                           desc->gate_mode == GA_GATE_NONE ? nullptr : gate, q_norm_w, positions, workspace, out,
                            (hipStream_t)stream);
 }
 
@@ -346,6 +418,7 @@ ga_status ga_prefill(const ga_attn_desc* desc, int32_t seq_len, const void* q, c
   if ((st = check_gate(gate, desc)) != GA_OK) return st;
   void* khat;
   int32_t kcap;
+  size_t khat_bytes = 0;
   if (k_cache) {
     if ((st = check_tensor(k_cache, "k_cache", desc)) != GA_OK) return st;
     if ((st = check_tensor(v_cache, "v_cache", desc)) != GA_OK) return st;
@@ -354,17 +427,21 @@ ga_status ga_prefill(const ga_attn_desc* desc, int32_t seq_len, const void* q, c
     kcap = cache_cap;
   } else {
     if (v_cache) return fail(GA_ERR_NULL_ARG, "v_cache given without k_cache");
-    const size_t need = ga_prefill_workspace_bytes(desc, seq_len);
-    if (!workspace || workspace_bytes < need)
-      return fail(GA_ERR_WORKSPACE, "workspace %zu bytes < %zu required", workspace ? workspace_bytes : 0, need);
-    if (!aligned(workspace, 16)) return fail(GA_ERR_MISALIGNED, "workspace is not 16-byte aligned");
     khat = workspace;
     kcap = seq_len;
+    khat_bytes = round_up((size_t)desc->batch * seq_len * desc->n_kv_heads * desc->head_dim * elem_bytes(desc), 256);
   }
+  // attention part of the workspace: after K-hat (no cache) or from its start
+  const size_t attn_need = prefill_attn_ws_bytes(desc, seq_len, kcap, seq_len);
+  const size_t need = khat_bytes + attn_need;
+  if (need && (!workspace || workspace_bytes < need))
+    return fail(GA_ERR_WORKSPACE, "workspace %zu bytes < %zu required", workspace ? workspace_bytes : 0, need);
+  if (need && !aligned(workspace, 16)) return fail(GA_ERR_MISALIGNED, "workspace is not 16-byte aligned");
+  void* attn_ws = attn_need ? (void*)((char*)workspace + khat_bytes) : nullptr;
   hipStream_t s = (hipStream_t)stream;
   if ((st = prefill_keys_impl(desc, seq_len, k, v, k_norm_w, positions, khat, v_cache, kcap, s)) != GA_OK) return st;
   return prefill_attn_impl(desc, seq_len, q, khat, kcap, v, seq_len,
-                           desc->gate_mode == GA_GATE_NONE ? nullptr : gate, q_norm_w, positions, out, s);
+                           desc->gate_mode == GA_GATE_NONE ? nullptr : gate, q_norm_w, positions, attn_ws, out, s);
 }
 
 int32_t ga_decode_split_keys(void) { return kDecodeChunk; }

@@ -39,6 +39,7 @@ namespace ga {
 
 template <int D>
 constexpr int kMirrorStages = (D == 256) ? 2 : 3;
+constexpr int kSc1 = 16;  // buffer load/store cache bits: coherent at device (agent) scope
 template <int D>
 using MirrorShape = TileShape<D, kMirrorStages<D>>;
 
@@ -52,17 +53,18 @@ __device__ __forceinline__ uint16_t* v2_qrow(unsigned char* smem, int r) {
 
 // One pipeline step: wait for stage st (buffer BUF), refill the buffer freed
 // by the previous step, and run this wave's tile if it has visible keys.
+// Stages run up to st_end (exclusive).
 template <int D, int BUF>
-__device__ __forceinline__ void v2_step(unsigned char* smem, WaveState<D>& ws, i32x4_t krs, i32x4_t vrs, int koff, int voff, int w, int st, int nst,
+__device__ __forceinline__ void v2_step(unsigned char* smem, WaveState<D>& ws, i32x4_t krs, i32x4_t vrs, int koff, int voff, int w, int st, int st_end,
                                         int kv_row_bytes, int phase, int wave_min_tok, int wave_max_tok,
                                         int my_lim_tok, int n, float sl2, int hi) {
   typedef MirrorShape<D> S;
-  if (S::NSTAGE == 3 && st + 1 < nst)
+  if (S::NSTAGE == 3 && st + 1 < st_end)
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * S::LOADS_PER_WAVE) : "memory");
   else
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   lds_barrier();
-  if (st + S::NSTAGE - 1 < nst)
+  if (st + S::NSTAGE - 1 < st_end)
     stage_issue<D, kMirrorStages<D>, (BUF + S::NSTAGE - 1) % S::NSTAGE>(smem, krs, vrs, koff, voff, w, st + S::NSTAGE - 1, kv_row_bytes);
   const int k0 = st * S::ST + phase * 32;
   if (k0 <= wave_max_tok) {
@@ -85,19 +87,20 @@ __device__ __forceinline__ void rope_quarter(float* x, const float2* cs) {
   }
 }
 
-template <int D, int GATE>
+// Stages (64 keys each) that the queries of unit u (blocks 2u and 2u + 1) see.
+__device__ __forceinline__ int v2_unit_stages(int u, int TB, int n) { return (min(n, (u + 1) * 2 * TB) + 63) / 64; }
+
+template <int D, int GATE, bool SPLIT>
 __global__ __launch_bounds__(512) void prefill_v2_kernel(const PrefillParams p) {
   typedef MirrorShape<D> S;
   static_assert(4 * 32 * D * 4 <= S::BUF_BYTES, "the phase merge reuses the stage buffers");
   __shared__ __attribute__((aligned(1024))) unsigned char smem[S::BUF_BYTES];
   __shared__ float2 table[2048];
   __shared__ float ml_x[4][64][2];
+  __shared__ float lse_x[4][32];  // split mode: log2-domain log-sum-exp of each row
+  __shared__ unsigned s_arrival, s_ready;
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index (uniform)
-  const int l32 = lane & 31;
-  const int hi = lane >> 5;
+  const int w = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);  // wave index (uniform)
   // wave -> (row group, phase): each SIMD (w % 4) gets one light and one heavy wave
   const int rg = (w < 4) ? w : ((w + 2) & 3);
   const int phase = (w < 4) ? 0 : 1;
@@ -108,12 +111,57 @@ __global__ __launch_bounds__(512) void prefill_v2_kernel(const PrefillParams p) 
   const int bg = u % nBG;
   const int b = bg / p.G;
   const int g = bg % p.G;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int l32 = lane & 31;
+  const int hi = lane >> 5;
   const int TB = p.TB;
   const int n = p.n;
-  const int blk_heavy = p.nblk - 1 - pair;
-  const int blk_light = (pair < blk_heavy) ? pair : -1;   // -1: no light block (odd middle)
-  const int kend = min(n, blk_heavy * TB + TB);
-  const int nst = (kend + S::ST - 1) / S::ST;
+  const int grp = p.grp;
+  const int nH = p.H;
+  const int nG = p.G;
+  const int nblk = p.nblk;
+  const long k_bstride = p.k_bstride;
+  const long v_bstride = p.v_bstride;
+
+  // ---- work of this workgroup -------------------------------------------------
+  // Two blocks (A in row groups 0-1, B in row groups 2-3) and a range of key
+  // stages; seg_slot >= 0 marks a partial result that meets the rest of the
+  // same key range in the workspace.
+  //  * mirrored mode: blocks (pair, nblk-1-pair), all their stages.
+  //  * split mode: units of two adjacent blocks; unit pair i = (light unit i,
+  //    heavy unit U-1-i). Workgroups, in launch order: the heavy units' heads
+  //    (stages [0, c_i)), their tails ([c_i, s_h)) and the light units, last
+  //    to first. Pieces shrink along that order, so the compute units that
+  //    finish a short tail first take the longest light units: each pair's
+  //    work, s_h + s_l stages, is shared by two compute units.
+  int blk_light, blk_heavy, st_lo = 0, st_hi = 0x7fffffff, seg_slot = -1;
+  if (!SPLIT) {
+    blk_heavy = nblk - 1 - pair;
+    blk_light = (pair < blk_heavy) ? pair : -1;   // -1: no light block (odd middle)
+  } else {
+    const int U = p.nunits, P = p.npairs, L = U / 2;  // light units: i < U-1-i
+    int unit;
+    if (pair < 2 * P) {
+      const int i = (pair < P) ? pair : pair - P;
+      unit = U - 1 - i;
+      const int s_h = v2_unit_stages(unit, TB, n);
+      const int s_l = (i < unit) ? v2_unit_stages(i, TB, n) : 0;
+      const bool split = s_h >= 2;
+      const int c = split ? min(max((s_h + s_l + (s_l > 0 ? p.split_ovh : 0) + 1) / 2, 1), s_h - 1) : s_h;
+      if (pair >= P && !split) return;  // (no tail)
+      st_lo = (pair < P) ? 0 : c;
+      st_hi = (pair < P) ? c : s_h;
+      seg_slot = split ? bg * P + i : -1;
+    } else {
+      unit = L - 1 - (pair - 2 * P);
+    }
+    blk_light = 2 * unit;
+    blk_heavy = (2 * unit + 1 < nblk) ? 2 * unit + 1 : -1;
+  }
+  const int kend = min(n, max(blk_light, blk_heavy) * TB + TB);
+  const int nst = min(st_hi, (kend + S::ST - 1) / S::ST);  // stages run over [st_lo, nst)
 
   // this lane's query row
   const int my_blk = (rg < 2) ? blk_light : blk_heavy;
@@ -121,9 +169,9 @@ __global__ __launch_bounds__(512) void prefill_v2_kernel(const PrefillParams p) 
   const int my_hh = my_local / TB;
   const int my_tt = my_local - my_hh * TB;
   const int my_tok0 = my_blk * TB + my_tt;
-  const bool my_valid = (my_blk >= 0) && (my_hh < p.grp) && (my_tok0 < n);
+  const bool my_valid = (my_blk >= 0) && (my_hh < grp) && (my_tok0 < n);
   const int my_tok = my_valid ? my_tok0 : 0x3fffffff;
-  const int my_h = g * p.grp + my_hh;
+  const int my_h = g * grp + my_hh;
   int wave_max_tok = my_valid ? my_tok : -1;
   int wave_min_tok = my_tok;
 #pragma unroll
@@ -139,10 +187,10 @@ __global__ __launch_bounds__(512) void prefill_v2_kernel(const PrefillParams p) 
   // ---- direct-to-LDS stage loads --------------------------------------------
   // Buffer resources cover keys [0, n) of this (b, g): rows past the end read
   // as zeros (out-of-range buffer loads return 0), which the mask then hides.
-  const int kv_row_bytes = p.G * D * 2;
+  const int kv_row_bytes = nG * D * 2;
   const uint32_t valid_bytes = (uint32_t)((n - 1) * kv_row_bytes + D * 2);
-  const i32x4_t krs = buffer_desc(p.khat + (long)b * p.k_bstride + (long)g * D, valid_bytes);
-  const i32x4_t vrs = buffer_desc(p.v + (long)b * p.v_bstride + (long)g * D, valid_bytes);
+  const i32x4_t krs = buffer_desc(p.khat + (long)b * k_bstride + (long)g * D, valid_bytes);
+  const i32x4_t vrs = buffer_desc(p.v + (long)b * v_bstride + (long)g * D, valid_bytes);
   int koff, voff;
   {
     // load j covers rows row0 + 8j*ROWS_PER_LOAD (multiples of 16 apart): same swizzle
@@ -170,11 +218,11 @@ __global__ __launch_bounds__(512) void prefill_v2_kernel(const PrefillParams p) 
     const int qblk = qside ? blk_heavy : blk_light;
     const int qhh = (qrow & 63) / TB;
     const int qtok = qblk * TB + qtt;
-    const bool qvalid = (qblk >= 0) && (qhh < p.grp) && (qtok < n);
+    const bool qvalid = (qblk >= 0) && (qhh < grp) && (qtok < n);
     // unconditional (a branch around the loads would make the wave wait for
     // them at its join): rows outside the block read row 0 and are never stored
     const uint16_t* src =
-        p.q + (((long)b * n + (qvalid ? qtok : 0)) * p.H + g * p.grp + (qvalid ? qhh : 0)) * D + qq * QE;
+        p.q + (((long)b * n + (qvalid ? qtok : 0)) * nH + g * grp + (qvalid ? qhh : 0)) * D + qq * QE;
 #pragma unroll
     for (int i = 0; i < QE / 8; ++i) qraw[i] = *(const u32x4_t*)(src + 8 * i);
   }
@@ -215,8 +263,9 @@ __global__ __launch_bounds__(512) void prefill_v2_kernel(const PrefillParams p) 
   // The first stage loads go out only now: every load above has been consumed,
   // so no later wait of the compiler (which does not count these loads) can
   // end up waiting for them.
-  if (nst > 0) stage_issue<D, kMirrorStages<D>, 0>(smem, krs, vrs, koff, voff, w, 0, kv_row_bytes);
-  if (S::NSTAGE == 3 && nst > 1) stage_issue<D, kMirrorStages<D>, 1>(smem, krs, vrs, koff, voff, w, 1, kv_row_bytes);
+  if (st_lo < nst) stage_issue<D, kMirrorStages<D>, 0>(smem, krs, vrs, koff, voff, w, st_lo, kv_row_bytes);
+  if (S::NSTAGE == 3 && st_lo + 1 < nst)
+    stage_issue<D, kMirrorStages<D>, 1>(smem, krs, vrs, koff, voff, w, st_lo + 1, kv_row_bytes);
   lds_barrier();
   {
     float x[QE];
@@ -276,7 +325,7 @@ __global__ __launch_bounds__(512) void prefill_v2_kernel(const PrefillParams p) 
   }
 
   // ---- main loop, unrolled over the stage buffers -----------------------------
-  for (int st0 = 0; st0 < nst; st0 += S::NSTAGE) {
+  for (int st0 = st_lo; st0 < nst; st0 += S::NSTAGE) {
     v2_step<D, 0>(smem, ws, krs, vrs, koff, voff, w, st0, nst, kv_row_bytes, phase, wave_min_tok, wave_max_tok,
                   my_lim_tok, n, sl2, hi);
     if (st0 + 1 < nst)
@@ -297,22 +346,30 @@ __global__ __launch_bounds__(512) void prefill_v2_kernel(const PrefillParams p) 
   constexpr int NIT = 16 / RPI;  // instructions for the wave's 16 rows
   const int qc = lane % LPR;
   const int rsub = lane / LPR;
-  long erow[NIT];  // row index (b, token, head) of each row of this wave's share, -1 if none
-  u32x4_t graw[NIT];
-  uint16_t ghead[NIT];
-#pragma unroll
-  for (int it = 0; it < NIT; ++it) {
+  // row index (b, token, head) of row it of this wave's share, -1 if none (B*n*H < 2^31)
+  auto row_index = [&](int it) {
     const int local = (rg & 1) * 32 + phase * 16 + it * RPI + rsub;  // row within the token block
     const int blk = (rg < 2) ? blk_light : blk_heavy;
     const int hh = local / TB;
     const int tt = local - hh * TB;
     const int tok = blk * TB + tt;
-    const bool valid = (blk >= 0) && (hh < p.grp) && (tok < n);
-    erow[it] = valid ? ((long)b * n + tok) * p.H + g * p.grp + hh : -1;
+    const bool valid = (blk >= 0) && (hh < grp) && (tok < n);
+    return valid ? (b * n + tok) * nH + g * grp + hh : -1;
+  };
+  // Mirrored mode: row indices and gate values are fetched before the merge
+  // so that their latency overlaps it. Split mode forms both after the merge,
+  // when the accumulators are free: the registers are needed there.
+  int erow[NIT];
+  u32x4_t graw[NIT];
+  uint16_t ghead[NIT];
+#pragma unroll
+  for (int it = 0; it < NIT; ++it) {
+    erow[it] = SPLIT ? -1 : row_index(it);
+    const bool valid = erow[it] >= 0;
     graw[it] = u32x4_t{0, 0, 0, 0};
     ghead[it] = 0;
-    if (valid && GATE == 2) graw[it] = *(const u32x4_t*)(p.gate + erow[it] * D + qc * 8);
-    if (valid && GATE == 1) ghead[it] = p.gate[erow[it]];
+    if (!SPLIT && valid && GATE == 2) graw[it] = *(const u32x4_t*)(p.gate + (long)erow[it] * D + qc * 8);
+    if (!SPLIT && valid && GATE == 1) ghead[it] = p.gate[erow[it]];
   }
 
   lds_barrier();  // stage buffers are free; the gate reads stay in flight
@@ -351,7 +408,9 @@ __global__ __launch_bounds__(512) void prefill_v2_kernel(const PrefillParams p) 
       auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_run), __float_as_uint(l_run), false, false);
       l_run = __uint_as_float(r[0]) + __uint_as_float(r[1]);
     }
-    const float inv_l = 1.0f / l_run;
+    // a row of a partial key range may see no key at all (l = 0): output 0, weight 0
+    const float inv_l = (l_run > 0.f) ? 1.0f / l_run : 0.f;
+    if (SPLIT && hi == 0) lse_x[rg][l32] = (l_run > 0.f) ? mt + log2f(l_run) : -INFINITY;
     // lane (l32, hi) holds row l32, elements mb*32 + ig*8 + hi*4 + [0, 4)
 #pragma unroll
     for (int mb = 0; mb < D / 32; ++mb)
@@ -365,13 +424,105 @@ __global__ __launch_bounds__(512) void prefill_v2_kernel(const PrefillParams p) 
       }
   }
   lds_barrier();
+
+  // ---- partial key range: the first of the two workgroups to get here
+  // leaves its normalised rows and their log-sum-exp in the workspace; the
+  // second combines them with its own (weights 2^(lse - max)) and stores.
+  bool merge = false;
+  if (SPLIT && seg_slot >= 0) {
+    unsigned* cnt = p.sync + 2 * seg_slot;
+    // this slot's 128 rows; the 16-byte chunk h (0, 1) of lane qc of row r sits
+    // at chunk h * LPR + qc of the row, so each store or load instruction
+    // covers whole contiguous rows
+    const __amdgpu_buffer_rsrc_t prs =
+        __builtin_amdgcn_make_buffer_rsrc(p.part + (size_t)seg_slot * 128 * D, 0, 128 * D * 4, 0x00020000);
+    float* plse = p.part_lse + (size_t)seg_slot * 128;
+    if (tid == 0) s_arrival = atomicAdd(cnt, 1u);
+    lds_barrier();
+    merge = s_arrival != 0;
+    // The partial rows move with device-coherent (sc1) buffer loads and
+    // stores, which skip the compute units' non-coherent caches, so neither
+    // side needs a cache-wide invalidate (which would also drop the K/V
+    // stages other workgroups on the same XCD are streaming).
+    if (!merge) {
+#pragma unroll
+      for (int it = 0; it < NIT; ++it) {
+        if (row_index(it) < 0) continue;
+        const int lr = phase * 16 + it * RPI + rsub;
+        const int rbase = (rg * 32 + lr) * D * 4;
+        const f32x4_t a = *(const f32x4_t*)(xr + lr * D + (((2 * qc) ^ (lr & 15)) << 2));
+        const f32x4_t c = *(const f32x4_t*)(xr + lr * D + (((2 * qc + 1) ^ (lr & 15)) << 2));
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, a), prs, rbase + qc * 16, 0, kSc1);
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, c), prs, rbase + (LPR + qc) * 16, 0, kSc1);
+        if (qc == 0) __hip_atomic_store(plse + rg * 32 + lr, lse_x[rg][lr], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      // every thread's rows are ordered before the flag (release at agent scope,
+      // no invalidate), then one thread raises it
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+      __syncthreads();
+      if (tid == 0) __hip_atomic_store(cnt + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      return;
+    }
+    // The other workgroup has already arrived and is only storing its rows,
+    // so this wait ends; the bound is a guard (rows read as NaN if it hit).
+    if (tid == 0) {
+      unsigned spins = 0;
+      while (__hip_atomic_load(cnt + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0u && ++spins < (1u << 20))
+        __builtin_amdgcn_s_sleep(8);
+      s_ready = (spins < (1u << 20)) ? 1u : 0u;
+      // leave the words zero for the next launch
+      __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(cnt + 1, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __syncthreads();
+  }
+  const bool ready = !SPLIT || !merge || s_ready != 0;
+  // the other part's rows, all loads in flight before the first use
+  f32x4_t tpart[SPLIT ? NIT : 1][2];
+  if (SPLIT && merge) {
+    const __amdgpu_buffer_rsrc_t prs =
+        __builtin_amdgcn_make_buffer_rsrc(p.part + (size_t)seg_slot * 128 * D, 0, 128 * D * 4, 0x00020000);
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) {
+      const int lr = phase * 16 + it * RPI + rsub;
+      const int rbase = (rg * 32 + lr) * D * 4;
+      tpart[it][0] = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(prs, rbase + qc * 16, 0, kSc1));
+      tpart[it][1] =
+          __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(prs, rbase + (LPR + qc) * 16, 0, kSc1));
+    }
+  }
 #pragma unroll
   for (int it = 0; it < NIT; ++it) {
-    if (erow[it] < 0) continue;
+    const int er = SPLIT ? row_index(it) : erow[it];
+    if (er < 0) continue;
     const int lr = phase * 16 + it * RPI + rsub;
     const f32x4_t y0 = *(const f32x4_t*)(xr + lr * D + (((2 * qc) ^ (lr & 15)) << 2));
     const f32x4_t y1 = *(const f32x4_t*)(xr + lr * D + (((2 * qc + 1) ^ (lr & 15)) << 2));
     float y[8] = {y0[0], y0[1], y0[2], y0[3], y1[0], y1[1], y1[2], y1[3]};
+    if (SPLIT && GATE == 2) graw[it] = *(const u32x4_t*)(p.gate + (long)er * D + qc * 8);
+    if (SPLIT && GATE == 1) ghead[it] = p.gate[er];
+    if (SPLIT && merge) {
+      const f32x4_t t0 = tpart[SPLIT ? it : 0][0];
+      const f32x4_t t1 = tpart[SPLIT ? it : 0][1];
+      // head part (stages from 0) first, whichever workgroup arrived last, so
+      // the result does not depend on the arrival order
+      const bool own_head = st_lo == 0;
+      const float lo = lse_x[rg][lr];
+      const float lt = ready ? __hip_atomic_load(p.part_lse + (size_t)seg_slot * 128 + rg * 32 + lr, __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT)
+                             : __builtin_nanf("");
+      const float lh = own_head ? lo : lt, ltl = own_head ? lt : lo;
+      const float mx = fmaxf(lh, ltl);  // finite: the head range holds key 0 of every row
+      const float wh = __builtin_amdgcn_exp2f(lh - mx);
+      const float wt = __builtin_amdgcn_exp2f(ltl - mx);
+      const float inv = 1.0f / (wh + wt);
+      const float tv[8] = {t0[0], t0[1], t0[2], t0[3], t1[0], t1[1], t1[2], t1[3]};
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) {
+        const float yh = own_head ? y[jj] : tv[jj], yt = own_head ? tv[jj] : y[jj];
+        y[jj] = __builtin_fmaf(yh, wh, yt * wt) * inv;
+      }
+    }
     if (GATE == 2) {
       float z[8];
       unpack8(graw[it], z);
@@ -382,21 +533,47 @@ __global__ __launch_bounds__(512) void prefill_v2_kernel(const PrefillParams p) 
 #pragma unroll
       for (int jj = 0; jj < 8; ++jj) y[jj] *= hg;
     }
-    *(u32x4_t*)(p.out + erow[it] * D + qc * 8) = pack8(y);
+    *(u32x4_t*)(p.out + (long)er * D + qc * 8) = pack8(y);
+  }
+}
+
+__global__ void zero_words_kernel(unsigned* w, long nwords) {
+  const long i = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < nwords) w[i] = 0u;
+}
+
+template <int D, bool SPLIT>
+static void launch_v2_gate(const PrefillParams& p, int gate_mode, long grid, hipStream_t s) {
+  switch (gate_mode) {
+    case 0: hipLaunchKernelGGL((prefill_v2_kernel<D, 0, SPLIT>), dim3((unsigned)grid), dim3(512), 0, s, p); break;
+    case 1: hipLaunchKernelGGL((prefill_v2_kernel<D, 1, SPLIT>), dim3((unsigned)grid), dim3(512), 0, s, p); break;
+    default: hipLaunchKernelGGL((prefill_v2_kernel<D, 2, SPLIT>), dim3((unsigned)grid), dim3(512), 0, s, p); break;
   }
 }
 
 template <int D>
 static hipError_t launch_v2_d(const PrefillParams& p, int gate_mode, hipStream_t s) {
-  const int npairs = (p.nblk + 1) / 2;
-  const long grid = (long)p.B * p.G * npairs;
-  if (grid <= 0) return hipSuccess;
-  switch (gate_mode) {
-    case 0: hipLaunchKernelGGL((prefill_v2_kernel<D, 0>), dim3((unsigned)grid), dim3(512), 0, s, p); break;
-    case 1: hipLaunchKernelGGL((prefill_v2_kernel<D, 1>), dim3((unsigned)grid), dim3(512), 0, s, p); break;
-    default: hipLaunchKernelGGL((prefill_v2_kernel<D, 2>), dim3((unsigned)grid), dim3(512), 0, s, p); break;
+  if (p.split) {
+    // heads and tails of the heavy units, then the light units; the arrival
+    // words start at zero
+    const long slots = (long)p.B * p.G * p.npairs;
+    const long grid = (long)p.B * p.G * (2L * p.npairs + p.nunits / 2);
+    if (grid <= 0) return hipSuccess;
+    const long nwords = 2 * slots;
+    hipLaunchKernelGGL(zero_words_kernel, dim3((unsigned)((nwords + 255) / 256)), dim3(256), 0, s, p.sync, nwords);
+    launch_v2_gate<D, true>(p, gate_mode, grid, s);
+  } else {
+    const int npairs = (p.nblk + 1) / 2;
+    const long grid = (long)p.B * p.G * npairs;
+    if (grid <= 0) return hipSuccess;
+    launch_v2_gate<D, false>(p, gate_mode, grid, s);
   }
   return hipGetLastError();
+}
+
+size_t prefill_split_bytes(long slots, int D) {
+  auto r256 = [](size_t x) { return (x + 255) / 256 * 256; };
+  return r256((size_t)slots * 128 * D * 4) + r256((size_t)slots * 128 * 4) + r256((size_t)slots * 2 * 4);
 }
 
 hipError_t launch_prefill_v2(const PrefillParams& p, int D, int gate_mode, hipStream_t s) {

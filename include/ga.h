@@ -84,8 +84,16 @@ typedef struct {
 
 /* ---- prefill ------------------------------------------------------------ */
 
+/* Workspace ga_prefill_attention needs (0 when the kernel chosen for the
+ * shape needs none). The split-key mode of the mirrored kernel keeps, per
+ * pair of token-block units of a (batch, KV head), one partial result of
+ * 128 rows: 128*(d+1) floats plus two 32-bit words, 256-byte aligned parts.
+ * The value depends on GA_PREFILL_KERNEL as read at the time of the call. */
+size_t ga_prefill_attention_workspace_bytes(const ga_attn_desc* desc, int32_t seq_len);
+
 /* Workspace ga_prefill needs when it is given no KV cache: room for K-hat
- * (B*n*G*d elements, rounded up to 256 bytes). */
+ * (B*n*G*d elements, rounded up to 256 bytes) followed by the attention
+ * workspace. With a KV cache it needs only the attention workspace. */
 size_t ga_prefill_workspace_bytes(const ga_attn_desc* desc, int32_t seq_len);
 
 /* Whole prefill: ga_prefill_keys, then ga_prefill_attention.
@@ -97,8 +105,9 @@ size_t ga_prefill_workspace_bytes(const ga_attn_desc* desc, int32_t seq_len);
  *                (normed, rotated, rounded to dtype) is written to slots
  *                [0,n) of k_cache and v to the same slots of v_cache (both
  *                required, cache_cap >= n); the attention then reads K-hat
- *                from the cache and the workspace may be NULL. Without a
- *                cache, K-hat goes to ``workspace``.
+ *                from the cache and the workspace holds only what
+ *                ga_prefill_attention_workspace_bytes names (NULL if 0).
+ *                Without a cache, K-hat goes to the start of ``workspace``.
  *  out           [B,n,H*d]. */
 ga_status ga_prefill(const ga_attn_desc* desc, int32_t seq_len,
                      const void* q, const void* k, const void* v, const void* gate,
@@ -115,20 +124,30 @@ ga_status ga_prefill_keys(const ga_attn_desc* desc, int32_t seq_len,
                           const int32_t* positions, void* k_hat, void* v_out, int32_t kv_cap,
                           void* stream);
 
-/* Second stage of ga_prefill (one kernel): causal attention of the normed,
- * rotated q against prepared keys, with the gate fused into the epilogue.
- * Kernel choice (bf16): a wide kernel (256 query rows per workgroup; d = 128,
- * rot % 32 == 0, at least 512 token blocks), a mirrored-block kernel (d in
- * {128, 256}, rot <= d/4) or a simple one (d in {64, 128, 256}); otherwise the
- * generic kernel. The environment variable GA_PREFILL_KERNEL = wide | mirror |
- * simple | generic, read at each call, forces a kernel that serves the shape
- * (for testing and tuning); results agree within the parity tolerance.
+/* Second stage of ga_prefill: causal attention of the normed, rotated q
+ * against prepared keys, with the gate fused into the epilogue. Kernel
+ * choice (bf16): a wide kernel (256 query rows per workgroup; d = 128,
+ * rot % 32 == 0, at least 512 token blocks), else the mirrored-block kernel
+ * (d in {128, 256}, rot <= d/4, B*n*H < 2^31), else a simple kernel (d in
+ * {64, 128, 256}), else the generic kernel. The environment variable
+ * GA_PREFILL_KERNEL = wide | split | mirror | simple | generic, read at each
+ * call, forces a kernel that serves the shape, for testing and tuning;
+ * results agree within the parity tolerance. "split" is the mirrored kernel
+ * in its split-key mode: the key range of each heavy pair of blocks is shared
+ * by two workgroups whose partial results meet in the workspace (a small
+ * zeroing kernel runs first); GA_PREFILL_SPLIT_BIAS (stages, default 8) tunes
+ * its balance. Only that mode needs a workspace.
  *  k_hat  [B,k_cap,G,d] as written by ga_prefill_keys (k_cap >= seq_len).
- *  v      [B,v_cap,G,d] (v_cap >= seq_len; the raw v input has v_cap = n). */
+ *  v      [B,v_cap,G,d] (v_cap >= seq_len; the raw v input has v_cap = n).
+ *  workspace  ga_prefill_attention_workspace_bytes(desc, seq_len) bytes,
+ *             16-byte aligned, owned by the caller (NULL allowed when that
+ *             is 0); too small: GA_ERR_WORKSPACE. Two calls that share a
+ *             workspace must not run at the same time. */
 ga_status ga_prefill_attention(const ga_attn_desc* desc, int32_t seq_len,
                                const void* q, const void* k_hat, int32_t k_cap,
                                const void* v, int32_t v_cap, const void* gate,
                                const float* q_norm_w, const int32_t* positions,
+                               void* workspace, size_t workspace_bytes,
                                void* out, void* stream);
 
 /* ---- decode ------------------------------------------------------------- */

@@ -49,6 +49,8 @@ def _desc(**kw):
 def test_host_queries():
     lib = _lib_or_build()
     d = _desc()
+    # the default kernel needs no attention workspace: K-hat only
+    assert lib.ga_prefill_attention_workspace_bytes(ctypes.byref(d), 4096) == 0
     assert lib.ga_prefill_workspace_bytes(ctypes.byref(d), 4096) == 4096 * 2 * 256 * 2
     ck = lib.ga_decode_split_keys()
     assert ck > 0
@@ -109,6 +111,38 @@ def test_prefill_rejects_bad_pointers_and_workspace():
     # empty inputs are a no-op
     assert _prefill(lib, d, n=0, q=None) == _lib.GA_OK
     assert _prefill(lib, _desc(batch=0), q=None) == _lib.GA_OK
+
+
+def test_prefill_attention_workspace(monkeypatch):
+    """The split-key mode needs its workspace; the other kernels none."""
+    lib = _lib_or_build()
+    d = _desc()
+    monkeypatch.setenv("GA_PREFILL_KERNEL", "split")
+    # split-key mode of the 4096-token, 8/2-head, d = 256 shape: 16-token blocks,
+    # 128 units of two blocks, 64 unit pairs per KV head -> 128 partial slots
+    slots = 2 * 64
+    split = slots * 128 * 256 * 4 + slots * 128 * 4 + slots * 2 * 4
+    assert lib.ga_prefill_attention_workspace_bytes(ctypes.byref(d), 4096) == split
+    assert lib.ga_prefill_workspace_bytes(ctypes.byref(d), 4096) == 4096 * 2 * 256 * 2 + split
+
+    def call(ws, ws_bytes, n=300):
+        return lib.ga_prefill_attention(ctypes.byref(d), n, A16, A16, n, A16, n, A16, None, None, ws, ws_bytes,
+                                        A16, None)
+
+    need = lib.ga_prefill_attention_workspace_bytes(ctypes.byref(d), 300)
+    assert need > 0
+    assert call(None, 0) == _lib.GA_ERR_WORKSPACE
+    assert call(A16, need - 1) == _lib.GA_ERR_WORKSPACE
+    assert call(MIS, need) == _lib.GA_ERR_MISALIGNED
+    monkeypatch.setenv("GA_PREFILL_KERNEL", "mirror")
+    assert lib.ga_prefill_attention_workspace_bytes(ctypes.byref(d), 300) == 0
+    monkeypatch.setenv("GA_PREFILL_KERNEL", "generic")
+    assert lib.ga_prefill_attention_workspace_bytes(ctypes.byref(d), 300) == 0
+    # f32 never takes the split path
+    monkeypatch.setenv("GA_PREFILL_KERNEL", "split")
+    assert lib.ga_prefill_attention_workspace_bytes(ctypes.byref(_desc(dtype=_lib.GA_F32)), 300) == 0
+    monkeypatch.delenv("GA_PREFILL_KERNEL")
+    assert lib.ga_prefill_attention_workspace_bytes(ctypes.byref(d), 300) == 0
 
 
 def test_decode_rejects_bad_arguments():

@@ -63,6 +63,16 @@ KERNEL_CASES = [
     ("wide", _case("d128_g128_n3", 1, 3, 128, 1, 128, 32, "elementwise", seed=113)),
     ("wide", _case("d128_g4_n700", 1, 700, 8, 2, 128, 32, "elementwise", seed=115)),
     ("wide", _case("d128_g2_n1_nogate", 2, 1, 4, 2, 128, 0, "none", seed=116)),
+    # split-key mode: heads/tails of heavy units merged through the workspace;
+    # n=300: 10 units (5 pairs); b2_n1000: 32 units; n129: 5 units, the middle
+    # one without a light partner; n37: one unit of one stage (no split)
+    ("split", _case("d256_g4_n300", 1, 300, 8, 2, 256, 64, "elementwise", seed=101)),
+    ("split", _case("d256_g4_b2_n1000", 2, 1000, 8, 2, 256, 64, "headwise", seed=122)),
+    ("split", _case("d256_g4_n129_nogate", 1, 129, 8, 2, 256, 64, "none", seed=123)),
+    ("split", _case("d256_g2_n37", 1, 37, 4, 2, 256, 64, "elementwise", seed=124)),
+    ("split", _case("d128_g8_n200", 1, 200, 32, 4, 128, 32, "elementwise", seed=103)),
+    ("split", _case("d128_g4_n700", 1, 700, 8, 2, 128, 32, "elementwise", seed=115)),
+    ("mirror", _case("d256_g4_n300", 1, 300, 8, 2, 256, 64, "elementwise", seed=101)),
     ("mirror", _case("d128_g8_n200", 1, 200, 32, 4, 128, 32, "elementwise", seed=103)),
     ("mirror", _case("d128_g4_n700", 1, 700, 8, 2, 128, 32, "elementwise", seed=115)),
     ("simple", _case("d128_g2_b2_n130", 2, 130, 16, 8, 128, 32, "headwise", seed=102)),
@@ -77,6 +87,30 @@ def test_prefill_forced_kernel(kernel, w, monkeypatch):
     x = inputs.make_prefill(w)
     got = host(gpu_prefill(w, x))
     assert_close(got, oracle_prefill(w, x), w, f"{kernel}:{w.name}")
+
+
+@pytest.mark.parametrize("bias", [0, 40])
+def test_prefill_split_balance_extremes(bias, monkeypatch):
+    """The split point c moves with GA_PREFILL_SPLIT_BIAS; at 40 the tails keep
+    one stage, so many tail rows see no key at all (zero weight in the merge)."""
+    w = _case(f"split_bias{bias}", 1, 1000, 8, 2, 256, 64, "elementwise", seed=125)
+    print(f"[prefill:split bias {bias}] {w.name}", flush=True)
+    monkeypatch.setenv("GA_PREFILL_KERNEL", "split")
+    monkeypatch.setenv("GA_PREFILL_SPLIT_BIAS", str(bias))
+    x = inputs.make_prefill(w)
+    got = host(gpu_prefill(w, x))
+    assert_close(got, oracle_prefill(w, x), w, f"split:{w.name}")
+
+
+def test_prefill_split_repeat_calls(monkeypatch):
+    """The arrival words are cleared per call: repeated calls on one workspace
+    give the same bits."""
+    w = _case("split_repeat", 1, 600, 8, 2, 256, 64, "elementwise", seed=126)
+    monkeypatch.setenv("GA_PREFILL_KERNEL", "split")
+    x = inputs.make_prefill(w)
+    first = host(gpu_prefill(w, x))
+    for _ in range(3):
+        assert np.array_equal(host(gpu_prefill(w, x)), first)
 
 
 def test_prefill_peaky_rows():
