@@ -50,7 +50,8 @@ def parse():
 ROOT = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(ROOT, "gated_gqa_softmax_amd", "csrc")
 KERNEL_SOURCES = {
-    "prefill_v2_kernel": ["ga_prefill_v2.hip", "ga_common.hpp", "ga_internal.hpp"],
+    "prefill_v2_kernel": ["ga_prefill_v2.hip", "ga_prefill_tile.hpp", "ga_common.hpp", "ga_internal.hpp"],
+    "prefill_wide_kernel": ["ga_prefill_wide.hip", "ga_prefill_tile.hpp", "ga_common.hpp", "ga_internal.hpp"],
     "decode_partials_kernel": ["ga_decode.hip", "ga_common.hpp", "ga_internal.hpp"],
 }
 
