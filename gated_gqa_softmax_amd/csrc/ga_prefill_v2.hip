@@ -53,19 +53,38 @@ __device__ __forceinline__ uint16_t* v2_qrow(unsigned char* smem, int r) {
 
 // One pipeline step: wait for stage st (buffer BUF), refill the buffer freed
 // by the previous step, and run this wave's tile if it has visible keys.
-// Stages run up to st_end (exclusive).
+// Stages run up to st_end (exclusive). From stage light_end on, row groups
+// 0-1 have no keys left (their block is done): with two stage buffers their
+// waves then issue the whole stage, their own share and that of wave w ^ 2
+// (the row group 2-3 wave), so the waves that compute never stall on a full
+// load queue. (Each wave waits for its own loads; the barrier for all.)
 template <int D, int BUF>
 __device__ __forceinline__ void v2_step(unsigned char* smem, WaveState<D>& ws, i32x4_t krs, i32x4_t vrs, int koff, int voff, int w, int st, int st_end,
                                         int kv_row_bytes, int phase, int wave_min_tok, int wave_max_tok,
-                                        int my_lim_tok, int n, float sl2, int hi) {
+                                        int my_lim_tok, int n, float sl2, int hi, int light_end, bool light_wave) {
   typedef MirrorShape<D> S;
   if (S::NSTAGE == 3 && st + 1 < st_end)
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * S::LOADS_PER_WAVE) : "memory");
   else
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   lds_barrier();
-  if (st + S::NSTAGE - 1 < st_end)
-    stage_issue<D, kMirrorStages<D>, (BUF + S::NSTAGE - 1) % S::NSTAGE>(smem, krs, vrs, koff, voff, w, st + S::NSTAGE - 1, kv_row_bytes);
+  constexpr int NB = (BUF + S::NSTAGE - 1) % S::NSTAGE;
+  if (st + S::NSTAGE - 1 < st_end) {
+    if (S::NSTAGE == 2 && st >= light_end) {
+      if (light_wave) {
+        stage_issue<D, kMirrorStages<D>, NB>(smem, krs, vrs, koff, voff, w, st + 1, kv_row_bytes);
+        const int lane = threadIdx.x & 63;
+        const int vw = w ^ 2;
+        const int row0 = vw * S::ROWS_PER_LOAD + lane / S::CPR;
+        const int ph = lane % S::CPR;
+        stage_issue<D, kMirrorStages<D>, NB>(smem, krs, vrs, row0 * kv_row_bytes + ((ph ^ swz_k(row0)) << 4),
+                                              row0 * kv_row_bytes + ((ph ^ swz_v(row0)) << 4), vw, st + 1,
+                                              kv_row_bytes);
+      }
+    } else {
+      stage_issue<D, kMirrorStages<D>, NB>(smem, krs, vrs, koff, voff, w, st + S::NSTAGE - 1, kv_row_bytes);
+    }
+  }
   const int k0 = st * S::ST + phase * 32;
   if (k0 <= wave_max_tok) {
     const bool need_mask = (k0 + 31 > wave_min_tok) || (k0 + 32 > n);  // wave-uniform
@@ -76,11 +95,11 @@ __device__ __forceinline__ void v2_step(unsigned char* smem, WaveState<D>& ws, i
 // RoPE of the first 2*HALF elements of a row held in x[0, N): pairs
 // (t, t + HALF) rotated by (cos, sin) = cs[t].
 template <int N, int HALF>
-__device__ __forceinline__ void rope_quarter(float* x, const float2* cs) {
+__device__ __forceinline__ void rope_quarter(float* x, const float2* cs, int sw) {
   static_assert(2 * HALF <= N, "rotated dims must lie in the lane's quarter");
 #pragma unroll
   for (int t = 0; t < HALF; ++t) {
-    const float2 e = cs[t];
+    const float2 e = cs[t ^ sw];
     const float a = x[t], c = x[t + HALF];
     x[t] = a * e.x - c * e.y;
     x[t + HALF] = c * e.x + a * e.y;
@@ -202,107 +221,152 @@ __global__ __launch_bounds__(512) void prefill_v2_kernel(const PrefillParams p) 
 
 
   // ---- Q prologue: RMSNorm + RoPE of 128 rows into LDS ------------------------
-  // Four adjacent lanes per row; lane quarter qq holds elements
-  // [qq*D/4, qq*D/4 + D/4). The RoPE pairs (t, t + rot/2) with rot <= D/4 all
-  // sit in quarter 0, and the row's sum of squares takes two quad shuffles.
-  // The q reads go out before the K/V stage loads, so waiting for them leaves
-  // the stage loads in flight (loads complete in issue order).
+  // Four adjacent lanes per row, each holding QE = D/4 elements in 16-byte
+  // chunks, so the row's sum of squares takes two quad shuffles. Which chunks
+  // a lane holds depends on the rotation width:
+  //  * half = D/8 (d = 256, rot = 64; "spread"): lane qq holds the RoPE pairs
+  //    t in [8qq, 8qq + 8) (chunks qq and 4 + qq) and six chunks of the
+  //    unrotated part, and rotates them in registers with (cos, sin) computed
+  //    in-lane: no table, every lane busy.
+  //  * otherwise: lane qq holds the contiguous quarter qq; all pairs
+  //    (t, t + half) with rot <= D/4 sit in quarter 0, rotated with (cos, sin)
+  //    from a table shared by the group's heads.
+  // Every load is consumed before the K/V stage loads go out, so no wait of
+  // the compiler (which does not count those loads) can end up waiting for
+  // them. Rows are staged in LDS with chunk c of row r at c ^ (r & 15).
   constexpr int QE = D / 4;
+  constexpr int QC = QE / 8;  // chunks per lane
   const int half = p.half;
+  const bool spread = (D == 256) && (half == D / 8);
   const int qrow = tid >> 2;  // 0..127
   const int qq = tid & 3;
   const int qside = qrow >> 6;
   const int qtt = (qrow & 63) % TB;
-  u32x4_t qraw[QE / 8];
-  {
-    const int qblk = qside ? blk_heavy : blk_light;
-    const int qhh = (qrow & 63) / TB;
-    const int qtok = qblk * TB + qtt;
-    const bool qvalid = (qblk >= 0) && (qhh < grp) && (qtok < n);
-    // unconditional (a branch around the loads would make the wave wait for
-    // them at its join): rows outside the block read row 0 and are never stored
-    const uint16_t* src =
-        p.q + (((long)b * n + (qvalid ? qtok : 0)) * nH + g * grp + (qvalid ? qhh : 0)) * D + qq * QE;
-#pragma unroll
-    for (int i = 0; i < QE / 8; ++i) qraw[i] = *(const u32x4_t*)(src + 8 * i);
-  }
-  f32x4_t qw[QE / 4];
-  if (p.wq) {
-#pragma unroll
-    for (int i = 0; i < QE / 4; ++i) qw[i] = *(const f32x4_t*)(p.wq + qq * QE + 4 * i);
-  }
+  const int qblk = qside ? blk_heavy : blk_light;
+  const int qhh = (qrow & 63) / TB;
+  const int qtok0 = qblk * TB + qtt;
+  const bool qvalid = (qblk >= 0) && (qhh < grp) && (qtok0 < n);
+  const int qtok = qvalid ? qtok0 : 0;
+  // spread: chunks qq, 4 + qq (rotated), then 8 + 6qq .. 13 + 6qq (unrotated)
+  auto qchunk = [&](int i) { return spread ? (i == 0 ? qq : (i == 1 ? 4 + qq : 6 + 6 * qq + i)) : qq * QC + i; };
 
-  // table inputs: up to 4 (token, pair) entries per thread
-  constexpr int TPT = 4;  // 2 * TB * half <= 2048 = TPT * 512 (checked on the host)
+  // RoPE inputs first (their wait then covers nothing else)
+  constexpr int TPT = 4;  // table entries per thread: 2 * TB * half <= 2048 = TPT * 512 (checked on the host)
   int tpos[TPT];
   double tfreq[TPT];
-  // (loads unconditional, indices clamped; only entries e < 2 * TB * half are stored)
+  int qpos = 0;
+  double qfreq[8];
+  if (spread) {
+    qpos = p.positions ? p.positions[(long)b * n + qtok] : qtok;
 #pragma unroll
-  for (int k = 0; k < TPT; ++k) {
-    const int e = half > 0 ? min(tid + 512 * k, 2 * TB * half - 1) : 0;
-    const int side = half > 0 ? e / (TB * half) : 0;
-    const int rem = e - side * TB * half;
-    const int tt = half > 0 ? rem / half : 0;
-    const int t = rem - tt * half;
-    const int blk = side ? blk_heavy : blk_light;
-    const int tok = (blk >= 0 && blk * TB + tt < n) ? blk * TB + tt : 0;
-    tpos[k] = p.positions ? p.positions[(long)b * n + tok] : tok;
-    tfreq[k] = p.inv_freq[t];
-  }
-
-  // (cos, sin) per (token of the two blocks, pair index), shared by the group's heads
+    for (int j = 0; j < 8; ++j) qfreq[j] = p.inv_freq[8 * qq + j];
+  } else {
+    // (loads unconditional, indices clamped; only entries e < 2 * TB * half are stored)
 #pragma unroll
-  for (int k = 0; k < TPT; ++k) {
-    const int e = tid + 512 * k;
-    if (e < 2 * TB * half) {
-      float c, s;
-      rope_cos_sin(tpos[k], tfreq[k], &c, &s);
-      table[e] = make_float2(c, s);
+    for (int k = 0; k < TPT; ++k) {
+      const int e = half > 0 ? min(tid + 512 * k, 2 * TB * half - 1) : 0;
+      const int side = half > 0 ? e / (TB * half) : 0;
+      const int rem = e - side * TB * half;
+      const int tt = half > 0 ? rem / half : 0;
+      const int t = rem - tt * half;
+      const int blk = side ? blk_heavy : blk_light;
+      const int tok = (blk >= 0 && blk * TB + tt < n) ? blk * TB + tt : 0;
+      tpos[k] = p.positions ? p.positions[(long)b * n + tok] : tok;
+      tfreq[k] = p.inv_freq[t];
     }
   }
-  // The first stage loads go out only now: every load above has been consumed,
-  // so no later wait of the compiler (which does not count these loads) can
-  // end up waiting for them.
+  // q row chunks: unconditional (a branch around the loads would make the
+  // wave wait for them at its join); rows outside the block read row 0 and
+  // are never stored
+  u32x4_t qraw[QC];
+  {
+    const uint16_t* src = p.q + (((long)b * n + qtok) * nH + g * grp + (qvalid ? qhh : 0)) * D;
+#pragma unroll
+    for (int i = 0; i < QC; ++i) qraw[i] = *(const u32x4_t*)(src + 8 * qchunk(i));
+  }
+  f32x4_t qw[2 * QC];
+  if (p.wq) {
+#pragma unroll
+    for (int i = 0; i < QC; ++i) {
+      qw[2 * i] = *(const f32x4_t*)(p.wq + 8 * qchunk(i));
+      qw[2 * i + 1] = *(const f32x4_t*)(p.wq + 8 * qchunk(i) + 4);
+    }
+  }
+
+  // table: (cos, sin) per (token of the two blocks, pair index); pair t of
+  // token tt sits at t ^ (tt & 7) (half % 8 == 0) so the quarter-0 lanes of
+  // one wave, which read the same t for different tokens, hit different banks
+  if (!spread) {
+#pragma unroll
+    for (int k = 0; k < TPT; ++k) {
+      const int e = tid + 512 * k;
+      if (e < 2 * TB * half) {
+        const int row = e / half, t = e - row * half;
+        const int tt = row % TB;
+        float c, s;
+        rope_cos_sin(tpos[k], tfreq[k], &c, &s);
+        table[row * half + (t ^ (tt & 7))] = make_float2(c, s);
+      }
+    }
+  }
+
+  float x[QE];
+#pragma unroll
+  for (int i = 0; i < QC; ++i) unpack8(qraw[i], x + 8 * i);
+  if (p.wq) {
+    float ss = 0.f;
+#pragma unroll
+    for (int e = 0; e < QE; ++e) ss += x[e] * x[e];
+    ss = quad_sum(ss);
+    const float inv = rsqrtf(ss * (1.0f / D) + p.eps);
+#pragma unroll
+    for (int e = 0; e < QE; ++e) x[e] *= inv * qw[e / 4][e % 4];
+  }
+  if (spread) {
+    // x[j] is element 8qq + j and x[8 + j] its partner 8qq + j + half
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      float c, sn;
+      rope_cos_sin(qpos, qfreq[j], &c, &sn);
+      const float a = x[j], o = x[8 + j];
+      x[j] = a * c - o * sn;
+      x[8 + j] = o * c + a * sn;
+    }
+  }
+
   if (st_lo < nst) stage_issue<D, kMirrorStages<D>, 0>(smem, krs, vrs, koff, voff, w, st_lo, kv_row_bytes);
   if (S::NSTAGE == 3 && st_lo + 1 < nst)
     stage_issue<D, kMirrorStages<D>, 1>(smem, krs, vrs, koff, voff, w, st_lo + 1, kv_row_bytes);
-  lds_barrier();
-  {
-    float x[QE];
-#pragma unroll
-    for (int i = 0; i < QE / 8; ++i) unpack8(qraw[i], x + 8 * i);
-    if (p.wq) {
-      float ss = 0.f;
-#pragma unroll
-      for (int e = 0; e < QE; ++e) ss += x[e] * x[e];
-      ss = quad_sum(ss);
-      const float inv = rsqrtf(ss * (1.0f / D) + p.eps);
-#pragma unroll
-      for (int e = 0; e < QE; ++e) x[e] *= inv * qw[e / 4][e % 4];
-    }
+
+  if (!spread) {
+    lds_barrier();  // the table is complete
     if (qq == 0) {
       const float2* cs = table + (qside * TB + qtt) * half;
+      const int sw = qtt & 7;
       // half % 8 == 0 and 2 * half <= D/4 (checked on the host)
-      if (half == 8) rope_quarter<QE, 8>(x, cs);
-      if (half == 16) rope_quarter<QE, 16>(x, cs);
+      if (half == 8) rope_quarter<QE, 8>(x, cs, sw);
+      if (half == 16) rope_quarter<QE, 16>(x, cs, sw);
       if constexpr (QE >= 48) {
-        if (half == 24) rope_quarter<QE, 24>(x, cs);
+        if (half == 24) rope_quarter<QE, 24>(x, cs, sw);
       }
       if constexpr (QE >= 64) {
-        if (half == 32) rope_quarter<QE, 32>(x, cs);
+        if (half == 32) rope_quarter<QE, 32>(x, cs, sw);
       }
     }
-    uint16_t* dst = v2_qrow<D>(smem, qrow) + qq * QE;
+  }
+  {
+    uint16_t* dst = v2_qrow<D>(smem, qrow);
 #pragma unroll
-    for (int i = 0; i < QE / 8; ++i) *(u32x4_t*)(dst + 8 * i) = pack8(x + 8 * i);
+    for (int i = 0; i < QC; ++i) *(u32x4_t*)(dst + 8 * (qchunk(i) ^ (qrow & 15))) = pack8(x + 8 * i);
   }
   lds_barrier();
 
   WaveState<D> ws;
   {
     const uint16_t* qr = v2_qrow<D>(smem, rg * 32 + l32);
+    const int sw = (rg * 32 + l32) & 15;
 #pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) ws.qf[kk] = *(const bf16x8_t*)(qr + kk * 16 + hi * 8);
+    for (int kk = 0; kk < D / 16; ++kk) ws.qf[kk] = *(const bf16x8_t*)(qr + 8 * ((2 * kk + hi) ^ sw));
   }
 #pragma unroll
   for (int mb = 0; mb < D / 32; ++mb)
@@ -324,16 +388,18 @@ __global__ __launch_bounds__(512) void prefill_v2_kernel(const PrefillParams p) 
     ws.vbase = S::VBASE + pbase + (hi * 4 + (i16 >> 2)) * S::ROW_BYTES + ((4 * x + c) << 4) + (i16 & 1) * 8;
   }
 
+  // first stage without keys for row groups 0-1 (0 if they have no block)
+  const int light_end = (blk_light >= 0) ? (min(n, blk_light * TB + TB) + S::ST - 1) / S::ST : 0;
   // ---- main loop, unrolled over the stage buffers -----------------------------
   for (int st0 = st_lo; st0 < nst; st0 += S::NSTAGE) {
     v2_step<D, 0>(smem, ws, krs, vrs, koff, voff, w, st0, nst, kv_row_bytes, phase, wave_min_tok, wave_max_tok,
-                  my_lim_tok, n, sl2, hi);
+                  my_lim_tok, n, sl2, hi, light_end, rg < 2);
     if (st0 + 1 < nst)
       v2_step<D, 1>(smem, ws, krs, vrs, koff, voff, w, st0 + 1, nst, kv_row_bytes, phase, wave_min_tok,
-                    wave_max_tok, my_lim_tok, n, sl2, hi);
+                    wave_max_tok, my_lim_tok, n, sl2, hi, light_end, rg < 2);
     if (S::NSTAGE == 3 && st0 + 2 < nst)
       v2_step<D, (S::NSTAGE == 3 ? 2 : 0)>(smem, ws, krs, vrs, koff, voff, w, st0 + 2, nst, kv_row_bytes, phase,
-                                           wave_min_tok, wave_max_tok, my_lim_tok, n, sl2, hi);
+                                           wave_min_tok, wave_max_tok, my_lim_tok, n, sl2, hi, light_end, rg < 2);
   }
 
   // ---- epilogue: merge the two phases, normalise, gate, store ---------------

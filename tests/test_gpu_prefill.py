@@ -73,6 +73,9 @@ KERNEL_CASES = [
     ("split", _case("d128_g8_n200", 1, 200, 32, 4, 128, 32, "elementwise", seed=103)),
     ("split", _case("d128_g4_n700", 1, 700, 8, 2, 128, 32, "elementwise", seed=115)),
     ("mirror", _case("d256_g4_n300", 1, 300, 8, 2, 256, 64, "elementwise", seed=101)),
+    # d = 256 with rot < 64 takes the tabled RoPE path of the q prologue
+    ("mirror", _case("d256_g4_n200_rot32", 1, 200, 8, 2, 256, 32, "elementwise", seed=127)),
+    ("mirror", _case("d256_g2_b2_n150_rot48", 2, 150, 4, 2, 256, 48, "headwise", seed=128)),
     ("mirror", _case("d128_g8_n200", 1, 200, 32, 4, 128, 32, "elementwise", seed=103)),
     ("mirror", _case("d128_g4_n700", 1, 700, 8, 2, 128, 32, "elementwise", seed=115)),
     ("simple", _case("d128_g2_b2_n130", 2, 130, 16, 8, 128, 32, "headwise", seed=102)),
