@@ -29,7 +29,6 @@ namespace ga {
 template <int D, int GRP>
 __global__ __launch_bounds__(256) void decode_partials_kernel(const DecodeParams p) {
   constexpr int C = kDecodeChunk;   // keys per workgroup
-  constexpr int KW = C / 4;         // keys per wave
   constexpr int SQ = D + 8;
   constexpr int LPR = D / 8;        // lanes per row (8 dims each) in the value mix
   constexpr int KPW = 64 / LPR;     // keys per value-mix step
@@ -72,9 +71,11 @@ __global__ __launch_bounds__(256) void decode_partials_kernel(const DecodeParams
   const long row = (long)p.G * D;
   const uint16_t* Kc = p.k_cache + (long)b * p.cache_bstride + (long)g * D;
   const uint16_t* Vc = p.v_cache + (long)b * p.cache_bstride + (long)g * D;
-  const int kbeg = start + w * KW;
-  const int kend = min(kbeg + KW, min(start + C, L));
-  const int ngroups = kend > kbeg ? (kend - kbeg + 15) / 16 : 0;
+  // The waves take interleaved 16-key groups (wave w: groups w, w + 4, ...),
+  // so at any time the workgroup streams one contiguous 64-row window.
+  const int kbeg = start + w * 16;
+  const int kend = min(start + C, L);
+  const int ngroups = kend > kbeg ? (kend - kbeg + 63) / 64 : 0;
   const float sl2 = p.scale_log2;
   const int dc = lane % LPR, ks = lane / LPR;
 
@@ -103,7 +104,7 @@ __global__ __launch_bounds__(256) void decode_partials_kernel(const DecodeParams
     }
   }
   for (int gi = 0; gi < ngroups; ++gi) {
-    const int k0 = kbeg + gi * 16;
+    const int k0 = kbeg + gi * 64;
     // scores of this group: S^T[key][head], v_mfma_f32_16x16x32_bf16 over d
     f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -111,7 +112,7 @@ __global__ __launch_bounds__(256) void decode_partials_kernel(const DecodeParams
       sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kr[c]), qf[c], sc, 0, 0, 0);
     // K rows of the next group
     {
-      const int key = min(k0 + 16 + l16, klast);
+      const int key = min(k0 + 64 + l16, klast);
 #pragma unroll
       for (int c = 0; c < D / 32; ++c) kr[c] = *(const u32x4_t*)(Kc + key * row + c * 32 + q4 * 8);
     }
@@ -153,7 +154,7 @@ __global__ __launch_bounds__(256) void decode_partials_kernel(const DecodeParams
     u32x4_t vn[VSTEPS];
 #pragma unroll
     for (int t = 0; t < VSTEPS; ++t) {
-      const int vkey = min(k0 + 16 + ks + KPW * t, klast);
+      const int vkey = min(k0 + 64 + ks + KPW * t, klast);
       vn[t] = *(const u32x4_t*)(Vc + vkey * row + dc * 8);
     }
 #pragma unroll
