@@ -49,10 +49,15 @@ def parse():
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(ROOT, "gated_gqa_softmax_amd", "csrc")
+# symbol of the kernel behind each name ga_prefill_attention_kernel returns
+PREFILL_KERNEL_SYMBOL = {"wide": "prefill_wide_kernel", "mirror": "prefill_v2_kernel", "split": "prefill_v2_kernel",
+                         "simple": "prefill_mfma_kernel", "generic": "naive_kernel"}
 KERNEL_SOURCES = {
     "prefill_v2_kernel": ["ga_prefill_v2.hip", "ga_prefill_tile.hpp", "ga_common.hpp", "ga_internal.hpp"],
     "prefill_wide_kernel": ["ga_prefill_wide.hip", "ga_prefill_tile.hpp", "ga_common.hpp", "ga_internal.hpp"],
     "decode_partials_kernel": ["ga_decode.hip", "ga_common.hpp", "ga_internal.hpp"],
+    "prefill_mfma_kernel": ["ga_prefill_mfma.hip", "ga_common.hpp", "ga_internal.hpp"],
+    "naive_kernel": ["ga_naive.hip", "ga_common.hpp", "ga_internal.hpp"],
 }
 
 
@@ -167,7 +172,19 @@ def time_prefill(torch, api, inputs, accounting, wname, steps, warmup):
         step(*ev[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    attn_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    attn_ms_events = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    # The attention kernel's launch duration: the same launches back to back
+    # between two events on its stream (per-launch event pairs add several
+    # microseconds of event overhead to a ~0.1 ms kernel).
+    k0, k1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    k0.record(stream)
+    for _ in range(steps):
+        api.ga_prefill_attention(d, q, khat, v, gate, wq, pos, out=out, workspace=ws_attn, stream=stream)
+    k1.record(stream)
+    torch.cuda.synchronize()
+    attn_ms = k0.elapsed_time(k1) / steps
+    kernel = PREFILL_KERNEL_SYMBOL[api.ga_prefill_attention_kernel(d, w.seq_len)]
     # whole ga_prefill calls, for the step figure
     ws = torch.empty(api.ga_prefill_workspace_bytes(d, w.seq_len), dtype=torch.uint8, device="cuda")
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -179,7 +196,8 @@ def time_prefill(torch, api, inputs, accounting, wname, steps, warmup):
     torch.cuda.synchronize()
     step_ms = e0.elapsed_time(e1) / steps
     flops = accounting.causal_prefill_flops(w.batch, w.n_q_heads, w.head_dim, w.seq_len)
-    return dict(w=w, x=x, flops=flops, attn_ms=attn_ms, step_ms=step_ms, wall_s=wall)
+    return dict(w=w, x=x, flops=flops, attn_ms=attn_ms, attn_ms_events=attn_ms_events, kernel=kernel,
+                step_ms=step_ms, wall_s=wall)
 
 
 def time_decode(torch, api, inputs, accounting, steps, warmup):
@@ -227,7 +245,16 @@ def time_decode(torch, api, inputs, accounting, steps, warmup):
     e1.record(stream)
     torch.cuda.synchronize()
     step_ms = e0.elapsed_time(e1) / steps
-    part_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    part_ms_events = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    # the partials kernel alone, back to back between two events
+    k0, k1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    k0.record(stream)
+    for _ in range(steps):
+        api.ga_decode_partials(d, q, kc, vc, dl, max_len, ws, q_norm_w=wq, stream=stream)
+    k1.record(stream)
+    torch.cuda.synchronize()
+    part_ms = k0.elapsed_time(k1) / steps
     total_bytes = accounting.decode_bytes(lens, w.n_q_heads, w.n_kv_heads, w.head_dim, 2, w.gate_mode)
     cache_bytes = int(lens.astype(np.int64).sum()) * 2 * w.n_kv_heads * w.head_dim * 2
     part_bytes = cache_bytes + w.batch * w.n_q_heads * w.head_dim * 2          # cache + q
@@ -245,7 +272,8 @@ def time_decode(torch, api, inputs, accounting, steps, warmup):
                      "peak": MI355X_HBM_GBS, "unit": "GB/s",
                      "frac": part_bytes / (part_ms * 1e-3) / 1e9 / MI355X_HBM_GBS,
                      "traffic": measured_traffic("decode_partials_kernel", w.name),
-                     "kernel_ms": part_ms, "algorithmic_bytes": part_bytes},
+                     "kernel_ms": part_ms, "kernel_ms_event_pairs": part_ms_events,
+                     "algorithmic_bytes": part_bytes},
     }
 
 
@@ -323,9 +351,10 @@ def main():
         "config": {"workload": w.name, "batch": w.batch, "seq_len": w.seq_len, "n_q_heads": w.n_q_heads,
                    "n_kv_heads": w.n_kv_heads, "head_dim": w.head_dim, "rot_dim": w.rot_dim, "gate": w.gate_mode,
                    "parallelism": "single-gpu"},
-        "roofline": {"bound": "mfma", "kernel": "prefill_v2_kernel", "achieved": achieved,
+        "roofline": {"bound": "mfma", "kernel": pre["kernel"], "achieved": achieved,
                      "peak": MI355X_BF16_DENSE_TFLOPS, "unit": "TFLOP/s", "frac": achieved / MI355X_BF16_DENSE_TFLOPS,
-                     "traffic": measured_traffic("prefill_v2_kernel", w.name), "kernel_ms": pre["attn_ms"],
+                     "traffic": measured_traffic(pre["kernel"], w.name), "kernel_ms": pre["attn_ms"],
+                     "kernel_ms_event_pairs": pre["attn_ms_events"],
                      "algorithmic_flops": pre["flops"]},
     }
     if not args.no_decode:

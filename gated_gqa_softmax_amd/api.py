@@ -96,6 +96,10 @@ def ga_prefill_attention_workspace_bytes(desc: AttnDesc, seq_len: int) -> int:
     return _lib.load().ga_prefill_attention_workspace_bytes(ctypes.byref(desc), seq_len)
 
 
+def ga_prefill_attention_kernel(desc: AttnDesc, seq_len: int) -> str:
+    return _lib.load().ga_prefill_attention_kernel(ctypes.byref(desc), seq_len).decode()
+
+
 def ga_decode_workspace_bytes(desc: AttnDesc, max_cache_len: int) -> int:
     return _lib.load().ga_decode_workspace_bytes(ctypes.byref(desc), max_cache_len)
 

@@ -351,6 +351,17 @@ void fill_decode_params(DecodeParams& dp, const ga_attn_desc* desc, const void* 
 
 extern "C" {
 
+const char* ga_prefill_attention_kernel(const ga_attn_desc* desc, int32_t seq_len) {
+  if (check_desc(desc) != GA_OK || seq_len < 0) return "invalid";
+  switch (prefill_choice(desc, seq_len, seq_len, seq_len)) {
+    case PK_WIDE: return "wide";
+    case PK_SPLIT: return "split";
+    case PK_MIRROR: return "mirror";
+    case PK_SIMPLE: return "simple";
+    default: return "generic";
+  }
+}
+
 size_t ga_prefill_attention_workspace_bytes(const ga_attn_desc* desc, int32_t seq_len) {
   if (check_desc(desc) != GA_OK || seq_len < 0) return 0;
   return prefill_attn_ws_bytes(desc, seq_len, seq_len, seq_len);

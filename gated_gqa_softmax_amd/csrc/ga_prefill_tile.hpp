@@ -47,16 +47,46 @@ __device__ __forceinline__ int swz_v(int row) { return (row & 3) << 2; }
 
 constexpr float kLazyRescale = 8.0f;  // log2 headroom before the output is rescaled
 
+// Q^T operand fragments of a wave's 32 rows (D/16 fragments of 16 bytes).
+// For d = 256 they are held as accumulator-shaped blocks (fragment kk is the
+// 16-byte piece kk % 4 of raw[kk / 4]): the register allocator then places
+// them without the spills it made for sixteen separate pieces at that
+// register budget.
+template <int D, bool BLOCKS = (D == 256)>
+struct QFrags {
+  bf16x8_t f[D / 16];
+  __device__ __forceinline__ bf16x8_t get(int kk) const { return f[kk]; }
+  __device__ __forceinline__ void set(int kk, bf16x8_t x) { f[kk] = x; }
+};
+template <int D>
+struct QFrags<D, true> {
+  f32x16_t raw[D / 64];
+  __device__ __forceinline__ bf16x8_t get(int kk) const {
+    const f32x16_t& b = raw[kk >> 2];
+    const int j = (kk & 3) * 4;
+    const f32x4_t v = {b[j], b[j + 1], b[j + 2], b[j + 3]};
+    return __builtin_bit_cast(bf16x8_t, v);
+  }
+  __device__ __forceinline__ void set(int kk, bf16x8_t x) {
+    const f32x4_t v = __builtin_bit_cast(f32x4_t, x);
+    const int j = (kk & 3) * 4;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) raw[kk >> 2][j + e] = v[e];
+  }
+};
+
 // Per-wave state of the main loop.
 template <int D>
 struct WaveState {
-  bf16x8_t qf[D / 16];   // Q^T operand fragments of this wave's 32 rows
+  QFrags<D> q;           // Q^T operand fragments of this wave's 32 rows
   f32x16_t o[D / 32];    // O^T accumulators
   float m_run, l_run;    // reference max (log2 domain) and lane-partial row sum
   int kbase;             // K operand LDS address of step 0 (lane part, phase included);
                          // step kk reads kbase ^ ((kk & 7) << 5), + 256 for kk >= 8
   int vbase;             // V^T operand LDS address of dim block 0 (lane part, phase and
                          // V base included); dim block mb reads vbase ^ ((mb & 3) << 6), + 256 for mb >= 4
+  __device__ __forceinline__ bf16x8_t qf(int kk) const { return q.get(kk); }
+  __device__ __forceinline__ void set_qf(int kk, bf16x8_t x) { q.set(kk, x); }
 };
 
 // Direct-to-LDS loads of one stage (64 keys of K-hat and V) for this wave:
@@ -126,7 +156,7 @@ __device__ __forceinline__ void attn_tile(const unsigned char* smem, WaveState<D
 #pragma unroll
   for (int kk = 0; kk < NK; ++kk) {
     if (kk + KPF < NK) ka[kk + KPF] = kread(kk + KPF);
-    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[kk], ws.qf[kk], s, 0, 0, 0);
+    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[kk], ws.qf(kk), s, 0, 0, 0);
   }
   // keep that order: KPF reads ahead, then one MFMA per read
   __builtin_amdgcn_sched_group_barrier(0x100, KPF, 0);

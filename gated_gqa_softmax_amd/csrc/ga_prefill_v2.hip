@@ -366,7 +366,7 @@ __global__ __launch_bounds__(512) void prefill_v2_kernel(const PrefillParams p) 
     const uint16_t* qr = v2_qrow<D>(smem, rg * 32 + l32);
     const int sw = (rg * 32 + l32) & 15;
 #pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) ws.qf[kk] = *(const bf16x8_t*)(qr + 8 * ((2 * kk + hi) ^ sw));
+    for (int kk = 0; kk < D / 16; ++kk) ws.set_qf(kk, *(const bf16x8_t*)(qr + 8 * ((2 * kk + hi) ^ sw)));
   }
 #pragma unroll
   for (int mb = 0; mb < D / 32; ++mb)

@@ -182,7 +182,7 @@ __global__ __launch_bounds__(512) void prefill_wide_kernel(const PrefillParams p
       }
     }
 #pragma unroll
-    for (int kk = 0; kk < NK; ++kk) ws.qf[kk] = __builtin_bit_cast(bf16x8_t, pack8(x[kk]));
+    for (int kk = 0; kk < NK; ++kk) ws.set_qf(kk, __builtin_bit_cast(bf16x8_t, pack8(x[kk])));
   }
 #pragma unroll
   for (int mb = 0; mb < D / 32; ++mb)

@@ -91,6 +91,12 @@ typedef struct {
  * The value depends on GA_PREFILL_KERNEL as read at the time of the call. */
 size_t ga_prefill_attention_workspace_bytes(const ga_attn_desc* desc, int32_t seq_len);
 
+/* Name of the kernel ga_prefill_attention runs for this shape (caches of
+ * seq_len rows), under GA_PREFILL_KERNEL as read now: "wide", "mirror",
+ * "split", "simple" or "generic" ("invalid" for a bad descriptor). A static
+ * string; the caller does not free it. */
+const char* ga_prefill_attention_kernel(const ga_attn_desc* desc, int32_t seq_len);
+
 /* Workspace ga_prefill needs when it is given no KV cache: room for K-hat
  * (B*n*G*d elements, rounded up to 256 bytes) followed by the attention
  * workspace. With a KV cache it needs only the attention workspace. */

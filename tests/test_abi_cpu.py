@@ -49,6 +49,14 @@ def _desc(**kw):
 def test_host_queries():
     lib = _lib_or_build()
     d = _desc()
+    # kernel choice: d = 256 -> mirrored; d = 128 with >= 512 token blocks -> wide
+    assert lib.ga_prefill_attention_kernel(ctypes.byref(d), 4096) == b"mirror"
+    d3 = _desc(batch=4, n_q_heads=16, n_kv_heads=8, head_dim=128, rot_dim=32)
+    assert lib.ga_prefill_attention_kernel(ctypes.byref(d3), 2048) == b"wide"
+    assert lib.ga_prefill_attention_kernel(ctypes.byref(d3), 100) == b"mirror"
+    assert lib.ga_prefill_attention_kernel(ctypes.byref(_desc(dtype=_lib.GA_F32)), 64) == b"generic"
+    assert lib.ga_prefill_attention_kernel(ctypes.byref(_desc(head_dim=64, rot_dim=16)), 64) == b"simple"
+    assert lib.ga_prefill_attention_kernel(None, 64) == b"invalid"
     # the default kernel needs no attention workspace: K-hat only
     assert lib.ga_prefill_attention_workspace_bytes(ctypes.byref(d), 4096) == 0
     assert lib.ga_prefill_workspace_bytes(ctypes.byref(d), 4096) == 4096 * 2 * 256 * 2
