@@ -228,6 +228,7 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(const DecodeParams p)
   __shared__ float qk[2][D];  // row 0: q-hat (bf16-rounded); row 1: new k-hat (bf16-rounded)
   __shared__ float red[8];
   __shared__ float wts[SPASS];
+  __shared__ __attribute__((aligned(16))) float ored[4][D];  // per-wave weighted sums
   __shared__ float sh_snew, sh_M, sh_L;
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -288,30 +289,50 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(const DecodeParams p)
   if (lane == 0) red[4 + w] = sm;
   __syncthreads();
   if (tid == 0) sh_L = red[4] + red[5] + red[6] + red[7] + __builtin_amdgcn_exp2f(snew - M);
-  // weighted sum of the chunk outputs, SPASS chunks at a time
-  float o0 = 0.f, o1 = 0.f;
+  // weighted sum of the chunk outputs, SPASS chunks at a time: wave w takes
+  // chunks w*CPW + sub (+ 4*CPW per step), lane (sub, e4) the 16-byte piece e4
+  // of that chunk's row, four steps in flight; waves meet in LDS at the end
+  constexpr int LPC = D / 4;    // lanes per chunk row (4 floats each)
+  constexpr int CPW = 64 / LPC;  // chunks per wave instruction
+  const int sub = lane / LPC, e4 = lane % LPC;
+  f32x4_t acc[4] = {};
   for (int s0 = 0; s0 < ns; s0 += SPASS) {
     __syncthreads();
     if (s0 + tid < ns) wts[tid] = __builtin_amdgcn_exp2f(ws_ml[(s0 + tid) * 2] - M);
     __syncthreads();
     const int sn = min(SPASS, ns - s0);
-    if (tid < D) {
-      const float* src = ws_o + (long)s0 * D + tid;
-      int s = 0;
-      for (; s + 4 <= sn; s += 4) {
-        const float a0 = src[(long)(s + 0) * D], a1 = src[(long)(s + 1) * D];
-        const float a2 = src[(long)(s + 2) * D], a3 = src[(long)(s + 3) * D];
-        o0 += a0 * wts[s] + a2 * wts[s + 2];
-        o1 += a1 * wts[s + 1] + a3 * wts[s + 3];
+    const float* src = ws_o + (long)s0 * D + e4 * 4;
+    int s = w * CPW + sub;
+    for (; s + 12 * CPW < sn; s += 16 * CPW) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const f32x4_t a = *(const f32x4_t*)(src + (long)(s + 4 * CPW * j) * D);
+        const float wt = wts[s + 4 * CPW * j];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) acc[j][c] += a[c] * wt;
       }
-      for (; s < sn; ++s) o0 += src[(long)s * D] * wts[s];
+    }
+    for (; s < sn; s += 4 * CPW) {
+      const f32x4_t a = *(const f32x4_t*)(src + (long)s * D);
+      const float wt = wts[s];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) acc[0][c] += a[c] * wt;
     }
   }
+  f32x4_t o4;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) o4[c] = (acc[0][c] + acc[1][c]) + (acc[2][c] + acc[3][c]);
+#pragma unroll
+  for (int m = LPC; m < 64; m <<= 1)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) o4[c] += __shfl_xor(o4[c], m, 64);
+  if (sub == 0) *(f32x4_t*)&ored[w][e4 * 4] = o4;
   __syncthreads();
   if (tid < D) {
     const int e = tid;
+    const float o = (ored[0][e] + ored[1][e]) + (ored[2][e] + ored[3][e]);
     const float vnew = bf16_bits_to_f32(p.v_new[((long)b * p.G + g) * D + e]);
-    float y = (o0 + o1 + vnew * __builtin_amdgcn_exp2f(snew - M)) / sh_L;
+    float y = (o + vnew * __builtin_amdgcn_exp2f(snew - M)) / sh_L;
     if (GATE == 2) y *= sigmoid_f32(bf16_bits_to_f32(p.gate[((long)b * p.H + h) * D + e]));
     if (GATE == 1) y *= sigmoid_f32(bf16_bits_to_f32(p.gate[(long)b * p.H + h]));
     out[e] = f32_to_bf16_bits(y);
