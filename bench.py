@@ -236,16 +236,24 @@ def time_decode(torch, api, inputs, accounting, steps, warmup):
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
+    # per-launch event pairs around the partials kernel (a diagnostic: each
+    # pair adds event overhead, so neither figure below comes from this loop)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    torch.cuda.synchronize()
+    for i in range(steps):
+        step(*ev[i])
+    torch.cuda.synchronize()
+    part_ms_events = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    # the step: whole ga_decode calls back to back between two events
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     e0.record(stream)
-    for i in range(steps):
-        step(*ev[i])
+    for _ in range(steps):
+        api.ga_decode(d, q, kn, vn, kc, vc, dl, max_len, gate=gate, q_norm_w=wq, k_norm_w=wk, out=out, workspace=ws,
+                      stream=stream)
     e1.record(stream)
     torch.cuda.synchronize()
     step_ms = e0.elapsed_time(e1) / steps
-    part_ms_events = float(np.mean([a.elapsed_time(b) for a, b in ev]))
     # the partials kernel alone, back to back between two events
     k0, k1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
