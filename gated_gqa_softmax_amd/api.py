@@ -170,6 +170,67 @@ def ga_prefill_attention(desc: AttnDesc, q, k_hat, v, gate=None, q_norm_w=None, 
     return out
 
 
+def ga_prefill_chunk_kernel(desc: AttnDesc, seq_len: int, cache_cap: int) -> str:
+    return _lib.load().ga_prefill_chunk_kernel(ctypes.byref(desc), seq_len, cache_cap).decode()
+
+
+def ga_prefill_chunk(desc: AttnDesc, q, k, v, k_cache, v_cache, cache_lens, max_cache_len: int, gate=None,
+                     q_norm_w=None, k_norm_w=None, positions=None, chunk_lens=None, out=None,
+                     stream=None) -> torch.Tensor:
+    """Chunk of seq_len new rows per sequence after cache_lens[b] cached tokens.
+
+    Writes K-hat/V of the real rows to cache slots [L_b, L_b + n_b) and the
+    gated attention of those rows to out [B,seq_len,H*d]; padding rows
+    (i >= chunk_lens[b]) are left as they were.
+    """
+    lib = _lib.load()
+    et = _elem_dtype(desc)
+    B, n = q.shape[0], q.shape[1]
+    if out is None:
+        out = torch.zeros((B, n, desc.n_q_heads * desc.head_dim), dtype=et, device=q.device)
+    st = lib.ga_prefill_chunk(ctypes.byref(desc), n, _ptr(q, "q", et), _ptr(k, "k", et), _ptr(v, "v", et),
+                              _ptr(gate, "gate", et), _ptr(q_norm_w, "q_norm_w", torch.float32),
+                              _ptr(k_norm_w, "k_norm_w", torch.float32), _ptr(positions, "positions", torch.int32),
+                              _ptr(k_cache, "k_cache", et), _ptr(v_cache, "v_cache", et), k_cache.shape[1],
+                              _ptr(cache_lens, "cache_lens", torch.int32), _ptr(chunk_lens, "chunk_lens", torch.int32),
+                              int(max_cache_len), _ptr(out, "out", et), _stream(stream))
+    _check(st, "ga_prefill_chunk")
+    return out
+
+
+def ga_prefill_chunk_keys(desc: AttnDesc, k, v, k_cache, v_cache, cache_lens, max_cache_len: int, k_norm_w=None,
+                          positions=None, chunk_lens=None, stream=None):
+    lib = _lib.load()
+    et = _elem_dtype(desc)
+    st = lib.ga_prefill_chunk_keys(ctypes.byref(desc), k.shape[1], _ptr(k, "k", et), _ptr(v, "v", et),
+                                   _ptr(k_norm_w, "k_norm_w", torch.float32),
+                                   _ptr(positions, "positions", torch.int32),
+                                   _ptr(cache_lens, "cache_lens", torch.int32),
+                                   _ptr(chunk_lens, "chunk_lens", torch.int32), int(max_cache_len),
+                                   _ptr(k_cache, "k_cache", et), _ptr(v_cache, "v_cache", et), k_cache.shape[1],
+                                   _stream(stream))
+    _check(st, "ga_prefill_chunk_keys")
+
+
+def ga_prefill_chunk_attention(desc: AttnDesc, q, k_cache, v_cache, cache_lens, max_cache_len: int, gate=None,
+                               q_norm_w=None, positions=None, chunk_lens=None, out=None,
+                               stream=None) -> torch.Tensor:
+    lib = _lib.load()
+    et = _elem_dtype(desc)
+    B, n = q.shape[0], q.shape[1]
+    if out is None:
+        out = torch.zeros((B, n, desc.n_q_heads * desc.head_dim), dtype=et, device=q.device)
+    st = lib.ga_prefill_chunk_attention(ctypes.byref(desc), n, _ptr(q, "q", et), _ptr(k_cache, "k_cache", et),
+                                        _ptr(v_cache, "v_cache", et), k_cache.shape[1],
+                                        _ptr(cache_lens, "cache_lens", torch.int32),
+                                        _ptr(chunk_lens, "chunk_lens", torch.int32), int(max_cache_len),
+                                        _ptr(gate, "gate", et), _ptr(q_norm_w, "q_norm_w", torch.float32),
+                                        _ptr(positions, "positions", torch.int32), _ptr(out, "out", et),
+                                        _stream(stream))
+    _check(st, "ga_prefill_chunk_attention")
+    return out
+
+
 def ga_decode(desc: AttnDesc, q, k_new, v_new, k_cache, v_cache, cache_lens, max_cache_len: int, gate=None,
               q_norm_w=None, k_norm_w=None, out=None, workspace=None, stream=None) -> torch.Tensor:
     """out [B,H*d] for one new token per sequence; appends K-hat/V at slot cache_lens[b]."""

@@ -199,11 +199,16 @@ size_t decode_nsplit(int32_t max_len) {
   return ns < 1 ? 1 : ns;
 }
 
+// slot_base / row_lens / max_base: a chunk against a cache (NULL, NULL, 0 otherwise)
 ga_status prefill_keys_impl(const ga_attn_desc* desc, int32_t n, const void* k, const void* v,
                             const float* k_norm_w, const int32_t* positions, void* k_hat, void* v_out,
-                            int32_t kv_cap, hipStream_t stream) {
+                            int32_t kv_cap, hipStream_t stream, const int32_t* slot_base = nullptr,
+                            const int32_t* row_lens = nullptr, int32_t max_base = 0) {
   PrepParams pp;
   memset(&pp, 0, sizeof(pp));
+  pp.slot_base = slot_base;
+  pp.row_lens = row_lens;
+  pp.max_base = max_base;
   pp.src = k;
   pp.vsrc = v;
   pp.dst = k_hat;
@@ -301,6 +306,93 @@ ga_status prefill_attn_impl(const ga_attn_desc* desc, int32_t n, const void* q, 
   np.scale = scale_of(desc);
   fill_inv_freq(desc, np.inv_freq);
   return hip_status(launch_naive(np, desc->dtype == GA_BF16, stream), "prefill attention launch");
+}
+
+// Kernel of a chunk against a cache: the mirrored kernel (with per-sequence key
+// offsets) where it serves the shape, else the generic one.
+bool chunk_uses_mirror(const ga_attn_desc* d, int32_t n, int32_t cache_cap) {
+  return prefill_kernel_request() != PK_GENERIC && prefill_v2_ok(d, cache_cap, cache_cap) &&
+         (long long)d->batch * n * d->n_q_heads < (1LL << 31);
+}
+
+ga_status check_chunk_common(const ga_attn_desc* desc, int32_t n, const void* k_cache, const void* v_cache,
+                             int32_t cache_cap, const int32_t* cache_lens, int32_t max_cache_len) {
+  ga_status st;
+  if ((st = check_tensor(k_cache, "k_cache", desc)) != GA_OK) return st;
+  if ((st = check_tensor(v_cache, "v_cache", desc)) != GA_OK) return st;
+  if (!cache_lens) return fail(GA_ERR_NULL_ARG, "cache_lens is NULL");
+  if (max_cache_len < 0) return fail(GA_ERR_BAD_SHAPE, "max_cache_len %d < 0", max_cache_len);
+  if ((long long)cache_cap < (long long)max_cache_len + n)
+    return fail(GA_ERR_BAD_SHAPE, "cache_cap %d < max_cache_len + seq_len (%lld)", cache_cap,
+                (long long)max_cache_len + n);
+  if ((long long)max_cache_len + n >= (1LL << 30))
+    return fail(GA_ERR_UNSUPPORTED, "max_cache_len + seq_len must stay below 2^30");
+  return GA_OK;
+}
+
+ga_status chunk_attn_impl(const ga_attn_desc* desc, int32_t n, const void* q, const void* k_cache,
+                          const void* v_cache, int32_t cap, const int32_t* cache_lens, const int32_t* chunk_lens,
+                          int32_t max_cache_len, const void* gate, const float* q_norm_w, const int32_t* positions,
+                          void* out, hipStream_t stream) {
+  const int H = desc->n_q_heads, G = desc->n_kv_heads, d = desc->head_dim;
+  const int grp = H / G;
+  if (chunk_uses_mirror(desc, n, cap)) {
+    PrefillParams pp;
+    memset(&pp, 0, sizeof(pp));
+    pp.q = (const uint16_t*)q;
+    pp.khat = (const uint16_t*)k_cache;
+    pp.v = (const uint16_t*)v_cache;
+    pp.gate = (const uint16_t*)gate;
+    pp.wq = q_norm_w;
+    pp.positions = positions;
+    pp.out = (uint16_t*)out;
+    pp.key_base = cache_lens;
+    pp.row_lens = chunk_lens;
+    pp.max_base = max_cache_len;
+    pp.k_bstride = (long)cap * G * d;
+    pp.v_bstride = pp.k_bstride;
+    pp.B = desc->batch;
+    pp.n = n;
+    pp.H = H;
+    pp.G = G;
+    pp.grp = grp;
+    pp.TB = 64 / grp;
+    pp.nblk = (n + pp.TB - 1) / pp.TB;
+    pp.rot = desc->rot_dim;
+    pp.half = desc->rot_dim / 2;
+    pp.use_table = (2 * pp.TB * pp.half <= 1024) ? 1 : 0;
+    pp.eps = desc->rms_eps;
+    pp.scale_log2 = scale_of(desc) * 1.4426950408889634f;
+    fill_inv_freq(desc, pp.inv_freq);
+    if ((long long)pp.B * G * pp.nblk > 0x7fffffffLL) return fail(GA_ERR_UNSUPPORTED, "grid too large");
+    return hip_status(launch_prefill_v2(pp, d, desc->gate_mode, stream), "chunk attention launch");
+  }
+  NaiveParams np;
+  memset(&np, 0, sizeof(np));
+  np.q = q;
+  np.khat = k_cache;
+  np.v = v_cache;
+  np.gate = gate;
+  np.wq = q_norm_w;
+  np.positions = positions;
+  np.cache_lens = cache_lens;
+  np.row_lens = chunk_lens;
+  np.out = out;
+  np.k_bstride = (long)cap * G * d;
+  np.v_bstride = np.k_bstride;
+  np.B = desc->batch;
+  np.n = n;
+  np.H = H;
+  np.G = G;
+  np.d = d;
+  np.rot = desc->rot_dim;
+  np.gate_mode = desc->gate_mode;
+  np.decode = 0;
+  np.max_len = max_cache_len;
+  np.eps = desc->rms_eps;
+  np.scale = scale_of(desc);
+  fill_inv_freq(desc, np.inv_freq);
+  return hip_status(launch_naive(np, desc->dtype == GA_BF16, stream), "chunk attention launch");
 }
 
 ga_status check_decode_common(const ga_attn_desc* desc, const void* q, const void* k_cache, const void* v_cache,
@@ -453,6 +545,68 @@ ga_status ga_prefill(const ga_attn_desc* desc, int32_t seq_len, const void* q, c
   if ((st = prefill_keys_impl(desc, seq_len, k, v, k_norm_w, positions, khat, v_cache, kcap, s)) != GA_OK) return st;
   return prefill_attn_impl(desc, seq_len, q, khat, kcap, v, seq_len,
                            desc->gate_mode == GA_GATE_NONE ? nullptr : gate, q_norm_w, positions, attn_ws, out, s);
+}
+
+const char* ga_prefill_chunk_kernel(const ga_attn_desc* desc, int32_t seq_len, int32_t cache_cap) {
+  if (check_desc(desc) != GA_OK || seq_len < 0 || cache_cap < 0) return "invalid";
+  return chunk_uses_mirror(desc, seq_len, cache_cap) ? "mirror" : "generic";
+}
+
+ga_status ga_prefill_chunk_keys(const ga_attn_desc* desc, int32_t seq_len, const void* k, const void* v,
+                                const float* k_norm_w, const int32_t* positions, const int32_t* cache_lens,
+                                const int32_t* chunk_lens, int32_t max_cache_len, void* k_cache, void* v_cache,
+                                int32_t cache_cap, void* stream) {
+  ga_status st;
+  if ((st = check_desc(desc)) != GA_OK) return st;
+  if (seq_len < 0) return fail(GA_ERR_BAD_SHAPE, "seq_len %d < 0", seq_len);
+  if (desc->batch == 0 || seq_len == 0) return ok();
+  if ((st = check_tensor(k, "k", desc)) != GA_OK) return st;
+  if ((st = check_tensor(v, "v", desc)) != GA_OK) return st;
+  if ((st = check_chunk_common(desc, seq_len, k_cache, v_cache, cache_cap, cache_lens, max_cache_len)) != GA_OK)
+    return st;
+  return prefill_keys_impl(desc, seq_len, k, v, k_norm_w, positions, k_cache, v_cache, cache_cap,
+                           (hipStream_t)stream, cache_lens, chunk_lens, max_cache_len);
+}
+
+ga_status ga_prefill_chunk_attention(const ga_attn_desc* desc, int32_t seq_len, const void* q, const void* k_cache,
+                                     const void* v_cache, int32_t cache_cap, const int32_t* cache_lens,
+                                     const int32_t* chunk_lens, int32_t max_cache_len, const void* gate,
+                                     const float* q_norm_w, const int32_t* positions, void* out, void* stream) {
+  ga_status st;
+  if ((st = check_desc(desc)) != GA_OK) return st;
+  if (seq_len < 0) return fail(GA_ERR_BAD_SHAPE, "seq_len %d < 0", seq_len);
+  if (desc->batch == 0 || seq_len == 0) return ok();
+  if ((st = check_tensor(q, "q", desc)) != GA_OK) return st;
+  if ((st = check_tensor(out, "out", desc)) != GA_OK) return st;
+  if ((st = check_gate(gate, desc)) != GA_OK) return st;
+  if ((st = check_chunk_common(desc, seq_len, k_cache, v_cache, cache_cap, cache_lens, max_cache_len)) != GA_OK)
+    return st;
+  return chunk_attn_impl(desc, seq_len, q, k_cache, v_cache, cache_cap, cache_lens, chunk_lens, max_cache_len,
+                         desc->gate_mode == GA_GATE_NONE ? nullptr : gate, q_norm_w, positions, out,
+                         (hipStream_t)stream);
+}
+
+ga_status ga_prefill_chunk(const ga_attn_desc* desc, int32_t seq_len, const void* q, const void* k, const void* v,
+                           const void* gate, const float* q_norm_w, const float* k_norm_w, const int32_t* positions,
+                           void* k_cache, void* v_cache, int32_t cache_cap, const int32_t* cache_lens,
+                           const int32_t* chunk_lens, int32_t max_cache_len, void* out, void* stream) {
+  ga_status st;
+  if ((st = check_desc(desc)) != GA_OK) return st;
+  if (seq_len < 0) return fail(GA_ERR_BAD_SHAPE, "seq_len %d < 0", seq_len);
+  if (desc->batch == 0 || seq_len == 0) return ok();
+  if ((st = check_tensor(q, "q", desc)) != GA_OK) return st;
+  if ((st = check_tensor(k, "k", desc)) != GA_OK) return st;
+  if ((st = check_tensor(v, "v", desc)) != GA_OK) return st;
+  if ((st = check_tensor(out, "out", desc)) != GA_OK) return st;
+  if ((st = check_gate(gate, desc)) != GA_OK) return st;
+  if ((st = check_chunk_common(desc, seq_len, k_cache, v_cache, cache_cap, cache_lens, max_cache_len)) != GA_OK)
+    return st;
+  hipStream_t s = (hipStream_t)stream;
+  if ((st = prefill_keys_impl(desc, seq_len, k, v, k_norm_w, positions, k_cache, v_cache, cache_cap, s, cache_lens,
+                              chunk_lens, max_cache_len)) != GA_OK)
+    return st;
+  return chunk_attn_impl(desc, seq_len, q, k_cache, v_cache, cache_cap, cache_lens, chunk_lens, max_cache_len,
+                         desc->gate_mode == GA_GATE_NONE ? nullptr : gate, q_norm_w, positions, out, s);
 }
 
 int32_t ga_decode_split_keys(void) { return kDecodeChunk; }

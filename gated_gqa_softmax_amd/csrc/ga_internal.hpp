@@ -17,7 +17,12 @@ struct PrepParams {
   void* vdst;          // copy of v, or null
   long src_bstride, vsrc_bstride, dst_bstride, vdst_bstride;  // elements per batch
   const float* w;      // [d] or null
-  const int* positions;  // [B, n] or null (= token index)
+  const int* positions;  // [B, n] or null (= slot index)
+  // Chunk against a cache (both null otherwise): row i of sequence b goes to
+  // slot slot_base[b] + i, and only rows i < row_lens[b] are written.
+  const int* slot_base;  // [B] or null (= 0)
+  const int* row_lens;   // [B] or null (= n)
+  int max_base;          // slot_base values outside [0, max_base] skip the sequence
   int B, n, G, d, rot;
   float eps;
   double inv_freq[kMaxHalfRot];
@@ -32,6 +37,12 @@ struct PrefillParams {
   const float* wq;
   const int* positions;
   uint16_t* out;
+  // Chunk against a cache (mirrored kernel only; both null otherwise): the
+  // n query rows of sequence b are tokens key_base[b] + i of it, of which
+  // rows i < row_lens[b] are real; row i sees keys [0, key_base[b] + i].
+  const int* key_base;  // [B] or null (= 0)
+  const int* row_lens;  // [B] or null (= n)
+  int max_base;         // key_base values outside [0, max_base] skip the sequence
   long k_bstride, v_bstride;
   int B, n, H, G, grp, TB, nblk, rot, half, use_table;
   float eps, scale_log2;
@@ -58,7 +69,8 @@ struct NaiveParams {
   const float* wq;
   const float* wk;      // decode: k_new norm weight
   const int* positions; // prefill positions or null
-  const int* cache_lens;  // decode only
+  const int* cache_lens;  // decode: cached keys; chunked prefill: keys before the chunk (or null)
+  const int* row_lens;    // chunked prefill: real rows per sequence (or null = n)
   const void* k_new;    // decode only
   const void* v_new;    // decode only
   void* k_cache_out;    // decode: slot L written (k_cache base)

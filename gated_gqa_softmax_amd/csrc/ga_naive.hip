@@ -73,12 +73,17 @@ __global__ __launch_bounds__(64) void naive_kernel(NaiveParams p) {
     pos = L;
     nkeys = L;  // cached keys; the new token is added after the loop
   } else {
+    // chunk against a cache: this row is token base + i of the sequence and
+    // sees keys [0, base + i]; padding rows (i >= chunk rows) are not written
+    const int base = p.cache_lens ? p.cache_lens[b] : 0;
+    const int nb = p.row_lens ? p.row_lens[b] : p.n;
+    if (base < 0 || base > p.max_len || i >= nb) return;  // (whole workgroup)
     const long row = ((long)b * p.n + i) * H + h;
     qoff = row * d;
     ooff = row * d;
     goff = (p.gate_mode == 2) ? row * d : row;
-    pos = p.positions ? p.positions[(long)b * p.n + i] : i;
-    nkeys = i + 1;
+    pos = p.positions ? p.positions[(long)b * p.n + i] : base + i;
+    nkeys = base + i + 1;
   }
 
   float qv[4];

@@ -60,8 +60,8 @@ __device__ __forceinline__ uint16_t* v2_qrow(unsigned char* smem, int r) {
 // load queue. (Each wave waits for its own loads; the barrier for all.)
 template <int D, int BUF>
 __device__ __forceinline__ void v2_step(unsigned char* smem, WaveState<D>& ws, i32x4_t krs, i32x4_t vrs, int koff, int voff, int w, int st, int st_end,
-                                        int kv_row_bytes, int phase, int wave_min_tok, int wave_max_tok,
-                                        int my_lim_tok, int n, float sl2, int hi, int light_end, bool light_wave) {
+                                        int kv_row_bytes, int phase, int wave_min_key, int wave_max_key,
+                                        int my_lim_key, int nkeys, float sl2, int hi, int light_end, bool light_wave) {
   typedef MirrorShape<D> S;
   if (S::NSTAGE == 3 && st + 1 < st_end)
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * S::LOADS_PER_WAVE) : "memory");
@@ -86,9 +86,9 @@ __device__ __forceinline__ void v2_step(unsigned char* smem, WaveState<D>& ws, i
     }
   }
   const int k0 = st * S::ST + phase * 32;
-  if (k0 <= wave_max_tok) {
-    const bool need_mask = (k0 + 31 > wave_min_tok) || (k0 + 32 > n);  // wave-uniform
-    attn_tile<D, kMirrorStages<D>, BUF, 0>(smem, ws, need_mask, my_lim_tok - (k0 + hi * 4), sl2);
+  if (k0 <= wave_max_key) {
+    const bool need_mask = (k0 + 31 > wave_min_key) || (k0 + 32 > nkeys);  // wave-uniform
+    attn_tile<D, kMirrorStages<D>, BUF, 0>(smem, ws, need_mask, my_lim_key - (k0 + hi * 4), sl2);
   }
 }
 
@@ -109,7 +109,10 @@ __device__ __forceinline__ void rope_quarter(float* x, const float2* cs, int sw)
 // Stages (64 keys each) that the queries of unit u (blocks 2u and 2u + 1) see.
 __device__ __forceinline__ int v2_unit_stages(int u, int TB, int n) { return (min(n, (u + 1) * 2 * TB) + 63) / 64; }
 
-template <int D, int GATE, bool SPLIT>
+// CHUNK: a chunk against a cache (per-sequence key offsets and real-row counts
+// from p.key_base / p.row_lens); a separate instantiation, so the
+// whole-sequence kernel carries none of it.
+template <int D, int GATE, bool SPLIT, bool CHUNK = false>
 __global__ __launch_bounds__(512) void prefill_v2_kernel(const PrefillParams p) {
   typedef MirrorShape<D> S;
   static_assert(4 * 32 * D * 4 <= S::BUF_BYTES, "the phase merge reuses the stage buffers");
@@ -138,6 +141,11 @@ __global__ __launch_bounds__(512) void prefill_v2_kernel(const PrefillParams p) 
   const int TB = p.TB;
   const int n = p.n;
   const int grp = p.grp;
+  // Chunk against a cache: the n query rows are tokens L0 + i of the sequence,
+  // rows i < nb are real, and keys [0, L0 + nb) are in the cache. (0 and n
+  // for a whole-sequence prefill.)
+  const int L0 = CHUNK ? p.key_base[b] : 0;
+  const int nb = (CHUNK && p.row_lens) ? min(p.row_lens[b], n) : n;
   const int nH = p.H;
   const int nG = p.G;
   const int nblk = p.nblk;
@@ -179,7 +187,11 @@ __global__ __launch_bounds__(512) void prefill_v2_kernel(const PrefillParams p) 
     blk_light = 2 * unit;
     blk_heavy = (2 * unit + 1 < nblk) ? 2 * unit + 1 : -1;
   }
-  const int kend = min(n, max(blk_light, blk_heavy) * TB + TB);
+  if (CHUNK) {
+    if (L0 < 0 || L0 > p.max_base || nb <= 0) return;  // sequence skipped (whole workgroup)
+    if ((blk_light < 0 || blk_light * TB >= nb) && (blk_heavy < 0 || blk_heavy * TB >= nb)) return;  // no real row
+  }
+  const int kend = L0 + min(nb, max(blk_light, blk_heavy) * TB + TB);  // keys [0, kend) are seen
   const int nst = min(st_hi, (kend + S::ST - 1) / S::ST);  // stages run over [st_lo, nst)
 
   // this lane's query row
@@ -188,7 +200,7 @@ __global__ __launch_bounds__(512) void prefill_v2_kernel(const PrefillParams p) 
   const int my_hh = my_local / TB;
   const int my_tt = my_local - my_hh * TB;
   const int my_tok0 = my_blk * TB + my_tt;
-  const bool my_valid = (my_blk >= 0) && (my_hh < grp) && (my_tok0 < n);
+  const bool my_valid = (my_blk >= 0) && (my_hh < grp) && (my_tok0 < nb);
   const int my_tok = my_valid ? my_tok0 : 0x3fffffff;
   const int my_h = g * grp + my_hh;
   int wave_max_tok = my_valid ? my_tok : -1;
@@ -201,13 +213,17 @@ __global__ __launch_bounds__(512) void prefill_v2_kernel(const PrefillParams p) 
   // wave-uniform: keep them in scalar registers so tile skips and masks branch uniformly
   wave_max_tok = __builtin_amdgcn_readfirstlane(wave_max_tok);
   wave_min_tok = __builtin_amdgcn_readfirstlane(wave_min_tok);
-  const int my_lim_tok = min(my_tok, n - 1);
+  // the same bounds in key indices (row i sees keys [0, L0 + i])
+  const int wave_max_key = (CHUNK && wave_max_tok >= 0) ? L0 + wave_max_tok : wave_max_tok;
+  const int wave_min_key = CHUNK ? L0 + min(wave_min_tok, nb) : wave_min_tok;
+  const int my_lim_key = L0 + min(my_tok, nb - 1);
+  const int nkeys = L0 + nb;
 
   // ---- direct-to-LDS stage loads --------------------------------------------
-  // Buffer resources cover keys [0, n) of this (b, g): rows past the end read
-  // as zeros (out-of-range buffer loads return 0), which the mask then hides.
+  // Buffer resources cover keys [0, nkeys) of this (b, g): rows past the end
+  // read as zeros (out-of-range buffer loads return 0), which the mask hides.
   const int kv_row_bytes = nG * D * 2;
-  const uint32_t valid_bytes = (uint32_t)((n - 1) * kv_row_bytes + D * 2);
+  const uint32_t valid_bytes = (uint32_t)((nkeys - 1) * kv_row_bytes + D * 2);
   const i32x4_t krs = buffer_desc(p.khat + (long)b * k_bstride + (long)g * D, valid_bytes);
   const i32x4_t vrs = buffer_desc(p.v + (long)b * v_bstride + (long)g * D, valid_bytes);
   int koff, voff;
@@ -245,7 +261,7 @@ __global__ __launch_bounds__(512) void prefill_v2_kernel(const PrefillParams p) 
   const int qblk = qside ? blk_heavy : blk_light;
   const int qhh = (qrow & 63) / TB;
   const int qtok0 = qblk * TB + qtt;
-  const bool qvalid = (qblk >= 0) && (qhh < grp) && (qtok0 < n);
+  const bool qvalid = (qblk >= 0) && (qhh < grp) && (qtok0 < nb);
   const int qtok = qvalid ? qtok0 : 0;
   // spread: chunks qq, 4 + qq (rotated), then 8 + 6qq .. 13 + 6qq (unrotated)
   auto qchunk = [&](int i) { return spread ? (i == 0 ? qq : (i == 1 ? 4 + qq : 6 + 6 * qq + i)) : qq * QC + i; };
@@ -257,7 +273,7 @@ __global__ __launch_bounds__(512) void prefill_v2_kernel(const PrefillParams p) 
   int qpos = 0;
   double qfreq[8];
   if (spread) {
-    qpos = p.positions ? p.positions[(long)b * n + qtok] : qtok;
+    qpos = p.positions ? p.positions[(long)b * n + qtok] : L0 + qtok;
 #pragma unroll
     for (int j = 0; j < 8; ++j) qfreq[j] = p.inv_freq[8 * qq + j];
   } else {
@@ -270,8 +286,8 @@ __global__ __launch_bounds__(512) void prefill_v2_kernel(const PrefillParams p) 
       const int tt = half > 0 ? rem / half : 0;
       const int t = rem - tt * half;
       const int blk = side ? blk_heavy : blk_light;
-      const int tok = (blk >= 0 && blk * TB + tt < n) ? blk * TB + tt : 0;
-      tpos[k] = p.positions ? p.positions[(long)b * n + tok] : tok;
+      const int tok = (blk >= 0 && blk * TB + tt < nb) ? blk * TB + tt : 0;
+      tpos[k] = p.positions ? p.positions[(long)b * n + tok] : L0 + tok;
       tfreq[k] = p.inv_freq[t];
     }
   }
@@ -389,17 +405,20 @@ __global__ __launch_bounds__(512) void prefill_v2_kernel(const PrefillParams p) 
   }
 
   // first stage without keys for row groups 0-1 (0 if they have no block)
-  const int light_end = (blk_light >= 0) ? (min(n, blk_light * TB + TB) + S::ST - 1) / S::ST : 0;
+  const int light_end = CHUNK ? ((blk_light >= 0 && blk_light * TB < nb)
+                                      ? (L0 + min(nb, blk_light * TB + TB) + S::ST - 1) / S::ST
+                                      : 0)
+                               : ((blk_light >= 0) ? (min(n, blk_light * TB + TB) + S::ST - 1) / S::ST : 0);
   // ---- main loop, unrolled over the stage buffers -----------------------------
   for (int st0 = st_lo; st0 < nst; st0 += S::NSTAGE) {
-    v2_step<D, 0>(smem, ws, krs, vrs, koff, voff, w, st0, nst, kv_row_bytes, phase, wave_min_tok, wave_max_tok,
-                  my_lim_tok, n, sl2, hi, light_end, rg < 2);
+    v2_step<D, 0>(smem, ws, krs, vrs, koff, voff, w, st0, nst, kv_row_bytes, phase, wave_min_key, wave_max_key,
+                  my_lim_key, nkeys, sl2, hi, light_end, rg < 2);
     if (st0 + 1 < nst)
-      v2_step<D, 1>(smem, ws, krs, vrs, koff, voff, w, st0 + 1, nst, kv_row_bytes, phase, wave_min_tok,
-                    wave_max_tok, my_lim_tok, n, sl2, hi, light_end, rg < 2);
+      v2_step<D, 1>(smem, ws, krs, vrs, koff, voff, w, st0 + 1, nst, kv_row_bytes, phase, wave_min_key,
+                    wave_max_key, my_lim_key, nkeys, sl2, hi, light_end, rg < 2);
     if (S::NSTAGE == 3 && st0 + 2 < nst)
       v2_step<D, (S::NSTAGE == 3 ? 2 : 0)>(smem, ws, krs, vrs, koff, voff, w, st0 + 2, nst, kv_row_bytes, phase,
-                                           wave_min_tok, wave_max_tok, my_lim_tok, n, sl2, hi, light_end, rg < 2);
+                                           wave_min_key, wave_max_key, my_lim_key, nkeys, sl2, hi, light_end, rg < 2);
   }
 
   // ---- epilogue: merge the two phases, normalise, gate, store ---------------
@@ -419,7 +438,7 @@ __global__ __launch_bounds__(512) void prefill_v2_kernel(const PrefillParams p) 
     const int hh = local / TB;
     const int tt = local - hh * TB;
     const int tok = blk * TB + tt;
-    const bool valid = (blk >= 0) && (hh < grp) && (tok < n);
+    const bool valid = (blk >= 0) && (hh < grp) && (tok < nb);
     return valid ? (b * n + tok) * nH + g * grp + hh : -1;
   };
   // Mirrored mode: row indices and gate values are fetched before the merge
@@ -608,12 +627,12 @@ __global__ void zero_words_kernel(unsigned* w, long nwords) {
   if (i < nwords) w[i] = 0u;
 }
 
-template <int D, bool SPLIT>
+template <int D, bool SPLIT, bool CHUNK = false>
 static void launch_v2_gate(const PrefillParams& p, int gate_mode, long grid, hipStream_t s) {
   switch (gate_mode) {
-    case 0: hipLaunchKernelGGL((prefill_v2_kernel<D, 0, SPLIT>), dim3((unsigned)grid), dim3(512), 0, s, p); break;
-    case 1: hipLaunchKernelGGL((prefill_v2_kernel<D, 1, SPLIT>), dim3((unsigned)grid), dim3(512), 0, s, p); break;
-    default: hipLaunchKernelGGL((prefill_v2_kernel<D, 2, SPLIT>), dim3((unsigned)grid), dim3(512), 0, s, p); break;
+    case 0: hipLaunchKernelGGL((prefill_v2_kernel<D, 0, SPLIT, CHUNK>), dim3((unsigned)grid), dim3(512), 0, s, p); break;
+    case 1: hipLaunchKernelGGL((prefill_v2_kernel<D, 1, SPLIT, CHUNK>), dim3((unsigned)grid), dim3(512), 0, s, p); break;
+    default: hipLaunchKernelGGL((prefill_v2_kernel<D, 2, SPLIT, CHUNK>), dim3((unsigned)grid), dim3(512), 0, s, p); break;
   }
 }
 
@@ -632,7 +651,8 @@ static hipError_t launch_v2_d(const PrefillParams& p, int gate_mode, hipStream_t
     const int npairs = (p.nblk + 1) / 2;
     const long grid = (long)p.B * p.G * npairs;
     if (grid <= 0) return hipSuccess;
-    launch_v2_gate<D, false>(p, gate_mode, grid, s);
+    if (p.key_base) launch_v2_gate<D, false, true>(p, gate_mode, grid, s);
+    else launch_v2_gate<D, false>(p, gate_mode, grid, s);
   }
   return hipGetLastError();
 }

@@ -21,7 +21,7 @@ __global__ __launch_bounds__(256) void prep_keys_kernel(PrepParams p) {
   const int l = threadIdx.x & 31;
   const long nrows = (long)p.B * p.n * p.G;
   const long row = (long)blockIdx.x * 8 + hw;
-  const bool valid = row < nrows;
+  bool valid = row < nrows;
   int b = 0, i = 0, g = 0;
   if (valid) {
     g = (int)(row % p.G);
@@ -29,6 +29,10 @@ __global__ __launch_bounds__(256) void prep_keys_kernel(PrepParams p) {
     i = (int)(t % p.n);
     b = (int)(t / p.n);
   }
+  // chunk against a cache: slot base and real rows of this sequence
+  const int base = (valid && p.slot_base) ? p.slot_base[b] : 0;
+  const int nb = (valid && p.row_lens) ? p.row_lens[b] : p.n;
+  if (base < 0 || base > p.max_base || i >= nb) valid = false;
   const int d = p.d;
   const T* src = (const T*)p.src + (long)b * p.src_bstride + ((long)i * p.G + g) * d;
   float x[8];
@@ -51,9 +55,10 @@ __global__ __launch_bounds__(256) void prep_keys_kernel(PrepParams p) {
   }
   __syncthreads();
   if (!valid) return;
-  const int pos = p.positions ? p.positions[(long)b * p.n + i] : i;
+  const int pos = p.positions ? p.positions[(long)b * p.n + i] : base + i;
   const int half = p.rot >> 1;
-  T* dst = (T*)p.dst + (long)b * p.dst_bstride + ((long)i * p.G + g) * d;
+  const long slot = (long)base + i;
+  T* dst = (T*)p.dst + (long)b * p.dst_bstride + (slot * p.G + g) * d;
 #pragma unroll
   for (int m = 0; m < 8; ++m) {
     const int e = l + 32 * m;
@@ -71,7 +76,7 @@ __global__ __launch_bounds__(256) void prep_keys_kernel(PrepParams p) {
   }
   if (p.vdst) {
     const T* vs = (const T*)p.vsrc + (long)b * p.vsrc_bstride + ((long)i * p.G + g) * d;
-    T* vd = (T*)p.vdst + (long)b * p.vdst_bstride + ((long)i * p.G + g) * d;
+    T* vd = (T*)p.vdst + (long)b * p.vdst_bstride + (slot * p.G + g) * d;
     for (int e = l; e < d; e += 32) vd[e] = vs[e];
   }
 }
@@ -106,19 +111,24 @@ __global__ __launch_bounds__(256) void prep_keys_vec_kernel(PrepParams p) {
 #pragma unroll
   for (int it = 0; it < NIT; ++it) {
     const int r = wave * RPW + it * RPI + rsub;
-    const bool valid = r < nrows;
+    bool valid = r < nrows;
     const int rc = valid ? r : 0;  // reads stay in range; invalid rows are not stored
     const int t = rc / p.G;
     const int g = rc - t * p.G;
     const int b = t / p.n;
     const int i = t - b * p.n;
+    // chunk against a cache: slot base and real rows of this sequence
+    const int base = p.slot_base ? p.slot_base[b] : 0;
+    const int nb = p.row_lens ? p.row_lens[b] : p.n;
+    if (base < 0 || base > p.max_base || i >= nb) valid = false;
     const long tail = ((long)i * p.G + g) * D + c * 8;
+    const long dtail = (((long)base + i) * p.G + g) * D + c * 8;
     raw[it] = *(const u32x4_t*)(src + (long)b * p.src_bstride + tail);
-    pos[it] = p.positions ? p.positions[(long)b * p.n + i] : i;
-    drow[it] = valid ? (long)b * p.dst_bstride + tail : -1;
+    pos[it] = p.positions ? p.positions[(long)b * p.n + i] : base + i;
+    drow[it] = valid ? (long)b * p.dst_bstride + dtail : -1;
     if (vdst) {
       vraw[it] = *(const u32x4_t*)(vsrc + (long)b * p.vsrc_bstride + tail);
-      vdrow[it] = (long)b * p.vdst_bstride + tail;
+      vdrow[it] = (long)b * p.vdst_bstride + dtail;
     }
   }
   float w8[8];

@@ -156,6 +156,63 @@ ga_status ga_prefill_attention(const ga_attn_desc* desc, int32_t seq_len,
                                void* workspace, size_t workspace_bytes,
                                void* out, void* stream);
 
+/* ---- chunked prefill against a KV cache ---------------------------------- */
+
+/* A chunk of new tokens per sequence, appended after the tokens already in a
+ * KV cache: the step between a whole-sequence prefill and decode. The
+ * attention mask M is the causal mask in cache slots plus a padding mask
+ * ("Gated Attention：算完注意力，再决定用多少", section "门放在哪里？": M is the
+ * causal / padding mask); the cached keys and values are read as stored
+ * ("多头注意力与 GQA", section "标准多头注意力（MHA）": history K and V are
+ * kept and re-read, Q is not). "Transformer by Hand · 6. Gated attention"
+ * leaves the state and mask arguments of its forward to a later chapter.
+ *
+ * For sequence b with L_b = cache_lens[b] tokens cached (K-hat and V in slots
+ * [0, L_b) of k_cache / v_cache) and n_b = chunk_lens[b] real rows of the
+ * seq_len-row chunk (chunk_lens NULL: n_b = seq_len):
+ *  - chunk row i < n_b is token L_b + i: its K-hat = RoPE(RMSNorm(k)) and v go
+ *    to slot L_b + i, and its query attends to slots [0, L_b + i];
+ *  - rows i >= n_b are padding: no cache slot and no output row is written;
+ *  - positions [B,seq_len] are the RoPE positions of the chunk rows (NULL:
+ *    L_b + i);
+ *  - a sequence with L_b outside [0, max_cache_len] is skipped entirely.
+ *  q, k, v       [B,seq_len,H,d] / [B,seq_len,G,d] / [B,seq_len,G,d], raw projections.
+ *  gate          as for ga_prefill.
+ *  k_cache, v_cache  [B,cache_cap,G,d], cache_cap >= max_cache_len + seq_len,
+ *                max_cache_len + seq_len < 2^30.
+ *  cache_lens, chunk_lens  device int32 [B] (chunk_lens may be NULL).
+ *  out           [B,seq_len,H*d]; rows of padding and skipped sequences are left as they were.
+ * The library does not advance cache_lens (the caller adds n_b afterwards).
+ * No workspace. Errors as for ga_prefill. */
+ga_status ga_prefill_chunk(const ga_attn_desc* desc, int32_t seq_len,
+                           const void* q, const void* k, const void* v, const void* gate,
+                           const float* q_norm_w, const float* k_norm_w, const int32_t* positions,
+                           void* k_cache, void* v_cache, int32_t cache_cap,
+                           const int32_t* cache_lens, const int32_t* chunk_lens, int32_t max_cache_len,
+                           void* out, void* stream);
+
+/* First stage of ga_prefill_chunk (one kernel): writes K-hat and v of the
+ * real chunk rows to cache slots [L_b, L_b + n_b). */
+ga_status ga_prefill_chunk_keys(const ga_attn_desc* desc, int32_t seq_len,
+                                const void* k, const void* v, const float* k_norm_w,
+                                const int32_t* positions, const int32_t* cache_lens,
+                                const int32_t* chunk_lens, int32_t max_cache_len,
+                                void* k_cache, void* v_cache, int32_t cache_cap, void* stream);
+
+/* Second stage of ga_prefill_chunk (one kernel): the chunk's queries against
+ * cache slots [0, L_b + i], gated, into out. Expects the chunk's own K-hat
+ * and v already in the cache (ga_prefill_chunk_keys). */
+ga_status ga_prefill_chunk_attention(const ga_attn_desc* desc, int32_t seq_len, const void* q,
+                                     const void* k_cache, const void* v_cache, int32_t cache_cap,
+                                     const int32_t* cache_lens, const int32_t* chunk_lens,
+                                     int32_t max_cache_len, const void* gate, const float* q_norm_w,
+                                     const int32_t* positions, void* out, void* stream);
+
+/* Name of the kernel ga_prefill_chunk_attention runs for this shape:
+ * "mirror" (the mirrored prefill kernel with per-sequence key offsets) or
+ * "generic"; "invalid" for a bad descriptor. */
+const char* ga_prefill_chunk_kernel(const ga_attn_desc* desc, int32_t seq_len, int32_t cache_cap);
+
 /* ---- decode ------------------------------------------------------------- */
 
 /* Key-chunk length of one decode split (keys per partial result). */

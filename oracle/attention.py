@@ -269,6 +269,59 @@ def prefill_rows(q, k, v, gate, rows: Sequence[tuple], *, gate_mode: str, q_norm
     return out
 
 
+def prefill_chunk(q, k, v, gate, *, gate_mode: str, q_norm_w, k_norm_w, k_cache_rows, cache_lens,
+                  chunk_lens=None, positions=None, max_cache_len: Optional[int] = None, rms_eps: float = 1e-6,
+                  rope_base: float = 10000.0, rot_dim: int = 0, scale: Optional[float] = None, dtype=np.float64):
+    """A chunk of new tokens per sequence after the tokens already in a KV cache.
+
+    q [B,n,H,d], k/v [B,n,G,d] (raw), gate as for ``prefill``.
+    ``k_cache_rows(b)`` returns (K-hat [L_b,G,d], V [L_b,G,d]) for sequence b,
+    the L_b = cache_lens[b] cached rows, used as stored. Chunk row i < n_b
+    (n_b = chunk_lens[b], default n) is token L_b + i: its K-hat is
+    RoPE(RMSNorm(k)) at position positions[b,i] (default L_b + i), and its
+    query attends to the cached rows and to chunk rows 0..i, i.e. to cache
+    slots [0, L_b + i]. Rows i >= n_b (padding), and every row of a sequence
+    whose L_b lies outside [0, max_cache_len], are not computed: NaN.
+    Returns (out [B,n,H*d], k_hat [B,n,G,d] of the chunk rows).
+
+    Sources: the mask M of "Gated Attention：算完注意力，再决定用多少", section
+    "门放在哪里？" (causal / padding mask), with the cache of "多头注意力与 GQA",
+    section "标准多头注意力（MHA）" (history K and V kept and re-read); for one
+    sequence this is rows L_b.. of ``prefill`` over the whole sequence.
+    """
+    for name, x in (("q", q), ("k", k), ("v", v)):
+        _check_finite(name, x)
+    q = np.asarray(q)
+    B, n, H, d = q.shape
+    G = np.asarray(k).shape[2]
+    sc = _default_scale(d, scale)
+    lens = np.asarray(cache_lens)
+    out = np.full((B, n, H, d), np.nan, dtype=dtype)
+    khat = np.full((B, n, G, d), np.nan, dtype=dtype)
+    for b in range(B):
+        L = int(lens[b])
+        nb = n if chunk_lens is None else max(0, min(n, int(np.asarray(chunk_lens)[b])))
+        if L < 0 or (max_cache_len is not None and L > max_cache_len) or nb == 0:
+            continue
+        pos = (np.arange(L, L + nb) if positions is None else np.asarray(positions)[b, :nb])
+        qh = rope(rms_norm(q[b, :nb], q_norm_w, rms_eps, dtype), pos, rot_dim, rope_base, dtype)       # [nb,H,d]
+        kh = rope(rms_norm(np.asarray(k)[b, :nb], k_norm_w, rms_eps, dtype), pos, rot_dim, rope_base, dtype)
+        khat[b, :nb] = kh
+        kc, vc = k_cache_rows(b)
+        keys = np.concatenate([np.asarray(kc, dtype=dtype)[:L], kh], axis=0)                          # [L+nb,G,d]
+        vals = np.concatenate([np.asarray(vc, dtype=dtype)[:L], np.asarray(v, dtype=dtype)[b, :nb]], axis=0)
+        rows = L + np.arange(nb)[:, None]                          # cache slot of each chunk row
+        hidden = np.arange(L + nb)[None, :] > rows                 # causal in cache slots
+        for h in range(H):
+            g = kv_group(h, H, G)
+            s = (qh[:, h] @ keys[:, g].T) * dtype(sc)
+            s = np.where(hidden, -np.inf, s)
+            out[b, :nb, h] = softmax_rows(s, dtype) @ vals[:, g]
+        z = None if gate_mode == GATE_NONE else np.asarray(gate)[b, :nb]   # [nb,H,d] or [nb,H]
+        out[b, :nb] = apply_gate(out[b, :nb], z, gate_mode, dtype)
+    return out.reshape(B, n, H * d), khat
+
+
 def decode(q, k_new, v_new, gate, *, gate_mode: str, q_norm_w, k_norm_w, k_cache_rows: Iterable,
            cache_lens, rms_eps: float = 1e-6, rope_base: float = 10000.0, rot_dim: int = 0,
            scale: Optional[float] = None, dtype=np.float64, seqs: Optional[Sequence[int]] = None):

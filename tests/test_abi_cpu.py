@@ -169,3 +169,31 @@ def test_decode_rejects_bad_arguments():
     assert call(desc=_desc(batch=0), q=None) == _lib.GA_OK
     assert lib.ga_decode_partials(ctypes.byref(_desc(head_dim=96, rot_dim=16)), A16, None, A16, A16, 101, A16,
                                   100, A16, 1 << 30, None) == _lib.GA_ERR_UNSUPPORTED
+
+
+def test_prefill_chunk_rejects_bad_arguments_and_names_its_kernel(monkeypatch):
+    lib = _lib_or_build()
+    d = _desc(batch=2)
+
+    def call(desc=d, n=64, cap=1100, max_len=1000, lens=A16, q=A16, k_cache=A16, out=A16, gate=A16):
+        return lib.ga_prefill_chunk(ctypes.byref(desc), n, q, A16, A16, gate, None, None, None, k_cache, A16, cap,
+                                    lens, None, max_len, out, None)
+
+    assert call(cap=1063) == _lib.GA_ERR_BAD_SHAPE             # cap < max_cache_len + seq_len
+    assert call(max_len=-1) == _lib.GA_ERR_BAD_SHAPE
+    assert call(lens=None) == _lib.GA_ERR_NULL_ARG
+    assert call(k_cache=None) == _lib.GA_ERR_NULL_ARG
+    assert call(gate=None) == _lib.GA_ERR_NULL_ARG             # elementwise gate required
+    assert call(out=MIS) == _lib.GA_ERR_MISALIGNED
+    assert call(n=-1) == _lib.GA_ERR_BAD_SHAPE
+    assert call(max_len=(1 << 30) - 10, cap=(1 << 30) + 100) == _lib.GA_ERR_UNSUPPORTED
+    assert call(desc=_desc(batch=0), q=None) == _lib.GA_OK
+    assert lib.ga_prefill_chunk_keys(ctypes.byref(d), 64, A16, A16, None, None, None, None, 1000, A16, A16, 1100,
+                                     None) == _lib.GA_ERR_NULL_ARG
+    assert lib.ga_prefill_chunk_attention(ctypes.byref(d), 64, A16, A16, A16, 1000, A16, None, 1000, A16, None,
+                                          None, A16, None) == _lib.GA_ERR_BAD_SHAPE
+    assert lib.ga_prefill_chunk_kernel(ctypes.byref(d), 64, 1100) == b"mirror"
+    assert lib.ga_prefill_chunk_kernel(ctypes.byref(_desc(dtype=_lib.GA_F32)), 64, 1100) == b"generic"
+    assert lib.ga_prefill_chunk_kernel(ctypes.byref(_desc(head_dim=64, rot_dim=16)), 64, 1100) == b"generic"
+    monkeypatch.setenv("GA_PREFILL_KERNEL", "generic")
+    assert lib.ga_prefill_chunk_kernel(ctypes.byref(d), 64, 1100) == b"generic"
