@@ -35,6 +35,7 @@ def parse():
     ap.add_argument("--workload", default="qwen35_0p8b_prefill",
                     help="prefill workload to time (default: the headline one)")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-chunk", action="store_true", help="skip the chunked-prefill measurement")
     ap.add_argument("--no-prefill", action="store_true", help="decode only (for counter runs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--decode-steps", type=int, default=20)
@@ -318,6 +319,64 @@ def cpu_baseline(w, x, flops, budget_s=15.0):
                       f"({t:.2f} s each)", "cpu": cpu}
 
 
+def time_chunk(torch, api, inputs, accounting, steps, warmup):
+    """Chunked prefill against a KV cache: four 1024-token chunks of the
+    Qwen3.5-0.8B attention shape after 0, 1024, 2048 and 3072 cached tokens."""
+    w = inputs.WORKLOADS["qwen35_0p8b_chunk"]
+    x = inputs.make_prefill(w)
+    et = torch.bfloat16
+    lens = np.array(w.extra["cache_lens"], dtype=np.int32)
+    max_len = int(lens.max())
+    cap = max_len + w.seq_len
+    gen = torch.Generator(device="cuda").manual_seed(w.seed)
+    shape = (w.batch, cap, w.n_kv_heads, w.head_dim)
+    kc = torch.randn(shape, generator=gen, device="cuda").to(et)   # cached K-hat / V prefix (synthetic)
+    vc = torch.randn(shape, generator=gen, device="cuda").to(et)
+    dv = lambda a, dt=None: torch.from_numpy(np.ascontiguousarray(a)).to("cuda", dtype=dt)
+    q, k, v, gate = dv(x["q"], et), dv(x["k"], et), dv(x["v"], et), dv(x["gate"], et)
+    wq, wk, dl = dv(x["q_norm_w"]), dv(x["k_norm_w"]), dv(lens)
+    d = api.make_desc(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.rot_dim, w.rope_base, w.rms_eps, 0.0, et,
+                      w.gate_mode)
+    out = torch.empty((w.batch, w.seq_len, w.n_q_heads * w.head_dim), dtype=et, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def whole():
+        api.ga_prefill_chunk(d, q, k, v, kc, vc, dl, max_len, gate=gate, q_norm_w=wq, k_norm_w=wk, out=out,
+                             stream=stream)
+
+    def attention():
+        api.ga_prefill_chunk_attention(d, q, kc, vc, dl, max_len, gate=gate, q_norm_w=wq, out=out, stream=stream)
+
+    for _ in range(warmup):
+        whole()
+    res = {}
+    for name, fn in (("step_ms", whole), ("kernel_ms", attention)):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(steps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        res[name] = e0.elapsed_time(e1) / steps
+    flops = accounting.chunk_prefill_flops(lens, w.n_q_heads, w.head_dim, w.seq_len)
+    achieved = flops / (res["kernel_ms"] * 1e-3) / 1e12
+    kernel = PREFILL_KERNEL_SYMBOL[api.ga_prefill_chunk_kernel(d, w.seq_len, cap)]
+    return {
+        "metric": "chunked prefill TFLOP/s",
+        "value": flops / (res["step_ms"] * 1e-3) / 1e12,
+        "unit": "TFLOP/s",
+        "ms_per_step": res["step_ms"],
+        "steps": steps,
+        "config": {"workload": w.name, "batch": w.batch, "chunk_len": w.seq_len, "cache_lens": lens.tolist(),
+                   "n_q_heads": w.n_q_heads, "n_kv_heads": w.n_kv_heads, "head_dim": w.head_dim,
+                   "rot_dim": w.rot_dim, "gate": w.gate_mode},
+        "roofline": {"bound": "mfma", "kernel": kernel, "achieved": achieved, "peak": MI355X_BF16_DENSE_TFLOPS,
+                     "unit": "TFLOP/s", "frac": achieved / MI355X_BF16_DENSE_TFLOPS, "kernel_ms": res["kernel_ms"],
+                     "algorithmic_flops": flops},
+    }
+
+
 def main():
     args = parse()
     if args.record_traffic:
@@ -367,6 +426,8 @@ def main():
     }
     if not args.no_decode:
         rec["decode"] = time_decode(torch, api, inputs, accounting, args.decode_steps, args.warmup)
+    if not args.no_chunk:
+        rec["chunk"] = time_chunk(torch, api, inputs, accounting, args.steps, args.warmup)
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(w, pre["x"], pre["flops"])
     print(json.dumps(rec), flush=True)

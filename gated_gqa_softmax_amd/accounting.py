@@ -14,6 +14,13 @@ def causal_prefill_flops(batch: int, n_q_heads: int, head_dim: int, seq_len: int
     return 2.0 * batch * n_q_heads * head_dim * seq_len * (seq_len + 1)
 
 
+def chunk_prefill_flops(cache_lens, n_q_heads: int, head_dim: int, chunk_len: int) -> float:
+    """Chunked prefill: row i of sequence b sees L_b + i + 1 keys, so
+    sum_b 2*H*d*(2*n*L_b + n*(n+1)) (the whole-sequence formula when L_b = 0)."""
+    n = chunk_len
+    return float(sum(2.0 * n_q_heads * head_dim * (2.0 * n * int(L) + n * (n + 1)) for L in cache_lens))
+
+
 def kv_numbers_per_token(n_kv_heads: int, head_dim: int) -> int:
     """Cached numbers per token per full-attention layer: 2 (K and V) * G * d."""
     return 2 * n_kv_heads * head_dim

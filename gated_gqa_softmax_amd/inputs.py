@@ -63,9 +63,11 @@ class Workload:
         return replace(self, **kw)
 
 
-# The five synthetic workloads (shapes taken from the pages' models: a toy,
+# The synthetic workloads (shapes taken from the pages' models: a toy,
 # Qwen3.5-0.8B's 8/2/256, Qwen3-0.6B's 16/8/128, the paper's MoE 32/4/128 at
-# 32K tokens, and a decode batch over a long cache).
+# 32K tokens, a decode batch over a long cache, and chunked prefill of the
+# Qwen3.5-0.8B shape: four 1024-token chunks after 0, 1024, 2048 and 3072
+# cached tokens).
 WORKLOADS = {
     "toy": Workload("toy", "prefill", 1, 16, 2, 1, 8, 2, "f32", GATE_ELEMENTWISE, seed=1),
     "qwen35_0p8b_prefill": Workload("qwen35_0p8b_prefill", "prefill", 1, 4096, 8, 2, 256, 64,
@@ -76,6 +78,8 @@ WORKLOADS = {
                                          128, 32, "bf16", GATE_ELEMENTWISE, seed=4),
     "decode_64seq": Workload("decode_64seq", "decode", 64, 1, 8, 2, 256, 64, "bf16",
                              GATE_ELEMENTWISE, seed=5, cache_len_lo=1024, cache_len_hi=32768),
+    "qwen35_0p8b_chunk": Workload("qwen35_0p8b_chunk", "prefill", 4, 1024, 8, 2, 256, 64, "bf16",
+                                  GATE_ELEMENTWISE, seed=6, extra={"cache_lens": [0, 1024, 2048, 3072]}),
 }
 
 

@@ -160,3 +160,16 @@ def test_causal_flop_count():
     n, d, H, B = 37, 8, 3, 2
     pairs = sum(i + 1 for i in range(n))
     assert accounting.causal_prefill_flops(B, H, d, n) == B * H * pairs * 4 * d
+
+
+def test_flop_counts_match_brute_force_pair_counts():
+    """The flop formulas count 4d per visible (query row, key) pair per query
+    head: compare with pairs counted one by one on small shapes."""
+    H, d = 3, 8
+    for n in (1, 2, 7, 16):
+        pairs = sum(i + 1 for i in range(n))
+        assert accounting.causal_prefill_flops(2, H, d, n) == 2 * H * 4 * d * pairs
+    lens, n = [0, 5, 9], 6
+    pairs = sum(L + i + 1 for L in lens for i in range(n))
+    assert accounting.chunk_prefill_flops(lens, H, d, n) == H * 4 * d * pairs
+    assert accounting.chunk_prefill_flops([0], H, d, n) == accounting.causal_prefill_flops(1, H, d, n)
