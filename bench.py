@@ -106,13 +106,17 @@ def counter_per_dispatch(csv_path: str, kernel: str, counter: str) -> float:
     """Mean over dispatches of one rocprofv3 counter (summed over its instances)
     for the kernels whose name contains `kernel`."""
     import csv
-    per = {}
+    per, names = {}, set()
     with open(csv_path) as f:
         for r in csv.DictReader(f):
             if kernel in r["Kernel_Name"] and r["Counter_Name"] == counter:
                 per[r["Dispatch_Id"]] = per.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
+                names.add(r["Kernel_Name"])
     if not per:
         raise SystemExit(f"{csv_path}: no {counter} rows for a kernel named *{kernel}*")
+    if len(names) > 1:
+        raise SystemExit(f"{csv_path}: *{kernel}* matches several kernels ({sorted(names)}); "
+                         "profile a run with only the one workload")
     return sum(per.values()) / len(per)
 
 
