@@ -186,6 +186,31 @@ def kv_group(h: int, n_q_heads: int, n_kv_heads: int) -> int:
     return h // (n_q_heads // n_kv_heads)
 
 
+def split_q_proj(qg: np.ndarray, head_dim: int, gate_mode: str):
+    """(q, gate) from the output of a q projection that also makes the gate.
+
+    "Transformer by Hand · 6. Gated attention", "Why the gate is packed into
+    q_proj" and the forward code and shape table of "The code:
+    qwen/attention.py": the projection's [.., H*2d] output, viewed per head as
+    [.., H, 2d], holds each head's d query values followed by its d gate
+    logits. ``qg`` is that per-head view. The pages pack only the elementwise
+    gate; for a headwise gate this reads the same layout with one logit per
+    head, [.., H, d+1] (query values, then the logit). Returns
+    q [.., H, d] and gate [.., H, d] (elementwise) or [.., H] (headwise).
+    """
+    qg = np.asarray(qg)
+    d = int(head_dim)
+    if gate_mode == GATE_ELEMENTWISE:
+        if qg.shape[-1] != 2 * d:
+            raise ValueError(f"fused q/gate rows have {qg.shape[-1]} values, expected {2 * d}")
+        return qg[..., :d], qg[..., d:]
+    if gate_mode == GATE_HEADWISE:
+        if qg.shape[-1] != d + 1:
+            raise ValueError(f"fused q/gate rows have {qg.shape[-1]} values, expected {d + 1}")
+        return qg[..., :d], qg[..., d]
+    raise ValueError(f"a fused q/gate projection needs a gate, got gate_mode {gate_mode!r}")
+
+
 def _default_scale(d: int, scale: Optional[float]) -> float:
     # 1/sqrt(head_dim): "The formula" on "Transformer by Hand · 6. Gated attention".
     return 1.0 / math.sqrt(d) if not scale else float(scale)
