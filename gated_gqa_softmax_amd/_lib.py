@@ -40,6 +40,8 @@ class AttnDesc(ctypes.Structure):
         ("softmax_scale", ctypes.c_float),
         ("dtype", ctypes.c_int32),
         ("gate_mode", ctypes.c_int32),
+        ("q_head_stride", ctypes.c_int32),
+        ("gate_head_stride", ctypes.c_int32),
     ]
 
 

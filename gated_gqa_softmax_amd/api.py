@@ -1,7 +1,9 @@
 """Python binding of the C ABI (include/ga.h), one function per entry point.
 
 Argument marshalling only: each function checks that tensors are on the
-GPU, contiguous and of the declared element type, fills the ``ga_attn_desc``,
+GPU, contiguous (q and the gate: rows of heads at a fixed stride, such as the
+two halves of a fused q projection's output) and of the declared element
+type, fills the ``ga_attn_desc``,
 passes raw device pointers and the current HIP stream to libga.so, and
 raises ``GaError`` when the library returns a non-OK status. Every step of
 the computation runs in the library's HIP kernels. PyTorch supplies device
@@ -33,11 +35,15 @@ class GaError(RuntimeError):
 
 
 def make_desc(batch, n_q_heads, n_kv_heads, head_dim, rot_dim=0, rope_base=10000.0, rms_eps=1e-6,
-              softmax_scale=0.0, dtype=torch.bfloat16, gate_mode="none") -> AttnDesc:
+              softmax_scale=0.0, dtype=torch.bfloat16, gate_mode="none", q_head_stride=0,
+              gate_head_stride=0) -> AttnDesc:
+    """Descriptor; the head strides matter only to the kernel-name queries
+    (the entry points below take them from the q and gate tensors)."""
     return AttnDesc(int(batch), int(n_q_heads), int(n_kv_heads), int(head_dim), int(rot_dim),
                     float(rope_base), float(rms_eps), float(softmax_scale),
                     _DTYPE[dtype] if isinstance(dtype, torch.dtype) else int(dtype),
-                    _GATE[gate_mode] if isinstance(gate_mode, str) else int(gate_mode))
+                    _GATE[gate_mode] if isinstance(gate_mode, str) else int(gate_mode),
+                    int(q_head_stride), int(gate_head_stride))
 
 
 def _ptr(t: Optional[torch.Tensor], name: str, dtype=None) -> Optional[int]:
@@ -50,6 +56,62 @@ def _ptr(t: Optional[torch.Tensor], name: str, dtype=None) -> Optional[int]:
     if dtype is not None and t.dtype != dtype:
         raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
     return t.data_ptr()
+
+
+def head_stride(shape, strides, lead: int, n_heads: int, width: int, name: str = "tensor") -> int:
+    """Head stride (elements) of q or a gate given as a shape and strides, as
+    the ABI reads them: dims [*lead, H, width] (a headwise gate: [*lead, H] or
+    [*lead, H, 1]) whose innermost dim is dense, with head rows ``stride``
+    apart and the rows of one token, then of one sequence, following each
+    other. Contiguous tensors and views of a fused [*lead, H, 2d] projection
+    output qualify; anything else raises ValueError."""
+    shape, strides = list(shape), list(strides)
+    if width == 1 and len(shape) == lead + 2 and shape[-1] == 1:
+        shape, strides = shape[:-1], strides[:-1]
+    rank = lead + (1 if width == 1 else 2)
+    if len(shape) != rank or shape[lead] != n_heads or (width > 1 and shape[-1] != width):
+        raise ValueError(f"{name} has shape {tuple(shape)}, expected {lead} leading dims, {n_heads} heads"
+                         f"{'' if width == 1 else f' and {width} values per head'}")
+    if width > 1 and strides[-1] != 1:
+        raise ValueError(f"{name}: the innermost dim must be dense")
+    # the head stride is what the outermost dims of size > 1 imply (a dim of
+    # size 1 has no meaningful stride); every such dim must agree with it
+    stride, inner = width, 1
+    for dim in range(lead, -1, -1):
+        if shape[dim] > 1:
+            if strides[dim] % inner:
+                raise ValueError(f"{name}: strides {tuple(strides)} are not head rows at one stride")
+            stride = strides[dim] // inner
+            break
+        inner *= shape[dim]
+    expect = stride
+    for dim in range(lead, -1, -1):
+        if shape[dim] > 1 and strides[dim] != expect:
+            raise ValueError(f"{name}: strides {tuple(strides)} are not head rows at one stride")
+        expect *= shape[dim]
+    if stride < width or stride >= 2 ** 31:
+        raise ValueError(f"{name}: head stride {stride} out of range")
+    return stride
+
+
+def _head_rows(t: torch.Tensor, name: str, dtype, lead: int, n_heads: int, width: int) -> int:
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    return head_stride(t.shape, t.stride(), lead, n_heads, width, name)
+
+
+def _qg(desc: AttnDesc, q, gate, lead: int, et):
+    """Copy of ``desc`` with the head strides of q and the gate, and their pointers."""
+    d2 = AttnDesc.from_buffer_copy(desc)
+    d2.q_head_stride = _head_rows(q, "q", et, lead, desc.n_q_heads, desc.head_dim)
+    gp = None
+    if gate is not None:
+        gw = desc.head_dim if desc.gate_mode == _lib.GA_GATE_ELEMENTWISE else 1
+        d2.gate_head_stride = _head_rows(gate, "gate", et, lead, desc.n_q_heads, gw)
+        gp = gate.data_ptr()
+    return d2, q.data_ptr(), gp
 
 
 def _stream(stream) -> int:
@@ -126,8 +188,9 @@ def ga_prefill(desc: AttnDesc, q, k, v, gate=None, q_norm_w=None, k_norm_w=None,
         ws_bytes = ga_prefill_workspace_bytes(desc, n)
     if ws_bytes:
         workspace = _workspace(ws_bytes, q.device, workspace)
-    st = lib.ga_prefill(ctypes.byref(desc), n, _ptr(q, "q", et), _ptr(k, "k", et), _ptr(v, "v", et),
-                        _ptr(gate, "gate", et), _ptr(q_norm_w, "q_norm_w", torch.float32),
+    d2, qp, gp = _qg(desc, q, gate, 2, et)
+    st = lib.ga_prefill(ctypes.byref(d2), n, qp, _ptr(k, "k", et), _ptr(v, "v", et),
+                        gp, _ptr(q_norm_w, "q_norm_w", torch.float32),
                         _ptr(k_norm_w, "k_norm_w", torch.float32), _ptr(positions, "positions", torch.int32),
                         _ptr(k_cache, "k_cache", et), _ptr(v_cache, "v_cache", et), cap,
                         _ptr(workspace, "workspace"), workspace.numel() if workspace is not None else 0,
@@ -161,8 +224,9 @@ def ga_prefill_attention(desc: AttnDesc, q, k_hat, v, gate=None, q_norm_w=None, 
     ws_bytes = ga_prefill_attention_workspace_bytes(desc, n)
     if ws_bytes:
         workspace = _workspace(ws_bytes, q.device, workspace)
-    st = lib.ga_prefill_attention(ctypes.byref(desc), n, _ptr(q, "q", et), _ptr(k_hat, "k_hat", et), k_hat.shape[1],
-                                  _ptr(v, "v", et), v.shape[1], _ptr(gate, "gate", et),
+    d2, qp, gp = _qg(desc, q, gate, 2, et)
+    st = lib.ga_prefill_attention(ctypes.byref(d2), n, qp, _ptr(k_hat, "k_hat", et), k_hat.shape[1],
+                                  _ptr(v, "v", et), v.shape[1], gp,
                                   _ptr(q_norm_w, "q_norm_w", torch.float32), _ptr(positions, "positions", torch.int32),
                                   _ptr(workspace, "workspace"), workspace.numel() if workspace is not None else 0,
                                   _ptr(out, "out", et), _stream(stream))
@@ -188,8 +252,9 @@ def ga_prefill_chunk(desc: AttnDesc, q, k, v, k_cache, v_cache, cache_lens, max_
     B, n = q.shape[0], q.shape[1]
     if out is None:
         out = torch.zeros((B, n, desc.n_q_heads * desc.head_dim), dtype=et, device=q.device)
-    st = lib.ga_prefill_chunk(ctypes.byref(desc), n, _ptr(q, "q", et), _ptr(k, "k", et), _ptr(v, "v", et),
-                              _ptr(gate, "gate", et), _ptr(q_norm_w, "q_norm_w", torch.float32),
+    d2, qp, gp = _qg(desc, q, gate, 2, et)
+    st = lib.ga_prefill_chunk(ctypes.byref(d2), n, qp, _ptr(k, "k", et), _ptr(v, "v", et),
+                              gp, _ptr(q_norm_w, "q_norm_w", torch.float32),
                               _ptr(k_norm_w, "k_norm_w", torch.float32), _ptr(positions, "positions", torch.int32),
                               _ptr(k_cache, "k_cache", et), _ptr(v_cache, "v_cache", et), k_cache.shape[1],
                               _ptr(cache_lens, "cache_lens", torch.int32), _ptr(chunk_lens, "chunk_lens", torch.int32),
@@ -220,11 +285,12 @@ def ga_prefill_chunk_attention(desc: AttnDesc, q, k_cache, v_cache, cache_lens, 
     B, n = q.shape[0], q.shape[1]
     if out is None:
         out = torch.zeros((B, n, desc.n_q_heads * desc.head_dim), dtype=et, device=q.device)
-    st = lib.ga_prefill_chunk_attention(ctypes.byref(desc), n, _ptr(q, "q", et), _ptr(k_cache, "k_cache", et),
+    d2, qp, gp = _qg(desc, q, gate, 2, et)
+    st = lib.ga_prefill_chunk_attention(ctypes.byref(d2), n, qp, _ptr(k_cache, "k_cache", et),
                                         _ptr(v_cache, "v_cache", et), k_cache.shape[1],
                                         _ptr(cache_lens, "cache_lens", torch.int32),
                                         _ptr(chunk_lens, "chunk_lens", torch.int32), int(max_cache_len),
-                                        _ptr(gate, "gate", et), _ptr(q_norm_w, "q_norm_w", torch.float32),
+                                        gp, _ptr(q_norm_w, "q_norm_w", torch.float32),
                                         _ptr(positions, "positions", torch.int32), _ptr(out, "out", et),
                                         _stream(stream))
     _check(st, "ga_prefill_chunk_attention")
@@ -240,8 +306,9 @@ def ga_decode(desc: AttnDesc, q, k_new, v_new, k_cache, v_cache, cache_lens, max
     if out is None:
         out = torch.empty((B, desc.n_q_heads * desc.head_dim), dtype=et, device=q.device)
     workspace = _workspace(ga_decode_workspace_bytes(desc, max_cache_len), q.device, workspace)
-    st = lib.ga_decode(ctypes.byref(desc), _ptr(q, "q", et), _ptr(k_new, "k_new", et), _ptr(v_new, "v_new", et),
-                       _ptr(gate, "gate", et), _ptr(q_norm_w, "q_norm_w", torch.float32),
+    d2, qp, gp = _qg(desc, q, gate, 1, et)
+    st = lib.ga_decode(ctypes.byref(d2), qp, _ptr(k_new, "k_new", et), _ptr(v_new, "v_new", et),
+                       gp, _ptr(q_norm_w, "q_norm_w", torch.float32),
                        _ptr(k_norm_w, "k_norm_w", torch.float32), _ptr(k_cache, "k_cache", et),
                        _ptr(v_cache, "v_cache", et), k_cache.shape[1], _ptr(cache_lens, "cache_lens", torch.int32),
                        int(max_cache_len), _ptr(workspace, "workspace"), workspace.numel(), _ptr(out, "out", et),
@@ -254,7 +321,8 @@ def ga_decode_partials(desc: AttnDesc, q, k_cache, v_cache, cache_lens, max_cach
                        q_norm_w=None, stream=None) -> torch.Tensor:
     lib = _lib.load()
     et = _elem_dtype(desc)
-    st = lib.ga_decode_partials(ctypes.byref(desc), _ptr(q, "q", et), _ptr(q_norm_w, "q_norm_w", torch.float32),
+    d2, qp, _ = _qg(desc, q, None, 1, et)
+    st = lib.ga_decode_partials(ctypes.byref(d2), qp, _ptr(q_norm_w, "q_norm_w", torch.float32),
                                 _ptr(k_cache, "k_cache", et), _ptr(v_cache, "v_cache", et), k_cache.shape[1],
                                 _ptr(cache_lens, "cache_lens", torch.int32), int(max_cache_len),
                                 _ptr(workspace, "workspace"), workspace.numel(), _stream(stream))
@@ -269,8 +337,9 @@ def ga_decode_merge(desc: AttnDesc, q, k_new, v_new, k_cache, v_cache, cache_len
     B = q.shape[0]
     if out is None:
         out = torch.empty((B, desc.n_q_heads * desc.head_dim), dtype=et, device=q.device)
-    st = lib.ga_decode_merge(ctypes.byref(desc), _ptr(q, "q", et), _ptr(k_new, "k_new", et), _ptr(v_new, "v_new", et),
-                             _ptr(gate, "gate", et), _ptr(q_norm_w, "q_norm_w", torch.float32),
+    d2, qp, gp = _qg(desc, q, gate, 1, et)
+    st = lib.ga_decode_merge(ctypes.byref(d2), qp, _ptr(k_new, "k_new", et), _ptr(v_new, "v_new", et),
+                             gp, _ptr(q_norm_w, "q_norm_w", torch.float32),
                              _ptr(k_norm_w, "k_norm_w", torch.float32), _ptr(k_cache, "k_cache", et),
                              _ptr(v_cache, "v_cache", et), k_cache.shape[1],
                              _ptr(cache_lens, "cache_lens", torch.int32), int(max_cache_len),

@@ -52,7 +52,25 @@ ga_status check_desc(const ga_attn_desc* d) {
   if (!(d->rms_eps >= 0.f && isfinite(d->rms_eps))) return fail(GA_ERR_BAD_SHAPE, "rms_eps must be finite, >= 0");
   if (!(d->softmax_scale >= 0.f && isfinite(d->softmax_scale)))
     return fail(GA_ERR_BAD_SHAPE, "softmax_scale must be finite, >= 0");
+  if (d->q_head_stride < 0 || (d->q_head_stride > 0 && d->q_head_stride < d->head_dim))
+    return fail(GA_ERR_BAD_SHAPE, "q_head_stride %d must be 0 or >= head_dim %d", d->q_head_stride, d->head_dim);
+  const int gw = d->gate_mode == GA_GATE_ELEMENTWISE ? d->head_dim : 1;
+  if (d->gate_head_stride < 0 || (d->gate_head_stride > 0 && d->gate_head_stride < gw))
+    return fail(GA_ERR_BAD_SHAPE, "gate_head_stride %d must be 0 or >= %d", d->gate_head_stride, gw);
   return GA_OK;
+}
+
+// Head strides of q and the gate in elements (0 in the descriptor = dense).
+long q_stride(const ga_attn_desc* d) { return d->q_head_stride > 0 ? d->q_head_stride : d->head_dim; }
+long gate_stride(const ga_attn_desc* d) {
+  if (d->gate_head_stride > 0) return d->gate_head_stride;
+  return d->gate_mode == GA_GATE_ELEMENTWISE ? d->head_dim : 1;
+}
+
+// The fused bf16 kernels read q rows and elementwise gate rows in 16-byte
+// pieces: their head strides must be multiples of 8 elements.
+bool strides_vec_ok(const ga_attn_desc* d) {
+  return q_stride(d) % 8 == 0 && (d->gate_mode != GA_GATE_ELEMENTWISE || gate_stride(d) % 8 == 0);
 }
 
 float scale_of(const ga_attn_desc* d) {
@@ -76,8 +94,8 @@ bool prefill_v2_ok(const ga_attn_desc* d, int32_t k_cap, int32_t v_cap) {
   // the q prologue keeps every RoPE pair inside one quarter of the row and
   // tables (cos, sin) for the 2 * (64 / grp) tokens of a workgroup
   const int tb = grp <= 64 ? 64 / grp : 0;
-  return d->dtype == GA_BF16 && (hd == 128 || hd == 256) && d->rot_dim % 16 == 0 && d->rot_dim <= hd / 4 &&
-         grp <= 64 && 2 * tb * (d->rot_dim / 2) <= 2048 && row * k_cap < (1LL << 31) && row * v_cap < (1LL << 31);
+  return d->dtype == GA_BF16 && strides_vec_ok(d) && (hd == 128 || hd == 256) && d->rot_dim % 16 == 0 &&
+         d->rot_dim <= hd / 4 && grp <= 64 && 2 * tb * (d->rot_dim / 2) <= 2048 && row * k_cap < (1LL << 31) && row * v_cap < (1LL << 31);
 }
 
 // The wide kernel: 256 query rows per workgroup, one causal block each,
@@ -87,7 +105,7 @@ bool prefill_wide_ok(const ga_attn_desc* d, int32_t n, int32_t k_cap, int32_t v_
   const int grp = d->n_q_heads / d->n_kv_heads;
   const int hd = d->head_dim;
   const long long row = 2LL * d->n_kv_heads * hd;
-  if (!(d->dtype == GA_BF16 && hd == 128 && d->rot_dim % 32 == 0 && grp <= 256 && row * k_cap < (1LL << 31) &&
+  if (!(d->dtype == GA_BF16 && strides_vec_ok(d) && hd == 128 && d->rot_dim % 32 == 0 && grp <= 256 && row * k_cap < (1LL << 31) &&
         row * v_cap < (1LL << 31)))
     return false;
   const long long tb = 256 / grp;
@@ -144,7 +162,8 @@ size_t prefill_attn_ws_bytes(const ga_attn_desc* d, int32_t n, int32_t k_cap, in
 bool prefill_fast(const ga_attn_desc* d) {
   const int grp = d->n_q_heads / d->n_kv_heads;
   const int hd = d->head_dim;
-  return d->dtype == GA_BF16 && (hd == 64 || hd == 128 || hd == 256) && d->rot_dim % 16 == 0 && grp <= 128;
+  return d->dtype == GA_BF16 && strides_vec_ok(d) && (hd == 64 || hd == 128 || hd == 256) && d->rot_dim % 16 == 0 &&
+         grp <= 128;
 }
 
 PrefillKernel prefill_choice(const ga_attn_desc* d, int32_t n, int32_t k_cap, int32_t v_cap) {
@@ -169,7 +188,7 @@ PrefillKernel prefill_choice(const ga_attn_desc* d, int32_t n, int32_t k_cap, in
 bool decode_fast(const ga_attn_desc* d, int32_t cache_cap) {
   const int grp = d->n_q_heads / d->n_kv_heads;
   const int hd = d->head_dim;
-  return d->dtype == GA_BF16 && (hd == 64 || hd == 128 || hd == 256) && d->rot_dim % 16 == 0 &&
+  return d->dtype == GA_BF16 && strides_vec_ok(d) && (hd == 64 || hd == 128 || hd == 256) && d->rot_dim % 16 == 0 &&
          (grp == 1 || grp == 2 || grp == 4 || grp == 8 || grp == 16) &&
          (long long)cache_cap * d->n_kv_heads * hd * 2 < (1LL << 31);
 }
@@ -254,6 +273,8 @@ ga_status prefill_attn_impl(const ga_attn_desc* desc, int32_t n, const void* q, 
     pp.out = (uint16_t*)out;
     pp.k_bstride = (long)k_cap * G * d;
     pp.v_bstride = (long)v_cap * G * d;
+    pp.qs = q_stride(desc);
+    pp.gs = gate_stride(desc);
     pp.B = desc->batch;
     pp.n = n;
     pp.H = H;
@@ -294,6 +315,8 @@ ga_status prefill_attn_impl(const ga_attn_desc* desc, int32_t n, const void* q, 
   np.out = out;
   np.k_bstride = (long)k_cap * G * d;
   np.v_bstride = (long)v_cap * G * d;
+  np.qs = q_stride(desc);
+  np.gs = gate_stride(desc);
   np.B = desc->batch;
   np.n = n;
   np.H = H;
@@ -351,6 +374,8 @@ ga_status chunk_attn_impl(const ga_attn_desc* desc, int32_t n, const void* q, co
     pp.max_base = max_cache_len;
     pp.k_bstride = (long)cap * G * d;
     pp.v_bstride = pp.k_bstride;
+    pp.qs = q_stride(desc);
+    pp.gs = gate_stride(desc);
     pp.B = desc->batch;
     pp.n = n;
     pp.H = H;
@@ -380,6 +405,8 @@ ga_status chunk_attn_impl(const ga_attn_desc* desc, int32_t n, const void* q, co
   np.out = out;
   np.k_bstride = (long)cap * G * d;
   np.v_bstride = np.k_bstride;
+  np.qs = q_stride(desc);
+  np.gs = gate_stride(desc);
   np.B = desc->batch;
   np.n = n;
   np.H = H;
@@ -426,6 +453,8 @@ void fill_decode_params(DecodeParams& dp, const ga_attn_desc* desc, const void* 
   dp.ws = (float*)workspace;
   dp.out = (uint16_t*)out;
   dp.cache_bstride = (long)cache_cap * G * d;
+  dp.qs = q_stride(desc);
+  dp.gs = gate_stride(desc);
   dp.B = desc->batch;
   dp.H = H;
   dp.G = G;
@@ -700,6 +729,8 @@ ga_status ga_decode(const ga_attn_desc* desc, const void* q, const void* k_new, 
   np.out = out;
   np.k_bstride = (long)cache_cap * G * d;
   np.v_bstride = np.k_bstride;
+  np.qs = q_stride(desc);
+  np.gs = gate_stride(desc);
   np.B = desc->batch;
   np.n = 1;
   np.H = desc->n_q_heads;
@@ -742,6 +773,6 @@ int32_t ga_fast_path(int32_t dtype, int32_t head_dim, int32_t rot_dim, int32_t g
   return (prefill_fast(&d) ? 1 : 0) | (decode_fast(&d, 0) ? 2 : 0);
 }
 
-int32_t ga_version(void) { return 1; }
+int32_t ga_version(void) { return 2; }
 
 }  // extern "C"

@@ -56,7 +56,7 @@ __global__ __launch_bounds__(256) void decode_partials_kernel(const DecodeParams
   for (int idx = tid; idx < 16 * LPR; idx += 256) {
     const int r = idx / LPR, c = idx % LPR;
     u32x4_t raw = {0, 0, 0, 0};
-    if (r < GRP) raw = *(const u32x4_t*)(p.q + ((long)b * p.H + g * GRP + r) * D + c * 8);
+    if (r < GRP) raw = *(const u32x4_t*)(p.q + ((long)b * p.H + g * GRP + r) * p.qs + c * 8);
     float x[8];
     unpack8(raw, x);
     norm_rope_chunk<D>(x, c, p.wq ? p.wq + c * 8 : nullptr, p.eps, p.rot, L, p.inv_freq, nullptr);
@@ -244,7 +244,7 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(const DecodeParams p)
   }
   if (tid < 2 * LPR) {  // two rows, LPR lanes each (whole lane groups of one wave)
     const int r = tid / LPR, c = tid % LPR;
-    const u32x4_t raw = (r == 0) ? *(const u32x4_t*)(p.q + ((long)b * p.H + h) * D + c * 8)
+    const u32x4_t raw = (r == 0) ? *(const u32x4_t*)(p.q + ((long)b * p.H + h) * p.qs + c * 8)
                                  : *(const u32x4_t*)(p.k_new + ((long)b * p.G + g) * D + c * 8);
     float x[8];
     unpack8(raw, x);
@@ -333,8 +333,8 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(const DecodeParams p)
     const float o = (ored[0][e] + ored[1][e]) + (ored[2][e] + ored[3][e]);
     const float vnew = bf16_bits_to_f32(p.v_new[((long)b * p.G + g) * D + e]);
     float y = (o + vnew * __builtin_amdgcn_exp2f(snew - M)) / sh_L;
-    if (GATE == 2) y *= sigmoid_f32(bf16_bits_to_f32(p.gate[((long)b * p.H + h) * D + e]));
-    if (GATE == 1) y *= sigmoid_f32(bf16_bits_to_f32(p.gate[(long)b * p.H + h]));
+    if (GATE == 2) y *= sigmoid_f32(bf16_bits_to_f32(p.gate[((long)b * p.H + h) * p.gs + e]));
+    if (GATE == 1) y *= sigmoid_f32(bf16_bits_to_f32(p.gate[((long)b * p.H + h) * p.gs]));
     out[e] = f32_to_bf16_bits(y);
   }
 }

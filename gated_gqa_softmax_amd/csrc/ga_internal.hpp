@@ -44,6 +44,9 @@ struct PrefillParams {
   const int* row_lens;  // [B] or null (= n)
   int max_base;         // key_base values outside [0, max_base] skip the sequence
   long k_bstride, v_bstride;
+  // elements between the rows of consecutive heads of q and of the gate (a
+  // token's rows follow each other: token stride = H * stride)
+  long qs, gs;
   int B, n, H, G, grp, TB, nblk, rot, half, use_table;
   float eps, scale_log2;
   // Split-key mode of the mirrored kernel (split != 0): units of two adjacent
@@ -77,6 +80,7 @@ struct NaiveParams {
   void* v_cache_out;
   void* out;
   long k_bstride, v_bstride;
+  long qs, gs;          // head strides of q and the gate (elements)
   int B, n, H, G, d, rot, gate_mode, decode, max_len;
   float eps, scale;
   double inv_freq[kMaxHalfRot];
@@ -96,6 +100,7 @@ struct DecodeParams {
   float* ws;                // partials
   uint16_t* out;            // [B,H*D]
   long cache_bstride;       // cap*G*D
+  long qs, gs;              // head strides of q and the gate (elements)
   int B, H, G, grp, rot, half, max_len, nsplit;
   float eps, scale_log2;
   double inv_freq[kMaxHalfRot];

@@ -63,9 +63,9 @@ __global__ __launch_bounds__(64) void naive_kernel(NaiveParams p) {
   long qoff, ooff, goff;
   if (p.decode) {
     const int L = p.cache_lens[b];
-    qoff = ((long)b * H + h) * d;
-    ooff = qoff;
-    goff = (p.gate_mode == 2) ? qoff : (long)b * H + h;
+    qoff = ((long)b * H + h) * p.qs;
+    ooff = ((long)b * H + h) * d;
+    goff = ((long)b * H + h) * p.gs;
     if (L < 0 || L > p.max_len) {
       for (int e = lane; e < d; e += 64) Elem<T>::store((T*)p.out, ooff + e, __builtin_nanf(""));
       return;
@@ -79,9 +79,9 @@ __global__ __launch_bounds__(64) void naive_kernel(NaiveParams p) {
     const int nb = p.row_lens ? p.row_lens[b] : p.n;
     if (base < 0 || base > p.max_len || i >= nb) return;  // (whole workgroup)
     const long row = ((long)b * p.n + i) * H + h;
-    qoff = row * d;
+    qoff = row * p.qs;
     ooff = row * d;
-    goff = (p.gate_mode == 2) ? row * d : row;
+    goff = row * p.gs;
     pos = p.positions ? p.positions[(long)b * p.n + i] : base + i;
     nkeys = base + i + 1;
   }

@@ -177,7 +177,7 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(const PrefillParams p
       u32x4_t raw = {0, 0, 0, 0};
       if (valid) {
         const int h = g * p.grp + hh;
-        raw = *(const u32x4_t*)(p.q + (((long)b * n + tok) * p.H + h) * D + c * 8);
+        raw = *(const u32x4_t*)(p.q + (((long)b * n + tok) * p.H + h) * p.qs + c * 8);
       }
       float x[8];
       unpack8(raw, x);
@@ -301,7 +301,7 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(const PrefillParams p
   const long row_off = ((long)b * n + my_tok) * p.H + my_h;  // (b, token, head) index
   uint16_t* orow = p.out + row_off * D;
   float hg = 1.0f;
-  if (GATE == 1) hg = sigmoid_f32(bf16_bits_to_f32(p.gate[row_off]));
+  if (GATE == 1) hg = sigmoid_f32(bf16_bits_to_f32(p.gate[row_off * p.gs]));
 #pragma unroll
   for (int mb = 0; mb < D / 32; ++mb) {
 #pragma unroll
@@ -311,7 +311,7 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(const PrefillParams p
 #pragma unroll
       for (int j = 0; j < 4; ++j) y[j] = o[mb][ig * 4 + j] * inv_l;
       if (GATE == 2) {
-        const u32x2_t z = *(const u32x2_t*)(p.gate + row_off * D + dm);
+        const u32x2_t z = *(const u32x2_t*)(p.gate + row_off * p.gs + dm);
         y[0] *= sigmoid_f32(lo_bf16(z[0]));
         y[1] *= sigmoid_f32(hi_bf16(z[0]));
         y[2] *= sigmoid_f32(lo_bf16(z[1]));

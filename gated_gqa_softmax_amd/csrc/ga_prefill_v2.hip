@@ -296,7 +296,7 @@ __global__ __launch_bounds__(512) void prefill_v2_kernel(const PrefillParams p) 
   // are never stored
   u32x4_t qraw[QC];
   {
-    const uint16_t* src = p.q + (((long)b * n + qtok) * nH + g * grp + (qvalid ? qhh : 0)) * D;
+    const uint16_t* src = p.q + (((long)b * n + qtok) * nH + g * grp + (qvalid ? qhh : 0)) * p.qs;
 #pragma unroll
     for (int i = 0; i < QC; ++i) qraw[i] = *(const u32x4_t*)(src + 8 * qchunk(i));
   }
@@ -453,8 +453,8 @@ __global__ __launch_bounds__(512) void prefill_v2_kernel(const PrefillParams p) 
     const bool valid = erow[it] >= 0;
     graw[it] = u32x4_t{0, 0, 0, 0};
     ghead[it] = 0;
-    if (!SPLIT && valid && GATE == 2) graw[it] = *(const u32x4_t*)(p.gate + (long)erow[it] * D + qc * 8);
-    if (!SPLIT && valid && GATE == 1) ghead[it] = p.gate[erow[it]];
+    if (!SPLIT && valid && GATE == 2) graw[it] = *(const u32x4_t*)(p.gate + (long)erow[it] * p.gs + qc * 8);
+    if (!SPLIT && valid && GATE == 1) ghead[it] = p.gate[(long)erow[it] * p.gs];
   }
 
   lds_barrier();  // stage buffers are free; the gate reads stay in flight
@@ -584,8 +584,8 @@ __global__ __launch_bounds__(512) void prefill_v2_kernel(const PrefillParams p) 
     const f32x4_t y0 = *(const f32x4_t*)(xr + lr * D + (((2 * qc) ^ (lr & 15)) << 2));
     const f32x4_t y1 = *(const f32x4_t*)(xr + lr * D + (((2 * qc + 1) ^ (lr & 15)) << 2));
     float y[8] = {y0[0], y0[1], y0[2], y0[3], y1[0], y1[1], y1[2], y1[3]};
-    if (SPLIT && GATE == 2) graw[it] = *(const u32x4_t*)(p.gate + (long)er * D + qc * 8);
-    if (SPLIT && GATE == 1) ghead[it] = p.gate[er];
+    if (SPLIT && GATE == 2) graw[it] = *(const u32x4_t*)(p.gate + (long)er * p.gs + qc * 8);
+    if (SPLIT && GATE == 1) ghead[it] = p.gate[(long)er * p.gs];
     if (SPLIT && merge) {
       const f32x4_t t0 = tpart[SPLIT ? it : 0][0];
       const f32x4_t t1 = tpart[SPLIT ? it : 0][1];

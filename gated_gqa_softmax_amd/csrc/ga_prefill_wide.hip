@@ -130,7 +130,7 @@ __global__ __launch_bounds__(512) void prefill_wide_kernel(const PrefillParams p
     const int half = p.half;
     const int hq = my_valid ? g * p.grp + my_hh : g * p.grp;  // rows outside the block read a real row
     const int tq = my_valid ? my_tok0 : 0;
-    const uint16_t* qrow = p.q + (((long)b * n + tq) * p.H + hq) * D + hi * 8;
+    const uint16_t* qrow = p.q + (((long)b * n + tq) * p.H + hq) * p.qs + hi * 8;
     u32x4_t raw[NK];
 #pragma unroll
     for (int kk = 0; kk < NK; ++kk) raw[kk] = *(const u32x4_t*)(qrow + kk * 16);
@@ -238,8 +238,8 @@ __global__ __launch_bounds__(512) void prefill_wide_kernel(const PrefillParams p
     const bool valid = (hh < p.grp) && (tok < n);
     erow[it] = valid ? ((long)b * n + tok) * p.H + g * p.grp + hh : -1;
     const long grow = valid ? erow[it] : ((long)b * n) * p.H + g * p.grp;  // unconditional read
-    if (GATE == 2) graw[it] = *(const u32x4_t*)(p.gate + grow * D + qc * 8);
-    if (GATE == 1) ghead[it] = p.gate[grow];
+    if (GATE == 2) graw[it] = *(const u32x4_t*)(p.gate + grow * p.gs + qc * 8);
+    if (GATE == 1) ghead[it] = p.gate[grow * p.gs];
   }
   float l_run = ws.l_run;
   l_run += swap_half(l_run);

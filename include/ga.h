@@ -32,11 +32,14 @@
  *  - The caller owns every buffer. The library writes only ``out``, the
  *    cache slots named below and the workspace. It keeps no state between
  *    calls; calls on different streams with disjoint outputs may overlap.
- *  - Layouts are dense, row-major, innermost index last:
+ *  - Layouts are row-major, innermost index last:
  *      q [B,n,H,d]  k,v [B,n,G,d]  gate [B,n,H,d] | [B,n,H]  out [B,n,H*d]
  *      caches [B,cap,G,d]  norm weights [d] float32  positions [B,n] int32
+ *    All are dense except q and the gate, whose head rows may be spaced
+ *    wider (``q_head_stride``, ``gate_head_stride`` in the descriptor), so
+ *    that the output of a fused q projection is read in place (see there).
  *    Element type of q, k, v, gate, out and caches is ``desc->dtype``.
- *    bf16 tensors must be 16-byte aligned.
+ *    bf16 tensors must be 16-byte aligned (a headwise gate: 2-byte).
  *  - Errors: shapes, pointers, alignment, capacities and workspace size are
  *    checked on the host before anything is launched; a failed check returns
  *    its status and launches nothing. ``ga_last_error()`` gives a message for
@@ -80,6 +83,24 @@ typedef struct {
   float softmax_scale;  /* 0 = 1/sqrt(head_dim); else used as given (> 0) */
   int32_t dtype;        /* ga_dtype: element type of q/k/v/gate/out/caches */
   int32_t gate_mode;    /* ga_gate_mode */
+  /* Head strides (elements) of q and the gate; 0 = dense (d for q and an
+   * elementwise gate, 1 for a headwise gate). Element e of head h of token i
+   * of sequence b is at ((b*n + i)*H + h) * stride + e: the rows of one
+   * token follow each other, so the token stride is H * stride. Nonzero
+   * values must be >= d (q, elementwise gate) or >= 1 (headwise gate).
+   *
+   * Fused q projection ("Transformer by Hand · 6. Gated attention", "Why the
+   * gate is packed into q_proj" and "The code: qwen/attention.py": each
+   * head's 2d outputs are its query followed by its gate): pass q = qg,
+   * gate = qg + d and both strides = 2d. A headwise gate packed as [q | z]
+   * per head has stride d + 1.
+   *
+   * The fused bf16 kernels read q rows and elementwise gate rows in 16-byte
+   * pieces: with a q stride or an elementwise gate stride that is not a
+   * multiple of 8 the call runs on the generic kernel (same results, no
+   * throughput claim), and ga_decode_partials / ga_decode_merge refuse it. */
+  int32_t q_head_stride;
+  int32_t gate_head_stride;
 } ga_attn_desc;
 
 /* ---- prefill ------------------------------------------------------------ */
@@ -270,8 +291,10 @@ const char* ga_last_error(void);
  * the MFMA prefill (bf16, d in {64,128,256}, rot % 16 == 0, group <= 128),
  * bit 1 = the split-K decode (same, group in {1,2,4,8,16}). Shapes without a
  * fused kernel run on the generic one-wave-per-row kernel (any d <= 256,
- * fp32 or bf16); ga_decode_partials/ga_decode_merge need bit 1. */
+ * fp32 or bf16); ga_decode_partials/ga_decode_merge need bit 1. The bits
+ * are for dense q and gate (see ga_attn_desc for wider head strides). */
 int32_t ga_fast_path(int32_t dtype, int32_t head_dim, int32_t rot_dim, int32_t group);
+/* ABI version: 2 (ga_attn_desc with q_head_stride and gate_head_stride). */
 int32_t ga_version(void);
 
 #ifdef __cplusplus

@@ -36,7 +36,8 @@ def test_library_exports_every_declared_entry_point():
     assert declared == set(_lib.SIGNATURES), declared ^ set(_lib.SIGNATURES)
     for name in declared:
         assert getattr(lib, name) is not None
-    assert lib.ga_version() >= 1
+    assert lib.ga_version() == 2
+    assert ctypes.sizeof(AttnDesc) == 48
 
 
 def _desc(**kw):
@@ -96,6 +97,10 @@ def _prefill(lib, d, n=16, q=A16, k=A16, v=A16, gate=A16, out=A16, ws=A16, ws_by
     (dict(dtype=7), _lib.GA_ERR_BAD_DTYPE),
     (dict(gate_mode=5), _lib.GA_ERR_BAD_DTYPE),
     (dict(batch=-1), _lib.GA_ERR_BAD_SHAPE),
+    (dict(q_head_stride=-8), _lib.GA_ERR_BAD_SHAPE),
+    (dict(q_head_stride=255), _lib.GA_ERR_BAD_SHAPE),           # narrower than a head
+    (dict(gate_head_stride=128), _lib.GA_ERR_BAD_SHAPE),        # elementwise gate: >= d
+    (dict(gate_mode=_lib.GA_GATE_HEADWISE, gate_head_stride=-1), _lib.GA_ERR_BAD_SHAPE),
 ])
 def test_prefill_rejects_bad_descriptors(kw, status):
     lib = _lib_or_build()
@@ -119,6 +124,32 @@ def test_prefill_rejects_bad_pointers_and_workspace():
     # empty inputs are a no-op
     assert _prefill(lib, d, n=0, q=None) == _lib.GA_OK
     assert _prefill(lib, _desc(batch=0), q=None) == _lib.GA_OK
+
+
+def test_head_strides_choose_the_kernel():
+    """Fused [q | gate] rows (stride 2d) keep the fused kernels; strides that
+    break their 16-byte row reads send the shape to the generic kernel, and
+    the split decode stages refuse it."""
+    lib = _lib_or_build()
+    packed = _desc(q_head_stride=512, gate_head_stride=512)
+    assert lib.ga_prefill_attention_kernel(ctypes.byref(packed), 4096) == b"mirror"
+    d3 = _desc(batch=4, n_q_heads=16, n_kv_heads=8, head_dim=128, rot_dim=32, q_head_stride=256,
+               gate_head_stride=256)
+    assert lib.ga_prefill_attention_kernel(ctypes.byref(d3), 2048) == b"wide"
+    d64 = _desc(head_dim=64, rot_dim=16, q_head_stride=128, gate_head_stride=128)
+    assert lib.ga_prefill_attention_kernel(ctypes.byref(d64), 64) == b"simple"
+    # headwise gate packed as [q | z]: q rows d + 1 apart are not 16-byte aligned
+    hw = _desc(gate_mode=_lib.GA_GATE_HEADWISE, q_head_stride=257, gate_head_stride=257)
+    assert lib.ga_prefill_attention_kernel(ctypes.byref(hw), 4096) == b"generic"
+    assert lib.ga_prefill_chunk_kernel(ctypes.byref(hw), 64, 4096) == b"generic"
+    hw8 = _desc(gate_mode=_lib.GA_GATE_HEADWISE, q_head_stride=264, gate_head_stride=264)
+    assert lib.ga_prefill_attention_kernel(ctypes.byref(hw8), 4096) == b"mirror"
+    assert lib.ga_prefill_chunk_kernel(ctypes.byref(hw8), 64, 4096) == b"mirror"
+    # an elementwise gate row stride off the 8-element grid
+    odd = _desc(q_head_stride=512, gate_head_stride=260)
+    assert lib.ga_prefill_attention_kernel(ctypes.byref(odd), 4096) == b"generic"
+    assert lib.ga_decode_partials(ctypes.byref(hw), A16, None, A16, A16, 101, A16, 100, A16, 1 << 30,
+                                  None) == _lib.GA_ERR_UNSUPPORTED
 
 
 def test_prefill_attention_workspace(monkeypatch):
@@ -197,3 +228,34 @@ def test_prefill_chunk_rejects_bad_arguments_and_names_its_kernel(monkeypatch):
     assert lib.ga_prefill_chunk_kernel(ctypes.byref(_desc(head_dim=64, rot_dim=16)), 64, 1100) == b"generic"
     monkeypatch.setenv("GA_PREFILL_KERNEL", "generic")
     assert lib.ga_prefill_chunk_kernel(ctypes.byref(d), 64, 1100) == b"generic"
+
+
+def test_binding_reads_head_strides_from_views():
+    """The binding's stride reading (host logic only; CPU tensors)."""
+    import torch
+    from gated_gqa_softmax_amd.api import head_stride
+
+    def hs(t, lead, H, width):
+        return head_stride(t.shape, t.stride(), lead, H, width)
+
+    B, n, H, d = 2, 5, 4, 8
+    qg = torch.zeros(B, n, H, 2 * d)
+    assert hs(qg[..., :d], 2, H, d) == 2 * d and hs(qg[..., d:], 2, H, d) == 2 * d
+    assert hs(torch.zeros(B, n, H, d), 2, H, d) == d                       # dense
+    assert hs(torch.zeros(B, n, H), 2, H, 1) == 1                          # dense headwise
+    qz = torch.zeros(B, n, H, d + 1)                                       # headwise [q | z]
+    assert hs(qz[..., :d], 2, H, d) == d + 1 and hs(qz[..., d], 2, H, 1) == d + 1
+    assert hs(qz[..., d:], 2, H, 1) == d + 1                               # [.., H, 1] view
+    dq = torch.zeros(B, H, 2 * d)                                          # decode: [B, H, 2d]
+    assert hs(dq[..., :d], 1, H, d) == 2 * d
+    assert hs(torch.zeros(1, 1, H, 2 * d)[..., :d], 2, H, d) == 2 * d       # size-1 leading dims
+    assert hs(torch.zeros(1, 1, 1, 2 * d)[..., d:], 2, 1, d) == d           # nothing to read: dense
+    with pytest.raises(ValueError):
+        hs(torch.zeros(B, H, n, d).transpose(1, 2), 2, H, d)              # head-major: not rows of a token
+    with pytest.raises(ValueError):
+        hs(torch.zeros(B, n, H, 2 * d)[..., ::2], 2, H, d)                # innermost dim not dense
+    assert hs(torch.zeros(B, n, 2 * H, d)[:, :, ::2], 2, H, d) == 2 * d   # every other head row
+    with pytest.raises(ValueError):
+        hs(torch.zeros(B, n, H, d), 2, H + 1, d)                          # wrong head count
+    with pytest.raises(ValueError):
+        hs(torch.zeros(B, 2 * n, H, 2 * d)[:, ::2, :, :d], 2, H, d)       # tokens two rows apart
