@@ -45,6 +45,7 @@ Readings where the pages are silent (each is also listed in the design notes):
 from __future__ import annotations
 
 import math
+from dataclasses import dataclass
 from typing import Iterable, Optional, Sequence
 
 import numpy as np
@@ -128,7 +129,8 @@ def sigmoid(z, dtype=np.float64):
     return out
 
 
-def apply_gate(y: np.ndarray, z: Optional[np.ndarray], gate_mode: str, dtype=np.float64) -> np.ndarray:
+def apply_gate(y: np.ndarray, z: Optional[np.ndarray], gate_mode: str, dtype=np.float64,
+               form: Optional[GateForm] = None) -> np.ndarray:
     """Output gate on per-head attention outputs y [..., H, d].
 
     Elementwise: y * sigmoid(z) with z [..., H, d]; headwise: one logit per
@@ -136,17 +138,86 @@ def apply_gate(y: np.ndarray, z: Optional[np.ndarray], gate_mode: str, dtype=np.
     再决定用多少", section "门放在哪里？" (G_h ⊙ O_h, headwise vs elementwise),
     and "Transformer by Hand · 6. Gated attention", "How the gate is computed:
     three steps" (g = sigmoid(z), multiplied dimension by dimension).
+    ``form`` (already expanded z) selects the variants of ``GateForm``: the
+    per-head output norm first, then combine(y, act(z)).
     """
+    form = DEFAULT_GATE if form is None else form
     y = np.asarray(y, dtype=dtype)
+    if form.out_norm_w is not None:
+        y = rms_norm(y, form.out_norm_w, form.out_norm_eps, dtype)
     if gate_mode == GATE_NONE:
         return y
     _check_finite("gate logits", z)
-    g = sigmoid(z, dtype=dtype)
+    g = gate_activation(z, form.act, dtype=dtype)
     if gate_mode == GATE_HEADWISE:
-        return y * g[..., None]
-    if gate_mode == GATE_ELEMENTWISE:
+        g = g[..., None]
+    elif gate_mode != GATE_ELEMENTWISE:
+        raise ValueError(f"unknown gate mode {gate_mode!r}")
+    if form.combine == "mul":
         return y * g
-    raise ValueError(f"unknown gate mode {gate_mode!r}")
+    if form.combine == "add":
+        return y + g
+    raise ValueError(f"unknown gate combine {form.combine!r}")
+
+
+@dataclass(frozen=True)
+class GateForm:
+    """Variants of the output gate, from "Gated Attention for Large Language
+    Models ... 论文阅读":
+
+    * act -- function of the gate logits: "sigmoid" (the default), "ns_sigmoid"
+      0.5 + 0.5 sigmoid(z) (section "第二条机制线索：当前 query 决定的稀疏过滤"),
+      "silu" z sigmoid(z) (SiLU against sigmoid, section "五个门控位置与训练结果
+      总览"), "identity" z (the additive gate with its SiLU removed, section
+      "第一条机制线索：value 与输出投影之间的非线性").
+    * combine -- "mul" Y * act(z) (the default) or "add" Y + act(z) (the
+      additive version, "五个门控位置与训练结果总览").
+    * share_heads -- one gate for every head of a token (the head-shared vector
+      of Table 1, "实验规模与参数预算怎样控制"): the gate has no head dim.
+    * input_independent -- one gate for every token (the input-independent
+      control of "第一条机制线索"): the gate has no batch or token dims.
+    * out_norm_w -- per-head RMSNorm of the attention output before the gate
+      (the per-head SDPA-output RMSNorm control of "第一条机制线索"), weight
+      [d], epsilon out_norm_eps; None = no norm.
+    """
+    act: str = "sigmoid"
+    combine: str = "mul"
+    share_heads: bool = False
+    input_independent: bool = False
+    out_norm_w: Optional[np.ndarray] = None
+    out_norm_eps: float = 1e-6
+
+
+DEFAULT_GATE = GateForm()
+
+
+def gate_activation(z, act: str, dtype=np.float64) -> np.ndarray:
+    """act(z) for the gate forms above."""
+    z = np.asarray(z, dtype=dtype)
+    if act == "sigmoid":
+        return sigmoid(z, dtype)
+    if act == "ns_sigmoid":
+        return 0.5 + 0.5 * sigmoid(z, dtype)
+    if act == "silu":
+        return z * sigmoid(z, dtype)
+    if act == "identity":
+        return z
+    raise ValueError(f"unknown gate activation {act!r}")
+
+
+def expand_gate(z, gate_mode: str, form: GateForm, lead: tuple, n_heads: int):
+    """Gate logits as given for ``form`` -> the per-(token, head) shape
+    [*lead, H, d] (elementwise) or [*lead, H] (headwise) by repeating them
+    over the dims the form leaves out."""
+    if gate_mode == GATE_NONE or z is None:
+        return None
+    z = np.asarray(z)
+    row = z.shape[-1:] if gate_mode == GATE_ELEMENTWISE else ()
+    if form.input_independent:
+        z = z.reshape((1,) * len(lead) + z.shape)
+    if form.share_heads:
+        z = np.expand_dims(z, axis=z.ndim - len(row))
+    return np.broadcast_to(z, tuple(lead) + (n_heads,) + tuple(row))
 
 
 def softmax_rows(s: np.ndarray, dtype=np.float64) -> np.ndarray:
@@ -225,7 +296,8 @@ def prefill_keys(k, k_norm_w, positions, *, rms_eps: float, rope_base: float, ro
 
 def prefill(q, k, v, gate, *, gate_mode: str, q_norm_w, k_norm_w, positions,
             rms_eps: float = 1e-6, rope_base: float = 10000.0, rot_dim: int = 0,
-            scale: Optional[float] = None, dtype=np.float64, block: int = 256) -> np.ndarray:
+            scale: Optional[float] = None, dtype=np.float64, block: int = 256,
+            gate_form: Optional[GateForm] = None) -> np.ndarray:
     """Gated GQA causal attention over whole sequences.
 
     q [B,n,H,d], k/v [B,n,G,d], gate [B,n,H,d] | [B,n,H] | None, norm weights
@@ -256,13 +328,15 @@ def prefill(q, k, v, gate, *, gate_mode: str, q_norm_w, k_norm_w, positions,
                 rows = np.arange(r0, r1)[:, None]
                 s = np.where(np.arange(r1)[None, :] > rows, -np.inf, s)   # causal: j <= i
                 y[b, r0:r1, h] = softmax_rows(s, dtype) @ vv[b, :r1, g]
-    out = apply_gate(y, gate, gate_mode, dtype=dtype)
+    form = DEFAULT_GATE if gate_form is None else gate_form
+    out = apply_gate(y, expand_gate(gate, gate_mode, form, (B, n), H), gate_mode, dtype=dtype, form=form)
     return out.reshape(B, n, H * d)
 
 
 def prefill_rows(q, k, v, gate, rows: Sequence[tuple], *, gate_mode: str, q_norm_w, k_norm_w,
                  positions, rms_eps: float = 1e-6, rope_base: float = 10000.0, rot_dim: int = 0,
-                 scale: Optional[float] = None, dtype=np.float64) -> np.ndarray:
+                 scale: Optional[float] = None, dtype=np.float64,
+                 gate_form: Optional[GateForm] = None) -> np.ndarray:
     """The same computation for selected (b, i, h) rows only; returns [len(rows), d].
 
     Used at sizes where the whole output is too expensive on the CPU.
@@ -271,6 +345,8 @@ def prefill_rows(q, k, v, gate, rows: Sequence[tuple], *, gate_mode: str, q_norm
     B, n, H, d = q.shape
     G = np.asarray(k).shape[2]
     sc = _default_scale(d, scale)
+    form = DEFAULT_GATE if gate_form is None else gate_form
+    gate = expand_gate(gate, gate_mode, form, (B, n), H)
     out = np.empty((len(rows), d), dtype=dtype)
     khat_cache = {}
     for r, (b, i, h) in enumerate(rows):
@@ -290,13 +366,14 @@ def prefill_rows(q, k, v, gate, rows: Sequence[tuple], *, gate_mode: str, q_norm
             zz = np.asarray(gate)[b, i, h:h + 1]             # [1 head]
         else:
             zz = None
-        out[r] = apply_gate(y[None, :], zz, gate_mode, dtype)[0]
+        out[r] = apply_gate(y[None, :], zz, gate_mode, dtype, form)[0]
     return out
 
 
 def prefill_chunk(q, k, v, gate, *, gate_mode: str, q_norm_w, k_norm_w, k_cache_rows, cache_lens,
                   chunk_lens=None, positions=None, max_cache_len: Optional[int] = None, rms_eps: float = 1e-6,
-                  rope_base: float = 10000.0, rot_dim: int = 0, scale: Optional[float] = None, dtype=np.float64):
+                  rope_base: float = 10000.0, rot_dim: int = 0, scale: Optional[float] = None, dtype=np.float64,
+                  gate_form: Optional[GateForm] = None):
     """A chunk of new tokens per sequence after the tokens already in a KV cache.
 
     q [B,n,H,d], k/v [B,n,G,d] (raw), gate as for ``prefill``.
@@ -321,6 +398,8 @@ def prefill_chunk(q, k, v, gate, *, gate_mode: str, q_norm_w, k_norm_w, k_cache_
     G = np.asarray(k).shape[2]
     sc = _default_scale(d, scale)
     lens = np.asarray(cache_lens)
+    form = DEFAULT_GATE if gate_form is None else gate_form
+    gate = expand_gate(gate, gate_mode, form, (B, n), H)
     out = np.full((B, n, H, d), np.nan, dtype=dtype)
     khat = np.full((B, n, G, d), np.nan, dtype=dtype)
     for b in range(B):
@@ -343,13 +422,14 @@ def prefill_chunk(q, k, v, gate, *, gate_mode: str, q_norm_w, k_norm_w, k_cache_
             s = np.where(hidden, -np.inf, s)
             out[b, :nb, h] = softmax_rows(s, dtype) @ vals[:, g]
         z = None if gate_mode == GATE_NONE else np.asarray(gate)[b, :nb]   # [nb,H,d] or [nb,H]
-        out[b, :nb] = apply_gate(out[b, :nb], z, gate_mode, dtype)
+        out[b, :nb] = apply_gate(out[b, :nb], z, gate_mode, dtype, form)
     return out.reshape(B, n, H * d), khat
 
 
 def decode(q, k_new, v_new, gate, *, gate_mode: str, q_norm_w, k_norm_w, k_cache_rows: Iterable,
            cache_lens, rms_eps: float = 1e-6, rope_base: float = 10000.0, rot_dim: int = 0,
-           scale: Optional[float] = None, dtype=np.float64, seqs: Optional[Sequence[int]] = None):
+           scale: Optional[float] = None, dtype=np.float64, seqs: Optional[Sequence[int]] = None,
+           gate_form: Optional[GateForm] = None):
     """One decode step per sequence.
 
     q [B,H,d], k_new/v_new [B,G,d] (raw, before norm), gate [B,H,d] | [B,H].
@@ -368,6 +448,8 @@ def decode(q, k_new, v_new, gate, *, gate_mode: str, q_norm_w, k_norm_w, k_cache
     sc = _default_scale(d, scale)
     lens = np.asarray(cache_lens)
     seqs = list(range(B)) if seqs is None else list(seqs)
+    form = DEFAULT_GATE if gate_form is None else gate_form
+    gate = expand_gate(gate, gate_mode, form, (B,), H)
     out = np.empty((len(seqs), H * d), dtype=dtype)
     khn = np.empty((len(seqs), G, d), dtype=dtype)
     for r, b in enumerate(seqs):
@@ -388,5 +470,5 @@ def decode(q, k_new, v_new, gate, *, gate_mode: str, q_norm_w, k_norm_w, k_cache
             s = (keys @ qh[h]) * dtype(sc)
             y[h] = softmax_rows(s[None], dtype)[0] @ vals
         z = None if gate is None else np.asarray(gate)[b]
-        out[r] = apply_gate(y, z, gate_mode, dtype).reshape(H * d)
+        out[r] = apply_gate(y, z, gate_mode, dtype, form).reshape(H * d)
     return out, khn
