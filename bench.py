@@ -37,6 +37,7 @@ def parse():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-chunk", action="store_true", help="skip the chunked-prefill measurement")
     ap.add_argument("--no-packed", action="store_true", help="skip the fused [q | gate] input measurement")
+    ap.add_argument("--no-variant", action="store_true", help="skip the gate-variant epilogue measurement")
     ap.add_argument("--no-prefill", action="store_true", help="decode only (for counter runs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--decode-steps", type=int, default=20)
@@ -55,10 +56,12 @@ CSRC = os.path.join(ROOT, "gated_gqa_softmax_amd", "csrc")
 PREFILL_KERNEL_SYMBOL = {"wide": "prefill_wide_kernel", "mirror": "prefill_v2_kernel", "split": "prefill_v2_kernel",
                          "simple": "prefill_mfma_kernel", "generic": "naive_kernel"}
 KERNEL_SOURCES = {
-    "prefill_v2_kernel": ["ga_prefill_v2.hip", "ga_prefill_tile.hpp", "ga_common.hpp", "ga_internal.hpp"],
-    "prefill_wide_kernel": ["ga_prefill_wide.hip", "ga_prefill_tile.hpp", "ga_common.hpp", "ga_internal.hpp"],
-    "decode_partials_kernel": ["ga_decode.hip", "ga_common.hpp", "ga_internal.hpp"],
-    "prefill_mfma_kernel": ["ga_prefill_mfma.hip", "ga_common.hpp", "ga_internal.hpp"],
+    "prefill_v2_kernel": ["ga_prefill_v2.hip", "ga_prefill_tile.hpp", "ga_gate.hpp", "ga_common.hpp",
+                          "ga_internal.hpp"],
+    "prefill_wide_kernel": ["ga_prefill_wide.hip", "ga_prefill_tile.hpp", "ga_gate.hpp", "ga_common.hpp",
+                            "ga_internal.hpp"],
+    "decode_partials_kernel": ["ga_decode.hip", "ga_gate.hpp", "ga_common.hpp", "ga_internal.hpp"],
+    "prefill_mfma_kernel": ["ga_prefill_mfma.hip", "ga_gate.hpp", "ga_common.hpp", "ga_internal.hpp"],
     "naive_kernel": ["ga_naive.hip", "ga_common.hpp", "ga_internal.hpp"],
 }
 
@@ -152,6 +155,25 @@ def ramp(torch, fn, seconds=0.25):
         for _ in range(10):
             fn()
         torch.cuda.synchronize()
+
+
+def time_whole_and_kernel(torch, whole, attention, stream, steps, warmup):
+    """Mean ms of ``whole`` (one step) and of ``attention`` (the attention
+    kernel's launch), each as ``steps`` calls back to back between two events."""
+    for _ in range(warmup):
+        whole()
+    ramp(torch, whole)
+    res = {}
+    for name, fn in (("step_ms", whole), ("kernel_ms", attention)):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(steps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        res[name] = e0.elapsed_time(e1) / steps
+    return res
 
 
 def time_prefill(torch, api, inputs, accounting, wname, steps, warmup):
@@ -363,19 +385,7 @@ def time_chunk(torch, api, inputs, accounting, steps, warmup):
     def attention():
         api.ga_prefill_chunk_attention(d, q, kc, vc, dl, max_len, gate=gate, q_norm_w=wq, out=out, stream=stream)
 
-    for _ in range(warmup):
-        whole()
-    ramp(torch, whole)
-    res = {}
-    for name, fn in (("step_ms", whole), ("kernel_ms", attention)):
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        e0.record(stream)
-        for _ in range(steps):
-            fn()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        res[name] = e0.elapsed_time(e1) / steps
+    res = time_whole_and_kernel(torch, whole, attention, stream, steps, warmup)
     flops = accounting.chunk_prefill_flops(lens, w.n_q_heads, w.head_dim, w.seq_len)
     achieved = flops / (res["kernel_ms"] * 1e-3) / 1e12
     kernel = PREFILL_KERNEL_SYMBOL[api.ga_prefill_chunk_kernel(d, w.seq_len, cap)]
@@ -422,19 +432,7 @@ def time_packed(torch, api, inputs, accounting, wname, steps, warmup):
     def attention():
         api.ga_prefill_attention(d, q, khat, v, gate, wq, pos, out=out, workspace=ws_attn, stream=stream)
 
-    for _ in range(warmup):
-        whole()
-    ramp(torch, whole)
-    res = {}
-    for name, fn in (("step_ms", whole), ("kernel_ms", attention)):
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        e0.record(stream)
-        for _ in range(steps):
-            fn()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        res[name] = e0.elapsed_time(e1) / steps
+    res = time_whole_and_kernel(torch, whole, attention, stream, steps, warmup)
     flops = accounting.causal_prefill_flops(w.batch, w.n_q_heads, hd, w.seq_len)
     achieved = flops / (res["kernel_ms"] * 1e-3) / 1e12
     kernel = PREFILL_KERNEL_SYMBOL[api.ga_prefill_attention_kernel(d, w.seq_len)]
@@ -450,6 +448,49 @@ def time_packed(torch, api, inputs, accounting, wname, steps, warmup):
         "roofline": {"bound": "mfma", "kernel": kernel, "achieved": achieved, "peak": MI355X_BF16_DENSE_TFLOPS,
                      "unit": "TFLOP/s", "frac": achieved / MI355X_BF16_DENSE_TFLOPS, "kernel_ms": res["kernel_ms"],
                      "algorithmic_flops": flops},
+    }
+
+
+def time_gate_variant(torch, api, inputs, accounting, wname, steps, warmup):
+    """The headline prefill with the extended epilogue: SiLU gate,
+    multiplicative, after a per-head RMSNorm of the attention output."""
+    w = inputs.WORKLOADS[wname]
+    x = inputs.make_prefill(w)
+    et = torch.bfloat16
+    dv = lambda a, dt=None: torch.from_numpy(np.ascontiguousarray(a)).to("cuda", dtype=dt)
+    q, k, v, gate = dv(x["q"], et), dv(x["k"], et), dv(x["v"], et), dv(x["gate"], et)
+    wq, wk, pos = dv(x["q_norm_w"]), dv(x["k_norm_w"]), dv(x["positions"])
+    onw = torch.ones(w.head_dim, dtype=torch.float32, device="cuda")
+    d = api.make_desc(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.rot_dim, w.rope_base, w.rms_eps, 0.0, et,
+                      w.gate_mode, gate_act="silu", gate_combine="mul", out_norm_w=onw, out_norm_eps=1e-6)
+    khat = torch.empty_like(k)
+    api.ga_prefill_keys(d, k, None, wk, pos, k_hat=khat)
+    out = torch.empty((w.batch, w.seq_len, w.n_q_heads * w.head_dim), dtype=et, device="cuda")
+    ws = torch.empty(api.ga_prefill_workspace_bytes(d, w.seq_len), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def whole():
+        api.ga_prefill(d, q, k, v, gate, wq, wk, pos, out=out, workspace=ws, stream=stream)
+
+    def attention():
+        api.ga_prefill_attention(d, q, khat, v, gate, wq, pos, out=out, stream=stream)
+
+    res = time_whole_and_kernel(torch, whole, attention, stream, steps, warmup)
+    flops = accounting.causal_prefill_flops(w.batch, w.n_q_heads, w.head_dim, w.seq_len)
+    achieved = flops / (res["kernel_ms"] * 1e-3) / 1e12
+    kernel = PREFILL_KERNEL_SYMBOL[api.ga_prefill_attention_kernel(d, w.seq_len)]
+    return {
+        "metric": METRIC,
+        "value": flops / (res["step_ms"] * 1e-3) / 1e12,
+        "unit": "TFLOP/s",
+        "ms_per_step": res["step_ms"],
+        "steps": steps,
+        "config": {"workload": w.name, "gate": "elementwise SiLU, multiplicative, after a per-head output RMSNorm",
+                   "batch": w.batch, "seq_len": w.seq_len, "n_q_heads": w.n_q_heads, "n_kv_heads": w.n_kv_heads,
+                   "head_dim": w.head_dim, "rot_dim": w.rot_dim},
+        "roofline": {"bound": "mfma", "kernel": kernel + " (extended epilogue)", "achieved": achieved,
+                     "peak": MI355X_BF16_DENSE_TFLOPS, "unit": "TFLOP/s", "frac": achieved / MI355X_BF16_DENSE_TFLOPS,
+                     "kernel_ms": res["kernel_ms"], "algorithmic_flops": flops},
     }
 
 
@@ -506,6 +547,9 @@ def main():
         rec["chunk"] = time_chunk(torch, api, inputs, accounting, args.steps, args.warmup)
     if not args.no_packed and w.gate_mode == "elementwise" and w.dtype == "bf16":
         rec["packed"] = time_packed(torch, api, inputs, accounting, args.workload, args.steps, args.warmup)
+    if not args.no_variant and w.gate_mode == "elementwise" and w.dtype == "bf16":
+        rec["gate_variant"] = time_gate_variant(torch, api, inputs, accounting, args.workload, args.steps,
+                                                args.warmup)
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(w, pre["x"], pre["flops"])
     print(json.dumps(rec), flush=True)

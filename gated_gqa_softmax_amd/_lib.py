@@ -26,6 +26,9 @@ GA_F32 = 1
 GA_GATE_NONE = 0
 GA_GATE_HEADWISE = 1
 GA_GATE_ELEMENTWISE = 2
+GA_ACT_SIGMOID, GA_ACT_NS_SIGMOID, GA_ACT_SILU, GA_ACT_IDENTITY = 0, 1, 2, 3
+GA_COMBINE_MUL, GA_COMBINE_ADD = 0, 1
+GA_SHARE_HEADS, GA_SHARE_TOKENS = 1, 2
 
 
 class AttnDesc(ctypes.Structure):
@@ -42,6 +45,11 @@ class AttnDesc(ctypes.Structure):
         ("gate_mode", ctypes.c_int32),
         ("q_head_stride", ctypes.c_int32),
         ("gate_head_stride", ctypes.c_int32),
+        ("gate_act", ctypes.c_int32),
+        ("gate_combine", ctypes.c_int32),
+        ("gate_share", ctypes.c_int32),
+        ("out_norm_eps", ctypes.c_float),
+        ("out_norm_w", ctypes.c_void_p),
     ]
 
 

@@ -23,6 +23,9 @@ from ._lib import AttnDesc
 _GATE = {"none": _lib.GA_GATE_NONE, "headwise": _lib.GA_GATE_HEADWISE,
          "elementwise": _lib.GA_GATE_ELEMENTWISE}
 _DTYPE = {torch.bfloat16: _lib.GA_BF16, torch.float32: _lib.GA_F32}
+_ACT = {"sigmoid": _lib.GA_ACT_SIGMOID, "ns_sigmoid": _lib.GA_ACT_NS_SIGMOID, "silu": _lib.GA_ACT_SILU,
+        "identity": _lib.GA_ACT_IDENTITY}
+_COMBINE = {"mul": _lib.GA_COMBINE_MUL, "add": _lib.GA_COMBINE_ADD}
 
 
 class GaError(RuntimeError):
@@ -36,14 +39,30 @@ class GaError(RuntimeError):
 
 def make_desc(batch, n_q_heads, n_kv_heads, head_dim, rot_dim=0, rope_base=10000.0, rms_eps=1e-6,
               softmax_scale=0.0, dtype=torch.bfloat16, gate_mode="none", q_head_stride=0,
-              gate_head_stride=0) -> AttnDesc:
-    """Descriptor; the head strides matter only to the kernel-name queries
-    (the entry points below take them from the q and gate tensors)."""
-    return AttnDesc(int(batch), int(n_q_heads), int(n_kv_heads), int(head_dim), int(rot_dim),
-                    float(rope_base), float(rms_eps), float(softmax_scale),
-                    _DTYPE[dtype] if isinstance(dtype, torch.dtype) else int(dtype),
-                    _GATE[gate_mode] if isinstance(gate_mode, str) else int(gate_mode),
-                    int(q_head_stride), int(gate_head_stride))
+              gate_head_stride=0, gate_act="sigmoid", gate_combine="mul", share_heads=False,
+              share_tokens=False, out_norm_w: Optional[torch.Tensor] = None, out_norm_eps=1e-6) -> AttnDesc:
+    """Descriptor. The head strides matter only to the kernel-name queries
+    (the entry points below take them from the q and gate tensors). Gate
+    variants: ``gate_act`` sigmoid | ns_sigmoid | silu | identity,
+    ``gate_combine`` mul | add, ``share_heads`` (gate [.., d] or [..] per
+    token), ``share_tokens`` (gate [H, d] or [H]); ``out_norm_w`` a float32
+    GPU tensor [d] for the per-head output RMSNorm (the descriptor keeps a
+    reference to it)."""
+    if out_norm_w is not None:
+        if not (out_norm_w.is_cuda and out_norm_w.dtype == torch.float32 and out_norm_w.is_contiguous()
+                and out_norm_w.numel() == int(head_dim)):
+            raise ValueError("out_norm_w must be a contiguous float32 GPU tensor of head_dim values")
+    share = (_lib.GA_SHARE_HEADS if share_heads else 0) | (_lib.GA_SHARE_TOKENS if share_tokens else 0)
+    d = AttnDesc(int(batch), int(n_q_heads), int(n_kv_heads), int(head_dim), int(rot_dim),
+                 float(rope_base), float(rms_eps), float(softmax_scale),
+                 _DTYPE[dtype] if isinstance(dtype, torch.dtype) else int(dtype),
+                 _GATE[gate_mode] if isinstance(gate_mode, str) else int(gate_mode),
+                 int(q_head_stride), int(gate_head_stride),
+                 _ACT[gate_act] if isinstance(gate_act, str) else int(gate_act),
+                 _COMBINE[gate_combine] if isinstance(gate_combine, str) else int(gate_combine),
+                 share, float(out_norm_eps), out_norm_w.data_ptr() if out_norm_w is not None else None)
+    d._keep = out_norm_w
+    return d
 
 
 def _ptr(t: Optional[torch.Tensor], name: str, dtype=None) -> Optional[int]:
@@ -109,9 +128,34 @@ def _qg(desc: AttnDesc, q, gate, lead: int, et):
     gp = None
     if gate is not None:
         gw = desc.head_dim if desc.gate_mode == _lib.GA_GATE_ELEMENTWISE else 1
-        d2.gate_head_stride = _head_rows(gate, "gate", et, lead, desc.n_q_heads, gw)
+        if desc.gate_share:
+            d2.gate_head_stride = _shared_gate(gate, desc, lead, et, gw)
+        else:
+            d2.gate_head_stride = _head_rows(gate, "gate", et, lead, desc.n_q_heads, gw)
         gp = gate.data_ptr()
     return d2, q.data_ptr(), gp
+
+
+def _shared_gate(gate: torch.Tensor, desc: AttnDesc, lead: int, et, width: int) -> int:
+    """A gate without its head dim and/or its batch and token dims: a dense
+    tensor of [*lead] (unless shared by the tokens) + [H] (unless shared by
+    the heads) + [d] (elementwise) values."""
+    if not gate.is_cuda or gate.dtype != et:
+        raise ValueError(f"gate must be a {et} GPU tensor")
+    if not gate.is_contiguous():
+        raise ValueError("a shared gate must be contiguous")
+    tail = (desc.head_dim,) if width > 1 else ()
+    heads = () if desc.gate_share & _lib.GA_SHARE_HEADS else (desc.n_q_heads,)
+    want = heads + tail
+    shape = tuple(gate.shape)
+    if desc.gate_share & _lib.GA_SHARE_TOKENS:
+        ok = shape == want or (not want and shape in ((1,),))
+    else:
+        ok = len(shape) == lead + len(want) and shape[lead:] == want
+    if not ok:
+        raise ValueError(f"gate has shape {shape}; the shared gate needs [{'' if desc.gate_share & 2 else 'lead dims, '}"
+                         f"{', '.join(map(str, want))}]")
+    return 0
 
 
 def _stream(stream) -> int:

@@ -57,6 +57,17 @@ ga_status check_desc(const ga_attn_desc* d) {
   const int gw = d->gate_mode == GA_GATE_ELEMENTWISE ? d->head_dim : 1;
   if (d->gate_head_stride < 0 || (d->gate_head_stride > 0 && d->gate_head_stride < gw))
     return fail(GA_ERR_BAD_SHAPE, "gate_head_stride %d must be 0 or >= %d", d->gate_head_stride, gw);
+  if (d->gate_act < GA_ACT_SIGMOID || d->gate_act > GA_ACT_IDENTITY)
+    return fail(GA_ERR_BAD_DTYPE, "gate_act %d out of range", d->gate_act);
+  if (d->gate_combine < GA_COMBINE_MUL || d->gate_combine > GA_COMBINE_ADD)
+    return fail(GA_ERR_BAD_DTYPE, "gate_combine %d out of range", d->gate_combine);
+  if (d->gate_share < 0 || d->gate_share > (GA_SHARE_HEADS | GA_SHARE_TOKENS))
+    return fail(GA_ERR_BAD_DTYPE, "gate_share %d out of range", d->gate_share);
+  if (d->out_norm_w) {
+    if (!(d->out_norm_eps >= 0.f && isfinite(d->out_norm_eps)))
+      return fail(GA_ERR_BAD_SHAPE, "out_norm_eps must be finite, >= 0");
+    if (!aligned(d->out_norm_w, 16)) return fail(GA_ERR_MISALIGNED, "out_norm_w is not 16-byte aligned");
+  }
   return GA_OK;
 }
 
@@ -65,6 +76,31 @@ long q_stride(const ga_attn_desc* d) { return d->q_head_stride > 0 ? d->q_head_s
 long gate_stride(const ga_attn_desc* d) {
   if (d->gate_head_stride > 0) return d->gate_head_stride;
   return d->gate_mode == GA_GATE_ELEMENTWISE ? d->head_dim : 1;
+}
+
+// A gate variant or the output norm: the kernels' extended epilogue.
+bool gate_ext(const ga_attn_desc* d) {
+  return d->gate_act != GA_ACT_SIGMOID || d->gate_combine != GA_COMBINE_MUL || d->gate_share != 0 ||
+         d->out_norm_w != nullptr;
+}
+
+// Gate argument of the kernel launchers: the gate mode, or kGateExt.
+int gate_arg(const ga_attn_desc* d) { return gate_ext(d) ? kGateExt : d->gate_mode; }
+
+// Offsets of the gate rows (token row t = b*n + i, head h): t * gts + h * ghs.
+GateEpi gate_epi(const ga_attn_desc* d) {
+  GateEpi ge;
+  memset(&ge, 0, sizeof(ge));
+  const long s = gate_stride(d);
+  const bool heads = d->gate_share & GA_SHARE_HEADS, tokens = d->gate_share & GA_SHARE_TOKENS;
+  ge.ghs = heads ? 0 : s;
+  ge.gts = tokens ? 0 : (heads ? s : (long)d->n_q_heads * s);
+  ge.onorm_w = d->out_norm_w;
+  ge.onorm_eps = d->out_norm_eps;
+  ge.mode = d->gate_mode;
+  ge.act = d->gate_act;
+  ge.add = d->gate_combine;
+  return ge;
 }
 
 // The fused bf16 kernels read q rows and elementwise gate rows in 16-byte
@@ -171,7 +207,7 @@ PrefillKernel prefill_choice(const ga_attn_desc* d, int32_t n, int32_t k_cap, in
   // (the mirrored kernel numbers output rows (b, token, head) in 32 bits)
   const bool v2 = prefill_v2_ok(d, k_cap, v_cap) && (long long)d->batch * n * d->n_q_heads < (1LL << 31);
   if (req == PK_WIDE && prefill_wide_ok(d, n, k_cap, v_cap, false)) return PK_WIDE;
-  if (req == PK_SPLIT && v2) return PK_SPLIT;
+  if (req == PK_SPLIT && v2 && !gate_ext(d)) return PK_SPLIT;
   if (req == PK_MIRROR && v2) return PK_MIRROR;
   if (req == PK_SIMPLE && prefill_fast(d)) return PK_SIMPLE;
   if (req == PK_GENERIC) return PK_GENERIC;
@@ -275,6 +311,7 @@ ga_status prefill_attn_impl(const ga_attn_desc* desc, int32_t n, const void* q, 
     pp.v_bstride = (long)v_cap * G * d;
     pp.qs = q_stride(desc);
     pp.gs = gate_stride(desc);
+    pp.ge = gate_epi(desc);
     pp.B = desc->batch;
     pp.n = n;
     pp.H = H;
@@ -300,9 +337,9 @@ ga_status prefill_attn_impl(const ga_attn_desc* desc, int32_t n, const void* q, 
       pp.split = 1;
       pp.split_ovh = split_overhead_stages();
     }
-    if (wide) return hip_status(launch_prefill_wide(pp, d, desc->gate_mode, stream), "prefill attention launch");
-    if (v2) return hip_status(launch_prefill_v2(pp, d, desc->gate_mode, stream), "prefill attention launch");
-    return hip_status(launch_prefill_mfma(pp, d, desc->gate_mode, stream), "prefill attention launch");
+    if (wide) return hip_status(launch_prefill_wide(pp, d, gate_arg(desc), stream), "prefill attention launch");
+    if (v2) return hip_status(launch_prefill_v2(pp, d, gate_arg(desc), stream), "prefill attention launch");
+    return hip_status(launch_prefill_mfma(pp, d, gate_arg(desc), stream), "prefill attention launch");
   }
   NaiveParams np;
   memset(&np, 0, sizeof(np));
@@ -317,6 +354,7 @@ ga_status prefill_attn_impl(const ga_attn_desc* desc, int32_t n, const void* q, 
   np.v_bstride = (long)v_cap * G * d;
   np.qs = q_stride(desc);
   np.gs = gate_stride(desc);
+  np.ge = gate_epi(desc);
   np.B = desc->batch;
   np.n = n;
   np.H = H;
@@ -376,6 +414,7 @@ ga_status chunk_attn_impl(const ga_attn_desc* desc, int32_t n, const void* q, co
     pp.v_bstride = pp.k_bstride;
     pp.qs = q_stride(desc);
     pp.gs = gate_stride(desc);
+    pp.ge = gate_epi(desc);
     pp.B = desc->batch;
     pp.n = n;
     pp.H = H;
@@ -390,7 +429,7 @@ ga_status chunk_attn_impl(const ga_attn_desc* desc, int32_t n, const void* q, co
     pp.scale_log2 = scale_of(desc) * 1.4426950408889634f;
     fill_inv_freq(desc, pp.inv_freq);
     if ((long long)pp.B * G * pp.nblk > 0x7fffffffLL) return fail(GA_ERR_UNSUPPORTED, "grid too large");
-    return hip_status(launch_prefill_v2(pp, d, desc->gate_mode, stream), "chunk attention launch");
+    return hip_status(launch_prefill_v2(pp, d, gate_arg(desc), stream), "chunk attention launch");
   }
   NaiveParams np;
   memset(&np, 0, sizeof(np));
@@ -407,6 +446,7 @@ ga_status chunk_attn_impl(const ga_attn_desc* desc, int32_t n, const void* q, co
   np.v_bstride = np.k_bstride;
   np.qs = q_stride(desc);
   np.gs = gate_stride(desc);
+  np.ge = gate_epi(desc);
   np.B = desc->batch;
   np.n = n;
   np.H = H;
@@ -455,6 +495,7 @@ void fill_decode_params(DecodeParams& dp, const ga_attn_desc* desc, const void* 
   dp.cache_bstride = (long)cache_cap * G * d;
   dp.qs = q_stride(desc);
   dp.gs = gate_stride(desc);
+  dp.ge = gate_epi(desc);
   dp.B = desc->batch;
   dp.H = H;
   dp.G = G;
@@ -688,7 +729,7 @@ ga_status ga_decode_merge(const ga_attn_desc* desc, const void* q, const void* k
   DecodeParams dp;
   fill_decode_params(dp, desc, q, k_new, v_new, desc->gate_mode == GA_GATE_NONE ? nullptr : gate, q_norm_w,
                      k_norm_w, k_cache, v_cache, cache_cap, cache_lens, max_cache_len, workspace, out);
-  return hip_status(launch_decode_merge(dp, desc->head_dim, desc->gate_mode, (hipStream_t)stream),
+  return hip_status(launch_decode_merge(dp, desc->head_dim, gate_arg(desc), (hipStream_t)stream),
                     "decode merge launch");
 }
 
@@ -731,6 +772,7 @@ ga_status ga_decode(const ga_attn_desc* desc, const void* q, const void* k_new, 
   np.v_bstride = np.k_bstride;
   np.qs = q_stride(desc);
   np.gs = gate_stride(desc);
+  np.ge = gate_epi(desc);
   np.B = desc->batch;
   np.n = 1;
   np.H = desc->n_q_heads;
@@ -773,6 +815,6 @@ int32_t ga_fast_path(int32_t dtype, int32_t head_dim, int32_t rot_dim, int32_t g
   return (prefill_fast(&d) ? 1 : 0) | (decode_fast(&d, 0) ? 2 : 0);
 }
 
-int32_t ga_version(void) { return 2; }
+int32_t ga_version(void) { return 3; }
 
 }  // extern "C"

@@ -22,6 +22,7 @@
 //    gate and stores bf16 output; appends the new K-hat and V to slot L.
 //    Chunks never read slot L, so the append cannot race with them.
 #include "ga_common.hpp"
+#include "ga_gate.hpp"
 #include "ga_internal.hpp"
 
 namespace ga {
@@ -328,7 +329,7 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(const DecodeParams p)
     for (int c = 0; c < 4; ++c) o4[c] += __shfl_xor(o4[c], m, 64);
   if (sub == 0) *(f32x4_t*)&ored[w][e4 * 4] = o4;
   __syncthreads();
-  if (tid < D) {
+  if (GATE != kGateExt && tid < D) {
     const int e = tid;
     const float o = (ored[0][e] + ored[1][e]) + (ored[2][e] + ored[3][e]);
     const float vnew = bf16_bits_to_f32(p.v_new[((long)b * p.G + g) * D + e]);
@@ -336,6 +337,28 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(const DecodeParams p)
     if (GATE == 2) y *= sigmoid_f32(bf16_bits_to_f32(p.gate[((long)b * p.H + h) * p.gs + e]));
     if (GATE == 1) y *= sigmoid_f32(bf16_bits_to_f32(p.gate[((long)b * p.H + h) * p.gs]));
     out[e] = f32_to_bf16_bits(y);
+  }
+  if (GATE == kGateExt) {
+    const int e = tid;
+    float y = 0.f;
+    if (e < D) {
+      const float o = (ored[0][e] + ored[1][e]) + (ored[2][e] + ored[3][e]);
+      const float vnew = bf16_bits_to_f32(p.v_new[((long)b * p.G + g) * D + e]);
+      y = (o + vnew * __builtin_amdgcn_exp2f(snew - M)) / sh_L;
+    }
+    if (p.ge.onorm_w) {  // per-head RMSNorm of the row over the D threads
+      const float ss = sum_xor<64>(y * y);
+      if (lane == 0) red[w] = ss;  // red[] was last read before the barrier above
+      __syncthreads();
+      const float tot = (red[0] + red[1]) + (red[2] + red[3]);
+      if (e < D) y = y * (1.0f / sqrtf(tot * (1.0f / D) + p.ge.onorm_eps)) * p.ge.onorm_w[e];
+    }
+    if (e < D) {
+      const long go = (long)b * p.ge.gts + (long)h * p.ge.ghs;
+      if (p.ge.mode == 2) y = gate_combine_f32(y, gate_act_f32(bf16_bits_to_f32(p.gate[go + e]), p.ge.act), p.ge.add);
+      if (p.ge.mode == 1) y = gate_combine_f32(y, gate_act_f32(bf16_bits_to_f32(p.gate[go]), p.ge.act), p.ge.add);
+      out[e] = f32_to_bf16_bits(y);
+    }
   }
 }
 
@@ -371,7 +394,8 @@ static hipError_t launch_merge_d(const DecodeParams& p, int gate_mode, hipStream
   switch (gate_mode) {
     case 0: hipLaunchKernelGGL((decode_merge_kernel<D, 0>), grid, dim3(256), 0, s, p); break;
     case 1: hipLaunchKernelGGL((decode_merge_kernel<D, 1>), grid, dim3(256), 0, s, p); break;
-    default: hipLaunchKernelGGL((decode_merge_kernel<D, 2>), grid, dim3(256), 0, s, p); break;
+    case 2: hipLaunchKernelGGL((decode_merge_kernel<D, 2>), grid, dim3(256), 0, s, p); break;
+    default: hipLaunchKernelGGL((decode_merge_kernel<D, kGateExt>), grid, dim3(256), 0, s, p); break;
   }
   return hipGetLastError();
 }

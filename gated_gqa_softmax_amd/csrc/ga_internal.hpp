@@ -9,6 +9,19 @@ namespace ga {
 
 constexpr int kMaxHalfRot = 128;  // rot_dim <= 256
 
+// Gate variants and the per-head output norm. The fused kernels read these
+// only in their extended-epilogue instantiation (gate template argument
+// kGateExt); their default instantiations apply y * sigmoid(z) as before.
+struct GateEpi {
+  long gts, ghs;          // logits of (token row t = b*n + i, head h) start at t * gts + h * ghs
+  const float* onorm_w;   // [d]: per-head RMSNorm of the attention output (before the gate), or null
+  float onorm_eps;
+  int mode;               // 0 none, 1 headwise, 2 elementwise
+  int act;                // 0 sigmoid(z), 1 0.5 + 0.5 sigmoid(z), 2 z sigmoid(z), 3 z
+  int add;                // 0: y * act(z); 1: y + act(z)
+};
+constexpr int kGateExt = 3;
+
 // K-hat = RoPE(RMSNorm(k)) for [B,n,G,d] rows; optional copy of v.
 struct PrepParams {
   const void* src;     // k rows, [B, *, G, d] with batch stride src_bstride
@@ -47,6 +60,7 @@ struct PrefillParams {
   // elements between the rows of consecutive heads of q and of the gate (a
   // token's rows follow each other: token stride = H * stride)
   long qs, gs;
+  GateEpi ge;
   int B, n, H, G, grp, TB, nblk, rot, half, use_table;
   float eps, scale_log2;
   // Split-key mode of the mirrored kernel (split != 0): units of two adjacent
@@ -81,6 +95,7 @@ struct NaiveParams {
   void* out;
   long k_bstride, v_bstride;
   long qs, gs;          // head strides of q and the gate (elements)
+  GateEpi ge;           // gate form and offsets (this kernel always reads them)
   int B, n, H, G, d, rot, gate_mode, decode, max_len;
   float eps, scale;
   double inv_freq[kMaxHalfRot];
@@ -101,6 +116,7 @@ struct DecodeParams {
   uint16_t* out;            // [B,H*D]
   long cache_bstride;       // cap*G*D
   long qs, gs;              // head strides of q and the gate (elements)
+  GateEpi ge;
   int B, H, G, grp, rot, half, max_len, nsplit;
   float eps, scale_log2;
   double inv_freq[kMaxHalfRot];

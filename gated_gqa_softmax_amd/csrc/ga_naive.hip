@@ -65,7 +65,7 @@ __global__ __launch_bounds__(64) void naive_kernel(NaiveParams p) {
     const int L = p.cache_lens[b];
     qoff = ((long)b * H + h) * p.qs;
     ooff = ((long)b * H + h) * d;
-    goff = ((long)b * H + h) * p.gs;
+    goff = (long)b * p.ge.gts + (long)h * p.ge.ghs;
     if (L < 0 || L > p.max_len) {
       for (int e = lane; e < d; e += 64) Elem<T>::store((T*)p.out, ooff + e, __builtin_nanf(""));
       return;
@@ -81,7 +81,7 @@ __global__ __launch_bounds__(64) void naive_kernel(NaiveParams p) {
     const long row = ((long)b * p.n + i) * H + h;
     qoff = row * p.qs;
     ooff = row * d;
-    goff = row * p.gs;
+    goff = ((long)b * p.n + i) * p.ge.gts + (long)h * p.ge.ghs;
     pos = p.positions ? p.positions[(long)b * p.n + i] : base + i;
     nkeys = base + i + 1;
   }
@@ -153,15 +153,35 @@ __global__ __launch_bounds__(64) void naive_kernel(NaiveParams p) {
     for (int m = 0; m < 4; ++m) o[m] = o[m] * alpha + pj * vv[m];
     m_run = m_new;
   }
-  const float hgate = (p.gate_mode == 1) ? 1.0f / (1.0f + expf(-Elem<T>::load((const T*)p.gate, goff))) : 1.0f;
+  // gate variants: act(z) = sigmoid, 0.5 + 0.5 sigmoid, z sigmoid(z) or z;
+  // y * act(z) or y + act(z); per-head output RMSNorm first
+  const GateEpi& ge = p.ge;
+  auto act = [&](float z) {
+    const float sg = 1.0f / (1.0f + expf(-z));
+    return ge.act == 0 ? sg : ge.act == 1 ? 0.5f + 0.5f * sg : ge.act == 2 ? z * sg : z;
+  };
+  const float hgate = (p.gate_mode == 1) ? act(Elem<T>::load((const T*)p.gate, goff)) : 1.0f;
+  float y[4];
+#pragma unroll
+  for (int m = 0; m < 4; ++m) y[m] = (lane + 64 * m < d) ? o[m] / l_run : 0.f;
+  if (ge.onorm_w) {
+    float ss = 0.f;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) ss += y[m] * y[m];
+    ss = sum_xor<64>(ss);
+    const float r = 1.0f / sqrtf(ss / d + ge.onorm_eps);
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+      if (lane + 64 * m < d) y[m] = y[m] * r * ge.onorm_w[lane + 64 * m];
+  }
 #pragma unroll
   for (int m = 0; m < 4; ++m) {
     const int e = lane + 64 * m;
     if (e < d) {
-      float y = o[m] / l_run;
-      if (p.gate_mode == 2) y *= 1.0f / (1.0f + expf(-Elem<T>::load((const T*)p.gate, goff + e)));
-      else if (p.gate_mode == 1) y *= hgate;
-      Elem<T>::store((T*)p.out, ooff + e, y);
+      float v = y[m];
+      const float gv = p.gate_mode == 2 ? act(Elem<T>::load((const T*)p.gate, goff + e)) : hgate;
+      if (p.gate_mode != 0) v = ge.add ? v + gv : v * gv;
+      Elem<T>::store((T*)p.out, ooff + e, v);
     }
   }
 }

@@ -25,6 +25,7 @@
 //  * blocks are dispatched heaviest (last token block) first, and
 //    consecutive workgroups alternate KV heads so each XCD's L2 sees few heads.
 #include "ga_common.hpp"
+#include "ga_gate.hpp"
 #include "ga_internal.hpp"
 
 namespace ga {
@@ -302,6 +303,23 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(const PrefillParams p
   uint16_t* orow = p.out + row_off * D;
   float hg = 1.0f;
   if (GATE == 1) hg = sigmoid_f32(bf16_bits_to_f32(p.gate[row_off * p.gs]));
+  // extended epilogue: the lane pair (l32, 0), (l32, 1) holds the whole row
+  float onorm_r = 1.0f;
+  long goff = 0;
+  if (GATE == kGateExt) {
+    if (p.ge.onorm_w) {
+      float ss = 0.f;
+#pragma unroll
+      for (int mb = 0; mb < D / 32; ++mb)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) ss += (o[mb][j] * inv_l) * (o[mb][j] * inv_l);
+      auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(ss), __float_as_uint(ss), false, false);
+      ss = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+      onorm_r = 1.0f / sqrtf(ss * (1.0f / D) + p.ge.onorm_eps);
+    }
+    goff = ext_gate_offset(p.ge, row_off, p.H);
+    if (p.ge.mode == 1) hg = gate_act_f32(bf16_bits_to_f32(p.gate[goff]), p.ge.act);
+  }
 #pragma unroll
   for (int mb = 0; mb < D / 32; ++mb) {
 #pragma unroll
@@ -310,7 +328,21 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(const PrefillParams p
       float y[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) y[j] = o[mb][ig * 4 + j] * inv_l;
-      if (GATE == 2) {
+      if (GATE == kGateExt) {
+        if (p.ge.onorm_w) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) y[j] = y[j] * onorm_r * p.ge.onorm_w[dm + j];
+        }
+        if (p.ge.mode == 2) {
+          const u32x2_t z = *(const u32x2_t*)(p.gate + goff + dm);
+          const float zz[4] = {lo_bf16(z[0]), hi_bf16(z[0]), lo_bf16(z[1]), hi_bf16(z[1])};
+#pragma unroll
+          for (int j = 0; j < 4; ++j) y[j] = gate_combine_f32(y[j], gate_act_f32(zz[j], p.ge.act), p.ge.add);
+        } else if (p.ge.mode == 1) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) y[j] = gate_combine_f32(y[j], hg, p.ge.add);
+        }
+      } else if (GATE == 2) {
         const u32x2_t z = *(const u32x2_t*)(p.gate + row_off * p.gs + dm);
         y[0] *= sigmoid_f32(lo_bf16(z[0]));
         y[1] *= sigmoid_f32(hi_bf16(z[0]));
@@ -333,7 +365,8 @@ static hipError_t launch_d(const PrefillParams& p, int gate_mode, hipStream_t s)
   switch (gate_mode) {
     case 0: hipLaunchKernelGGL((prefill_mfma_kernel<D, KN, 0>), dim3(grid), dim3(256), 0, s, p); break;
     case 1: hipLaunchKernelGGL((prefill_mfma_kernel<D, KN, 1>), dim3(grid), dim3(256), 0, s, p); break;
-    default: hipLaunchKernelGGL((prefill_mfma_kernel<D, KN, 2>), dim3(grid), dim3(256), 0, s, p); break;
+    case 2: hipLaunchKernelGGL((prefill_mfma_kernel<D, KN, 2>), dim3(grid), dim3(256), 0, s, p); break;
+    default: hipLaunchKernelGGL((prefill_mfma_kernel<D, KN, kGateExt>), dim3(grid), dim3(256), 0, s, p); break;
   }
   return hipGetLastError();
 }

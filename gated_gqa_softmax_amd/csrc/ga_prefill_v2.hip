@@ -33,6 +33,7 @@
 //    a tile's max exceeds the reference by more than 2^8, so probabilities
 //    stay below 256 (exact in fp32, fine as bf16 operands) and most tiles
 //    skip the rescale.
+#include "ga_gate.hpp"
 #include "ga_prefill_tile.hpp"
 
 namespace ga {
@@ -455,6 +456,11 @@ __global__ __launch_bounds__(512) void prefill_v2_kernel(const PrefillParams p) 
     ghead[it] = 0;
     if (!SPLIT && valid && GATE == 2) graw[it] = *(const u32x4_t*)(p.gate + (long)erow[it] * p.gs + qc * 8);
     if (!SPLIT && valid && GATE == 1) ghead[it] = p.gate[(long)erow[it] * p.gs];
+    if (!SPLIT && valid && GATE == kGateExt && p.ge.mode != 0) {
+      const long go = ext_gate_offset(p.ge, erow[it], nH);
+      if (p.ge.mode == 2) graw[it] = *(const u32x4_t*)(p.gate + go + qc * 8);
+      else ghead[it] = p.gate[go];
+    }
   }
 
   lds_barrier();  // stage buffers are free; the gate reads stay in flight
@@ -608,7 +614,9 @@ __global__ __launch_bounds__(512) void prefill_v2_kernel(const PrefillParams p) 
         y[jj] = __builtin_fmaf(yh, wh, yt * wt) * inv;
       }
     }
-    if (GATE == 2) {
+    if (GATE == kGateExt) {
+      ext_epilogue8<D>(y, p.ge, qc, graw[it], ghead[it]);
+    } else if (GATE == 2) {
       float z[8];
       unpack8(graw[it], z);
 #pragma unroll
@@ -632,7 +640,12 @@ static void launch_v2_gate(const PrefillParams& p, int gate_mode, long grid, hip
   switch (gate_mode) {
     case 0: hipLaunchKernelGGL((prefill_v2_kernel<D, 0, SPLIT, CHUNK>), dim3((unsigned)grid), dim3(512), 0, s, p); break;
     case 1: hipLaunchKernelGGL((prefill_v2_kernel<D, 1, SPLIT, CHUNK>), dim3((unsigned)grid), dim3(512), 0, s, p); break;
-    default: hipLaunchKernelGGL((prefill_v2_kernel<D, 2, SPLIT, CHUNK>), dim3((unsigned)grid), dim3(512), 0, s, p); break;
+    case 2: hipLaunchKernelGGL((prefill_v2_kernel<D, 2, SPLIT, CHUNK>), dim3((unsigned)grid), dim3(512), 0, s, p); break;
+    default:
+      // extended epilogue: mirrored mode only (the host never pairs it with split keys)
+      if constexpr (!SPLIT)
+        hipLaunchKernelGGL((prefill_v2_kernel<D, kGateExt, SPLIT, CHUNK>), dim3((unsigned)grid), dim3(512), 0, s, p);
+      break;
   }
 }
 

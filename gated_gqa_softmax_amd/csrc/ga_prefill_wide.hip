@@ -22,6 +22,7 @@
 //    sit in the same lane.
 //  * The gated output leaves through LDS in row-major order: 16-byte gate
 //    reads and output writes.
+#include "ga_gate.hpp"
 #include "ga_prefill_tile.hpp"
 
 namespace ga {
@@ -240,6 +241,13 @@ __global__ __launch_bounds__(512) void prefill_wide_kernel(const PrefillParams p
     const long grow = valid ? erow[it] : ((long)b * n) * p.H + g * p.grp;  // unconditional read
     if (GATE == 2) graw[it] = *(const u32x4_t*)(p.gate + grow * p.gs + qc * 8);
     if (GATE == 1) ghead[it] = p.gate[grow * p.gs];
+    if (GATE == kGateExt) {
+      graw[it] = u32x4_t{0, 0, 0, 0};
+      ghead[it] = 0;
+      const long go = ext_gate_offset(p.ge, grow, p.H);
+      if (p.ge.mode == 2) graw[it] = *(const u32x4_t*)(p.gate + go + qc * 8);
+      else if (p.ge.mode == 1) ghead[it] = p.gate[go];
+    }
   }
   float l_run = ws.l_run;
   l_run += swap_half(l_run);
@@ -268,7 +276,9 @@ __global__ __launch_bounds__(512) void prefill_wide_kernel(const PrefillParams p
     const f32x4_t y0 = *(const f32x4_t*)(xr + lr * D + (((2 * qc) ^ (lr & 15)) << 2));
     const f32x4_t y1 = *(const f32x4_t*)(xr + lr * D + (((2 * qc + 1) ^ (lr & 15)) << 2));
     float y[8] = {y0[0], y0[1], y0[2], y0[3], y1[0], y1[1], y1[2], y1[3]};
-    if (GATE == 2) {
+    if (GATE == kGateExt) {
+      ext_epilogue8<D>(y, p.ge, qc, graw[it], ghead[it]);
+    } else if (GATE == 2) {
       float z[8];
       unpack8(graw[it], z);
 #pragma unroll
@@ -289,7 +299,8 @@ static hipError_t launch_wide_d(const PrefillParams& p, int gate_mode, hipStream
   switch (gate_mode) {
     case 0: hipLaunchKernelGGL((prefill_wide_kernel<D, 0>), dim3((unsigned)grid), dim3(512), 0, s, p); break;
     case 1: hipLaunchKernelGGL((prefill_wide_kernel<D, 1>), dim3((unsigned)grid), dim3(512), 0, s, p); break;
-    default: hipLaunchKernelGGL((prefill_wide_kernel<D, 2>), dim3((unsigned)grid), dim3(512), 0, s, p); break;
+    case 2: hipLaunchKernelGGL((prefill_wide_kernel<D, 2>), dim3((unsigned)grid), dim3(512), 0, s, p); break;
+    default: hipLaunchKernelGGL((prefill_wide_kernel<D, kGateExt>), dim3((unsigned)grid), dim3(512), 0, s, p); break;
   }
   return hipGetLastError();
 }

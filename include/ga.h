@@ -72,6 +72,20 @@ typedef enum {
 typedef enum { GA_BF16 = 0, GA_F32 = 1 } ga_dtype;
 typedef enum { GA_GATE_NONE = 0, GA_GATE_HEADWISE = 1, GA_GATE_ELEMENTWISE = 2 } ga_gate_mode;
 
+/* Gate variants ("Gated Attention for Large Language Models ... 论文阅读"):
+ * the function of the logits z -- sigmoid (the method's gate), NS-sigmoid
+ * 0.5 + 0.5 sigmoid(z) ("第二条机制线索：当前 query 决定的稀疏过滤"), SiLU
+ * z sigmoid(z) ("五个门控位置与训练结果总览"), identity z (the additive gate
+ * without its SiLU, "第一条机制线索：value 与输出投影之间的非线性") -- ... */
+typedef enum { GA_ACT_SIGMOID = 0, GA_ACT_NS_SIGMOID = 1, GA_ACT_SILU = 2, GA_ACT_IDENTITY = 3 } ga_gate_act;
+/* ... how it meets the attention output y: y * act(z) or y + act(z) (the
+ * additive version, "五个门控位置与训练结果总览") ... */
+typedef enum { GA_COMBINE_MUL = 0, GA_COMBINE_ADD = 1 } ga_gate_combine;
+/* ... and which dims the logits have: one gate per token shared by every
+ * head (Table 1's head-shared gate, "实验规模与参数预算怎样控制") and/or one
+ * gate for every token (the input-independent gate, "第一条机制线索"). */
+typedef enum { GA_SHARE_HEADS = 1, GA_SHARE_TOKENS = 2 } ga_gate_share;
+
 typedef struct {
   int32_t batch;        /* B >= 0 */
   int32_t n_q_heads;    /* H >= 1, a multiple of n_kv_heads */
@@ -101,6 +115,20 @@ typedef struct {
    * throughput claim), and ga_decode_partials / ga_decode_merge refuse it. */
   int32_t q_head_stride;
   int32_t gate_head_stride;
+  /* Gate variants (all 0 = the method's gate: y * sigmoid(z), one gate row
+   * per token and head). gate_share changes the gate's dims: with
+   * GA_SHARE_HEADS a prefill gate is [B,n,d] | [B,n] (decode [B,d] | [B]),
+   * with GA_SHARE_TOKENS it is [H,d] | [H], with both [d] | [1]; its rows
+   * are gate_head_stride apart (0 = dense). */
+  int32_t gate_act;      /* ga_gate_act */
+  int32_t gate_combine;  /* ga_gate_combine */
+  int32_t gate_share;    /* ga_gate_share bits */
+  /* Per-head RMSNorm of the attention output before the gate (the per-head
+   * SDPA-output RMSNorm of "第一条机制线索"): y_h / sqrt(mean(y_h^2) + eps) * w.
+   * out_norm_w: DEVICE pointer to [d] float32, 16-byte aligned, or NULL for
+   * no norm; it must stay valid until the calls that use it have run. */
+  float out_norm_eps;    /* >= 0 */
+  const float* out_norm_w;
 } ga_attn_desc;
 
 /* ---- prefill ------------------------------------------------------------ */
@@ -294,7 +322,8 @@ const char* ga_last_error(void);
  * fp32 or bf16); ga_decode_partials/ga_decode_merge need bit 1. The bits
  * are for dense q and gate (see ga_attn_desc for wider head strides). */
 int32_t ga_fast_path(int32_t dtype, int32_t head_dim, int32_t rot_dim, int32_t group);
-/* ABI version: 2 (ga_attn_desc with q_head_stride and gate_head_stride). */
+/* ABI version: 3 (ga_attn_desc with head strides, gate variants and the
+ * output norm). */
 int32_t ga_version(void);
 
 #ifdef __cplusplus

@@ -36,8 +36,8 @@ def test_library_exports_every_declared_entry_point():
     assert declared == set(_lib.SIGNATURES), declared ^ set(_lib.SIGNATURES)
     for name in declared:
         assert getattr(lib, name) is not None
-    assert lib.ga_version() == 2
-    assert ctypes.sizeof(AttnDesc) == 48
+    assert lib.ga_version() == 3
+    assert ctypes.sizeof(AttnDesc) == 72
 
 
 def _desc(**kw):
@@ -101,6 +101,13 @@ def _prefill(lib, d, n=16, q=A16, k=A16, v=A16, gate=A16, out=A16, ws=A16, ws_by
     (dict(q_head_stride=255), _lib.GA_ERR_BAD_SHAPE),           # narrower than a head
     (dict(gate_head_stride=128), _lib.GA_ERR_BAD_SHAPE),        # elementwise gate: >= d
     (dict(gate_mode=_lib.GA_GATE_HEADWISE, gate_head_stride=-1), _lib.GA_ERR_BAD_SHAPE),
+    (dict(gate_act=4), _lib.GA_ERR_BAD_DTYPE),
+    (dict(gate_act=-1), _lib.GA_ERR_BAD_DTYPE),
+    (dict(gate_combine=2), _lib.GA_ERR_BAD_DTYPE),
+    (dict(gate_share=4), _lib.GA_ERR_BAD_DTYPE),
+    (dict(out_norm_w=A16 + 4), _lib.GA_ERR_MISALIGNED),
+    (dict(out_norm_w=A16, out_norm_eps=-1.0), _lib.GA_ERR_BAD_SHAPE),
+    (dict(out_norm_w=A16, out_norm_eps=float("inf")), _lib.GA_ERR_BAD_SHAPE),
 ])
 def test_prefill_rejects_bad_descriptors(kw, status):
     lib = _lib_or_build()
@@ -150,6 +157,19 @@ def test_head_strides_choose_the_kernel():
     assert lib.ga_prefill_attention_kernel(ctypes.byref(odd), 4096) == b"generic"
     assert lib.ga_decode_partials(ctypes.byref(hw), A16, None, A16, A16, 101, A16, 100, A16, 1 << 30,
                                   None) == _lib.GA_ERR_UNSUPPORTED
+
+
+def test_gate_variants_never_take_the_split_mode(monkeypatch):
+    """The split-key mode has no extended epilogue: a gate variant or the
+    output norm keeps the mirrored kernel even when split is requested."""
+    lib = _lib_or_build()
+    monkeypatch.setenv("GA_PREFILL_KERNEL", "split")
+    assert lib.ga_prefill_attention_kernel(ctypes.byref(_desc()), 4096) == b"split"
+    for kw in (dict(gate_act=_lib.GA_ACT_SILU), dict(gate_combine=_lib.GA_COMBINE_ADD),
+               dict(gate_share=_lib.GA_SHARE_HEADS), dict(out_norm_w=A16)):
+        d = _desc(**kw)
+        assert lib.ga_prefill_attention_kernel(ctypes.byref(d), 4096) == b"mirror", kw
+        assert lib.ga_prefill_attention_workspace_bytes(ctypes.byref(d), 4096) == 0
 
 
 def test_prefill_attention_workspace(monkeypatch):
