@@ -341,6 +341,36 @@ def ga_prefill_chunk_attention(desc: AttnDesc, q, k_cache, v_cache, cache_lens, 
     return out
 
 
+def ga_prefill_backward_workspace_bytes(desc: AttnDesc, seq_len: int) -> int:
+    return int(_lib.load().ga_prefill_backward_workspace_bytes(ctypes.byref(desc), seq_len))
+
+
+def ga_prefill_backward(desc: AttnDesc, q, k, v, dout, gate=None, q_norm_w=None, k_norm_w=None, positions=None,
+                        workspace=None, stream=None, weight_grads=True) -> dict:
+    """Gradients of sum(dout * ga_prefill(...)): dict with dq, dk, dv, dgate
+    (None without a gate) and dq_norm_w, dk_norm_w (None without that norm
+    weight, or with weight_grads=False)."""
+    lib = _lib.load()
+    et = _elem_dtype(desc)
+    B, n = q.shape[0], q.shape[1]
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    dgate = torch.empty_like(gate) if gate is not None else None
+    dwq = torch.empty_like(q_norm_w) if (q_norm_w is not None and weight_grads) else None
+    dwk = torch.empty_like(k_norm_w) if (k_norm_w is not None and weight_grads) else None
+    nbytes = ga_prefill_backward_workspace_bytes(desc, n)
+    if workspace is None or workspace.numel() < nbytes:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    st = lib.ga_prefill_backward(ctypes.byref(desc), n, _ptr(q, "q", et), _ptr(k, "k", et), _ptr(v, "v", et),
+                                 _ptr(gate, "gate", et), _ptr(q_norm_w, "q_norm_w", torch.float32),
+                                 _ptr(k_norm_w, "k_norm_w", torch.float32), _ptr(positions, "positions", torch.int32),
+                                 _ptr(dout, "dout", et), _ptr(dq, "dq", et), _ptr(dk, "dk", et), _ptr(dv, "dv", et),
+                                 _ptr(dgate, "dgate", et), _ptr(dwq, "dq_norm_w", torch.float32),
+                                 _ptr(dwk, "dk_norm_w", torch.float32), _ptr(workspace, "workspace"),
+                                 workspace.numel(), _stream(stream))
+    _check(st, "ga_prefill_backward")
+    return dict(dq=dq, dk=dk, dv=dv, dgate=dgate, dq_norm_w=dwq, dk_norm_w=dwk)
+
+
 def ga_decode(desc: AttnDesc, q, k_new, v_new, k_cache, v_cache, cache_lens, max_cache_len: int, gate=None,
               q_norm_w=None, k_norm_w=None, out=None, workspace=None, stream=None) -> torch.Tensor:
     """out [B,H*d] for one new token per sequence; appends K-hat/V at slot cache_lens[b]."""

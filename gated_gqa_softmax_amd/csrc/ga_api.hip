@@ -509,9 +509,200 @@ void fill_decode_params(DecodeParams& dp, const ga_attn_desc* desc, const void* 
   fill_inv_freq(desc, dp.inv_freq);
 }
 
+// Backward workspace: the parts in order, each 256-byte aligned.
+struct BwdLayout {
+  size_t qh, kh, y, dy, qhT, khT, dyT, lse, dsum, dqh, dkh, wq, wk, total;
+  int npad, nwg;
+};
+
+constexpr int kBwdNormWorkgroups = 512;
+
+BwdLayout bwd_layout(const ga_attn_desc* d, int32_t n) {
+  BwdLayout L;
+  const size_t B = (size_t)d->batch, H = (size_t)d->n_q_heads, G = (size_t)d->n_kv_heads, D = (size_t)d->head_dim;
+  L.npad = (int)((n + 63) / 64 * 64);
+  L.nwg = kBwdNormWorkgroups;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off += round_up(bytes, 256);
+    return at;
+  };
+  L.qh = take(B * n * H * D * 2);
+  L.kh = take(B * n * G * D * 2);
+  L.y = take(B * n * H * D * 2);
+  L.dy = take(B * n * H * D * 2);
+  L.qhT = take(B * H * D * L.npad * 2);
+  L.khT = take(B * G * D * L.npad * 2);
+  L.dyT = take(B * H * D * L.npad * 2);
+  L.lse = take(B * n * H * 4);
+  L.dsum = take(B * n * H * 4);
+  L.dqh = take(B * n * H * D * 4);
+  L.dkh = take(B * n * G * D * 4);
+  L.wq = take((size_t)L.nwg * D * 4);
+  L.wk = take((size_t)L.nwg * D * 4);
+  L.total = off;
+  return L;
+}
+
+// Shapes the backward serves: bf16, d in {64, 128, 256}, group <= 128, the
+// method's gate (no variants), dense q and gate.
+ga_status check_bwd_desc(const ga_attn_desc* d) {
+  const int grp = d->n_q_heads / d->n_kv_heads;
+  if (d->dtype != GA_BF16) return fail(GA_ERR_UNSUPPORTED, "the backward pass runs in bf16 only");
+  if (!(d->head_dim == 64 || d->head_dim == 128 || d->head_dim == 256))
+    return fail(GA_ERR_UNSUPPORTED, "backward: head_dim %d not in {64, 128, 256}", d->head_dim);
+  if (grp > 128) return fail(GA_ERR_UNSUPPORTED, "backward: group %d > 128", grp);
+  if (gate_ext(d)) return fail(GA_ERR_UNSUPPORTED, "backward: gate variants and the output norm are forward-only");
+  if (q_stride(d) != d->head_dim || (d->gate_mode == GA_GATE_ELEMENTWISE && gate_stride(d) != d->head_dim) ||
+      (d->gate_mode == GA_GATE_HEADWISE && gate_stride(d) != 1))
+    return fail(GA_ERR_UNSUPPORTED, "backward: q and the gate must be dense");
+  return GA_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+size_t ga_prefill_backward_workspace_bytes(const ga_attn_desc* desc, int32_t seq_len) {
+  if (check_desc(desc) != GA_OK || seq_len < 0) return 0;
+  return bwd_layout(desc, seq_len).total;
+}
+
+ga_status ga_prefill_backward(const ga_attn_desc* desc, int32_t seq_len, const void* q, const void* k, const void* v,
+                              const void* gate, const float* q_norm_w, const float* k_norm_w,
+                              const int32_t* positions, const void* dout, void* dq, void* dk, void* dv, void* dgate,
+                              float* dq_norm_w, float* dk_norm_w, void* workspace, size_t workspace_bytes,
+                              void* stream) {
+  ga_status st;
+  if ((st = check_desc(desc)) != GA_OK) return st;
+  if (seq_len < 0) return fail(GA_ERR_BAD_SHAPE, "seq_len %d < 0", seq_len);
+  if ((st = check_bwd_desc(desc)) != GA_OK) return st;
+  if (desc->batch == 0 || seq_len == 0) return ok();
+  const char* names[] = {"q", "k", "v", "dout", "dq", "dk", "dv"};
+  const void* ptrs[] = {q, k, v, dout, dq, dk, dv};
+  for (int i = 0; i < 7; ++i)
+    if ((st = check_tensor(ptrs[i], names[i], desc)) != GA_OK) return st;
+  if ((st = check_gate(gate, desc)) != GA_OK) return st;
+  if (desc->gate_mode != GA_GATE_NONE && (st = check_gate(dgate, desc)) != GA_OK) return st;
+  const BwdLayout L = bwd_layout(desc, seq_len);
+  if (!workspace || workspace_bytes < L.total)
+    return fail(GA_ERR_WORKSPACE, "workspace %zu bytes < %zu required", workspace ? workspace_bytes : 0, L.total);
+  if (!aligned(workspace, 256)) return fail(GA_ERR_MISALIGNED, "workspace is not 256-byte aligned");
+  const long long rows = (long long)desc->batch * seq_len * desc->n_q_heads;
+  if (rows >= (1LL << 31)) return fail(GA_ERR_UNSUPPORTED, "backward: B*n*H must stay below 2^31");
+  hipStream_t s = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  const int B = desc->batch, n = seq_len, H = desc->n_q_heads, G = desc->n_kv_heads, D = desc->head_dim;
+  uint16_t* qh = (uint16_t*)(ws + L.qh);
+  uint16_t* kh = (uint16_t*)(ws + L.kh);
+  uint16_t* y = (uint16_t*)(ws + L.y);
+  uint16_t* dyb = (uint16_t*)(ws + L.dy);
+  uint16_t* qhT = (uint16_t*)(ws + L.qhT);
+  uint16_t* khT = (uint16_t*)(ws + L.khT);
+  uint16_t* dyT = (uint16_t*)(ws + L.dyT);
+  float* lse = (float*)(ws + L.lse);
+  float* dsum = (float*)(ws + L.dsum);
+  float* dqh = (float*)(ws + L.dqh);
+  float* dkh = (float*)(ws + L.dkh);
+
+  // q-hat and k-hat (bf16, as the forward's MFMA operands)
+  if ((st = prefill_keys_impl(desc, n, k, nullptr, k_norm_w, positions, kh, nullptr, n, s)) != GA_OK) return st;
+  {
+    ga_attn_desc dq_desc = *desc;
+    dq_desc.n_kv_heads = H;  // the key-preparation kernel over the H query rows of each token
+    if ((st = prefill_keys_impl(&dq_desc, n, q, nullptr, q_norm_w, positions, qh, nullptr, n, s)) != GA_OK)
+      return st;
+  }
+  // the forward's ungated output y and the log-sum-exp of each row, from
+  // q-hat and k-hat (no norm and no RoPE left to apply)
+  {
+    PrefillParams pp;
+    memset(&pp, 0, sizeof(pp));
+    pp.q = qh;
+    pp.khat = kh;
+    pp.v = (const uint16_t*)v;
+    pp.out = y;
+    pp.lse = lse;
+    pp.k_bstride = (long)n * G * D;
+    pp.v_bstride = pp.k_bstride;
+    pp.qs = D;
+    pp.gs = D;
+    pp.B = B;
+    pp.n = n;
+    pp.H = H;
+    pp.G = G;
+    pp.grp = H / G;
+    pp.TB = 128 / pp.grp;
+    pp.nblk = (n + pp.TB - 1) / pp.TB;
+    pp.use_table = 1;
+    pp.scale_log2 = scale_of(desc) * 1.4426950408889634f;
+    if ((long long)pp.B * G * pp.nblk > 0x7fffffffLL) return fail(GA_ERR_UNSUPPORTED, "grid too large");
+    if ((st = hip_status(launch_prefill_mfma(pp, D, GA_GATE_NONE, s), "backward forward-stats launch")) != GA_OK)
+      return st;
+  }
+  BwdParams bp;
+  memset(&bp, 0, sizeof(bp));
+  bp.qh = qh;
+  bp.kh = kh;
+  bp.v = (const uint16_t*)v;
+  bp.y = y;
+  bp.dy = dyb;
+  bp.qhT = qhT;
+  bp.khT = khT;
+  bp.dyT = dyT;
+  bp.dout = (const uint16_t*)dout;
+  bp.gate = (const uint16_t*)gate;
+  bp.lse = lse;
+  bp.dsum = dsum;
+  bp.dy_out = dyb;
+  bp.dsum_out = dsum;
+  bp.dgate = (uint16_t*)dgate;
+  bp.dqh = dqh;
+  bp.dkh = dkh;
+  bp.dv = (uint16_t*)dv;
+  bp.B = B;
+  bp.n = n;
+  bp.npad = L.npad;
+  bp.H = H;
+  bp.G = G;
+  bp.grp = H / G;
+  bp.gate_mode = desc->gate_mode;
+  bp.scale = scale_of(desc);
+  bp.scale_log2 = bp.scale * 1.4426950408889634f;
+  if ((st = hip_status(launch_bwd_pre(bp, D, s), "backward gate launch")) != GA_OK) return st;
+  if ((st = hip_status(launch_bwd_transpose(qh, qhT, B, n, L.npad, H, D, s), "backward transpose")) != GA_OK) return st;
+  if ((st = hip_status(launch_bwd_transpose(kh, khT, B, n, L.npad, G, D, s), "backward transpose")) != GA_OK) return st;
+  if ((st = hip_status(launch_bwd_transpose(dyb, dyT, B, n, L.npad, H, D, s), "backward transpose")) != GA_OK)
+    return st;
+  if ((st = hip_status(launch_bwd_dq(bp, D, s), "backward dq launch")) != GA_OK) return st;
+  if ((st = hip_status(launch_bwd_dkv(bp, D, s), "backward dk/dv launch")) != GA_OK) return st;
+  // through RoPE and RMSNorm, q rows then k rows
+  for (int which = 0; which < 2; ++which) {
+    BwdNormParams np;
+    memset(&np, 0, sizeof(np));
+    const float* w = which == 0 ? q_norm_w : k_norm_w;
+    float* dw = which == 0 ? dq_norm_w : dk_norm_w;
+    np.grad = which == 0 ? dqh : dkh;
+    np.x = (const uint16_t*)(which == 0 ? q : k);
+    np.w = w;
+    np.positions = positions;
+    np.dx = (uint16_t*)(which == 0 ? dq : dk);
+    np.wpart = (w && dw) ? (float*)(ws + (which == 0 ? L.wq : L.wk)) : nullptr;
+    np.B = B;
+    np.n = n;
+    np.HX = which == 0 ? H : G;
+    np.d = D;
+    np.rot = desc->rot_dim;
+    np.eps = desc->rms_eps;
+    fill_inv_freq(desc, np.inv_freq);
+    if ((st = hip_status(launch_bwd_norm_rope(np, L.nwg, s), "backward norm launch")) != GA_OK) return st;
+    if (np.wpart && (st = hip_status(launch_bwd_reduce_rows(np.wpart, dw, L.nwg, D, s), "backward reduce")) != GA_OK)
+      return st;
+  }
+  return ok();
+}
+
 
 const char* ga_prefill_attention_kernel(const ga_attn_desc* desc, int32_t seq_len) {
   if (check_desc(desc) != GA_OK || seq_len < 0) return "invalid";

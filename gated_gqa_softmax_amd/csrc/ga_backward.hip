@@ -1,0 +1,422 @@
+// Backward pass of the gated GQA causal attention prefill (bf16 in and out,
+// fp32 accumulation), for training the layer of "Transformer by Hand · 6.
+// Gated attention" ("How the gate is learned": the gate's gradient
+// (y - t) o g(1 - g) x). With dout = dL/dout:
+//
+//   dy = dout * sigmoid(z),  dz = dout * y * g(1 - g)      (bwd_pre_kernel)
+//   P = exp2(s * scale * log2 e - lse),  dP = dy V^T,  dS = P * (dP - rowsum(dy * y))
+//   dq_hat = dS k_hat * scale                              (bwd_dq_kernel)
+//   dk_hat = sum_heads dS^T q_hat * scale,  dV = sum_heads P^T dy   (bwd_dkv_kernel)
+//   dq, dk, dw_q, dw_k through RoPE and RMSNorm           (bwd_norm_rope_kernel)
+//
+// The attention kernels run one wave per 32-row (dq) or 32-key (dk, dv)
+// block and one slice of at most 128 output dims, on v_mfma_f32_32x32x16_bf16
+// with every operand read as 16- or 8-byte pieces straight from L2: the
+// row-major q-hat, k-hat, v and dy rows, and transposed copies (q-hat, k-hat,
+// dy with the token index innermost) for the operands whose contraction runs
+// over tokens. A 32x32 accumulator holds, in lane l and slot i, row
+// 8(i/4) + 4(l/32) + i%4 and column l%32, so a probability tile computed with
+// the key (or query) in the column is already the B operand of the product
+// that contracts over the other index, provided the A operand reads the same
+// permutation of that index (two 8-byte pieces: rows 4(l/32) + 0..3 and
+// 8 + 4(l/32) + 0..3 of each 16-row step).
+#include "ga_common.hpp"
+#include "ga_internal.hpp"
+
+namespace ga {
+
+namespace {
+
+__device__ __forceinline__ f32x16_t mfma32(bf16x8_t a, bf16x8_t b, f32x16_t c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// A operand over a permuted 16-token step of a transposed row: tokens
+// t0 + 4hi + 0..3 and t0 + 8 + 4hi + 0..3 (t0 a multiple of 16).
+__device__ __forceinline__ bf16x8_t perm_operand(const uint16_t* row, int t0, int hi) {
+  const u32x2_t lo = *(const u32x2_t*)(row + t0 + 4 * hi);
+  const u32x2_t up = *(const u32x2_t*)(row + t0 + 8 + 4 * hi);
+  const u32x4_t v = {lo[0], lo[1], up[0], up[1]};
+  return __builtin_bit_cast(bf16x8_t, v);
+}
+
+__device__ __forceinline__ bf16x8_t pack_operand(const f32x16_t& x, int half) {
+  float f[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) f[j] = x[8 * half + j];
+  return __builtin_bit_cast(bf16x8_t, pack8(f));
+}
+
+}  // namespace
+
+// ---- gate backward, dy and rowsum(dy * y): one wave per (b, i, h) row -------------
+template <int D, int GATE>
+__global__ __launch_bounds__(256) void bwd_pre_kernel(const BwdParams p) {
+  constexpr int EPL = D / 64;  // elements per lane
+  const int lane = threadIdx.x & 63;
+  const long row = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= (long)p.B * p.n * p.H) return;
+  const long base = row * D + lane * EPL;
+  float y[EPL], go[EPL], z[EPL];
+#pragma unroll
+  for (int m = 0; m < EPL; ++m) {
+    y[m] = bf16_bits_to_f32(p.y[base + m]);
+    go[m] = bf16_bits_to_f32(p.dout[base + m]);
+    z[m] = GATE == 2 ? bf16_bits_to_f32(p.gate[base + m]) : 0.f;
+  }
+  float gh = 1.f, dyy = 0.f;
+  if (GATE == 1) {
+    gh = sigmoid_f32(bf16_bits_to_f32(p.gate[row]));
+#pragma unroll
+    for (int m = 0; m < EPL; ++m) dyy += go[m] * y[m];
+    dyy = sum_xor<64>(dyy);
+    if (lane == 0) p.dgate[row] = f32_to_bf16_bits(dyy * gh * (1.f - gh));
+  }
+  float ds = 0.f;
+#pragma unroll
+  for (int m = 0; m < EPL; ++m) {
+    const float g = GATE == 2 ? sigmoid_f32(z[m]) : gh;
+    if (GATE == 2) p.dgate[base + m] = f32_to_bf16_bits(go[m] * y[m] * g * (1.f - g));
+    const uint16_t dyb = f32_to_bf16_bits(GATE == 0 ? go[m] : go[m] * g);
+    p.dy_out[base + m] = dyb;
+    ds += bf16_bits_to_f32(dyb) * y[m];  // the rounded dy the products use
+  }
+  ds = sum_xor<64>(ds);
+  if (lane == 0) p.dsum_out[row] = ds;
+}
+
+// ---- dst[b][hx][e][t] = src[b][t][hx][e], zero for n <= t < npad --------------------
+__global__ __launch_bounds__(256) void bwd_transpose_kernel(const uint16_t* __restrict__ src,
+                                                            uint16_t* __restrict__ dst, int n, int npad, int HX,
+                                                            int D) {
+  __shared__ uint16_t tile[64][66];
+  const int t0 = blockIdx.x * 64, e0 = blockIdx.y * 64;
+  const int b = blockIdx.z / HX, hx = blockIdx.z % HX;
+  for (int idx = threadIdx.x; idx < 64 * 64; idx += 256) {
+    const int tt = idx >> 6, ee = idx & 63;
+    const int t = t0 + tt;
+    tile[tt][ee] = t < n ? src[(((long)b * n + t) * HX + hx) * D + e0 + ee] : (uint16_t)0;
+  }
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < 64 * 64; idx += 256) {
+    const int ee = idx >> 6, tt = idx & 63;
+    dst[(((long)b * HX + hx) * D + e0 + ee) * npad + t0 + tt] = tile[tt][ee];
+  }
+}
+
+// ---- dq-hat: one wave per (b, h, 32 queries, DP output dims) --------------------------
+// S^T = K Q^T and dP^T = V dy^T put the query in the accumulator column, so
+// dS^T is the B operand of dQ^T += K^T dS^T.
+template <int D, int DP>
+__global__ __launch_bounds__(256) void bwd_dq_kernel(const BwdParams p) {
+  constexpr int NPASS = D / DP;
+  const int lane = threadIdx.x & 63, l32 = lane & 31, hi = lane >> 5;
+  const int nqb = (p.n + 31) / 32;
+  const long total = (long)p.B * p.H * nqb * NPASS;
+  const long wi = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (wi >= total) return;
+  // heaviest (last) query blocks first
+  const int pass = (int)(wi % NPASS);
+  const long rest = wi / NPASS;
+  const int bh = (int)(rest % ((long)p.B * p.H));
+  const int qb = nqb - 1 - (int)(rest / ((long)p.B * p.H));
+  const int b = bh / p.H, h = bh % p.H, g = h / p.grp;
+  const int d0 = pass * DP;
+  const int q0 = qb * 32;
+  const int query = q0 + l32;
+  const int qrow = min(query, p.n - 1);
+  const long qoff = ((long)b * p.n + qrow) * p.H + h;
+  const float lse = p.lse[qoff], dsum = p.dsum[qoff];
+  const uint16_t* qp = p.qh + qoff * D + hi * 8;
+  const uint16_t* yp = p.dy + qoff * D + hi * 8;
+  f32x16_t acc[DP / 32];
+#pragma unroll
+  for (int mb = 0; mb < DP / 32; ++mb) acc[mb] = f32x16_t{};
+  for (int kt = 0; kt <= qb; ++kt) {
+    const int k0 = kt * 32;
+    const int krow = min(k0 + l32, p.n - 1);
+    const uint16_t* kp = p.kh + (((long)b * p.n + krow) * p.G + g) * D + hi * 8;
+    const uint16_t* vp = p.v + (((long)b * p.n + krow) * p.G + g) * D + hi * 8;
+    f32x16_t s = f32x16_t{}, dp = f32x16_t{};
+#pragma unroll 4
+    for (int kk = 0; kk < D / 16; ++kk) {
+      s = mfma32(*(const bf16x8_t*)(kp + kk * 16), *(const bf16x8_t*)(qp + kk * 16), s);
+      dp = mfma32(*(const bf16x8_t*)(vp + kk * 16), *(const bf16x8_t*)(yp + kk * 16), dp);
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int key = k0 + (i >> 2) * 8 + hi * 4 + (i & 3);
+      const bool valid = key <= query && query < p.n;
+      const float pv = valid ? __builtin_amdgcn_exp2f(s[i] * p.scale_log2 - lse) : 0.f;
+      s[i] = pv * (dp[i] - dsum);  // dS^T
+    }
+    const bf16x8_t ds0 = pack_operand(s, 0), ds1 = pack_operand(s, 1);
+#pragma unroll
+    for (int mb = 0; mb < DP / 32; ++mb) {
+      const uint16_t* kt_row = p.khT + (((long)b * p.G + g) * D + d0 + mb * 32 + l32) * p.npad;
+      acc[mb] = mfma32(perm_operand(kt_row, k0, hi), ds0, acc[mb]);
+      acc[mb] = mfma32(perm_operand(kt_row, k0 + 16, hi), ds1, acc[mb]);
+    }
+  }
+  if (query >= p.n) return;
+  float* dst = p.dqh + (((long)b * p.n + query) * p.H + h) * D + d0;
+#pragma unroll
+  for (int mb = 0; mb < DP / 32; ++mb)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) dst[mb * 32 + (i >> 2) * 8 + hi * 4 + (i & 3)] = acc[mb][i] * p.scale;
+}
+
+// ---- dk-hat and dv: one wave per (b, g, 32 keys, DP output dims) ------------------------
+// S = Q K^T and dP = dy V^T put the key in the accumulator column, so P and
+// dS are the B operands of dV^T += dy^T P and dK^T += Q^T dS.
+template <int D, int DP>
+__global__ __launch_bounds__(256) void bwd_dkv_kernel(const BwdParams p) {
+  constexpr int NPASS = D / DP;
+  const int lane = threadIdx.x & 63, l32 = lane & 31, hi = lane >> 5;
+  const int nkb = (p.n + 31) / 32;
+  const long total = (long)p.B * p.G * nkb * NPASS;
+  const long wi = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (wi >= total) return;
+  // heaviest (first) key blocks first
+  const int pass = (int)(wi % NPASS);
+  const long rest = wi / NPASS;
+  const int bg = (int)(rest % ((long)p.B * p.G));
+  const int kb = (int)(rest / ((long)p.B * p.G));
+  const int b = bg / p.G, g = bg % p.G;
+  const int d0 = pass * DP;
+  const int k0 = kb * 32;
+  const int key = k0 + l32;
+  const int krow = min(key, p.n - 1);
+  const uint16_t* kp = p.kh + (((long)b * p.n + krow) * p.G + g) * D + hi * 8;
+  const uint16_t* vp = p.v + (((long)b * p.n + krow) * p.G + g) * D + hi * 8;
+  f32x16_t dv[DP / 32], dk[DP / 32];
+#pragma unroll
+  for (int mb = 0; mb < DP / 32; ++mb) dv[mb] = dk[mb] = f32x16_t{};
+  const int nqt = (p.n + 31) / 32;
+  for (int hh = 0; hh < p.grp; ++hh) {
+    const int h = g * p.grp + hh;
+    for (int qt = kb; qt < nqt; ++qt) {
+      const int q0 = qt * 32;
+      const int qrow = min(q0 + l32, p.n - 1);
+      const long qoff = ((long)b * p.n + qrow) * p.H + h;
+      const uint16_t* qp = p.qh + qoff * D + hi * 8;
+      const uint16_t* yp = p.dy + qoff * D + hi * 8;
+      f32x16_t s = f32x16_t{}, dp = f32x16_t{};
+#pragma unroll 4
+      for (int kk = 0; kk < D / 16; ++kk) {
+        s = mfma32(*(const bf16x8_t*)(qp + kk * 16), *(const bf16x8_t*)(kp + kk * 16), s);
+        dp = mfma32(*(const bf16x8_t*)(yp + kk * 16), *(const bf16x8_t*)(vp + kk * 16), dp);
+      }
+      f32x16_t pm;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int query = q0 + (i >> 2) * 8 + hi * 4 + (i & 3);
+        const bool valid = key <= query && query < p.n;
+        const long ro = ((long)b * p.n + min(query, p.n - 1)) * p.H + h;
+        const float pv = valid ? __builtin_amdgcn_exp2f(s[i] * p.scale_log2 - p.lse[ro]) : 0.f;
+        pm[i] = pv;
+        s[i] = pv * (dp[i] - p.dsum[ro]);  // dS
+      }
+      const bf16x8_t p0 = pack_operand(pm, 0), p1 = pack_operand(pm, 1);
+      const bf16x8_t ds0 = pack_operand(s, 0), ds1 = pack_operand(s, 1);
+#pragma unroll
+      for (int mb = 0; mb < DP / 32; ++mb) {
+        const long trow = ((long)b * p.H + h) * D + d0 + mb * 32 + l32;
+        const uint16_t* yt = p.dyT + trow * p.npad;
+        const uint16_t* qt_row = p.qhT + trow * p.npad;
+        dv[mb] = mfma32(perm_operand(yt, q0, hi), p0, dv[mb]);
+        dv[mb] = mfma32(perm_operand(yt, q0 + 16, hi), p1, dv[mb]);
+        dk[mb] = mfma32(perm_operand(qt_row, q0, hi), ds0, dk[mb]);
+        dk[mb] = mfma32(perm_operand(qt_row, q0 + 16, hi), ds1, dk[mb]);
+      }
+    }
+  }
+  if (key >= p.n) return;
+  const long ko = (((long)b * p.n + key) * p.G + g) * D + d0;
+#pragma unroll
+  for (int mb = 0; mb < DP / 32; ++mb)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int e = mb * 32 + (i >> 2) * 8 + hi * 4 + (i & 3);
+      p.dkh[ko + e] = dk[mb][i] * p.scale;
+      p.dv[ko + e] = f32_to_bf16_bits(dv[mb][i]);
+    }
+}
+
+// ---- through RoPE and RMSNorm: each wave takes rows w, w + nwaves, ... ----------------
+template <int D>
+__global__ __launch_bounds__(256) void bwd_norm_rope_kernel(const BwdNormParams p) {
+  constexpr int EPL = D / 64;
+  __shared__ float stage[4][D];
+  __shared__ float wsum[4][D];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const long rows = (long)p.B * p.n * p.HX;
+  const long nwaves = (long)gridDim.x * 4;
+  const int half = p.rot / 2;
+  float wacc[EPL];
+#pragma unroll
+  for (int m = 0; m < EPL; ++m) wacc[m] = 0.f;
+  for (long row = (long)blockIdx.x * 4 + w; row < rows; row += nwaves) {
+    const long t = row / p.HX;  // b * n + i
+    const int i = (int)(t % p.n);
+    const int pos = p.positions ? p.positions[t] : i;
+    float gr[EPL];
+#pragma unroll
+    for (int m = 0; m < EPL; ++m) gr[m] = p.grad[row * D + lane + 64 * m];
+    if (half > 0) {
+      // the previous row's reads of stage come before these writes
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+      for (int m = 0; m < EPL; ++m) stage[w][lane + 64 * m] = gr[m];
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+      for (int m = 0; m < EPL; ++m) {
+        const int e = lane + 64 * m;
+        if (e < p.rot) {
+          const bool first = e < half;
+          float c, sn;
+          rope_cos_sin(pos, p.inv_freq[first ? e : e - half], &c, &sn);
+          const float other = stage[w][first ? e + half : e - half];
+          gr[m] = first ? gr[m] * c + other * sn : gr[m] * c - other * sn;
+        }
+      }
+    }
+    float dx[EPL];
+    if (p.w) {
+      float x[EPL], ss = 0.f;
+#pragma unroll
+      for (int m = 0; m < EPL; ++m) {
+        x[m] = bf16_bits_to_f32(p.x[row * D + lane + 64 * m]);
+        ss += x[m] * x[m];
+      }
+      ss = sum_xor<64>(ss);
+      const float r = sqrtf(ss / D + p.eps);
+      const float inv_r = 1.0f / r;
+      float dot = 0.f;
+#pragma unroll
+      for (int m = 0; m < EPL; ++m) {
+        const float xh = x[m] * inv_r;
+        dot += gr[m] * p.w[lane + 64 * m] * xh;
+        wacc[m] += gr[m] * xh;
+      }
+      dot = sum_xor<64>(dot) / D;
+#pragma unroll
+      for (int m = 0; m < EPL; ++m) dx[m] = (gr[m] * p.w[lane + 64 * m] - x[m] * inv_r * dot) * inv_r;
+    } else {
+#pragma unroll
+      for (int m = 0; m < EPL; ++m) dx[m] = gr[m];
+    }
+#pragma unroll
+    for (int m = 0; m < EPL; ++m) p.dx[row * D + lane + 64 * m] = f32_to_bf16_bits(dx[m]);
+  }
+  if (!p.w || !p.wpart) return;  // (uniform over the workgroup)
+#pragma unroll
+  for (int m = 0; m < EPL; ++m) wsum[w][lane + 64 * m] = wacc[m];
+  __syncthreads();
+  for (int e = threadIdx.x; e < D; e += 256)
+    p.wpart[(long)blockIdx.x * D + e] = (wsum[0][e] + wsum[1][e]) + (wsum[2][e] + wsum[3][e]);
+}
+
+// out[e] = sum over rows r < nrows of part[r][e]
+__global__ __launch_bounds__(256) void bwd_reduce_rows_kernel(const float* part, float* out, int nrows, int d) {
+  __shared__ float red[4][64];
+  const int e = blockIdx.x * 64 + (threadIdx.x & 63);
+  const int w = threadIdx.x >> 6;
+  float s = 0.f;
+  if (e < d)
+    for (int r = w; r < nrows; r += 4) s += part[(long)r * d + e];
+  red[w][threadIdx.x & 63] = s;
+  __syncthreads();
+  if (w == 0 && e < d) out[e] = (red[0][threadIdx.x] + red[1][threadIdx.x]) + (red[2][threadIdx.x] + red[3][threadIdx.x]);
+}
+
+// ---- launchers ----------------------------------------------------------------------------
+
+template <int D>
+static hipError_t launch_pre_d(const BwdParams& p, hipStream_t s) {
+  const long rows = (long)p.B * p.n * p.H;
+  const unsigned grid = (unsigned)((rows + 3) / 4);
+  if (rows == 0) return hipSuccess;
+  switch (p.gate_mode) {
+    case 0: hipLaunchKernelGGL((bwd_pre_kernel<D, 0>), dim3(grid), dim3(256), 0, s, p); break;
+    case 1: hipLaunchKernelGGL((bwd_pre_kernel<D, 1>), dim3(grid), dim3(256), 0, s, p); break;
+    default: hipLaunchKernelGGL((bwd_pre_kernel<D, 2>), dim3(grid), dim3(256), 0, s, p); break;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_pre(const BwdParams& p, int D, hipStream_t s) {
+  switch (D) {
+    case 64: return launch_pre_d<64>(p, s);
+    case 128: return launch_pre_d<128>(p, s);
+    case 256: return launch_pre_d<256>(p, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_bwd_transpose(const uint16_t* src, uint16_t* dst, int B, int n, int npad, int HX, int D,
+                                hipStream_t s) {
+  if (B == 0 || npad == 0) return hipSuccess;
+  const dim3 grid((unsigned)(npad / 64), (unsigned)(D / 64), (unsigned)(B * HX));
+  hipLaunchKernelGGL(bwd_transpose_kernel, grid, dim3(256), 0, s, src, dst, n, npad, HX, D);
+  return hipGetLastError();
+}
+
+template <int D>
+static hipError_t launch_dq_d(const BwdParams& p, hipStream_t s) {
+  constexpr int DP = D < 128 ? D : 128;
+  const long waves = (long)p.B * p.H * ((p.n + 31) / 32) * (D / DP);
+  if (waves == 0) return hipSuccess;
+  hipLaunchKernelGGL((bwd_dq_kernel<D, DP>), dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+template <int D>
+static hipError_t launch_dkv_d(const BwdParams& p, hipStream_t s) {
+  constexpr int DP = D < 128 ? D : 128;
+  const long waves = (long)p.B * p.G * ((p.n + 31) / 32) * (D / DP);
+  if (waves == 0) return hipSuccess;
+  hipLaunchKernelGGL((bwd_dkv_kernel<D, DP>), dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_dq(const BwdParams& p, int D, hipStream_t s) {
+  switch (D) {
+    case 64: return launch_dq_d<64>(p, s);
+    case 128: return launch_dq_d<128>(p, s);
+    case 256: return launch_dq_d<256>(p, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_bwd_dkv(const BwdParams& p, int D, hipStream_t s) {
+  switch (D) {
+    case 64: return launch_dkv_d<64>(p, s);
+    case 128: return launch_dkv_d<128>(p, s);
+    case 256: return launch_dkv_d<256>(p, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_bwd_norm_rope(const BwdNormParams& p, int nwg, hipStream_t s) {
+  if ((long)p.B * p.n * p.HX == 0) return hipSuccess;
+  switch (p.d) {
+    case 64: hipLaunchKernelGGL((bwd_norm_rope_kernel<64>), dim3(nwg), dim3(256), 0, s, p); break;
+    case 128: hipLaunchKernelGGL((bwd_norm_rope_kernel<128>), dim3(nwg), dim3(256), 0, s, p); break;
+    case 256: hipLaunchKernelGGL((bwd_norm_rope_kernel<256>), dim3(nwg), dim3(256), 0, s, p); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_reduce_rows(const float* part, float* out, int nrows, int d, hipStream_t s) {
+  hipLaunchKernelGGL(bwd_reduce_rows_kernel, dim3((unsigned)((d + 63) / 64)), dim3(256), 0, s, part, out, nrows,
+                     d);
+  return hipGetLastError();
+}
+
+}  // namespace ga

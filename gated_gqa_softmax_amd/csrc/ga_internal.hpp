@@ -72,6 +72,9 @@ struct PrefillParams {
   float* part_lse;
   unsigned* sync;
   int split, nunits, npairs, split_ovh;
+  // simple kernel only: log2-domain log-sum-exp of each output row (b, token,
+  // head), for the backward pass; null otherwise
+  float* lse;
   double inv_freq[kMaxHalfRot];
 };
 
@@ -123,6 +126,58 @@ struct DecodeParams {
 };
 
 constexpr int kDecodeChunk = 512;  // keys per decode split
+
+// Backward of the prefill (bf16). Row-major workspace copies: qh [B,n,H,d],
+// kh [B,n,G,d] (q-hat, k-hat), y [B,n,H,d] (ungated attention output), dy
+// [B,n,H,d] (gradient of y); transposed copies qhT, dyT [B,H,d,npad] and khT
+// [B,G,d,npad] (zero past n); lse, dsum [B,n,H] fp32 (log2-domain
+// log-sum-exp of each score row; rowsum(dy * y)); dqh [B,n,H,d] and dkh
+// [B,n,G,d] fp32 (gradients of q-hat and k-hat).
+struct BwdParams {
+  const uint16_t* qh;
+  const uint16_t* kh;
+  const uint16_t* v;
+  const uint16_t* y;
+  const uint16_t* dy;
+  const uint16_t* qhT;
+  const uint16_t* khT;
+  const uint16_t* dyT;
+  const uint16_t* dout;
+  const uint16_t* gate;
+  const float* lse;
+  const float* dsum;
+  uint16_t* dy_out;     // pre kernel: dy
+  float* dsum_out;      // pre kernel: dsum
+  uint16_t* dgate;      // pre kernel: gradient of the gate logits (or null)
+  float* dqh;
+  float* dkh;
+  uint16_t* dv;
+  int B, n, npad, H, G, grp, gate_mode;
+  float scale, scale_log2;
+};
+
+// Gradient of x through n = RoPE(RMSNorm(x, w)) for rows [B, n, HX, d]:
+// grad (fp32 gradient of n) -> dx (bf16); per-workgroup partial sums of the
+// weight gradient in wpart [gridDim.x][d] when w is not null.
+struct BwdNormParams {
+  const float* grad;
+  const uint16_t* x;
+  const float* w;
+  const int* positions;
+  uint16_t* dx;
+  float* wpart;
+  int B, n, HX, d, rot;
+  float eps;
+  double inv_freq[kMaxHalfRot];
+};
+
+hipError_t launch_bwd_pre(const BwdParams& p, int D, hipStream_t s);
+hipError_t launch_bwd_transpose(const uint16_t* src, uint16_t* dst, int B, int n, int npad, int HX, int D,
+                                hipStream_t s);
+hipError_t launch_bwd_dq(const BwdParams& p, int D, hipStream_t s);
+hipError_t launch_bwd_dkv(const BwdParams& p, int D, hipStream_t s);
+hipError_t launch_bwd_norm_rope(const BwdNormParams& p, int nwg, hipStream_t s);
+hipError_t launch_bwd_reduce_rows(const float* part, float* out, int nrows, int d, hipStream_t s);
 
 hipError_t launch_prep_keys(const PrepParams& p, int is_bf16, hipStream_t s);
 hipError_t launch_prefill_mfma(const PrefillParams& p, int D, int gate_mode, hipStream_t s);

@@ -300,6 +300,7 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(const PrefillParams p
   if (!my_valid) return;
   const float inv_l = 1.0f / l_run;
   const long row_off = ((long)b * n + my_tok) * p.H + my_h;  // (b, token, head) index
+  if (p.lse && hi == 0) p.lse[row_off] = m_run + __log2f(l_run);
   uint16_t* orow = p.out + row_off * D;
   float hg = 1.0f;
   if (GATE == 1) hg = sigmoid_f32(bf16_bits_to_f32(p.gate[row_off * p.gs]));

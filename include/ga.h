@@ -310,6 +310,38 @@ ga_status ga_decode_merge(const ga_attn_desc* desc, const void* q, const void* k
                           const int32_t* cache_lens, int32_t max_cache_len,
                           const void* workspace, size_t workspace_bytes, void* out, void* stream);
 
+/* ---- backward (training) -------------------------------------------------- */
+
+/* Workspace ga_prefill_backward needs (256-byte aligned): bf16 copies of
+ * q-hat, k-hat, the ungated attention output y and its gradient dy (row-major
+ * and, for q-hat, k-hat and dy, transposed with the token index innermost,
+ * padded to a multiple of 64 tokens), fp32 row statistics, fp32 gradients of
+ * q-hat and k-hat, and 2 x 512 x d floats of weight-gradient partials. */
+size_t ga_prefill_backward_workspace_bytes(const ga_attn_desc* desc, int32_t seq_len);
+
+/* Backward of ga_prefill: the gradients of sum(dout * out) with respect to
+ * every input, for training the layer ("Transformer by Hand · 6. Gated
+ * attention", "How the gate is learned": the gate's gradient is
+ * dout * y * g(1 - g), then the chain rule through the causal softmax, GQA,
+ * RoPE and the RMSNorms of the forward definition above).
+ *  q, k, v, gate, q_norm_w, k_norm_w, positions: the forward's inputs.
+ *  dout          [B,n,H*d] gradient of the output.
+ *  dq [B,n,H,d], dk, dv [B,n,G,d]: written (not accumulated), bf16.
+ *  dgate         the gate's shape (required with a gate, unused without).
+ *  dq_norm_w, dk_norm_w  [d] float32, written; NULL skips that weight
+ *                gradient (also skipped when the weight itself is NULL).
+ * Serves bf16, d in {64, 128, 256}, group <= 128, the method's gate
+ * (GA_ERR_UNSUPPORTED for gate variants, the output norm, head strides other
+ * than dense, fp32). The forward's softmax statistics are recomputed inside
+ * the call from q-hat and k-hat, so nothing from the forward call is needed.
+ * Deterministic: no atomics, fixed summation orders. */
+ga_status ga_prefill_backward(const ga_attn_desc* desc, int32_t seq_len,
+                              const void* q, const void* k, const void* v, const void* gate,
+                              const float* q_norm_w, const float* k_norm_w, const int32_t* positions,
+                              const void* dout, void* dq, void* dk, void* dv, void* dgate,
+                              float* dq_norm_w, float* dk_norm_w,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
 /* ---- misc --------------------------------------------------------------- */
 
 const char* ga_status_string(ga_status status);
