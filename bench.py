@@ -38,6 +38,7 @@ def parse():
     ap.add_argument("--no-chunk", action="store_true", help="skip the chunked-prefill measurement")
     ap.add_argument("--no-packed", action="store_true", help="skip the fused [q | gate] input measurement")
     ap.add_argument("--no-variant", action="store_true", help="skip the gate-variant epilogue measurement")
+    ap.add_argument("--no-backward", action="store_true", help="skip the backward-pass measurement")
     ap.add_argument("--no-prefill", action="store_true", help="decode only (for counter runs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--decode-steps", type=int, default=20)
@@ -494,6 +495,56 @@ def time_gate_variant(torch, api, inputs, accounting, wname, steps, warmup):
     }
 
 
+def time_backward(torch, api, inputs, accounting, wname, steps, warmup):
+    """ga_prefill_backward on the prefill workload (all gradients, the norm
+    weights' included), whole calls back to back between two events."""
+    w = inputs.WORKLOADS[wname]
+    x = inputs.make_prefill(w)
+    et = torch.bfloat16
+    dv = lambda a, dt=None: torch.from_numpy(np.ascontiguousarray(a)).to("cuda", dtype=dt)
+    q, k, v, gate = dv(x["q"], et), dv(x["k"], et), dv(x["v"], et), dv(x["gate"], et)
+    wq, wk, pos = dv(x["q_norm_w"]), dv(x["k_norm_w"]), dv(x["positions"])
+    gen = torch.Generator(device="cuda").manual_seed(w.seed + 1000)
+    dout = torch.randn((w.batch, w.seq_len, w.n_q_heads * w.head_dim), generator=gen, device="cuda").to(et)
+    d = api.make_desc(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.rot_dim, w.rope_base, w.rms_eps, 0.0, et,
+                      w.gate_mode)
+    ws = torch.empty(api.ga_prefill_backward_workspace_bytes(d, w.seq_len), dtype=torch.uint8, device="cuda")
+    grads = dict(dq=torch.empty_like(q), dk=torch.empty_like(k), dv=torch.empty_like(v), dgate=torch.empty_like(gate),
+                 dq_norm_w=torch.empty_like(wq), dk_norm_w=torch.empty_like(wk))
+    stream = torch.cuda.current_stream()
+
+    def whole():
+        api.ga_prefill_backward(d, q, k, v, dout, gate=gate, q_norm_w=wq, k_norm_w=wk, positions=pos, workspace=ws,
+                                stream=stream, grads=grads)
+
+    for _ in range(warmup):
+        whole()
+    ramp(torch, whole)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(steps):
+        whole()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    step_ms = e0.elapsed_time(e1) / steps
+    flops = accounting.causal_backward_flops(w.batch, w.n_q_heads, w.head_dim, w.seq_len)
+    achieved = flops / (step_ms * 1e-3) / 1e12
+    return {
+        "metric": "prefill backward TFLOP/s",
+        "value": achieved,
+        "unit": "TFLOP/s",
+        "ms_per_step": step_ms,
+        "steps": steps,
+        "config": {"workload": w.name, "batch": w.batch, "seq_len": w.seq_len, "n_q_heads": w.n_q_heads,
+                   "n_kv_heads": w.n_kv_heads, "head_dim": w.head_dim, "rot_dim": w.rot_dim, "gate": w.gate_mode,
+                   "gradients": "q, k, v, gate, q_norm_w, k_norm_w"},
+        "roofline": {"bound": "mfma", "kernel": "ga_prefill_backward (whole call: all its kernels)",
+                     "achieved": achieved, "peak": MI355X_BF16_DENSE_TFLOPS, "unit": "TFLOP/s",
+                     "frac": achieved / MI355X_BF16_DENSE_TFLOPS, "kernel_ms": step_ms, "algorithmic_flops": flops},
+    }
+
+
 def main():
     args = parse()
     if args.record_traffic:
@@ -550,6 +601,9 @@ def main():
     if not args.no_variant and w.gate_mode == "elementwise" and w.dtype == "bf16":
         rec["gate_variant"] = time_gate_variant(torch, api, inputs, accounting, args.workload, args.steps,
                                                 args.warmup)
+    if not args.no_backward and w.gate_mode == "elementwise" and w.dtype == "bf16":
+        rec["backward"] = time_backward(torch, api, inputs, accounting, args.workload, max(5, args.steps // 5),
+                                        args.warmup)
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(w, pre["x"], pre["flops"])
     print(json.dumps(rec), flush=True)

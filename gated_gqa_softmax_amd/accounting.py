@@ -14,6 +14,14 @@ def causal_prefill_flops(batch: int, n_q_heads: int, head_dim: int, seq_len: int
     return 2.0 * batch * n_q_heads * head_dim * seq_len * (seq_len + 1)
 
 
+def causal_backward_flops(batch: int, n_q_heads: int, head_dim: int, seq_len: int) -> float:
+    """Backward of the causal prefill: five products per visible (i, j <= i)
+    pair per query head (q.k again, dy.v, P^T dy, dS^T q, dS k), 2d flops each:
+    2.5 times ``causal_prefill_flops``. Recomputing the forward's softmax
+    statistics, the gate, norm and rotation backward are excluded."""
+    return 2.5 * causal_prefill_flops(batch, n_q_heads, head_dim, seq_len)
+
+
 def chunk_prefill_flops(cache_lens, n_q_heads: int, head_dim: int, chunk_len: int) -> float:
     """Chunked prefill: row i of sequence b sees L_b + i + 1 keys, so
     sum_b 2*H*d*(2*n*L_b + n*(n+1)) (the whole-sequence formula when L_b = 0)."""

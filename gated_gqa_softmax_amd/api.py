@@ -346,17 +346,30 @@ def ga_prefill_backward_workspace_bytes(desc: AttnDesc, seq_len: int) -> int:
 
 
 def ga_prefill_backward(desc: AttnDesc, q, k, v, dout, gate=None, q_norm_w=None, k_norm_w=None, positions=None,
-                        workspace=None, stream=None, weight_grads=True) -> dict:
+                        workspace=None, stream=None, weight_grads=True, grads: Optional[dict] = None) -> dict:
     """Gradients of sum(dout * ga_prefill(...)): dict with dq, dk, dv, dgate
     (None without a gate) and dq_norm_w, dk_norm_w (None without that norm
-    weight, or with weight_grads=False)."""
+    weight, or with weight_grads=False). ``grads`` may hold preallocated
+    output tensors under the same keys."""
     lib = _lib.load()
     et = _elem_dtype(desc)
     B, n = q.shape[0], q.shape[1]
-    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    dgate = torch.empty_like(gate) if gate is not None else None
-    dwq = torch.empty_like(q_norm_w) if (q_norm_w is not None and weight_grads) else None
-    dwk = torch.empty_like(k_norm_w) if (k_norm_w is not None and weight_grads) else None
+    grads = grads or {}
+    dq = grads.get("dq", None)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = grads.get("dk", None)
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = grads.get("dv", None)
+    dv = torch.empty_like(v) if dv is None else dv
+    dgate = grads.get("dgate", None)
+    if dgate is None and gate is not None:
+        dgate = torch.empty_like(gate)
+    dwq = grads.get("dq_norm_w", None)
+    if dwq is None and q_norm_w is not None and weight_grads:
+        dwq = torch.empty_like(q_norm_w)
+    dwk = grads.get("dk_norm_w", None)
+    if dwk is None and k_norm_w is not None and weight_grads:
+        dwk = torch.empty_like(k_norm_w)
     nbytes = ga_prefill_backward_workspace_bytes(desc, n)
     if workspace is None or workspace.numel() < nbytes:
         workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)

@@ -511,7 +511,7 @@ void fill_decode_params(DecodeParams& dp, const ga_attn_desc* desc, const void* 
 
 // Backward workspace: the parts in order, each 256-byte aligned.
 struct BwdLayout {
-  size_t qh, kh, y, dy, qhT, khT, dyT, lse, dsum, dqh, dkh, wq, wk, total;
+  size_t qh, kh, y, dy, q_rb, q_cb, k_rb, k_cb, v_rb, dy_rb, dy_cb, lse, dsum, dqh, dkp, dvp, wq, wk, total;
   int npad, nwg;
 };
 
@@ -532,13 +532,18 @@ BwdLayout bwd_layout(const ga_attn_desc* d, int32_t n) {
   L.kh = take(B * n * G * D * 2);
   L.y = take(B * n * H * D * 2);
   L.dy = take(B * n * H * D * 2);
-  L.qhT = take(B * H * D * L.npad * 2);
-  L.khT = take(B * G * D * L.npad * 2);
-  L.dyT = take(B * H * D * L.npad * 2);
+  L.q_rb = take(B * H * L.npad * D * 2);
+  L.q_cb = take(B * H * L.npad * D * 2);
+  L.k_rb = take(B * G * L.npad * D * 2);
+  L.k_cb = take(B * G * L.npad * D * 2);
+  L.v_rb = take(B * G * L.npad * D * 2);
+  L.dy_rb = take(B * H * L.npad * D * 2);
+  L.dy_cb = take(B * H * L.npad * D * 2);
   L.lse = take(B * n * H * 4);
   L.dsum = take(B * n * H * 4);
   L.dqh = take(B * n * H * D * 4);
-  L.dkh = take(B * n * G * D * 4);
+  L.dkp = take(B * n * H * D * 4);
+  L.dvp = take(B * n * H * D * 4);
   L.wq = take((size_t)L.nwg * D * 4);
   L.wk = take((size_t)L.nwg * D * 4);
   L.total = off;
@@ -598,13 +603,18 @@ ga_status ga_prefill_backward(const ga_attn_desc* desc, int32_t seq_len, const v
   uint16_t* kh = (uint16_t*)(ws + L.kh);
   uint16_t* y = (uint16_t*)(ws + L.y);
   uint16_t* dyb = (uint16_t*)(ws + L.dy);
-  uint16_t* qhT = (uint16_t*)(ws + L.qhT);
-  uint16_t* khT = (uint16_t*)(ws + L.khT);
-  uint16_t* dyT = (uint16_t*)(ws + L.dyT);
+  uint16_t* q_rb = (uint16_t*)(ws + L.q_rb);
+  uint16_t* q_cb = (uint16_t*)(ws + L.q_cb);
+  uint16_t* k_rb = (uint16_t*)(ws + L.k_rb);
+  uint16_t* k_cb = (uint16_t*)(ws + L.k_cb);
+  uint16_t* v_rb = (uint16_t*)(ws + L.v_rb);
+  uint16_t* dy_rb = (uint16_t*)(ws + L.dy_rb);
+  uint16_t* dy_cb = (uint16_t*)(ws + L.dy_cb);
   float* lse = (float*)(ws + L.lse);
   float* dsum = (float*)(ws + L.dsum);
   float* dqh = (float*)(ws + L.dqh);
-  float* dkh = (float*)(ws + L.dkh);
+  float* dkp = (float*)(ws + L.dkp);
+  float* dvp = (float*)(ws + L.dvp);
 
   // q-hat and k-hat (bf16, as the forward's MFMA operands)
   if ((st = prefill_keys_impl(desc, n, k, nullptr, k_norm_w, positions, kh, nullptr, n, s)) != GA_OK) return st;
@@ -643,14 +653,14 @@ ga_status ga_prefill_backward(const ga_attn_desc* desc, int32_t seq_len, const v
   }
   BwdParams bp;
   memset(&bp, 0, sizeof(bp));
-  bp.qh = qh;
-  bp.kh = kh;
-  bp.v = (const uint16_t*)v;
+  bp.q_rb = q_rb;
+  bp.q_cb = q_cb;
+  bp.k_rb = k_rb;
+  bp.k_cb = k_cb;
+  bp.v_rb = v_rb;
+  bp.dy_rb = dy_rb;
+  bp.dy_cb = dy_cb;
   bp.y = y;
-  bp.dy = dyb;
-  bp.qhT = qhT;
-  bp.khT = khT;
-  bp.dyT = dyT;
   bp.dout = (const uint16_t*)dout;
   bp.gate = (const uint16_t*)gate;
   bp.lse = lse;
@@ -659,8 +669,8 @@ ga_status ga_prefill_backward(const ga_attn_desc* desc, int32_t seq_len, const v
   bp.dsum_out = dsum;
   bp.dgate = (uint16_t*)dgate;
   bp.dqh = dqh;
-  bp.dkh = dkh;
-  bp.dv = (uint16_t*)dv;
+  bp.dkp = dkp;
+  bp.dvp = dvp;
   bp.B = B;
   bp.n = n;
   bp.npad = L.npad;
@@ -671,9 +681,11 @@ ga_status ga_prefill_backward(const ga_attn_desc* desc, int32_t seq_len, const v
   bp.scale = scale_of(desc);
   bp.scale_log2 = bp.scale * 1.4426950408889634f;
   if ((st = hip_status(launch_bwd_pre(bp, D, s), "backward gate launch")) != GA_OK) return st;
-  if ((st = hip_status(launch_bwd_transpose(qh, qhT, B, n, L.npad, H, D, s), "backward transpose")) != GA_OK) return st;
-  if ((st = hip_status(launch_bwd_transpose(kh, khT, B, n, L.npad, G, D, s), "backward transpose")) != GA_OK) return st;
-  if ((st = hip_status(launch_bwd_transpose(dyb, dyT, B, n, L.npad, H, D, s), "backward transpose")) != GA_OK)
+  if ((st = hip_status(launch_bwd_blocks(qh, q_rb, q_cb, B, n, L.npad, H, D, s), "backward operand copies")) != GA_OK ||
+      (st = hip_status(launch_bwd_blocks(kh, k_rb, k_cb, B, n, L.npad, G, D, s), "backward operand copies")) != GA_OK ||
+      (st = hip_status(launch_bwd_blocks((const uint16_t*)v, v_rb, nullptr, B, n, L.npad, G, D, s),
+                       "backward operand copies")) != GA_OK ||
+      (st = hip_status(launch_bwd_blocks(dyb, dy_rb, dy_cb, B, n, L.npad, H, D, s), "backward operand copies")) != GA_OK)
     return st;
   if ((st = hip_status(launch_bwd_dq(bp, D, s), "backward dq launch")) != GA_OK) return st;
   if ((st = hip_status(launch_bwd_dkv(bp, D, s), "backward dk/dv launch")) != GA_OK) return st;
@@ -683,7 +695,8 @@ ga_status ga_prefill_backward(const ga_attn_desc* desc, int32_t seq_len, const v
     memset(&np, 0, sizeof(np));
     const float* w = which == 0 ? q_norm_w : k_norm_w;
     float* dw = which == 0 ? dq_norm_w : dk_norm_w;
-    np.grad = which == 0 ? dqh : dkh;
+    np.grad = which == 0 ? dqh : dkp;
+    np.gsum = which == 0 ? 1 : H / G;
     np.x = (const uint16_t*)(which == 0 ? q : k);
     np.w = w;
     np.positions = positions;
@@ -700,7 +713,7 @@ ga_status ga_prefill_backward(const ga_attn_desc* desc, int32_t seq_len, const v
     if (np.wpart && (st = hip_status(launch_bwd_reduce_rows(np.wpart, dw, L.nwg, D, s), "backward reduce")) != GA_OK)
       return st;
   }
-  return ok();
+  return hip_status(launch_bwd_dv_sum(dvp, (uint16_t*)dv, B, n, H, G, D, s), "backward dv launch");
 }
 
 

@@ -9,17 +9,18 @@
 //   dk_hat = sum_heads dS^T q_hat * scale,  dV = sum_heads P^T dy   (bwd_dkv_kernel)
 //   dq, dk, dw_q, dw_k through RoPE and RMSNorm           (bwd_norm_rope_kernel)
 //
-// The attention kernels run one wave per 32-row (dq) or 32-key (dk, dv)
-// block and one slice of at most 128 output dims, on v_mfma_f32_32x32x16_bf16
-// with every operand read as 16- or 8-byte pieces straight from L2: the
-// row-major q-hat, k-hat, v and dy rows, and transposed copies (q-hat, k-hat,
-// dy with the token index innermost) for the operands whose contraction runs
-// over tokens. A 32x32 accumulator holds, in lane l and slot i, row
-// 8(i/4) + 4(l/32) + i%4 and column l%32, so a probability tile computed with
-// the key (or query) in the column is already the B operand of the product
-// that contracts over the other index, provided the A operand reads the same
-// permutation of that index (two 8-byte pieces: rows 4(l/32) + 0..3 and
-// 8 + 4(l/32) + 0..3 of each 16-row step).
+// The attention kernels run one wave per (query head, 32-row block) (dq) or
+// (query head, 32-key block) (per-head dk, dv partials) and one slice of at
+// most 128 output dims, on v_mfma_f32_32x32x16_bf16, with every operand one
+// coalesced 1 KiB load from L2: copies of q-hat, k-hat, v and dy laid out in
+// the MFMA's operand order (bwd_blocks_kernel), row-blocked for contractions
+// over dims and column-blocked for contractions over tokens. A 32x32
+// accumulator holds, in lane l and slot i, row 8(i/4) + 4(l/32) + i%4 and
+// column l%32, so a probability tile computed with the key (or query) in the
+// column is already the B operand of the product that contracts over the
+// other index, provided the A operand holds the same permutation of that
+// index: the column-blocked pieces hold tokens 4(l/32) + 0..3 and
+// 8 + 4(l/32) + 0..3 of each 16-token step.
 #include "ga_common.hpp"
 #include "ga_internal.hpp"
 
@@ -29,15 +30,6 @@ namespace {
 
 __device__ __forceinline__ f32x16_t mfma32(bf16x8_t a, bf16x8_t b, f32x16_t c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-}
-
-// A operand over a permuted 16-token step of a transposed row: tokens
-// t0 + 4hi + 0..3 and t0 + 8 + 4hi + 0..3 (t0 a multiple of 16).
-__device__ __forceinline__ bf16x8_t perm_operand(const uint16_t* row, int t0, int hi) {
-  const u32x2_t lo = *(const u32x2_t*)(row + t0 + 4 * hi);
-  const u32x2_t up = *(const u32x2_t*)(row + t0 + 8 + 4 * hi);
-  const u32x4_t v = {lo[0], lo[1], up[0], up[1]};
-  return __builtin_bit_cast(bf16x8_t, v);
 }
 
 __device__ __forceinline__ bf16x8_t pack_operand(const f32x16_t& x, int half) {
@@ -85,23 +77,56 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const BwdParams p) {
   if (lane == 0) p.dsum_out[row] = ds;
 }
 
-// ---- dst[b][hx][e][t] = src[b][t][hx][e], zero for n <= t < npad --------------------
-__global__ __launch_bounds__(256) void bwd_transpose_kernel(const uint16_t* __restrict__ src,
-                                                            uint16_t* __restrict__ dst, int n, int npad, int HX,
-                                                            int D) {
-  __shared__ uint16_t tile[64][66];
-  const int t0 = blockIdx.x * 64, e0 = blockIdx.y * 64;
-  const int b = blockIdx.z / HX, hx = blockIdx.z % HX;
-  for (int idx = threadIdx.x; idx < 64 * 64; idx += 256) {
-    const int tt = idx >> 6, ee = idx & 63;
-    const int t = t0 + tt;
-    tile[tt][ee] = t < n ? src[(((long)b * n + t) * HX + hx) * D + e0 + ee] : (uint16_t)0;
+// ---- MFMA-operand copies ----------------------------------------------------------------
+// One thread per 16-byte piece. Row-blocked piece (bh, tb, kk), lane l:
+// token tb*32 + l%32, dims kk*16 + 8(l/32) + 0..7. Column-blocked piece
+// (bh, db, ts), lane l: dim db*32 + l%32, tokens ts*16 + 4(l/32) + 0..3 and
+// ts*16 + 8 + 4(l/32) + 0..3. Tokens >= n read as zero.
+__global__ __launch_bounds__(256) void bwd_blocks_kernel(const uint16_t* __restrict__ src, uint16_t* __restrict__ rb,
+                                                         uint16_t* __restrict__ cb, int B, int n, int npad, int HX,
+                                                         int D) {
+  const long pieces = (long)B * HX * npad * D / 8;  // per layout
+  const long idx = (long)blockIdx.x * 256 + threadIdx.x;
+  const bool col = idx >= pieces;
+  const long k = col ? idx - pieces : idx;
+  if (k >= pieces || (col ? cb == nullptr : rb == nullptr)) return;
+  const int lane = (int)(k & 63);
+  const long piece = k >> 6;
+  const int l32 = lane & 31, hi = lane >> 5;
+  if (!col) {
+    const int KK = D / 16;
+    const int kk = (int)(piece % KK);
+    const long rest = piece / KK;
+    const int tb = (int)(rest % (npad / 32));
+    const long bh = rest / (npad / 32);
+    const int b = (int)(bh / HX), hx = (int)(bh % HX);
+    const int t = tb * 32 + l32;
+    u32x4_t v = {0u, 0u, 0u, 0u};
+    if (t < n) v = *(const u32x4_t*)(src + (((long)b * n + t) * HX + hx) * D + kk * 16 + hi * 8);
+    *(u32x4_t*)(rb + k * 8) = v;
+  } else {
+    const int TS = npad / 16;
+    const int ts = (int)(piece % TS);
+    const long rest = piece / TS;
+    const int db = (int)(rest % (D / 32));
+    const long bh = rest / (D / 32);
+    const int b = (int)(bh / HX), hx = (int)(bh % HX);
+    const int e = db * 32 + l32;
+    uint16_t h16[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int t = ts * 16 + (j < 4 ? 4 * hi + j : 8 + 4 * hi + j - 4);
+      h16[j] = t < n ? src[(((long)b * n + t) * HX + hx) * D + e] : (uint16_t)0;
+    }
+    u32x4_t v;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) v[j] = (uint32_t)h16[2 * j] | ((uint32_t)h16[2 * j + 1] << 16);
+    *(u32x4_t*)(cb + k * 8) = v;
   }
-  __syncthreads();
-  for (int idx = threadIdx.x; idx < 64 * 64; idx += 256) {
-    const int ee = idx >> 6, tt = idx & 63;
-    dst[(((long)b * HX + hx) * D + e0 + ee) * npad + t0 + tt] = tile[tt][ee];
-  }
+}
+
+__device__ __forceinline__ bf16x8_t piece(const uint16_t* base, long index, int lane) {
+  return *(const bf16x8_t*)(base + (index * 64 + lane) * 8);
 }
 
 // ---- dq-hat: one wave per (b, h, 32 queries, DP output dims) --------------------------
@@ -109,9 +134,9 @@ __global__ __launch_bounds__(256) void bwd_transpose_kernel(const uint16_t* __re
 // dS^T is the B operand of dQ^T += K^T dS^T.
 template <int D, int DP>
 __global__ __launch_bounds__(256) void bwd_dq_kernel(const BwdParams p) {
-  constexpr int NPASS = D / DP;
+  constexpr int NPASS = D / DP, KK = D / 16, DB = D / 32;
   const int lane = threadIdx.x & 63, l32 = lane & 31, hi = lane >> 5;
-  const int nqb = (p.n + 31) / 32;
+  const int nqb = (p.n + 31) / 32, NB = p.npad / 32, TS = p.npad / 16;
   const long total = (long)p.B * p.H * nqb * NPASS;
   const long wi = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (wi >= total) return;
@@ -121,27 +146,23 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(const BwdParams p) {
   const int bh = (int)(rest % ((long)p.B * p.H));
   const int qb = nqb - 1 - (int)(rest / ((long)p.B * p.H));
   const int b = bh / p.H, h = bh % p.H, g = h / p.grp;
+  const long bg = (long)b * p.G + g;
   const int d0 = pass * DP;
-  const int q0 = qb * 32;
-  const int query = q0 + l32;
-  const int qrow = min(query, p.n - 1);
-  const long qoff = ((long)b * p.n + qrow) * p.H + h;
+  const int query = qb * 32 + l32;
+  const long qoff = ((long)b * p.n + min(query, p.n - 1)) * p.H + h;
   const float lse = p.lse[qoff], dsum = p.dsum[qoff];
-  const uint16_t* qp = p.qh + qoff * D + hi * 8;
-  const uint16_t* yp = p.dy + qoff * D + hi * 8;
+  const long qpiece = ((long)bh * NB + qb) * KK;
   f32x16_t acc[DP / 32];
 #pragma unroll
   for (int mb = 0; mb < DP / 32; ++mb) acc[mb] = f32x16_t{};
   for (int kt = 0; kt <= qb; ++kt) {
     const int k0 = kt * 32;
-    const int krow = min(k0 + l32, p.n - 1);
-    const uint16_t* kp = p.kh + (((long)b * p.n + krow) * p.G + g) * D + hi * 8;
-    const uint16_t* vp = p.v + (((long)b * p.n + krow) * p.G + g) * D + hi * 8;
+    const long kpiece = (bg * NB + kt) * KK;
     f32x16_t s = f32x16_t{}, dp = f32x16_t{};
 #pragma unroll 4
-    for (int kk = 0; kk < D / 16; ++kk) {
-      s = mfma32(*(const bf16x8_t*)(kp + kk * 16), *(const bf16x8_t*)(qp + kk * 16), s);
-      dp = mfma32(*(const bf16x8_t*)(vp + kk * 16), *(const bf16x8_t*)(yp + kk * 16), dp);
+    for (int kk = 0; kk < KK; ++kk) {
+      s = mfma32(piece(p.k_rb, kpiece + kk, lane), piece(p.q_rb, qpiece + kk, lane), s);
+      dp = mfma32(piece(p.v_rb, kpiece + kk, lane), piece(p.dy_rb, qpiece + kk, lane), dp);
     }
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
@@ -153,9 +174,9 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(const BwdParams p) {
     const bf16x8_t ds0 = pack_operand(s, 0), ds1 = pack_operand(s, 1);
 #pragma unroll
     for (int mb = 0; mb < DP / 32; ++mb) {
-      const uint16_t* kt_row = p.khT + (((long)b * p.G + g) * D + d0 + mb * 32 + l32) * p.npad;
-      acc[mb] = mfma32(perm_operand(kt_row, k0, hi), ds0, acc[mb]);
-      acc[mb] = mfma32(perm_operand(kt_row, k0 + 16, hi), ds1, acc[mb]);
+      const long cpiece = (bg * DB + d0 / 32 + mb) * TS + kt * 2;
+      acc[mb] = mfma32(piece(p.k_cb, cpiece, lane), ds0, acc[mb]);
+      acc[mb] = mfma32(piece(p.k_cb, cpiece + 1, lane), ds1, acc[mb]);
     }
   }
   if (query >= p.n) return;
@@ -166,81 +187,91 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(const BwdParams p) {
     for (int i = 0; i < 16; ++i) dst[mb * 32 + (i >> 2) * 8 + hi * 4 + (i & 3)] = acc[mb][i] * p.scale;
 }
 
-// ---- dk-hat and dv: one wave per (b, g, 32 keys, DP output dims) ------------------------
+// ---- per-head dk-hat and dv: one wave per (b, h, 32 keys, DP output dims) ----------------
 // S = Q K^T and dP = dy V^T put the key in the accumulator column, so P and
-// dS are the B operands of dV^T += dy^T P and dK^T += Q^T dS.
+// dS are the B operands of dV^T += dy^T P and dK^T += Q^T dS. The group's
+// heads write separate partials (summed afterwards, in a fixed order).
 template <int D, int DP>
-__global__ __launch_bounds__(256) void bwd_dkv_kernel(const BwdParams p) {
-  constexpr int NPASS = D / DP;
+__global__ __launch_bounds__(256, 2) void bwd_dkv_kernel(const BwdParams p) {
+  constexpr int NPASS = D / DP, KK = D / 16, DB = D / 32;
   const int lane = threadIdx.x & 63, l32 = lane & 31, hi = lane >> 5;
-  const int nkb = (p.n + 31) / 32;
-  const long total = (long)p.B * p.G * nkb * NPASS;
+  const int nkb = (p.n + 31) / 32, NB = p.npad / 32, TS = p.npad / 16;
+  const long total = (long)p.B * p.H * nkb * NPASS;
   const long wi = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (wi >= total) return;
   // heaviest (first) key blocks first
   const int pass = (int)(wi % NPASS);
   const long rest = wi / NPASS;
-  const int bg = (int)(rest % ((long)p.B * p.G));
-  const int kb = (int)(rest / ((long)p.B * p.G));
-  const int b = bg / p.G, g = bg % p.G;
+  const int bh = (int)(rest % ((long)p.B * p.H));
+  const int kb = (int)(rest / ((long)p.B * p.H));
+  const int b = bh / p.H, h = bh % p.H, g = h / p.grp;
+  const long bg = (long)b * p.G + g;
   const int d0 = pass * DP;
-  const int k0 = kb * 32;
-  const int key = k0 + l32;
-  const int krow = min(key, p.n - 1);
-  const uint16_t* kp = p.kh + (((long)b * p.n + krow) * p.G + g) * D + hi * 8;
-  const uint16_t* vp = p.v + (((long)b * p.n + krow) * p.G + g) * D + hi * 8;
+  const int key = kb * 32 + l32;
+  const long kpiece = (bg * NB + kb) * KK;
   f32x16_t dv[DP / 32], dk[DP / 32];
 #pragma unroll
   for (int mb = 0; mb < DP / 32; ++mb) dv[mb] = dk[mb] = f32x16_t{};
-  const int nqt = (p.n + 31) / 32;
-  for (int hh = 0; hh < p.grp; ++hh) {
-    const int h = g * p.grp + hh;
-    for (int qt = kb; qt < nqt; ++qt) {
-      const int q0 = qt * 32;
-      const int qrow = min(q0 + l32, p.n - 1);
-      const long qoff = ((long)b * p.n + qrow) * p.H + h;
-      const uint16_t* qp = p.qh + qoff * D + hi * 8;
-      const uint16_t* yp = p.dy + qoff * D + hi * 8;
-      f32x16_t s = f32x16_t{}, dp = f32x16_t{};
+  for (int qt = kb; qt < nkb; ++qt) {
+    const int q0 = qt * 32;
+    const long qpiece = ((long)bh * NB + qt) * KK;
+    f32x16_t s = f32x16_t{}, dp = f32x16_t{};
 #pragma unroll 4
-      for (int kk = 0; kk < D / 16; ++kk) {
-        s = mfma32(*(const bf16x8_t*)(qp + kk * 16), *(const bf16x8_t*)(kp + kk * 16), s);
-        dp = mfma32(*(const bf16x8_t*)(yp + kk * 16), *(const bf16x8_t*)(vp + kk * 16), dp);
-      }
-      f32x16_t pm;
+    for (int kk = 0; kk < KK; ++kk) {
+      s = mfma32(piece(p.q_rb, qpiece + kk, lane), piece(p.k_rb, kpiece + kk, lane), s);
+      dp = mfma32(piece(p.dy_rb, qpiece + kk, lane), piece(p.v_rb, kpiece + kk, lane), dp);
+    }
+    // this lane's query row statistics, handed to the lanes whose slots hold that row
+    const long ro = ((long)b * p.n + min(q0 + l32, p.n - 1)) * p.H + h;
+    const float lse_l = p.lse[ro], dsum_l = p.dsum[ro];
+    f32x16_t pm;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int query = q0 + (i >> 2) * 8 + hi * 4 + (i & 3);
-        const bool valid = key <= query && query < p.n;
-        const long ro = ((long)b * p.n + min(query, p.n - 1)) * p.H + h;
-        const float pv = valid ? __builtin_amdgcn_exp2f(s[i] * p.scale_log2 - p.lse[ro]) : 0.f;
-        pm[i] = pv;
-        s[i] = pv * (dp[i] - p.dsum[ro]);  // dS
-      }
-      const bf16x8_t p0 = pack_operand(pm, 0), p1 = pack_operand(pm, 1);
-      const bf16x8_t ds0 = pack_operand(s, 0), ds1 = pack_operand(s, 1);
+    for (int i = 0; i < 16; ++i) {
+      const int r = (i >> 2) * 8 + hi * 4 + (i & 3);
+      const float lse = __shfl(lse_l, r, 64), dsum = __shfl(dsum_l, r, 64);
+      const int query = q0 + r;
+      const bool valid = key <= query && query < p.n;
+      const float pv = valid ? __builtin_amdgcn_exp2f(s[i] * p.scale_log2 - lse) : 0.f;
+      pm[i] = pv;
+      s[i] = pv * (dp[i] - dsum);  // dS
+    }
+    const bf16x8_t p0 = pack_operand(pm, 0), p1 = pack_operand(pm, 1);
+    const bf16x8_t ds0 = pack_operand(s, 0), ds1 = pack_operand(s, 1);
 #pragma unroll
-      for (int mb = 0; mb < DP / 32; ++mb) {
-        const long trow = ((long)b * p.H + h) * D + d0 + mb * 32 + l32;
-        const uint16_t* yt = p.dyT + trow * p.npad;
-        const uint16_t* qt_row = p.qhT + trow * p.npad;
-        dv[mb] = mfma32(perm_operand(yt, q0, hi), p0, dv[mb]);
-        dv[mb] = mfma32(perm_operand(yt, q0 + 16, hi), p1, dv[mb]);
-        dk[mb] = mfma32(perm_operand(qt_row, q0, hi), ds0, dk[mb]);
-        dk[mb] = mfma32(perm_operand(qt_row, q0 + 16, hi), ds1, dk[mb]);
-      }
+    for (int mb = 0; mb < DP / 32; ++mb) {
+      const long cpiece = ((long)bh * DB + d0 / 32 + mb) * TS + qt * 2;
+      dv[mb] = mfma32(piece(p.dy_cb, cpiece, lane), p0, dv[mb]);
+      dv[mb] = mfma32(piece(p.dy_cb, cpiece + 1, lane), p1, dv[mb]);
+      dk[mb] = mfma32(piece(p.q_cb, cpiece, lane), ds0, dk[mb]);
+      dk[mb] = mfma32(piece(p.q_cb, cpiece + 1, lane), ds1, dk[mb]);
     }
   }
   if (key >= p.n) return;
-  const long ko = (((long)b * p.n + key) * p.G + g) * D + d0;
+  const long ko = (((long)b * p.n + key) * p.H + h) * D + d0;
 #pragma unroll
   for (int mb = 0; mb < DP / 32; ++mb)
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int e = mb * 32 + (i >> 2) * 8 + hi * 4 + (i & 3);
-      p.dkh[ko + e] = dk[mb][i] * p.scale;
-      p.dv[ko + e] = f32_to_bf16_bits(dv[mb][i]);
+      p.dkp[ko + e] = dk[mb][i] * p.scale;
+      p.dvp[ko + e] = dv[mb][i];
     }
+}
+
+// dv[b, j, g] = the group's per-head partials summed in head order, bf16
+__global__ __launch_bounds__(256) void bwd_dv_sum_kernel(const float* __restrict__ dvp, uint16_t* __restrict__ dv,
+                                                         int B, int n, int H, int G, int D) {
+  const long idx = (long)blockIdx.x * 256 + threadIdx.x;
+  const long total = (long)B * n * G * D;
+  if (idx >= total) return;
+  const int e = (int)(idx % D);
+  const long r = idx / D;  // (b*n + j)*G + g
+  const long t = r / G;
+  const int g = (int)(r % G), grp = H / G;
+  const float* src = dvp + (t * H + (long)g * grp) * D + e;
+  float acc = 0.f;
+  for (int hh = 0; hh < grp; ++hh) acc += src[(long)hh * D];
+  dv[idx] = f32_to_bf16_bits(acc);
 }
 
 // ---- through RoPE and RMSNorm: each wave takes rows w, w + nwaves, ... ----------------
@@ -261,8 +292,12 @@ __global__ __launch_bounds__(256) void bwd_norm_rope_kernel(const BwdNormParams 
     const int i = (int)(t % p.n);
     const int pos = p.positions ? p.positions[t] : i;
     float gr[EPL];
+    const float* gsrc = p.grad + (t * p.HX * p.gsum + (row - t * p.HX) * p.gsum) * D + lane;
 #pragma unroll
-    for (int m = 0; m < EPL; ++m) gr[m] = p.grad[row * D + lane + 64 * m];
+    for (int m = 0; m < EPL; ++m) gr[m] = 0.f;
+    for (int hh = 0; hh < p.gsum; ++hh)
+#pragma unroll
+      for (int m = 0; m < EPL; ++m) gr[m] += gsrc[(long)hh * D + 64 * m];
     if (half > 0) {
       // the previous row's reads of stage come before these writes
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -358,11 +393,20 @@ hipError_t launch_bwd_pre(const BwdParams& p, int D, hipStream_t s) {
   }
 }
 
-hipError_t launch_bwd_transpose(const uint16_t* src, uint16_t* dst, int B, int n, int npad, int HX, int D,
-                                hipStream_t s) {
-  if (B == 0 || npad == 0) return hipSuccess;
-  const dim3 grid((unsigned)(npad / 64), (unsigned)(D / 64), (unsigned)(B * HX));
-  hipLaunchKernelGGL(bwd_transpose_kernel, grid, dim3(256), 0, s, src, dst, n, npad, HX, D);
+hipError_t launch_bwd_blocks(const uint16_t* src, uint16_t* rb, uint16_t* cb, int B, int n, int npad, int HX, int D,
+                             hipStream_t s) {
+  const long pieces = (long)B * HX * npad * D / 8;
+  if (pieces == 0) return hipSuccess;
+  hipLaunchKernelGGL(bwd_blocks_kernel, dim3((unsigned)((2 * pieces + 255) / 256)), dim3(256), 0, s, src, rb, cb, B,
+                     n, npad, HX, D);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_dv_sum(const float* dvp, uint16_t* dv, int B, int n, int H, int G, int D, hipStream_t s) {
+  const long total = (long)B * n * G * D;
+  if (total == 0) return hipSuccess;
+  hipLaunchKernelGGL(bwd_dv_sum_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, dvp, dv, B, n, H, G,
+                     D);
   return hipGetLastError();
 }
 
@@ -378,7 +422,7 @@ static hipError_t launch_dq_d(const BwdParams& p, hipStream_t s) {
 template <int D>
 static hipError_t launch_dkv_d(const BwdParams& p, hipStream_t s) {
   constexpr int DP = D < 128 ? D : 128;
-  const long waves = (long)p.B * p.G * ((p.n + 31) / 32) * (D / DP);
+  const long waves = (long)p.B * p.H * ((p.n + 31) / 32) * (D / DP);
   if (waves == 0) return hipSuccess;
   hipLaunchKernelGGL((bwd_dkv_kernel<D, DP>), dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, s, p);
   return hipGetLastError();

@@ -127,21 +127,25 @@ struct DecodeParams {
 
 constexpr int kDecodeChunk = 512;  // keys per decode split
 
-// Backward of the prefill (bf16). Row-major workspace copies: qh [B,n,H,d],
-// kh [B,n,G,d] (q-hat, k-hat), y [B,n,H,d] (ungated attention output), dy
-// [B,n,H,d] (gradient of y); transposed copies qhT, dyT [B,H,d,npad] and khT
-// [B,G,d,npad] (zero past n); lse, dsum [B,n,H] fp32 (log2-domain
-// log-sum-exp of each score row; rowsum(dy * y)); dqh [B,n,H,d] and dkh
-// [B,n,G,d] fp32 (gradients of q-hat and k-hat).
+// Backward of the prefill (bf16). Row-major workspace copies: y [B,n,H,d]
+// (ungated attention output), dy [B,n,H,d] (gradient of y); lse, dsum
+// [B,n,H] fp32 (log2-domain log-sum-exp of each score row; rowsum(dy * y)).
+// MFMA-operand copies (bf16, zero past n, npad tokens): row-blocked
+// ("rb": 32 tokens x 16 dims per 1 KiB piece, lane l holding token l%32,
+// dims 8(l/32)..+8) of q-hat, dy [B,H] and k-hat, v [B,G]; column-blocked
+// ("cb": 32 dims x 16 tokens per piece, lane l holding dim l%32, tokens
+// 4(l/32)+0..3 and 8+4(l/32)+0..3) of q-hat, dy [B,H] and k-hat [B,G].
+// Outputs: dqh [B,n,H,d] fp32; per-head partial dk-hat and dv, dkp and dvp
+// [B,n,H,d] fp32 (summed over each group's heads afterwards).
 struct BwdParams {
-  const uint16_t* qh;
-  const uint16_t* kh;
-  const uint16_t* v;
+  const uint16_t* q_rb;
+  const uint16_t* q_cb;
+  const uint16_t* k_rb;
+  const uint16_t* k_cb;
+  const uint16_t* v_rb;
+  const uint16_t* dy_rb;
+  const uint16_t* dy_cb;
   const uint16_t* y;
-  const uint16_t* dy;
-  const uint16_t* qhT;
-  const uint16_t* khT;
-  const uint16_t* dyT;
   const uint16_t* dout;
   const uint16_t* gate;
   const float* lse;
@@ -150,17 +154,20 @@ struct BwdParams {
   float* dsum_out;      // pre kernel: dsum
   uint16_t* dgate;      // pre kernel: gradient of the gate logits (or null)
   float* dqh;
-  float* dkh;
-  uint16_t* dv;
+  float* dkp;
+  float* dvp;
   int B, n, npad, H, G, grp, gate_mode;
   float scale, scale_log2;
 };
 
 // Gradient of x through n = RoPE(RMSNorm(x, w)) for rows [B, n, HX, d]:
 // grad (fp32 gradient of n) -> dx (bf16); per-workgroup partial sums of the
-// weight gradient in wpart [gridDim.x][d] when w is not null.
+// weight gradient in wpart [gridDim.x][d] when w is not null. The gradient
+// of row (t, x) is the sum of gsum rows (t, x*gsum + 0..gsum-1) of grad
+// [B, n, HX*gsum, d] (the per-head partials of a KV head; gsum = 1 for q).
 struct BwdNormParams {
   const float* grad;
+  int gsum;
   const uint16_t* x;
   const float* w;
   const int* positions;
@@ -172,8 +179,11 @@ struct BwdNormParams {
 };
 
 hipError_t launch_bwd_pre(const BwdParams& p, int D, hipStream_t s);
-hipError_t launch_bwd_transpose(const uint16_t* src, uint16_t* dst, int B, int n, int npad, int HX, int D,
-                                hipStream_t s);
+// MFMA-operand copies of src [B, n, HX, D]: row-blocked and/or column-blocked (null skips)
+hipError_t launch_bwd_blocks(const uint16_t* src, uint16_t* rb, uint16_t* cb, int B, int n, int npad, int HX, int D,
+                             hipStream_t s);
+// dv [B,n,G,D] bf16 = sum of the group's per-head partials dvp [B,n,H,D]
+hipError_t launch_bwd_dv_sum(const float* dvp, uint16_t* dv, int B, int n, int H, int G, int D, hipStream_t s);
 hipError_t launch_bwd_dq(const BwdParams& p, int D, hipStream_t s);
 hipError_t launch_bwd_dkv(const BwdParams& p, int D, hipStream_t s);
 hipError_t launch_bwd_norm_rope(const BwdNormParams& p, int nwg, hipStream_t s);

@@ -313,10 +313,11 @@ ga_status ga_decode_merge(const ga_attn_desc* desc, const void* q, const void* k
 /* ---- backward (training) -------------------------------------------------- */
 
 /* Workspace ga_prefill_backward needs (256-byte aligned): bf16 copies of
- * q-hat, k-hat, the ungated attention output y and its gradient dy (row-major
- * and, for q-hat, k-hat and dy, transposed with the token index innermost,
- * padded to a multiple of 64 tokens), fp32 row statistics, fp32 gradients of
- * q-hat and k-hat, and 2 x 512 x d floats of weight-gradient partials. */
+ * q-hat, k-hat, the ungated attention output y and its gradient dy, of q-hat,
+ * k-hat, v and dy laid out in MFMA operand order (padded to a multiple of 64
+ * tokens), fp32 row statistics, fp32 gradients of q-hat and per-head partial
+ * gradients of k-hat and v, and 2 x 512 x d floats of weight-gradient
+ * partials (about 24 x B*n*H*d bytes for the configs). */
 size_t ga_prefill_backward_workspace_bytes(const ga_attn_desc* desc, int32_t seq_len);
 
 /* Backward of ga_prefill: the gradients of sum(dout * out) with respect to

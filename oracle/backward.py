@@ -151,3 +151,77 @@ def prefill_backward(q, k, v, gate, dout, *, gate_mode: str, q_norm_w, k_norm_w,
     dq, dwq = rms_norm_backward(q, q_norm_w, rms_eps, dqn, dtype)
     dk, dwk = rms_norm_backward(k, k_norm_w, rms_eps, dkn, dtype)
     return dict(dq=dq, dk=dk, dv=dv, dgate=dgate, dq_norm_w=dwq, dk_norm_w=dwk, y=y)
+
+
+def backward_rows(q, k, v, gate, dout, *, q_rows, k_rows, gate_mode: str, q_norm_w, k_norm_w, positions,
+                  rms_eps: float = 1e-6, rope_base: float = 10000.0, rot_dim: int = 0,
+                  scale: Optional[float] = None, dtype=np.float64) -> dict:
+    """The gradients of selected rows only, for sizes where the whole
+    backward is too expensive on the CPU (the same definition, row by row).
+
+    q_rows: (b, i, h) -> dq[b, i, h] and dgate[b, i, h] (elementwise: [d],
+    headwise: a scalar); k_rows: (b, j, g) -> dk[b, j, g] and dv[b, j, g],
+    which need every query row i >= j of the group's heads (cheap for keys
+    near the end of the sequence)."""
+    q = np.asarray(q)
+    B, n, H, d = q.shape
+    G = np.asarray(k).shape[2]
+    grp = H // G
+    sc = dtype(_default_scale(d, scale))
+    pos = np.asarray(positions)
+    z_all = None if gate is None else np.asarray(gate)
+    dout = np.asarray(dout, dtype=dtype).reshape(B, n, H, d)
+    cache = {}
+
+    def khat(b, g):
+        if ("k", b, g) not in cache:
+            kn = rms_norm(np.asarray(k)[b, :, g][:, None, :], k_norm_w, rms_eps, dtype)
+            cache[("k", b, g)] = rope(kn, pos[b], rot_dim, rope_base, dtype)[:, 0, :]
+        return cache[("k", b, g)]
+
+    def qhat_row(b, i, h):
+        qn = rms_norm(q[b, i, h][None, None, :], q_norm_w, rms_eps, dtype)
+        return rope(qn, pos[b, i:i + 1], rot_dim, rope_base, dtype)[0, 0]
+
+    def row(b, i, h):
+        """P row, y, dy, dP row and dS row of query (b, i, h)."""
+        g = h // grp
+        kh = khat(b, g)[: i + 1]
+        vv = np.asarray(v, dtype=dtype)[b, : i + 1, g]
+        qv = qhat_row(b, i, h)
+        p = softmax_rows(((kh @ qv) * sc)[None, :], dtype)[0]
+        y = p @ vv
+        if gate_mode == GATE_ELEMENTWISE:
+            dy = dout[b, i, h] * sigmoid(z_all[b, i, h], dtype)
+        elif gate_mode == GATE_HEADWISE:
+            dy = dout[b, i, h] * sigmoid(z_all[b, i, h], dtype)
+        else:
+            dy = dout[b, i, h]
+        dp = vv @ dy
+        ds = p * (dp - np.sum(p * dp))
+        return qv, kh, p, y, dy, ds
+
+    out = {"dq": [], "dgate": [], "dk": [], "dv": []}
+    for (b, i, h) in q_rows:
+        qv, kh, p, y, dy, ds = row(b, i, h)
+        dqh = (ds @ kh) * sc
+        dqn = rope_backward(dqh[None, None, :], pos[b, i:i + 1], rot_dim, rope_base, dtype)[0, 0]
+        dq, _ = rms_norm_backward(q[b, i, h][None, :], q_norm_w, rms_eps, dqn[None, :], dtype)
+        out["dq"].append(dq[0])
+        if gate_mode != GATE_NONE:
+            _, dz = gate_backward(y[None, None, :], np.asarray(z_all[b, i, h])[None, None],
+                                  dout[b, i, h][None, None, :], gate_mode, dtype)
+            out["dgate"].append(dz[0, 0])
+    for (b, j, g) in k_rows:
+        dkh = np.zeros(d, dtype=dtype)
+        dvj = np.zeros(d, dtype=dtype)
+        for h in range(g * grp, (g + 1) * grp):
+            for i in range(j, n):
+                qv, kh, p, y, dy, ds = row(b, i, h)
+                dvj += p[j] * dy
+                dkh += ds[j] * qv * sc
+        dkn = rope_backward(dkh[None, None, :], pos[b, j:j + 1], rot_dim, rope_base, dtype)[0, 0]
+        dk, _ = rms_norm_backward(np.asarray(k)[b, j, g][None, :], k_norm_w, rms_eps, dkn[None, :], dtype)
+        out["dk"].append(dk[0])
+        out["dv"].append(dvj)
+    return {key: np.array(val) for key, val in out.items()}

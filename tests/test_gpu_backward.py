@@ -83,3 +83,37 @@ def test_backward_is_deterministic():
     torch.cuda.synchronize()
     for name in a:
         assert torch.equal(a[name], b[name]), name
+
+
+def test_backward_full_workload_sampled():
+    """The 4096-token workload the bench times: sampled dq / dgate rows, dk /
+    dv rows of keys near the end (every query row they need), and the column
+    sums of dV, which equal the sums of dy over each group's heads whatever
+    the size (each softmax row sums to one)."""
+    w = inputs.WORKLOADS["qwen35_0p8b_prefill"]
+    print(f"[backward] {w.name} full size", flush=True)
+    et = tdt(w)
+    x = inputs.make_prefill(w)
+    dout = inputs.round_bf16(np.random.default_rng(w.seed + 70).standard_normal(
+        (w.batch, w.seq_len, w.n_q_heads * w.head_dim)).astype(np.float32))
+    got = api.ga_prefill_backward(desc_for(w), dev(x["q"], et), dev(x["k"], et), dev(x["v"], et), dev(dout, et),
+                                  gate=dev(x["gate"], et), q_norm_w=dev(x["q_norm_w"]), k_norm_w=dev(x["k_norm_w"]),
+                                  positions=dev(x["positions"]))
+    torch.cuda.synchronize()
+    q_rows = [(0, 0, 0), (0, 1, 7), (0, 1000, 3), (0, 2049, 4), (0, 4095, 5)]
+    k_rows = [(0, 4095, 0), (0, 4090, 1), (0, 4064, 0)]
+    want = BW.backward_rows(x["q"], x["k"], x["v"], x["gate"], dout, q_rows=q_rows, k_rows=k_rows,
+                            gate_mode=w.gate_mode, q_norm_w=x["q_norm_w"], k_norm_w=x["k_norm_w"],
+                            positions=x["positions"], rms_eps=w.rms_eps, rope_base=w.rope_base, rot_dim=w.rot_dim)
+    dq, dgate, dk, dv = (host(got[k_]) for k_ in ("dq", "dgate", "dk", "dv"))
+    _assert_rel(np.stack([dq[b, i, h] for b, i, h in q_rows]), want["dq"], "dq rows")
+    _assert_rel(np.stack([dgate[b, i, h] for b, i, h in q_rows]), want["dgate"], "dgate rows")
+    _assert_rel(np.stack([dk[b, j, g] for b, j, g in k_rows]), want["dk"], "dk rows")
+    _assert_rel(np.stack([dv[b, j, g] for b, j, g in k_rows]), want["dv"], "dv rows")
+    # sum over keys of dV = sum over queries and the group's heads of dy = dout * sigmoid(z)
+    sig = 1.0 / (1.0 + np.exp(-x["gate"].astype(np.float64)))
+    dy = dout.reshape(x["gate"].shape).astype(np.float64) * sig
+    grp = w.n_q_heads // w.n_kv_heads
+    for g in range(w.n_kv_heads):
+        want_sum = dy[0, :, g * grp:(g + 1) * grp].sum(axis=(0, 1))
+        _assert_rel(dv[0, :, g].sum(axis=0), want_sum, f"column sums of dv, group {g}")

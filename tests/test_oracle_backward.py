@@ -131,3 +131,20 @@ def test_norm_and_rope_backward_pieces():
     gb = BW.rope_backward(g[:, :, None, :], pos, 8, 10000.0)
     np.testing.assert_allclose(A.rope(gb, pos, 8, 10000.0), g[:, :, None, :], atol=1e-13)
     assert dw.shape == (8,) and dx.shape == x.shape
+
+
+@pytest.mark.parametrize("gate_mode", [A.GATE_ELEMENTWISE, A.GATE_HEADWISE])
+def test_backward_rows_equal_the_whole_backward(gate_mode):
+    x = _setup(69, gate_mode, B=2, n=9, H=4, G=2, d=8, rot=4)
+    kw = dict(gate_mode=gate_mode, q_norm_w=x["wq"], k_norm_w=x["wk"], positions=x["pos"], rms_eps=1e-3,
+              rope_base=100.0, rot_dim=4)
+    full = BW.prefill_backward(x["q"], x["k"], x["v"], x["gate"], x["dout"], **kw)
+    qr = [(0, 0, 0), (1, 8, 3), (0, 5, 2)]
+    kr = [(1, 8, 1), (0, 6, 0), (1, 0, 1)]
+    rows = BW.backward_rows(x["q"], x["k"], x["v"], x["gate"], x["dout"], q_rows=qr, k_rows=kr, **kw)
+    for r, (b, i, h) in enumerate(qr):
+        np.testing.assert_allclose(rows["dq"][r], full["dq"][b, i, h], rtol=1e-10, atol=1e-12)
+        np.testing.assert_allclose(rows["dgate"][r], full["dgate"][b, i, h], rtol=1e-10, atol=1e-12)
+    for r, (b, j, g) in enumerate(kr):
+        np.testing.assert_allclose(rows["dk"][r], full["dk"][b, j, g], rtol=1e-10, atol=1e-12)
+        np.testing.assert_allclose(rows["dv"][r], full["dv"][b, j, g], rtol=1e-10, atol=1e-12)
