@@ -643,13 +643,18 @@ ga_status ga_prefill_backward(const ga_attn_desc* desc, int32_t seq_len, const v
     pp.H = H;
     pp.G = G;
     pp.grp = H / G;
-    pp.TB = 128 / pp.grp;
+    // the mirrored kernel where it serves the shape (no RoPE left to apply), else the simple one
+    ga_attn_desc sd = *desc;
+    sd.rot_dim = 0;
+    sd.gate_mode = GA_GATE_NONE;
+    const bool mirror = prefill_v2_ok(&sd, n, n) && (long long)B * n * H < (1LL << 31);
+    pp.TB = (mirror ? 64 : 128) / pp.grp;
     pp.nblk = (n + pp.TB - 1) / pp.TB;
     pp.use_table = 1;
     pp.scale_log2 = scale_of(desc) * 1.4426950408889634f;
     if ((long long)pp.B * G * pp.nblk > 0x7fffffffLL) return fail(GA_ERR_UNSUPPORTED, "grid too large");
-    if ((st = hip_status(launch_prefill_mfma(pp, D, GA_GATE_NONE, s), "backward forward-stats launch")) != GA_OK)
-      return st;
+    const hipError_t e = mirror ? launch_prefill_v2(pp, D, GA_GATE_NONE, s) : launch_prefill_mfma(pp, D, GA_GATE_NONE, s);
+    if ((st = hip_status(e, "backward forward-stats launch")) != GA_OK) return st;
   }
   BwdParams bp;
   memset(&bp, 0, sizeof(bp));

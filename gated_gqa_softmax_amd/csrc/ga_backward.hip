@@ -362,8 +362,10 @@ __global__ __launch_bounds__(256) void bwd_reduce_rows_kernel(const float* part,
   const int e = blockIdx.x * 64 + (threadIdx.x & 63);
   const int w = threadIdx.x >> 6;
   float s = 0.f;
-  if (e < d)
+  if (e < d) {
+#pragma unroll 8
     for (int r = w; r < nrows; r += 4) s += part[(long)r * d + e];
+  }
   red[w][threadIdx.x & 63] = s;
   __syncthreads();
   if (w == 0 && e < d) out[e] = (red[0][threadIdx.x] + red[1][threadIdx.x]) + (red[2][threadIdx.x] + red[3][threadIdx.x]);

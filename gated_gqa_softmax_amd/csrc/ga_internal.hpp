@@ -72,8 +72,8 @@ struct PrefillParams {
   float* part_lse;
   unsigned* sync;
   int split, nunits, npairs, split_ovh;
-  // simple kernel only: log2-domain log-sum-exp of each output row (b, token,
-  // head), for the backward pass; null otherwise
+  // log2-domain log-sum-exp of each output row (b, token, head), for the
+  // backward pass (simple kernel; mirrored kernel without a gate); null otherwise
   float* lse;
   double inv_freq[kMaxHalfRot];
 };

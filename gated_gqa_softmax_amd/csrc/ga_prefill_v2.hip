@@ -113,7 +113,7 @@ __device__ __forceinline__ int v2_unit_stages(int u, int TB, int n) { return (mi
 // CHUNK: a chunk against a cache (per-sequence key offsets and real-row counts
 // from p.key_base / p.row_lens); a separate instantiation, so the
 // whole-sequence kernel carries none of it.
-template <int D, int GATE, bool SPLIT, bool CHUNK = false>
+template <int D, int GATE, bool SPLIT, bool CHUNK = false, bool LSE = false>
 __global__ __launch_bounds__(512) void prefill_v2_kernel(const PrefillParams p) {
   typedef MirrorShape<D> S;
   static_assert(4 * 32 * D * 4 <= S::BUF_BYTES, "the phase merge reuses the stage buffers");
@@ -502,6 +502,7 @@ __global__ __launch_bounds__(512) void prefill_v2_kernel(const PrefillParams p) 
     // a row of a partial key range may see no key at all (l = 0): output 0, weight 0
     const float inv_l = (l_run > 0.f) ? 1.0f / l_run : 0.f;
     if (SPLIT && hi == 0) lse_x[rg][l32] = (l_run > 0.f) ? mt + log2f(l_run) : -INFINITY;
+    if (LSE && hi == 0) lse_x[rg][l32] = mt + log2f(l_run);  // stored with the rows below
     // lane (l32, hi) holds row l32, elements mb*32 + ig*8 + hi*4 + [0, 4)
 #pragma unroll
     for (int mb = 0; mb < D / 32; ++mb)
@@ -590,6 +591,7 @@ __global__ __launch_bounds__(512) void prefill_v2_kernel(const PrefillParams p) 
     const f32x4_t y0 = *(const f32x4_t*)(xr + lr * D + (((2 * qc) ^ (lr & 15)) << 2));
     const f32x4_t y1 = *(const f32x4_t*)(xr + lr * D + (((2 * qc + 1) ^ (lr & 15)) << 2));
     float y[8] = {y0[0], y0[1], y0[2], y0[3], y1[0], y1[1], y1[2], y1[3]};
+    if (LSE && qc == 0) p.lse[er] = lse_x[rg][lr];  // the row statistics for the backward pass
     if (SPLIT && GATE == 2) graw[it] = *(const u32x4_t*)(p.gate + (long)er * p.gs + qc * 8);
     if (SPLIT && GATE == 1) ghead[it] = p.gate[(long)er * p.gs];
     if (SPLIT && merge) {
@@ -664,8 +666,12 @@ static hipError_t launch_v2_d(const PrefillParams& p, int gate_mode, hipStream_t
     const int npairs = (p.nblk + 1) / 2;
     const long grid = (long)p.B * p.G * npairs;
     if (grid <= 0) return hipSuccess;
-    if (p.key_base) launch_v2_gate<D, false, true>(p, gate_mode, grid, s);
-    else launch_v2_gate<D, false>(p, gate_mode, grid, s);
+    if (p.key_base)
+      launch_v2_gate<D, false, true>(p, gate_mode, grid, s);
+    else if (p.lse)  // ungated output with the row statistics, for the backward pass
+      hipLaunchKernelGGL((prefill_v2_kernel<D, 0, false, false, true>), dim3((unsigned)grid), dim3(512), 0, s, p);
+    else
+      launch_v2_gate<D, false>(p, gate_mode, grid, s);
   }
   return hipGetLastError();
 }
