@@ -132,26 +132,36 @@ __device__ __forceinline__ bf16x8_t piece(const uint16_t* base, long index, int 
 // ---- dq-hat: one wave per (b, h, 32 queries, DP output dims) --------------------------
 // S^T = K Q^T and dP^T = V dy^T put the query in the accumulator column, so
 // dS^T is the B operand of dQ^T += K^T dS^T.
+// A workgroup holds the NPASS dim slices of 4 / NPASS consecutive heads of
+// one query block; each head's q-hat and dy operands sit in LDS for its slices.
 template <int D, int DP>
 __global__ __launch_bounds__(256) void bwd_dq_kernel(const BwdParams p) {
-  constexpr int NPASS = D / DP, KK = D / 16, DB = D / 32;
-  const int lane = threadIdx.x & 63, l32 = lane & 31, hi = lane >> 5;
+  constexpr int NPASS = D / DP, KK = D / 16, DB = D / 32, HPW = 4 / NPASS;
+  __shared__ __attribute__((aligned(16))) uint16_t qy_lds[HPW][2][KK * 64 * 8];
+  const int lane = threadIdx.x & 63, l32 = lane & 31, hi = lane >> 5, w = threadIdx.x >> 6;
   const int nqb = (p.n + 31) / 32, NB = p.npad / 32, TS = p.npad / 16;
-  const long total = (long)p.B * p.H * nqb * NPASS;
-  const long wi = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (wi >= total) return;
+  const int hgroups = (p.H + HPW - 1) / HPW;
   // heaviest (last) query blocks first
-  const int pass = (int)(wi % NPASS);
-  const long rest = wi / NPASS;
-  const int bh = (int)(rest % ((long)p.B * p.H));
-  const int qb = nqb - 1 - (int)(rest / ((long)p.B * p.H));
-  const int b = bh / p.H, h = bh % p.H, g = h / p.grp;
+  const int hgi = (int)(blockIdx.x % ((long)p.B * hgroups));
+  const int qb = nqb - 1 - (int)(blockIdx.x / ((long)p.B * hgroups));
+  const int b = hgi / hgroups, h0 = (hgi % hgroups) * HPW;
+  for (int i = threadIdx.x; i < HPW * KK * 64; i += 256) {
+    const int hs = i / (KK * 64), j = i % (KK * 64);
+    const int hq = min(h0 + hs, p.H - 1);
+    const long qp = (((long)b * p.H + hq) * NB + qb) * KK;
+    *(u32x4_t*)(qy_lds[hs][0] + j * 8) = *(const u32x4_t*)(p.q_rb + (qp * 64 + j) * 8);
+    *(u32x4_t*)(qy_lds[hs][1] + j * 8) = *(const u32x4_t*)(p.dy_rb + (qp * 64 + j) * 8);
+  }
+  __syncthreads();
+  const int hs = w / NPASS, pass = w % NPASS;
+  const int h = h0 + hs;
+  if (h >= p.H) return;  // (no barrier follows)
+  const int bh = b * p.H + h, g = h / p.grp;
   const long bg = (long)b * p.G + g;
   const int d0 = pass * DP;
   const int query = qb * 32 + l32;
   const long qoff = ((long)b * p.n + min(query, p.n - 1)) * p.H + h;
   const float lse = p.lse[qoff], dsum = p.dsum[qoff];
-  const long qpiece = ((long)bh * NB + qb) * KK;
   f32x16_t acc[DP / 32];
 #pragma unroll
   for (int mb = 0; mb < DP / 32; ++mb) acc[mb] = f32x16_t{};
@@ -161,8 +171,8 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(const BwdParams p) {
     f32x16_t s = f32x16_t{}, dp = f32x16_t{};
 #pragma unroll 4
     for (int kk = 0; kk < KK; ++kk) {
-      s = mfma32(piece(p.k_rb, kpiece + kk, lane), piece(p.q_rb, qpiece + kk, lane), s);
-      dp = mfma32(piece(p.v_rb, kpiece + kk, lane), piece(p.dy_rb, qpiece + kk, lane), dp);
+      s = mfma32(piece(p.k_rb, kpiece + kk, lane), *(const bf16x8_t*)(qy_lds[hs][0] + (kk * 64 + lane) * 8), s);
+      dp = mfma32(piece(p.v_rb, kpiece + kk, lane), *(const bf16x8_t*)(qy_lds[hs][1] + (kk * 64 + lane) * 8), dp);
     }
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
@@ -190,25 +200,35 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(const BwdParams p) {
 // ---- per-head dk-hat and dv: one wave per (b, h, 32 keys, DP output dims) ----------------
 // S = Q K^T and dP = dy V^T put the key in the accumulator column, so P and
 // dS are the B operands of dV^T += dy^T P and dK^T += Q^T dS. The group's
-// heads write separate partials (summed afterwards, in a fixed order).
+// heads write separate partials (summed afterwards, in a fixed order). A
+// workgroup holds the NPASS dim slices of HPW heads of one key block, which
+// share that block's k-hat and v operands through LDS.
 template <int D, int DP>
 __global__ __launch_bounds__(256, 2) void bwd_dkv_kernel(const BwdParams p) {
-  constexpr int NPASS = D / DP, KK = D / 16, DB = D / 32;
-  const int lane = threadIdx.x & 63, l32 = lane & 31, hi = lane >> 5;
+  constexpr int NPASS = D / DP, KK = D / 16, DB = D / 32, HPW = 4 / NPASS;
+  __shared__ __attribute__((aligned(16))) uint16_t kv_lds[2][KK * 64 * 8];
+  const int lane = threadIdx.x & 63, l32 = lane & 31, hi = lane >> 5, w = threadIdx.x >> 6;
   const int nkb = (p.n + 31) / 32, NB = p.npad / 32, TS = p.npad / 16;
-  const long total = (long)p.B * p.H * nkb * NPASS;
-  const long wi = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (wi >= total) return;
+  const int hgroups = (p.grp + HPW - 1) / HPW;
   // heaviest (first) key blocks first
-  const int pass = (int)(wi % NPASS);
-  const long rest = wi / NPASS;
-  const int bh = (int)(rest % ((long)p.B * p.H));
-  const int kb = (int)(rest / ((long)p.B * p.H));
-  const int b = bh / p.H, h = bh % p.H, g = h / p.grp;
-  const long bg = (long)b * p.G + g;
+  const int hg = (int)(blockIdx.x % hgroups);
+  const long rest = blockIdx.x / hgroups;
+  const int bgi = (int)(rest % ((long)p.B * p.G));
+  const int kb = (int)(rest / ((long)p.B * p.G));
+  const int b = bgi / p.G, g = bgi % p.G;
+  const long bg = bgi;
+  const int pass = w % NPASS, hh = hg * HPW + w / NPASS;
+  const long kpiece = (bg * NB + kb) * KK;
+  for (int i = threadIdx.x; i < KK * 64; i += 256) {
+    *(u32x4_t*)(kv_lds[0] + i * 8) = *(const u32x4_t*)(p.k_rb + (kpiece * 64 + i) * 8);
+    *(u32x4_t*)(kv_lds[1] + i * 8) = *(const u32x4_t*)(p.v_rb + (kpiece * 64 + i) * 8);
+  }
+  __syncthreads();
+  if (hh >= p.grp) return;  // (no barrier follows)
+  const int h = g * p.grp + hh;
+  const int bh = b * p.H + h;
   const int d0 = pass * DP;
   const int key = kb * 32 + l32;
-  const long kpiece = (bg * NB + kb) * KK;
   f32x16_t dv[DP / 32], dk[DP / 32];
 #pragma unroll
   for (int mb = 0; mb < DP / 32; ++mb) dv[mb] = dk[mb] = f32x16_t{};
@@ -218,8 +238,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dkv_kernel(const BwdParams p) {
     f32x16_t s = f32x16_t{}, dp = f32x16_t{};
 #pragma unroll 4
     for (int kk = 0; kk < KK; ++kk) {
-      s = mfma32(piece(p.q_rb, qpiece + kk, lane), piece(p.k_rb, kpiece + kk, lane), s);
-      dp = mfma32(piece(p.dy_rb, qpiece + kk, lane), piece(p.v_rb, kpiece + kk, lane), dp);
+      s = mfma32(piece(p.q_rb, qpiece + kk, lane), *(const bf16x8_t*)(kv_lds[0] + (kk * 64 + lane) * 8), s);
+      dp = mfma32(piece(p.dy_rb, qpiece + kk, lane), *(const bf16x8_t*)(kv_lds[1] + (kk * 64 + lane) * 8), dp);
     }
     // this lane's query row statistics, handed to the lanes whose slots hold that row
     const long ro = ((long)b * p.n + min(q0 + l32, p.n - 1)) * p.H + h;
@@ -414,19 +434,19 @@ hipError_t launch_bwd_dv_sum(const float* dvp, uint16_t* dv, int B, int n, int H
 
 template <int D>
 static hipError_t launch_dq_d(const BwdParams& p, hipStream_t s) {
-  constexpr int DP = D < 128 ? D : 128;
-  const long waves = (long)p.B * p.H * ((p.n + 31) / 32) * (D / DP);
-  if (waves == 0) return hipSuccess;
-  hipLaunchKernelGGL((bwd_dq_kernel<D, DP>), dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, s, p);
+  constexpr int DP = D < 128 ? D : 128, HPW = 4 / (D / DP);
+  const long wgs = (long)p.B * ((p.H + HPW - 1) / HPW) * ((p.n + 31) / 32);
+  if (wgs == 0) return hipSuccess;
+  hipLaunchKernelGGL((bwd_dq_kernel<D, DP>), dim3((unsigned)wgs), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 
 template <int D>
 static hipError_t launch_dkv_d(const BwdParams& p, hipStream_t s) {
-  constexpr int DP = D < 128 ? D : 128;
-  const long waves = (long)p.B * p.H * ((p.n + 31) / 32) * (D / DP);
-  if (waves == 0) return hipSuccess;
-  hipLaunchKernelGGL((bwd_dkv_kernel<D, DP>), dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, s, p);
+  constexpr int DP = D < 128 ? D : 128, HPW = 4 / (D / DP);
+  const long wgs = (long)p.B * p.G * ((p.n + 31) / 32) * ((p.grp + HPW - 1) / HPW);
+  if (wgs == 0) return hipSuccess;
+  hipLaunchKernelGGL((bwd_dkv_kernel<D, DP>), dim3((unsigned)wgs), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 
