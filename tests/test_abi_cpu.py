@@ -279,3 +279,29 @@ def test_binding_reads_head_strides_from_views():
         hs(torch.zeros(B, n, H, d), 2, H + 1, d)                          # wrong head count
     with pytest.raises(ValueError):
         hs(torch.zeros(B, 2 * n, H, 2 * d)[:, ::2, :, :d], 2, H, d)       # tokens two rows apart
+
+
+def test_backward_rejects_bad_arguments():
+    lib = _lib_or_build()
+    d = _desc(batch=1)
+    need = lib.ga_prefill_backward_workspace_bytes(ctypes.byref(d), 64)
+    assert need > 0 and need % 256 == 0
+
+    def call(desc=d, n=64, q=A16, gate=A16, dgate=A16, ws=A16, ws_bytes=1 << 40, dq=A16):
+        return lib.ga_prefill_backward(ctypes.byref(desc), n, q, A16, A16, gate, None, None, None, A16, dq, A16,
+                                       A16, dgate, None, None, ws, ws_bytes, None)
+
+    assert call(n=-1) == _lib.GA_ERR_BAD_SHAPE
+    assert call(q=None) == _lib.GA_ERR_NULL_ARG
+    assert call(dq=MIS) == _lib.GA_ERR_MISALIGNED
+    assert call(gate=None) == _lib.GA_ERR_NULL_ARG                 # elementwise gate needs the gate
+    assert call(dgate=None) == _lib.GA_ERR_NULL_ARG                # ... and its gradient
+    assert call(ws_bytes=need - 256) == _lib.GA_ERR_WORKSPACE
+    assert call(ws=A16 + 16) == _lib.GA_ERR_MISALIGNED             # the workspace is 256-byte aligned
+    assert call(desc=_desc(dtype=_lib.GA_F32)) == _lib.GA_ERR_UNSUPPORTED
+    assert call(desc=_desc(head_dim=96, rot_dim=16)) == _lib.GA_ERR_UNSUPPORTED
+    assert call(desc=_desc(gate_act=_lib.GA_ACT_SILU)) == _lib.GA_ERR_UNSUPPORTED
+    assert call(desc=_desc(q_head_stride=512)) == _lib.GA_ERR_UNSUPPORTED
+    # empty inputs are a no-op, even without buffers
+    assert call(n=0, q=None, ws=None, ws_bytes=0) == _lib.GA_OK
+    assert call(desc=_desc(batch=0), q=None, ws=None, ws_bytes=0) == _lib.GA_OK

@@ -173,3 +173,11 @@ def test_flop_counts_match_brute_force_pair_counts():
     pairs = sum(L + i + 1 for L in lens for i in range(n))
     assert accounting.chunk_prefill_flops(lens, H, d, n) == H * 4 * d * pairs
     assert accounting.chunk_prefill_flops([0], H, d, n) == accounting.causal_prefill_flops(1, H, d, n)
+
+
+def test_backward_flop_count_is_five_products_per_pair():
+    # q.k recomputed, dy.v, P^T dy, dS^T q, dS k: 2d flops each per visible pair per query head
+    H, d = 3, 8
+    for n in (1, 5, 12):
+        pairs = sum(i + 1 for i in range(n))
+        assert accounting.causal_backward_flops(2, H, d, n) == 2 * H * pairs * 5 * 2 * d
