@@ -282,9 +282,22 @@ def ga_prefill_chunk_kernel(desc: AttnDesc, seq_len: int, cache_cap: int) -> str
     return _lib.load().ga_prefill_chunk_kernel(ctypes.byref(desc), seq_len, cache_cap).decode()
 
 
+def ga_prefill_chunk_workspace_bytes(desc: AttnDesc, seq_len: int, cache_cap: int, max_cache_len: int) -> int:
+    return int(_lib.load().ga_prefill_chunk_workspace_bytes(ctypes.byref(desc), seq_len, cache_cap, max_cache_len))
+
+
+def _chunk_workspace(desc, n, cap, max_cache_len, device, workspace):
+    """(pointer, bytes) of the chunk workspace, allocated here when not given."""
+    nbytes = ga_prefill_chunk_workspace_bytes(desc, n, cap, int(max_cache_len))
+    if nbytes == 0:
+        return None, 0, None
+    workspace = _workspace(nbytes, device, workspace)
+    return _ptr(workspace, "workspace"), workspace.numel(), workspace
+
+
 def ga_prefill_chunk(desc: AttnDesc, q, k, v, k_cache, v_cache, cache_lens, max_cache_len: int, gate=None,
                      q_norm_w=None, k_norm_w=None, positions=None, chunk_lens=None, out=None,
-                     stream=None) -> torch.Tensor:
+                     workspace=None, stream=None) -> torch.Tensor:
     """Chunk of seq_len new rows per sequence after cache_lens[b] cached tokens.
 
     Writes K-hat/V of the real rows to cache slots [L_b, L_b + n_b) and the
@@ -297,12 +310,13 @@ def ga_prefill_chunk(desc: AttnDesc, q, k, v, k_cache, v_cache, cache_lens, max_
     if out is None:
         out = torch.zeros((B, n, desc.n_q_heads * desc.head_dim), dtype=et, device=q.device)
     d2, qp, gp = _qg(desc, q, gate, 2, et)
+    wp, wb, _keep = _chunk_workspace(d2, n, k_cache.shape[1], max_cache_len, q.device, workspace)
     st = lib.ga_prefill_chunk(ctypes.byref(d2), n, qp, _ptr(k, "k", et), _ptr(v, "v", et),
                               gp, _ptr(q_norm_w, "q_norm_w", torch.float32),
                               _ptr(k_norm_w, "k_norm_w", torch.float32), _ptr(positions, "positions", torch.int32),
                               _ptr(k_cache, "k_cache", et), _ptr(v_cache, "v_cache", et), k_cache.shape[1],
                               _ptr(cache_lens, "cache_lens", torch.int32), _ptr(chunk_lens, "chunk_lens", torch.int32),
-                              int(max_cache_len), _ptr(out, "out", et), _stream(stream))
+                              int(max_cache_len), wp, wb, _ptr(out, "out", et), _stream(stream))
     _check(st, "ga_prefill_chunk")
     return out
 
@@ -322,7 +336,7 @@ def ga_prefill_chunk_keys(desc: AttnDesc, k, v, k_cache, v_cache, cache_lens, ma
 
 
 def ga_prefill_chunk_attention(desc: AttnDesc, q, k_cache, v_cache, cache_lens, max_cache_len: int, gate=None,
-                               q_norm_w=None, positions=None, chunk_lens=None, out=None,
+                               q_norm_w=None, positions=None, chunk_lens=None, out=None, workspace=None,
                                stream=None) -> torch.Tensor:
     lib = _lib.load()
     et = _elem_dtype(desc)
@@ -330,12 +344,13 @@ def ga_prefill_chunk_attention(desc: AttnDesc, q, k_cache, v_cache, cache_lens, 
     if out is None:
         out = torch.zeros((B, n, desc.n_q_heads * desc.head_dim), dtype=et, device=q.device)
     d2, qp, gp = _qg(desc, q, gate, 2, et)
+    wp, wb, _keep = _chunk_workspace(d2, n, k_cache.shape[1], max_cache_len, q.device, workspace)
     st = lib.ga_prefill_chunk_attention(ctypes.byref(d2), n, qp, _ptr(k_cache, "k_cache", et),
                                         _ptr(v_cache, "v_cache", et), k_cache.shape[1],
                                         _ptr(cache_lens, "cache_lens", torch.int32),
                                         _ptr(chunk_lens, "chunk_lens", torch.int32), int(max_cache_len),
                                         gp, _ptr(q_norm_w, "q_norm_w", torch.float32),
-                                        _ptr(positions, "positions", torch.int32), _ptr(out, "out", et),
+                                        _ptr(positions, "positions", torch.int32), wp, wb, _ptr(out, "out", et),
                                         _stream(stream))
     _check(st, "ga_prefill_chunk_attention")
     return out

@@ -376,6 +376,38 @@ bool chunk_uses_mirror(const ga_attn_desc* d, int32_t n, int32_t cache_cap) {
          (long long)d->batch * n * d->n_q_heads < (1LL << 31);
 }
 
+// Cached prefixes of different lengths give the chunk's workgroups different
+// amounts of work: on request (GA_PREFILL_CHUNK_SPLIT=1, read at each call)
+// each mirrored pair's key range is cut in two workgroups whose partial rows
+// meet in the workspace, when the cache may hold a stage of keys. Opt-in: on
+// the measured chunk workload the two prologues and epilogues per pair and the
+// split instantiation's register spills cost more than the balance gains.
+bool chunk_split(const ga_attn_desc* d, int32_t n, int32_t cap, int32_t max_cache_len) {
+  const char* e = getenv("GA_PREFILL_CHUNK_SPLIT");
+  if (!e || strcmp(e, "1")) return false;
+  return chunk_uses_mirror(d, n, cap) && !gate_ext(d) && max_cache_len >= 64;
+}
+
+int chunk_npairs(const ga_attn_desc* d, int32_t n) {
+  const int tb = 64 / (d->n_q_heads / d->n_kv_heads);
+  return ((n + tb - 1) / tb + 1) / 2;
+}
+
+size_t chunk_ws_bytes(const ga_attn_desc* d, int32_t n, int32_t cap, int32_t max_cache_len) {
+  if (d->batch <= 0 || n <= 0 || !chunk_split(d, n, cap, max_cache_len)) return 0;
+  return prefill_split_bytes((long)d->batch * d->n_kv_heads * chunk_npairs(d, n), d->head_dim);
+}
+
+ga_status check_chunk_workspace(const ga_attn_desc* d, int32_t n, int32_t cap, int32_t max_cache_len,
+                                const void* workspace, size_t workspace_bytes) {
+  const size_t need = chunk_ws_bytes(d, n, cap, max_cache_len);
+  if (need == 0) return GA_OK;
+  if (!workspace || workspace_bytes < need)
+    return fail(GA_ERR_WORKSPACE, "workspace %zu bytes < %zu required", workspace ? workspace_bytes : 0, need);
+  if (!aligned(workspace, 256)) return fail(GA_ERR_MISALIGNED, "workspace is not 256-byte aligned");
+  return GA_OK;
+}
+
 ga_status check_chunk_common(const ga_attn_desc* desc, int32_t n, const void* k_cache, const void* v_cache,
                              int32_t cache_cap, const int32_t* cache_lens, int32_t max_cache_len) {
   ga_status st;
@@ -394,7 +426,7 @@ ga_status check_chunk_common(const ga_attn_desc* desc, int32_t n, const void* k_
 ga_status chunk_attn_impl(const ga_attn_desc* desc, int32_t n, const void* q, const void* k_cache,
                           const void* v_cache, int32_t cap, const int32_t* cache_lens, const int32_t* chunk_lens,
                           int32_t max_cache_len, const void* gate, const float* q_norm_w, const int32_t* positions,
-                          void* out, hipStream_t stream) {
+                          void* workspace, void* out, hipStream_t stream) {
   const int H = desc->n_q_heads, G = desc->n_kv_heads, d = desc->head_dim;
   const int grp = H / G;
   if (chunk_uses_mirror(desc, n, cap)) {
@@ -429,6 +461,16 @@ ga_status chunk_attn_impl(const ga_attn_desc* desc, int32_t n, const void* q, co
     pp.scale_log2 = scale_of(desc) * 1.4426950408889634f;
     fill_inv_freq(desc, pp.inv_freq);
     if ((long long)pp.B * G * pp.nblk > 0x7fffffffLL) return fail(GA_ERR_UNSUPPORTED, "grid too large");
+    if (chunk_split(desc, n, cap, max_cache_len)) {
+      pp.npairs = chunk_npairs(desc, n);
+      const size_t slots = (size_t)pp.B * G * pp.npairs;
+      auto r256 = [](size_t x) { return (x + 255) / 256 * 256; };
+      char* base = (char*)workspace;
+      pp.part = (float*)base;
+      pp.part_lse = (float*)(base + r256(slots * 128 * d * 4));
+      pp.sync = (unsigned*)(base + r256(slots * 128 * d * 4) + r256(slots * 128 * 4));
+      pp.split = 1;
+    }
     return hip_status(launch_prefill_v2(pp, d, gate_arg(desc), stream), "chunk attention launch");
   }
   NaiveParams np;
@@ -831,6 +873,12 @@ const char* ga_prefill_chunk_kernel(const ga_attn_desc* desc, int32_t seq_len, i
   return chunk_uses_mirror(desc, seq_len, cache_cap) ? "mirror" : "generic";
 }
 
+size_t ga_prefill_chunk_workspace_bytes(const ga_attn_desc* desc, int32_t seq_len, int32_t cache_cap,
+                                        int32_t max_cache_len) {
+  if (check_desc(desc) != GA_OK || seq_len < 0 || cache_cap < 0 || max_cache_len < 0) return 0;
+  return chunk_ws_bytes(desc, seq_len, cache_cap, max_cache_len);
+}
+
 ga_status ga_prefill_chunk_keys(const ga_attn_desc* desc, int32_t seq_len, const void* k, const void* v,
                                 const float* k_norm_w, const int32_t* positions, const int32_t* cache_lens,
                                 const int32_t* chunk_lens, int32_t max_cache_len, void* k_cache, void* v_cache,
@@ -850,7 +898,8 @@ ga_status ga_prefill_chunk_keys(const ga_attn_desc* desc, int32_t seq_len, const
 ga_status ga_prefill_chunk_attention(const ga_attn_desc* desc, int32_t seq_len, const void* q, const void* k_cache,
                                      const void* v_cache, int32_t cache_cap, const int32_t* cache_lens,
                                      const int32_t* chunk_lens, int32_t max_cache_len, const void* gate,
-                                     const float* q_norm_w, const int32_t* positions, void* out, void* stream) {
+                                     const float* q_norm_w, const int32_t* positions, void* workspace,
+                                     size_t workspace_bytes, void* out, void* stream) {
   ga_status st;
   if ((st = check_desc(desc)) != GA_OK) return st;
   if (seq_len < 0) return fail(GA_ERR_BAD_SHAPE, "seq_len %d < 0", seq_len);
@@ -860,15 +909,18 @@ ga_status ga_prefill_chunk_attention(const ga_attn_desc* desc, int32_t seq_len, 
   if ((st = check_gate(gate, desc)) != GA_OK) return st;
   if ((st = check_chunk_common(desc, seq_len, k_cache, v_cache, cache_cap, cache_lens, max_cache_len)) != GA_OK)
     return st;
+  if ((st = check_chunk_workspace(desc, seq_len, cache_cap, max_cache_len, workspace, workspace_bytes)) != GA_OK)
+    return st;
   return chunk_attn_impl(desc, seq_len, q, k_cache, v_cache, cache_cap, cache_lens, chunk_lens, max_cache_len,
-                         desc->gate_mode == GA_GATE_NONE ? nullptr : gate, q_norm_w, positions, out,
+                         desc->gate_mode == GA_GATE_NONE ? nullptr : gate, q_norm_w, positions, workspace, out,
                          (hipStream_t)stream);
 }
 
 ga_status ga_prefill_chunk(const ga_attn_desc* desc, int32_t seq_len, const void* q, const void* k, const void* v,
                            const void* gate, const float* q_norm_w, const float* k_norm_w, const int32_t* positions,
                            void* k_cache, void* v_cache, int32_t cache_cap, const int32_t* cache_lens,
-                           const int32_t* chunk_lens, int32_t max_cache_len, void* out, void* stream) {
+                           const int32_t* chunk_lens, int32_t max_cache_len, void* workspace,
+                           size_t workspace_bytes, void* out, void* stream) {
   ga_status st;
   if ((st = check_desc(desc)) != GA_OK) return st;
   if (seq_len < 0) return fail(GA_ERR_BAD_SHAPE, "seq_len %d < 0", seq_len);
@@ -880,12 +932,14 @@ ga_status ga_prefill_chunk(const ga_attn_desc* desc, int32_t seq_len, const void
   if ((st = check_gate(gate, desc)) != GA_OK) return st;
   if ((st = check_chunk_common(desc, seq_len, k_cache, v_cache, cache_cap, cache_lens, max_cache_len)) != GA_OK)
     return st;
+  if ((st = check_chunk_workspace(desc, seq_len, cache_cap, max_cache_len, workspace, workspace_bytes)) != GA_OK)
+    return st;
   hipStream_t s = (hipStream_t)stream;
   if ((st = prefill_keys_impl(desc, seq_len, k, v, k_norm_w, positions, k_cache, v_cache, cache_cap, s, cache_lens,
                               chunk_lens, max_cache_len)) != GA_OK)
     return st;
   return chunk_attn_impl(desc, seq_len, q, k_cache, v_cache, cache_cap, cache_lens, chunk_lens, max_cache_len,
-                         desc->gate_mode == GA_GATE_NONE ? nullptr : gate, q_norm_w, positions, out, s);
+                         desc->gate_mode == GA_GATE_NONE ? nullptr : gate, q_norm_w, positions, workspace, out, s);
 }
 
 int32_t ga_decode_split_keys(void) { return kDecodeChunk; }

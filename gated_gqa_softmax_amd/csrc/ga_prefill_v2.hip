@@ -164,10 +164,24 @@ __global__ __launch_bounds__(512) void prefill_v2_kernel(const PrefillParams p) 
   //    to first. Pieces shrink along that order, so the compute units that
   //    finish a short tail first take the longest light units: each pair's
   //    work, s_h + s_l stages, is shared by two compute units.
+  //  * chunk split mode (SPLIT and CHUNK): mirrored pairs whose key range is
+  //    cut in two halves of its stages, head and tail in two workgroups;
+  //    launch order: pair-major, the heads then the tails of every (b, g).
   int blk_light, blk_heavy, st_lo = 0, st_hi = 0x7fffffff, seg_slot = -1;
   if (!SPLIT) {
     blk_heavy = nblk - 1 - pair;
     blk_light = (pair < blk_heavy) ? pair : -1;   // -1: no light block (odd middle)
+  } else if (CHUNK) {
+    const int cpair = pair >> 1, part = pair & 1;
+    blk_heavy = nblk - 1 - cpair;
+    blk_light = (cpair < blk_heavy) ? cpair : -1;
+    const int s_all = (L0 + min(nb, blk_heavy * TB + TB) + S::ST - 1) / S::ST;
+    const bool split = s_all >= 2;
+    const int c = split ? (s_all + 1) / 2 : s_all;
+    if (part == 1 && !split) return;  // (no tail; the head stores its rows itself)
+    st_lo = part ? c : 0;
+    st_hi = part ? s_all : c;
+    seg_slot = split ? bg * p.npairs + cpair : -1;
   } else {
     const int U = p.nunits, P = p.npairs, L = U / 2;  // light units: i < U-1-i
     int unit;
@@ -654,14 +668,18 @@ static void launch_v2_gate(const PrefillParams& p, int gate_mode, long grid, hip
 template <int D>
 static hipError_t launch_v2_d(const PrefillParams& p, int gate_mode, hipStream_t s) {
   if (p.split) {
-    // heads and tails of the heavy units, then the light units; the arrival
-    // words start at zero
+    // whole sequences: heads and tails of the heavy units, then the light
+    // units; chunks: head and tail of every mirrored pair. The arrival words
+    // start at zero.
     const long slots = (long)p.B * p.G * p.npairs;
-    const long grid = (long)p.B * p.G * (2L * p.npairs + p.nunits / 2);
+    const long grid = p.key_base ? 2 * slots : (long)p.B * p.G * (2L * p.npairs + p.nunits / 2);
     if (grid <= 0) return hipSuccess;
     const long nwords = 2 * slots;
     hipLaunchKernelGGL(zero_words_kernel, dim3((unsigned)((nwords + 255) / 256)), dim3(256), 0, s, p.sync, nwords);
-    launch_v2_gate<D, true>(p, gate_mode, grid, s);
+    if (p.key_base)
+      launch_v2_gate<D, true, true>(p, gate_mode, grid, s);
+    else
+      launch_v2_gate<D, true>(p, gate_mode, grid, s);
   } else {
     const int npairs = (p.nblk + 1) / 2;
     const long grid = (long)p.B * p.G * npairs;

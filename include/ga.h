@@ -231,14 +231,27 @@ ga_status ga_prefill_attention(const ga_attn_desc* desc, int32_t seq_len,
  *                max_cache_len + seq_len < 2^30.
  *  cache_lens, chunk_lens  device int32 [B] (chunk_lens may be NULL).
  *  out           [B,seq_len,H*d]; rows of padding and skipped sequences are left as they were.
+ *  workspace     ga_prefill_chunk_workspace_bytes bytes, 256-byte aligned
+ *                (NULL when that is 0).
  * The library does not advance cache_lens (the caller adds n_b afterwards).
- * No workspace. Errors as for ga_prefill. */
+ * Errors as for ga_prefill. */
 ga_status ga_prefill_chunk(const ga_attn_desc* desc, int32_t seq_len,
                            const void* q, const void* k, const void* v, const void* gate,
                            const float* q_norm_w, const float* k_norm_w, const int32_t* positions,
                            void* k_cache, void* v_cache, int32_t cache_cap,
                            const int32_t* cache_lens, const int32_t* chunk_lens, int32_t max_cache_len,
-                           void* out, void* stream);
+                           void* workspace, size_t workspace_bytes, void* out, void* stream);
+
+/* Workspace of ga_prefill_chunk / ga_prefill_chunk_attention. Sequences with
+ * cached prefixes of different lengths give the mirrored kernel's workgroups
+ * different amounts of work. With GA_PREFILL_CHUNK_SPLIT=1 (read at each
+ * call; opt-in, as it measured slower), the mirrored kernel, the method's
+ * gate and max_cache_len >= 64, every mirrored pair's key range is cut in two
+ * workgroups whose partial rows meet here: 128 * (d + 1) floats + 2 words per
+ * pair of token blocks per (batch, KV head), 256-byte aligned parts. 0
+ * otherwise. */
+size_t ga_prefill_chunk_workspace_bytes(const ga_attn_desc* desc, int32_t seq_len, int32_t cache_cap,
+                                        int32_t max_cache_len);
 
 /* First stage of ga_prefill_chunk (one kernel): writes K-hat and v of the
  * real chunk rows to cache slots [L_b, L_b + n_b). */
@@ -255,7 +268,8 @@ ga_status ga_prefill_chunk_attention(const ga_attn_desc* desc, int32_t seq_len, 
                                      const void* k_cache, const void* v_cache, int32_t cache_cap,
                                      const int32_t* cache_lens, const int32_t* chunk_lens,
                                      int32_t max_cache_len, const void* gate, const float* q_norm_w,
-                                     const int32_t* positions, void* out, void* stream);
+                                     const int32_t* positions, void* workspace, size_t workspace_bytes,
+                                     void* out, void* stream);
 
 /* Name of the kernel ga_prefill_chunk_attention runs for this shape:
  * "mirror" (the mirrored prefill kernel with per-sequence key offsets) or

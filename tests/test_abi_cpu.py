@@ -226,9 +226,10 @@ def test_prefill_chunk_rejects_bad_arguments_and_names_its_kernel(monkeypatch):
     lib = _lib_or_build()
     d = _desc(batch=2)
 
-    def call(desc=d, n=64, cap=1100, max_len=1000, lens=A16, q=A16, k_cache=A16, out=A16, gate=A16):
+    def call(desc=d, n=64, cap=1100, max_len=1000, lens=A16, q=A16, k_cache=A16, out=A16, gate=A16, ws=A16,
+             ws_bytes=1 << 30):
         return lib.ga_prefill_chunk(ctypes.byref(desc), n, q, A16, A16, gate, None, None, None, k_cache, A16, cap,
-                                    lens, None, max_len, out, None)
+                                    lens, None, max_len, ws, ws_bytes, out, None)
 
     assert call(cap=1063) == _lib.GA_ERR_BAD_SHAPE             # cap < max_cache_len + seq_len
     assert call(max_len=-1) == _lib.GA_ERR_BAD_SHAPE
@@ -239,10 +240,24 @@ def test_prefill_chunk_rejects_bad_arguments_and_names_its_kernel(monkeypatch):
     assert call(n=-1) == _lib.GA_ERR_BAD_SHAPE
     assert call(max_len=(1 << 30) - 10, cap=(1 << 30) + 100) == _lib.GA_ERR_UNSUPPORTED
     assert call(desc=_desc(batch=0), q=None) == _lib.GA_OK
+    # the key-range split of long cached prefixes (opt-in) needs its workspace
+    assert lib.ga_prefill_chunk_workspace_bytes(ctypes.byref(d), 64, 1100, 1000) == 0
+    monkeypatch.setenv("GA_PREFILL_CHUNK_SPLIT", "1")
+    need = lib.ga_prefill_chunk_workspace_bytes(ctypes.byref(d), 64, 1100, 1000)
+    assert need > 0 and need % 256 == 0
+    assert call(ws=None) == _lib.GA_ERR_WORKSPACE
+    assert call(ws_bytes=need - 1) == _lib.GA_ERR_WORKSPACE
+    assert call(ws=A16 + 16) == _lib.GA_ERR_MISALIGNED
+    assert lib.ga_prefill_chunk_workspace_bytes(ctypes.byref(d), 64, 1100, 63) == 0      # no stage of cached keys
+    assert lib.ga_prefill_chunk_workspace_bytes(ctypes.byref(_desc(gate_act=_lib.GA_ACT_SILU)), 64, 1100, 1000) == 0
+    monkeypatch.setenv("GA_PREFILL_CHUNK_SPLIT", "0")
+    assert lib.ga_prefill_chunk_workspace_bytes(ctypes.byref(d), 64, 1100, 1000) == 0
+    assert call(ws=None, ws_bytes=0, lens=None) == _lib.GA_ERR_NULL_ARG                 # reaches the next check
+    monkeypatch.delenv("GA_PREFILL_CHUNK_SPLIT")
     assert lib.ga_prefill_chunk_keys(ctypes.byref(d), 64, A16, A16, None, None, None, None, 1000, A16, A16, 1100,
                                      None) == _lib.GA_ERR_NULL_ARG
     assert lib.ga_prefill_chunk_attention(ctypes.byref(d), 64, A16, A16, A16, 1000, A16, None, 1000, A16, None,
-                                          None, A16, None) == _lib.GA_ERR_BAD_SHAPE
+                                          None, A16, 1 << 30, A16, None) == _lib.GA_ERR_BAD_SHAPE
     assert lib.ga_prefill_chunk_kernel(ctypes.byref(d), 64, 1100) == b"mirror"
     assert lib.ga_prefill_chunk_kernel(ctypes.byref(_desc(dtype=_lib.GA_F32)), 64, 1100) == b"generic"
     assert lib.ga_prefill_chunk_kernel(ctypes.byref(_desc(head_dim=64, rot_dim=16)), 64, 1100) == b"generic"

@@ -104,6 +104,21 @@ def test_chunk_small(w):
     _run(w, stages=w.name.endswith("stages"))
 
 
+@pytest.mark.parametrize("split", ["1", "0"])
+def test_chunk_key_range_split_on_and_off(split, monkeypatch):
+    """The mirrored kernel with each pair's key range cut in two workgroups
+    (cached prefixes of very different lengths) and without the cut."""
+    monkeypatch.setenv("GA_PREFILL_CHUNK_SPLIT", split)
+    w = _case(f"mirror_split{split}", 4, 96, 8, 2, 256, 64, "elementwise", [0, 64, 700, 1500], [96, 50, 96, 7],
+              seed=310)
+    cap = 1500 + 96 + 2
+    want_bytes = api.ga_prefill_chunk_workspace_bytes(desc_for(w), w.seq_len, cap, 1500)
+    assert (want_bytes > 0) == (split == "1")
+    print(f"[chunk] {w.name}", flush=True)
+    _run(w, stages=True)
+    _run(w, stages=False)
+
+
 def test_chunk_forced_generic_kernel(monkeypatch):
     monkeypatch.setenv("GA_PREFILL_KERNEL", "generic")
     w = CASES[0]
