@@ -34,7 +34,7 @@ __device__ __forceinline__ f32x16_t mfma32(bf16x8_t a, bf16x8_t b, f32x16_t c) {
 
 __device__ __forceinline__ bf16x8_t pack_operand(const f32x16_t& x, int half) {
   float f[8];
-#pragma unroll 4
+#pragma unroll
   for (int j = 0; j < 8; ++j) f[j] = x[8 * half + j];
   return __builtin_bit_cast(bf16x8_t, pack8(f));
 }
@@ -50,7 +50,7 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const BwdParams p) {
   if (row >= (long)p.B * p.n * p.H) return;
   const long base = row * D + lane * EPL;
   float y[EPL], go[EPL], z[EPL];
-#pragma unroll 4
+#pragma unroll
   for (int m = 0; m < EPL; ++m) {
     y[m] = bf16_bits_to_f32(p.y[base + m]);
     go[m] = bf16_bits_to_f32(p.dout[base + m]);
@@ -59,13 +59,13 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const BwdParams p) {
   float gh = 1.f, dyy = 0.f;
   if (GATE == 1) {
     gh = sigmoid_f32(bf16_bits_to_f32(p.gate[row]));
-#pragma unroll 4
+#pragma unroll
     for (int m = 0; m < EPL; ++m) dyy += go[m] * y[m];
     dyy = sum_xor<64>(dyy);
     if (lane == 0) p.dgate[row] = f32_to_bf16_bits(dyy * gh * (1.f - gh));
   }
   float ds = 0.f;
-#pragma unroll 4
+#pragma unroll
   for (int m = 0; m < EPL; ++m) {
     const float g = GATE == 2 ? sigmoid_f32(z[m]) : gh;
     if (GATE == 2) p.dgate[base + m] = f32_to_bf16_bits(go[m] * y[m] * g * (1.f - g));
@@ -113,13 +113,13 @@ __global__ __launch_bounds__(256) void bwd_blocks_kernel(const uint16_t* __restr
     const int b = (int)(bh / HX), hx = (int)(bh % HX);
     const int e = db * 32 + l32;
     uint16_t h16[8];
-#pragma unroll 4
+#pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int t = ts * 16 + (j < 4 ? 4 * hi + j : 8 + 4 * hi + j - 4);
       h16[j] = t < n ? src[(((long)b * n + t) * HX + hx) * D + e] : (uint16_t)0;
     }
     u32x4_t v;
-#pragma unroll 4
+#pragma unroll
     for (int j = 0; j < 4; ++j) v[j] = (uint32_t)h16[2 * j] | ((uint32_t)h16[2 * j + 1] << 16);
     *(u32x4_t*)(cb + k * 8) = v;
   }
@@ -131,9 +131,10 @@ __device__ __forceinline__ bf16x8_t piece(const uint16_t* base, long index, int 
 
 // ---- dq-hat: one wave per (b, h, 32 queries, DP output dims) --------------------------
 // S^T = K Q^T and dP^T = V dy^T put the query in the accumulator column, so
-// dS^T is the B operand of dQ^T += K^T dS^T.
-// A workgroup holds the NPASS dim slices of 4 / NPASS consecutive heads of
-// one query block; each head's q-hat and dy operands sit in LDS for its slices.
+// dS^T is the B operand of dQ^T += K^T dS^T. A workgroup holds the NPASS dim
+// slices of 4 / NPASS consecutive heads and two mirrored query blocks (qb and
+// nqb - 1 - qb, so every workgroup has about the same number of key tiles);
+// each head's q-hat and dy operands of the current block sit in LDS.
 template <int D, int DP>
 __global__ __launch_bounds__(256) void bwd_dq_kernel(const BwdParams p) {
   constexpr int NPASS = D / DP, KK = D / 16, DB = D / 32, HPW = 4 / NPASS;
@@ -141,166 +142,177 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(const BwdParams p) {
   const int lane = threadIdx.x & 63, l32 = lane & 31, hi = lane >> 5, w = threadIdx.x >> 6;
   const int nqb = (p.n + 31) / 32, NB = p.npad / 32, TS = p.npad / 16;
   const int hgroups = (p.H + HPW - 1) / HPW;
-  // heaviest (last) query blocks first
   const int hgi = (int)(blockIdx.x % ((long)p.B * hgroups));
-  const int qb = nqb - 1 - (int)(blockIdx.x / ((long)p.B * hgroups));
+  const int qpair = (int)(blockIdx.x / ((long)p.B * hgroups));
   const int b = hgi / hgroups, h0 = (hgi % hgroups) * HPW;
-  for (int i = threadIdx.x; i < HPW * KK * 64; i += 256) {
-    const int hs = i / (KK * 64), j = i % (KK * 64);
-    const int hq = min(h0 + hs, p.H - 1);
-    const long qp = (((long)b * p.H + hq) * NB + qb) * KK;
-    *(u32x4_t*)(qy_lds[hs][0] + j * 8) = *(const u32x4_t*)(p.q_rb + (qp * 64 + j) * 8);
-    *(u32x4_t*)(qy_lds[hs][1] + j * 8) = *(const u32x4_t*)(p.dy_rb + (qp * 64 + j) * 8);
-  }
-  __syncthreads();
   const int hs = w / NPASS, pass = w % NPASS;
-  const int h = h0 + hs;
-  if (h >= p.H) return;  // (no barrier follows)
+  // a wave of a missing head computes on the last head and stores nothing
+  const bool active = h0 + hs < p.H;
+  const int h = min(h0 + hs, p.H - 1);
   const int bh = b * p.H + h, g = h / p.grp;
   const long bg = (long)b * p.G + g;
   const int d0 = pass * DP;
-  const int query = qb * 32 + l32;
-  const long qoff = ((long)b * p.n + min(query, p.n - 1)) * p.H + h;
-  const float lse = p.lse[qoff], dsum = p.dsum[qoff];
-  f32x16_t acc[DP / 32];
-#pragma unroll 4
-  for (int mb = 0; mb < DP / 32; ++mb) acc[mb] = f32x16_t{};
-  for (int kt = 0; kt <= qb; ++kt) {
-    const int k0 = kt * 32;
-    const long kpiece = (bg * NB + kt) * KK;
-    f32x16_t s = f32x16_t{}, dp = f32x16_t{};
-#pragma unroll 4
-    for (int kk = 0; kk < KK; ++kk) {
-      s = mfma32(piece(p.k_rb, kpiece + kk, lane), *(const bf16x8_t*)(qy_lds[hs][0] + (kk * 64 + lane) * 8), s);
-      dp = mfma32(piece(p.v_rb, kpiece + kk, lane), *(const bf16x8_t*)(qy_lds[hs][1] + (kk * 64 + lane) * 8), dp);
+  for (int half = 0; half < 2; ++half) {
+    const int qb = half == 0 ? nqb - 1 - qpair : qpair;  // heavy block first
+    if (half == 1 && qb == nqb - 1 - qpair) break;       // (odd middle block: one only)
+    __syncthreads();  // the previous block's readers of qy_lds are done
+    for (int i = threadIdx.x; i < HPW * KK * 64; i += 256) {
+      const int hsl = i / (KK * 64), j = i % (KK * 64);
+      const int hq = min(h0 + hsl, p.H - 1);
+      const long qp = (((long)b * p.H + hq) * NB + qb) * KK;
+      *(u32x4_t*)(qy_lds[hsl][0] + j * 8) = *(const u32x4_t*)(p.q_rb + (qp * 64 + j) * 8);
+      *(u32x4_t*)(qy_lds[hsl][1] + j * 8) = *(const u32x4_t*)(p.dy_rb + (qp * 64 + j) * 8);
     }
+    __syncthreads();
+    const int query = qb * 32 + l32;
+    const long qoff = ((long)b * p.n + min(query, p.n - 1)) * p.H + h;
+    const float lse = p.lse[qoff], dsum = p.dsum[qoff];
+    f32x16_t acc[DP / 32];
+#pragma unroll
+    for (int mb = 0; mb < DP / 32; ++mb) acc[mb] = f32x16_t{};
+    for (int kt = 0; kt <= qb; ++kt) {
+      const int k0 = kt * 32;
+      const long kpiece = (bg * NB + kt) * KK;
+      f32x16_t s = f32x16_t{}, dp = f32x16_t{};
 #pragma unroll 4
-    for (int i = 0; i < 16; ++i) {
-      const int key = k0 + (i >> 2) * 8 + hi * 4 + (i & 3);
-      const bool valid = key <= query && query < p.n;
-      const float pv = valid ? __builtin_amdgcn_exp2f(s[i] * p.scale_log2 - lse) : 0.f;
-      s[i] = pv * (dp[i] - dsum);  // dS^T
+      for (int kk = 0; kk < KK; ++kk) {
+        s = mfma32(piece(p.k_rb, kpiece + kk, lane), *(const bf16x8_t*)(qy_lds[hs][0] + (kk * 64 + lane) * 8), s);
+        dp = mfma32(piece(p.v_rb, kpiece + kk, lane), *(const bf16x8_t*)(qy_lds[hs][1] + (kk * 64 + lane) * 8), dp);
+      }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int key = k0 + (i >> 2) * 8 + hi * 4 + (i & 3);
+        const bool valid = key <= query && query < p.n;
+        const float pv = valid ? __builtin_amdgcn_exp2f(s[i] * p.scale_log2 - lse) : 0.f;
+        s[i] = pv * (dp[i] - dsum);  // dS^T
+      }
+      const bf16x8_t ds0 = pack_operand(s, 0), ds1 = pack_operand(s, 1);
+#pragma unroll
+      for (int mb = 0; mb < DP / 32; ++mb) {
+        const long cpiece = (bg * DB + d0 / 32 + mb) * TS + kt * 2;
+        acc[mb] = mfma32(piece(p.k_cb, cpiece, lane), ds0, acc[mb]);
+        acc[mb] = mfma32(piece(p.k_cb, cpiece + 1, lane), ds1, acc[mb]);
+      }
     }
-    const bf16x8_t ds0 = pack_operand(s, 0), ds1 = pack_operand(s, 1);
-#pragma unroll 4
-    for (int mb = 0; mb < DP / 32; ++mb) {
-      const long cpiece = (bg * DB + d0 / 32 + mb) * TS + kt * 2;
-      acc[mb] = mfma32(piece(p.k_cb, cpiece, lane), ds0, acc[mb]);
-      acc[mb] = mfma32(piece(p.k_cb, cpiece + 1, lane), ds1, acc[mb]);
+    if (active && query < p.n) {
+      float* dst = p.dqh + (((long)b * p.n + query) * p.H + h) * D + d0;
+#pragma unroll
+      for (int mb = 0; mb < DP / 32; ++mb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) dst[mb * 32 + (i >> 2) * 8 + hi * 4 + (i & 3)] = acc[mb][i] * p.scale;
     }
   }
-  if (query >= p.n) return;
-  float* dst = p.dqh + (((long)b * p.n + query) * p.H + h) * D + d0;
-#pragma unroll 4
-  for (int mb = 0; mb < DP / 32; ++mb)
-#pragma unroll 4
-    for (int i = 0; i < 16; ++i) dst[mb * 32 + (i >> 2) * 8 + hi * 4 + (i & 3)] = acc[mb][i] * p.scale;
 }
 
 // ---- per-head dk-hat and dv: one wave per (b, h, 32 keys, DP output dims) ----------------
 // S = Q K^T and dP = dy V^T put the key in the accumulator column, so P and
 // dS are the B operands of dV^T += dy^T P and dK^T += Q^T dS. The group's
 // heads write separate partials (summed afterwards, in a fixed order). A
-// workgroup holds the NPASS dim slices of HPW heads of one key block, which
-// share that block's k-hat and v operands through LDS.
+// workgroup holds the NPASS dim slices of HPW heads and two mirrored key
+// blocks (kb and nkb - 1 - kb, so every workgroup has about the same number
+// of query tiles); the current block's k-hat and v operands sit in LDS. With
+// two dim slices per head, the slices' waves (w and w ^ 1) share the tile's
+// S and dP: one computes S, the other dP, and they swap through LDS
+// (double-buffered by tile parity, one barrier per tile). Every wave runs
+// every tile so the barriers line up; a wave of a missing head computes on
+// the group's last head and stores nothing.
 template <int D, int DP>
 __global__ __launch_bounds__(256, 2) void bwd_dkv_kernel(const BwdParams p) {
   constexpr int NPASS = D / DP, KK = D / 16, DB = D / 32, HPW = 4 / NPASS;
   __shared__ __attribute__((aligned(16))) uint16_t kv_lds[2][KK * 64 * 8];
+  __shared__ __attribute__((aligned(16))) float xch[NPASS == 2 ? 2 : 1][4][16 * 64];
   const int lane = threadIdx.x & 63, l32 = lane & 31, hi = lane >> 5, w = threadIdx.x >> 6;
   const int nkb = (p.n + 31) / 32, NB = p.npad / 32, TS = p.npad / 16;
   const int hgroups = (p.grp + HPW - 1) / HPW;
-  // heaviest (first) key blocks first
   const int hg = (int)(blockIdx.x % hgroups);
   const long rest = blockIdx.x / hgroups;
   const int bgi = (int)(rest % ((long)p.B * p.G));
-  const int kb = (int)(rest / ((long)p.B * p.G));
+  const int kpair = (int)(rest / ((long)p.B * p.G));
   const int b = bgi / p.G, g = bgi % p.G;
   const long bg = bgi;
   const int pass = w % NPASS, hh = hg * HPW + w / NPASS;
-  const long kpiece = (bg * NB + kb) * KK;
-  for (int i = threadIdx.x; i < KK * 64; i += 256) {
-    *(u32x4_t*)(kv_lds[0] + i * 8) = *(const u32x4_t*)(p.k_rb + (kpiece * 64 + i) * 8);
-    *(u32x4_t*)(kv_lds[1] + i * 8) = *(const u32x4_t*)(p.v_rb + (kpiece * 64 + i) * 8);
-  }
-  __syncthreads();
-  // With two dim slices per head, the slices' waves (w and w ^ 1) share the
-  // tile's S and dP: one computes S, the other dP, and they swap through LDS
-  // (double-buffered by tile parity, one barrier per tile). Every wave runs
-  // every tile so the barriers line up; a wave of a missing head computes on
-  // the group's last head and stores nothing.
-  __shared__ __attribute__((aligned(16))) float xch[NPASS == 2 ? 2 : 1][4][16 * 64];
   const bool active = hh < p.grp;
-  if (NPASS != 2 && !active) return;  // (no barrier follows in that case)
   const int h = g * p.grp + min(hh, p.grp - 1);
   const int bh = b * p.H + h;
   const int d0 = pass * DP;
-  const int key = kb * 32 + l32;
-  f32x16_t dv[DP / 32], dk[DP / 32];
+  for (int half = 0; half < 2; ++half) {
+    const int kb = half == 0 ? kpair : nkb - 1 - kpair;  // heavy block first
+    if (half == 1 && kb == kpair) break;                 // (odd middle block: one only)
+    const long kpiece = (bg * NB + kb) * KK;
+    __syncthreads();  // the previous block's readers of kv_lds are done
+    for (int i = threadIdx.x; i < KK * 64; i += 256) {
+      *(u32x4_t*)(kv_lds[0] + i * 8) = *(const u32x4_t*)(p.k_rb + (kpiece * 64 + i) * 8);
+      *(u32x4_t*)(kv_lds[1] + i * 8) = *(const u32x4_t*)(p.v_rb + (kpiece * 64 + i) * 8);
+    }
+    __syncthreads();
+    const int key = kb * 32 + l32;
+    f32x16_t dv[DP / 32], dk[DP / 32];
+#pragma unroll
+    for (int mb = 0; mb < DP / 32; ++mb) dv[mb] = dk[mb] = f32x16_t{};
+    for (int qt = kb; qt < nkb; ++qt) {
+      const int q0 = qt * 32;
+      const long qpiece = ((long)bh * NB + qt) * KK;
+      f32x16_t s = f32x16_t{}, dp = f32x16_t{};
+      if constexpr (NPASS == 2) {
+        const uint16_t* arow = pass == 0 ? p.q_rb : p.dy_rb;
+        const uint16_t* brow = kv_lds[pass];
+        f32x16_t mine = f32x16_t{};
 #pragma unroll 4
-  for (int mb = 0; mb < DP / 32; ++mb) dv[mb] = dk[mb] = f32x16_t{};
-  for (int qt = kb; qt < nkb; ++qt) {
-    const int q0 = qt * 32;
-    const long qpiece = ((long)bh * NB + qt) * KK;
-    f32x16_t s = f32x16_t{}, dp = f32x16_t{};
-    if constexpr (NPASS == 2) {
-      const uint16_t* arow = pass == 0 ? p.q_rb : p.dy_rb;
-      const uint16_t* brow = kv_lds[pass];
-      f32x16_t mine = f32x16_t{};
+        for (int kk = 0; kk < KK; ++kk)
+          mine = mfma32(piece(arow, qpiece + kk, lane), *(const bf16x8_t*)(brow + (kk * 64 + lane) * 8), mine);
+        float* xb = xch[qt & 1][0];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) xb[(w * 16 + i) * 64 + lane] = mine[i];
+        __syncthreads();
+        f32x16_t other;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) other[i] = xb[((w ^ 1) * 16 + i) * 64 + lane];
+        s = pass == 0 ? mine : other;
+        dp = pass == 0 ? other : mine;
+      } else {
 #pragma unroll 4
-      for (int kk = 0; kk < KK; ++kk)
-        mine = mfma32(piece(arow, qpiece + kk, lane), *(const bf16x8_t*)(brow + (kk * 64 + lane) * 8), mine);
-      float* xb = xch[qt & 1][0];
-#pragma unroll 4
-      for (int i = 0; i < 16; ++i) xb[(w * 16 + i) * 64 + lane] = mine[i];
-      __syncthreads();
-      f32x16_t other;
-#pragma unroll 4
-      for (int i = 0; i < 16; ++i) other[i] = xb[((w ^ 1) * 16 + i) * 64 + lane];
-      s = pass == 0 ? mine : other;
-      dp = pass == 0 ? other : mine;
-    } else {
-#pragma unroll 4
-      for (int kk = 0; kk < KK; ++kk) {
-        s = mfma32(piece(p.q_rb, qpiece + kk, lane), *(const bf16x8_t*)(kv_lds[0] + (kk * 64 + lane) * 8), s);
-        dp = mfma32(piece(p.dy_rb, qpiece + kk, lane), *(const bf16x8_t*)(kv_lds[1] + (kk * 64 + lane) * 8), dp);
+        for (int kk = 0; kk < KK; ++kk) {
+          s = mfma32(piece(p.q_rb, qpiece + kk, lane), *(const bf16x8_t*)(kv_lds[0] + (kk * 64 + lane) * 8), s);
+          dp = mfma32(piece(p.dy_rb, qpiece + kk, lane), *(const bf16x8_t*)(kv_lds[1] + (kk * 64 + lane) * 8), dp);
+        }
+      }
+      // this lane's query row statistics, handed to the lanes whose slots hold that row
+      const long ro = ((long)b * p.n + min(q0 + l32, p.n - 1)) * p.H + h;
+      const float lse_l = p.lse[ro], dsum_l = p.dsum[ro];
+      f32x16_t pm;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int r = (i >> 2) * 8 + hi * 4 + (i & 3);
+        const float lse = __shfl(lse_l, r, 64), dsum = __shfl(dsum_l, r, 64);
+        const int query = q0 + r;
+        const bool valid = key <= query && query < p.n;
+        const float pv = valid ? __builtin_amdgcn_exp2f(s[i] * p.scale_log2 - lse) : 0.f;
+        pm[i] = pv;
+        s[i] = pv * (dp[i] - dsum);  // dS
+      }
+      const bf16x8_t p0 = pack_operand(pm, 0), p1 = pack_operand(pm, 1);
+      const bf16x8_t ds0 = pack_operand(s, 0), ds1 = pack_operand(s, 1);
+#pragma unroll
+      for (int mb = 0; mb < DP / 32; ++mb) {
+        const long cpiece = ((long)bh * DB + d0 / 32 + mb) * TS + qt * 2;
+        dv[mb] = mfma32(piece(p.dy_cb, cpiece, lane), p0, dv[mb]);
+        dv[mb] = mfma32(piece(p.dy_cb, cpiece + 1, lane), p1, dv[mb]);
+        dk[mb] = mfma32(piece(p.q_cb, cpiece, lane), ds0, dk[mb]);
+        dk[mb] = mfma32(piece(p.q_cb, cpiece + 1, lane), ds1, dk[mb]);
       }
     }
-    // this lane's query row statistics, handed to the lanes whose slots hold that row
-    const long ro = ((long)b * p.n + min(q0 + l32, p.n - 1)) * p.H + h;
-    const float lse_l = p.lse[ro], dsum_l = p.dsum[ro];
-    f32x16_t pm;
-#pragma unroll 4
-    for (int i = 0; i < 16; ++i) {
-      const int r = (i >> 2) * 8 + hi * 4 + (i & 3);
-      const float lse = __shfl(lse_l, r, 64), dsum = __shfl(dsum_l, r, 64);
-      const int query = q0 + r;
-      const bool valid = key <= query && query < p.n;
-      const float pv = valid ? __builtin_amdgcn_exp2f(s[i] * p.scale_log2 - lse) : 0.f;
-      pm[i] = pv;
-      s[i] = pv * (dp[i] - dsum);  // dS
-    }
-    const bf16x8_t p0 = pack_operand(pm, 0), p1 = pack_operand(pm, 1);
-    const bf16x8_t ds0 = pack_operand(s, 0), ds1 = pack_operand(s, 1);
-#pragma unroll 4
-    for (int mb = 0; mb < DP / 32; ++mb) {
-      const long cpiece = ((long)bh * DB + d0 / 32 + mb) * TS + qt * 2;
-      dv[mb] = mfma32(piece(p.dy_cb, cpiece, lane), p0, dv[mb]);
-      dv[mb] = mfma32(piece(p.dy_cb, cpiece + 1, lane), p1, dv[mb]);
-      dk[mb] = mfma32(piece(p.q_cb, cpiece, lane), ds0, dk[mb]);
-      dk[mb] = mfma32(piece(p.q_cb, cpiece + 1, lane), ds1, dk[mb]);
+    if (active && key < p.n) {
+      const long ko = (((long)b * p.n + key) * p.H + h) * D + d0;
+#pragma unroll
+      for (int mb = 0; mb < DP / 32; ++mb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int e = mb * 32 + (i >> 2) * 8 + hi * 4 + (i & 3);
+          p.dkp[ko + e] = dk[mb][i] * p.scale;
+          p.dvp[ko + e] = dv[mb][i];
+        }
     }
   }
-  if (!active || key >= p.n) return;
-  const long ko = (((long)b * p.n + key) * p.H + h) * D + d0;
-#pragma unroll 4
-  for (int mb = 0; mb < DP / 32; ++mb)
-#pragma unroll 4
-    for (int i = 0; i < 16; ++i) {
-      const int e = mb * 32 + (i >> 2) * 8 + hi * 4 + (i & 3);
-      p.dkp[ko + e] = dk[mb][i] * p.scale;
-      p.dvp[ko + e] = dv[mb][i];
-    }
 }
 
 // dv[b, j, g] = the group's per-head partials summed in head order, bf16
@@ -330,7 +342,7 @@ __global__ __launch_bounds__(256) void bwd_norm_rope_kernel(const BwdNormParams 
   const long nwaves = (long)gridDim.x * 4;
   const int half = p.rot / 2;
   float wacc[EPL];
-#pragma unroll 4
+#pragma unroll
   for (int m = 0; m < EPL; ++m) wacc[m] = 0.f;
   for (long row = (long)blockIdx.x * 4 + w; row < rows; row += nwaves) {
     const long t = row / p.HX;  // b * n + i
@@ -338,22 +350,22 @@ __global__ __launch_bounds__(256) void bwd_norm_rope_kernel(const BwdNormParams 
     const int pos = p.positions ? p.positions[t] : i;
     float gr[EPL];
     const float* gsrc = p.grad + (t * p.HX * p.gsum + (row - t * p.HX) * p.gsum) * D + lane;
-#pragma unroll 4
+#pragma unroll
     for (int m = 0; m < EPL; ++m) gr[m] = 0.f;
     for (int hh = 0; hh < p.gsum; ++hh)
-#pragma unroll 4
+#pragma unroll
       for (int m = 0; m < EPL; ++m) gr[m] += gsrc[(long)hh * D + 64 * m];
     if (half > 0) {
       // the previous row's reads of stage come before these writes
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-#pragma unroll 4
+#pragma unroll
       for (int m = 0; m < EPL; ++m) stage[w][lane + 64 * m] = gr[m];
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-#pragma unroll 4
+#pragma unroll
       for (int m = 0; m < EPL; ++m) {
         const int e = lane + 64 * m;
         if (e < p.rot) {
@@ -368,7 +380,7 @@ __global__ __launch_bounds__(256) void bwd_norm_rope_kernel(const BwdNormParams 
     float dx[EPL];
     if (p.w) {
       float x[EPL], ss = 0.f;
-#pragma unroll 4
+#pragma unroll
       for (int m = 0; m < EPL; ++m) {
         x[m] = bf16_bits_to_f32(p.x[row * D + lane + 64 * m]);
         ss += x[m] * x[m];
@@ -377,24 +389,24 @@ __global__ __launch_bounds__(256) void bwd_norm_rope_kernel(const BwdNormParams 
       const float r = sqrtf(ss / D + p.eps);
       const float inv_r = 1.0f / r;
       float dot = 0.f;
-#pragma unroll 4
+#pragma unroll
       for (int m = 0; m < EPL; ++m) {
         const float xh = x[m] * inv_r;
         dot += gr[m] * p.w[lane + 64 * m] * xh;
         wacc[m] += gr[m] * xh;
       }
       dot = sum_xor<64>(dot) / D;
-#pragma unroll 4
+#pragma unroll
       for (int m = 0; m < EPL; ++m) dx[m] = (gr[m] * p.w[lane + 64 * m] - x[m] * inv_r * dot) * inv_r;
     } else {
-#pragma unroll 4
+#pragma unroll
       for (int m = 0; m < EPL; ++m) dx[m] = gr[m];
     }
-#pragma unroll 4
+#pragma unroll
     for (int m = 0; m < EPL; ++m) p.dx[row * D + lane + 64 * m] = f32_to_bf16_bits(dx[m]);
   }
   if (!p.w || !p.wpart) return;  // (uniform over the workgroup)
-#pragma unroll 4
+#pragma unroll
   for (int m = 0; m < EPL; ++m) wsum[w][lane + 64 * m] = wacc[m];
   __syncthreads();
   for (int e = threadIdx.x; e < D; e += 256)
@@ -460,7 +472,7 @@ hipError_t launch_bwd_dv_sum(const float* dvp, uint16_t* dv, int B, int n, int H
 template <int D>
 static hipError_t launch_dq_d(const BwdParams& p, hipStream_t s) {
   constexpr int DP = D < 128 ? D : 128, HPW = 4 / (D / DP);
-  const long wgs = (long)p.B * ((p.H + HPW - 1) / HPW) * ((p.n + 31) / 32);
+  const long wgs = (long)p.B * ((p.H + HPW - 1) / HPW) * (((p.n + 31) / 32 + 1) / 2);  // mirrored block pairs
   if (wgs == 0) return hipSuccess;
   hipLaunchKernelGGL((bwd_dq_kernel<D, DP>), dim3((unsigned)wgs), dim3(256), 0, s, p);
   return hipGetLastError();
@@ -469,7 +481,7 @@ static hipError_t launch_dq_d(const BwdParams& p, hipStream_t s) {
 template <int D>
 static hipError_t launch_dkv_d(const BwdParams& p, hipStream_t s) {
   constexpr int DP = D < 128 ? D : 128, HPW = 4 / (D / DP);
-  const long wgs = (long)p.B * p.G * ((p.n + 31) / 32) * ((p.grp + HPW - 1) / HPW);
+  const long wgs = (long)p.B * p.G * (((p.n + 31) / 32 + 1) / 2) * ((p.grp + HPW - 1) / HPW);  // mirrored pairs
   if (wgs == 0) return hipSuccess;
   hipLaunchKernelGGL((bwd_dkv_kernel<D, DP>), dim3((unsigned)wgs), dim3(256), 0, s, p);
   return hipGetLastError();
