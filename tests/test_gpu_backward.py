@@ -117,3 +117,36 @@ def test_backward_full_workload_sampled():
     for g in range(w.n_kv_heads):
         want_sum = dy[0, :, g * grp:(g + 1) * grp].sum(axis=(0, 1))
         _assert_rel(dv[0, :, g].sum(axis=0), want_sum, f"column sums of dv, group {g}")
+
+
+def test_backward_batched_headwise_workload_sampled():
+    """The 4 x 2048-token, d = 128, headwise-gate workload: sampled rows of
+    dq, the headwise dgate, dk and dv, and the column sums of dv."""
+    w = inputs.WORKLOADS["qwen3_0p6b_batched_prefill"]
+    print(f"[backward] {w.name} full size", flush=True)
+    et = tdt(w)
+    x = inputs.make_prefill(w)
+    dout = inputs.round_bf16(np.random.default_rng(w.seed + 71).standard_normal(
+        (w.batch, w.seq_len, w.n_q_heads * w.head_dim)).astype(np.float32))
+    got = api.ga_prefill_backward(desc_for(w), dev(x["q"], et), dev(x["k"], et), dev(x["v"], et), dev(dout, et),
+                                  gate=dev(x["gate"], et), q_norm_w=dev(x["q_norm_w"]), k_norm_w=dev(x["k_norm_w"]),
+                                  positions=dev(x["positions"]))
+    torch.cuda.synchronize()
+    n = w.seq_len
+    q_rows = [(0, 0, 0), (1, 1, 15), (2, 1000, 6), (3, 2047, 9), (3, 512, 1)]
+    k_rows = [(0, n - 1, 0), (1, n - 5, 7), (3, n - 40, 3)]
+    want = BW.backward_rows(x["q"], x["k"], x["v"], x["gate"], dout, q_rows=q_rows, k_rows=k_rows,
+                            gate_mode=w.gate_mode, q_norm_w=x["q_norm_w"], k_norm_w=x["k_norm_w"],
+                            positions=x["positions"], rms_eps=w.rms_eps, rope_base=w.rope_base, rot_dim=w.rot_dim)
+    dq, dgate, dk, dv = (host(got[k_]) for k_ in ("dq", "dgate", "dk", "dv"))
+    _assert_rel(np.stack([dq[b, i, h] for b, i, h in q_rows]), want["dq"], "dq rows")
+    _assert_rel(np.array([dgate[b, i, h] for b, i, h in q_rows]), want["dgate"], "dgate rows (headwise)")
+    _assert_rel(np.stack([dk[b, j, g] for b, j, g in k_rows]), want["dk"], "dk rows")
+    _assert_rel(np.stack([dv[b, j, g] for b, j, g in k_rows]), want["dv"], "dv rows")
+    sig = 1.0 / (1.0 + np.exp(-x["gate"].astype(np.float64)))                  # [B, n, H]
+    dy = dout.reshape(w.batch, n, w.n_q_heads, w.head_dim).astype(np.float64) * sig[..., None]
+    grp = w.n_q_heads // w.n_kv_heads
+    for b in (0, 3):
+        for g in (0, w.n_kv_heads - 1):
+            _assert_rel(dv[b, :, g].sum(axis=0), dy[b, :, g * grp:(g + 1) * grp].sum(axis=(0, 1)),
+                        f"column sums of dv, seq {b} group {g}")

@@ -257,3 +257,30 @@ def test_gate_forms_decode(w, f):
     zf = oracle.expand_gate(_oracle_z(z, f), w.gate_mode, of, (w.batch,), w.n_q_heads)
     mx, mean, smax = _assert_variant(host(out), want, plain, w, f, zf, nw, f"{w.name} {_label(f)}")
     print(f"  max-abs {mx:.2e} mean-abs {mean:.2e} (max S {smax:.1f})", flush=True)
+
+
+def test_gate_forms_full_workload_sampled():
+    """The 4096-token workload with the extended epilogue the bench times
+    (elementwise SiLU gate after the per-head output RMSNorm): sampled rows."""
+    w = inputs.WORKLOADS["qwen35_0p8b_prefill"]
+    f = _form("silu", "mul", norm=True)
+    print(f"[gate forms] {w.name} {_label(f)} full size", flush=True)
+    x = inputs.make_prefill(w)
+    et = tdt(w)
+    nw = _norm_w(w, 541)
+    d, of = _descs(w, f, nw)
+    assert api.ga_prefill_attention_kernel(d, w.seq_len) == "mirror"
+    out = api.ga_prefill(d, dev(x["q"], et), dev(x["k"], et), dev(x["v"], et), dev(x["gate"], et),
+                         dev(x["q_norm_w"]), dev(x["k_norm_w"]), dev(x["positions"]))
+    torch.cuda.synchronize()
+    rows = [(0, 0, 0), (0, 1, 7), (0, 1000, 3), (0, 2049, 4), (0, 4095, 5), (0, 4095, 0)]
+    kw = dict(q_norm_w=x["q_norm_w"], k_norm_w=x["k_norm_w"], positions=x["positions"], rms_eps=w.rms_eps,
+              rope_base=w.rope_base, rot_dim=w.rot_dim)
+    want = oracle.prefill_rows(x["q"], x["k"], x["v"], x["gate"], rows, gate_mode=w.gate_mode, gate_form=of, **kw)
+    plain = oracle.prefill_rows(x["q"], x["k"], x["v"], None, rows, gate_mode="none", **kw)
+    got = host(out)
+    dd = w.head_dim
+    w1 = w.with_(batch=1, seq_len=len(rows), n_q_heads=1, n_kv_heads=1)
+    z1 = np.stack([x["gate"][b, i, h] for b, i, h in rows])[:, None]
+    _assert_variant(np.stack([got[b, i, h * dd:(h + 1) * dd] for b, i, h in rows]), want, plain, w1, f, z1, nw,
+                    w.name)
