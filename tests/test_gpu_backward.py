@@ -6,7 +6,9 @@ modes, with and without the norms, ragged token counts (not multiples of the
 Tolerance. The backward products read bf16 operands (q-hat, k-hat, dy, P,
 dS) and accumulate in fp32; each gradient is stored in bf16. The gradients
 have no fixed scale, so the bar is relative to each gradient tensor:
-max|err| <= 2e-2 * max|want| and mean|err| <= 1e-2 * mean|want|."""
+max|err| <= 2e-2 * max|want| and mean|err| <= 1e-2 * mean|want|, with the
+scales floored at 1e-3 for gradients that vanish (a one-token sequence has
+dq = dk = 0 exactly; the kernels give rounding residue there)."""
 import numpy as np
 import pytest
 import torch
@@ -18,6 +20,7 @@ from tests.gpu_helpers import dev, desc_for, host, tdt
 pytestmark = pytest.mark.gpu
 
 REL_MAX, REL_MEAN = 2e-2, 1e-2
+FLOOR = 1e-3
 
 
 def _case(name, B, n, H, G, d, rot, gate, norm=True, seed=600):
@@ -30,6 +33,9 @@ CASES = [
     _case("d64_g3_none_nonorm", 2, 45, 6, 2, 64, 16, "none", norm=False, seed=603),
     _case("d256_g8_elem", 1, 33, 8, 1, 256, 64, "elementwise", seed=604),
     _case("d128_g2_elem_long", 1, 300, 4, 2, 128, 32, "elementwise", seed=605),
+    _case("d256_one_token", 3, 1, 8, 2, 256, 64, "elementwise", seed=606),
+    _case("d128_g1_one_block_plus_one", 2, 65, 2, 2, 128, 32, "headwise", seed=607),
+    _case("d64_g16_none", 1, 80, 16, 1, 64, 16, "none", seed=608),
 ]
 
 
@@ -40,10 +46,10 @@ def _assert_rel(got, want, label):
     assert np.all(np.isfinite(got)), f"{label}: non-finite"
     err = np.abs(got - want)
     mx, mean = float(err.max()), float(err.mean())
-    assert mx <= REL_MAX * float(np.abs(want).max()), f"{label}: max err {mx:.3e} vs max|want| {np.abs(want).max():.3e}"
-    assert mean <= REL_MEAN * float(np.abs(want).mean()), \
-        f"{label}: mean err {mean:.3e} vs mean|want| {np.abs(want).mean():.3e}"
-    return mx / float(np.abs(want).max()), mean / float(np.abs(want).mean())
+    smax, smean = max(float(np.abs(want).max()), FLOOR), max(float(np.abs(want).mean()), FLOOR)
+    assert mx <= REL_MAX * smax, f"{label}: max err {mx:.3e} vs max|want| {np.abs(want).max():.3e}"
+    assert mean <= REL_MEAN * smean, f"{label}: mean err {mean:.3e} vs mean|want| {np.abs(want).mean():.3e}"
+    return mx / smax, mean / smean
 
 
 @pytest.mark.parametrize("w", CASES, ids=lambda w: w.name)
