@@ -21,6 +21,9 @@
 // other index, provided the A operand holds the same permutation of that
 // index: the column-blocked pieces hold tokens 4(l/32) + 0..3 and
 // 8 + 4(l/32) + 0..3 of each 16-token step.
+#include <cstdlib>
+#include <cstring>
+
 #include "ga_common.hpp"
 #include "ga_internal.hpp"
 
@@ -129,6 +132,35 @@ __device__ __forceinline__ bf16x8_t piece(const uint16_t* base, long index, int 
   return *(const bf16x8_t*)(base + (index * 64 + lane) * 8);
 }
 
+// Two accumulator chains over KK steps: x += piece(kk) bx[kk] and
+// y += piece(KK + kk) by[kk], the A operands 1 KiB LDS pieces from base (this
+// lane's 16 bytes already added), alternating x and y. The LDS reads run PF
+// MFMAs ahead, pinned one read per MFMA, so their latency hides under the
+// matrix pipe instead of stalling every MFMA.
+template <int KK, int PF>
+__device__ __forceinline__ void lds_two_chains(const unsigned char* base, const bf16x8_t* bx, const bf16x8_t* by,
+                                               f32x16_t& x, f32x16_t& y) {
+  constexpr int N = 2 * KK;
+  bf16x8_t a[N];
+#pragma unroll
+  for (int t = 0; t < PF; ++t) a[t] = *(const bf16x8_t*)(base + ((t & 1) * KK + (t >> 1)) * 1024);
+#pragma unroll
+  for (int t = 0; t < N; ++t) {
+    if (t + PF < N) a[t + PF] = *(const bf16x8_t*)(base + (((t + PF) & 1) * KK + ((t + PF) >> 1)) * 1024);
+    if (t & 1)
+      y = mfma32(a[t], by[t >> 1], y);
+    else
+      x = mfma32(a[t], bx[t >> 1], x);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x100, PF, 0);
+#pragma unroll
+  for (int t = 0; t < N - PF; ++t) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, PF, 0);
+}
+
 // ---- dq-hat: one wave per (b, h, 32 queries, DP output dims) --------------------------
 // S^T = K Q^T and dP^T = V dy^T put the query in the accumulator column, so
 // dS^T is the B operand of dQ^T += K^T dS^T. A workgroup holds the NPASS dim
@@ -195,6 +227,126 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(const BwdParams p) {
       }
     }
     if (active && query < p.n) {
+      float* dst = p.dqh + (((long)b * p.n + query) * p.H + h) * D + d0;
+#pragma unroll
+      for (int mb = 0; mb < DP / 32; ++mb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) dst[mb * 32 + (i >> 2) * 8 + hi * 4 + (i & 3)] = acc[mb][i] * p.scale;
+    }
+  }
+}
+
+// ---- dq-hat, staged: the key tiles stream through LDS ---------------------------------
+// The same products as bwd_dq_kernel. A workgroup holds HPW heads of one KV
+// group (NPASS = D / 128 dim slices each, one wave per slice) and a mirrored
+// pair of query blocks. The operands of key tile kt that every wave reads
+// (row-blocked k-hat and v, KK pieces each, and the column-blocked k-hat of
+// all D dims, 2 DB pieces) go HBM -> LDS with direct loads NS - 1 tiles
+// ahead, one copy for the four waves; each wave keeps its head's q-hat and dy
+// operands of the current block in registers. The pieces are stored in their
+// 1 KiB MFMA order, so every LDS operand read is one lane-contiguous b128.
+template <int D>
+__global__ __launch_bounds__(256) void bwd_dq_staged_kernel(const BwdParams p) {
+  constexpr int DP = 128, NPASS = D / DP, HPW = 4 / NPASS, KK = D / 16, DB = D / 32;
+  constexpr int NP = 2 * KK + 2 * DB;  // 1 KiB pieces per stage
+  constexpr int NPW = NP / 4;          // direct loads per wave per stage
+  constexpr int NS = 3;                // stages in the ring
+  static_assert(KK % 4 == 0 && (2 * DB) % 4 == 0 && NPW < 64, "stage split over the four waves");
+  __shared__ __attribute__((aligned(16))) unsigned char stg[NS * NP * 1024];
+  const int lane = threadIdx.x & 63, hi = lane >> 5, l32 = lane & 31;
+  const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int nqb = (p.n + 31) / 32, NB = p.npad / 32, TS = p.npad / 16;
+  const int hgroups = p.H / HPW;  // the host checks that HPW divides the group size
+  const int hgi = (int)(blockIdx.x % ((long)p.B * hgroups));
+  const int qpair = (int)(blockIdx.x / ((long)p.B * hgroups));
+  const int b = hgi / hgroups, h = (hgi % hgroups) * HPW + w / NPASS;
+  const int d0 = (w % NPASS) * DP;
+  const long bg = (long)b * p.G + h / p.grp;
+  // one KV head's slice of each operand copy: npad * D elements
+  const uint32_t slice = (uint32_t)p.npad * D * 2;
+  const i32x4_t krs = buffer_desc(p.k_rb + bg * p.npad * D, slice);
+  const i32x4_t vrs = buffer_desc(p.v_rb + bg * p.npad * D, slice);
+  const i32x4_t crs = buffer_desc(p.k_cb + bg * p.npad * D, slice);
+  const uint32_t stg0 = lds_addr(stg);
+  // stage piece j: k-hat rows (j < KK), v rows (KK <= j < 2 KK), then the
+  // column-blocked k-hat pieces (dim block (j - 2 KK) / 2, 16-key half (j - 2 KK) % 2)
+  auto issue = [&](int kt, int buf) {
+    const uint32_t base = stg0 + (uint32_t)(buf * NP * 1024);
+#pragma unroll
+    for (int i = 0; i < NPW; ++i) {
+      const int j = w + 4 * i;
+      if (i < KK / 4) {
+        buffer_load_lds16(krs, base + j * 1024, (kt * KK + j) * 1024 + lane * 16);
+      } else if (i < KK / 2) {
+        buffer_load_lds16(vrs, base + j * 1024, (kt * KK + j - KK) * 1024 + lane * 16);
+      } else {
+        const int jj = j - 2 * KK;
+        buffer_load_lds16(crs, base + j * 1024, ((jj >> 1) * TS + kt * 2 + (jj & 1)) * 1024 + lane * 16);
+      }
+    }
+  };
+  for (int half = 0; half < 2; ++half) {
+    const int qb = half == 0 ? nqb - 1 - qpair : qpair;  // heavy block first
+    if (half == 1 && qb == nqb - 1 - qpair) break;       // (odd middle block: one only)
+    const int T = qb + 1;  // key tiles of this block
+    // every wave is done with the previous block's stage buffers
+    lds_barrier();
+#pragma unroll
+    for (int t = 0; t < NS - 1; ++t)
+      if (t < T) issue(t, t);
+    // the block's own operands land before the tile loop, so no wait the
+    // compiler places for them sits behind a later stage's loads
+    bf16x8_t qo[KK], yo[KK];
+    const long qp = (((long)b * p.H + h) * NB + qb) * KK;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      qo[kk] = piece(p.q_rb, qp + kk, lane);
+      yo[kk] = piece(p.dy_rb, qp + kk, lane);
+    }
+    const int query = qb * 32 + l32;
+    const long qoff = ((long)b * p.n + min(query, p.n - 1)) * p.H + h;
+    const float lse = p.lse[qoff], dsum = p.dsum[qoff];
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) asm volatile("" ::"v"(qo[kk]), "v"(yo[kk]));
+    asm volatile("" ::"v"(lse), "v"(dsum));
+    f32x16_t acc[DP / 32];
+#pragma unroll
+    for (int mb = 0; mb < DP / 32; ++mb) acc[mb] = f32x16_t{};
+    for (int kt = 0; kt < T; ++kt) {
+      // this wave's loads of stage kt are done once at most the later
+      // stage's loads are outstanding (loads complete in order)
+      if (kt + 1 < T)
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NPW) : "memory");
+      else
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      lds_barrier();  // all of stage kt is in LDS; every wave is past tile kt - 1
+      if (kt + NS - 1 < T) issue(kt + NS - 1, (kt + NS - 1) % NS);
+      const unsigned char* sb = stg + (kt % NS) * (NP * 1024) + lane * 16;
+      f32x16_t s = f32x16_t{}, dp = f32x16_t{};
+      lds_two_chains<KK, 4>(sb, qo, yo, s, dp);
+      // the first column-blocked k-hat operands do not depend on dS
+      constexpr int NC = DP / 16, CPF = 4;
+      const unsigned char* cb0 = sb + (2 * KK + 2 * (d0 / 32)) * 1024;
+      bf16x8_t ca[NC];
+#pragma unroll
+      for (int t = 0; t < CPF; ++t) ca[t] = *(const bf16x8_t*)(cb0 + t * 1024);
+      const int k0 = kt * 32;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int key = k0 + (i >> 2) * 8 + hi * 4 + (i & 3);
+        const bool valid = key <= query && query < p.n;
+        const float pv = valid ? __builtin_amdgcn_exp2f(s[i] * p.scale_log2 - lse) : 0.f;
+        s[i] = pv * (dp[i] - dsum);  // dS^T
+      }
+      const bf16x8_t ds0 = pack_operand(s, 0), ds1 = pack_operand(s, 1);
+      // piece t: dim block d0 / 32 + t / 2, 16-key half t % 2
+#pragma unroll
+      for (int t = 0; t < NC; ++t) {
+        if (t + CPF < NC) ca[t + CPF] = *(const bf16x8_t*)(cb0 + (t + CPF) * 1024);
+        acc[t >> 1] = mfma32(ca[t], (t & 1) ? ds1 : ds0, acc[t >> 1]);
+      }
+    }
+    if (query < p.n) {
       float* dst = p.dqh + (((long)b * p.n + query) * p.H + h) * D + d0;
 #pragma unroll
       for (int mb = 0; mb < DP / 32; ++mb)
@@ -310,6 +462,142 @@ __global__ __launch_bounds__(256, 2) void bwd_dkv_kernel(const BwdParams p) {
           const int e = mb * 32 + (i >> 2) * 8 + hi * 4 + (i & 3);
           p.dkp[ko + e] = dk[mb][i] * p.scale;
           p.dvp[ko + e] = dv[mb][i];
+        }
+    }
+  }
+}
+
+// ---- per-head dk-hat and dv, staged: the query tiles stream through LDS ------------------
+// The same products as bwd_dkv_kernel. A workgroup takes one query head and
+// a mirrored pair of 64-key super blocks (m and M - 1 - m, two 32-key blocks
+// each); wave w holds key block w & 1 of the super block (its k-hat and v
+// operands in registers) and output dims [(w >> 1) D / 2, (w >> 1 + 1) D / 2).
+// Every wave computes the full S and dP tiles of its key block; the query
+// tile's operands (row-blocked q-hat and dy, KK pieces each, their
+// column-blocked pieces over all D dims, 2 DB each, and the rows' log-sum-exp
+// and rowsum(dy y)) go HBM -> LDS with direct loads one tile ahead, one copy
+// for the four waves. No tracked load is left outstanding inside the tile
+// loop, so no compiler-placed wait drains the next tile's loads early.
+template <int D>
+__global__ __launch_bounds__(256) void bwd_dkv_staged_kernel(const BwdParams p) {
+  constexpr int KK = D / 16, DB = D / 32, DPW = D / 2, MB = DPW / 32;
+  constexpr int NP = 2 * KK + 4 * DB;  // 1 KiB pieces per stage
+  constexpr int NPW = NP / 4;          // direct loads per wave per stage
+  constexpr int NS = 2;                // stages in the ring
+  static_assert(KK % 4 == 0 && DB % 2 == 0 && NPW < 64, "stage split over the four waves");
+  __shared__ __attribute__((aligned(16))) unsigned char stg[NS * NP * 1024];
+  __shared__ __attribute__((aligned(16))) float stat[NS][128];  // [lse of 32 rows x2 | dsum of 32 rows x2]
+  const int lane = threadIdx.x & 63, hi = lane >> 5, l32 = lane & 31;
+  const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int nkb = (p.n + 31) / 32, NB = p.npad / 32, TS = p.npad / 16;
+  const int M = (nkb + 1) / 2;  // 64-key super blocks
+  const uint32_t nstat = (uint32_t)((long)p.B * p.n * p.H * 4);
+  const i32x4_t lrs = buffer_desc(p.lse, nstat), srs = buffer_desc(p.dsum, nstat);
+  const int bh = (int)(blockIdx.x % ((long)p.B * p.H));
+  const int spair = (int)(blockIdx.x / ((long)p.B * p.H));
+  const int b = bh / p.H, h = bh % p.H;
+  const long bg = (long)b * p.G + h / p.grp;
+  const int kbw = w & 1, d0 = (w >> 1) * DPW;
+  const uint32_t slice = (uint32_t)p.npad * D * 2;
+  const i32x4_t qrs = buffer_desc(p.q_rb + (long)bh * p.npad * D, slice);
+  const i32x4_t yrs = buffer_desc(p.dy_rb + (long)bh * p.npad * D, slice);
+  const i32x4_t qcs = buffer_desc(p.q_cb + (long)bh * p.npad * D, slice);
+  const i32x4_t ycs = buffer_desc(p.dy_cb + (long)bh * p.npad * D, slice);
+  const uint32_t stg0 = lds_addr(stg);
+  // stage piece j: q-hat rows (j < KK), dy rows (KK <= j < 2 KK), then the
+  // column-blocked q-hat and dy pieces (dim block jj / 2, 16-query half jj % 2)
+  auto issue = [&](int qt, int buf) {
+    const uint32_t base = stg0 + (uint32_t)(buf * NP * 1024);
+    if (w < 2) {  // lanes l and l + 32: row qt * 32 + l (clamped to the last row)
+      const int so = ((b * p.n + min(qt * 32 + l32, p.n - 1)) * p.H + h) * 4;
+      buffer_load_lds4(w == 0 ? lrs : srs, lds_addr(stat[buf]) + w * 256, so);
+    }
+#pragma unroll
+    for (int i = 0; i < NPW; ++i) {
+      const int j = w + 4 * i;
+      if (i < KK / 4) {
+        buffer_load_lds16(qrs, base + j * 1024, (qt * KK + j) * 1024 + lane * 16);
+      } else if (i < KK / 2) {
+        buffer_load_lds16(yrs, base + j * 1024, (qt * KK + j - KK) * 1024 + lane * 16);
+      } else if (i < KK / 2 + DB / 2) {
+        const int jj = j - 2 * KK;
+        buffer_load_lds16(qcs, base + j * 1024, ((jj >> 1) * TS + qt * 2 + (jj & 1)) * 1024 + lane * 16);
+      } else {
+        const int jj = j - 2 * KK - 2 * DB;
+        buffer_load_lds16(ycs, base + j * 1024, ((jj >> 1) * TS + qt * 2 + (jj & 1)) * 1024 + lane * 16);
+      }
+    }
+  };
+  for (int half = 0; half < 2; ++half) {
+    const int sbk = half == 0 ? spair : M - 1 - spair;  // heavy super block first
+    if (half == 1 && sbk == spair) break;               // (odd middle super block: one only)
+    const int kb = 2 * sbk + kbw;  // < NB: npad is a multiple of 64
+    bf16x8_t ko[KK], vo[KK];
+    const long kpiece = (bg * NB + kb) * KK;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      ko[kk] = piece(p.k_rb, kpiece + kk, lane);
+      vo[kk] = piece(p.v_rb, kpiece + kk, lane);
+    }
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) asm volatile("" ::"v"(ko[kk]), "v"(vo[kk]));  // landed before the loop
+    const int key = kb * 32 + l32;
+    f32x16_t dv[MB], dk[MB];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) dv[mb] = dk[mb] = f32x16_t{};
+    const int qt0 = 2 * sbk, T = nkb - qt0;  // query tiles [qt0, nkb)
+    lds_barrier();                           // every wave is done with the previous block's stages
+    issue(qt0, 0);
+    for (int t = 0; t < T; ++t) {
+      const int qt = qt0 + t, q0 = qt * 32;
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      lds_barrier();  // all of stage t is in LDS; every wave is past tile t - 1
+      if (t + 1 < T) issue(qt + 1, (t + 1) & 1);
+      const unsigned char* sb = stg + (t & 1) * (NP * 1024) + lane * 16;
+      f32x16_t s = f32x16_t{}, dp = f32x16_t{};
+      lds_two_chains<KK, 4>(sb, ko, vo, s, dp);
+      // the first column-blocked operands do not depend on P or dS; product
+      // u: dim block d0 / 32 + u / 4; u % 4 = dy half 0, dy half 1 (dV), q-hat
+      // half 0, q-hat half 1 (dK)
+      constexpr int NC = 4 * MB, CPF = 4;
+      const unsigned char* qcb = sb + (2 * KK + 2 * (d0 / 32)) * 1024;
+      auto coff = [&](int u) { return ((u & 2) ? 0 : 2 * DB * 1024) + (u >> 2) * 2048 + (u & 1) * 1024; };
+      bf16x8_t ca[NC];
+#pragma unroll
+      for (int u = 0; u < CPF; ++u) ca[u] = *(const bf16x8_t*)(qcb + coff(u));
+      const float* st = stat[t & 1];
+      f32x16_t pm;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int r = (i >> 2) * 8 + hi * 4 + (i & 3);
+        const float lse = st[r], dsum = st[64 + r];
+        const int query = q0 + r;
+        const bool valid = key <= query && query < p.n;
+        const float pv = valid ? __builtin_amdgcn_exp2f(s[i] * p.scale_log2 - lse) : 0.f;
+        pm[i] = pv;
+        s[i] = pv * (dp[i] - dsum);  // dS
+      }
+      const bf16x8_t p0 = pack_operand(pm, 0), p1 = pack_operand(pm, 1);
+      const bf16x8_t ds0 = pack_operand(s, 0), ds1 = pack_operand(s, 1);
+#pragma unroll
+      for (int u = 0; u < NC; ++u) {
+        if (u + CPF < NC) ca[u + CPF] = *(const bf16x8_t*)(qcb + coff(u + CPF));
+        const int mb = u >> 2, r = u & 3;
+        if (r == 0) dv[mb] = mfma32(ca[u], p0, dv[mb]);
+        if (r == 1) dv[mb] = mfma32(ca[u], p1, dv[mb]);
+        if (r == 2) dk[mb] = mfma32(ca[u], ds0, dk[mb]);
+        if (r == 3) dk[mb] = mfma32(ca[u], ds1, dk[mb]);
+      }
+    }
+    if (key < p.n) {
+      const long ko_ = (((long)b * p.n + key) * p.H + h) * D + d0;
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int e = mb * 32 + (i >> 2) * 8 + hi * 4 + (i & 3);
+          p.dkp[ko_ + e] = dk[mb][i] * p.scale;
+          p.dvp[ko_ + e] = dv[mb][i];
         }
     }
   }
@@ -469,18 +757,55 @@ hipError_t launch_bwd_dv_sum(const float* dvp, uint16_t* dv, int B, int n, int H
   return hipGetLastError();
 }
 
+// The staged kernel serves d = 128 and 256 when its workgroup's heads share
+// one KV group and an operand slice fits the buffer loads' 32-bit offsets;
+// GA_BWD_DQ_KERNEL=plain selects the register-operand kernel everywhere.
+static bool dq_staged_ok(const BwdParams& p, int D) {
+  if (D < 128) return false;
+  const int hpw = 4 / (D / 128);
+  if (p.grp % hpw != 0) return false;
+  if ((long)p.npad * D * 2 >= (1L << 31)) return false;
+  const char* e = getenv("GA_BWD_DQ_KERNEL");
+  return !(e && strcmp(e, "plain") == 0);
+}
+
 template <int D>
 static hipError_t launch_dq_d(const BwdParams& p, hipStream_t s) {
   constexpr int DP = D < 128 ? D : 128, HPW = 4 / (D / DP);
-  const long wgs = (long)p.B * ((p.H + HPW - 1) / HPW) * (((p.n + 31) / 32 + 1) / 2);  // mirrored block pairs
-  if (wgs == 0) return hipSuccess;
+  const long pairs = ((p.n + 31) / 32 + 1) / 2;  // mirrored block pairs
+  if ((long)p.B * p.H * pairs == 0) return hipSuccess;
+  if constexpr (D >= 128) {
+    if (dq_staged_ok(p, D)) {
+      hipLaunchKernelGGL((bwd_dq_staged_kernel<D>), dim3((unsigned)((long)p.B * (p.H / HPW) * pairs)), dim3(256), 0, s,
+                         p);
+      return hipGetLastError();
+    }
+  }
+  const long wgs = (long)p.B * ((p.H + HPW - 1) / HPW) * pairs;
   hipLaunchKernelGGL((bwd_dq_kernel<D, DP>), dim3((unsigned)wgs), dim3(256), 0, s, p);
   return hipGetLastError();
+}
+
+// GA_BWD_DKV_KERNEL=plain selects the register-operand kernel everywhere.
+static bool dkv_staged_ok(const BwdParams& p, int D) {
+  if (D < 128) return false;
+  if ((long)p.npad * D * 2 >= (1L << 31) || (long)p.B * p.n * p.H * 4 >= (1L << 31)) return false;
+  const char* e = getenv("GA_BWD_DKV_KERNEL");
+  return !(e && strcmp(e, "plain") == 0);
 }
 
 template <int D>
 static hipError_t launch_dkv_d(const BwdParams& p, hipStream_t s) {
   constexpr int DP = D < 128 ? D : 128, HPW = 4 / (D / DP);
+  if constexpr (D >= 128) {
+    if (dkv_staged_ok(p, D)) {
+      const long M = ((p.n + 31) / 32 + 1) / 2;  // 64-key super blocks
+      const long wgs = (long)p.B * p.H * ((M + 1) / 2);
+      if (wgs == 0) return hipSuccess;
+      hipLaunchKernelGGL((bwd_dkv_staged_kernel<D>), dim3((unsigned)wgs), dim3(256), 0, s, p);
+      return hipGetLastError();
+    }
+  }
   const long wgs = (long)p.B * p.G * (((p.n + 31) / 32 + 1) / 2) * ((p.grp + HPW - 1) / HPW);  // mirrored pairs
   if (wgs == 0) return hipSuccess;
   hipLaunchKernelGGL((bwd_dkv_kernel<D, DP>), dim3((unsigned)wgs), dim3(256), 0, s, p);

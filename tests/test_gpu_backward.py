@@ -36,6 +36,10 @@ CASES = [
     _case("d256_one_token", 3, 1, 8, 2, 256, 64, "elementwise", seed=606),
     _case("d128_g1_one_block_plus_one", 2, 65, 2, 2, 128, 32, "headwise", seed=607),
     _case("d64_g16_none", 1, 80, 16, 1, 64, 16, "none", seed=608),
+    # the LDS-staged dq kernel: d = 128 with groups of 4 and 8, d = 256 with group 2
+    _case("d128_g4_elem_staged", 2, 97, 8, 2, 128, 32, "elementwise", seed=609),
+    _case("d128_g8_head_staged", 1, 200, 8, 1, 128, 32, "headwise", seed=610),
+    _case("d256_g2_head_staged", 1, 130, 4, 2, 256, 64, "headwise", seed=611),
 ]
 
 
