@@ -335,7 +335,7 @@ __global__ __launch_bounds__(256) void bwd_dq_staged_kernel(const BwdParams p) {
       for (int i = 0; i < 16; ++i) {
         const int key = k0 + (i >> 2) * 8 + hi * 4 + (i & 3);
         const bool valid = key <= query && query < p.n;
-        const float pv = valid ? __builtin_amdgcn_exp2f(s[i] * p.scale_log2 - lse) : 0.f;
+        const float pv = __builtin_amdgcn_exp2f(valid ? s[i] * p.scale_log2 - lse : -INFINITY);  // branch-free: exp2(-inf) = 0
         s[i] = pv * (dp[i] - dsum);  // dS^T
       }
       const bf16x8_t ds0 = pack_operand(s, 0), ds1 = pack_operand(s, 1);
@@ -438,7 +438,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dkv_kernel(const BwdParams p) {
         const float lse = __shfl(lse_l, r, 64), dsum = __shfl(dsum_l, r, 64);
         const int query = q0 + r;
         const bool valid = key <= query && query < p.n;
-        const float pv = valid ? __builtin_amdgcn_exp2f(s[i] * p.scale_log2 - lse) : 0.f;
+        const float pv = __builtin_amdgcn_exp2f(valid ? s[i] * p.scale_log2 - lse : -INFINITY);  // branch-free: exp2(-inf) = 0
         pm[i] = pv;
         s[i] = pv * (dp[i] - dsum);  // dS
       }
@@ -468,44 +468,46 @@ __global__ __launch_bounds__(256, 2) void bwd_dkv_kernel(const BwdParams p) {
 }
 
 // ---- per-head dk-hat and dv, staged: the query tiles stream through LDS ------------------
-// The same products as bwd_dkv_kernel. A workgroup takes one query head and
-// a mirrored pair of 64-key super blocks (m and M - 1 - m, two 32-key blocks
-// each); wave w holds key block w & 1 of the super block (its k-hat and v
-// operands in registers) and output dims [(w >> 1) D / 2, (w >> 1 + 1) D / 2).
-// Every wave computes the full S and dP tiles of its key block; the query
-// tile's operands (row-blocked q-hat and dy, KK pieces each, their
-// column-blocked pieces over all D dims, 2 DB each, and the rows' log-sum-exp
-// and rowsum(dy y)) go HBM -> LDS with direct loads one tile ahead, one copy
-// for the four waves. No tracked load is left outstanding inside the tile
-// loop, so no compiler-placed wait drains the next tile's loads early.
+// The same products as bwd_dkv_kernel. A workgroup takes one query head, one
+// half of the output dims ([dh D / 2, (dh + 1) D / 2)) and a mirrored pair of
+// 128-key units (u and U - 1 - u, four 32-key blocks each); wave w holds key
+// block 4u + w, its k-hat and v operands in registers, and computes the full
+// S and dP tiles of that block. The query tile's operands (row-blocked q-hat
+// and dy, KK pieces each, their column-blocked pieces over the workgroup's
+// dims, DB each, and the rows' log-sum-exp and rowsum(dy y)) go HBM -> LDS
+// with direct loads two tiles ahead in a three-stage ring, one copy for the
+// four waves. No tracked load is left outstanding inside the tile loop, so no
+// compiler-placed wait drains a later stage's loads early.
 template <int D>
 __global__ __launch_bounds__(256) void bwd_dkv_staged_kernel(const BwdParams p) {
   constexpr int KK = D / 16, DB = D / 32, DPW = D / 2, MB = DPW / 32;
-  constexpr int NP = 2 * KK + 4 * DB;  // 1 KiB pieces per stage
-  constexpr int NPW = NP / 4;          // direct loads per wave per stage
-  constexpr int NS = 2;                // stages in the ring
-  static_assert(KK % 4 == 0 && DB % 2 == 0 && NPW < 64, "stage split over the four waves");
+  constexpr int NP = 2 * KK + 2 * DB;  // 1 KiB pieces per stage
+  constexpr int NPW = NP / 4;          // 16-byte direct loads per wave per stage
+  constexpr int NS = 3;                // stages in the ring
+  static_assert(KK % 4 == 0 && DB % 4 == 0 && NPW + 1 < 32, "stage split over the four waves");
   __shared__ __attribute__((aligned(16))) unsigned char stg[NS * NP * 1024];
   __shared__ __attribute__((aligned(16))) float stat[NS][128];  // [lse of 32 rows x2 | dsum of 32 rows x2]
   const int lane = threadIdx.x & 63, hi = lane >> 5, l32 = lane & 31;
   const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int nkb = (p.n + 31) / 32, NB = p.npad / 32, TS = p.npad / 16;
-  const int M = (nkb + 1) / 2;  // 64-key super blocks
-  const uint32_t nstat = (uint32_t)((long)p.B * p.n * p.H * 4);
-  const i32x4_t lrs = buffer_desc(p.lse, nstat), srs = buffer_desc(p.dsum, nstat);
-  const int bh = (int)(blockIdx.x % ((long)p.B * p.H));
-  const int spair = (int)(blockIdx.x / ((long)p.B * p.H));
+  const int U = (nkb + 3) / 4;  // 128-key units
+  const long bhd = blockIdx.x % ((long)p.B * p.H * 2);
+  const int upair = (int)(blockIdx.x / ((long)p.B * p.H * 2));
+  const int bh = (int)(bhd >> 1), dh = (int)(bhd & 1);
   const int b = bh / p.H, h = bh % p.H;
   const long bg = (long)b * p.G + h / p.grp;
-  const int kbw = w & 1, d0 = (w >> 1) * DPW;
+  const int d0 = dh * DPW;
   const uint32_t slice = (uint32_t)p.npad * D * 2;
   const i32x4_t qrs = buffer_desc(p.q_rb + (long)bh * p.npad * D, slice);
   const i32x4_t yrs = buffer_desc(p.dy_rb + (long)bh * p.npad * D, slice);
   const i32x4_t qcs = buffer_desc(p.q_cb + (long)bh * p.npad * D, slice);
   const i32x4_t ycs = buffer_desc(p.dy_cb + (long)bh * p.npad * D, slice);
+  const uint32_t nstat = (uint32_t)((long)p.B * p.n * p.H * 4);
+  const i32x4_t lrs = buffer_desc(p.lse, nstat), srs = buffer_desc(p.dsum, nstat);
   const uint32_t stg0 = lds_addr(stg);
   // stage piece j: q-hat rows (j < KK), dy rows (KK <= j < 2 KK), then the
-  // column-blocked q-hat and dy pieces (dim block jj / 2, 16-query half jj % 2)
+  // column-blocked q-hat and dy pieces of the workgroup's dims (dim block
+  // dh DB / 2 + jj / 2, 16-query half jj % 2)
   auto issue = [&](int qt, int buf) {
     const uint32_t base = stg0 + (uint32_t)(buf * NP * 1024);
     if (w < 2) {  // lanes l and l + 32: row qt * 32 + l (clamped to the last row)
@@ -519,21 +521,28 @@ __global__ __launch_bounds__(256) void bwd_dkv_staged_kernel(const BwdParams p) 
         buffer_load_lds16(qrs, base + j * 1024, (qt * KK + j) * 1024 + lane * 16);
       } else if (i < KK / 2) {
         buffer_load_lds16(yrs, base + j * 1024, (qt * KK + j - KK) * 1024 + lane * 16);
-      } else if (i < KK / 2 + DB / 2) {
+      } else if (i < KK / 2 + DB / 4) {
         const int jj = j - 2 * KK;
-        buffer_load_lds16(qcs, base + j * 1024, ((jj >> 1) * TS + qt * 2 + (jj & 1)) * 1024 + lane * 16);
+        buffer_load_lds16(qcs, base + j * 1024,
+                          ((dh * (DB / 2) + (jj >> 1)) * TS + qt * 2 + (jj & 1)) * 1024 + lane * 16);
       } else {
-        const int jj = j - 2 * KK - 2 * DB;
-        buffer_load_lds16(ycs, base + j * 1024, ((jj >> 1) * TS + qt * 2 + (jj & 1)) * 1024 + lane * 16);
+        const int jj = j - 2 * KK - DB;
+        buffer_load_lds16(ycs, base + j * 1024,
+                          ((dh * (DB / 2) + (jj >> 1)) * TS + qt * 2 + (jj & 1)) * 1024 + lane * 16);
       }
     }
   };
   for (int half = 0; half < 2; ++half) {
-    const int sbk = half == 0 ? spair : M - 1 - spair;  // heavy super block first
-    if (half == 1 && sbk == spair) break;               // (odd middle super block: one only)
-    const int kb = 2 * sbk + kbw;  // < NB: npad is a multiple of 64
+    const int unit = half == 0 ? upair : U - 1 - upair;  // heavy unit first
+    if (half == 1 && unit == upair) break;               // (odd middle unit: one only)
+    const int kb = 4 * unit + w;                         // may pass the last block: then no key is real
+    const int qt0 = 4 * unit, T = nkb - qt0;             // query tiles [qt0, nkb)
+    lds_barrier();  // every wave is done with the previous unit's stages
+#pragma unroll
+    for (int t = 0; t < NS - 1; ++t)
+      if (t < T) issue(qt0 + t, t);
     bf16x8_t ko[KK], vo[KK];
-    const long kpiece = (bg * NB + kb) * KK;
+    const long kpiece = (bg * NB + min(kb, NB - 1)) * KK;
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
       ko[kk] = piece(p.k_rb, kpiece + kk, lane);
@@ -545,35 +554,51 @@ __global__ __launch_bounds__(256) void bwd_dkv_staged_kernel(const BwdParams p) 
     f32x16_t dv[MB], dk[MB];
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) dv[mb] = dk[mb] = f32x16_t{};
-    const int qt0 = 2 * sbk, T = nkb - qt0;  // query tiles [qt0, nkb)
-    lds_barrier();                           // every wave is done with the previous block's stages
-    issue(qt0, 0);
     for (int t = 0; t < T; ++t) {
       const int qt = qt0 + t, q0 = qt * 32;
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      // this wave's loads of stage t are done once at most the next stage's
+      // loads are outstanding (loads complete in order); waves 0 and 1 also
+      // load one row-statistics vector per stage
+      if (t + 1 < T) {
+        if (w < 2)
+          asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NPW + 1) : "memory");
+        else
+          asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NPW) : "memory");
+      } else {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      }
       lds_barrier();  // all of stage t is in LDS; every wave is past tile t - 1
-      if (t + 1 < T) issue(qt + 1, (t + 1) & 1);
-      const unsigned char* sb = stg + (t & 1) * (NP * 1024) + lane * 16;
+      if (t + NS - 1 < T) issue(qt + NS - 1, (t + NS - 1) % NS);
+      const int buf = t % NS;
+      const unsigned char* sb = stg + buf * (NP * 1024) + lane * 16;
       f32x16_t s = f32x16_t{}, dp = f32x16_t{};
       lds_two_chains<KK, 4>(sb, ko, vo, s, dp);
       // the first column-blocked operands do not depend on P or dS; product
       // u: dim block d0 / 32 + u / 4; u % 4 = dy half 0, dy half 1 (dV), q-hat
       // half 0, q-hat half 1 (dK)
       constexpr int NC = 4 * MB, CPF = 4;
-      const unsigned char* qcb = sb + (2 * KK + 2 * (d0 / 32)) * 1024;
-      auto coff = [&](int u) { return ((u & 2) ? 0 : 2 * DB * 1024) + (u >> 2) * 2048 + (u & 1) * 1024; };
+      const unsigned char* qcb = sb + 2 * KK * 1024;
+      auto coff = [&](int u) { return ((u & 2) ? 0 : DB * 1024) + (u >> 2) * 2048 + (u & 1) * 1024; };
       bf16x8_t ca[NC];
 #pragma unroll
       for (int u = 0; u < CPF; ++u) ca[u] = *(const bf16x8_t*)(qcb + coff(u));
-      const float* st = stat[t & 1];
+      // rows 8 (i / 4) + 4 hi + i % 4 of slot i: four 16-byte reads each, all
+      // issued before the first use
+      const float* st = stat[buf];
+      f32x4_t lse4[4], dsum4[4];
+#pragma unroll
+      for (int ib = 0; ib < 4; ++ib) {
+        lse4[ib] = *(const f32x4_t*)(st + ib * 8 + hi * 4);
+        dsum4[ib] = *(const f32x4_t*)(st + 64 + ib * 8 + hi * 4);
+      }
       f32x16_t pm;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int r = (i >> 2) * 8 + hi * 4 + (i & 3);
-        const float lse = st[r], dsum = st[64 + r];
+        const float lse = lse4[i >> 2][i & 3], dsum = dsum4[i >> 2][i & 3];
         const int query = q0 + r;
         const bool valid = key <= query && query < p.n;
-        const float pv = valid ? __builtin_amdgcn_exp2f(s[i] * p.scale_log2 - lse) : 0.f;
+        const float pv = __builtin_amdgcn_exp2f(valid ? s[i] * p.scale_log2 - lse : -INFINITY);  // branch-free: exp2(-inf) = 0
         pm[i] = pv;
         s[i] = pv * (dp[i] - dsum);  // dS
       }
@@ -799,8 +824,8 @@ static hipError_t launch_dkv_d(const BwdParams& p, hipStream_t s) {
   constexpr int DP = D < 128 ? D : 128, HPW = 4 / (D / DP);
   if constexpr (D >= 128) {
     if (dkv_staged_ok(p, D)) {
-      const long M = ((p.n + 31) / 32 + 1) / 2;  // 64-key super blocks
-      const long wgs = (long)p.B * p.H * ((M + 1) / 2);
+      const long U = ((p.n + 31) / 32 + 3) / 4;  // 128-key units
+      const long wgs = (long)p.B * p.H * 2 * ((U + 1) / 2);
       if (wgs == 0) return hipSuccess;
       hipLaunchKernelGGL((bwd_dkv_staged_kernel<D>), dim3((unsigned)wgs), dim3(256), 0, s, p);
       return hipGetLastError();
