@@ -137,6 +137,27 @@ __device__ __forceinline__ bf16x8_t piece(const uint16_t* base, long index, int 
 // lane's 16 bytes already added), alternating x and y. The LDS reads run PF
 // MFMAs ahead, pinned one read per MFMA, so their latency hides under the
 // matrix pipe instead of stalling every MFMA.
+// One accumulator chain x += piece(kk) bx[kk] over KK steps, A operands as
+// in lds_two_chains.
+template <int KK, int PF>
+__device__ __forceinline__ void lds_one_chain(const unsigned char* base, const bf16x8_t* bx, f32x16_t& x) {
+  bf16x8_t a[KK];
+#pragma unroll
+  for (int t = 0; t < PF; ++t) a[t] = *(const bf16x8_t*)(base + t * 1024);
+#pragma unroll
+  for (int t = 0; t < KK; ++t) {
+    if (t + PF < KK) a[t + PF] = *(const bf16x8_t*)(base + (t + PF) * 1024);
+    x = mfma32(a[t], bx[t], x);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x100, PF, 0);
+#pragma unroll
+  for (int t = 0; t < KK - PF; ++t) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, PF, 0);
+}
+
 template <int KK, int PF>
 __device__ __forceinline__ void lds_two_chains(const unsigned char* base, const bf16x8_t* bx, const bf16x8_t* by,
                                                f32x16_t& x, f32x16_t& y) {
@@ -245,6 +266,9 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(const BwdParams p) {
 // ahead, one copy for the four waves; each wave keeps its head's q-hat and dy
 // operands of the current block in registers. The pieces are stored in their
 // 1 KiB MFMA order, so every LDS operand read is one lane-contiguous b128.
+// With two dim slices per head (d = 256) the slices' waves split the tile's
+// S and dP: slice 0 holds q-hat and computes S, slice 1 holds dy and computes
+// dP, and they swap the tiles through LDS.
 template <int D>
 __global__ __launch_bounds__(256) void bwd_dq_staged_kernel(const BwdParams p) {
   constexpr int DP = 128, NPASS = D / DP, HPW = 4 / NPASS, KK = D / 16, DB = D / 32;
@@ -253,6 +277,7 @@ __global__ __launch_bounds__(256) void bwd_dq_staged_kernel(const BwdParams p) {
   constexpr int NS = 3;                // stages in the ring
   static_assert(KK % 4 == 0 && (2 * DB) % 4 == 0 && NPW < 64, "stage split over the four waves");
   __shared__ __attribute__((aligned(16))) unsigned char stg[NS * NP * 1024];
+  __shared__ __attribute__((aligned(16))) float xch[NPASS == 2 ? 4 : 1][NPASS == 2 ? 16 * 64 : 1];
   const int lane = threadIdx.x & 63, hi = lane >> 5, l32 = lane & 31;
   const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int nqb = (p.n + 31) / 32, NB = p.npad / 32, TS = p.npad / 16;
@@ -296,18 +321,24 @@ __global__ __launch_bounds__(256) void bwd_dq_staged_kernel(const BwdParams p) {
       if (t < T) issue(t, t);
     // the block's own operands land before the tile loop, so no wait the
     // compiler places for them sits behind a later stage's loads
-    bf16x8_t qo[KK], yo[KK];
+    // q-hat (S) and dy (dP) operands; with the split, slice 0 holds q-hat and slice 1 dy
+    constexpr int NOP = NPASS == 2 ? 1 : 2;
+    bf16x8_t qo[KK], yo[NOP == 2 ? KK : 1];
     const long qp = (((long)b * p.H + h) * NB + qb) * KK;
+    const uint16_t* own = (NPASS == 2 && (w & 1)) ? p.dy_rb : p.q_rb;
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
-      qo[kk] = piece(p.q_rb, qp + kk, lane);
-      yo[kk] = piece(p.dy_rb, qp + kk, lane);
+      qo[kk] = piece(own, qp + kk, lane);
+      if constexpr (NOP == 2) yo[kk] = piece(p.dy_rb, qp + kk, lane);
     }
     const int query = qb * 32 + l32;
     const long qoff = ((long)b * p.n + min(query, p.n - 1)) * p.H + h;
     const float lse = p.lse[qoff], dsum = p.dsum[qoff];
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk) asm volatile("" ::"v"(qo[kk]), "v"(yo[kk]));
+    for (int kk = 0; kk < KK; ++kk) {
+      asm volatile("" ::"v"(qo[kk]));
+      if constexpr (NOP == 2) asm volatile("" ::"v"(yo[kk]));
+    }
     asm volatile("" ::"v"(lse), "v"(dsum));
     f32x16_t acc[DP / 32];
 #pragma unroll
@@ -323,7 +354,21 @@ __global__ __launch_bounds__(256) void bwd_dq_staged_kernel(const BwdParams p) {
       if (kt + NS - 1 < T) issue(kt + NS - 1, (kt + NS - 1) % NS);
       const unsigned char* sb = stg + (kt % NS) * (NP * 1024) + lane * 16;
       f32x16_t s = f32x16_t{}, dp = f32x16_t{};
-      lds_two_chains<KK, 4>(sb, qo, yo, s, dp);
+      if constexpr (NPASS == 2) {
+        // slice 0: S from the k-hat pieces, slice 1: dP from the v pieces; swap
+        f32x16_t mine = f32x16_t{};
+        lds_one_chain<KK, 4>(sb + (w & 1) * KK * 1024, qo, mine);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) xch[w][i * 64 + lane] = mine[i];
+        lds_barrier();  // both tiles written (the reads of the previous swap ended before this tile's stage barrier)
+        f32x16_t other;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) other[i] = xch[w ^ 1][i * 64 + lane];
+        s = (w & 1) ? other : mine;
+        dp = (w & 1) ? mine : other;
+      } else {
+        lds_two_chains<KK, 4>(sb, qo, yo, s, dp);
+      }
       // the first column-blocked k-hat operands do not depend on dS
       constexpr int NC = DP / 16, CPF = 4;
       const unsigned char* cb0 = sb + (2 * KK + 2 * (d0 / 32)) * 1024;
