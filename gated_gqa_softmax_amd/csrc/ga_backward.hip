@@ -513,35 +513,36 @@ __global__ __launch_bounds__(256, 2) void bwd_dkv_kernel(const BwdParams p) {
 }
 
 // ---- per-head dk-hat and dv, staged: the query tiles stream through LDS ------------------
-// The same products as bwd_dkv_kernel. A workgroup takes one query head, one
-// half of the output dims ([dh D / 2, (dh + 1) D / 2)) and a mirrored pair of
-// 128-key units (u and U - 1 - u, four 32-key blocks each); wave w holds key
-// block 4u + w, its k-hat and v operands in registers, and computes the full
-// S and dP tiles of that block. The query tile's operands (row-blocked q-hat
-// and dy, KK pieces each, their column-blocked pieces over the workgroup's
-// dims, DB each, and the rows' log-sum-exp and rowsum(dy y)) go HBM -> LDS
-// with direct loads two tiles ahead in a three-stage ring, one copy for the
-// four waves. No tracked load is left outstanding inside the tile loop, so no
-// compiler-placed wait drains a later stage's loads early.
+// The same products as bwd_dkv_kernel. A workgroup takes one query head and a
+// mirrored pair of 64-key super blocks (m and M - 1 - m, two 32-key blocks
+// each). Wave w holds key block w & 1 of the super block; the waves split the
+// work by role: role 0 (w < 2) holds k-hat, computes S, P and dV over all D
+// dims; role 1 holds v, computes dP, takes P from its partner (wave w ^ 2)
+// through LDS, and computes dS and dK over all D dims. The query tile's
+// operands (row-blocked q-hat and dy, KK pieces each, their column-blocked
+// pieces over all D dims, 2 DB each, and the rows' log-sum-exp and rowsum(dy
+// y)) go HBM -> LDS with direct loads one tile ahead, one copy for the four
+// waves. No tracked load is left outstanding inside the tile loop, so no
+// compiler-placed wait drains the next tile's loads early.
 template <int D>
 __global__ __launch_bounds__(256) void bwd_dkv_staged_kernel(const BwdParams p) {
-  constexpr int KK = D / 16, DB = D / 32, DPW = D / 2, MB = DPW / 32;
-  constexpr int NP = 2 * KK + 2 * DB;  // 1 KiB pieces per stage
+  constexpr int KK = D / 16, DB = D / 32;
+  constexpr int NP = 2 * KK + 4 * DB;  // 1 KiB pieces per stage
   constexpr int NPW = NP / 4;          // 16-byte direct loads per wave per stage
-  constexpr int NS = 3;                // stages in the ring
-  static_assert(KK % 4 == 0 && DB % 4 == 0 && NPW + 1 < 32, "stage split over the four waves");
+  constexpr int NS = 2;                // stages in the ring
+  static_assert(KK % 4 == 0 && DB % 2 == 0 && NPW + 1 < 32, "stage split over the four waves");
   __shared__ __attribute__((aligned(16))) unsigned char stg[NS * NP * 1024];
   __shared__ __attribute__((aligned(16))) float stat[NS][128];  // [lse of 32 rows x2 | dsum of 32 rows x2]
+  __shared__ __attribute__((aligned(16))) float pxch[2][16 * 64];  // P of key block kbw, role 0 -> role 1
   const int lane = threadIdx.x & 63, hi = lane >> 5, l32 = lane & 31;
   const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int kbw = w & 1, role = w >> 1;
   const int nkb = (p.n + 31) / 32, NB = p.npad / 32, TS = p.npad / 16;
-  const int U = (nkb + 3) / 4;  // 128-key units
-  const long bhd = blockIdx.x % ((long)p.B * p.H * 2);
-  const int upair = (int)(blockIdx.x / ((long)p.B * p.H * 2));
-  const int bh = (int)(bhd >> 1), dh = (int)(bhd & 1);
+  const int M = (nkb + 1) / 2;  // 64-key super blocks
+  const int bh = (int)(blockIdx.x % ((long)p.B * p.H));
+  const int spair = (int)(blockIdx.x / ((long)p.B * p.H));
   const int b = bh / p.H, h = bh % p.H;
   const long bg = (long)b * p.G + h / p.grp;
-  const int d0 = dh * DPW;
   const uint32_t slice = (uint32_t)p.npad * D * 2;
   const i32x4_t qrs = buffer_desc(p.q_rb + (long)bh * p.npad * D, slice);
   const i32x4_t yrs = buffer_desc(p.dy_rb + (long)bh * p.npad * D, slice);
@@ -551,8 +552,7 @@ __global__ __launch_bounds__(256) void bwd_dkv_staged_kernel(const BwdParams p) 
   const i32x4_t lrs = buffer_desc(p.lse, nstat), srs = buffer_desc(p.dsum, nstat);
   const uint32_t stg0 = lds_addr(stg);
   // stage piece j: q-hat rows (j < KK), dy rows (KK <= j < 2 KK), then the
-  // column-blocked q-hat and dy pieces of the workgroup's dims (dim block
-  // dh DB / 2 + jj / 2, 16-query half jj % 2)
+  // column-blocked q-hat and dy pieces (dim block jj / 2, 16-query half jj % 2)
   auto issue = [&](int qt, int buf) {
     const uint32_t base = stg0 + (uint32_t)(buf * NP * 1024);
     if (w < 2) {  // lanes l and l + 32: row qt * 32 + l (clamped to the last row)
@@ -566,69 +566,51 @@ __global__ __launch_bounds__(256) void bwd_dkv_staged_kernel(const BwdParams p) 
         buffer_load_lds16(qrs, base + j * 1024, (qt * KK + j) * 1024 + lane * 16);
       } else if (i < KK / 2) {
         buffer_load_lds16(yrs, base + j * 1024, (qt * KK + j - KK) * 1024 + lane * 16);
-      } else if (i < KK / 2 + DB / 4) {
+      } else if (i < KK / 2 + DB / 2) {
         const int jj = j - 2 * KK;
-        buffer_load_lds16(qcs, base + j * 1024,
-                          ((dh * (DB / 2) + (jj >> 1)) * TS + qt * 2 + (jj & 1)) * 1024 + lane * 16);
+        buffer_load_lds16(qcs, base + j * 1024, ((jj >> 1) * TS + qt * 2 + (jj & 1)) * 1024 + lane * 16);
       } else {
-        const int jj = j - 2 * KK - DB;
-        buffer_load_lds16(ycs, base + j * 1024,
-                          ((dh * (DB / 2) + (jj >> 1)) * TS + qt * 2 + (jj & 1)) * 1024 + lane * 16);
+        const int jj = j - 2 * KK - 2 * DB;
+        buffer_load_lds16(ycs, base + j * 1024, ((jj >> 1) * TS + qt * 2 + (jj & 1)) * 1024 + lane * 16);
       }
     }
   };
   for (int half = 0; half < 2; ++half) {
-    const int unit = half == 0 ? upair : U - 1 - upair;  // heavy unit first
-    if (half == 1 && unit == upair) break;               // (odd middle unit: one only)
-    const int kb = 4 * unit + w;                         // may pass the last block: then no key is real
-    const int qt0 = 4 * unit, T = nkb - qt0;             // query tiles [qt0, nkb)
-    lds_barrier();  // every wave is done with the previous unit's stages
+    const int sbk = half == 0 ? spair : M - 1 - spair;  // heavy super block first
+    if (half == 1 && sbk == spair) break;               // (odd middle super block: one only)
+    const int kb = 2 * sbk + kbw;                       // < NB: npad is a multiple of 64
+    const int qt0 = 2 * sbk, T = nkb - qt0;             // query tiles [qt0, nkb)
+    lds_barrier();  // every wave is done with the previous block's stages
+    issue(qt0, 0);
+    // role 0: k-hat pieces of the block (S = Q K^T), role 1: v pieces (dP = dy V^T)
+    bf16x8_t bo[KK];
+    const long kpiece = (bg * NB + kb) * KK;
+    const uint16_t* own = role ? p.v_rb : p.k_rb;
 #pragma unroll
-    for (int t = 0; t < NS - 1; ++t)
-      if (t < T) issue(qt0 + t, t);
-    bf16x8_t ko[KK], vo[KK];
-    const long kpiece = (bg * NB + min(kb, NB - 1)) * KK;
+    for (int kk = 0; kk < KK; ++kk) bo[kk] = piece(own, kpiece + kk, lane);
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
-      ko[kk] = piece(p.k_rb, kpiece + kk, lane);
-      vo[kk] = piece(p.v_rb, kpiece + kk, lane);
-    }
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk) asm volatile("" ::"v"(ko[kk]), "v"(vo[kk]));  // landed before the loop
+    for (int kk = 0; kk < KK; ++kk) asm volatile("" ::"v"(bo[kk]));  // landed before the loop
     const int key = kb * 32 + l32;
-    f32x16_t dv[MB], dk[MB];
+    f32x16_t acc[DB];  // role 0: dV^T, role 1: dK^T, all D dims
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) dv[mb] = dk[mb] = f32x16_t{};
+    for (int mb = 0; mb < DB; ++mb) acc[mb] = f32x16_t{};
     for (int t = 0; t < T; ++t) {
       const int qt = qt0 + t, q0 = qt * 32;
-      // this wave's loads of stage t are done once at most the next stage's
-      // loads are outstanding (loads complete in order); waves 0 and 1 also
-      // load one row-statistics vector per stage
-      if (t + 1 < T) {
-        if (w < 2)
-          asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NPW + 1) : "memory");
-        else
-          asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NPW) : "memory");
-      } else {
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      }
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       lds_barrier();  // all of stage t is in LDS; every wave is past tile t - 1
-      if (t + NS - 1 < T) issue(qt + NS - 1, (t + NS - 1) % NS);
-      const int buf = t % NS;
+      if (t + 1 < T) issue(qt + 1, (t + 1) & 1);
+      const int buf = t & 1;
       const unsigned char* sb = stg + buf * (NP * 1024) + lane * 16;
-      f32x16_t s = f32x16_t{}, dp = f32x16_t{};
-      lds_two_chains<KK, 4>(sb, ko, vo, s, dp);
-      // the first column-blocked operands do not depend on P or dS; product
-      // u: dim block d0 / 32 + u / 4; u % 4 = dy half 0, dy half 1 (dV), q-hat
-      // half 0, q-hat half 1 (dK)
-      constexpr int NC = 4 * MB, CPF = 4;
-      const unsigned char* qcb = sb + 2 * KK * 1024;
-      auto coff = [&](int u) { return ((u & 2) ? 0 : DB * 1024) + (u >> 2) * 2048 + (u & 1) * 1024; };
+      f32x16_t x = f32x16_t{};  // role 0: S, role 1: dP
+      lds_one_chain<KK, 4>(sb + role * KK * 1024, bo, x);
+      // the first column-blocked operands do not depend on P or dS; piece u:
+      // dim block u / 2, 16-query half u % 2 of dy (role 0) or q-hat (role 1)
+      constexpr int NC = 2 * DB, CPF = 4;
+      const unsigned char* cbase = sb + (2 * KK + (role ? 0 : 2 * DB)) * 1024;
       bf16x8_t ca[NC];
 #pragma unroll
-      for (int u = 0; u < CPF; ++u) ca[u] = *(const bf16x8_t*)(qcb + coff(u));
-      // rows 8 (i / 4) + 4 hi + i % 4 of slot i: four 16-byte reads each, all
-      // issued before the first use
+      for (int u = 0; u < CPF; ++u) ca[u] = *(const bf16x8_t*)(cbase + u * 1024);
+      // rows 8 (i / 4) + 4 hi + i % 4 of slot i
       const float* st = stat[buf];
       f32x4_t lse4[4], dsum4[4];
 #pragma unroll
@@ -637,38 +619,38 @@ __global__ __launch_bounds__(256) void bwd_dkv_staged_kernel(const BwdParams p) 
         dsum4[ib] = *(const f32x4_t*)(st + 64 + ib * 8 + hi * 4);
       }
       f32x16_t pm;
+      if (role == 0) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int r = (i >> 2) * 8 + hi * 4 + (i & 3);
-        const float lse = lse4[i >> 2][i & 3], dsum = dsum4[i >> 2][i & 3];
-        const int query = q0 + r;
-        const bool valid = key <= query && query < p.n;
-        const float pv = __builtin_amdgcn_exp2f(valid ? s[i] * p.scale_log2 - lse : -INFINITY);  // branch-free: exp2(-inf) = 0
-        pm[i] = pv;
-        s[i] = pv * (dp[i] - dsum);  // dS
+        for (int i = 0; i < 16; ++i) {
+          const int query = q0 + (i >> 2) * 8 + hi * 4 + (i & 3);
+          const bool valid = key <= query && query < p.n;
+          pm[i] = __builtin_amdgcn_exp2f(valid ? x[i] * p.scale_log2 - lse4[i >> 2][i & 3] : -INFINITY);
+          pxch[kbw][i * 64 + lane] = pm[i];
+        }
       }
-      const bf16x8_t p0 = pack_operand(pm, 0), p1 = pack_operand(pm, 1);
-      const bf16x8_t ds0 = pack_operand(s, 0), ds1 = pack_operand(s, 1);
+      lds_barrier();  // P written (the previous tile's reads ended before this tile's stage barrier)
+      if (role == 1) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float pv = pxch[kbw][i * 64 + lane];
+          pm[i] = pv * (x[i] - dsum4[i >> 2][i & 3]);  // dS
+        }
+      }
+      const bf16x8_t o0 = pack_operand(pm, 0), o1 = pack_operand(pm, 1);
 #pragma unroll
       for (int u = 0; u < NC; ++u) {
-        if (u + CPF < NC) ca[u + CPF] = *(const bf16x8_t*)(qcb + coff(u + CPF));
-        const int mb = u >> 2, r = u & 3;
-        if (r == 0) dv[mb] = mfma32(ca[u], p0, dv[mb]);
-        if (r == 1) dv[mb] = mfma32(ca[u], p1, dv[mb]);
-        if (r == 2) dk[mb] = mfma32(ca[u], ds0, dk[mb]);
-        if (r == 3) dk[mb] = mfma32(ca[u], ds1, dk[mb]);
+        if (u + CPF < NC) ca[u + CPF] = *(const bf16x8_t*)(cbase + (u + CPF) * 1024);
+        acc[u >> 1] = mfma32(ca[u], (u & 1) ? o1 : o0, acc[u >> 1]);
       }
     }
     if (key < p.n) {
-      const long ko_ = (((long)b * p.n + key) * p.H + h) * D + d0;
+      const long ko_ = (((long)b * p.n + key) * p.H + h) * D;
+      float* dst = role ? p.dkp : p.dvp;
+      const float sc = role ? p.scale : 1.f;
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
+      for (int mb = 0; mb < DB; ++mb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int e = mb * 32 + (i >> 2) * 8 + hi * 4 + (i & 3);
-          p.dkp[ko_ + e] = dk[mb][i] * p.scale;
-          p.dvp[ko_ + e] = dv[mb][i];
-        }
+        for (int i = 0; i < 16; ++i) dst[ko_ + mb * 32 + (i >> 2) * 8 + hi * 4 + (i & 3)] = acc[mb][i] * sc;
     }
   }
 }
@@ -869,8 +851,8 @@ static hipError_t launch_dkv_d(const BwdParams& p, hipStream_t s) {
   constexpr int DP = D < 128 ? D : 128, HPW = 4 / (D / DP);
   if constexpr (D >= 128) {
     if (dkv_staged_ok(p, D)) {
-      const long U = ((p.n + 31) / 32 + 3) / 4;  // 128-key units
-      const long wgs = (long)p.B * p.H * 2 * ((U + 1) / 2);
+      const long M = ((p.n + 31) / 32 + 1) / 2;  // 64-key super blocks
+      const long wgs = (long)p.B * p.H * ((M + 1) / 2);
       if (wgs == 0) return hipSuccess;
       hipLaunchKernelGGL((bwd_dkv_staged_kernel<D>), dim3((unsigned)wgs), dim3(256), 0, s, p);
       return hipGetLastError();
