@@ -1,7 +1,9 @@
 """GPU parity of ga_prefill_backward with the fp64 backward oracle, through
-the C ABI: d in {64, 128, 256}, GQA groups 1, 3, 4 and 8, the three gate
-modes, with and without the norms, ragged token counts (not multiples of the
-32-row blocks).
+the C ABI: d in {64, 128, 256}, GQA groups 1, 2, 3, 4, 8 and 16, the three
+gate modes, with and without the norms, ragged token counts (not multiples of
+the 32-row blocks), the LDS-staged attention kernels (d = 128, 256) and the
+register-operand ones (d = 64, odd groups at d = 256, or forced by
+GA_BWD_DQ_KERNEL / GA_BWD_DKV_KERNEL = plain).
 
 Tolerance. The backward products read bf16 operands (q-hat, k-hat, dy, P,
 dS) and accumulate in fp32; each gradient is stored in bf16. The gradients
@@ -40,6 +42,14 @@ CASES = [
     _case("d128_g4_elem_staged", 2, 97, 8, 2, 128, 32, "elementwise", seed=609),
     _case("d128_g8_head_staged", 1, 200, 8, 1, 128, 32, "headwise", seed=610),
     _case("d256_g2_head_staged", 1, 130, 4, 2, 256, 64, "headwise", seed=611),
+    # group 3 at d = 256: the staged dq cannot pair its dim slices, so the register-operand dq runs
+    _case("d256_g3_elem_plain_dq", 1, 90, 6, 2, 256, 64, "elementwise", seed=612),
+]
+
+# The register-operand kernels, forced everywhere by their switches
+PLAIN_CASES = [
+    _case("d256_g4_elem_plain", 1, 100, 8, 2, 256, 64, "elementwise", seed=613),
+    _case("d128_g4_head_plain", 2, 77, 8, 2, 128, 32, "headwise", seed=614),
 ]
 
 
@@ -54,6 +64,13 @@ def _assert_rel(got, want, label):
     assert mx <= REL_MAX * smax, f"{label}: max err {mx:.3e} vs max|want| {np.abs(want).max():.3e}"
     assert mean <= REL_MEAN * smean, f"{label}: mean err {mean:.3e} vs mean|want| {np.abs(want).mean():.3e}"
     return mx / smax, mean / smean
+
+
+@pytest.mark.parametrize("w", PLAIN_CASES, ids=lambda w: w.name)
+def test_backward_plain_kernels(w, monkeypatch):
+    monkeypatch.setenv("GA_BWD_DQ_KERNEL", "plain")
+    monkeypatch.setenv("GA_BWD_DKV_KERNEL", "plain")
+    test_backward_small(w)
 
 
 @pytest.mark.parametrize("w", CASES, ids=lambda w: w.name)
