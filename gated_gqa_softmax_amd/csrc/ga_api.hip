@@ -557,7 +557,7 @@ struct BwdLayout {
   int npad, nwg;
 };
 
-constexpr int kBwdNormWorkgroups = 512;
+constexpr int kBwdNormWorkgroups = 1024;
 
 BwdLayout bwd_layout(const ga_attn_desc* d, int32_t n) {
   BwdLayout L;

@@ -9,12 +9,14 @@
 //   dk_hat = sum_heads dS^T q_hat * scale,  dV = sum_heads P^T dy   (bwd_dkv_kernel)
 //   dq, dk, dw_q, dw_k through RoPE and RMSNorm           (bwd_norm_rope_kernel)
 //
-// The attention kernels run one wave per (query head, 32-row block) (dq) or
-// (query head, 32-key block) (per-head dk, dv partials) and one slice of at
-// most 128 output dims, on v_mfma_f32_32x32x16_bf16, with every operand one
-// coalesced 1 KiB load from L2: copies of q-hat, k-hat, v and dy laid out in
-// the MFMA's operand order (bwd_blocks_kernel), row-blocked for contractions
-// over dims and column-blocked for contractions over tokens. A 32x32
+// The attention kernels run on v_mfma_f32_32x32x16_bf16 over copies of
+// q-hat, k-hat, v and dy laid out in the MFMA's operand order
+// (bwd_blocks_kernel), row-blocked for contractions over dims and
+// column-blocked for contractions over tokens, so every operand is one
+// coalesced 1 KiB piece. For d = 128 and 256 the staged kernels stream the
+// tiles' pieces HBM -> LDS and keep each wave's invariant operands in
+// registers; the register-operand kernels (one wave per head, 32 rows and at
+// most 128 output dims, pieces read from L2) serve the other shapes. A 32x32
 // accumulator holds, in lane l and slot i, row 8(i/4) + 4(l/32) + i%4 and
 // column l%32, so a probability tile computed with the key (or query) in the
 // column is already the B operand of the product that contracts over the
@@ -754,18 +756,23 @@ __global__ __launch_bounds__(256) void bwd_norm_rope_kernel(const BwdNormParams 
 }
 
 // out[e] = sum over rows r < nrows of part[r][e]
-__global__ __launch_bounds__(256) void bwd_reduce_rows_kernel(const float* part, float* out, int nrows, int d) {
-  __shared__ float red[4][64];
+__global__ __launch_bounds__(1024) void bwd_reduce_rows_kernel(const float* part, float* out, int nrows, int d) {
+  __shared__ float red[16][64];
   const int e = blockIdx.x * 64 + (threadIdx.x & 63);
-  const int w = threadIdx.x >> 6;
+  const int w = threadIdx.x >> 6;  // 16 waves, each over rows w, w + 16, ...
   float s = 0.f;
   if (e < d) {
 #pragma unroll 8
-    for (int r = w; r < nrows; r += 4) s += part[(long)r * d + e];
+    for (int r = w; r < nrows; r += 16) s += part[(long)r * d + e];
   }
   red[w][threadIdx.x & 63] = s;
   __syncthreads();
-  if (w == 0 && e < d) out[e] = (red[0][threadIdx.x] + red[1][threadIdx.x]) + (red[2][threadIdx.x] + red[3][threadIdx.x]);
+  if (w == 0 && e < d) {
+    float t = 0.f;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) t += red[k][threadIdx.x];  // fixed order: bit-identical run to run
+    out[e] = t;
+  }
 }
 
 // ---- launchers ----------------------------------------------------------------------------
@@ -894,7 +901,7 @@ hipError_t launch_bwd_norm_rope(const BwdNormParams& p, int nwg, hipStream_t s) 
 }
 
 hipError_t launch_bwd_reduce_rows(const float* part, float* out, int nrows, int d, hipStream_t s) {
-  hipLaunchKernelGGL(bwd_reduce_rows_kernel, dim3((unsigned)((d + 63) / 64)), dim3(256), 0, s, part, out, nrows,
+  hipLaunchKernelGGL(bwd_reduce_rows_kernel, dim3((unsigned)((d + 63) / 64)), dim3(1024), 0, s, part, out, nrows,
                      d);
   return hipGetLastError();
 }
