@@ -37,6 +37,15 @@ __device__ __forceinline__ f32x16_t mfma32(bf16x8_t a, bf16x8_t b, f32x16_t c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+// 4 bytes per lane from byte offset voffset of the buffer straight into LDS
+// at lds_base + 4 * lane; waited for like buffer_load_lds16 (ga_common.hpp).
+__device__ __forceinline__ void buffer_load_lds4(i32x4_t rsrc, uint32_t lds_base, int voffset) {
+  asm volatile("s_nop 0\n\tbuffer_load_dword %0, %1, 0 offen lds"
+               :
+               : "v"(voffset), "s"(rsrc), "{m0}"(lds_base)
+               : "memory");
+}
+
 __device__ __forceinline__ bf16x8_t pack_operand(const f32x16_t& x, int half) {
   float f[8];
 #pragma unroll

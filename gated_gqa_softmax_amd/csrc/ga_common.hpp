@@ -119,15 +119,6 @@ __device__ __forceinline__ void buffer_load_lds16(i32x4_t rsrc, uint32_t lds_bas
                : "memory");
 }
 
-// 4 bytes per lane from byte offset voffset of the buffer straight into LDS
-// at lds_base + 4 * lane; waited for like buffer_load_lds16.
-__device__ __forceinline__ void buffer_load_lds4(i32x4_t rsrc, uint32_t lds_base, int voffset) {
-  asm volatile("s_nop 0\n\tbuffer_load_dword %0, %1, 0 offen lds"
-               :
-               : "v"(voffset), "s"(rsrc), "{m0}"(lds_base)
-               : "memory");
-}
-
 // LDS byte address of a pointer into a __shared__ array.
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
