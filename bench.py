@@ -1,16 +1,21 @@
 #!/usr/bin/env python3
 """Throughput of gated GQA causal attention on one MI355X.
 
-One step is one prefill pass (ga_prefill: the K-hat kernel then the fused
-attention kernel) over the Qwen3.5-0.8B-shaped workload (B=1, n=4096, H=8,
-G=2, d=256, RoPE on 64 dims, elementwise gate, bf16). The decode half of the
-metric (ga_decode over 64 sequences with cache lengths ~U[1024, 32768]) is
-measured in the same run and reported under "decode".
+One step is one whole prefill pass (ga_prefill: the K-hat kernel, then the
+fused attention kernel) over the paper-MoE-shaped long-context workload
+(B=1, n=32768, H=32, G=4, d=128, RoPE on 32 dims, elementwise gate, bf16),
+the largest single-GPU configuration. The other workloads are measured in the
+same run as extra objects: the Qwen3.5-0.8B-shaped prefill (4096 tokens,
+8/2/256), the Qwen3-0.6B-shaped batched prefill (4 x 2048, 16/8/128,
+headwise gate), the fp32 toy (latency), decode over 64 long caches (GB/s),
+and the adjacent paths (chunked prefill, fused [q | gate] input, a gate
+variant, the backward).
 
 Printed: one JSON line. ``value`` is prefill TFLOP/s counting only the
 unmasked causal work 2*B*H*d*n*(n+1); ``roofline`` relates the attention
-kernel's own duration (HIP events around each launch, on its stream) to the
-bf16 dense MFMA peak; ``cpu_baseline`` times the CPU oracle on the host.
+kernel's own duration (K launches back to back on its stream between two HIP
+events, median of 5 such samples) to the bf16 dense MFMA peak;
+``cpu_baseline`` times the fp64 CPU oracle on the host's cores.
 """
 from __future__ import annotations
 
@@ -22,6 +27,9 @@ import time
 
 import numpy as np
 
+HEADLINE = "moe_long_context_prefill"
+EXTRA_PREFILL = {"qwen35_0p8b_prefill": 100, "qwen3_0p6b_batched_prefill": 100}  # workload: K launches per sample
+VARIANT_WORKLOAD = "qwen35_0p8b_prefill"  # fused-input, gate-variant and backward measurements
 MI355X_BF16_DENSE_TFLOPS = 2500.0
 MI355X_HBM_GBS = 8000.0
 METRIC = "gated GQA attn fwd TFLOP/s (prefill) + decode KV GB/s, % of MI355X roofline"
@@ -30,10 +38,14 @@ METRIC = "gated GQA attn fwd TFLOP/s (prefill) + decode KV GB/s, % of MI355X roo
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="qwen35_0p8b_prefill",
-                    help="prefill workload to time (default: the headline one)")
+    ap.add_argument("--workload", default=HEADLINE,
+                    help="prefill workload of the headline line (default: the 32K-token one)")
+    ap.add_argument("--only", action="store_true",
+                    help="the headline prefill only (for profiler runs)")
+    ap.add_argument("--no-extra-prefill", action="store_true",
+                    help="skip the other prefill workloads and the toy")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-chunk", action="store_true", help="skip the chunked-prefill measurement")
     ap.add_argument("--no-packed", action="store_true", help="skip the fused [q | gate] input measurement")
@@ -42,6 +54,7 @@ def parse():
     ap.add_argument("--no-prefill", action="store_true", help="decode only (for counter runs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--decode-steps", type=int, default=20)
+    ap.add_argument("--samples", type=int, default=5, help="timed samples of K launches (median reported)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (reference for HBM byte counters)")
     ap.add_argument("--record-traffic", nargs=6,
@@ -54,7 +67,7 @@ def parse():
 ROOT = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(ROOT, "gated_gqa_softmax_amd", "csrc")
 # symbol of the kernel behind each name ga_prefill_attention_kernel returns
-PREFILL_KERNEL_SYMBOL = {"wide": "prefill_wide_kernel", "mirror": "prefill_v2_kernel", "split": "prefill_v2_kernel",
+PREFILL_KERNEL_SYMBOL = {"wide": "prefill_wide_kernel", "mirror": "prefill_v2_kernel",
                          "simple": "prefill_mfma_kernel", "generic": "naive_kernel"}
 KERNEL_SOURCES = {
     "prefill_v2_kernel": ["ga_prefill_v2.hip", "ga_prefill_tile.hpp", "ga_gate.hpp", "ga_common.hpp",
@@ -158,26 +171,36 @@ def ramp(torch, fn, seconds=0.25):
         torch.cuda.synchronize()
 
 
-def time_whole_and_kernel(torch, whole, attention, stream, steps, warmup):
-    """Mean ms of ``whole`` (one step) and of ``attention`` (the attention
-    kernel's launch), each as ``steps`` calls back to back between two events."""
-    for _ in range(warmup):
-        whole()
-    ramp(torch, whole)
-    res = {}
-    for name, fn in (("step_ms", whole), ("kernel_ms", attention)):
+def timed_ms(torch, fn, stream, k, samples):
+    """Median over ``samples`` of the mean ms per call of ``k`` calls of
+    ``fn`` back to back between two HIP events on ``stream`` (each sample
+    bracketed by synchronisations); also returns every sample."""
+    res = []
+    for _ in range(samples):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         e0.record(stream)
-        for _ in range(steps):
+        for _ in range(k):
             fn()
         e1.record(stream)
         torch.cuda.synchronize()
-        res[name] = e0.elapsed_time(e1) / steps
-    return res
+        res.append(e0.elapsed_time(e1) / k)
+    return float(np.median(res)), res
 
 
-def time_prefill(torch, api, inputs, accounting, wname, steps, warmup):
+def time_whole_and_kernel(torch, whole, attention, stream, steps, warmup, samples=5):
+    """Median ms of ``whole`` (one step) and of ``attention`` (the attention
+    kernel's launch), each from ``samples`` samples of ``steps`` calls."""
+    for _ in range(warmup):
+        whole()
+    ramp(torch, whole)
+    step_ms, step_s = timed_ms(torch, whole, stream, steps, samples)
+    kernel_ms, kernel_s = timed_ms(torch, attention, stream, steps, samples)
+    return {"step_ms": step_ms, "kernel_ms": kernel_ms, "step_samples_ms": step_s, "kernel_samples_ms": kernel_s}
+
+
+def time_prefill(torch, api, inputs, accounting, wname, steps, warmup, samples=5):
+    """Whole ga_prefill steps and the attention launch alone on one prefill workload."""
     w = inputs.WORKLOADS[wname]
     x = inputs.make_prefill(w)
     et = torch.bfloat16 if w.dtype == "bf16" else torch.float32
@@ -187,60 +210,76 @@ def time_prefill(torch, api, inputs, accounting, wname, steps, warmup):
     wq, wk, pos = dv(x["q_norm_w"]), dv(x["k_norm_w"]), dv(x["positions"])
     d = api.make_desc(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.rot_dim, w.rope_base, w.rms_eps, 0.0, et,
                       w.gate_mode)
-    khat = torch.empty_like(k)
+    khat = api.ga_prefill_keys(d, k, None, wk, pos)
     out = torch.empty((w.batch, w.seq_len, w.n_q_heads * w.head_dim), dtype=et, device="cuda")
-    ws_attn = torch.empty(max(1, api.ga_prefill_attention_workspace_bytes(d, w.seq_len)), dtype=torch.uint8,
-                          device="cuda")
+    ws = torch.empty(api.ga_prefill_workspace_bytes(d, w.seq_len), dtype=torch.uint8, device="cuda")
     stream = torch.cuda.current_stream()
 
-    def step(ev0=None, ev1=None):
-        # exactly what ga_prefill does, with events around the attention kernel
-        api.ga_prefill_keys(d, k, None, wk, pos, k_hat=khat, stream=stream)
-        if ev0 is not None:
-            ev0.record(stream)
-        api.ga_prefill_attention(d, q, khat, v, gate, wq, pos, out=out, workspace=ws_attn, stream=stream)
-        if ev1 is not None:
-            ev1.record(stream)
+    def whole():
+        api.ga_prefill(d, q, k, v, gate, wq, wk, pos, out=out, workspace=ws, stream=stream)
+
+    def attention():
+        api.ga_prefill_attention(d, q, khat, v, gate, wq, pos, out=out, stream=stream)
+
+    t0 = time.perf_counter()
+    res = time_whole_and_kernel(torch, whole, attention, stream, steps, warmup, samples)
+    wall = time.perf_counter() - t0
+    kernel = PREFILL_KERNEL_SYMBOL[api.ga_prefill_attention_kernel(d, w.seq_len)]
+    flops = accounting.causal_prefill_flops(w.batch, w.n_q_heads, w.head_dim, w.seq_len)
+    del q, k, v, gate, khat, out, ws
+    return dict(w=w, x=x, flops=flops, attn_ms=res["kernel_ms"], kernel=kernel, step_ms=res["step_ms"],
+                step_samples_ms=res["step_samples_ms"], kernel_samples_ms=res["kernel_samples_ms"], wall_s=wall)
+
+
+def prefill_config(w):
+    return {"workload": w.name, "batch": w.batch, "seq_len": w.seq_len, "n_q_heads": w.n_q_heads,
+            "n_kv_heads": w.n_kv_heads, "head_dim": w.head_dim, "rot_dim": w.rot_dim, "gate": w.gate_mode}
+
+
+def prefill_roofline(pre):
+    w = pre["w"]
+    achieved = pre["flops"] / (pre["attn_ms"] * 1e-3) / 1e12
+    return {"bound": "mfma", "kernel": pre["kernel"], "achieved": achieved, "peak": MI355X_BF16_DENSE_TFLOPS,
+            "unit": "TFLOP/s", "frac": achieved / MI355X_BF16_DENSE_TFLOPS,
+            "traffic": measured_traffic(pre["kernel"], w.name), "kernel_ms": pre["attn_ms"],
+            "kernel_samples_ms": pre["kernel_samples_ms"], "algorithmic_flops": pre["flops"]}
+
+
+def prefill_object(pre, steps):
+    return {"metric": METRIC, "value": pre["flops"] / (pre["step_ms"] * 1e-3) / 1e12, "unit": "TFLOP/s",
+            "ms_per_step": pre["step_ms"], "step_samples_ms": pre["step_samples_ms"], "steps": steps,
+            "dtype": "bf16" if pre["w"].dtype == "bf16" else "f32", "config": prefill_config(pre["w"]),
+            "roofline": prefill_roofline(pre)}
+
+
+def time_toy(torch, api, inputs, steps, warmup, samples=5):
+    """The fp32 toy workload: latency of one whole ga_prefill call (8.7 kflop:
+    launch-bound; no roofline claim)."""
+    w = inputs.WORKLOADS["toy"]
+    x = inputs.make_prefill(w)
+    dv = lambda a, dt=None: torch.from_numpy(np.ascontiguousarray(a)).to("cuda", dtype=dt)
+    f = torch.float32
+    q, k, v, gate = dv(x["q"], f), dv(x["k"], f), dv(x["v"], f), dv(x["gate"], f)
+    wq, wk, pos = dv(x["q_norm_w"]), dv(x["k_norm_w"]), dv(x["positions"])
+    d = api.make_desc(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.rot_dim, w.rope_base, w.rms_eps, 0.0, f,
+                      w.gate_mode)
+    out = torch.empty((w.batch, w.seq_len, w.n_q_heads * w.head_dim), dtype=f, device="cuda")
+    ws = torch.empty(max(1, api.ga_prefill_workspace_bytes(d, w.seq_len)), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def whole():
+        api.ga_prefill(d, q, k, v, gate, wq, wk, pos, out=out, workspace=ws, stream=stream)
 
     for _ in range(warmup):
-        step()
-    ramp(torch, step)
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(steps):
-        step(*ev[i])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    attn_ms_events = float(np.mean([a.elapsed_time(b) for a, b in ev]))
-    # The attention kernel's launch duration: the same launches back to back
-    # between two events on its stream (per-launch event pairs add several
-    # microseconds of event overhead to a ~0.1 ms kernel).
-    k0, k1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    k0.record(stream)
-    for _ in range(steps):
-        api.ga_prefill_attention(d, q, khat, v, gate, wq, pos, out=out, workspace=ws_attn, stream=stream)
-    k1.record(stream)
-    torch.cuda.synchronize()
-    attn_ms = k0.elapsed_time(k1) / steps
-    kernel = PREFILL_KERNEL_SYMBOL[api.ga_prefill_attention_kernel(d, w.seq_len)]
-    # whole ga_prefill calls, for the step figure
-    ws = torch.empty(api.ga_prefill_workspace_bytes(d, w.seq_len), dtype=torch.uint8, device="cuda")
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e0.record(stream)
-    for _ in range(steps):
-        api.ga_prefill(d, q, k, v, gate, wq, wk, pos, out=out, workspace=ws, stream=stream)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    step_ms = e0.elapsed_time(e1) / steps
-    flops = accounting.causal_prefill_flops(w.batch, w.n_q_heads, w.head_dim, w.seq_len)
-    return dict(w=w, x=x, flops=flops, attn_ms=attn_ms, attn_ms_events=attn_ms_events, kernel=kernel,
-                step_ms=step_ms, wall_s=wall)
+        whole()
+    ms, samples_ms = timed_ms(torch, whole, stream, steps, samples)
+    return {"metric": "toy prefill latency", "value": ms * 1e3, "unit": "us per call", "higher_is_better": False,
+            "samples_us": [t * 1e3 for t in samples_ms], "steps": steps, "dtype": "f32",
+            "config": prefill_config(w), "kernel": api.ga_prefill_attention_kernel(d, w.seq_len),
+            "note": "two launches (K-hat, attention) per call; latency-bound, no roofline claim"}
 
 
-def time_decode(torch, api, inputs, accounting, steps, warmup):
+def time_decode(torch, api, inputs, accounting, steps, warmup, samples=5):
     w = inputs.WORKLOADS["decode_64seq"]
     x = inputs.make_decode(w)
     et = torch.bfloat16
@@ -264,45 +303,18 @@ def time_decode(torch, api, inputs, accounting, steps, warmup):
     out = torch.empty((w.batch, w.n_q_heads * w.head_dim), dtype=et, device="cuda")
     stream = torch.cuda.current_stream()
 
-    def step(ev0=None, ev1=None):
-        if ev0 is not None:
-            ev0.record(stream)
-        api.ga_decode_partials(d, q, kc, vc, dl, max_len, ws, q_norm_w=wq, stream=stream)
-        if ev1 is not None:
-            ev1.record(stream)
-        api.ga_decode_merge(d, q, kn, vn, kc, vc, dl, max_len, ws, gate=gate, q_norm_w=wq, k_norm_w=wk, out=out,
-                            stream=stream)
+    def step():
+        api.ga_decode(d, q, kn, vn, kc, vc, dl, max_len, gate=gate, q_norm_w=wq, k_norm_w=wk, out=out, workspace=ws,
+                      stream=stream)
 
     for _ in range(warmup):
         step()
     ramp(torch, step)
-    # per-launch event pairs around the partials kernel (a diagnostic: each
-    # pair adds event overhead, so neither figure below comes from this loop)
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-    torch.cuda.synchronize()
-    for i in range(steps):
-        step(*ev[i])
-    torch.cuda.synchronize()
-    part_ms_events = float(np.mean([a.elapsed_time(b) for a, b in ev]))
     # the step: whole ga_decode calls back to back between two events
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e0.record(stream)
-    for _ in range(steps):
-        api.ga_decode(d, q, kn, vn, kc, vc, dl, max_len, gate=gate, q_norm_w=wq, k_norm_w=wk, out=out, workspace=ws,
-                      stream=stream)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    step_ms = e0.elapsed_time(e1) / steps
+    step_ms, step_s = timed_ms(torch, step, stream, steps, samples)
     # the partials kernel alone, back to back between two events
-    k0, k1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    k0.record(stream)
-    for _ in range(steps):
-        api.ga_decode_partials(d, q, kc, vc, dl, max_len, ws, q_norm_w=wq, stream=stream)
-    k1.record(stream)
-    torch.cuda.synchronize()
-    part_ms = k0.elapsed_time(k1) / steps
+    part_ms, part_s = timed_ms(torch, lambda: api.ga_decode_partials(d, q, kc, vc, dl, max_len, ws, q_norm_w=wq,
+                                                                     stream=stream), stream, steps, samples)
     total_bytes = accounting.decode_bytes(lens, w.n_q_heads, w.n_kv_heads, w.head_dim, 2, w.gate_mode)
     cache_bytes = int(lens.astype(np.int64).sum()) * 2 * w.n_kv_heads * w.head_dim * 2
     part_bytes = cache_bytes + w.batch * w.n_q_heads * w.head_dim * 2          # cache + q
@@ -311,6 +323,7 @@ def time_decode(torch, api, inputs, accounting, steps, warmup):
         "value": total_bytes / (step_ms * 1e-3) / 1e9,
         "unit": "GB/s",
         "ms_per_step": step_ms,
+        "step_samples_ms": step_s,
         "steps": steps,
         "config": {"workload": w.name, "batch": w.batch, "cache_len_range": [w.cache_len_lo, w.cache_len_hi],
                    "sum_cache_len": int(lens.sum()), "n_q_heads": w.n_q_heads, "n_kv_heads": w.n_kv_heads,
@@ -320,31 +333,19 @@ def time_decode(torch, api, inputs, accounting, steps, warmup):
                      "peak": MI355X_HBM_GBS, "unit": "GB/s",
                      "frac": part_bytes / (part_ms * 1e-3) / 1e9 / MI355X_HBM_GBS,
                      "traffic": measured_traffic("decode_partials_kernel", w.name),
-                     "kernel_ms": part_ms, "kernel_ms_event_pairs": part_ms_events,
-                     "algorithmic_bytes": part_bytes},
+                     "kernel_ms": part_ms, "kernel_samples_ms": part_s, "algorithmic_bytes": part_bytes},
     }
 
 
-def cpu_baseline(w, x, flops, budget_s=15.0):
-    """The CPU oracle, as it stands, on the whole prefill workload, repeated
-    until about budget_s seconds of work (at least once)."""
-    from oracle import attention as oracle
+def _cpu_env():
+    """Cores of this process, the CPU model and numpy's BLAS build; BLAS
+    threads are set to the core count."""
+    cores = len(os.sched_getaffinity(0))
     try:
         import threadpoolctl
-        threads = max((i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()), default=1)
+        threadpoolctl.threadpool_limits(cores)
     except Exception:  # pragma: no cover
-        threads = 1
-    times = []
-    t_start = time.perf_counter()
-    while True:
-        t0 = time.perf_counter()
-        oracle.prefill(x["q"], x["k"], x["v"], x["gate"], gate_mode=w.gate_mode, q_norm_w=x["q_norm_w"],
-                       k_norm_w=x["k_norm_w"], positions=x["positions"], rms_eps=w.rms_eps, rope_base=w.rope_base,
-                       rot_dim=w.rot_dim)
-        times.append(time.perf_counter() - t0)
-        if time.perf_counter() - t_start > budget_s:
-            break
-    t = float(np.median(times))
+        pass
     cpu = ""
     try:
         for line in open("/proc/cpuinfo"):
@@ -353,9 +354,86 @@ def cpu_baseline(w, x, flops, budget_s=15.0):
                 break
     except OSError:
         pass
-    return {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"whole {w.name} workload, fp64 NumPy oracle, median of {len(times)} runs "
-                      f"({t:.2f} s each)", "cpu": cpu}
+    blas = ""
+    try:
+        cfg = np.show_config(mode="dicts")
+        b = cfg.get("Build Dependencies", {}).get("blas", {})
+        blas = f"{b.get('name', '')} {b.get('version', '')}".strip()
+    except Exception:  # pragma: no cover
+        pass
+    return cores, cpu, blas
+
+
+def _median_wall(fn, reps=3):
+    times = []
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        fn()
+        times.append(time.perf_counter() - t0)
+    return float(np.median(times)), times
+
+
+def cpu_baseline(inputs, accounting, headline_x=None, decode_sample=8):
+    """The fp64 CPU oracle, as it stands, timed on this host's cores.
+
+    Headline: the 32K-token workload on a seeded sample of 16 query blocks of
+    256 rows (all 32 heads, the last block included), one run, extrapolated
+    to the whole workload by its share of the unmasked flops (the rate in
+    TFLOP/s is the sample's). The other workloads: whole prefill workloads
+    (toy, 4096-token, batched) and decode over a seeded sample of sequences of
+    the 64-sequence batch (rate extrapolated by cached bytes), median of 3
+    runs each."""
+    from oracle import attention as oracle
+    cores, cpu, blas = _cpu_env()
+    per = {}
+
+    def kw(w, x):
+        return dict(gate_mode=w.gate_mode, q_norm_w=x["q_norm_w"], k_norm_w=x["k_norm_w"], positions=x["positions"],
+                    rms_eps=w.rms_eps, rope_base=w.rope_base, rot_dim=w.rot_dim)
+
+    # headline: sampled blocks of the 32K-token workload
+    w = inputs.WORKLOADS[HEADLINE]
+    x = headline_x if headline_x is not None else inputs.make_prefill(w)
+    starts = inputs.sample_row_blocks(w, 16, 256)
+    t0 = time.perf_counter()
+    oracle.prefill_blocks(x["q"], x["k"], x["v"], x["gate"], [(0, r0) for r0 in starts], **kw(w, x))
+    t_sample = time.perf_counter() - t0
+    d, H = w.head_dim, w.n_q_heads
+    sample_flops = sum(2.0 * H * d * sum(i + 1 for i in range(r0, min(w.seq_len, r0 + 256))) for r0 in starts)
+    total_flops = accounting.causal_prefill_flops(w.batch, H, d, w.seq_len)
+    rate = sample_flops / t_sample / 1e12
+    head = {"value": rate, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"{HEADLINE}: 16 seeded query blocks of 256 rows x all {H} heads (the last block included), "
+                      f"{sample_flops:.3e} of the workload's {total_flops:.3e} unmasked flops, one run of "
+                      f"{t_sample:.1f} s, fp64 NumPy oracle; whole-workload time extrapolated by flop share",
+            "extrapolated_whole_s": total_flops / (rate * 1e12), "cpu": cpu, "blas": blas}
+    del x
+    # whole prefill workloads, median of 3
+    for name in ("toy", "qwen35_0p8b_prefill", "qwen3_0p6b_batched_prefill"):
+        w = inputs.WORKLOADS[name]
+        x = inputs.make_prefill(w)
+        t, ts = _median_wall(lambda: oracle.prefill(x["q"], x["k"], x["v"], x["gate"], **kw(w, x)))
+        flops = accounting.causal_prefill_flops(w.batch, w.n_q_heads, w.head_dim, w.seq_len)
+        per[name] = {"value": flops / t / 1e12, "unit": "TFLOP/s", "seconds": t, "runs_s": ts,
+                     "sample": "whole workload, median of 3"}
+    # decode: a seeded sample of the 64 sequences, median of 3, rate by cached bytes
+    w = inputs.WORKLOADS["decode_64seq"]
+    xd = inputs.make_decode(w)
+    pick = sorted(np.random.default_rng(9).choice(w.batch, decode_sample, replace=False).tolist())
+    rows = {b: inputs.decode_cache_rows(w, b, int(xd["cache_lens"][b])) for b in pick}
+    sub = {k_: (v_[pick] if isinstance(v_, np.ndarray) and v_.shape[:1] == (w.batch,) else v_)
+           for k_, v_ in xd.items()}
+    lens = xd["cache_lens"][pick]
+    t, ts = _median_wall(lambda: oracle.decode(
+        sub["q"], sub["k_new"], sub["v_new"], sub["gate"], gate_mode=w.gate_mode, q_norm_w=sub["q_norm_w"],
+        k_norm_w=sub["k_norm_w"], k_cache_rows=lambda i: rows[pick[i]], cache_lens=lens, rms_eps=w.rms_eps,
+        rope_base=w.rope_base, rot_dim=w.rot_dim))
+    nbytes = accounting.decode_bytes(lens, w.n_q_heads, w.n_kv_heads, w.head_dim, 2, w.gate_mode)
+    per["decode_64seq"] = {"value": nbytes / t / 1e9, "unit": "GB/s", "seconds": t, "runs_s": ts,
+                           "sample": f"sequences {pick} of 64 (sum L = {int(lens.sum())}), median of 3; "
+                                     "bytes as the GPU step counts them"}
+    head["per_workload"] = per
+    return head
 
 
 def time_chunk(torch, api, inputs, accounting, steps, warmup):
@@ -377,8 +455,8 @@ def time_chunk(torch, api, inputs, accounting, steps, warmup):
     d = api.make_desc(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.rot_dim, w.rope_base, w.rms_eps, 0.0, et,
                       w.gate_mode)
     out = torch.empty((w.batch, w.seq_len, w.n_q_heads * w.head_dim), dtype=et, device="cuda")
-    ws = torch.empty(max(1, api.ga_prefill_chunk_workspace_bytes(d, w.seq_len, cap, max_len)), dtype=torch.uint8,
-                     device="cuda")
+    wsb = api.ga_prefill_chunk_workspace_bytes(d, w.seq_len, cap, max_len)
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda") if wsb else None
     stream = torch.cuda.current_stream()
 
     def whole():
@@ -402,15 +480,14 @@ def time_chunk(torch, api, inputs, accounting, steps, warmup):
         "config": {"workload": w.name, "batch": w.batch, "chunk_len": w.seq_len, "cache_lens": lens.tolist(),
                    "n_q_heads": w.n_q_heads, "n_kv_heads": w.n_kv_heads, "head_dim": w.head_dim,
                    "rot_dim": w.rot_dim, "gate": w.gate_mode},
-        "roofline": {"bound": "mfma", "kernel": kernel + (" (key ranges split in two)" if ws.numel() > 1 else ""),
-                     "achieved": achieved, "peak": MI355X_BF16_DENSE_TFLOPS,
+        "roofline": {"bound": "mfma", "kernel": kernel, "achieved": achieved, "peak": MI355X_BF16_DENSE_TFLOPS,
                      "unit": "TFLOP/s", "frac": achieved / MI355X_BF16_DENSE_TFLOPS, "kernel_ms": res["kernel_ms"],
                      "algorithmic_flops": flops},
     }
 
 
 def time_packed(torch, api, inputs, accounting, wname, steps, warmup):
-    """The headline prefill with q and the gate read in place from a fused q
+    """A prefill workload with q and the gate read in place from a fused q
     projection's output: per-head [q | gate] rows, head stride 2d."""
     w = inputs.WORKLOADS[wname]
     x = inputs.make_prefill(w)
@@ -427,15 +504,13 @@ def time_packed(torch, api, inputs, accounting, wname, steps, warmup):
     api.ga_prefill_keys(d, k, None, wk, pos, k_hat=khat)
     out = torch.empty((w.batch, w.seq_len, w.n_q_heads * hd), dtype=et, device="cuda")
     ws = torch.empty(api.ga_prefill_workspace_bytes(d, w.seq_len), dtype=torch.uint8, device="cuda")
-    ws_attn = torch.empty(max(1, api.ga_prefill_attention_workspace_bytes(d, w.seq_len)), dtype=torch.uint8,
-                          device="cuda")
     stream = torch.cuda.current_stream()
 
     def whole():
         api.ga_prefill(d, q, k, v, gate, wq, wk, pos, out=out, workspace=ws, stream=stream)
 
     def attention():
-        api.ga_prefill_attention(d, q, khat, v, gate, wq, pos, out=out, workspace=ws_attn, stream=stream)
+        api.ga_prefill_attention(d, q, khat, v, gate, wq, pos, out=out, stream=stream)
 
     res = time_whole_and_kernel(torch, whole, attention, stream, steps, warmup)
     flops = accounting.causal_prefill_flops(w.batch, w.n_q_heads, hd, w.seq_len)
@@ -457,7 +532,7 @@ def time_packed(torch, api, inputs, accounting, wname, steps, warmup):
 
 
 def time_gate_variant(torch, api, inputs, accounting, wname, steps, warmup):
-    """The headline prefill with the extended epilogue: SiLU gate,
+    """A prefill workload with the extended epilogue: SiLU gate,
     multiplicative, after a per-head RMSNorm of the attention output."""
     w = inputs.WORKLOADS[wname]
     x = inputs.make_prefill(w)
@@ -524,14 +599,7 @@ def time_backward(torch, api, inputs, accounting, wname, steps, warmup):
     for _ in range(warmup):
         whole()
     ramp(torch, whole)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e0.record(stream)
-    for _ in range(steps):
-        whole()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    step_ms = e0.elapsed_time(e1) / steps
+    step_ms, step_s = timed_ms(torch, whole, stream, steps, 5)
     flops = accounting.causal_backward_flops(w.batch, w.n_q_heads, w.head_dim, w.seq_len)
     achieved = flops / (step_ms * 1e-3) / 1e12
     return {
@@ -539,6 +607,7 @@ def time_backward(torch, api, inputs, accounting, wname, steps, warmup):
         "value": achieved,
         "unit": "TFLOP/s",
         "ms_per_step": step_ms,
+        "step_samples_ms": step_s,
         "steps": steps,
         "config": {"workload": w.name, "batch": w.batch, "seq_len": w.seq_len, "n_q_heads": w.n_q_heads,
                    "n_kv_heads": w.n_kv_heads, "head_dim": w.head_dim, "rot_dim": w.rot_dim, "gate": w.gate_mode,
@@ -568,12 +637,12 @@ def main():
         copy_calibration(torch)
         return
     if args.no_prefill:
-        dec = time_decode(torch, api, inputs, accounting, args.decode_steps, args.warmup)
+        dec = time_decode(torch, api, inputs, accounting, args.decode_steps, args.warmup, args.samples)
         print(json.dumps({"decode": dec}), flush=True)
         return
-    pre = time_prefill(torch, api, inputs, accounting, args.workload, args.steps, args.warmup)
+    print(f"[bench] {args.workload}: timing", file=sys.stderr, flush=True)
+    pre = time_prefill(torch, api, inputs, accounting, args.workload, args.steps, args.warmup, args.samples)
     w = pre["w"]
-    achieved = pre["flops"] / (pre["attn_ms"] * 1e-3) / 1e12
     rec = {
         "metric": METRIC,
         "value": pre["flops"] / (pre["step_ms"] * 1e-3) / 1e12,
@@ -581,35 +650,47 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "samples": args.samples,
         "ms_per_step": pre["step_ms"],
+        "step_samples_ms": pre["step_samples_ms"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16" if w.dtype == "bf16" else "f32",
         "data": "synthetic",
-        "config": {"workload": w.name, "batch": w.batch, "seq_len": w.seq_len, "n_q_heads": w.n_q_heads,
-                   "n_kv_heads": w.n_kv_heads, "head_dim": w.head_dim, "rot_dim": w.rot_dim, "gate": w.gate_mode,
-                   "parallelism": "single-gpu"},
-        "roofline": {"bound": "mfma", "kernel": pre["kernel"], "achieved": achieved,
-                     "peak": MI355X_BF16_DENSE_TFLOPS, "unit": "TFLOP/s", "frac": achieved / MI355X_BF16_DENSE_TFLOPS,
-                     "traffic": measured_traffic(pre["kernel"], w.name), "kernel_ms": pre["attn_ms"],
-                     "kernel_ms_event_pairs": pre["attn_ms_events"],
-                     "algorithmic_flops": pre["flops"]},
+        "config": dict(prefill_config(w), parallelism="single-gpu"),
+        "roofline": prefill_roofline(pre),
     }
-    if not args.no_decode:
-        rec["decode"] = time_decode(torch, api, inputs, accounting, args.decode_steps, args.warmup)
-    if not args.no_chunk:
-        rec["chunk"] = time_chunk(torch, api, inputs, accounting, args.steps, args.warmup)
-    if not args.no_packed and w.gate_mode == "elementwise" and w.dtype == "bf16":
-        rec["packed"] = time_packed(torch, api, inputs, accounting, args.workload, args.steps, args.warmup)
-    if not args.no_variant and w.gate_mode == "elementwise" and w.dtype == "bf16":
-        rec["gate_variant"] = time_gate_variant(torch, api, inputs, accounting, args.workload, args.steps,
-                                                args.warmup)
-    if not args.no_backward and w.gate_mode == "elementwise" and w.dtype == "bf16":
-        rec["backward"] = time_backward(torch, api, inputs, accounting, args.workload, max(5, args.steps // 5),
-                                        args.warmup)
+    headline_x = pre["x"] if w.name == HEADLINE else None
+    if not args.only:
+        if not args.no_extra_prefill:
+            for name, k in EXTRA_PREFILL.items():
+                if name == w.name:
+                    continue
+                print(f"[bench] {name}: timing", file=sys.stderr, flush=True)
+                rec[name] = prefill_object(time_prefill(torch, api, inputs, accounting, name, k, args.warmup,
+                                                        args.samples), k)
+            print("[bench] toy: timing", file=sys.stderr, flush=True)
+            rec["toy"] = time_toy(torch, api, inputs, 100, args.warmup, args.samples)
+        if not args.no_decode:
+            print("[bench] decode_64seq: timing", file=sys.stderr, flush=True)
+            rec["decode"] = time_decode(torch, api, inputs, accounting, args.decode_steps, args.warmup, args.samples)
+        if not args.no_chunk:
+            print("[bench] chunk: timing", file=sys.stderr, flush=True)
+            rec["chunk"] = time_chunk(torch, api, inputs, accounting, 50, args.warmup)
+        if not args.no_packed:
+            print("[bench] packed: timing", file=sys.stderr, flush=True)
+            rec["packed"] = time_packed(torch, api, inputs, accounting, VARIANT_WORKLOAD, 50, args.warmup)
+        if not args.no_variant:
+            print("[bench] gate variant: timing", file=sys.stderr, flush=True)
+            rec["gate_variant"] = time_gate_variant(torch, api, inputs, accounting, VARIANT_WORKLOAD, 50,
+                                                    args.warmup)
+        if not args.no_backward:
+            print("[bench] backward: timing", file=sys.stderr, flush=True)
+            rec["backward"] = time_backward(torch, api, inputs, accounting, VARIANT_WORKLOAD, 10, args.warmup)
     if not args.no_cpu_baseline:
-        rec["cpu_baseline"] = cpu_baseline(w, pre["x"], pre["flops"])
+        print("[bench] CPU oracle baseline", file=sys.stderr, flush=True)
+        rec["cpu_baseline"] = cpu_baseline(inputs, accounting, headline_x)
     print(json.dumps(rec), flush=True)
 
 

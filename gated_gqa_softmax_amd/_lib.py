@@ -29,6 +29,8 @@ GA_GATE_ELEMENTWISE = 2
 GA_ACT_SIGMOID, GA_ACT_NS_SIGMOID, GA_ACT_SILU, GA_ACT_IDENTITY = 0, 1, 2, 3
 GA_COMBINE_MUL, GA_COMBINE_ADD = 0, 1
 GA_SHARE_HEADS, GA_SHARE_TOKENS = 1, 2
+GA_KERNEL_AUTO, GA_KERNEL_WIDE, GA_KERNEL_MIRROR, GA_KERNEL_SIMPLE, GA_KERNEL_GENERIC = 0, 1, 2, 3, 4
+GA_BWD_AUTO, GA_BWD_PLAIN = 0, 1
 
 
 class AttnDesc(ctypes.Structure):
@@ -50,6 +52,8 @@ class AttnDesc(ctypes.Structure):
         ("gate_share", ctypes.c_int32),
         ("out_norm_eps", ctypes.c_float),
         ("out_norm_w", ctypes.c_void_p),
+        ("kernel", ctypes.c_int32),
+        ("bwd_kernel", ctypes.c_int32),
     ]
 
 
@@ -60,11 +64,10 @@ _D = ctypes.POINTER(AttnDesc)
 
 SIGNATURES = {
     "ga_prefill_workspace_bytes": (_S, [_D, _I]),
-    "ga_prefill_attention_workspace_bytes": (_S, [_D, _I]),
     "ga_prefill_attention_kernel": (ctypes.c_char_p, [_D, _I]),
     "ga_prefill": (_I, [_D, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _P, _S, _P, _P]),
     "ga_prefill_keys": (_I, [_D, _I, _P, _P, _P, _P, _P, _P, _I, _P]),
-    "ga_prefill_attention": (_I, [_D, _I, _P, _P, _I, _P, _I, _P, _P, _P, _P, _S, _P, _P]),
+    "ga_prefill_attention": (_I, [_D, _I, _P, _P, _I, _P, _I, _P, _P, _P, _P, _P]),
     "ga_prefill_chunk": (_I, [_D, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _P, _P, _I, _P, _S, _P, _P]),
     "ga_prefill_chunk_workspace_bytes": (_S, [_D, _I, _I, _I]),
     "ga_prefill_chunk_keys": (_I, [_D, _I, _P, _P, _P, _P, _P, _P, _I, _P, _P, _I, _P]),

@@ -26,6 +26,9 @@ _DTYPE = {torch.bfloat16: _lib.GA_BF16, torch.float32: _lib.GA_F32}
 _ACT = {"sigmoid": _lib.GA_ACT_SIGMOID, "ns_sigmoid": _lib.GA_ACT_NS_SIGMOID, "silu": _lib.GA_ACT_SILU,
         "identity": _lib.GA_ACT_IDENTITY}
 _COMBINE = {"mul": _lib.GA_COMBINE_MUL, "add": _lib.GA_COMBINE_ADD}
+_KERNEL = {"auto": _lib.GA_KERNEL_AUTO, "wide": _lib.GA_KERNEL_WIDE, "mirror": _lib.GA_KERNEL_MIRROR,
+           "simple": _lib.GA_KERNEL_SIMPLE, "generic": _lib.GA_KERNEL_GENERIC}
+_BWD_KERNEL = {"auto": _lib.GA_BWD_AUTO, "plain": _lib.GA_BWD_PLAIN}
 
 
 class GaError(RuntimeError):
@@ -40,14 +43,17 @@ class GaError(RuntimeError):
 def make_desc(batch, n_q_heads, n_kv_heads, head_dim, rot_dim=0, rope_base=10000.0, rms_eps=1e-6,
               softmax_scale=0.0, dtype=torch.bfloat16, gate_mode="none", q_head_stride=0,
               gate_head_stride=0, gate_act="sigmoid", gate_combine="mul", share_heads=False,
-              share_tokens=False, out_norm_w: Optional[torch.Tensor] = None, out_norm_eps=1e-6) -> AttnDesc:
+              share_tokens=False, out_norm_w: Optional[torch.Tensor] = None, out_norm_eps=1e-6,
+              kernel="auto", bwd_kernel="auto") -> AttnDesc:
     """Descriptor. The head strides matter only to the kernel-name queries
     (the entry points below take them from the q and gate tensors). Gate
     variants: ``gate_act`` sigmoid | ns_sigmoid | silu | identity,
     ``gate_combine`` mul | add, ``share_heads`` (gate [.., d] or [..] per
     token), ``share_tokens`` (gate [H, d] or [H]); ``out_norm_w`` a float32
     GPU tensor [d] for the per-head output RMSNorm (the descriptor keeps a
-    reference to it)."""
+    reference to it). ``kernel`` auto | wide | mirror | simple | generic
+    forces the prefill / chunk attention kernel, ``bwd_kernel`` auto | plain
+    the backward's product kernels (tests and tuning)."""
     if out_norm_w is not None:
         if not (out_norm_w.is_cuda and out_norm_w.dtype == torch.float32 and out_norm_w.is_contiguous()
                 and out_norm_w.numel() == int(head_dim)):
@@ -60,7 +66,9 @@ def make_desc(batch, n_q_heads, n_kv_heads, head_dim, rot_dim=0, rope_base=10000
                  int(q_head_stride), int(gate_head_stride),
                  _ACT[gate_act] if isinstance(gate_act, str) else int(gate_act),
                  _COMBINE[gate_combine] if isinstance(gate_combine, str) else int(gate_combine),
-                 share, float(out_norm_eps), out_norm_w.data_ptr() if out_norm_w is not None else None)
+                 share, float(out_norm_eps), out_norm_w.data_ptr() if out_norm_w is not None else None,
+                 _KERNEL[kernel] if isinstance(kernel, str) else int(kernel),
+                 _BWD_KERNEL[bwd_kernel] if isinstance(bwd_kernel, str) else int(bwd_kernel))
     d._keep = out_norm_w
     return d
 
@@ -75,6 +83,60 @@ def _ptr(t: Optional[torch.Tensor], name: str, dtype=None) -> Optional[int]:
     if dtype is not None and t.dtype != dtype:
         raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
     return t.data_ptr()
+
+
+def _tensor(t: Optional[torch.Tensor], name: str, shape, dtype, required=True) -> Optional[int]:
+    """Pointer of a dense GPU tensor of exactly ``shape`` and ``dtype`` (None
+    allowed when not ``required``); ValueError otherwise, so that no kernel is
+    ever handed a buffer smaller than the descriptor implies."""
+    if t is None:
+        if required:
+            raise ValueError(f"{name} is required")
+        return None
+    if tuple(t.shape) != tuple(int(s) for s in shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(int(s) for s in shape)}")
+    return _ptr(t, name, dtype)
+
+
+def _lens(t: Optional[torch.Tensor], name: str, batch: int, required=True) -> Optional[int]:
+    """Pointer of a per-sequence int32 GPU vector with at least ``batch`` entries."""
+    if t is None:
+        if required:
+            raise ValueError(f"{name} is required")
+        return None
+    if t.dim() != 1 or t.numel() < batch:
+        raise ValueError(f"{name} must be a 1-D tensor of at least {batch} entries, got shape {tuple(t.shape)}")
+    return _ptr(t, name, torch.int32)
+
+
+def _norm_w(t: Optional[torch.Tensor], name: str, desc: AttnDesc) -> Optional[int]:
+    return _tensor(t, name, (desc.head_dim,), torch.float32, required=False)
+
+
+def _cache_pair(k_cache, v_cache, desc: AttnDesc, et, min_cap: int):
+    """(k_cache ptr, v_cache ptr, capacity) of two [B, cap, G, d] caches of one shape."""
+    if k_cache is None or v_cache is None:
+        raise ValueError("k_cache and v_cache are both required")
+    cap = int(k_cache.shape[1]) if k_cache.dim() == 4 else -1
+    shape = (desc.batch, cap, desc.n_kv_heads, desc.head_dim)
+    kp = _tensor(k_cache, "k_cache", shape, et)
+    vp = _tensor(v_cache, "v_cache", shape, et)
+    if cap < min_cap:
+        raise ValueError(f"cache capacity {cap} < {min_cap} required")
+    return kp, vp, cap
+
+
+def _workspace_arg(workspace: Optional[torch.Tensor], nbytes: int, device):
+    """(tensor, pointer, bytes) of a workspace of at least ``nbytes`` bytes,
+    allocated here (torch) when the caller passes none."""
+    if nbytes == 0 and workspace is None:
+        return None, None, 0
+    if workspace is None:
+        workspace = torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+    nb = workspace.numel() * workspace.element_size()
+    if nb < nbytes:
+        raise ValueError(f"workspace holds {nb} bytes, {nbytes} required")
+    return workspace, _ptr(workspace, "workspace"), nb
 
 
 def head_stride(shape, strides, lead: int, n_heads: int, width: int, name: str = "tensor") -> int:
@@ -121,17 +183,28 @@ def _head_rows(t: torch.Tensor, name: str, dtype, lead: int, n_heads: int, width
     return head_stride(t.shape, t.stride(), lead, n_heads, width, name)
 
 
-def _qg(desc: AttnDesc, q, gate, lead: int, et):
-    """Copy of ``desc`` with the head strides of q and the gate, and their pointers."""
+def _qg(desc: AttnDesc, q, gate, lead_shape, et):
+    """Copy of ``desc`` with the head strides of q and the gate, and their
+    pointers. ``lead_shape`` is (B, n) for prefill, (B,) for decode: q and an
+    unshared gate must have exactly those leading dims."""
+    lead = len(lead_shape)
+    if q is None:
+        raise ValueError("q is required")
+    if tuple(q.shape[:lead]) != tuple(lead_shape):
+        raise ValueError(f"q has shape {tuple(q.shape)}, expected leading dims {tuple(lead_shape)}")
     d2 = AttnDesc.from_buffer_copy(desc)
     d2.q_head_stride = _head_rows(q, "q", et, lead, desc.n_q_heads, desc.head_dim)
     gp = None
-    if gate is not None:
+    if desc.gate_mode != _lib.GA_GATE_NONE and gate is None:
+        raise ValueError("gate is required by the descriptor's gate mode")
+    if gate is not None and desc.gate_mode != _lib.GA_GATE_NONE:
         gw = desc.head_dim if desc.gate_mode == _lib.GA_GATE_ELEMENTWISE else 1
         if desc.gate_share:
             d2.gate_head_stride = _shared_gate(gate, desc, lead, et, gw)
         else:
             d2.gate_head_stride = _head_rows(gate, "gate", et, lead, desc.n_q_heads, gw)
+        if not (desc.gate_share & _lib.GA_SHARE_TOKENS) and tuple(gate.shape[:lead]) != tuple(lead_shape):
+            raise ValueError(f"gate has shape {tuple(gate.shape)}, expected leading dims {tuple(lead_shape)}")
         gp = gate.data_ptr()
     return d2, q.data_ptr(), gp
 
@@ -198,10 +271,6 @@ def ga_prefill_workspace_bytes(desc: AttnDesc, seq_len: int) -> int:
     return _lib.load().ga_prefill_workspace_bytes(ctypes.byref(desc), seq_len)
 
 
-def ga_prefill_attention_workspace_bytes(desc: AttnDesc, seq_len: int) -> int:
-    return _lib.load().ga_prefill_attention_workspace_bytes(ctypes.byref(desc), seq_len)
-
-
 def ga_prefill_attention_kernel(desc: AttnDesc, seq_len: int) -> str:
     return _lib.load().ga_prefill_attention_kernel(ctypes.byref(desc), seq_len).decode()
 
@@ -210,10 +279,10 @@ def ga_decode_workspace_bytes(desc: AttnDesc, max_cache_len: int) -> int:
     return _lib.load().ga_decode_workspace_bytes(ctypes.byref(desc), max_cache_len)
 
 
-def _workspace(nbytes: int, device, workspace: Optional[torch.Tensor]):
-    if workspace is not None:
-        return workspace
-    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+def _seq(q, lead: int = 2):
+    if q is None or q.dim() < lead:
+        raise ValueError("q must have batch and token dims")
+    return int(q.shape[0]), int(q.shape[1])
 
 
 def ga_prefill(desc: AttnDesc, q, k, v, gate=None, q_norm_w=None, k_norm_w=None, positions=None,
@@ -221,24 +290,24 @@ def ga_prefill(desc: AttnDesc, q, k, v, gate=None, q_norm_w=None, k_norm_w=None,
     """out [B,n,H*d] = gated GQA causal attention of q [B,n,H,d], k, v [B,n,G,d]."""
     lib = _lib.load()
     et = _elem_dtype(desc)
-    B, n = q.shape[0], q.shape[1]
+    B, n = desc.batch, _seq(q)[1]
+    G, hd = desc.n_kv_heads, desc.head_dim
+    d2, qp, gp = _qg(desc, q, gate, (B, n), et)
     if out is None:
-        out = torch.empty((B, n, desc.n_q_heads * desc.head_dim), dtype=et, device=q.device)
-    cap = 0
-    if k_cache is not None:
-        cap = k_cache.shape[1]
-        ws_bytes = ga_prefill_attention_workspace_bytes(desc, n)
+        out = torch.empty((B, n, desc.n_q_heads * hd), dtype=et, device=q.device)
+    op = _tensor(out, "out", (B, n, desc.n_q_heads * hd), et)
+    kp = _tensor(k, "k", (B, n, G, hd), et)
+    vp = _tensor(v, "v", (B, n, G, hd), et)
+    cap, kcp, vcp = 0, None, None
+    if k_cache is not None or v_cache is not None:
+        kcp, vcp, cap = _cache_pair(k_cache, v_cache, desc, et, n)
+        ws, wp, wb = _workspace_arg(workspace, 0, q.device)
     else:
-        ws_bytes = ga_prefill_workspace_bytes(desc, n)
-    if ws_bytes:
-        workspace = _workspace(ws_bytes, q.device, workspace)
-    d2, qp, gp = _qg(desc, q, gate, 2, et)
-    st = lib.ga_prefill(ctypes.byref(d2), n, qp, _ptr(k, "k", et), _ptr(v, "v", et),
-                        gp, _ptr(q_norm_w, "q_norm_w", torch.float32),
-                        _ptr(k_norm_w, "k_norm_w", torch.float32), _ptr(positions, "positions", torch.int32),
-                        _ptr(k_cache, "k_cache", et), _ptr(v_cache, "v_cache", et), cap,
-                        _ptr(workspace, "workspace"), workspace.numel() if workspace is not None else 0,
-                        _ptr(out, "out", et), _stream(stream))
+        ws, wp, wb = _workspace_arg(workspace, ga_prefill_workspace_bytes(desc, n), q.device)
+    st = lib.ga_prefill(ctypes.byref(d2), n, qp, kp, vp, gp, _norm_w(q_norm_w, "q_norm_w", desc),
+                        _norm_w(k_norm_w, "k_norm_w", desc),
+                        _tensor(positions, "positions", (B, n), torch.int32, required=False),
+                        kcp, vcp, cap, wp, wb, op, _stream(stream))
     _check(st, "ga_prefill")
     return out
 
@@ -247,33 +316,46 @@ def ga_prefill_keys(desc: AttnDesc, k, v=None, k_norm_w=None, positions=None, k_
                     stream=None) -> torch.Tensor:
     lib = _lib.load()
     et = _elem_dtype(desc)
-    n = k.shape[1]
+    B, n = desc.batch, _seq(k)[1]
+    G, hd = desc.n_kv_heads, desc.head_dim
+    kp = _tensor(k, "k", (B, n, G, hd), et)
     if k_hat is None:
         k_hat = torch.empty_like(k)
-    cap = k_hat.shape[1]
-    st = lib.ga_prefill_keys(ctypes.byref(desc), n, _ptr(k, "k", et), _ptr(v, "v", et),
-                             _ptr(k_norm_w, "k_norm_w", torch.float32), _ptr(positions, "positions", torch.int32),
-                             _ptr(k_hat, "k_hat", et), _ptr(v_out, "v_out", et), cap, _stream(stream))
+    cap = int(k_hat.shape[1]) if k_hat.dim() == 4 else -1
+    khp = _tensor(k_hat, "k_hat", (B, cap, G, hd), et)
+    if cap < n:
+        raise ValueError(f"k_hat holds {cap} rows per sequence, {n} required")
+    vp = vop = None
+    if v_out is not None:
+        vp = _tensor(v, "v", (B, n, G, hd), et)
+        vop = _tensor(v_out, "v_out", (B, cap, G, hd), et)
+    st = lib.ga_prefill_keys(ctypes.byref(desc), n, kp, vp, _norm_w(k_norm_w, "k_norm_w", desc),
+                             _tensor(positions, "positions", (B, n), torch.int32, required=False),
+                             khp, vop, cap, _stream(stream))
     _check(st, "ga_prefill_keys")
     return k_hat
 
 
 def ga_prefill_attention(desc: AttnDesc, q, k_hat, v, gate=None, q_norm_w=None, positions=None, out=None,
-                         workspace=None, stream=None) -> torch.Tensor:
+                         stream=None) -> torch.Tensor:
     lib = _lib.load()
     et = _elem_dtype(desc)
-    B, n = q.shape[0], q.shape[1]
+    B, n = desc.batch, _seq(q)[1]
+    G, hd = desc.n_kv_heads, desc.head_dim
+    d2, qp, gp = _qg(desc, q, gate, (B, n), et)
     if out is None:
-        out = torch.empty((B, n, desc.n_q_heads * desc.head_dim), dtype=et, device=q.device)
-    ws_bytes = ga_prefill_attention_workspace_bytes(desc, n)
-    if ws_bytes:
-        workspace = _workspace(ws_bytes, q.device, workspace)
-    d2, qp, gp = _qg(desc, q, gate, 2, et)
-    st = lib.ga_prefill_attention(ctypes.byref(d2), n, qp, _ptr(k_hat, "k_hat", et), k_hat.shape[1],
-                                  _ptr(v, "v", et), v.shape[1], gp,
-                                  _ptr(q_norm_w, "q_norm_w", torch.float32), _ptr(positions, "positions", torch.int32),
-                                  _ptr(workspace, "workspace"), workspace.numel() if workspace is not None else 0,
-                                  _ptr(out, "out", et), _stream(stream))
+        out = torch.empty((B, n, desc.n_q_heads * hd), dtype=et, device=q.device)
+    op = _tensor(out, "out", (B, n, desc.n_q_heads * hd), et)
+    kcap = int(k_hat.shape[1]) if k_hat is not None and k_hat.dim() == 4 else -1
+    vcap = int(v.shape[1]) if v is not None and v.dim() == 4 else -1
+    khp = _tensor(k_hat, "k_hat", (B, kcap, G, hd), et)
+    vp = _tensor(v, "v", (B, vcap, G, hd), et)
+    if kcap < n or vcap < n:
+        raise ValueError(f"k_hat / v hold {kcap} / {vcap} rows per sequence, {n} required")
+    st = lib.ga_prefill_attention(ctypes.byref(d2), n, qp, khp, kcap, vp, vcap, gp,
+                                  _norm_w(q_norm_w, "q_norm_w", desc),
+                                  _tensor(positions, "positions", (B, n), torch.int32, required=False),
+                                  op, _stream(stream))
     _check(st, "ga_prefill_attention")
     return out
 
@@ -286,13 +368,16 @@ def ga_prefill_chunk_workspace_bytes(desc: AttnDesc, seq_len: int, cache_cap: in
     return int(_lib.load().ga_prefill_chunk_workspace_bytes(ctypes.byref(desc), seq_len, cache_cap, max_cache_len))
 
 
-def _chunk_workspace(desc, n, cap, max_cache_len, device, workspace):
-    """(pointer, bytes) of the chunk workspace, allocated here when not given."""
+def _chunk_args(desc, q, k_cache, v_cache, cache_lens, chunk_lens, max_cache_len, workspace, et):
+    B, n = desc.batch, _seq(q)[1]
+    if int(max_cache_len) < 0:
+        raise ValueError("max_cache_len must be >= 0")
+    kcp, vcp, cap = _cache_pair(k_cache, v_cache, desc, et, int(max_cache_len) + n)
+    lp = _lens(cache_lens, "cache_lens", B)
+    clp = _lens(chunk_lens, "chunk_lens", B, required=False)
     nbytes = ga_prefill_chunk_workspace_bytes(desc, n, cap, int(max_cache_len))
-    if nbytes == 0:
-        return None, 0, None
-    workspace = _workspace(nbytes, device, workspace)
-    return _ptr(workspace, "workspace"), workspace.numel(), workspace
+    ws, wp, wb = _workspace_arg(workspace, nbytes, q.device)
+    return B, n, kcp, vcp, cap, lp, clp, ws, wp, wb
 
 
 def ga_prefill_chunk(desc: AttnDesc, q, k, v, k_cache, v_cache, cache_lens, max_cache_len: int, gate=None,
@@ -306,17 +391,18 @@ def ga_prefill_chunk(desc: AttnDesc, q, k, v, k_cache, v_cache, cache_lens, max_
     """
     lib = _lib.load()
     et = _elem_dtype(desc)
-    B, n = q.shape[0], q.shape[1]
+    B, n, kcp, vcp, cap, lp, clp, _ws, wp, wb = _chunk_args(desc, q, k_cache, v_cache, cache_lens, chunk_lens,
+                                                            max_cache_len, workspace, et)
+    G, hd = desc.n_kv_heads, desc.head_dim
+    d2, qp, gp = _qg(desc, q, gate, (B, n), et)
     if out is None:
-        out = torch.zeros((B, n, desc.n_q_heads * desc.head_dim), dtype=et, device=q.device)
-    d2, qp, gp = _qg(desc, q, gate, 2, et)
-    wp, wb, _keep = _chunk_workspace(d2, n, k_cache.shape[1], max_cache_len, q.device, workspace)
-    st = lib.ga_prefill_chunk(ctypes.byref(d2), n, qp, _ptr(k, "k", et), _ptr(v, "v", et),
-                              gp, _ptr(q_norm_w, "q_norm_w", torch.float32),
-                              _ptr(k_norm_w, "k_norm_w", torch.float32), _ptr(positions, "positions", torch.int32),
-                              _ptr(k_cache, "k_cache", et), _ptr(v_cache, "v_cache", et), k_cache.shape[1],
-                              _ptr(cache_lens, "cache_lens", torch.int32), _ptr(chunk_lens, "chunk_lens", torch.int32),
-                              int(max_cache_len), wp, wb, _ptr(out, "out", et), _stream(stream))
+        out = torch.zeros((B, n, desc.n_q_heads * hd), dtype=et, device=q.device)
+    op = _tensor(out, "out", (B, n, desc.n_q_heads * hd), et)
+    st = lib.ga_prefill_chunk(ctypes.byref(d2), n, qp, _tensor(k, "k", (B, n, G, hd), et),
+                              _tensor(v, "v", (B, n, G, hd), et), gp, _norm_w(q_norm_w, "q_norm_w", desc),
+                              _norm_w(k_norm_w, "k_norm_w", desc),
+                              _tensor(positions, "positions", (B, n), torch.int32, required=False),
+                              kcp, vcp, cap, lp, clp, int(max_cache_len), wp, wb, op, _stream(stream))
     _check(st, "ga_prefill_chunk")
     return out
 
@@ -325,13 +411,16 @@ def ga_prefill_chunk_keys(desc: AttnDesc, k, v, k_cache, v_cache, cache_lens, ma
                           positions=None, chunk_lens=None, stream=None):
     lib = _lib.load()
     et = _elem_dtype(desc)
-    st = lib.ga_prefill_chunk_keys(ctypes.byref(desc), k.shape[1], _ptr(k, "k", et), _ptr(v, "v", et),
-                                   _ptr(k_norm_w, "k_norm_w", torch.float32),
-                                   _ptr(positions, "positions", torch.int32),
-                                   _ptr(cache_lens, "cache_lens", torch.int32),
-                                   _ptr(chunk_lens, "chunk_lens", torch.int32), int(max_cache_len),
-                                   _ptr(k_cache, "k_cache", et), _ptr(v_cache, "v_cache", et), k_cache.shape[1],
-                                   _stream(stream))
+    B, n = desc.batch, _seq(k)[1]
+    G, hd = desc.n_kv_heads, desc.head_dim
+    if int(max_cache_len) < 0:
+        raise ValueError("max_cache_len must be >= 0")
+    kcp, vcp, cap = _cache_pair(k_cache, v_cache, desc, et, int(max_cache_len) + n)
+    st = lib.ga_prefill_chunk_keys(ctypes.byref(desc), n, _tensor(k, "k", (B, n, G, hd), et),
+                                   _tensor(v, "v", (B, n, G, hd), et), _norm_w(k_norm_w, "k_norm_w", desc),
+                                   _tensor(positions, "positions", (B, n), torch.int32, required=False),
+                                   _lens(cache_lens, "cache_lens", B), _lens(chunk_lens, "chunk_lens", B, False),
+                                   int(max_cache_len), kcp, vcp, cap, _stream(stream))
     _check(st, "ga_prefill_chunk_keys")
 
 
@@ -340,18 +429,17 @@ def ga_prefill_chunk_attention(desc: AttnDesc, q, k_cache, v_cache, cache_lens, 
                                stream=None) -> torch.Tensor:
     lib = _lib.load()
     et = _elem_dtype(desc)
-    B, n = q.shape[0], q.shape[1]
+    B, n, kcp, vcp, cap, lp, clp, _ws, wp, wb = _chunk_args(desc, q, k_cache, v_cache, cache_lens, chunk_lens,
+                                                            max_cache_len, workspace, et)
+    hd = desc.head_dim
+    d2, qp, gp = _qg(desc, q, gate, (B, n), et)
     if out is None:
-        out = torch.zeros((B, n, desc.n_q_heads * desc.head_dim), dtype=et, device=q.device)
-    d2, qp, gp = _qg(desc, q, gate, 2, et)
-    wp, wb, _keep = _chunk_workspace(d2, n, k_cache.shape[1], max_cache_len, q.device, workspace)
-    st = lib.ga_prefill_chunk_attention(ctypes.byref(d2), n, qp, _ptr(k_cache, "k_cache", et),
-                                        _ptr(v_cache, "v_cache", et), k_cache.shape[1],
-                                        _ptr(cache_lens, "cache_lens", torch.int32),
-                                        _ptr(chunk_lens, "chunk_lens", torch.int32), int(max_cache_len),
-                                        gp, _ptr(q_norm_w, "q_norm_w", torch.float32),
-                                        _ptr(positions, "positions", torch.int32), wp, wb, _ptr(out, "out", et),
-                                        _stream(stream))
+        out = torch.zeros((B, n, desc.n_q_heads * hd), dtype=et, device=q.device)
+    op = _tensor(out, "out", (B, n, desc.n_q_heads * hd), et)
+    st = lib.ga_prefill_chunk_attention(ctypes.byref(d2), n, qp, kcp, vcp, cap, lp, clp, int(max_cache_len),
+                                        gp, _norm_w(q_norm_w, "q_norm_w", desc),
+                                        _tensor(positions, "positions", (B, n), torch.int32, required=False),
+                                        wp, wb, op, _stream(stream))
     _check(st, "ga_prefill_chunk_attention")
     return out
 
@@ -368,35 +456,50 @@ def ga_prefill_backward(desc: AttnDesc, q, k, v, dout, gate=None, q_norm_w=None,
     output tensors under the same keys."""
     lib = _lib.load()
     et = _elem_dtype(desc)
-    B, n = q.shape[0], q.shape[1]
+    B, n = desc.batch, _seq(q)[1]
+    H, G, hd = desc.n_q_heads, desc.n_kv_heads, desc.head_dim
+    qshape, kshape = (B, n, H, hd), (B, n, G, hd)
+    if desc.gate_mode == _lib.GA_GATE_NONE:
+        gshape = None
+    else:
+        gshape = qshape if desc.gate_mode == _lib.GA_GATE_ELEMENTWISE else (B, n, H)
     grads = grads or {}
     dq = grads.get("dq", None)
-    dq = torch.empty_like(q) if dq is None else dq
+    dq = torch.empty(qshape, dtype=et, device=q.device) if dq is None else dq
     dk = grads.get("dk", None)
-    dk = torch.empty_like(k) if dk is None else dk
+    dk = torch.empty(kshape, dtype=et, device=q.device) if dk is None else dk
     dv = grads.get("dv", None)
-    dv = torch.empty_like(v) if dv is None else dv
+    dv = torch.empty(kshape, dtype=et, device=q.device) if dv is None else dv
     dgate = grads.get("dgate", None)
-    if dgate is None and gate is not None:
-        dgate = torch.empty_like(gate)
+    if dgate is None and gshape is not None:
+        dgate = torch.empty(gshape, dtype=et, device=q.device)
     dwq = grads.get("dq_norm_w", None)
     if dwq is None and q_norm_w is not None and weight_grads:
         dwq = torch.empty_like(q_norm_w)
     dwk = grads.get("dk_norm_w", None)
     if dwk is None and k_norm_w is not None and weight_grads:
         dwk = torch.empty_like(k_norm_w)
-    nbytes = ga_prefill_backward_workspace_bytes(desc, n)
-    if workspace is None or workspace.numel() < nbytes:
-        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
-    st = lib.ga_prefill_backward(ctypes.byref(desc), n, _ptr(q, "q", et), _ptr(k, "k", et), _ptr(v, "v", et),
-                                 _ptr(gate, "gate", et), _ptr(q_norm_w, "q_norm_w", torch.float32),
-                                 _ptr(k_norm_w, "k_norm_w", torch.float32), _ptr(positions, "positions", torch.int32),
-                                 _ptr(dout, "dout", et), _ptr(dq, "dq", et), _ptr(dk, "dk", et), _ptr(dv, "dv", et),
-                                 _ptr(dgate, "dgate", et), _ptr(dwq, "dq_norm_w", torch.float32),
-                                 _ptr(dwk, "dk_norm_w", torch.float32), _ptr(workspace, "workspace"),
-                                 workspace.numel(), _stream(stream))
+    ws, wp, wb = _workspace_arg(workspace, ga_prefill_backward_workspace_bytes(desc, n), q.device)
+    st = lib.ga_prefill_backward(ctypes.byref(desc), n, _tensor(q, "q", qshape, et), _tensor(k, "k", kshape, et),
+                                 _tensor(v, "v", kshape, et),
+                                 _tensor(gate, "gate", gshape, et) if gshape is not None else None,
+                                 _norm_w(q_norm_w, "q_norm_w", desc), _norm_w(k_norm_w, "k_norm_w", desc),
+                                 _tensor(positions, "positions", (B, n), torch.int32, required=False),
+                                 _tensor(dout, "dout", (B, n, H * hd), et), _tensor(dq, "dq", qshape, et),
+                                 _tensor(dk, "dk", kshape, et), _tensor(dv, "dv", kshape, et),
+                                 _tensor(dgate, "dgate", gshape, et) if gshape is not None else None,
+                                 _norm_w(dwq, "dq_norm_w", desc), _norm_w(dwk, "dk_norm_w", desc), wp, wb,
+                                 _stream(stream))
     _check(st, "ga_prefill_backward")
     return dict(dq=dq, dk=dk, dv=dv, dgate=dgate, dq_norm_w=dwq, dk_norm_w=dwk)
+
+
+def _decode_args(desc, q, k_cache, v_cache, cache_lens, max_cache_len, et):
+    B = desc.batch
+    if int(max_cache_len) < 0:
+        raise ValueError("max_cache_len must be >= 0")
+    kcp, vcp, cap = _cache_pair(k_cache, v_cache, desc, et, int(max_cache_len) + 1)
+    return B, kcp, vcp, cap, _lens(cache_lens, "cache_lens", B)
 
 
 def ga_decode(desc: AttnDesc, q, k_new, v_new, k_cache, v_cache, cache_lens, max_cache_len: int, gate=None,
@@ -404,16 +507,16 @@ def ga_decode(desc: AttnDesc, q, k_new, v_new, k_cache, v_cache, cache_lens, max
     """out [B,H*d] for one new token per sequence; appends K-hat/V at slot cache_lens[b]."""
     lib = _lib.load()
     et = _elem_dtype(desc)
-    B = q.shape[0]
+    B, kcp, vcp, cap, lp = _decode_args(desc, q, k_cache, v_cache, cache_lens, max_cache_len, et)
+    G, hd = desc.n_kv_heads, desc.head_dim
+    d2, qp, gp = _qg(desc, q, gate, (B,), et)
     if out is None:
-        out = torch.empty((B, desc.n_q_heads * desc.head_dim), dtype=et, device=q.device)
-    workspace = _workspace(ga_decode_workspace_bytes(desc, max_cache_len), q.device, workspace)
-    d2, qp, gp = _qg(desc, q, gate, 1, et)
-    st = lib.ga_decode(ctypes.byref(d2), qp, _ptr(k_new, "k_new", et), _ptr(v_new, "v_new", et),
-                       gp, _ptr(q_norm_w, "q_norm_w", torch.float32),
-                       _ptr(k_norm_w, "k_norm_w", torch.float32), _ptr(k_cache, "k_cache", et),
-                       _ptr(v_cache, "v_cache", et), k_cache.shape[1], _ptr(cache_lens, "cache_lens", torch.int32),
-                       int(max_cache_len), _ptr(workspace, "workspace"), workspace.numel(), _ptr(out, "out", et),
+        out = torch.empty((B, desc.n_q_heads * hd), dtype=et, device=q.device)
+    op = _tensor(out, "out", (B, desc.n_q_heads * hd), et)
+    ws, wp, wb = _workspace_arg(workspace, ga_decode_workspace_bytes(desc, max_cache_len), q.device)
+    st = lib.ga_decode(ctypes.byref(d2), qp, _tensor(k_new, "k_new", (B, G, hd), et),
+                       _tensor(v_new, "v_new", (B, G, hd), et), gp, _norm_w(q_norm_w, "q_norm_w", desc),
+                       _norm_w(k_norm_w, "k_norm_w", desc), kcp, vcp, cap, lp, int(max_cache_len), wp, wb, op,
                        _stream(stream))
     _check(st, "ga_decode")
     return out
@@ -423,28 +526,36 @@ def ga_decode_partials(desc: AttnDesc, q, k_cache, v_cache, cache_lens, max_cach
                        q_norm_w=None, stream=None) -> torch.Tensor:
     lib = _lib.load()
     et = _elem_dtype(desc)
-    d2, qp, _ = _qg(desc, q, None, 1, et)
-    st = lib.ga_decode_partials(ctypes.byref(d2), qp, _ptr(q_norm_w, "q_norm_w", torch.float32),
-                                _ptr(k_cache, "k_cache", et), _ptr(v_cache, "v_cache", et), k_cache.shape[1],
-                                _ptr(cache_lens, "cache_lens", torch.int32), int(max_cache_len),
-                                _ptr(workspace, "workspace"), workspace.numel(), _stream(stream))
+    B, kcp, vcp, cap, lp = _decode_args(desc, q, k_cache, v_cache, cache_lens, max_cache_len, et)
+    d2, qp, _ = _qg(_no_gate(desc), q, None, (B,), et)  # (the partials read no gate)
+    ws, wp, wb = _workspace_arg(workspace, ga_decode_workspace_bytes(desc, max_cache_len), q.device)
+    st = lib.ga_decode_partials(ctypes.byref(d2), qp, _norm_w(q_norm_w, "q_norm_w", desc), kcp, vcp, cap, lp,
+                                int(max_cache_len), wp, wb, _stream(stream))
     _check(st, "ga_decode_partials")
-    return workspace
+    return ws
+
+
+def _no_gate(desc: AttnDesc) -> AttnDesc:
+    d2 = AttnDesc.from_buffer_copy(desc)
+    d2.gate_mode = _lib.GA_GATE_NONE
+    d2.gate_share = 0
+    return d2
 
 
 def ga_decode_merge(desc: AttnDesc, q, k_new, v_new, k_cache, v_cache, cache_lens, max_cache_len: int, workspace,
                     gate=None, q_norm_w=None, k_norm_w=None, out=None, stream=None) -> torch.Tensor:
     lib = _lib.load()
     et = _elem_dtype(desc)
-    B = q.shape[0]
+    B, kcp, vcp, cap, lp = _decode_args(desc, q, k_cache, v_cache, cache_lens, max_cache_len, et)
+    G, hd = desc.n_kv_heads, desc.head_dim
+    d2, qp, gp = _qg(desc, q, gate, (B,), et)
     if out is None:
-        out = torch.empty((B, desc.n_q_heads * desc.head_dim), dtype=et, device=q.device)
-    d2, qp, gp = _qg(desc, q, gate, 1, et)
-    st = lib.ga_decode_merge(ctypes.byref(d2), qp, _ptr(k_new, "k_new", et), _ptr(v_new, "v_new", et),
-                             gp, _ptr(q_norm_w, "q_norm_w", torch.float32),
-                             _ptr(k_norm_w, "k_norm_w", torch.float32), _ptr(k_cache, "k_cache", et),
-                             _ptr(v_cache, "v_cache", et), k_cache.shape[1],
-                             _ptr(cache_lens, "cache_lens", torch.int32), int(max_cache_len),
-                             _ptr(workspace, "workspace"), workspace.numel(), _ptr(out, "out", et), _stream(stream))
+        out = torch.empty((B, desc.n_q_heads * hd), dtype=et, device=q.device)
+    op = _tensor(out, "out", (B, desc.n_q_heads * hd), et)
+    ws, wp, wb = _workspace_arg(workspace, ga_decode_workspace_bytes(desc, max_cache_len), q.device)
+    st = lib.ga_decode_merge(ctypes.byref(d2), qp, _tensor(k_new, "k_new", (B, G, hd), et),
+                             _tensor(v_new, "v_new", (B, G, hd), et), gp, _norm_w(q_norm_w, "q_norm_w", desc),
+                             _norm_w(k_norm_w, "k_norm_w", desc), kcp, vcp, cap, lp, int(max_cache_len), wp, wb,
+                             op, _stream(stream))
     _check(st, "ga_decode_merge")
     return out

@@ -63,6 +63,10 @@ ga_status check_desc(const ga_attn_desc* d) {
     return fail(GA_ERR_BAD_DTYPE, "gate_combine %d out of range", d->gate_combine);
   if (d->gate_share < 0 || d->gate_share > (GA_SHARE_HEADS | GA_SHARE_TOKENS))
     return fail(GA_ERR_BAD_DTYPE, "gate_share %d out of range", d->gate_share);
+  if (d->kernel < GA_KERNEL_AUTO || d->kernel > GA_KERNEL_GENERIC)
+    return fail(GA_ERR_BAD_DTYPE, "kernel %d out of range", d->kernel);
+  if (d->bwd_kernel < GA_BWD_AUTO || d->bwd_kernel > GA_BWD_PLAIN)
+    return fail(GA_ERR_BAD_DTYPE, "bwd_kernel %d out of range", d->bwd_kernel);
   if (d->out_norm_w) {
     if (!(d->out_norm_eps >= 0.f && isfinite(d->out_norm_eps)))
       return fail(GA_ERR_BAD_SHAPE, "out_norm_eps must be finite, >= 0");
@@ -149,51 +153,10 @@ bool prefill_wide_ok(const ga_attn_desc* d, int32_t n, int32_t k_cap, int32_t v_
   return !require_large || blocks >= 512;
 }
 
-// Kernel choice for prefill attention: automatic, or forced (when the forced
-// kernel serves the shape) by GA_PREFILL_KERNEL = wide | split | mirror | simple | generic.
-enum PrefillKernel { PK_AUTO, PK_WIDE, PK_SPLIT, PK_MIRROR, PK_SIMPLE, PK_GENERIC };
-PrefillKernel prefill_kernel_request() {
-  const char* e = getenv("GA_PREFILL_KERNEL");
-  if (!e) return PK_AUTO;
-  if (!strcmp(e, "wide")) return PK_WIDE;
-  if (!strcmp(e, "split")) return PK_SPLIT;
-  if (!strcmp(e, "mirror")) return PK_MIRROR;
-  if (!strcmp(e, "simple")) return PK_SIMPLE;
-  if (!strcmp(e, "generic")) return PK_GENERIC;
-  return PK_AUTO;
-}
-
-// Split-key balance: the second workgroup of a pair, which also runs the light
-// unit, gets this many fewer stages of the heavy unit, for its extra prologue
-// and epilogue (GA_PREFILL_SPLIT_BIAS overrides it, for tuning).
-int split_overhead_stages() {
-  const char* e = getenv("GA_PREFILL_SPLIT_BIAS");
-  if (e && *e) {
-    const int v = atoi(e);
-    return v < 0 ? 0 : (v > 64 ? 64 : v);
-  }
-  return 8;
-}
-
-// The kernel prefill attention runs for a shape (automatic choice: wide, then
-// mirrored, then simple, then generic; the split-key mode only on request).
-PrefillKernel prefill_choice(const ga_attn_desc* d, int32_t n, int32_t k_cap, int32_t v_cap);
-
-// Mirrored-kernel units (two blocks of 64 rows) and unit pairs per (batch, KV head).
-void split_shape(const ga_attn_desc* d, int32_t n, int* nunits, int* npairs) {
-  const int tb = 64 / (d->n_q_heads / d->n_kv_heads);
-  const int nblk = (n + tb - 1) / tb;
-  *nunits = (nblk + 1) / 2;
-  *npairs = (*nunits + 1) / 2;
-}
-
-// Workspace bytes of the attention stage (nonzero only for the split-key mode).
-size_t prefill_attn_ws_bytes(const ga_attn_desc* d, int32_t n, int32_t k_cap, int32_t v_cap) {
-  if (d->batch <= 0 || n <= 0 || prefill_choice(d, n, k_cap, v_cap) != PK_SPLIT) return 0;
-  int nunits, npairs;
-  split_shape(d, n, &nunits, &npairs);
-  return prefill_split_bytes((long)d->batch * d->n_kv_heads * npairs, d->head_dim);
-}
+// Kernel choice for prefill attention: automatic, or the one the descriptor's
+// ``kernel`` field names (an error when that kernel does not serve the shape).
+enum PrefillKernel { PK_INVALID = -1, PK_AUTO = GA_KERNEL_AUTO, PK_WIDE = GA_KERNEL_WIDE, PK_MIRROR = GA_KERNEL_MIRROR,
+                     PK_SIMPLE = GA_KERNEL_SIMPLE, PK_GENERIC = GA_KERNEL_GENERIC };
 
 bool prefill_fast(const ga_attn_desc* d) {
   const int grp = d->n_q_heads / d->n_kv_heads;
@@ -202,18 +165,18 @@ bool prefill_fast(const ga_attn_desc* d) {
          grp <= 128;
 }
 
+// PK_INVALID when a forced kernel does not serve the shape.
 PrefillKernel prefill_choice(const ga_attn_desc* d, int32_t n, int32_t k_cap, int32_t v_cap) {
-  const PrefillKernel req = prefill_kernel_request();
   // (the mirrored kernel numbers output rows (b, token, head) in 32 bits)
   const bool v2 = prefill_v2_ok(d, k_cap, v_cap) && (long long)d->batch * n * d->n_q_heads < (1LL << 31);
-  if (req == PK_WIDE && prefill_wide_ok(d, n, k_cap, v_cap, false)) return PK_WIDE;
-  if (req == PK_SPLIT && v2 && !gate_ext(d)) return PK_SPLIT;
-  if (req == PK_MIRROR && v2) return PK_MIRROR;
-  if (req == PK_SIMPLE && prefill_fast(d)) return PK_SIMPLE;
-  if (req == PK_GENERIC) return PK_GENERIC;
+  switch (d->kernel) {
+    case GA_KERNEL_WIDE: return prefill_wide_ok(d, n, k_cap, v_cap, false) ? PK_WIDE : PK_INVALID;
+    case GA_KERNEL_MIRROR: return v2 ? PK_MIRROR : PK_INVALID;
+    case GA_KERNEL_SIMPLE: return prefill_fast(d) ? PK_SIMPLE : PK_INVALID;
+    case GA_KERNEL_GENERIC: return PK_GENERIC;
+    default: break;
+  }
   if (prefill_wide_ok(d, n, k_cap, v_cap, true)) return PK_WIDE;
-  // (the split-key mode is opt-in: on the measured shapes its extra
-  // workgroup prologues and epilogues cost more than the balance gains)
   if (v2) return PK_MIRROR;
   if (prefill_fast(d)) return PK_SIMPLE;
   return PK_GENERIC;
@@ -241,6 +204,12 @@ ga_status check_gate(const void* gate, const ga_attn_desc* d) {
   if (!gate) return fail(GA_ERR_NULL_ARG, "gate is NULL but gate_mode is %d", d->gate_mode);
   const size_t a = d->gate_mode == GA_GATE_ELEMENTWISE ? (d->dtype == GA_BF16 ? 16 : 4) : (size_t)elem_bytes(d);
   if (!aligned(gate, a)) return fail(GA_ERR_MISALIGNED, "gate is not %zu-byte aligned", a);
+  return GA_OK;
+}
+
+// RMSNorm weights: [d] float32, read by the fused kernels in 16-byte pieces.
+ga_status check_norm_w(const float* w, const char* name) {
+  if (w && !aligned(w, 16)) return fail(GA_ERR_MISALIGNED, "%s is not 16-byte aligned", name);
   return GA_OK;
 }
 
@@ -284,18 +253,14 @@ ga_status prefill_keys_impl(const ga_attn_desc* desc, int32_t n, const void* k, 
   return hip_status(launch_prep_keys(pp, desc->dtype == GA_BF16, stream), "prefill keys launch");
 }
 
-// workspace: at least prefill_attn_ws_bytes(desc, n, k_cap, v_cap) bytes
-// (checked by the callers), 16-byte aligned; may be NULL when that is 0.
 ga_status prefill_attn_impl(const ga_attn_desc* desc, int32_t n, const void* q, const void* k_hat,
                             int32_t k_cap, const void* v, int32_t v_cap, const void* gate,
-                            const float* q_norm_w, const int32_t* positions, void* workspace, void* out,
-                            hipStream_t stream) {
+                            const float* q_norm_w, const int32_t* positions, void* out, hipStream_t stream) {
   const int H = desc->n_q_heads, G = desc->n_kv_heads, d = desc->head_dim;
   const int grp = H / G;
   const PrefillKernel choice = prefill_choice(desc, n, k_cap, v_cap);
   const bool wide = choice == PK_WIDE;
-  const bool split = choice == PK_SPLIT;
-  const bool v2 = split || choice == PK_MIRROR;
+  const bool v2 = choice == PK_MIRROR;
   const bool v1 = choice == PK_SIMPLE;
   if (wide || v2 || v1) {
     PrefillParams pp;
@@ -326,17 +291,6 @@ ga_status prefill_attn_impl(const ga_attn_desc* desc, int32_t n, const void* q, 
     pp.scale_log2 = scale_of(desc) * 1.4426950408889634f;
     fill_inv_freq(desc, pp.inv_freq);
     if ((long long)pp.B * G * pp.nblk > 0x7fffffffLL) return fail(GA_ERR_UNSUPPORTED, "grid too large");
-    if (split) {
-      split_shape(desc, n, &pp.nunits, &pp.npairs);
-      const size_t slots = (size_t)pp.B * G * pp.npairs;
-      auto r256 = [](size_t x) { return (x + 255) / 256 * 256; };
-      char* base = (char*)workspace;
-      pp.part = (float*)base;
-      pp.part_lse = (float*)(base + r256(slots * 128 * d * 4));
-      pp.sync = (unsigned*)(base + r256(slots * 128 * d * 4) + r256(slots * 128 * 4));
-      pp.split = 1;
-      pp.split_ovh = split_overhead_stages();
-    }
     if (wide) return hip_status(launch_prefill_wide(pp, d, gate_arg(desc), stream), "prefill attention launch");
     if (v2) return hip_status(launch_prefill_v2(pp, d, gate_arg(desc), stream), "prefill attention launch");
     return hip_status(launch_prefill_mfma(pp, d, gate_arg(desc), stream), "prefill attention launch");
@@ -370,33 +324,21 @@ ga_status prefill_attn_impl(const ga_attn_desc* desc, int32_t n, const void* q, 
 }
 
 // Kernel of a chunk against a cache: the mirrored kernel (with per-sequence key
-// offsets) where it serves the shape, else the generic one.
-bool chunk_uses_mirror(const ga_attn_desc* d, int32_t n, int32_t cache_cap) {
-  return prefill_kernel_request() != PK_GENERIC && prefill_v2_ok(d, cache_cap, cache_cap) &&
-         (long long)d->batch * n * d->n_q_heads < (1LL << 31);
+// offsets) where it serves the shape, else the generic one; the descriptor
+// may force either (an error for a forced mirrored kernel that does not serve it).
+PrefillKernel chunk_choice(const ga_attn_desc* d, int32_t n, int32_t cache_cap) {
+  const bool mirror = prefill_v2_ok(d, cache_cap, cache_cap) && (long long)d->batch * n * d->n_q_heads < (1LL << 31);
+  switch (d->kernel) {
+    case GA_KERNEL_AUTO: return mirror ? PK_MIRROR : PK_GENERIC;
+    case GA_KERNEL_MIRROR: return mirror ? PK_MIRROR : PK_INVALID;
+    case GA_KERNEL_GENERIC: return PK_GENERIC;
+    default: return PK_INVALID;
+  }
 }
 
-// Cached prefixes of different lengths give the chunk's workgroups different
-// amounts of work: on request (GA_PREFILL_CHUNK_SPLIT=1, read at each call)
-// each mirrored pair's key range is cut in two workgroups whose partial rows
-// meet in the workspace, when the cache may hold a stage of keys. Opt-in: on
-// the measured chunk workload the two prologues and epilogues per pair and the
-// split instantiation's register spills cost more than the balance gains.
-bool chunk_split(const ga_attn_desc* d, int32_t n, int32_t cap, int32_t max_cache_len) {
-  const char* e = getenv("GA_PREFILL_CHUNK_SPLIT");
-  if (!e || strcmp(e, "1")) return false;
-  return chunk_uses_mirror(d, n, cap) && !gate_ext(d) && max_cache_len >= 64;
-}
-
-int chunk_npairs(const ga_attn_desc* d, int32_t n) {
-  const int tb = 64 / (d->n_q_heads / d->n_kv_heads);
-  return ((n + tb - 1) / tb + 1) / 2;
-}
-
-size_t chunk_ws_bytes(const ga_attn_desc* d, int32_t n, int32_t cap, int32_t max_cache_len) {
-  if (d->batch <= 0 || n <= 0 || !chunk_split(d, n, cap, max_cache_len)) return 0;
-  return prefill_split_bytes((long)d->batch * d->n_kv_heads * chunk_npairs(d, n), d->head_dim);
-}
+// Workspace of the chunk kernels: none today (kept in the ABI for kernels
+// that keep partial results).
+size_t chunk_ws_bytes(const ga_attn_desc*, int32_t, int32_t, int32_t) { return 0; }
 
 ga_status check_chunk_workspace(const ga_attn_desc* d, int32_t n, int32_t cap, int32_t max_cache_len,
                                 const void* workspace, size_t workspace_bytes) {
@@ -427,9 +369,12 @@ ga_status chunk_attn_impl(const ga_attn_desc* desc, int32_t n, const void* q, co
                           const void* v_cache, int32_t cap, const int32_t* cache_lens, const int32_t* chunk_lens,
                           int32_t max_cache_len, const void* gate, const float* q_norm_w, const int32_t* positions,
                           void* workspace, void* out, hipStream_t stream) {
+  (void)workspace;
   const int H = desc->n_q_heads, G = desc->n_kv_heads, d = desc->head_dim;
   const int grp = H / G;
-  if (chunk_uses_mirror(desc, n, cap)) {
+  const PrefillKernel choice = chunk_choice(desc, n, cap);
+  if (choice == PK_INVALID) return fail(GA_ERR_UNSUPPORTED, "the forced kernel does not serve this chunk shape");
+  if (choice == PK_MIRROR) {
     PrefillParams pp;
     memset(&pp, 0, sizeof(pp));
     pp.q = (const uint16_t*)q;
@@ -461,16 +406,6 @@ ga_status chunk_attn_impl(const ga_attn_desc* desc, int32_t n, const void* q, co
     pp.scale_log2 = scale_of(desc) * 1.4426950408889634f;
     fill_inv_freq(desc, pp.inv_freq);
     if ((long long)pp.B * G * pp.nblk > 0x7fffffffLL) return fail(GA_ERR_UNSUPPORTED, "grid too large");
-    if (chunk_split(desc, n, cap, max_cache_len)) {
-      pp.npairs = chunk_npairs(desc, n);
-      const size_t slots = (size_t)pp.B * G * pp.npairs;
-      auto r256 = [](size_t x) { return (x + 255) / 256 * 256; };
-      char* base = (char*)workspace;
-      pp.part = (float*)base;
-      pp.part_lse = (float*)(base + r256(slots * 128 * d * 4));
-      pp.sync = (unsigned*)(base + r256(slots * 128 * d * 4) + r256(slots * 128 * 4));
-      pp.split = 1;
-    }
     return hip_status(launch_prefill_v2(pp, d, gate_arg(desc), stream), "chunk attention launch");
   }
   NaiveParams np;
@@ -632,6 +567,8 @@ ga_status ga_prefill_backward(const ga_attn_desc* desc, int32_t seq_len, const v
     if ((st = check_tensor(ptrs[i], names[i], desc)) != GA_OK) return st;
   if ((st = check_gate(gate, desc)) != GA_OK) return st;
   if (desc->gate_mode != GA_GATE_NONE && (st = check_gate(dgate, desc)) != GA_OK) return st;
+  if ((st = check_norm_w(q_norm_w, "q_norm_w")) != GA_OK) return st;
+  if ((st = check_norm_w(k_norm_w, "k_norm_w")) != GA_OK) return st;
   const BwdLayout L = bwd_layout(desc, seq_len);
   if (!workspace || workspace_bytes < L.total)
     return fail(GA_ERR_WORKSPACE, "workspace %zu bytes < %zu required", workspace ? workspace_bytes : 0, L.total);
@@ -725,6 +662,7 @@ ga_status ga_prefill_backward(const ga_attn_desc* desc, int32_t seq_len, const v
   bp.G = G;
   bp.grp = H / G;
   bp.gate_mode = desc->gate_mode;
+  bp.plain = desc->bwd_kernel == GA_BWD_PLAIN;
   bp.scale = scale_of(desc);
   bp.scale_log2 = bp.scale * 1.4426950408889634f;
   if ((st = hip_status(launch_bwd_pre(bp, D, s), "backward gate launch")) != GA_OK) return st;
@@ -768,22 +706,17 @@ const char* ga_prefill_attention_kernel(const ga_attn_desc* desc, int32_t seq_le
   if (check_desc(desc) != GA_OK || seq_len < 0) return "invalid";
   switch (prefill_choice(desc, seq_len, seq_len, seq_len)) {
     case PK_WIDE: return "wide";
-    case PK_SPLIT: return "split";
     case PK_MIRROR: return "mirror";
     case PK_SIMPLE: return "simple";
-    default: return "generic";
+    case PK_GENERIC: return "generic";
+    default: return "unsupported";
   }
-}
-
-size_t ga_prefill_attention_workspace_bytes(const ga_attn_desc* desc, int32_t seq_len) {
-  if (check_desc(desc) != GA_OK || seq_len < 0) return 0;
-  return prefill_attn_ws_bytes(desc, seq_len, seq_len, seq_len);
 }
 
 size_t ga_prefill_workspace_bytes(const ga_attn_desc* desc, int32_t seq_len) {
   if (check_desc(desc) != GA_OK || seq_len < 0) return 0;
   const size_t elems = (size_t)desc->batch * seq_len * desc->n_kv_heads * desc->head_dim;
-  return round_up(elems * elem_bytes(desc), 256) + prefill_attn_ws_bytes(desc, seq_len, seq_len, seq_len);
+  return round_up(elems * elem_bytes(desc), 256);
 }
 
 ga_status ga_prefill_keys(const ga_attn_desc* desc, int32_t seq_len, const void* k, const void* v,
@@ -795,6 +728,7 @@ ga_status ga_prefill_keys(const ga_attn_desc* desc, int32_t seq_len, const void*
   if (desc->batch == 0 || seq_len == 0) return ok();
   if ((st = check_tensor(k, "k", desc)) != GA_OK) return st;
   if ((st = check_tensor(k_hat, "k_hat", desc)) != GA_OK) return st;
+  if ((st = check_norm_w(k_norm_w, "k_norm_w")) != GA_OK) return st;
   if (v_out) {
     if ((st = check_tensor(v, "v", desc)) != GA_OK) return st;
     if ((st = check_tensor(v_out, "v_out", desc)) != GA_OK) return st;
@@ -805,8 +739,7 @@ ga_status ga_prefill_keys(const ga_attn_desc* desc, int32_t seq_len, const void*
 
 ga_status ga_prefill_attention(const ga_attn_desc* desc, int32_t seq_len, const void* q, const void* k_hat,
                                int32_t k_cap, const void* v, int32_t v_cap, const void* gate,
-                               const float* q_norm_w, const int32_t* positions, void* workspace,
-                               size_t workspace_bytes, void* out, void* stream) {
+                               const float* q_norm_w, const int32_t* positions, void* out, void* stream) {
   ga_status st;
   if ((st = check_desc(desc)) != GA_OK) return st;
   if (seq_len < 0) return fail(GA_ERR_BAD_SHAPE, "seq_len %d < 0", seq_len);
@@ -816,14 +749,13 @@ ga_status ga_prefill_attention(const ga_attn_desc* desc, int32_t seq_len, const 
   if ((st = check_tensor(v, "v", desc)) != GA_OK) return st;
   if ((st = check_tensor(out, "out", desc)) != GA_OK) return st;
   if ((st = check_gate(gate, desc)) != GA_OK) return st;
+  if ((st = check_norm_w(q_norm_w, "q_norm_w")) != GA_OK) return st;
   if (k_cap < seq_len || v_cap < seq_len)
     return fail(GA_ERR_BAD_SHAPE, "k_cap %d / v_cap %d < seq_len %d", k_cap, v_cap, seq_len);
-  const size_t need = prefill_attn_ws_bytes(desc, seq_len, k_cap, v_cap);
-  if (need && (!workspace || workspace_bytes < need))
-    return fail(GA_ERR_WORKSPACE, "workspace %zu bytes < %zu required", workspace ? workspace_bytes : 0, need);
-  if (need && !aligned(workspace, 16)) return fail(GA_ERR_MISALIGNED, "workspace is not 16-byte aligned");
+  if (prefill_choice(desc, seq_len, k_cap, v_cap) == PK_INVALID)
+    return fail(GA_ERR_UNSUPPORTED, "the forced kernel %d does not serve this shape", desc->kernel);
   return prefill_attn_impl(desc, seq_len, q, k_hat, k_cap, v, v_cap,
-                           desc->gate_mode == GA_GATE_NONE ? nullptr : gate, q_norm_w, positions, workspace, out,
+                           desc->gate_mode == GA_GATE_NONE ? nullptr : gate, q_norm_w, positions, out,
                            (hipStream_t)stream);
 }
 
@@ -840,9 +772,10 @@ ga_status ga_prefill(const ga_attn_desc* desc, int32_t seq_len, const void* q, c
   if ((st = check_tensor(v, "v", desc)) != GA_OK) return st;
   if ((st = check_tensor(out, "out", desc)) != GA_OK) return st;
   if ((st = check_gate(gate, desc)) != GA_OK) return st;
+  if ((st = check_norm_w(q_norm_w, "q_norm_w")) != GA_OK) return st;
+  if ((st = check_norm_w(k_norm_w, "k_norm_w")) != GA_OK) return st;
   void* khat;
   int32_t kcap;
-  size_t khat_bytes = 0;
   if (k_cache) {
     if ((st = check_tensor(k_cache, "k_cache", desc)) != GA_OK) return st;
     if ((st = check_tensor(v_cache, "v_cache", desc)) != GA_OK) return st;
@@ -851,26 +784,28 @@ ga_status ga_prefill(const ga_attn_desc* desc, int32_t seq_len, const void* q, c
     kcap = cache_cap;
   } else {
     if (v_cache) return fail(GA_ERR_NULL_ARG, "v_cache given without k_cache");
+    const size_t need = ga_prefill_workspace_bytes(desc, seq_len);
+    if (!workspace || workspace_bytes < need)
+      return fail(GA_ERR_WORKSPACE, "workspace %zu bytes < %zu required", workspace ? workspace_bytes : 0, need);
+    if (!aligned(workspace, 16)) return fail(GA_ERR_MISALIGNED, "workspace is not 16-byte aligned");
     khat = workspace;
     kcap = seq_len;
-    khat_bytes = round_up((size_t)desc->batch * seq_len * desc->n_kv_heads * desc->head_dim * elem_bytes(desc), 256);
   }
-  // attention part of the workspace: after K-hat (no cache) or from its start
-  const size_t attn_need = prefill_attn_ws_bytes(desc, seq_len, kcap, seq_len);
-  const size_t need = khat_bytes + attn_need;
-  if (need && (!workspace || workspace_bytes < need))
-    return fail(GA_ERR_WORKSPACE, "workspace %zu bytes < %zu required", workspace ? workspace_bytes : 0, need);
-  if (need && !aligned(workspace, 16)) return fail(GA_ERR_MISALIGNED, "workspace is not 16-byte aligned");
-  void* attn_ws = attn_need ? (void*)((char*)workspace + khat_bytes) : nullptr;
+  if (prefill_choice(desc, seq_len, kcap, seq_len) == PK_INVALID)
+    return fail(GA_ERR_UNSUPPORTED, "the forced kernel %d does not serve this shape", desc->kernel);
   hipStream_t s = (hipStream_t)stream;
   if ((st = prefill_keys_impl(desc, seq_len, k, v, k_norm_w, positions, khat, v_cache, kcap, s)) != GA_OK) return st;
   return prefill_attn_impl(desc, seq_len, q, khat, kcap, v, seq_len,
-                           desc->gate_mode == GA_GATE_NONE ? nullptr : gate, q_norm_w, positions, attn_ws, out, s);
+                           desc->gate_mode == GA_GATE_NONE ? nullptr : gate, q_norm_w, positions, out, s);
 }
 
 const char* ga_prefill_chunk_kernel(const ga_attn_desc* desc, int32_t seq_len, int32_t cache_cap) {
   if (check_desc(desc) != GA_OK || seq_len < 0 || cache_cap < 0) return "invalid";
-  return chunk_uses_mirror(desc, seq_len, cache_cap) ? "mirror" : "generic";
+  switch (chunk_choice(desc, seq_len, cache_cap)) {
+    case PK_MIRROR: return "mirror";
+    case PK_GENERIC: return "generic";
+    default: return "unsupported";
+  }
 }
 
 size_t ga_prefill_chunk_workspace_bytes(const ga_attn_desc* desc, int32_t seq_len, int32_t cache_cap,
@@ -889,6 +824,7 @@ ga_status ga_prefill_chunk_keys(const ga_attn_desc* desc, int32_t seq_len, const
   if (desc->batch == 0 || seq_len == 0) return ok();
   if ((st = check_tensor(k, "k", desc)) != GA_OK) return st;
   if ((st = check_tensor(v, "v", desc)) != GA_OK) return st;
+  if ((st = check_norm_w(k_norm_w, "k_norm_w")) != GA_OK) return st;
   if ((st = check_chunk_common(desc, seq_len, k_cache, v_cache, cache_cap, cache_lens, max_cache_len)) != GA_OK)
     return st;
   return prefill_keys_impl(desc, seq_len, k, v, k_norm_w, positions, k_cache, v_cache, cache_cap,
@@ -907,10 +843,13 @@ ga_status ga_prefill_chunk_attention(const ga_attn_desc* desc, int32_t seq_len, 
   if ((st = check_tensor(q, "q", desc)) != GA_OK) return st;
   if ((st = check_tensor(out, "out", desc)) != GA_OK) return st;
   if ((st = check_gate(gate, desc)) != GA_OK) return st;
+  if ((st = check_norm_w(q_norm_w, "q_norm_w")) != GA_OK) return st;
   if ((st = check_chunk_common(desc, seq_len, k_cache, v_cache, cache_cap, cache_lens, max_cache_len)) != GA_OK)
     return st;
   if ((st = check_chunk_workspace(desc, seq_len, cache_cap, max_cache_len, workspace, workspace_bytes)) != GA_OK)
     return st;
+  if (chunk_choice(desc, seq_len, cache_cap) == PK_INVALID)
+    return fail(GA_ERR_UNSUPPORTED, "the forced kernel %d does not serve this chunk shape", desc->kernel);
   return chunk_attn_impl(desc, seq_len, q, k_cache, v_cache, cache_cap, cache_lens, chunk_lens, max_cache_len,
                          desc->gate_mode == GA_GATE_NONE ? nullptr : gate, q_norm_w, positions, workspace, out,
                          (hipStream_t)stream);
@@ -930,10 +869,14 @@ ga_status ga_prefill_chunk(const ga_attn_desc* desc, int32_t seq_len, const void
   if ((st = check_tensor(v, "v", desc)) != GA_OK) return st;
   if ((st = check_tensor(out, "out", desc)) != GA_OK) return st;
   if ((st = check_gate(gate, desc)) != GA_OK) return st;
+  if ((st = check_norm_w(q_norm_w, "q_norm_w")) != GA_OK) return st;
+  if ((st = check_norm_w(k_norm_w, "k_norm_w")) != GA_OK) return st;
   if ((st = check_chunk_common(desc, seq_len, k_cache, v_cache, cache_cap, cache_lens, max_cache_len)) != GA_OK)
     return st;
   if ((st = check_chunk_workspace(desc, seq_len, cache_cap, max_cache_len, workspace, workspace_bytes)) != GA_OK)
     return st;
+  if (chunk_choice(desc, seq_len, cache_cap) == PK_INVALID)
+    return fail(GA_ERR_UNSUPPORTED, "the forced kernel %d does not serve this chunk shape", desc->kernel);
   hipStream_t s = (hipStream_t)stream;
   if ((st = prefill_keys_impl(desc, seq_len, k, v, k_norm_w, positions, k_cache, v_cache, cache_cap, s, cache_lens,
                               chunk_lens, max_cache_len)) != GA_OK)
@@ -960,6 +903,7 @@ ga_status ga_decode_partials(const ga_attn_desc* desc, const void* q, const floa
     return fail(GA_ERR_UNSUPPORTED, "decode stages need the fused path (bf16, d in {64,128,256}, rot %% 16 == 0, "
                                     "group in {1,2,4,8,16}, cache_cap * G * d * 2 < 2^31)");
   if ((st = check_decode_common(desc, q, k_cache, v_cache, cache_cap, cache_lens, max_cache_len)) != GA_OK) return st;
+  if ((st = check_norm_w(q_norm_w, "q_norm_w")) != GA_OK) return st;
   const size_t need = ga_decode_workspace_bytes(desc, max_cache_len);
   if (!workspace || workspace_bytes < need)
     return fail(GA_ERR_WORKSPACE, "workspace %zu bytes < %zu required", workspace ? workspace_bytes : 0, need);
@@ -985,6 +929,8 @@ ga_status ga_decode_merge(const ga_attn_desc* desc, const void* q, const void* k
   if ((st = check_tensor(v_new, "v_new", desc)) != GA_OK) return st;
   if ((st = check_tensor(out, "out", desc)) != GA_OK) return st;
   if ((st = check_gate(gate, desc)) != GA_OK) return st;
+  if ((st = check_norm_w(q_norm_w, "q_norm_w")) != GA_OK) return st;
+  if ((st = check_norm_w(k_norm_w, "k_norm_w")) != GA_OK) return st;
   const size_t need = ga_decode_workspace_bytes(desc, max_cache_len);
   if (!workspace || workspace_bytes < need)
     return fail(GA_ERR_WORKSPACE, "workspace %zu bytes < %zu required", workspace ? workspace_bytes : 0, need);
@@ -1008,6 +954,8 @@ ga_status ga_decode(const ga_attn_desc* desc, const void* q, const void* k_new, 
   if ((st = check_tensor(v_new, "v_new", desc)) != GA_OK) return st;
   if ((st = check_tensor(out, "out", desc)) != GA_OK) return st;
   if ((st = check_gate(gate, desc)) != GA_OK) return st;
+  if ((st = check_norm_w(q_norm_w, "q_norm_w")) != GA_OK) return st;
+  if ((st = check_norm_w(k_norm_w, "k_norm_w")) != GA_OK) return st;
   hipStream_t s = (hipStream_t)stream;
   if (decode_fast(desc, cache_cap)) {
     if ((st = ga_decode_partials(desc, q, q_norm_w, k_cache, v_cache, cache_cap, cache_lens, max_cache_len,
@@ -1078,6 +1026,6 @@ int32_t ga_fast_path(int32_t dtype, int32_t head_dim, int32_t rot_dim, int32_t g
   return (prefill_fast(&d) ? 1 : 0) | (decode_fast(&d, 0) ? 2 : 0);
 }
 
-int32_t ga_version(void) { return 3; }
+int32_t ga_version(void) { return 4; }
 
 }  // extern "C"

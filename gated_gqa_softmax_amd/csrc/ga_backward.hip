@@ -827,14 +827,12 @@ hipError_t launch_bwd_dv_sum(const float* dvp, uint16_t* dv, int B, int n, int H
 
 // The staged kernel serves d = 128 and 256 when its workgroup's heads share
 // one KV group and an operand slice fits the buffer loads' 32-bit offsets;
-// GA_BWD_DQ_KERNEL=plain selects the register-operand kernel everywhere.
+// p.plain selects the register-operand kernel everywhere.
 static bool dq_staged_ok(const BwdParams& p, int D) {
-  if (D < 128) return false;
+  if (D < 128 || p.plain) return false;
   const int hpw = 4 / (D / 128);
   if (p.grp % hpw != 0) return false;
-  if ((long)p.npad * D * 2 >= (1L << 31)) return false;
-  const char* e = getenv("GA_BWD_DQ_KERNEL");
-  return !(e && strcmp(e, "plain") == 0);
+  return (long)p.npad * D * 2 < (1L << 31);
 }
 
 template <int D>
@@ -854,12 +852,10 @@ static hipError_t launch_dq_d(const BwdParams& p, hipStream_t s) {
   return hipGetLastError();
 }
 
-// GA_BWD_DKV_KERNEL=plain selects the register-operand kernel everywhere.
+// p.plain selects the register-operand kernel everywhere.
 static bool dkv_staged_ok(const BwdParams& p, int D) {
-  if (D < 128) return false;
-  if ((long)p.npad * D * 2 >= (1L << 31) || (long)p.B * p.n * p.H * 4 >= (1L << 31)) return false;
-  const char* e = getenv("GA_BWD_DKV_KERNEL");
-  return !(e && strcmp(e, "plain") == 0);
+  if (D < 128 || p.plain) return false;
+  return (long)p.npad * D * 2 < (1L << 31) && (long)p.B * p.n * p.H * 4 < (1L << 31);
 }
 
 template <int D>

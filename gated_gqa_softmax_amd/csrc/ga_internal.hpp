@@ -63,15 +63,6 @@ struct PrefillParams {
   GateEpi ge;
   int B, n, H, G, grp, TB, nblk, rot, half, use_table;
   float eps, scale_log2;
-  // Split-key mode of the mirrored kernel (split != 0): units of two adjacent
-  // blocks, nunits per (b, g), mirrored into npairs pairs; the key range of a
-  // pair's heavy unit is shared by two workgroups whose partial results meet
-  // in the workspace (part: [slot][128][d] fp32 rows, part_lse: [slot][128],
-  // sync: [slot][2] arrival count and ready flag, zero at launch).
-  float* part;
-  float* part_lse;
-  unsigned* sync;
-  int split, nunits, npairs, split_ovh;
   // log2-domain log-sum-exp of each output row (b, token, head), for the
   // backward pass (simple kernel; mirrored kernel without a gate); null otherwise
   float* lse;
@@ -157,6 +148,7 @@ struct BwdParams {
   float* dkp;
   float* dvp;
   int B, n, npad, H, G, grp, gate_mode;
+  int plain;            // 1: the register-operand dq and dK/dV kernels for every shape
   float scale, scale_log2;
 };
 
@@ -192,8 +184,6 @@ hipError_t launch_bwd_reduce_rows(const float* part, float* out, int nrows, int 
 hipError_t launch_prep_keys(const PrepParams& p, int is_bf16, hipStream_t s);
 hipError_t launch_prefill_mfma(const PrefillParams& p, int D, int gate_mode, hipStream_t s);
 hipError_t launch_prefill_v2(const PrefillParams& p, int D, int gate_mode, hipStream_t s);
-// Bytes of workspace the split-key mode needs: slots * (128 * (d + 1) floats + 2 words), 256-aligned parts.
-size_t prefill_split_bytes(long slots, int D);
 hipError_t launch_prefill_wide(const PrefillParams& p, int D, int gate_mode, hipStream_t s);
 hipError_t launch_naive(const NaiveParams& p, int is_bf16, hipStream_t s);
 hipError_t launch_decode_partials(const DecodeParams& p, int D, hipStream_t s);

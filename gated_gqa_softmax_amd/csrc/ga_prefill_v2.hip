@@ -40,7 +40,6 @@ namespace ga {
 
 template <int D>
 constexpr int kMirrorStages = (D == 256) ? 2 : 3;
-constexpr int kSc1 = 16;  // buffer load/store cache bits: coherent at device (agent) scope
 template <int D>
 using MirrorShape = TileShape<D, kMirrorStages<D>>;
 
@@ -113,15 +112,14 @@ __device__ __forceinline__ int v2_unit_stages(int u, int TB, int n) { return (mi
 // CHUNK: a chunk against a cache (per-sequence key offsets and real-row counts
 // from p.key_base / p.row_lens); a separate instantiation, so the
 // whole-sequence kernel carries none of it.
-template <int D, int GATE, bool SPLIT, bool CHUNK = false, bool LSE = false>
+template <int D, int GATE, bool CHUNK = false, bool LSE = false>
 __global__ __launch_bounds__(512) void prefill_v2_kernel(const PrefillParams p) {
   typedef MirrorShape<D> S;
   static_assert(4 * 32 * D * 4 <= S::BUF_BYTES, "the phase merge reuses the stage buffers");
   __shared__ __attribute__((aligned(1024))) unsigned char smem[S::BUF_BYTES];
   __shared__ float2 table[2048];
   __shared__ float ml_x[4][64][2];
-  __shared__ float lse_x[4][32];  // split mode: log2-domain log-sum-exp of each row
-  __shared__ unsigned s_arrival, s_ready;
+  __shared__ float lse_x[4][32];  // LSE: log2-domain log-sum-exp of each row
 
   const int w = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);  // wave index (uniform)
   // wave -> (row group, phase): each SIMD (w % 4) gets one light and one heavy wave
@@ -154,60 +152,16 @@ __global__ __launch_bounds__(512) void prefill_v2_kernel(const PrefillParams p) 
   const long v_bstride = p.v_bstride;
 
   // ---- work of this workgroup -------------------------------------------------
-  // Two blocks (A in row groups 0-1, B in row groups 2-3) and a range of key
-  // stages; seg_slot >= 0 marks a partial result that meets the rest of the
-  // same key range in the workspace.
-  //  * mirrored mode: blocks (pair, nblk-1-pair), all their stages.
-  //  * split mode: units of two adjacent blocks; unit pair i = (light unit i,
-  //    heavy unit U-1-i). Workgroups, in launch order: the heavy units' heads
-  //    (stages [0, c_i)), their tails ([c_i, s_h)) and the light units, last
-  //    to first. Pieces shrink along that order, so the compute units that
-  //    finish a short tail first take the longest light units: each pair's
-  //    work, s_h + s_l stages, is shared by two compute units.
-  //  * chunk split mode (SPLIT and CHUNK): mirrored pairs whose key range is
-  //    cut in two halves of its stages, head and tail in two workgroups;
-  //    launch order: pair-major, the heads then the tails of every (b, g).
-  int blk_light, blk_heavy, st_lo = 0, st_hi = 0x7fffffff, seg_slot = -1;
-  if (!SPLIT) {
-    blk_heavy = nblk - 1 - pair;
-    blk_light = (pair < blk_heavy) ? pair : -1;   // -1: no light block (odd middle)
-  } else if (CHUNK) {
-    const int cpair = pair >> 1, part = pair & 1;
-    blk_heavy = nblk - 1 - cpair;
-    blk_light = (cpair < blk_heavy) ? cpair : -1;
-    const int s_all = (L0 + min(nb, blk_heavy * TB + TB) + S::ST - 1) / S::ST;
-    const bool split = s_all >= 2;
-    const int c = split ? (s_all + 1) / 2 : s_all;
-    if (part == 1 && !split) return;  // (no tail; the head stores its rows itself)
-    st_lo = part ? c : 0;
-    st_hi = part ? s_all : c;
-    seg_slot = split ? bg * p.npairs + cpair : -1;
-  } else {
-    const int U = p.nunits, P = p.npairs, L = U / 2;  // light units: i < U-1-i
-    int unit;
-    if (pair < 2 * P) {
-      const int i = (pair < P) ? pair : pair - P;
-      unit = U - 1 - i;
-      const int s_h = v2_unit_stages(unit, TB, n);
-      const int s_l = (i < unit) ? v2_unit_stages(i, TB, n) : 0;
-      const bool split = s_h >= 2;
-      const int c = split ? min(max((s_h + s_l + (s_l > 0 ? p.split_ovh : 0) + 1) / 2, 1), s_h - 1) : s_h;
-      if (pair >= P && !split) return;  // (no tail)
-      st_lo = (pair < P) ? 0 : c;
-      st_hi = (pair < P) ? c : s_h;
-      seg_slot = split ? bg * P + i : -1;
-    } else {
-      unit = L - 1 - (pair - 2 * P);
-    }
-    blk_light = 2 * unit;
-    blk_heavy = (2 * unit + 1 < nblk) ? 2 * unit + 1 : -1;
-  }
+  // Two blocks: the light block `pair` in row groups 0-1 and its mirror
+  // nblk-1-pair in row groups 2-3, with all the stages they see.
+  const int blk_heavy = nblk - 1 - pair;
+  const int blk_light = (pair < blk_heavy) ? pair : -1;  // -1: no light block (odd middle)
   if (CHUNK) {
     if (L0 < 0 || L0 > p.max_base || nb <= 0) return;  // sequence skipped (whole workgroup)
     if ((blk_light < 0 || blk_light * TB >= nb) && (blk_heavy < 0 || blk_heavy * TB >= nb)) return;  // no real row
   }
   const int kend = L0 + min(nb, max(blk_light, blk_heavy) * TB + TB);  // keys [0, kend) are seen
-  const int nst = min(st_hi, (kend + S::ST - 1) / S::ST);  // stages run over [st_lo, nst)
+  const int nst = (kend + S::ST - 1) / S::ST;  // stages run over [0, nst)
 
   // this lane's query row
   const int my_blk = (rg < 2) ? blk_light : blk_heavy;
@@ -365,9 +319,9 @@ __global__ __launch_bounds__(512) void prefill_v2_kernel(const PrefillParams p) 
     }
   }
 
-  if (st_lo < nst) stage_issue<D, kMirrorStages<D>, 0>(smem, krs, vrs, koff, voff, w, st_lo, kv_row_bytes);
-  if (S::NSTAGE == 3 && st_lo + 1 < nst)
-    stage_issue<D, kMirrorStages<D>, 1>(smem, krs, vrs, koff, voff, w, st_lo + 1, kv_row_bytes);
+  if (0 < nst) stage_issue<D, kMirrorStages<D>, 0>(smem, krs, vrs, koff, voff, w, 0, kv_row_bytes);
+  if (S::NSTAGE == 3 && 1 < nst)
+    stage_issue<D, kMirrorStages<D>, 1>(smem, krs, vrs, koff, voff, w, 1, kv_row_bytes);
 
   if (!spread) {
     lds_barrier();  // the table is complete
@@ -425,7 +379,7 @@ __global__ __launch_bounds__(512) void prefill_v2_kernel(const PrefillParams p) 
                                       : 0)
                                : ((blk_light >= 0) ? (min(n, blk_light * TB + TB) + S::ST - 1) / S::ST : 0);
   // ---- main loop, unrolled over the stage buffers -----------------------------
-  for (int st0 = st_lo; st0 < nst; st0 += S::NSTAGE) {
+  for (int st0 = 0; st0 < nst; st0 += S::NSTAGE) {
     v2_step<D, 0>(smem, ws, krs, vrs, koff, voff, w, st0, nst, kv_row_bytes, phase, wave_min_key, wave_max_key,
                   my_lim_key, nkeys, sl2, hi, light_end, rg < 2);
     if (st0 + 1 < nst)
@@ -456,21 +410,20 @@ __global__ __launch_bounds__(512) void prefill_v2_kernel(const PrefillParams p) 
     const bool valid = (blk >= 0) && (hh < grp) && (tok < nb);
     return valid ? (b * n + tok) * nH + g * grp + hh : -1;
   };
-  // Mirrored mode: row indices and gate values are fetched before the merge
-  // so that their latency overlaps it. Split mode forms both after the merge,
-  // when the accumulators are free: the registers are needed there.
+  // Row indices and gate values are fetched before the merge so that their
+  // latency overlaps it.
   int erow[NIT];
   u32x4_t graw[NIT];
   uint16_t ghead[NIT];
 #pragma unroll
   for (int it = 0; it < NIT; ++it) {
-    erow[it] = SPLIT ? -1 : row_index(it);
+    erow[it] = row_index(it);
     const bool valid = erow[it] >= 0;
     graw[it] = u32x4_t{0, 0, 0, 0};
     ghead[it] = 0;
-    if (!SPLIT && valid && GATE == 2) graw[it] = *(const u32x4_t*)(p.gate + (long)erow[it] * p.gs + qc * 8);
-    if (!SPLIT && valid && GATE == 1) ghead[it] = p.gate[(long)erow[it] * p.gs];
-    if (!SPLIT && valid && GATE == kGateExt && p.ge.mode != 0) {
+    if (valid && GATE == 2) graw[it] = *(const u32x4_t*)(p.gate + (long)erow[it] * p.gs + qc * 8);
+    if (valid && GATE == 1) ghead[it] = p.gate[(long)erow[it] * p.gs];
+    if (valid && GATE == kGateExt && p.ge.mode != 0) {
       const long go = ext_gate_offset(p.ge, erow[it], nH);
       if (p.ge.mode == 2) graw[it] = *(const u32x4_t*)(p.gate + go + qc * 8);
       else ghead[it] = p.gate[go];
@@ -513,9 +466,7 @@ __global__ __launch_bounds__(512) void prefill_v2_kernel(const PrefillParams p) 
       auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_run), __float_as_uint(l_run), false, false);
       l_run = __uint_as_float(r[0]) + __uint_as_float(r[1]);
     }
-    // a row of a partial key range may see no key at all (l = 0): output 0, weight 0
-    const float inv_l = (l_run > 0.f) ? 1.0f / l_run : 0.f;
-    if (SPLIT && hi == 0) lse_x[rg][l32] = (l_run > 0.f) ? mt + log2f(l_run) : -INFINITY;
+    const float inv_l = 1.0f / l_run;
     if (LSE && hi == 0) lse_x[rg][l32] = mt + log2f(l_run);  // stored with the rows below
     // lane (l32, hi) holds row l32, elements mb*32 + ig*8 + hi*4 + [0, 4)
 #pragma unroll
@@ -531,105 +482,15 @@ __global__ __launch_bounds__(512) void prefill_v2_kernel(const PrefillParams p) 
   }
   lds_barrier();
 
-  // ---- partial key range: the first of the two workgroups to get here
-  // leaves its normalised rows and their log-sum-exp in the workspace; the
-  // second combines them with its own (weights 2^(lse - max)) and stores.
-  bool merge = false;
-  if (SPLIT && seg_slot >= 0) {
-    unsigned* cnt = p.sync + 2 * seg_slot;
-    // this slot's 128 rows; the 16-byte chunk h (0, 1) of lane qc of row r sits
-    // at chunk h * LPR + qc of the row, so each store or load instruction
-    // covers whole contiguous rows
-    const __amdgpu_buffer_rsrc_t prs =
-        __builtin_amdgcn_make_buffer_rsrc(p.part + (size_t)seg_slot * 128 * D, 0, 128 * D * 4, 0x00020000);
-    float* plse = p.part_lse + (size_t)seg_slot * 128;
-    if (tid == 0) s_arrival = atomicAdd(cnt, 1u);
-    lds_barrier();
-    merge = s_arrival != 0;
-    // The partial rows move with device-coherent (sc1) buffer loads and
-    // stores, which skip the compute units' non-coherent caches, so neither
-    // side needs a cache-wide invalidate (which would also drop the K/V
-    // stages other workgroups on the same XCD are streaming).
-    if (!merge) {
-#pragma unroll
-      for (int it = 0; it < NIT; ++it) {
-        if (row_index(it) < 0) continue;
-        const int lr = phase * 16 + it * RPI + rsub;
-        const int rbase = (rg * 32 + lr) * D * 4;
-        const f32x4_t a = *(const f32x4_t*)(xr + lr * D + (((2 * qc) ^ (lr & 15)) << 2));
-        const f32x4_t c = *(const f32x4_t*)(xr + lr * D + (((2 * qc + 1) ^ (lr & 15)) << 2));
-        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, a), prs, rbase + qc * 16, 0, kSc1);
-        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, c), prs, rbase + (LPR + qc) * 16, 0, kSc1);
-        if (qc == 0) __hip_atomic_store(plse + rg * 32 + lr, lse_x[rg][lr], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
-      // every thread's rows are ordered before the flag (release at agent scope,
-      // no invalidate), then one thread raises it
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-      __syncthreads();
-      if (tid == 0) __hip_atomic_store(cnt + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      return;
-    }
-    // The other workgroup has already arrived and is only storing its rows,
-    // so this wait ends; the bound is a guard (rows read as NaN if it hit).
-    if (tid == 0) {
-      unsigned spins = 0;
-      while (__hip_atomic_load(cnt + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0u && ++spins < (1u << 20))
-        __builtin_amdgcn_s_sleep(8);
-      s_ready = (spins < (1u << 20)) ? 1u : 0u;
-      // leave the words zero for the next launch
-      __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(cnt + 1, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-    __syncthreads();
-  }
-  const bool ready = !SPLIT || !merge || s_ready != 0;
-  // the other part's rows, all loads in flight before the first use
-  f32x4_t tpart[SPLIT ? NIT : 1][2];
-  if (SPLIT && merge) {
-    const __amdgpu_buffer_rsrc_t prs =
-        __builtin_amdgcn_make_buffer_rsrc(p.part + (size_t)seg_slot * 128 * D, 0, 128 * D * 4, 0x00020000);
-#pragma unroll
-    for (int it = 0; it < NIT; ++it) {
-      const int lr = phase * 16 + it * RPI + rsub;
-      const int rbase = (rg * 32 + lr) * D * 4;
-      tpart[it][0] = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(prs, rbase + qc * 16, 0, kSc1));
-      tpart[it][1] =
-          __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(prs, rbase + (LPR + qc) * 16, 0, kSc1));
-    }
-  }
 #pragma unroll
   for (int it = 0; it < NIT; ++it) {
-    const int er = SPLIT ? row_index(it) : erow[it];
+    const int er = erow[it];
     if (er < 0) continue;
     const int lr = phase * 16 + it * RPI + rsub;
     const f32x4_t y0 = *(const f32x4_t*)(xr + lr * D + (((2 * qc) ^ (lr & 15)) << 2));
     const f32x4_t y1 = *(const f32x4_t*)(xr + lr * D + (((2 * qc + 1) ^ (lr & 15)) << 2));
     float y[8] = {y0[0], y0[1], y0[2], y0[3], y1[0], y1[1], y1[2], y1[3]};
     if (LSE && qc == 0) p.lse[er] = lse_x[rg][lr];  // the row statistics for the backward pass
-    if (SPLIT && GATE == 2) graw[it] = *(const u32x4_t*)(p.gate + (long)er * p.gs + qc * 8);
-    if (SPLIT && GATE == 1) ghead[it] = p.gate[(long)er * p.gs];
-    if (SPLIT && merge) {
-      const f32x4_t t0 = tpart[SPLIT ? it : 0][0];
-      const f32x4_t t1 = tpart[SPLIT ? it : 0][1];
-      // head part (stages from 0) first, whichever workgroup arrived last, so
-      // the result does not depend on the arrival order
-      const bool own_head = st_lo == 0;
-      const float lo = lse_x[rg][lr];
-      const float lt = ready ? __hip_atomic_load(p.part_lse + (size_t)seg_slot * 128 + rg * 32 + lr, __ATOMIC_RELAXED,
-                                                 __HIP_MEMORY_SCOPE_AGENT)
-                             : __builtin_nanf("");
-      const float lh = own_head ? lo : lt, ltl = own_head ? lt : lo;
-      const float mx = fmaxf(lh, ltl);  // finite: the head range holds key 0 of every row
-      const float wh = __builtin_amdgcn_exp2f(lh - mx);
-      const float wt = __builtin_amdgcn_exp2f(ltl - mx);
-      const float inv = 1.0f / (wh + wt);
-      const float tv[8] = {t0[0], t0[1], t0[2], t0[3], t1[0], t1[1], t1[2], t1[3]};
-#pragma unroll
-      for (int jj = 0; jj < 8; ++jj) {
-        const float yh = own_head ? y[jj] : tv[jj], yt = own_head ? tv[jj] : y[jj];
-        y[jj] = __builtin_fmaf(yh, wh, yt * wt) * inv;
-      }
-    }
     if (GATE == kGateExt) {
       ext_epilogue8<D>(y, p.ge, qc, graw[it], ghead[it]);
     } else if (GATE == 2) {
@@ -646,57 +507,28 @@ __global__ __launch_bounds__(512) void prefill_v2_kernel(const PrefillParams p) 
   }
 }
 
-__global__ void zero_words_kernel(unsigned* w, long nwords) {
-  const long i = (long)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < nwords) w[i] = 0u;
-}
-
-template <int D, bool SPLIT, bool CHUNK = false>
+template <int D, bool CHUNK = false>
 static void launch_v2_gate(const PrefillParams& p, int gate_mode, long grid, hipStream_t s) {
   switch (gate_mode) {
-    case 0: hipLaunchKernelGGL((prefill_v2_kernel<D, 0, SPLIT, CHUNK>), dim3((unsigned)grid), dim3(512), 0, s, p); break;
-    case 1: hipLaunchKernelGGL((prefill_v2_kernel<D, 1, SPLIT, CHUNK>), dim3((unsigned)grid), dim3(512), 0, s, p); break;
-    case 2: hipLaunchKernelGGL((prefill_v2_kernel<D, 2, SPLIT, CHUNK>), dim3((unsigned)grid), dim3(512), 0, s, p); break;
-    default:
-      // extended epilogue: mirrored mode only (the host never pairs it with split keys)
-      if constexpr (!SPLIT)
-        hipLaunchKernelGGL((prefill_v2_kernel<D, kGateExt, SPLIT, CHUNK>), dim3((unsigned)grid), dim3(512), 0, s, p);
-      break;
+    case 0: hipLaunchKernelGGL((prefill_v2_kernel<D, 0, CHUNK>), dim3((unsigned)grid), dim3(512), 0, s, p); break;
+    case 1: hipLaunchKernelGGL((prefill_v2_kernel<D, 1, CHUNK>), dim3((unsigned)grid), dim3(512), 0, s, p); break;
+    case 2: hipLaunchKernelGGL((prefill_v2_kernel<D, 2, CHUNK>), dim3((unsigned)grid), dim3(512), 0, s, p); break;
+    default: hipLaunchKernelGGL((prefill_v2_kernel<D, kGateExt, CHUNK>), dim3((unsigned)grid), dim3(512), 0, s, p); break;
   }
 }
 
 template <int D>
 static hipError_t launch_v2_d(const PrefillParams& p, int gate_mode, hipStream_t s) {
-  if (p.split) {
-    // whole sequences: heads and tails of the heavy units, then the light
-    // units; chunks: head and tail of every mirrored pair. The arrival words
-    // start at zero.
-    const long slots = (long)p.B * p.G * p.npairs;
-    const long grid = p.key_base ? 2 * slots : (long)p.B * p.G * (2L * p.npairs + p.nunits / 2);
-    if (grid <= 0) return hipSuccess;
-    const long nwords = 2 * slots;
-    hipLaunchKernelGGL(zero_words_kernel, dim3((unsigned)((nwords + 255) / 256)), dim3(256), 0, s, p.sync, nwords);
-    if (p.key_base)
-      launch_v2_gate<D, true, true>(p, gate_mode, grid, s);
-    else
-      launch_v2_gate<D, true>(p, gate_mode, grid, s);
-  } else {
-    const int npairs = (p.nblk + 1) / 2;
-    const long grid = (long)p.B * p.G * npairs;
-    if (grid <= 0) return hipSuccess;
-    if (p.key_base)
-      launch_v2_gate<D, false, true>(p, gate_mode, grid, s);
-    else if (p.lse)  // ungated output with the row statistics, for the backward pass
-      hipLaunchKernelGGL((prefill_v2_kernel<D, 0, false, false, true>), dim3((unsigned)grid), dim3(512), 0, s, p);
-    else
-      launch_v2_gate<D, false>(p, gate_mode, grid, s);
-  }
+  const int npairs = (p.nblk + 1) / 2;
+  const long grid = (long)p.B * p.G * npairs;
+  if (grid <= 0) return hipSuccess;
+  if (p.key_base)
+    launch_v2_gate<D, true>(p, gate_mode, grid, s);
+  else if (p.lse)  // ungated output with the row statistics, for the backward pass
+    hipLaunchKernelGGL((prefill_v2_kernel<D, 0, false, true>), dim3((unsigned)grid), dim3(512), 0, s, p);
+  else
+    launch_v2_gate<D>(p, gate_mode, grid, s);
   return hipGetLastError();
-}
-
-size_t prefill_split_bytes(long slots, int D) {
-  auto r256 = [](size_t x) { return (x + 255) / 256 * 256; };
-  return r256((size_t)slots * 128 * D * 4) + r256((size_t)slots * 128 * 4) + r256((size_t)slots * 2 * 4);
 }
 
 hipError_t launch_prefill_v2(const PrefillParams& p, int D, int gate_mode, hipStream_t s) {

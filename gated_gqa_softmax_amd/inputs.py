@@ -172,3 +172,14 @@ def for_each_cache_rows(w: Workload, cache_lens, fn, threads: int = 8) -> None:
     with ThreadPoolExecutor(max_workers=max(1, threads)) as ex:
         for b, (kh, vv) in ex.map(job, range(w.batch)):
             fn(b, kh, vv)
+
+
+def sample_row_blocks(w: Workload, count: int = 16, rows: int = 256, seed: int = 7) -> list:
+    """Seeded sample of query-row blocks for workloads too large to check or
+    time on the CPU whole: ``count`` distinct block starts (multiples of
+    ``rows``), sorted, the last block always included."""
+    nblk = -(-w.seq_len // rows)
+    if count >= nblk:
+        return [i * rows for i in range(nblk)]
+    pick = np.random.default_rng(seed).choice(nblk - 1, count - 1, replace=False)
+    return sorted(int(p) * rows for p in pick) + [(nblk - 1) * rows]

@@ -39,7 +39,8 @@
  *    wider (``q_head_stride``, ``gate_head_stride`` in the descriptor), so
  *    that the output of a fused q projection is read in place (see there).
  *    Element type of q, k, v, gate, out and caches is ``desc->dtype``.
- *    bf16 tensors must be 16-byte aligned (a headwise gate: 2-byte).
+ *    bf16 tensors must be 16-byte aligned (a headwise gate: 2-byte), norm
+ *    weights 16-byte aligned.
  *  - Errors: shapes, pointers, alignment, capacities and workspace size are
  *    checked on the host before anything is launched; a failed check returns
  *    its status and launches nothing. ``ga_last_error()`` gives a message for
@@ -86,6 +87,23 @@ typedef enum { GA_COMBINE_MUL = 0, GA_COMBINE_ADD = 1 } ga_gate_combine;
  * gate for every token (the input-independent gate, "第一条机制线索"). */
 typedef enum { GA_SHARE_HEADS = 1, GA_SHARE_TOKENS = 2 } ga_gate_share;
 
+/* Kernel choice of the prefill attention (ga_prefill, ga_prefill_attention)
+ * and of the chunk attention (ga_prefill_chunk*): automatic, or forced, for
+ * tests and tuning. A forced kernel that does not serve the shape makes the
+ * call fail with GA_ERR_UNSUPPORTED (the chunk path serves only MIRROR and
+ * GENERIC). Results of every kernel agree within the parity tolerance. */
+typedef enum {
+  GA_KERNEL_AUTO = 0,
+  GA_KERNEL_WIDE = 1,     /* 256 query rows per workgroup, heaviest blocks first (d = 128) */
+  GA_KERNEL_MIRROR = 2,   /* 128 rows from a block and its mirror, two key phases (d = 128, 256) */
+  GA_KERNEL_SIMPLE = 3,   /* 128 rows of one block (d = 64, 128, 256) */
+  GA_KERNEL_GENERIC = 4   /* one wave per query row (any d <= 256, fp32 or bf16) */
+} ga_kernel;
+/* Kernels of the backward's dq and dK/dV products: automatic (LDS-staged
+ * operands where they serve the shape) or the register-operand kernels for
+ * every shape. */
+typedef enum { GA_BWD_AUTO = 0, GA_BWD_PLAIN = 1 } ga_bwd_kernel;
+
 typedef struct {
   int32_t batch;        /* B >= 0 */
   int32_t n_q_heads;    /* H >= 1, a multiple of n_kv_heads */
@@ -129,26 +147,21 @@ typedef struct {
    * no norm; it must stay valid until the calls that use it have run. */
   float out_norm_eps;    /* >= 0 */
   const float* out_norm_w;
+  int32_t kernel;        /* ga_kernel (0 = automatic) */
+  int32_t bwd_kernel;    /* ga_bwd_kernel (0 = automatic) */
 } ga_attn_desc;
 
 /* ---- prefill ------------------------------------------------------------ */
 
-/* Workspace ga_prefill_attention needs (0 when the kernel chosen for the
- * shape needs none). The split-key mode of the mirrored kernel keeps, per
- * pair of token-block units of a (batch, KV head), one partial result of
- * 128 rows: 128*(d+1) floats plus two 32-bit words, 256-byte aligned parts.
- * The value depends on GA_PREFILL_KERNEL as read at the time of the call. */
-size_t ga_prefill_attention_workspace_bytes(const ga_attn_desc* desc, int32_t seq_len);
-
 /* Name of the kernel ga_prefill_attention runs for this shape (caches of
- * seq_len rows), under GA_PREFILL_KERNEL as read now: "wide", "mirror",
- * "split", "simple" or "generic" ("invalid" for a bad descriptor). A static
- * string; the caller does not free it. */
+ * seq_len rows): "wide", "mirror", "simple" or "generic"; "unsupported" when
+ * the descriptor forces a kernel that does not serve the shape, "invalid"
+ * for a bad descriptor. A static string; the caller does not free it. */
 const char* ga_prefill_attention_kernel(const ga_attn_desc* desc, int32_t seq_len);
 
 /* Workspace ga_prefill needs when it is given no KV cache: room for K-hat
- * (B*n*G*d elements, rounded up to 256 bytes) followed by the attention
- * workspace. With a KV cache it needs only the attention workspace. */
+ * (B*n*G*d elements, rounded up to 256 bytes). With a KV cache it needs
+ * none. Depends on its arguments only. */
 size_t ga_prefill_workspace_bytes(const ga_attn_desc* desc, int32_t seq_len);
 
 /* Whole prefill: ga_prefill_keys, then ga_prefill_attention.
@@ -160,9 +173,9 @@ size_t ga_prefill_workspace_bytes(const ga_attn_desc* desc, int32_t seq_len);
  *                (normed, rotated, rounded to dtype) is written to slots
  *                [0,n) of k_cache and v to the same slots of v_cache (both
  *                required, cache_cap >= n); the attention then reads K-hat
- *                from the cache and the workspace holds only what
- *                ga_prefill_attention_workspace_bytes names (NULL if 0).
- *                Without a cache, K-hat goes to the start of ``workspace``.
+ *                from the cache and ``workspace`` may be NULL. Without a
+ *                cache, K-hat goes to ``workspace`` (16-byte aligned,
+ *                ga_prefill_workspace_bytes bytes).
  *  out           [B,n,H*d]. */
 ga_status ga_prefill(const ga_attn_desc* desc, int32_t seq_len,
                      const void* q, const void* k, const void* v, const void* gate,
@@ -180,29 +193,18 @@ ga_status ga_prefill_keys(const ga_attn_desc* desc, int32_t seq_len,
                           void* stream);
 
 /* Second stage of ga_prefill: causal attention of the normed, rotated q
- * against prepared keys, with the gate fused into the epilogue. Kernel
- * choice (bf16): a wide kernel (256 query rows per workgroup; d = 128,
- * rot % 32 == 0, at least 512 token blocks), else the mirrored-block kernel
- * (d in {128, 256}, rot <= d/4, B*n*H < 2^31), else a simple kernel (d in
- * {64, 128, 256}), else the generic kernel. The environment variable
- * GA_PREFILL_KERNEL = wide | split | mirror | simple | generic, read at each
- * call, forces a kernel that serves the shape, for testing and tuning;
- * results agree within the parity tolerance. "split" is the mirrored kernel
- * in its split-key mode: the key range of each heavy pair of blocks is shared
- * by two workgroups whose partial results meet in the workspace (a small
- * zeroing kernel runs first); GA_PREFILL_SPLIT_BIAS (stages, default 8) tunes
- * its balance. Only that mode needs a workspace.
+ * against prepared keys, with the gate fused into the epilogue. Automatic
+ * kernel choice (bf16): the wide kernel (256 query rows per workgroup; d =
+ * 128, rot % 32 == 0, at least 512 token blocks), else the mirrored-block
+ * kernel (d in {128, 256}, rot <= d/4, B*n*H < 2^31), else the simple kernel
+ * (d in {64, 128, 256}), else the generic kernel; desc->kernel may force one.
+ * Needs no workspace.
  *  k_hat  [B,k_cap,G,d] as written by ga_prefill_keys (k_cap >= seq_len).
- *  v      [B,v_cap,G,d] (v_cap >= seq_len; the raw v input has v_cap = n).
- *  workspace  ga_prefill_attention_workspace_bytes(desc, seq_len) bytes,
- *             16-byte aligned, owned by the caller (NULL allowed when that
- *             is 0); too small: GA_ERR_WORKSPACE. Two calls that share a
- *             workspace must not run at the same time. */
+ *  v      [B,v_cap,G,d] (v_cap >= seq_len; the raw v input has v_cap = n). */
 ga_status ga_prefill_attention(const ga_attn_desc* desc, int32_t seq_len,
                                const void* q, const void* k_hat, int32_t k_cap,
                                const void* v, int32_t v_cap, const void* gate,
                                const float* q_norm_w, const int32_t* positions,
-                               void* workspace, size_t workspace_bytes,
                                void* out, void* stream);
 
 /* ---- chunked prefill against a KV cache ---------------------------------- */
@@ -242,14 +244,9 @@ ga_status ga_prefill_chunk(const ga_attn_desc* desc, int32_t seq_len,
                            const int32_t* cache_lens, const int32_t* chunk_lens, int32_t max_cache_len,
                            void* workspace, size_t workspace_bytes, void* out, void* stream);
 
-/* Workspace of ga_prefill_chunk / ga_prefill_chunk_attention. Sequences with
- * cached prefixes of different lengths give the mirrored kernel's workgroups
- * different amounts of work. With GA_PREFILL_CHUNK_SPLIT=1 (read at each
- * call; opt-in, as it measured slower), the mirrored kernel, the method's
- * gate and max_cache_len >= 64, every mirrored pair's key range is cut in two
- * workgroups whose partial rows meet here: 128 * (d + 1) floats + 2 words per
- * pair of token blocks per (batch, KV head), 256-byte aligned parts. 0
- * otherwise. */
+/* Workspace of ga_prefill_chunk / ga_prefill_chunk_attention, in bytes
+ * (256-byte aligned; NULL is accepted when this is 0). Depends on its
+ * arguments only. */
 size_t ga_prefill_chunk_workspace_bytes(const ga_attn_desc* desc, int32_t seq_len, int32_t cache_cap,
                                         int32_t max_cache_len);
 
@@ -273,7 +270,8 @@ ga_status ga_prefill_chunk_attention(const ga_attn_desc* desc, int32_t seq_len, 
 
 /* Name of the kernel ga_prefill_chunk_attention runs for this shape:
  * "mirror" (the mirrored prefill kernel with per-sequence key offsets) or
- * "generic"; "invalid" for a bad descriptor. */
+ * "generic"; "unsupported" for a forced kernel that does not serve the
+ * shape; "invalid" for a bad descriptor. */
 const char* ga_prefill_chunk_kernel(const ga_attn_desc* desc, int32_t seq_len, int32_t cache_cap);
 
 /* ---- decode ------------------------------------------------------------- */
@@ -369,8 +367,8 @@ const char* ga_last_error(void);
  * fp32 or bf16); ga_decode_partials/ga_decode_merge need bit 1. The bits
  * are for dense q and gate (see ga_attn_desc for wider head strides). */
 int32_t ga_fast_path(int32_t dtype, int32_t head_dim, int32_t rot_dim, int32_t group);
-/* ABI version: 3 (ga_attn_desc with head strides, gate variants and the
- * output norm). */
+/* ABI version: 4 (ga_attn_desc with head strides, gate variants, the output
+ * norm and the kernel-choice fields). */
 int32_t ga_version(void);
 
 #ifdef __cplusplus

@@ -370,6 +370,46 @@ def prefill_rows(q, k, v, gate, rows: Sequence[tuple], *, gate_mode: str, q_norm
     return out
 
 
+def prefill_blocks(q, k, v, gate, blocks: Sequence[tuple], *, gate_mode: str, q_norm_w, k_norm_w,
+                   positions, block_rows: int = 256, rms_eps: float = 1e-6, rope_base: float = 10000.0,
+                   rot_dim: int = 0, scale: Optional[float] = None, dtype=np.float64) -> np.ndarray:
+    """The definition for whole query-row blocks: for each (b, r0) in
+    ``blocks``, rows r0 .. r0 + block_rows - 1 (clipped to n) of every head,
+    each against keys [0, i] ("The formula": causal softmax(QK^T/sqrt(d)) V,
+    GQA head h reading KV head floor(h / group)). Returns [len(blocks),
+    block_rows, H*d]; rows past n are NaN. Used at sizes where the whole
+    output is too expensive on the CPU; equals the matching rows of
+    ``prefill``."""
+    q = np.asarray(q)
+    B, n, H, d = q.shape
+    G = np.asarray(k).shape[2]
+    sc = _default_scale(d, scale)
+    pos = np.asarray(positions)
+    out = np.full((len(blocks), block_rows, H * d), np.nan, dtype=dtype)
+    khat = {}
+    for o, (b, r0) in enumerate(blocks):
+        r1 = min(n, r0 + block_rows)
+        if r0 >= r1:
+            continue
+        if b not in khat:
+            khat[b] = rope(rms_norm(np.asarray(k)[b][None], k_norm_w, rms_eps, dtype), pos[b][None], rot_dim,
+                           rope_base, dtype)[0]                                   # [n, G, d]
+        kh = khat[b]
+        qh = rope(rms_norm(q[b, r0:r1][None], q_norm_w, rms_eps, dtype), pos[b, r0:r1][None], rot_dim,
+                  rope_base, dtype)[0]                                          # [rows, H, d]
+        vv = np.asarray(v)[b, :r1]
+        y = np.empty((r1 - r0, H, d), dtype=dtype)
+        rows = np.arange(r0, r1)[:, None]
+        for h in range(H):
+            g = kv_group(h, H, G)
+            s = (qh[:, h] @ kh[:r1, g].T) * dtype(sc)                          # [rows, r1]
+            s = np.where(np.arange(r1)[None, :] > rows, -np.inf, s)             # causal: j <= i
+            y[:, h] = softmax_rows(s, dtype) @ vv[:, g].astype(dtype)
+        z = None if gate is None else np.asarray(gate)[b, r0:r1][None]
+        out[o, : r1 - r0] = apply_gate(y[None], z, gate_mode, dtype=dtype).reshape(r1 - r0, H * d)
+    return out
+
+
 def prefill_chunk(q, k, v, gate, *, gate_mode: str, q_norm_w, k_norm_w, k_cache_rows, cache_lens,
                   chunk_lens=None, positions=None, max_cache_len: Optional[int] = None, rms_eps: float = 1e-6,
                   rope_base: float = 10000.0, rot_dim: int = 0, scale: Optional[float] = None, dtype=np.float64,

@@ -29,9 +29,10 @@ def host(t):
     return t.detach().float().cpu().numpy().astype(np.float64)
 
 
-def desc_for(w: inputs.Workload, batch=None, softmax_scale=0.0):
+def desc_for(w: inputs.Workload, batch=None, softmax_scale=0.0, kernel="auto", bwd_kernel="auto"):
     return api.make_desc(w.batch if batch is None else batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.rot_dim,
-                         w.rope_base, w.rms_eps, softmax_scale, tdt(w), w.gate_mode)
+                         w.rope_base, w.rms_eps, softmax_scale, tdt(w), w.gate_mode, kernel=kernel,
+                         bwd_kernel=bwd_kernel)
 
 
 def tol(w: inputs.Workload):
@@ -50,9 +51,9 @@ def assert_close(got, want, w: inputs.Workload, label=""):
     return mx, mean
 
 
-def gpu_prefill(w: inputs.Workload, x: dict, with_cache=False, cap=None, softmax_scale=0.0):
+def gpu_prefill(w: inputs.Workload, x: dict, with_cache=False, cap=None, softmax_scale=0.0, kernel="auto"):
     et = tdt(w)
-    d = desc_for(w, softmax_scale=softmax_scale)
+    d = desc_for(w, softmax_scale=softmax_scale, kernel=kernel)
     q, k, v = dev(x["q"], et), dev(x["k"], et), dev(x["v"], et)
     gate = dev(x["gate"], et) if x["gate"] is not None else None
     wq = dev(x["q_norm_w"]) if x.get("q_norm_w") is not None else None

@@ -36,8 +36,8 @@ def test_library_exports_every_declared_entry_point():
     assert declared == set(_lib.SIGNATURES), declared ^ set(_lib.SIGNATURES)
     for name in declared:
         assert getattr(lib, name) is not None
-    assert lib.ga_version() == 3
-    assert ctypes.sizeof(AttnDesc) == 72
+    assert lib.ga_version() == 4
+    assert ctypes.sizeof(AttnDesc) == 80
 
 
 def _desc(**kw):
@@ -58,8 +58,7 @@ def test_host_queries():
     assert lib.ga_prefill_attention_kernel(ctypes.byref(_desc(dtype=_lib.GA_F32)), 64) == b"generic"
     assert lib.ga_prefill_attention_kernel(ctypes.byref(_desc(head_dim=64, rot_dim=16)), 64) == b"simple"
     assert lib.ga_prefill_attention_kernel(None, 64) == b"invalid"
-    # the default kernel needs no attention workspace: K-hat only
-    assert lib.ga_prefill_attention_workspace_bytes(ctypes.byref(d), 4096) == 0
+    # the prefill workspace holds K-hat only
     assert lib.ga_prefill_workspace_bytes(ctypes.byref(d), 4096) == 4096 * 2 * 256 * 2
     ck = lib.ga_decode_split_keys()
     assert ck > 0
@@ -108,6 +107,9 @@ def _prefill(lib, d, n=16, q=A16, k=A16, v=A16, gate=A16, out=A16, ws=A16, ws_by
     (dict(out_norm_w=A16 + 4), _lib.GA_ERR_MISALIGNED),
     (dict(out_norm_w=A16, out_norm_eps=-1.0), _lib.GA_ERR_BAD_SHAPE),
     (dict(out_norm_w=A16, out_norm_eps=float("inf")), _lib.GA_ERR_BAD_SHAPE),
+    (dict(kernel=5), _lib.GA_ERR_BAD_DTYPE),
+    (dict(kernel=-1), _lib.GA_ERR_BAD_DTYPE),
+    (dict(bwd_kernel=2), _lib.GA_ERR_BAD_DTYPE),
 ])
 def test_prefill_rejects_bad_descriptors(kw, status):
     lib = _lib_or_build()
@@ -159,49 +161,50 @@ def test_head_strides_choose_the_kernel():
                                   None) == _lib.GA_ERR_UNSUPPORTED
 
 
-def test_gate_variants_never_take_the_split_mode(monkeypatch):
-    """The split-key mode has no extended epilogue: a gate variant or the
-    output norm keeps the mirrored kernel even when split is requested."""
+def test_forced_kernel_field():
+    """desc.kernel forces a kernel that serves the shape; one that does not is
+    an error (named "unsupported" by the query), never a silent fallback."""
     lib = _lib_or_build()
-    monkeypatch.setenv("GA_PREFILL_KERNEL", "split")
-    assert lib.ga_prefill_attention_kernel(ctypes.byref(_desc()), 4096) == b"split"
-    for kw in (dict(gate_act=_lib.GA_ACT_SILU), dict(gate_combine=_lib.GA_COMBINE_ADD),
-               dict(gate_share=_lib.GA_SHARE_HEADS), dict(out_norm_w=A16)):
-        d = _desc(**kw)
-        assert lib.ga_prefill_attention_kernel(ctypes.byref(d), 4096) == b"mirror", kw
-        assert lib.ga_prefill_attention_workspace_bytes(ctypes.byref(d), 4096) == 0
+    d3 = dict(batch=4, n_q_heads=16, n_kv_heads=8, head_dim=128, rot_dim=32)
+    for k, name in ((_lib.GA_KERNEL_WIDE, b"wide"), (_lib.GA_KERNEL_MIRROR, b"mirror"),
+                    (_lib.GA_KERNEL_SIMPLE, b"simple"), (_lib.GA_KERNEL_GENERIC, b"generic")):
+        assert lib.ga_prefill_attention_kernel(ctypes.byref(_desc(kernel=k, **d3)), 100) == name
+    d256 = _desc(kernel=_lib.GA_KERNEL_WIDE)                  # the wide kernel serves d = 128 only
+    assert lib.ga_prefill_attention_kernel(ctypes.byref(d256), 4096) == b"unsupported"
+    assert _prefill(lib, d256) == _lib.GA_ERR_UNSUPPORTED
+    assert lib.ga_prefill_attention(ctypes.byref(d256), 16, A16, A16, 16, A16, 16, A16, None, None, A16,
+                                    None) == _lib.GA_ERR_UNSUPPORTED
+    f32 = _desc(dtype=_lib.GA_F32, kernel=_lib.GA_KERNEL_MIRROR)
+    assert lib.ga_prefill_attention_kernel(ctypes.byref(f32), 64) == b"unsupported"
+    # chunks: mirrored or generic only
+    assert lib.ga_prefill_chunk_kernel(ctypes.byref(_desc(kernel=_lib.GA_KERNEL_GENERIC)), 64, 1100) == b"generic"
+    assert lib.ga_prefill_chunk_kernel(ctypes.byref(_desc(kernel=_lib.GA_KERNEL_WIDE)), 64, 1100) == b"unsupported"
+    assert lib.ga_prefill_chunk_kernel(ctypes.byref(_desc(kernel=_lib.GA_KERNEL_MIRROR, dtype=_lib.GA_F32)), 64,
+                                       1100) == b"unsupported"
 
 
-def test_prefill_attention_workspace(monkeypatch):
-    """The split-key mode needs its workspace; the other kernels none."""
+def test_workspace_queries_depend_on_arguments_only():
+    """No kernel needs a prefill-attention or chunk workspace: the sizes are
+    functions of the arguments (the forced-kernel field changes nothing)."""
+    lib = _lib_or_build()
+    for k in range(5):
+        d = _desc(kernel=k)
+        assert lib.ga_prefill_workspace_bytes(ctypes.byref(d), 4096) == 4096 * 2 * 256 * 2
+        assert lib.ga_prefill_chunk_workspace_bytes(ctypes.byref(d), 64, 1100, 1000) == 0
+
+
+def test_norm_weights_must_be_aligned():
+    """The fused kernels read the RMSNorm weights in 16-byte pieces."""
     lib = _lib_or_build()
     d = _desc()
-    monkeypatch.setenv("GA_PREFILL_KERNEL", "split")
-    # split-key mode of the 4096-token, 8/2-head, d = 256 shape: 16-token blocks,
-    # 128 units of two blocks, 64 unit pairs per KV head -> 128 partial slots
-    slots = 2 * 64
-    split = slots * 128 * 256 * 4 + slots * 128 * 4 + slots * 2 * 4
-    assert lib.ga_prefill_attention_workspace_bytes(ctypes.byref(d), 4096) == split
-    assert lib.ga_prefill_workspace_bytes(ctypes.byref(d), 4096) == 4096 * 2 * 256 * 2 + split
-
-    def call(ws, ws_bytes, n=300):
-        return lib.ga_prefill_attention(ctypes.byref(d), n, A16, A16, n, A16, n, A16, None, None, ws, ws_bytes,
-                                        A16, None)
-
-    need = lib.ga_prefill_attention_workspace_bytes(ctypes.byref(d), 300)
-    assert need > 0
-    assert call(None, 0) == _lib.GA_ERR_WORKSPACE
-    assert call(A16, need - 1) == _lib.GA_ERR_WORKSPACE
-    assert call(MIS, need) == _lib.GA_ERR_MISALIGNED
-    monkeypatch.setenv("GA_PREFILL_KERNEL", "mirror")
-    assert lib.ga_prefill_attention_workspace_bytes(ctypes.byref(d), 300) == 0
-    monkeypatch.setenv("GA_PREFILL_KERNEL", "generic")
-    assert lib.ga_prefill_attention_workspace_bytes(ctypes.byref(d), 300) == 0
-    # f32 never takes the split path
-    monkeypatch.setenv("GA_PREFILL_KERNEL", "split")
-    assert lib.ga_prefill_attention_workspace_bytes(ctypes.byref(_desc(dtype=_lib.GA_F32)), 300) == 0
-    monkeypatch.delenv("GA_PREFILL_KERNEL")
-    assert lib.ga_prefill_attention_workspace_bytes(ctypes.byref(d), 300) == 0
+    assert lib.ga_prefill(ctypes.byref(d), 16, A16, A16, A16, A16, A16 + 4, None, None, None, None, 0, A16,
+                          1 << 30, A16, None) == _lib.GA_ERR_MISALIGNED
+    assert lib.ga_prefill(ctypes.byref(d), 16, A16, A16, A16, A16, None, A16 + 8, None, None, None, 0, A16,
+                          1 << 30, A16, None) == _lib.GA_ERR_MISALIGNED
+    assert lib.ga_prefill_keys(ctypes.byref(d), 16, A16, None, A16 + 4, None, A16, None, 16,
+                               None) == _lib.GA_ERR_MISALIGNED
+    assert lib.ga_decode(ctypes.byref(_desc(batch=4)), A16, A16, A16, A16, A16 + 4, None, A16, A16, 101, A16, 100,
+                         A16, 1 << 30, A16, None) == _lib.GA_ERR_MISALIGNED
 
 
 def test_decode_rejects_bad_arguments():
@@ -222,7 +225,7 @@ def test_decode_rejects_bad_arguments():
                                   100, A16, 1 << 30, None) == _lib.GA_ERR_UNSUPPORTED
 
 
-def test_prefill_chunk_rejects_bad_arguments_and_names_its_kernel(monkeypatch):
+def test_prefill_chunk_rejects_bad_arguments_and_names_its_kernel():
     lib = _lib_or_build()
     d = _desc(batch=2)
 
@@ -240,20 +243,8 @@ def test_prefill_chunk_rejects_bad_arguments_and_names_its_kernel(monkeypatch):
     assert call(n=-1) == _lib.GA_ERR_BAD_SHAPE
     assert call(max_len=(1 << 30) - 10, cap=(1 << 30) + 100) == _lib.GA_ERR_UNSUPPORTED
     assert call(desc=_desc(batch=0), q=None) == _lib.GA_OK
-    # the key-range split of long cached prefixes (opt-in) needs its workspace
     assert lib.ga_prefill_chunk_workspace_bytes(ctypes.byref(d), 64, 1100, 1000) == 0
-    monkeypatch.setenv("GA_PREFILL_CHUNK_SPLIT", "1")
-    need = lib.ga_prefill_chunk_workspace_bytes(ctypes.byref(d), 64, 1100, 1000)
-    assert need > 0 and need % 256 == 0
-    assert call(ws=None) == _lib.GA_ERR_WORKSPACE
-    assert call(ws_bytes=need - 1) == _lib.GA_ERR_WORKSPACE
-    assert call(ws=A16 + 16) == _lib.GA_ERR_MISALIGNED
-    assert lib.ga_prefill_chunk_workspace_bytes(ctypes.byref(d), 64, 1100, 63) == 0      # no stage of cached keys
-    assert lib.ga_prefill_chunk_workspace_bytes(ctypes.byref(_desc(gate_act=_lib.GA_ACT_SILU)), 64, 1100, 1000) == 0
-    monkeypatch.setenv("GA_PREFILL_CHUNK_SPLIT", "0")
-    assert lib.ga_prefill_chunk_workspace_bytes(ctypes.byref(d), 64, 1100, 1000) == 0
-    assert call(ws=None, ws_bytes=0, lens=None) == _lib.GA_ERR_NULL_ARG                 # reaches the next check
-    monkeypatch.delenv("GA_PREFILL_CHUNK_SPLIT")
+    assert call(ws=None, ws_bytes=0, lens=None) == _lib.GA_ERR_NULL_ARG
     assert lib.ga_prefill_chunk_keys(ctypes.byref(d), 64, A16, A16, None, None, None, None, 1000, A16, A16, 1100,
                                      None) == _lib.GA_ERR_NULL_ARG
     assert lib.ga_prefill_chunk_attention(ctypes.byref(d), 64, A16, A16, A16, 1000, A16, None, 1000, A16, None,
@@ -261,8 +252,6 @@ def test_prefill_chunk_rejects_bad_arguments_and_names_its_kernel(monkeypatch):
     assert lib.ga_prefill_chunk_kernel(ctypes.byref(d), 64, 1100) == b"mirror"
     assert lib.ga_prefill_chunk_kernel(ctypes.byref(_desc(dtype=_lib.GA_F32)), 64, 1100) == b"generic"
     assert lib.ga_prefill_chunk_kernel(ctypes.byref(_desc(head_dim=64, rot_dim=16)), 64, 1100) == b"generic"
-    monkeypatch.setenv("GA_PREFILL_KERNEL", "generic")
-    assert lib.ga_prefill_chunk_kernel(ctypes.byref(d), 64, 1100) == b"generic"
 
 
 def test_binding_reads_head_strides_from_views():

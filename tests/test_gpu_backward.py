@@ -3,7 +3,7 @@ the C ABI: d in {64, 128, 256}, GQA groups 1, 2, 3, 4, 8 and 16, the three
 gate modes, with and without the norms, ragged token counts (not multiples of
 the 32-row blocks), the LDS-staged attention kernels (d = 128, 256) and the
 register-operand ones (d = 64, odd groups at d = 256, or forced by
-GA_BWD_DQ_KERNEL / GA_BWD_DKV_KERNEL = plain).
+desc.bwd_kernel = plain).
 
 Tolerance. The backward products read bf16 operands (q-hat, k-hat, dy, P,
 dS) and accumulate in fp32; each gradient is stored in bf16. The gradients
@@ -67,14 +67,16 @@ def _assert_rel(got, want, label):
 
 
 @pytest.mark.parametrize("w", PLAIN_CASES, ids=lambda w: w.name)
-def test_backward_plain_kernels(w, monkeypatch):
-    monkeypatch.setenv("GA_BWD_DQ_KERNEL", "plain")
-    monkeypatch.setenv("GA_BWD_DKV_KERNEL", "plain")
-    test_backward_small(w)
+def test_backward_plain_kernels(w):
+    _backward_case(w, bwd_kernel="plain")
 
 
 @pytest.mark.parametrize("w", CASES, ids=lambda w: w.name)
 def test_backward_small(w):
+    _backward_case(w)
+
+
+def _backward_case(w, bwd_kernel="auto"):
     print(f"[backward] {w.name}", flush=True)
     et = tdt(w)
     x = inputs.make_prefill(w)
@@ -82,9 +84,9 @@ def test_backward_small(w):
     dout = inputs.round_bf16(rng.standard_normal((w.batch, w.seq_len, w.n_q_heads * w.head_dim)).astype(np.float32))
     wq = x["q_norm_w"] if w.extra["norm"] else None
     wk = x["k_norm_w"] if w.extra["norm"] else None
-    got = api.ga_prefill_backward(desc_for(w), dev(x["q"], et), dev(x["k"], et), dev(x["v"], et), dev(dout, et),
-                                  gate=dev(x["gate"], et), q_norm_w=dev(wq), k_norm_w=dev(wk),
-                                  positions=dev(x["positions"]))
+    got = api.ga_prefill_backward(desc_for(w, bwd_kernel=bwd_kernel), dev(x["q"], et), dev(x["k"], et),
+                                  dev(x["v"], et), dev(dout, et), gate=dev(x["gate"], et), q_norm_w=dev(wq),
+                                  k_norm_w=dev(wk), positions=dev(x["positions"]))
     torch.cuda.synchronize()
     want = BW.prefill_backward(x["q"], x["k"], x["v"], x["gate"], dout, gate_mode=w.gate_mode, q_norm_w=wq,
                                k_norm_w=wk, positions=x["positions"], rms_eps=w.rms_eps, rope_base=w.rope_base,

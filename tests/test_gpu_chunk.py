@@ -23,7 +23,7 @@ def _case(name, B, n, H, G, d, rot, gate, lens, chunk_lens=None, max_len=None, d
                                   "max_len": max(lens) if max_len is None else max_len})
 
 
-def _run(w, stages=False):
+def _run(w, stages=False, kernel="auto"):
     et = tdt(w)
     x = inputs.make_prefill(w)
     B, n, G, d = w.batch, w.seq_len, w.n_kv_heads, w.head_dim
@@ -45,7 +45,7 @@ def _run(w, stages=False):
         prefix[b] = (kp.double().numpy(), vp.double().numpy())
     kc0, vc0 = kc.clone(), vc.clone()
     out = torch.full((B, n, w.n_q_heads * d), SENT_OUT, dtype=et, device="cuda")
-    d_ = desc_for(w)
+    d_ = desc_for(w, kernel=kernel)
     q, k, v = dev(x["q"], et), dev(x["k"], et), dev(x["v"], et)
     gate = dev(x["gate"], et) if x["gate"] is not None else None
     wq, wk = dev(x["q_norm_w"]), dev(x["k_norm_w"])
@@ -104,27 +104,11 @@ def test_chunk_small(w):
     _run(w, stages=w.name.endswith("stages"))
 
 
-@pytest.mark.parametrize("split", ["1", "0"])
-def test_chunk_key_range_split_on_and_off(split, monkeypatch):
-    """The mirrored kernel with each pair's key range cut in two workgroups
-    (cached prefixes of very different lengths) and without the cut."""
-    monkeypatch.setenv("GA_PREFILL_CHUNK_SPLIT", split)
-    w = _case(f"mirror_split{split}", 4, 96, 8, 2, 256, 64, "elementwise", [0, 64, 700, 1500], [96, 50, 96, 7],
-              seed=310)
-    cap = 1500 + 96 + 2
-    want_bytes = api.ga_prefill_chunk_workspace_bytes(desc_for(w), w.seq_len, cap, 1500)
-    assert (want_bytes > 0) == (split == "1")
-    print(f"[chunk] {w.name}", flush=True)
-    _run(w, stages=True)
-    _run(w, stages=False)
-
-
-def test_chunk_forced_generic_kernel(monkeypatch):
-    monkeypatch.setenv("GA_PREFILL_KERNEL", "generic")
+def test_chunk_forced_generic_kernel():
     w = CASES[0]
     print(f"[chunk] {w.name} on the generic kernel", flush=True)
-    assert api.ga_prefill_chunk_kernel(desc_for(w), w.seq_len, 400) == "generic"
-    _run(w)
+    assert api.ga_prefill_chunk_kernel(desc_for(w, kernel="generic"), w.seq_len, 400) == "generic"
+    _run(w, kernel="generic")
 
 
 def _whole_vs_chunk(B, T, L, H, G, d, rot, gate, seed, sample_rows=None):

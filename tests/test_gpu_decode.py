@@ -149,3 +149,27 @@ def test_decode_stages_match_fused_call():
     torch.cuda.synchronize()
     assert torch.equal(a, b)
     assert torch.equal(kc, kc2) and torch.equal(vc, vc2)
+
+
+def test_decode_is_deterministic():
+    """Repeated ga_decode calls over the same caches give the same bits (fixed
+    split and merge orders, no atomics); the appended slot is rewritten with
+    the same values each time."""
+    w = _decode_case("det", [3000, 17, 1025, 512], 8, 2, 256, 64, "elementwise", seed=240)
+    et = tdt(w)
+    lens_np = np.array(w.extra["lens"], np.int32)
+    x = inputs.make_decode(w, cache_lens=lens_np)
+    cap = int(lens_np.max()) + 1
+    gen = torch.Generator(device="cuda").manual_seed(241)
+    kc = torch.randn((4, cap, 2, 256), generator=gen, device="cuda").to(et)
+    vc = torch.randn((4, cap, 2, 256), generator=gen, device="cuda").to(et)
+    d = desc_for(w)
+    args = (dev(x["q"], et), dev(x["k_new"], et), dev(x["v_new"], et), kc, vc, dev(lens_np), int(lens_np.max()))
+    kw = dict(gate=dev(x["gate"], et), q_norm_w=dev(x["q_norm_w"]), k_norm_w=dev(x["k_norm_w"]))
+    first = api.ga_decode(d, *args, **kw).clone()
+    k0, v0 = kc.clone(), vc.clone()
+    for _ in range(4):
+        again = api.ga_decode(d, *args, **kw)
+        torch.cuda.synchronize()
+        assert torch.equal(again, first)
+        assert torch.equal(kc, k0) and torch.equal(vc, v0)

@@ -51,11 +51,11 @@ def _norm_w(w, seed):
     return (1.0 + 0.1 * rng.standard_normal(w.head_dim)).astype(np.float32)
 
 
-def _descs(w, f, nw):
+def _descs(w, f, nw, kernel="auto"):
     wt = dev(nw) if f["norm"] else None
     d = api.make_desc(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.rot_dim, w.rope_base, w.rms_eps, 0.0,
                       tdt(w), w.gate_mode, gate_act=f["act"], gate_combine=f["combine"], share_heads=f["heads"],
-                      share_tokens=f["tokens"], out_norm_w=wt, out_norm_eps=1e-6)
+                      share_tokens=f["tokens"], out_norm_w=wt, out_norm_eps=1e-6, kernel=kernel)
     of = oracle.GateForm(act=f["act"], combine=f["combine"], share_heads=f["heads"],
                          input_independent=f["tokens"], out_norm_w=nw if f["norm"] else None, out_norm_eps=1e-6)
     return d, of
@@ -121,15 +121,13 @@ PREFILL_CASES = [(w, f) for w, forms in PREFILL for f in forms]
 
 
 @pytest.mark.parametrize("w,f", PREFILL_CASES, ids=[f"{w.name}-{_label(f)}" for w, f in PREFILL_CASES])
-def test_gate_forms_prefill(w, f, monkeypatch):
+def test_gate_forms_prefill(w, f):
     print(f"[gate forms] {w.name} {_label(f)}", flush=True)
-    if w.extra["kernel"] == "simple":
-        monkeypatch.setenv("GA_PREFILL_KERNEL", "simple")
     x = inputs.make_prefill(w)
     et = tdt(w)
     z = _gate_logits(w, (w.batch, w.seq_len), f, w.seed + 10)
     nw = _norm_w(w, w.seed + 11)
-    d, of = _descs(w, f, nw)
+    d, of = _descs(w, f, nw, kernel="simple" if w.extra["kernel"] == "simple" else "auto")
     assert api.ga_prefill_attention_kernel(d, w.seq_len) == w.extra["kernel"]
     out = api.ga_prefill(d, dev(x["q"], et), dev(x["k"], et), dev(x["v"], et), dev(z, et), dev(x["q_norm_w"]),
                          dev(x["k_norm_w"]), dev(x["positions"]))

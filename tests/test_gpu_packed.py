@@ -1,6 +1,6 @@
 """GPU parity of the fused q-projection layout (per-head [q | gate] rows, q and
 the gate read in place through head strides) through the C ABI: every
-prefill kernel (mirrored, split-key, wide, simple, generic), the chunked
+prefill kernel (mirrored, wide, simple, generic), the chunked
 prefill, decode (fused and generic, whole and in stages) and the full
 4096-token workload. Packed calls must give the same bits as the dense
 layout on the same kernel, and match the fp64 oracle, which reads the packed
@@ -43,7 +43,7 @@ def _width(w, pad):
     return (2 * d if w.gate_mode == "elementwise" else d + 1) + pad
 
 
-def _prefill_pair(w, x, qg_np):
+def _prefill_pair(w, x, qg_np, kernel="auto"):
     """(packed output, dense output) of ga_prefill on the same inputs."""
     et = tdt(w)
     d = w.head_dim
@@ -53,8 +53,8 @@ def _prefill_pair(w, x, qg_np):
     qg = dev(qg_np, et)
     qv, gv = _views(qg, d, w.gate_mode)
     assert not qv.is_contiguous()
-    packed = api.ga_prefill(desc_for(w), qv, k, v, gv, wq, wk, pos)
-    dense = api.ga_prefill(desc_for(w), dev(x["q"], et), k, v, dev(x["gate"], et), wq, wk, pos)
+    packed = api.ga_prefill(desc_for(w, kernel=kernel), qv, k, v, gv, wq, wk, pos)
+    dense = api.ga_prefill(desc_for(w, kernel=kernel), dev(x["q"], et), k, v, dev(x["gate"], et), wq, wk, pos)
     torch.cuda.synchronize()
     return packed, dense
 
@@ -74,36 +74,19 @@ PREFILL = [
 
 
 @pytest.mark.parametrize("w", PREFILL, ids=lambda w: w.name)
-def test_packed_prefill_small(w, monkeypatch):
+def test_packed_prefill_small(w):
     print(f"[packed] {w.name}", flush=True)
     d, width = w.head_dim, _width(w, w.extra["pad"])
     assert api.ga_prefill_attention_kernel(
         api.make_desc(w.batch, w.n_q_heads, w.n_kv_heads, d, w.rot_dim, dtype=tdt(w), gate_mode=w.gate_mode,
                       q_head_stride=width, gate_head_stride=width), w.seq_len) == w.extra["kernel"]
-    if w.extra["kernel"] == "generic":
-        # the dense layout of this shape has a fused kernel: compare on the same one
-        monkeypatch.setenv("GA_PREFILL_KERNEL", "generic")
+    # the dense layout of a generic-kernel shape may have a fused kernel: compare on the same one
+    kernel = "generic" if w.extra["kernel"] == "generic" else "auto"
     x = inputs.make_prefill(w)
     qg = _pack(x["q"], x["gate"], w.gate_mode, width)
-    packed, dense = _prefill_pair(w, x, qg)
+    packed, dense = _prefill_pair(w, x, qg, kernel=kernel)
     assert torch.equal(packed, dense), f"{w.name}: packed and dense layouts differ"
     q, gate = _oracle_split(qg, d, w.gate_mode)
-    want = oracle.prefill(q, x["k"], x["v"], gate, gate_mode=w.gate_mode, q_norm_w=x["q_norm_w"],
-                          k_norm_w=x["k_norm_w"], positions=x["positions"], rms_eps=w.rms_eps,
-                          rope_base=w.rope_base, rot_dim=w.rot_dim)
-    assert_close(host(packed), want, w, w.name)
-
-
-def test_packed_prefill_split_mode(monkeypatch):
-    monkeypatch.setenv("GA_PREFILL_KERNEL", "split")
-    w = _prefill_case("split_d256_elem", 1, 300, 8, 2, 256, 64, "elementwise", seed=406)
-    print(f"[packed] {w.name}", flush=True)
-    assert api.ga_prefill_attention_kernel(desc_for(w), w.seq_len) == "split"
-    x = inputs.make_prefill(w)
-    qg = _pack(x["q"], x["gate"], w.gate_mode, _width(w, 0))
-    packed, dense = _prefill_pair(w, x, qg)
-    assert torch.equal(packed, dense)
-    q, gate = _oracle_split(qg, w.head_dim, w.gate_mode)
     want = oracle.prefill(q, x["k"], x["v"], gate, gate_mode=w.gate_mode, q_norm_w=x["q_norm_w"],
                           k_norm_w=x["k_norm_w"], positions=x["positions"], rms_eps=w.rms_eps,
                           rope_base=w.rope_base, rot_dim=w.rot_dim)

@@ -181,3 +181,49 @@ def test_backward_flop_count_is_five_products_per_pair():
     for n in (1, 5, 12):
         pairs = sum(i + 1 for i in range(n))
         assert accounting.causal_backward_flops(2, H, d, n) == 2 * H * pairs * 5 * 2 * d
+
+
+@pytest.mark.parametrize("gate_mode", ["elementwise", "headwise", "none"])
+def test_prefill_blocks_equals_whole_prefill_rows(gate_mode):
+    """The blocked call used at the 32K-token size is the definition applied
+    to row blocks: it equals the matching rows of ``prefill`` (several blocks,
+    a ragged last block, two sequences, groups of 4) and of the independent
+    brute-force loops."""
+    from oracle import loops
+    rng = np.random.default_rng(41)
+    B, n, H, G, d, rot = 2, 45, 8, 2, 8, 4
+    q = rng.standard_normal((B, n, H, d))
+    k = rng.standard_normal((B, n, G, d))
+    v = rng.standard_normal((B, n, G, d))
+    gate = {"elementwise": rng.standard_normal((B, n, H, d)), "headwise": rng.standard_normal((B, n, H)),
+            "none": None}[gate_mode]
+    wq, wk = 1 + 0.1 * rng.standard_normal(d), 1 + 0.1 * rng.standard_normal(d)
+    pos = np.tile(np.arange(n, dtype=np.int32), (B, 1)) + np.array([[0], [7]], dtype=np.int32)
+    kw = dict(gate_mode=gate_mode, q_norm_w=wq, k_norm_w=wk, positions=pos, rms_eps=1e-6, rope_base=10000.0,
+              rot_dim=rot)
+    whole = A.prefill(q, k, v, gate, **kw)
+    blocks = [(0, 0), (1, 16), (0, 32), (1, 32)]
+    got = A.prefill_blocks(q, k, v, gate, blocks, block_rows=16, **kw)
+    for o, (b, r0) in enumerate(blocks):
+        r1 = min(n, r0 + 16)
+        assert np.allclose(got[o, : r1 - r0], whole[b, r0:r1], rtol=0, atol=1e-12)
+        assert np.all(np.isnan(got[o, r1 - r0:]))                     # rows past n
+    brute = np.array(loops.gated_attention(q.tolist(), k.tolist(), v.tolist(),
+                                           None if gate is None else gate.tolist(), gate_mode, wq.tolist(),
+                                           wk.tolist(), pos.tolist(), 1e-6, 10000.0, rot))
+    assert np.allclose(got[1, :16], brute[1, 16:32], rtol=0, atol=1e-12)
+
+
+def test_prefill_blocks_catches_a_shifted_mask():
+    """A block whose mask is taken relative to the block start instead of the
+    token index would see too few keys: the pin above would fail on it."""
+    rng = np.random.default_rng(42)
+    q, k, v = (rng.standard_normal((1, 40, 2, 8)) for _ in range(3))
+    k, v = k[:, :, :1], v[:, :, :1]
+    pos = np.arange(40, dtype=np.int32)[None]
+    kw = dict(gate_mode="none", q_norm_w=None, k_norm_w=None, positions=pos, rot_dim=0)
+    whole = A.prefill(q, k, v, None, **kw)
+    got = A.prefill_blocks(q, k, v, None, [(0, 20)], block_rows=16, **kw)
+    wrong = A.prefill(q[:, 20:], k[:, 20:], v[:, 20:], None, **dict(kw, positions=pos[:, 20:]))
+    assert np.allclose(got[0], whole[0, 20:36], atol=1e-12)
+    assert not np.allclose(got[0], wrong[0, :16], atol=1e-3)
