@@ -219,7 +219,7 @@ def time_prefill(torch, api, inputs, accounting, wname, steps, warmup, samples=5
         api.ga_prefill(d, q, k, v, gate, wq, wk, pos, out=out, workspace=ws, stream=stream)
 
     def attention():
-        api.ga_prefill_attention(d, q, khat, v, gate, wq, pos, out=out, stream=stream)
+        api.ga_prefill_attention(d, q, khat, v, gate, wq, pos, out=out, stream=stream, k_norm_w=wk)
 
     t0 = time.perf_counter()
     res = time_whole_and_kernel(torch, whole, attention, stream, steps, warmup, samples)
@@ -510,7 +510,7 @@ def time_packed(torch, api, inputs, accounting, wname, steps, warmup):
         api.ga_prefill(d, q, k, v, gate, wq, wk, pos, out=out, workspace=ws, stream=stream)
 
     def attention():
-        api.ga_prefill_attention(d, q, khat, v, gate, wq, pos, out=out, stream=stream)
+        api.ga_prefill_attention(d, q, khat, v, gate, wq, pos, out=out, stream=stream, k_norm_w=wk)
 
     res = time_whole_and_kernel(torch, whole, attention, stream, steps, warmup)
     flops = accounting.causal_prefill_flops(w.batch, w.n_q_heads, hd, w.seq_len)
@@ -553,7 +553,7 @@ def time_gate_variant(torch, api, inputs, accounting, wname, steps, warmup):
         api.ga_prefill(d, q, k, v, gate, wq, wk, pos, out=out, workspace=ws, stream=stream)
 
     def attention():
-        api.ga_prefill_attention(d, q, khat, v, gate, wq, pos, out=out, stream=stream)
+        api.ga_prefill_attention(d, q, khat, v, gate, wq, pos, out=out, stream=stream, k_norm_w=wk)
 
     res = time_whole_and_kernel(torch, whole, attention, stream, steps, warmup)
     flops = accounting.causal_prefill_flops(w.batch, w.n_q_heads, w.head_dim, w.seq_len)

@@ -337,7 +337,10 @@ def ga_prefill_keys(desc: AttnDesc, k, v=None, k_norm_w=None, positions=None, k_
 
 
 def ga_prefill_attention(desc: AttnDesc, q, k_hat, v, gate=None, q_norm_w=None, positions=None, out=None,
-                         stream=None) -> torch.Tensor:
+                         stream=None, k_norm_w=None) -> torch.Tensor:
+    """Attention stage of ga_prefill over prepared keys; ``k_norm_w`` = the
+    weights ga_prefill_keys normed k_hat with (lets the kernels bound the
+    scores), or None."""
     lib = _lib.load()
     et = _elem_dtype(desc)
     B, n = desc.batch, _seq(q)[1]
@@ -353,7 +356,7 @@ def ga_prefill_attention(desc: AttnDesc, q, k_hat, v, gate=None, q_norm_w=None, 
     if kcap < n or vcap < n:
         raise ValueError(f"k_hat / v hold {kcap} / {vcap} rows per sequence, {n} required")
     st = lib.ga_prefill_attention(ctypes.byref(d2), n, qp, khp, kcap, vp, vcap, gp,
-                                  _norm_w(q_norm_w, "q_norm_w", desc),
+                                  _norm_w(q_norm_w, "q_norm_w", desc), _norm_w(k_norm_w, "k_norm_w", desc),
                                   _tensor(positions, "positions", (B, n), torch.int32, required=False),
                                   op, _stream(stream))
     _check(st, "ga_prefill_attention")

@@ -253,9 +253,12 @@ ga_status prefill_keys_impl(const ga_attn_desc* desc, int32_t n, const void* k, 
   return hip_status(launch_prep_keys(pp, desc->dtype == GA_BF16, stream), "prefill keys launch");
 }
 
+// k_norm_w: the weights k_hat was normed with, or null when unknown (then no
+// score bound is used).
 ga_status prefill_attn_impl(const ga_attn_desc* desc, int32_t n, const void* q, const void* k_hat,
                             int32_t k_cap, const void* v, int32_t v_cap, const void* gate,
-                            const float* q_norm_w, const int32_t* positions, void* out, hipStream_t stream) {
+                            const float* q_norm_w, const float* k_norm_w, const int32_t* positions, void* out,
+                            hipStream_t stream) {
   const int H = desc->n_q_heads, G = desc->n_kv_heads, d = desc->head_dim;
   const int grp = H / G;
   const PrefillKernel choice = prefill_choice(desc, n, k_cap, v_cap);
@@ -270,6 +273,7 @@ ga_status prefill_attn_impl(const ga_attn_desc* desc, int32_t n, const void* q, 
     pp.v = (const uint16_t*)v;
     pp.gate = (const uint16_t*)gate;
     pp.wq = q_norm_w;
+    pp.wk = k_norm_w;
     pp.positions = positions;
     pp.out = (uint16_t*)out;
     pp.k_bstride = (long)k_cap * G * d;
@@ -739,7 +743,8 @@ ga_status ga_prefill_keys(const ga_attn_desc* desc, int32_t seq_len, const void*
 
 ga_status ga_prefill_attention(const ga_attn_desc* desc, int32_t seq_len, const void* q, const void* k_hat,
                                int32_t k_cap, const void* v, int32_t v_cap, const void* gate,
-                               const float* q_norm_w, const int32_t* positions, void* out, void* stream) {
+                               const float* q_norm_w, const float* k_norm_w, const int32_t* positions, void* out,
+                               void* stream) {
   ga_status st;
   if ((st = check_desc(desc)) != GA_OK) return st;
   if (seq_len < 0) return fail(GA_ERR_BAD_SHAPE, "seq_len %d < 0", seq_len);
@@ -750,12 +755,13 @@ ga_status ga_prefill_attention(const ga_attn_desc* desc, int32_t seq_len, const 
   if ((st = check_tensor(out, "out", desc)) != GA_OK) return st;
   if ((st = check_gate(gate, desc)) != GA_OK) return st;
   if ((st = check_norm_w(q_norm_w, "q_norm_w")) != GA_OK) return st;
+  if ((st = check_norm_w(k_norm_w, "k_norm_w")) != GA_OK) return st;
   if (k_cap < seq_len || v_cap < seq_len)
     return fail(GA_ERR_BAD_SHAPE, "k_cap %d / v_cap %d < seq_len %d", k_cap, v_cap, seq_len);
   if (prefill_choice(desc, seq_len, k_cap, v_cap) == PK_INVALID)
     return fail(GA_ERR_UNSUPPORTED, "the forced kernel %d does not serve this shape", desc->kernel);
   return prefill_attn_impl(desc, seq_len, q, k_hat, k_cap, v, v_cap,
-                           desc->gate_mode == GA_GATE_NONE ? nullptr : gate, q_norm_w, positions, out,
+                           desc->gate_mode == GA_GATE_NONE ? nullptr : gate, q_norm_w, k_norm_w, positions, out,
                            (hipStream_t)stream);
 }
 
@@ -796,7 +802,7 @@ ga_status ga_prefill(const ga_attn_desc* desc, int32_t seq_len, const void* q, c
   hipStream_t s = (hipStream_t)stream;
   if ((st = prefill_keys_impl(desc, seq_len, k, v, k_norm_w, positions, khat, v_cache, kcap, s)) != GA_OK) return st;
   return prefill_attn_impl(desc, seq_len, q, khat, kcap, v, seq_len,
-                           desc->gate_mode == GA_GATE_NONE ? nullptr : gate, q_norm_w, positions, out, s);
+                           desc->gate_mode == GA_GATE_NONE ? nullptr : gate, q_norm_w, k_norm_w, positions, out, s);
 }
 
 const char* ga_prefill_chunk_kernel(const ga_attn_desc* desc, int32_t seq_len, int32_t cache_cap) {

@@ -48,6 +48,9 @@ struct PrefillParams {
   const uint16_t* v;
   const uint16_t* gate;
   const float* wq;
+  // k-norm weights that k_hat was normed with (null: unknown). With wq they
+  // bound every score, and the kernels drop the running row max.
+  const float* wk;
   const int* positions;
   uint16_t* out;
   // Chunk against a cache (mirrored kernel only; both null otherwise): the

@@ -13,9 +13,18 @@
 //    in LDS through ds_read_b64_tr_b16.
 //  * K and V rows are XOR-swizzled in LDS per 16-byte chunk (K: chunk ^
 //    (row & 15); V: chunk ^ 4 (row & 3)) so those reads are conflict-free.
-//  * The running max is raised lazily: the output is rescaled only when a
-//    tile's max exceeds the reference by more than 2^8, so probabilities stay
-//    below 256 (exact in fp32, fine as bf16 operands).
+//  * Two forms of the softmax. With QK-norm on both sides the scores have a
+//    known bound: |q_hat . k_hat| <= |q_hat| |k_hat| and |k_hat| <= sqrt(d)
+//    max|w_k| (an RMS-normed row has norm sqrt(d) before its weights; RoPE
+//    keeps norms). The bounded tile (attn_tile_b) then subtracts that bound,
+//    per query row, inside the QK MFMA (its accumulator starts at -c), so the
+//    MFMA result is already the exponent: p = 2^(s - c) <= 1, with no running
+//    max, no rescale and no row-max reduction. Subtracting any constant is
+//    exact for softmax (it cancels between numerator and denominator); the
+//    max is only needed when nothing bounds the scores.
+//  * Otherwise (attn_tile) the running max is raised lazily: the output is
+//    rescaled only when a tile's max exceeds the reference by more than 2^8,
+//    so probabilities stay below 256 (exact in fp32, fine as bf16 operands).
 #pragma once
 
 #include "ga_common.hpp"
@@ -80,7 +89,9 @@ template <int D>
 struct WaveState {
   QFrags<D> q;           // Q^T operand fragments of this wave's 32 rows
   f32x16_t o[D / 32];    // O^T accumulators
-  float m_run, l_run;    // reference max (log2 domain) and lane-partial row sum
+  f32x16_t cinit;        // bounded tiles, d < 256: -c (the row's score bound) in every element
+  float m_run, l_run;    // reference max (log2 domain; bounded tiles at d = 256: -c) and
+                         // lane-partial row sum
   int kbase;             // K operand LDS address of step 0 (lane part, phase included);
                          // step kk reads kbase ^ ((kk & 7) << 5), + 256 for kk >= 8
   int vbase;             // V^T operand LDS address of dim block 0 (lane part, phase and
@@ -224,5 +235,126 @@ __device__ __forceinline__ void attn_tile(const unsigned char* smem, WaveState<D
   }
   __builtin_amdgcn_sched_group_barrier(0x008, VPF, 1);
 }
+
+// Bounded-score tile: the same 32 keys as attn_tile, for rows whose scores
+// (log2 domain, softmax scale folded into q_hat) never exceed their bound c.
+// With CINIT the QK chain starts from ws.cinit = -c, so the scores come out
+// as s - c; otherwise (d = 256, where the 16 registers of ws.cinit do not fit
+// beside two waves per SIMD) c = -ws.cinit[0] is subtracted before the exp.
+// p = 2^(s - c) needs one exp each; the row sum adds the bf16-rounded
+// probabilities (the PV operands) two at a time with v_dot2c_f32_bf16.
+template <int D, int NS, int BUF, int HALF, bool CINIT = (D < 256)>
+__device__ __forceinline__ void attn_tile_b(const unsigned char* smem, WaveState<D>& ws, bool need_mask, int lim) {
+  typedef TileShape<D, NS> S;
+  constexpr int NK = D / 16;
+  constexpr int NV = D / 16;
+  constexpr int KPF = (D == 256) ? 3 : 4;
+  constexpr int VPF = (D == 256) ? 2 : 3;
+  int kb = ws.kbase, vb = ws.vbase;
+  asm volatile("" : "+v"(kb), "+v"(vb));
+  auto kread = [&](int kk) {
+    int a = kb ^ ((kk & 7) << 5);
+    asm volatile("" : "+v"(a));
+    return *(const bf16x8_t*)(smem + a + (BUF * S::TILE_BYTES + HALF * 32 * S::ROW_BYTES + ((kk >> 3) << 8)));
+  };
+  auto vread = [&](int t) {
+    const int ks = t / (D / 32), mb = t % (D / 32);
+    int a = vb ^ ((mb & 3) << 6);
+    asm volatile("" : "+v"(a));
+    const unsigned char* a1 =
+        smem + a + (BUF * S::TILE_BYTES + HALF * 32 * S::ROW_BYTES + ((mb & 4) << 6) + ks * 16 * S::ROW_BYTES);
+    const i16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)a1);
+    const i16x4_t v2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(a1 + 8 * S::ROW_BYTES));
+    const u32x4_t av = {__builtin_bit_cast(u32x2_t, v1)[0], __builtin_bit_cast(u32x2_t, v1)[1],
+                        __builtin_bit_cast(u32x2_t, v2)[0], __builtin_bit_cast(u32x2_t, v2)[1]};
+    return __builtin_bit_cast(bf16x8_t, av);
+  };
+
+  bf16x8_t ka[NK];
+  f32x16_t s;
+#pragma unroll
+  for (int kk = 0; kk < KPF; ++kk) ka[kk] = kread(kk);
+#pragma unroll
+  for (int kk = 0; kk < NK; ++kk) {
+    if (kk + KPF < NK) ka[kk + KPF] = kread(kk + KPF);
+    if (CINIT)
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[kk], ws.qf(kk), kk == 0 ? ws.cinit : s, 0, 0, 0);
+    else
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[kk], ws.qf(kk), kk == 0 ? f32x16_t{} : s, 0, 0, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x100, KPF, 0);
+#pragma unroll
+  for (int kk = 0; kk < NK - KPF; ++kk) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, KPF, 0);
+  bf16x8_t va[NV];
+#pragma unroll
+  for (int t = 0; t < VPF; ++t) va[t] = vread(t);
+  if (!CINIT) {
+    const float nc = ws.m_run;  // -c
+#pragma unroll
+    for (int i = 0; i < 16; ++i) s[i] += nc;
+  }
+  if (need_mask) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) s[i] = ((i >> 2) * 8 + (i & 3) <= lim) ? s[i] : -INFINITY;
+  }
+  bf16x8_t pb[2];
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    u32x4_t pk;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      pk[j] = pack_bf16x2(__builtin_amdgcn_exp2f(s[ks * 8 + 2 * j]), __builtin_amdgcn_exp2f(s[ks * 8 + 2 * j + 1]));
+    pb[ks] = __builtin_bit_cast(bf16x8_t, pk);
+  }
+  {
+    const bf16x2_t one2 = {(__bf16)1.0f, (__bf16)1.0f};
+    float l = ws.l_run;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const u32x4_t pk = __builtin_bit_cast(u32x4_t, pb[ks]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        // (the element goes through a scalar: a bit cast of the subscript
+        // itself compiled to a read of element 0)
+        const uint32_t wj = pk[j];
+        l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, wj), one2, l, false);
+      }
+    }
+    ws.l_run = l;
+  }
+#pragma unroll
+  for (int t = 0; t < NV; ++t) {
+    if (t + VPF < NV) va[t + VPF] = vread(t + VPF);
+    const int ks = t / (D / 32), mb = t % (D / 32);
+    ws.o[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[t], pb[ks], ws.o[mb], 0, 0, 0);
+  }
+#pragma unroll
+  for (int t = 0; t < NV - VPF; ++t) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, VPF, 1);
+}
+
+// Largest |w[e]| over the d weights, the same value in every lane (0 for a
+// null pointer). Each lane reads d/64 of them.
+template <int D>
+__device__ __forceinline__ float max_abs_weight(const float* w) {
+  if (!w) return 0.f;
+  const int lane = threadIdx.x & 63;
+  float m = 0.f;
+#pragma unroll
+  for (int e = lane; e < D; e += 64) m = fmaxf(m, fabsf(w[e]));
+  return max_xor<64>(m);
+}
+
+// Largest log2-domain score bound a row may have before the bounded tiles'
+// probabilities 2^(s - c) could leave the normal fp32 range (the row's
+// largest one is at least 2^(-2c)).
+constexpr float kMaxScoreBound = 60.0f;
 
 }  // namespace ga

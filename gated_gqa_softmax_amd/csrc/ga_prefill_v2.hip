@@ -58,7 +58,7 @@ __device__ __forceinline__ uint16_t* v2_qrow(unsigned char* smem, int r) {
 // waves then issue the whole stage, their own share and that of wave w ^ 2
 // (the row group 2-3 wave), so the waves that compute never stall on a full
 // load queue. (Each wave waits for its own loads; the barrier for all.)
-template <int D, int BUF>
+template <int D, int BUF, bool BOUNDED>
 __device__ __forceinline__ void v2_step(unsigned char* smem, WaveState<D>& ws, i32x4_t krs, i32x4_t vrs, int koff, int voff, int w, int st, int st_end,
                                         int kv_row_bytes, int phase, int wave_min_key, int wave_max_key,
                                         int my_lim_key, int nkeys, float sl2, int hi, int light_end, bool light_wave) {
@@ -88,7 +88,30 @@ __device__ __forceinline__ void v2_step(unsigned char* smem, WaveState<D>& ws, i
   const int k0 = st * S::ST + phase * 32;
   if (k0 <= wave_max_key) {
     const bool need_mask = (k0 + 31 > wave_min_key) || (k0 + 32 > nkeys);  // wave-uniform
-    attn_tile<D, kMirrorStages<D>, BUF, 0>(smem, ws, need_mask, my_lim_key - (k0 + hi * 4), sl2);
+    if (BOUNDED)
+      attn_tile_b<D, kMirrorStages<D>, BUF, 0>(smem, ws, need_mask, my_lim_key - (k0 + hi * 4));
+    else
+      attn_tile<D, kMirrorStages<D>, BUF, 0>(smem, ws, need_mask, my_lim_key - (k0 + hi * 4), sl2);
+  }
+}
+
+// The main loop, unrolled over the stage buffers.
+template <int D, bool BOUNDED>
+__device__ __forceinline__ void v2_loop(unsigned char* smem, WaveState<D>& ws, i32x4_t krs, i32x4_t vrs, int koff,
+                                        int voff, int w, int nst, int kv_row_bytes, int phase, int wave_min_key,
+                                        int wave_max_key, int my_lim_key, int nkeys, float sl2, int hi, int light_end,
+                                        bool light_wave) {
+  constexpr int NS = kMirrorStages<D>;
+  for (int st0 = 0; st0 < nst; st0 += NS) {
+    v2_step<D, 0, BOUNDED>(smem, ws, krs, vrs, koff, voff, w, st0, nst, kv_row_bytes, phase, wave_min_key,
+                           wave_max_key, my_lim_key, nkeys, sl2, hi, light_end, light_wave);
+    if (st0 + 1 < nst)
+      v2_step<D, 1, BOUNDED>(smem, ws, krs, vrs, koff, voff, w, st0 + 1, nst, kv_row_bytes, phase, wave_min_key,
+                             wave_max_key, my_lim_key, nkeys, sl2, hi, light_end, light_wave);
+    if (NS == 3 && st0 + 2 < nst)
+      v2_step<D, (NS == 3 ? 2 : 0), BOUNDED>(smem, ws, krs, vrs, koff, voff, w, st0 + 2, nst, kv_row_bytes, phase,
+                                             wave_min_key, wave_max_key, my_lim_key, nkeys, sl2, hi, light_end,
+                                             light_wave);
   }
 }
 
@@ -120,6 +143,7 @@ __global__ __launch_bounds__(512) void prefill_v2_kernel(const PrefillParams p) 
   __shared__ float2 table[2048];
   __shared__ float ml_x[4][64][2];
   __shared__ float lse_x[4][32];  // LSE: log2-domain log-sum-exp of each row
+  __shared__ float c_x[128];      // bounded rows: the score bound c of each row
 
   const int w = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);  // wave index (uniform)
   // wave -> (row group, phase): each SIMD (w % 4) gets one light and one heavy wave
@@ -204,6 +228,14 @@ __global__ __launch_bounds__(512) void prefill_v2_kernel(const PrefillParams p) 
     voff = row0 * kv_row_bytes + ((ph ^ swz_v(row0)) << 4);
   }
 
+
+  // ---- score bound (see attn_tile_b): with both norm weights every score
+  // s * log2(e) is at most scale * |q_hat| * sqrt(d) max|w_k| (2% margin for
+  // the bf16 roundings and the sin/cos error); bounded rows fold the scale
+  // into q_hat. Workgroup-uniform: it depends on the weights only.
+  const float sl2 = p.scale_log2;
+  const float kb_norm = max_abs_weight<D>(p.wk) * sqrtf((float)D) * 1.02f;
+  const bool bounded = !LSE && p.wq && p.wk && sl2 * sqrtf((float)D) * max_abs_weight<D>(p.wq) * kb_norm <= kMaxScoreBound;
 
   // ---- Q prologue: RMSNorm + RoPE of 128 rows into LDS ------------------------
   // Four adjacent lanes per row, each holding QE = D/4 elements in 16-byte
@@ -303,9 +335,16 @@ __global__ __launch_bounds__(512) void prefill_v2_kernel(const PrefillParams p) 
 #pragma unroll
     for (int e = 0; e < QE; ++e) ss += x[e] * x[e];
     ss = quad_sum(ss);
-    const float inv = rsqrtf(ss * (1.0f / D) + p.eps);
+    const float inv = rsqrtf(ss * (1.0f / D) + p.eps) * (bounded ? sl2 : 1.0f);
+    float s2 = 0.f;
 #pragma unroll
-    for (int e = 0; e < QE; ++e) x[e] *= inv * qw[e / 4][e % 4];
+    for (int e = 0; e < QE; ++e) {
+      x[e] *= inv * qw[e / 4][e % 4];
+      s2 += x[e] * x[e];
+    }
+    // |q_hat| (RoPE below keeps it) times the bound on |k_hat|
+    const float qn2 = quad_sum(s2);  // (all four lanes of the quad take part)
+    if (bounded && qq == 0) c_x[qrow] = sqrtf(qn2) * kb_norm;
   }
   if (spread) {
     // x[j] is element 8qq + j and x[8 + j] its partner 8qq + j + half
@@ -357,9 +396,16 @@ __global__ __launch_bounds__(512) void prefill_v2_kernel(const PrefillParams p) 
   for (int mb = 0; mb < D / 32; ++mb)
 #pragma unroll
     for (int i = 0; i < 16; ++i) ws.o[mb][i] = 0.f;
-  ws.m_run = kNegBig;
+  // bounded rows: the scores are shifted by -c (d = 128: accumulators start at
+  // -c; d = 256: m_run holds -c for the tile's subtraction); both phases of a
+  // row share the shift, so the phase merge below adds them unscaled
+  const float bound_c = bounded ? c_x[rg * 32 + l32] : 0.f;
+  if (D < 256) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) ws.cinit[i] = -bound_c;
+  }
+  ws.m_run = bounded ? (D < 256 ? 0.f : -bound_c) : kNegBig;
   ws.l_run = 0.f;
-  const float sl2 = p.scale_log2;
   {
     const int i16 = lane & 15;
     const int g16 = lane >> 4;
@@ -378,17 +424,13 @@ __global__ __launch_bounds__(512) void prefill_v2_kernel(const PrefillParams p) 
                                       ? (L0 + min(nb, blk_light * TB + TB) + S::ST - 1) / S::ST
                                       : 0)
                                : ((blk_light >= 0) ? (min(n, blk_light * TB + TB) + S::ST - 1) / S::ST : 0);
-  // ---- main loop, unrolled over the stage buffers -----------------------------
-  for (int st0 = 0; st0 < nst; st0 += S::NSTAGE) {
-    v2_step<D, 0>(smem, ws, krs, vrs, koff, voff, w, st0, nst, kv_row_bytes, phase, wave_min_key, wave_max_key,
-                  my_lim_key, nkeys, sl2, hi, light_end, rg < 2);
-    if (st0 + 1 < nst)
-      v2_step<D, 1>(smem, ws, krs, vrs, koff, voff, w, st0 + 1, nst, kv_row_bytes, phase, wave_min_key,
-                    wave_max_key, my_lim_key, nkeys, sl2, hi, light_end, rg < 2);
-    if (S::NSTAGE == 3 && st0 + 2 < nst)
-      v2_step<D, (S::NSTAGE == 3 ? 2 : 0)>(smem, ws, krs, vrs, koff, voff, w, st0 + 2, nst, kv_row_bytes, phase,
-                                           wave_min_key, wave_max_key, my_lim_key, nkeys, sl2, hi, light_end, rg < 2);
-  }
+  // ---- main loop ----------------------------------------------------------------
+  if (bounded)
+    v2_loop<D, true>(smem, ws, krs, vrs, koff, voff, w, nst, kv_row_bytes, phase, wave_min_key, wave_max_key,
+                     my_lim_key, nkeys, sl2, hi, light_end, rg < 2);
+  else
+    v2_loop<D, false>(smem, ws, krs, vrs, koff, voff, w, nst, kv_row_bytes, phase, wave_min_key, wave_max_key,
+                      my_lim_key, nkeys, sl2, hi, light_end, rg < 2);
 
   // ---- epilogue: merge the two phases, normalise, gate, store ---------------
   // Both waves of a row group finish it: phase f writes rows [16f, 16f + 16),

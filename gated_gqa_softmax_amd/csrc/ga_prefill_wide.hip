@@ -44,7 +44,7 @@ __device__ __forceinline__ void wait_stage(int ahead) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
-template <int D, int BUF>
+template <int D, int BUF, bool BOUNDED>
 __device__ __forceinline__ void wide_step(unsigned char* smem, WaveState<D>& ws, i32x4_t krs, i32x4_t vrs,
                                           int koff, int voff, int w, int st, int nst, int kv_row_bytes,
                                           int wave_min_tok, int wave_max_tok, int my_lim_tok, int n, float sl2,
@@ -58,11 +58,37 @@ __device__ __forceinline__ void wide_step(unsigned char* smem, WaveState<D>& ws,
   const int k0 = st * S::ST;
   if (k0 <= wave_max_tok) {
     const bool need_mask = (k0 + 31 > wave_min_tok) || (k0 + 32 > n);
-    attn_tile<D, S::NSTAGE, BUF, 0>(smem, ws, need_mask, my_lim_tok - (k0 + hi * 4), sl2);
+    if (BOUNDED)
+      attn_tile_b<D, S::NSTAGE, BUF, 0>(smem, ws, need_mask, my_lim_tok - (k0 + hi * 4));
+    else
+      attn_tile<D, S::NSTAGE, BUF, 0>(smem, ws, need_mask, my_lim_tok - (k0 + hi * 4), sl2);
   }
   if (k0 + 32 <= wave_max_tok) {
     const bool need_mask = (k0 + 63 > wave_min_tok) || (k0 + 64 > n);
-    attn_tile<D, S::NSTAGE, BUF, 1>(smem, ws, need_mask, my_lim_tok - (k0 + 32 + hi * 4), sl2);
+    if (BOUNDED)
+      attn_tile_b<D, S::NSTAGE, BUF, 1>(smem, ws, need_mask, my_lim_tok - (k0 + 32 + hi * 4));
+    else
+      attn_tile<D, S::NSTAGE, BUF, 1>(smem, ws, need_mask, my_lim_tok - (k0 + 32 + hi * 4), sl2);
+  }
+}
+
+// The main loop, unrolled over the ring.
+template <int D, bool BOUNDED>
+__device__ __forceinline__ void wide_loop(unsigned char* smem, WaveState<D>& ws, i32x4_t krs, i32x4_t vrs,
+                                          int koff, int voff, int w, int nst, int kv_row_bytes, int wave_min_tok,
+                                          int wave_max_tok, int my_lim_tok, int n, float sl2, int hi) {
+  for (int st0 = 0; st0 < nst; st0 += kWideStages) {
+    wide_step<D, 0, BOUNDED>(smem, ws, krs, vrs, koff, voff, w, st0, nst, kv_row_bytes, wave_min_tok, wave_max_tok,
+                             my_lim_tok, n, sl2, hi);
+    if (st0 + 1 < nst)
+      wide_step<D, 1, BOUNDED>(smem, ws, krs, vrs, koff, voff, w, st0 + 1, nst, kv_row_bytes, wave_min_tok,
+                               wave_max_tok, my_lim_tok, n, sl2, hi);
+    if (st0 + 2 < nst)
+      wide_step<D, 2, BOUNDED>(smem, ws, krs, vrs, koff, voff, w, st0 + 2, nst, kv_row_bytes, wave_min_tok,
+                               wave_max_tok, my_lim_tok, n, sl2, hi);
+    if (st0 + 3 < nst)
+      wide_step<D, 3, BOUNDED>(smem, ws, krs, vrs, koff, voff, w, st0 + 3, nst, kv_row_bytes, wave_min_tok,
+                               wave_max_tok, my_lim_tok, n, sl2, hi);
   }
 }
 
@@ -123,8 +149,19 @@ __global__ __launch_bounds__(512) void prefill_wide_kernel(const PrefillParams p
   if (nst > 1) stage_issue<D, S::NSTAGE, 1>(smem, krs, vrs, koff, voff, w, 1, kv_row_bytes);
   if (nst > 2) stage_issue<D, S::NSTAGE, 2>(smem, krs, vrs, koff, voff, w, 2, kv_row_bytes);
 
+  // ---- score bound: with both norm weights, |s| * log2(e) <= scale * d *
+  // max|w_q| * max|w_k| (RMS-normed rows have norm sqrt(d) before their
+  // weights, RoPE keeps norms; 2% margin for the bf16 roundings of q_hat and
+  // k_hat and the sin/cos error). Workgroup-uniform: it depends on the
+  // weights only.
+  const float sl2 = p.scale_log2;
+  const float kb_norm = max_abs_weight<D>(p.wk) * sqrtf((float)D) * 1.02f;  // bound on |k_hat|
+  const bool bounded = p.wq && p.wk && sl2 * sqrtf((float)D) * max_abs_weight<D>(p.wq) * kb_norm <= kMaxScoreBound;
+
   // ---- q_hat of this lane's row, straight into the MFMA operand layout -------
   // Lane (l32, hi) holds elements 16kk + 8hi + [0, 8) of row l32 for every kk.
+  // Bounded rows fold the softmax scale (log2 domain) into q_hat and start
+  // their score accumulators at -c, c = |q_hat| * (bound on |k_hat|).
   WaveState<D> ws;
   {
     constexpr int NK = D / 16;
@@ -182,6 +219,21 @@ __global__ __launch_bounds__(512) void prefill_wide_kernel(const PrefillParams p
         }
       }
     }
+    float c = 0.f;
+    if (bounded) {
+      float ss = 0.f;
+#pragma unroll
+      for (int kk = 0; kk < NK; ++kk)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          x[kk][j] *= sl2;
+          ss += x[kk][j] * x[kk][j];
+        }
+      ss += swap_half(ss);
+      c = sqrtf(ss) * kb_norm;
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) ws.cinit[i] = -c;
 #pragma unroll
     for (int kk = 0; kk < NK; ++kk) ws.set_qf(kk, __builtin_bit_cast(bf16x8_t, pack8(x[kk])));
   }
@@ -191,7 +243,6 @@ __global__ __launch_bounds__(512) void prefill_wide_kernel(const PrefillParams p
     for (int i = 0; i < 16; ++i) ws.o[mb][i] = 0.f;
   ws.m_run = kNegBig;
   ws.l_run = 0.f;
-  const float sl2 = p.scale_log2;
   {
     const int i16 = lane & 15;
     const int g16 = lane >> 4;
@@ -204,20 +255,13 @@ __global__ __launch_bounds__(512) void prefill_wide_kernel(const PrefillParams p
     ws.vbase = S::VBASE + (hi * 4 + (i16 >> 2)) * S::ROW_BYTES + ((4 * x + c) << 4) + (i16 & 1) * 8;
   }
 
-  // ---- main loop, unrolled over the ring --------------------------------------
-  for (int st0 = 0; st0 < nst; st0 += S::NSTAGE) {
-    wide_step<D, 0>(smem, ws, krs, vrs, koff, voff, w, st0, nst, kv_row_bytes, wave_min_tok, wave_max_tok,
-                    my_lim_tok, n, sl2, hi);
-    if (st0 + 1 < nst)
-      wide_step<D, 1>(smem, ws, krs, vrs, koff, voff, w, st0 + 1, nst, kv_row_bytes, wave_min_tok, wave_max_tok,
-                      my_lim_tok, n, sl2, hi);
-    if (st0 + 2 < nst)
-      wide_step<D, 2>(smem, ws, krs, vrs, koff, voff, w, st0 + 2, nst, kv_row_bytes, wave_min_tok, wave_max_tok,
-                      my_lim_tok, n, sl2, hi);
-    if (st0 + 3 < nst)
-      wide_step<D, 3>(smem, ws, krs, vrs, koff, voff, w, st0 + 3, nst, kv_row_bytes, wave_min_tok, wave_max_tok,
-                      my_lim_tok, n, sl2, hi);
-  }
+  // ---- main loop ---------------------------------------------------------------
+  if (bounded)
+    wide_loop<D, true>(smem, ws, krs, vrs, koff, voff, w, nst, kv_row_bytes, wave_min_tok, wave_max_tok, my_lim_tok,
+                       n, sl2, hi);
+  else
+    wide_loop<D, false>(smem, ws, krs, vrs, koff, voff, w, nst, kv_row_bytes, wave_min_tok, wave_max_tok,
+                        my_lim_tok, n, sl2, hi);
 
   // ---- epilogue: normalise, gate, store ----------------------------------------
   // The wave's 32 rows, RPI rows per instruction and LPR lanes of 8 elements

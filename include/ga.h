@@ -200,12 +200,19 @@ ga_status ga_prefill_keys(const ga_attn_desc* desc, int32_t seq_len,
  * (d in {64, 128, 256}), else the generic kernel; desc->kernel may force one.
  * Needs no workspace.
  *  k_hat  [B,k_cap,G,d] as written by ga_prefill_keys (k_cap >= seq_len).
- *  v      [B,v_cap,G,d] (v_cap >= seq_len; the raw v input has v_cap = n). */
+ *  v      [B,v_cap,G,d] (v_cap >= seq_len; the raw v input has v_cap = n).
+ *  k_norm_w  [d] float32: the weights ga_prefill_keys normed k_hat with, or
+ *         NULL when k_hat has no such norm. With q_norm_w it bounds every
+ *         score (|q_hat . k_hat| <= |q_hat| sqrt(d) max|w_k|), and the fused
+ *         kernels then subtract that bound instead of a running row max
+ *         (softmax is unchanged by any shift). A k_hat whose rows are longer
+ *         than the weights allow still gives correct results as long as its
+ *         scores stay within about 2^60 of the bound (exp2 range of fp32). */
 ga_status ga_prefill_attention(const ga_attn_desc* desc, int32_t seq_len,
                                const void* q, const void* k_hat, int32_t k_cap,
                                const void* v, int32_t v_cap, const void* gate,
-                               const float* q_norm_w, const int32_t* positions,
-                               void* out, void* stream);
+                               const float* q_norm_w, const float* k_norm_w,
+                               const int32_t* positions, void* out, void* stream);
 
 /* ---- chunked prefill against a KV cache ---------------------------------- */
 

@@ -172,8 +172,10 @@ def test_forced_kernel_field():
     d256 = _desc(kernel=_lib.GA_KERNEL_WIDE)                  # the wide kernel serves d = 128 only
     assert lib.ga_prefill_attention_kernel(ctypes.byref(d256), 4096) == b"unsupported"
     assert _prefill(lib, d256) == _lib.GA_ERR_UNSUPPORTED
-    assert lib.ga_prefill_attention(ctypes.byref(d256), 16, A16, A16, 16, A16, 16, A16, None, None, A16,
+    assert lib.ga_prefill_attention(ctypes.byref(d256), 16, A16, A16, 16, A16, 16, A16, None, None, None, A16,
                                     None) == _lib.GA_ERR_UNSUPPORTED
+    assert lib.ga_prefill_attention(ctypes.byref(_desc()), 16, A16, A16, 16, A16, 16, A16, None, A16 + 4, None, A16,
+                                    None) == _lib.GA_ERR_MISALIGNED
     f32 = _desc(dtype=_lib.GA_F32, kernel=_lib.GA_KERNEL_MIRROR)
     assert lib.ga_prefill_attention_kernel(ctypes.byref(f32), 64) == b"unsupported"
     # chunks: mirrored or generic only

@@ -225,6 +225,6 @@ def test_prefill_cache_write_and_stages():
     d = desc_for(w)
     khat = api.ga_prefill_keys(d, dev(x["k"], et), None, dev(x["k_norm_w"]), dev(x["positions"]))
     o2 = api.ga_prefill_attention(d, dev(x["q"], et), khat, dev(x["v"], et), dev(x["gate"], et), dev(x["q_norm_w"]),
-                                  dev(x["positions"]))
+                                  dev(x["positions"]), k_norm_w=dev(x["k_norm_w"]))
     torch.cuda.synchronize()
     assert torch.equal(o2, out)
