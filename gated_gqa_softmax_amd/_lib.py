@@ -31,6 +31,7 @@ GA_COMBINE_MUL, GA_COMBINE_ADD = 0, 1
 GA_SHARE_HEADS, GA_SHARE_TOKENS = 1, 2
 GA_KERNEL_AUTO, GA_KERNEL_WIDE, GA_KERNEL_MIRROR, GA_KERNEL_SIMPLE, GA_KERNEL_GENERIC = 0, 1, 2, 3, 4
 GA_BWD_AUTO, GA_BWD_PLAIN = 0, 1
+GA_NOALLOC_SCRATCH_BYTES = 48 * 1024 * 1024
 
 
 class AttnDesc(ctypes.Structure):
@@ -78,6 +79,7 @@ SIGNATURES = {
     "ga_decode_split_keys": (_I, []),
     "ga_decode_workspace_bytes": (_S, [_D, _I]),
     "ga_decode": (_I, [_D, _P, _P, _P, _P, _P, _P, _P, _P, _I, _P, _I, _P, _S, _P, _P]),
+    "ga_decode_noalloc": (_I, [_D, _P, _P, _P, _P, _P, _P, _P, _P, _I, _P, _I, _P, _P]),
     "ga_decode_partials": (_I, [_D, _P, _P, _P, _P, _I, _P, _I, _P, _S, _P]),
     "ga_decode_merge": (_I, [_D, _P, _P, _P, _P, _P, _P, _P, _P, _I, _P, _I, _P, _S, _P, _P]),
     "ga_status_string": (ctypes.c_char_p, [_I]),

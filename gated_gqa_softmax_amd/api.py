@@ -562,3 +562,21 @@ def ga_decode_merge(desc: AttnDesc, q, k_new, v_new, k_cache, v_cache, cache_len
                              op, _stream(stream))
     _check(st, "ga_decode_merge")
     return out
+
+
+def ga_decode_noalloc(desc: AttnDesc, q, k_new, v_new, k_cache, v_cache, cache_lens, max_cache_len: int, out,
+                      gate=None, q_norm_w=None, k_norm_w=None, stream=None) -> torch.Tensor:
+    """ga_decode without a workspace (partials in the library's static device
+    scratch; see include/ga.h): allocates nothing, so ``out`` is required."""
+    lib = _lib.load()
+    et = _elem_dtype(desc)
+    B, kcp, vcp, cap, lp = _decode_args(desc, q, k_cache, v_cache, cache_lens, max_cache_len, et)
+    G, hd = desc.n_kv_heads, desc.head_dim
+    d2, qp, gp = _qg(desc, q, gate, (B,), et)
+    op = _tensor(out, "out", (B, desc.n_q_heads * hd), et)
+    st = lib.ga_decode_noalloc(ctypes.byref(d2), qp, _tensor(k_new, "k_new", (B, G, hd), et),
+                               _tensor(v_new, "v_new", (B, G, hd), et), gp, _norm_w(q_norm_w, "q_norm_w", desc),
+                               _norm_w(k_norm_w, "k_norm_w", desc), kcp, vcp, cap, lp, int(max_cache_len), op,
+                               _stream(stream))
+    _check(st, "ga_decode_noalloc")
+    return out

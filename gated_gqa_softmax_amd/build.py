@@ -18,7 +18,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libga.so")
 SOURCES = ["ga_api.hip", "ga_prep.hip", "ga_prefill_mfma.hip", "ga_prefill_v2.hip", "ga_prefill_wide.hip",
-           "ga_naive.hip", "ga_decode.hip", "ga_backward.hip"]
+           "ga_naive.hip", "ga_decode.hip", "ga_backward.hip", "ga_noalloc.hip"]
 
 ARCH = "gfx950"
 FLAGS = [

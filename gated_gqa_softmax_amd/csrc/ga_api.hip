@@ -548,6 +548,14 @@ ga_status check_bwd_desc(const ga_attn_desc* d) {
 
 }  // namespace
 
+int ga::report(int st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
 extern "C" {
 
 size_t ga_prefill_backward_workspace_bytes(const ga_attn_desc* desc, int32_t seq_len) {

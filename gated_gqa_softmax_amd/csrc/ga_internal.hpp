@@ -184,6 +184,10 @@ hipError_t launch_bwd_dkv(const BwdParams& p, int D, hipStream_t s);
 hipError_t launch_bwd_norm_rope(const BwdNormParams& p, int nwg, hipStream_t s);
 hipError_t launch_bwd_reduce_rows(const float* part, float* out, int nrows, int d, hipStream_t s);
 
+// Records a message for ga_last_error() on the calling thread and returns st
+// (the status codes of include/ga.h).
+int report(int st, const char* fmt, ...);
+
 hipError_t launch_prep_keys(const PrepParams& p, int is_bf16, hipStream_t s);
 hipError_t launch_prefill_mfma(const PrefillParams& p, int D, int gate_mode, hipStream_t s);
 hipError_t launch_prefill_v2(const PrefillParams& p, int D, int gate_mode, hipStream_t s);

@@ -311,6 +311,27 @@ ga_status ga_decode(const ga_attn_desc* desc,
                     void* workspace, size_t workspace_bytes,
                     void* out, void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): ga_decode
+ * without a workspace. The split-K partial results go to a static device
+ * array of GA_NOALLOC_SCRATCH_BYTES that each GPU holds, at its own address,
+ * from the first call on that device (the calling thread's current device,
+ * which must be the stream's) until the process ends; the call allocates
+ * nothing. A step whose partials need more than that
+ * (ga_decode_workspace_bytes(desc, max_cache_len) > GA_NOALLOC_SCRATCH_BYTES;
+ * 48 MiB covers 64 sequences x 8 query heads x 32768 cached tokens at
+ * d = 256) returns GA_ERR_WORKSPACE before any launch. Every call on one GPU
+ * shares that GPU's array: calls that overlap on one GPU (different streams,
+ * or host threads) race and must be ordered by the caller. Arguments,
+ * results and the other errors are those of ga_decode. */
+#define GA_NOALLOC_SCRATCH_BYTES (48 * 1024 * 1024)
+ga_status ga_decode_noalloc(const ga_attn_desc* desc,
+                            const void* q, const void* k_new, const void* v_new, const void* gate,
+                            const float* q_norm_w, const float* k_norm_w,
+                            void* k_cache, void* v_cache, int32_t cache_cap,
+                            const int32_t* cache_lens, int32_t max_cache_len,
+                            void* out, void* stream);
+
 /* First stage of ga_decode (one kernel): for every sequence, KV head and key
  * chunk of the cache, the partial softmax state (row max, row sum, unnormed
  * weighted V) of the group's query heads, into the workspace. Reads only

@@ -311,3 +311,16 @@ def test_backward_rejects_bad_arguments():
     # empty inputs are a no-op, even without buffers
     assert call(n=0, q=None, ws=None, ws_bytes=0) == _lib.GA_OK
     assert call(desc=_desc(batch=0), q=None, ws=None, ws_bytes=0) == _lib.GA_OK
+
+
+def test_noalloc_decode_rejects_oversized_steps_before_any_launch():
+    """The static-scratch decode refuses a step whose partials exceed the
+    scratch, before touching a device (q is also NULL, so nothing further
+    could run even if the size check were passed)."""
+    lib = _lib_or_build()
+    d = _desc(batch=64)
+    big = 1 << 20
+    assert lib.ga_decode_workspace_bytes(ctypes.byref(d), big) > _lib.GA_NOALLOC_SCRATCH_BYTES
+    assert lib.ga_decode_noalloc(ctypes.byref(d), None, A16, A16, A16, None, None, A16, A16, big + 1, A16, big, A16,
+                                 None) == _lib.GA_ERR_WORKSPACE
+    assert b"static scratch" in lib.ga_last_error()
