@@ -164,3 +164,18 @@ def test_chunk_full_size_sampled_rows():
     got = np.stack([part[0, i - L, h * d:(h + 1) * d] for _, i, h in rows])
     assert np.all(np.isfinite(part))
     assert_close(got, want, w, "full-size chunk rows")
+
+
+def test_chunk_bench_workload_in_full():
+    """The mixed-length chunk workload the bench times (four 1024-token chunks
+    of the Qwen3.5-0.8B attention shape after 0, 1024, 2048 and 3072 cached
+    tokens, elementwise gate), in its launch configuration, compared with the
+    oracle on every row of every sequence (and the cache slots written)."""
+    wb = inputs.WORKLOADS["qwen35_0p8b_chunk"]
+    w = wb.with_(extra={"lens": list(wb.extra["cache_lens"]), "chunk_lens": None,
+                        "max_len": max(wb.extra["cache_lens"])})
+    print(f"[chunk] {wb.name} in full", flush=True)
+    d = desc_for(w)
+    assert api.ga_prefill_chunk_kernel(d, w.seq_len, max(w.extra["lens"]) + w.seq_len + 2) == "mirror"
+    got, want = _run(w)
+    assert np.all(np.isfinite(got))
