@@ -27,6 +27,37 @@
 
 namespace ga {
 
+// Work item t of the partials grid: the t-th (sequence, chunk) pair among the
+// chunks that hold keys, sequences in order, chunks in order within each.
+// Lengths outside [0, max_len] count as empty. Wave-uniform; false when t is
+// past the last chunk.
+template <int C>
+__device__ __forceinline__ bool locate_chunk(const int32_t* lens, int B, int max_len, int t, int lane, int& b,
+                                             int& split, int& L) {
+  int before = 0;  // chunks of the sequences before this 64-sequence window
+  for (int base = 0; base < B; base += 64) {
+    int len = base + lane < B ? lens[base + lane] : 0;
+    if (len < 0 || len > max_len) len = 0;
+    const int cnt = (len + C - 1) / C;
+    int incl = cnt;  // inclusive prefix sum over the window's lanes
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int y = __shfl_up(incl, off, 64);
+      if (lane >= off) incl += y;
+    }
+    const unsigned long long hit = __ballot(before + incl > t);
+    if (hit) {
+      const int j = __builtin_ctzll(hit);
+      b = base + j;
+      L = __shfl(len, j, 64);
+      split = t - (before + __shfl(incl, j, 64) - __shfl(cnt, j, 64));
+      return true;
+    }
+    before += __shfl(incl, 63, 64);
+  }
+  return false;
+}
+
 template <int D, int GRP>
 __global__ __launch_bounds__(256) void decode_partials_kernel(const DecodeParams p) {
   constexpr int C = kDecodeChunk;   // keys per workgroup
@@ -43,15 +74,13 @@ __global__ __launch_bounds__(256) void decode_partials_kernel(const DecodeParams
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   // consecutive workgroups take the KV heads of one chunk, so the heads'
-  // halves of each cache row are read at the same time
-  const int u = blockIdx.x;
-  const int g = u % p.G;
-  const int split = (u / p.G) % p.nsplit;
-  const int b = u / (p.G * p.nsplit);
-  int L = p.cache_lens[b];
-  if (L < 0 || L > p.max_len) L = 0;
+  // halves of each cache row are read at the same time; the chunks that hold
+  // keys come first, sequence by sequence, and the grid's surplus (sized for
+  // every sequence at max_len) exits at the end
+  const int g = blockIdx.x % p.G;
+  int b, split, L;
+  if (!locate_chunk<C>(p.cache_lens, p.B, p.max_len, (int)(blockIdx.x / p.G), lane, b, split, L)) return;
   const int start = split * C;
-  if (start >= L) return;  // whole workgroup: no keys in this chunk
 
   // q-hat of the group's heads at position L (bf16, the MFMA operand precision)
   for (int idx = tid; idx < 16 * LPR; idx += 256) {
