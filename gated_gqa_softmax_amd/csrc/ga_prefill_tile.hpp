@@ -240,43 +240,47 @@ __device__ __forceinline__ void attn_tile(const unsigned char* smem, WaveState<D
 // (log2 domain, softmax scale folded into q_hat) never exceed their bound c.
 // With CINIT the QK chain starts from ws.cinit = -c, so the scores come out
 // as s - c; otherwise (d = 256, where the 16 registers of ws.cinit do not fit
-// beside two waves per SIMD) c = -ws.cinit[0] is subtracted before the exp.
+// beside two waves per SIMD) ws.m_run = -c is added before the exp.
 // p = 2^(s - c) needs one exp each; the row sum adds the bf16-rounded
 // probabilities (the PV operands) two at a time with v_dot2c_f32_bf16.
-template <int D, int NS, int BUF, int HALF, bool CINIT = (D < 256)>
-__device__ __forceinline__ void attn_tile_b(const unsigned char* smem, WaveState<D>& ws, bool need_mask, int lim) {
+// The tile is two halves, tile_b_qk (the QK MFMAs) and tile_b_finish
+// (softmax and PV), so a wave may run them in different stages.
+template <int D, int NS, int BUF, int HALF>
+__device__ __forceinline__ bf16x8_t tile_kread(const unsigned char* smem, int kb, int kk) {
   typedef TileShape<D, NS> S;
-  constexpr int NK = D / 16;
-  constexpr int NV = D / 16;
-  constexpr int KPF = (D == 256) ? 3 : 4;
-  constexpr int VPF = (D == 256) ? 2 : 3;
-  int kb = ws.kbase, vb = ws.vbase;
-  asm volatile("" : "+v"(kb), "+v"(vb));
-  auto kread = [&](int kk) {
-    int a = kb ^ ((kk & 7) << 5);
-    asm volatile("" : "+v"(a));
-    return *(const bf16x8_t*)(smem + a + (BUF * S::TILE_BYTES + HALF * 32 * S::ROW_BYTES + ((kk >> 3) << 8)));
-  };
-  auto vread = [&](int t) {
-    const int ks = t / (D / 32), mb = t % (D / 32);
-    int a = vb ^ ((mb & 3) << 6);
-    asm volatile("" : "+v"(a));
-    const unsigned char* a1 =
-        smem + a + (BUF * S::TILE_BYTES + HALF * 32 * S::ROW_BYTES + ((mb & 4) << 6) + ks * 16 * S::ROW_BYTES);
-    const i16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)a1);
-    const i16x4_t v2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(a1 + 8 * S::ROW_BYTES));
-    const u32x4_t av = {__builtin_bit_cast(u32x2_t, v1)[0], __builtin_bit_cast(u32x2_t, v1)[1],
-                        __builtin_bit_cast(u32x2_t, v2)[0], __builtin_bit_cast(u32x2_t, v2)[1]};
-    return __builtin_bit_cast(bf16x8_t, av);
-  };
+  int a = kb ^ ((kk & 7) << 5);
+  asm volatile("" : "+v"(a));
+  return *(const bf16x8_t*)(smem + a + (BUF * S::TILE_BYTES + HALF * 32 * S::ROW_BYTES + ((kk >> 3) << 8)));
+}
 
+template <int D, int NS, int BUF, int HALF>
+__device__ __forceinline__ bf16x8_t tile_vread(const unsigned char* smem, int vb, int t) {
+  typedef TileShape<D, NS> S;
+  const int ks = t / (D / 32), mb = t % (D / 32);
+  int a = vb ^ ((mb & 3) << 6);
+  asm volatile("" : "+v"(a));
+  const unsigned char* a1 =
+      smem + a + (BUF * S::TILE_BYTES + HALF * 32 * S::ROW_BYTES + ((mb & 4) << 6) + ks * 16 * S::ROW_BYTES);
+  const i16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)a1);
+  const i16x4_t v2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(a1 + 8 * S::ROW_BYTES));
+  const u32x4_t av = {__builtin_bit_cast(u32x2_t, v1)[0], __builtin_bit_cast(u32x2_t, v1)[1],
+                      __builtin_bit_cast(u32x2_t, v2)[0], __builtin_bit_cast(u32x2_t, v2)[1]};
+  return __builtin_bit_cast(bf16x8_t, av);
+}
+
+template <int D, int NS, int BUF, int HALF, bool CINIT = (D < 256)>
+__device__ __forceinline__ f32x16_t tile_b_qk(const unsigned char* smem, const WaveState<D>& ws) {
+  constexpr int NK = D / 16;
+  constexpr int KPF = (D == 256) ? 3 : 4;
+  int kb = ws.kbase;
+  asm volatile("" : "+v"(kb));
   bf16x8_t ka[NK];
   f32x16_t s;
 #pragma unroll
-  for (int kk = 0; kk < KPF; ++kk) ka[kk] = kread(kk);
+  for (int kk = 0; kk < KPF; ++kk) ka[kk] = tile_kread<D, NS, BUF, HALF>(smem, kb, kk);
 #pragma unroll
   for (int kk = 0; kk < NK; ++kk) {
-    if (kk + KPF < NK) ka[kk + KPF] = kread(kk + KPF);
+    if (kk + KPF < NK) ka[kk + KPF] = tile_kread<D, NS, BUF, HALF>(smem, kb, kk + KPF);
     if (CINIT)
       s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[kk], ws.qf(kk), kk == 0 ? ws.cinit : s, 0, 0, 0);
     else
@@ -289,9 +293,19 @@ __device__ __forceinline__ void attn_tile_b(const unsigned char* smem, WaveState
     __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
   }
   __builtin_amdgcn_sched_group_barrier(0x008, KPF, 0);
+  return s;
+}
+
+template <int D, int NS, int BUF, int HALF, bool CINIT = (D < 256)>
+__device__ __forceinline__ void tile_b_finish(const unsigned char* smem, WaveState<D>& ws, f32x16_t s,
+                                              bool need_mask, int lim) {
+  constexpr int NV = D / 16;
+  constexpr int VPF = (D == 256) ? 2 : 3;
+  int vb = ws.vbase;
+  asm volatile("" : "+v"(vb));
   bf16x8_t va[NV];
 #pragma unroll
-  for (int t = 0; t < VPF; ++t) va[t] = vread(t);
+  for (int t = 0; t < VPF; ++t) va[t] = tile_vread<D, NS, BUF, HALF>(smem, vb, t);
   if (!CINIT) {
     const float nc = ws.m_run;  // -c
 #pragma unroll
@@ -328,7 +342,7 @@ __device__ __forceinline__ void attn_tile_b(const unsigned char* smem, WaveState
   }
 #pragma unroll
   for (int t = 0; t < NV; ++t) {
-    if (t + VPF < NV) va[t + VPF] = vread(t + VPF);
+    if (t + VPF < NV) va[t + VPF] = tile_vread<D, NS, BUF, HALF>(smem, vb, t + VPF);
     const int ks = t / (D / 32), mb = t % (D / 32);
     ws.o[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[t], pb[ks], ws.o[mb], 0, 0, 0);
   }
@@ -338,6 +352,11 @@ __device__ __forceinline__ void attn_tile_b(const unsigned char* smem, WaveState
     __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
   }
   __builtin_amdgcn_sched_group_barrier(0x008, VPF, 1);
+}
+
+template <int D, int NS, int BUF, int HALF, bool CINIT = (D < 256)>
+__device__ __forceinline__ void attn_tile_b(const unsigned char* smem, WaveState<D>& ws, bool need_mask, int lim) {
+  tile_b_finish<D, NS, BUF, HALF, CINIT>(smem, ws, tile_b_qk<D, NS, BUF, HALF, CINIT>(smem, ws), need_mask, lim);
 }
 
 // Largest |w[e]| over the d weights, the same value in every lane (0 for a
