@@ -464,8 +464,8 @@ def time_chunk(torch, api, inputs, accounting, steps, warmup):
                              workspace=ws, stream=stream)
 
     def attention():
-        api.ga_prefill_chunk_attention(d, q, kc, vc, dl, max_len, gate=gate, q_norm_w=wq, out=out, workspace=ws,
-                                       stream=stream)
+        api.ga_prefill_chunk_attention(d, q, kc, vc, dl, max_len, gate=gate, q_norm_w=wq, k_norm_w=wk, out=out,
+                                       workspace=ws, stream=stream)
 
     res = time_whole_and_kernel(torch, whole, attention, stream, steps, warmup)
     flops = accounting.chunk_prefill_flops(lens, w.n_q_heads, w.head_dim, w.seq_len)

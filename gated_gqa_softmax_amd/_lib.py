@@ -72,7 +72,7 @@ SIGNATURES = {
     "ga_prefill_chunk": (_I, [_D, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _P, _P, _I, _P, _S, _P, _P]),
     "ga_prefill_chunk_workspace_bytes": (_S, [_D, _I, _I, _I]),
     "ga_prefill_chunk_keys": (_I, [_D, _I, _P, _P, _P, _P, _P, _P, _I, _P, _P, _I, _P]),
-    "ga_prefill_chunk_attention": (_I, [_D, _I, _P, _P, _P, _I, _P, _P, _I, _P, _P, _P, _P, _S, _P, _P]),
+    "ga_prefill_chunk_attention": (_I, [_D, _I, _P, _P, _P, _I, _P, _P, _I, _P, _P, _P, _P, _P, _S, _P, _P]),
     "ga_prefill_chunk_kernel": (ctypes.c_char_p, [_D, _I, _I]),
     "ga_prefill_backward_workspace_bytes": (_S, [_D, _I]),
     "ga_prefill_backward": (_I, [_D, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _S, _P]),

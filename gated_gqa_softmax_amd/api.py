@@ -428,8 +428,8 @@ def ga_prefill_chunk_keys(desc: AttnDesc, k, v, k_cache, v_cache, cache_lens, ma
 
 
 def ga_prefill_chunk_attention(desc: AttnDesc, q, k_cache, v_cache, cache_lens, max_cache_len: int, gate=None,
-                               q_norm_w=None, positions=None, chunk_lens=None, out=None, workspace=None,
-                               stream=None) -> torch.Tensor:
+                               q_norm_w=None, k_norm_w=None, positions=None, chunk_lens=None, out=None,
+                               workspace=None, stream=None) -> torch.Tensor:
     lib = _lib.load()
     et = _elem_dtype(desc)
     B, n, kcp, vcp, cap, lp, clp, _ws, wp, wb = _chunk_args(desc, q, k_cache, v_cache, cache_lens, chunk_lens,
@@ -440,7 +440,7 @@ def ga_prefill_chunk_attention(desc: AttnDesc, q, k_cache, v_cache, cache_lens, 
         out = torch.zeros((B, n, desc.n_q_heads * hd), dtype=et, device=q.device)
     op = _tensor(out, "out", (B, n, desc.n_q_heads * hd), et)
     st = lib.ga_prefill_chunk_attention(ctypes.byref(d2), n, qp, kcp, vcp, cap, lp, clp, int(max_cache_len),
-                                        gp, _norm_w(q_norm_w, "q_norm_w", desc),
+                                        gp, _norm_w(q_norm_w, "q_norm_w", desc), _norm_w(k_norm_w, "k_norm_w", desc),
                                         _tensor(positions, "positions", (B, n), torch.int32, required=False),
                                         wp, wb, op, _stream(stream))
     _check(st, "ga_prefill_chunk_attention")

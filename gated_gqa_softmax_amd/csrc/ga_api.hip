@@ -371,8 +371,8 @@ ga_status check_chunk_common(const ga_attn_desc* desc, int32_t n, const void* k_
 
 ga_status chunk_attn_impl(const ga_attn_desc* desc, int32_t n, const void* q, const void* k_cache,
                           const void* v_cache, int32_t cap, const int32_t* cache_lens, const int32_t* chunk_lens,
-                          int32_t max_cache_len, const void* gate, const float* q_norm_w, const int32_t* positions,
-                          void* workspace, void* out, hipStream_t stream) {
+                          int32_t max_cache_len, const void* gate, const float* q_norm_w, const float* k_norm_w,
+                          const int32_t* positions, void* workspace, void* out, hipStream_t stream) {
   (void)workspace;
   const int H = desc->n_q_heads, G = desc->n_kv_heads, d = desc->head_dim;
   const int grp = H / G;
@@ -386,6 +386,7 @@ ga_status chunk_attn_impl(const ga_attn_desc* desc, int32_t n, const void* q, co
     pp.v = (const uint16_t*)v_cache;
     pp.gate = (const uint16_t*)gate;
     pp.wq = q_norm_w;
+    pp.wk = k_norm_w;
     pp.positions = positions;
     pp.out = (uint16_t*)out;
     pp.key_base = cache_lens;
@@ -848,8 +849,8 @@ ga_status ga_prefill_chunk_keys(const ga_attn_desc* desc, int32_t seq_len, const
 ga_status ga_prefill_chunk_attention(const ga_attn_desc* desc, int32_t seq_len, const void* q, const void* k_cache,
                                      const void* v_cache, int32_t cache_cap, const int32_t* cache_lens,
                                      const int32_t* chunk_lens, int32_t max_cache_len, const void* gate,
-                                     const float* q_norm_w, const int32_t* positions, void* workspace,
-                                     size_t workspace_bytes, void* out, void* stream) {
+                                     const float* q_norm_w, const float* k_norm_w, const int32_t* positions,
+                                     void* workspace, size_t workspace_bytes, void* out, void* stream) {
   ga_status st;
   if ((st = check_desc(desc)) != GA_OK) return st;
   if (seq_len < 0) return fail(GA_ERR_BAD_SHAPE, "seq_len %d < 0", seq_len);
@@ -858,6 +859,7 @@ ga_status ga_prefill_chunk_attention(const ga_attn_desc* desc, int32_t seq_len, 
   if ((st = check_tensor(out, "out", desc)) != GA_OK) return st;
   if ((st = check_gate(gate, desc)) != GA_OK) return st;
   if ((st = check_norm_w(q_norm_w, "q_norm_w")) != GA_OK) return st;
+  if ((st = check_norm_w(k_norm_w, "k_norm_w")) != GA_OK) return st;
   if ((st = check_chunk_common(desc, seq_len, k_cache, v_cache, cache_cap, cache_lens, max_cache_len)) != GA_OK)
     return st;
   if ((st = check_chunk_workspace(desc, seq_len, cache_cap, max_cache_len, workspace, workspace_bytes)) != GA_OK)
@@ -865,8 +867,8 @@ ga_status ga_prefill_chunk_attention(const ga_attn_desc* desc, int32_t seq_len, 
   if (chunk_choice(desc, seq_len, cache_cap) == PK_INVALID)
     return fail(GA_ERR_UNSUPPORTED, "the forced kernel %d does not serve this chunk shape", desc->kernel);
   return chunk_attn_impl(desc, seq_len, q, k_cache, v_cache, cache_cap, cache_lens, chunk_lens, max_cache_len,
-                         desc->gate_mode == GA_GATE_NONE ? nullptr : gate, q_norm_w, positions, workspace, out,
-                         (hipStream_t)stream);
+                         desc->gate_mode == GA_GATE_NONE ? nullptr : gate, q_norm_w, k_norm_w, positions, workspace,
+                         out, (hipStream_t)stream);
 }
 
 ga_status ga_prefill_chunk(const ga_attn_desc* desc, int32_t seq_len, const void* q, const void* k, const void* v,
@@ -896,7 +898,8 @@ ga_status ga_prefill_chunk(const ga_attn_desc* desc, int32_t seq_len, const void
                               chunk_lens, max_cache_len)) != GA_OK)
     return st;
   return chunk_attn_impl(desc, seq_len, q, k_cache, v_cache, cache_cap, cache_lens, chunk_lens, max_cache_len,
-                         desc->gate_mode == GA_GATE_NONE ? nullptr : gate, q_norm_w, positions, workspace, out, s);
+                         desc->gate_mode == GA_GATE_NONE ? nullptr : gate, q_norm_w, k_norm_w, positions, workspace,
+                         out, s);
 }
 
 int32_t ga_decode_split_keys(void) { return kDecodeChunk; }
@@ -1040,6 +1043,6 @@ int32_t ga_fast_path(int32_t dtype, int32_t head_dim, int32_t rot_dim, int32_t g
   return (prefill_fast(&d) ? 1 : 0) | (decode_fast(&d, 0) ? 2 : 0);
 }
 
-int32_t ga_version(void) { return 4; }
+int32_t ga_version(void) { return 5; }
 
 }  // extern "C"

@@ -267,13 +267,15 @@ ga_status ga_prefill_chunk_keys(const ga_attn_desc* desc, int32_t seq_len,
 
 /* Second stage of ga_prefill_chunk (one kernel): the chunk's queries against
  * cache slots [0, L_b + i], gated, into out. Expects the chunk's own K-hat
- * and v already in the cache (ga_prefill_chunk_keys). */
+ * and v already in the cache (ga_prefill_chunk_keys). k_norm_w is the weight
+ * the cached K-hat was normed with (or NULL): it is not applied again, it
+ * bounds the scores for the bounded softmax, as in ga_prefill_attention. */
 ga_status ga_prefill_chunk_attention(const ga_attn_desc* desc, int32_t seq_len, const void* q,
                                      const void* k_cache, const void* v_cache, int32_t cache_cap,
                                      const int32_t* cache_lens, const int32_t* chunk_lens,
                                      int32_t max_cache_len, const void* gate, const float* q_norm_w,
-                                     const int32_t* positions, void* workspace, size_t workspace_bytes,
-                                     void* out, void* stream);
+                                     const float* k_norm_w, const int32_t* positions, void* workspace,
+                                     size_t workspace_bytes, void* out, void* stream);
 
 /* Name of the kernel ga_prefill_chunk_attention runs for this shape:
  * "mirror" (the mirrored prefill kernel with per-sequence key offsets) or
@@ -395,8 +397,8 @@ const char* ga_last_error(void);
  * fp32 or bf16); ga_decode_partials/ga_decode_merge need bit 1. The bits
  * are for dense q and gate (see ga_attn_desc for wider head strides). */
 int32_t ga_fast_path(int32_t dtype, int32_t head_dim, int32_t rot_dim, int32_t group);
-/* ABI version: 4 (ga_attn_desc with head strides, gate variants, the output
- * norm and the kernel-choice fields). */
+/* ABI version: 5 (ga_attn_desc with head strides, gate variants, the output
+ * norm and the kernel-choice fields; k_norm_w in ga_prefill_chunk_attention). */
 int32_t ga_version(void);
 
 #ifdef __cplusplus

@@ -36,7 +36,7 @@ def test_library_exports_every_declared_entry_point():
     assert declared == set(_lib.SIGNATURES), declared ^ set(_lib.SIGNATURES)
     for name in declared:
         assert getattr(lib, name) is not None
-    assert lib.ga_version() == 4
+    assert lib.ga_version() == 5
     assert ctypes.sizeof(AttnDesc) == 80
 
 
@@ -250,7 +250,7 @@ def test_prefill_chunk_rejects_bad_arguments_and_names_its_kernel():
     assert lib.ga_prefill_chunk_keys(ctypes.byref(d), 64, A16, A16, None, None, None, None, 1000, A16, A16, 1100,
                                      None) == _lib.GA_ERR_NULL_ARG
     assert lib.ga_prefill_chunk_attention(ctypes.byref(d), 64, A16, A16, A16, 1000, A16, None, 1000, A16, None,
-                                          None, A16, 1 << 30, A16, None) == _lib.GA_ERR_BAD_SHAPE
+                                          None, None, A16, 1 << 30, A16, None) == _lib.GA_ERR_BAD_SHAPE
     assert lib.ga_prefill_chunk_kernel(ctypes.byref(d), 64, 1100) == b"mirror"
     assert lib.ga_prefill_chunk_kernel(ctypes.byref(_desc(dtype=_lib.GA_F32)), 64, 1100) == b"generic"
     assert lib.ga_prefill_chunk_kernel(ctypes.byref(_desc(head_dim=64, rot_dim=16)), 64, 1100) == b"generic"

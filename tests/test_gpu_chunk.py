@@ -23,7 +23,7 @@ def _case(name, B, n, H, G, d, rot, gate, lens, chunk_lens=None, max_len=None, d
                                   "max_len": max(lens) if max_len is None else max_len})
 
 
-def _run(w, stages=False, kernel="auto"):
+def _run(w, stages=False, kernel="auto", bound=True):
     et = tdt(w)
     x = inputs.make_prefill(w)
     B, n, G, d = w.batch, w.seq_len, w.n_kv_heads, w.head_dim
@@ -52,8 +52,9 @@ def _run(w, stages=False, kernel="auto"):
     lens_d, cl_d = dev(L), (dev(cl) if cl is not None else None)
     if stages:
         api.ga_prefill_chunk_keys(d_, k, v, kc, vc, lens_d, max_len, k_norm_w=wk, chunk_lens=cl_d)
-        api.ga_prefill_chunk_attention(d_, q, kc, vc, lens_d, max_len, gate=gate, q_norm_w=wq, chunk_lens=cl_d,
-                                       out=out)
+        # without k_norm_w the kernel has no score bound and keeps a running max
+        api.ga_prefill_chunk_attention(d_, q, kc, vc, lens_d, max_len, gate=gate, q_norm_w=wq,
+                                       k_norm_w=wk if bound else None, chunk_lens=cl_d, out=out)
     else:
         api.ga_prefill_chunk(d_, q, k, v, kc, vc, lens_d, max_len, gate=gate, q_norm_w=wq, k_norm_w=wk,
                              chunk_lens=cl_d, out=out)
@@ -102,6 +103,14 @@ def test_chunk_small(w):
     cap = max(w.extra["max_len"], max(w.extra["lens"])) + w.seq_len + 2
     assert api.ga_prefill_chunk_kernel(desc_for(w), w.seq_len, cap) == want_kernel
     _run(w, stages=w.name.endswith("stages"))
+
+
+def test_chunk_running_max_form():
+    """The attention stage without k_norm_w: the mirrored kernel's running-max
+    softmax instead of the bounded one, same results."""
+    w = CASES[0]
+    print(f"[chunk] {w.name} without the score bound", flush=True)
+    _run(w, stages=True, bound=False)
 
 
 def test_chunk_forced_generic_kernel():
