@@ -188,3 +188,43 @@ def test_chunk_bench_workload_in_full():
     assert api.ga_prefill_chunk_kernel(d, w.seq_len, max(w.extra["lens"]) + w.seq_len + 2) == "mirror"
     got, want = _run(w)
     assert np.all(np.isfinite(got))
+
+
+# Cached prefixes of very different lengths in one call (one sequence with a
+# prefix 25x the chunk), ragged chunk lengths, three gate forms.
+SKEW_CASES = [
+    _case("skew_d256_elementwise", 3, 256, 8, 2, 256, 64, "elementwise", [0, 6000, 100], [256, 200, 17], seed=320),
+    _case("skew_d128_headwise", 4, 128, 16, 8, 128, 32, "headwise", [4000, 0, 2500, 64], seed=321),
+    _case("skew_d256_nogate", 2, 64, 8, 2, 256, 32, "none", [3000, 1], seed=322),
+]
+
+
+@pytest.mark.parametrize("w", SKEW_CASES, ids=lambda w: w.name)
+def test_chunk_skewed_prefixes(w):
+    print(f"[chunk] {w.name}", flush=True)
+    _run(w)
+
+
+def test_chunk_repeat_bits():
+    """Repeated chunk attention calls over the same cache give the same bits."""
+    w = SKEW_CASES[0]
+    print(f"[chunk] {w.name}: repeats", flush=True)
+    et = tdt(w)
+    x = inputs.make_prefill(w)
+    B, n, G, d = w.batch, w.seq_len, w.n_kv_heads, w.head_dim
+    L = np.array(w.extra["lens"], np.int32)
+    cl = np.array(w.extra["chunk_lens"], np.int32)
+    max_len = int(L.max())
+    cap = max_len + n + 2
+    gen = torch.Generator(device="cuda").manual_seed(323)
+    kc = torch.randn((B, cap, G, d), generator=gen, device="cuda").to(et)
+    vc = torch.randn((B, cap, G, d), generator=gen, device="cuda").to(et)
+    dsc = desc_for(w)
+    args = (dsc, dev(x["q"], et), kc, vc, dev(L), max_len)
+    kw = dict(gate=dev(x["gate"], et), q_norm_w=dev(x["q_norm_w"]), k_norm_w=dev(x["k_norm_w"]),
+              chunk_lens=dev(cl))
+    first = api.ga_prefill_chunk_attention(*args, **kw).clone()
+    for _ in range(3):
+        again = api.ga_prefill_chunk_attention(*args, **kw)
+        torch.cuda.synchronize()
+        assert torch.equal(again, first)
