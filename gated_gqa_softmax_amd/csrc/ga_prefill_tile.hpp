@@ -354,6 +354,69 @@ __device__ __forceinline__ void tile_b_finish(const unsigned char* smem, WaveSta
   __builtin_amdgcn_sched_group_barrier(0x008, VPF, 1);
 }
 
+// Software-pipelined bounded tiles: the QK MFMAs of the next tile (buffer
+// BN, half HN) with the softmax of this tile's scores s between them (the
+// exponentials do not wait for the matrix pipe), then this tile's PV (buffer
+// B, half H). Returns the next tile's scores. The instruction order is left
+// to the compiler.
+template <int D, int NS, int B, int H, int BN, int HN, bool CINIT = (D < 256)>
+__device__ __forceinline__ f32x16_t tile_b_pipe(const unsigned char* smem, WaveState<D>& ws, f32x16_t s,
+                                                bool need_mask, int lim) {
+  constexpr int NK = D / 16;
+  constexpr int NV = D / 16;
+  constexpr int KPF = (D == 256) ? 3 : 2;
+  constexpr int VPF = (D == 256) ? 2 : 3;
+  constexpr int PPM = (8 + NK - 1) / NK;  // probability pairs per QK MFMA
+  if (!CINIT) {
+    const float nc = ws.m_run;  // -c
+#pragma unroll
+    for (int i = 0; i < 16; ++i) s[i] += nc;
+  }
+  if (need_mask) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) s[i] = ((i >> 2) * 8 + (i & 3) <= lim) ? s[i] : -INFINITY;
+  }
+  int kb = ws.kbase;
+  asm volatile("" : "+v"(kb));
+  bf16x8_t ka[NK];
+  f32x16_t sn;
+  u32x4_t pk[2];
+  float l = ws.l_run;
+  const bf16x2_t one2 = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+  for (int kk = 0; kk < KPF; ++kk) ka[kk] = tile_kread<D, NS, BN, HN>(smem, kb, kk);
+#pragma unroll
+  for (int kk = 0; kk < NK; ++kk) {
+    if (kk + KPF < NK) ka[kk + KPF] = tile_kread<D, NS, BN, HN>(smem, kb, kk + KPF);
+    if (CINIT)
+      sn = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[kk], ws.qf(kk), kk == 0 ? ws.cinit : sn, 0, 0, 0);
+    else
+      sn = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[kk], ws.qf(kk), kk == 0 ? f32x16_t{} : sn, 0, 0, 0);
+#pragma unroll
+    for (int j = 0; j < PPM; ++j) {
+      const int k = kk * PPM + j;
+      if (k < 8) {
+        const uint32_t w = pack_bf16x2(__builtin_amdgcn_exp2f(s[2 * k]), __builtin_amdgcn_exp2f(s[2 * k + 1]));
+        pk[k >> 2][k & 3] = w;
+        l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w), one2, l, false);
+      }
+    }
+  }
+  ws.l_run = l;
+  int vb = ws.vbase;
+  asm volatile("" : "+v"(vb));
+  bf16x8_t va[NV];
+#pragma unroll
+  for (int t = 0; t < VPF; ++t) va[t] = tile_vread<D, NS, B, H>(smem, vb, t);
+#pragma unroll
+  for (int t = 0; t < NV; ++t) {
+    if (t + VPF < NV) va[t + VPF] = tile_vread<D, NS, B, H>(smem, vb, t + VPF);
+    const int ks = t / (D / 32), mb = t % (D / 32);
+    ws.o[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[t], __builtin_bit_cast(bf16x8_t, pk[ks]), ws.o[mb], 0, 0, 0);
+  }
+  return sn;
+}
+
 template <int D, int NS, int BUF, int HALF, bool CINIT = (D < 256)>
 __device__ __forceinline__ void attn_tile_b(const unsigned char* smem, WaveState<D>& ws, bool need_mask, int lim) {
   tile_b_finish<D, NS, BUF, HALF, CINIT>(smem, ws, tile_b_qk<D, NS, BUF, HALF, CINIT>(smem, ws), need_mask, lim);

@@ -92,6 +92,66 @@ __device__ __forceinline__ void wide_loop(unsigned char* smem, WaveState<D>& ws,
   }
 }
 
+// Pipelined bounded loop: every tile's softmax and PV run under the QK MFMAs
+// of the wave's next tile, also across stages (the second tile of stage st
+// finishes under the first QK of stage st + 1). The previous stage's V must
+// then survive one more stage: loads run two stages ahead (not three) in the
+// four-stage ring. The step has no branches around tiles (tiles past a
+// wave's rows are fully masked instead), so the accumulators stay in place;
+// before stage 0 the pending tile is an all-masked one over a zeroed V buffer.
+template <int D, int BUF>
+__device__ __forceinline__ void wide_step_p(unsigned char* smem, WaveState<D>& ws, f32x16_t& cs, bool& cmask,
+                                            int& clim, i32x4_t krs, i32x4_t vrs, int koff, int voff, int w, int st,
+                                            int nst, int kv_row_bytes, int wave_min_tok, int my_lim_tok, int n,
+                                            int hi) {
+  typedef WideShape<D> S;
+  constexpr int NS = S::NSTAGE;
+  constexpr int PB = (BUF + NS - 1) % NS;  // the previous stage's buffer
+  wait_stage<2 * S::LOADS_PER_WAVE>(min(1, nst - 1 - st));
+  lds_barrier();
+  if (st + 2 < nst) stage_issue<D, NS, (BUF + 2) % NS>(smem, krs, vrs, koff, voff, w, st + 2, kv_row_bytes);
+  const int k0 = st * S::ST;
+  const bool m0 = (k0 + 31 > wave_min_tok) || (k0 + 32 > n), m1 = (k0 + 63 > wave_min_tok) || (k0 + 64 > n);
+  const int l0 = my_lim_tok - (k0 + hi * 4), l1 = my_lim_tok - (k0 + 32 + hi * 4);
+  const f32x16_t s0 = tile_b_pipe<D, NS, PB, 1, BUF, 0>(smem, ws, cs, cmask, clim);
+  cs = tile_b_pipe<D, NS, BUF, 0, BUF, 1>(smem, ws, s0, m0, l0);
+  cmask = m1;
+  clim = l1;
+}
+
+template <int D>
+__device__ __forceinline__ void wide_loop_p(unsigned char* smem, WaveState<D>& ws, i32x4_t krs, i32x4_t vrs, int koff,
+                                            int voff, int w, int nst, int kv_row_bytes, int wave_min_tok,
+                                            int my_lim_tok, int n, int hi) {
+  f32x16_t cs;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) cs[i] = -INFINITY;
+  bool cmask = false;
+  int clim = 0;
+  for (int st0 = 0; st0 < nst; st0 += kWideStages) {
+    wide_step_p<D, 0>(smem, ws, cs, cmask, clim, krs, vrs, koff, voff, w, st0, nst, kv_row_bytes, wave_min_tok,
+                      my_lim_tok, n, hi);
+    if (st0 + 1 < nst)
+      wide_step_p<D, 1>(smem, ws, cs, cmask, clim, krs, vrs, koff, voff, w, st0 + 1, nst, kv_row_bytes,
+                        wave_min_tok, my_lim_tok, n, hi);
+    if (st0 + 2 < nst)
+      wide_step_p<D, 2>(smem, ws, cs, cmask, clim, krs, vrs, koff, voff, w, st0 + 2, nst, kv_row_bytes,
+                        wave_min_tok, my_lim_tok, n, hi);
+    if (st0 + 3 < nst)
+      wide_step_p<D, 3>(smem, ws, cs, cmask, clim, krs, vrs, koff, voff, w, st0 + 3, nst, kv_row_bytes,
+                        wave_min_tok, my_lim_tok, n, hi);
+  }
+  // the last pending tile (its stage's buffer is never reloaded)
+  typedef WideShape<D> S;
+  constexpr int NS = S::NSTAGE;
+  switch ((nst - 1) % NS) {
+    case 0: tile_b_finish<D, NS, 0, 1>(smem, ws, cs, cmask, clim); break;
+    case 1: tile_b_finish<D, NS, 1, 1>(smem, ws, cs, cmask, clim); break;
+    case 2: tile_b_finish<D, NS, 2, 1>(smem, ws, cs, cmask, clim); break;
+    default: tile_b_finish<D, NS, 3, 1>(smem, ws, cs, cmask, clim); break;
+  }
+}
+
 template <int D, int GATE>
 __global__ __launch_bounds__(512) void prefill_wide_kernel(const PrefillParams p) {
   typedef WideShape<D> S;
@@ -147,7 +207,6 @@ __global__ __launch_bounds__(512) void prefill_wide_kernel(const PrefillParams p
   }
   if (nst > 0) stage_issue<D, S::NSTAGE, 0>(smem, krs, vrs, koff, voff, w, 0, kv_row_bytes);
   if (nst > 1) stage_issue<D, S::NSTAGE, 1>(smem, krs, vrs, koff, voff, w, 1, kv_row_bytes);
-  if (nst > 2) stage_issue<D, S::NSTAGE, 2>(smem, krs, vrs, koff, voff, w, 2, kv_row_bytes);
 
   // ---- score bound: with both norm weights, |s| * log2(e) <= scale * d *
   // max|w_q| * max|w_k| (RMS-normed rows have norm sqrt(d) before their
@@ -157,6 +216,14 @@ __global__ __launch_bounds__(512) void prefill_wide_kernel(const PrefillParams p
   const float sl2 = p.scale_log2;
   const float kb_norm = max_abs_weight<D>(p.wk) * sqrtf((float)D) * 1.02f;  // bound on |k_hat|
   const bool bounded = p.wq && p.wk && sl2 * sqrtf((float)D) * max_abs_weight<D>(p.wq) * kb_norm <= kMaxScoreBound;
+  // the running-max loop keeps three stages in flight, the pipelined one two;
+  // the pipelined one starts from an all-masked tile over V buffer NSTAGE - 1,
+  // zeroed here (it is first loaded in step 1, after step 0's barrier)
+  if (!bounded && nst > 2) stage_issue<D, S::NSTAGE, 2>(smem, krs, vrs, koff, voff, w, 2, kv_row_bytes);
+  if (bounded) {
+    u32x4_t* zv = (u32x4_t*)(smem + S::VBASE + (S::NSTAGE - 1) * S::TILE_BYTES);
+    for (int i = threadIdx.x; i < S::TILE_BYTES / 16; i += 512) zv[i] = u32x4_t{0, 0, 0, 0};
+  }
 
   // ---- q_hat of this lane's row, straight into the MFMA operand layout -------
   // Lane (l32, hi) holds elements 16kk + 8hi + [0, 8) of row l32 for every kk.
@@ -257,8 +324,7 @@ __global__ __launch_bounds__(512) void prefill_wide_kernel(const PrefillParams p
 
   // ---- main loop ---------------------------------------------------------------
   if (bounded)
-    wide_loop<D, true>(smem, ws, krs, vrs, koff, voff, w, nst, kv_row_bytes, wave_min_tok, wave_max_tok, my_lim_tok,
-                       n, sl2, hi);
+    wide_loop_p<D>(smem, ws, krs, vrs, koff, voff, w, nst, kv_row_bytes, wave_min_tok, my_lim_tok, n, hi);
   else
     wide_loop<D, false>(smem, ws, krs, vrs, koff, voff, w, nst, kv_row_bytes, wave_min_tok, wave_max_tok,
                         my_lim_tok, n, sl2, hi);
