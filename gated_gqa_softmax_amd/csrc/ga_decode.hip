@@ -250,15 +250,19 @@ __global__ __launch_bounds__(256) void decode_partials_kernel(const DecodeParams
 
 // One workgroup per (sequence, query head): the new token's own key and value,
 // the chunk partials, the gate; the group's first head also appends the new
-// K-hat and V to the cache.
+// K-hat and V to the cache. The merge is a handful of small dependent steps,
+// so every global load it needs (q and k_new rows, the chunks' (m, l) and
+// output rows, v_new, the gate) is issued before the first of them.
 template <int D, int GATE>
 __global__ __launch_bounds__(256) void decode_merge_kernel(const DecodeParams p) {
-  constexpr int LPR = D / 8;
-  constexpr int SPASS = 256;
-  __shared__ float qk[2][D];  // row 0: q-hat (bf16-rounded); row 1: new k-hat (bf16-rounded)
+  constexpr int LPR = D / 8;      // lanes per q / k row, 8 elements each
+  constexpr int PPR = D / 4;      // 16-byte pieces per chunk output row
+  constexpr int CPP = 256 / PPR;  // chunks per pass of the workgroup
+  constexpr int PF = 16;          // passes held in registers; later chunks are read in a loop
+  __shared__ float qk[2][D];      // row 0: q-hat (bf16-rounded); row 1: new k-hat (bf16-rounded)
   __shared__ float red[8];
-  __shared__ float wts[SPASS];
-  __shared__ __attribute__((aligned(16))) float ored[4][D];  // per-wave weighted sums
+  __shared__ float wts[256];
+  __shared__ __attribute__((aligned(16))) float ored[CPP][D];  // per chunk lane: weighted sums
   __shared__ float sh_snew, sh_M, sh_L;
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -272,10 +276,41 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(const DecodeParams p)
     for (int e = tid; e < D; e += 256) out[e] = 0x7fc0;  // NaN
     return;
   }
-  if (tid < 2 * LPR) {  // two rows, LPR lanes each (whole lane groups of one wave)
+  const int ns = (L + kDecodeChunk - 1) / kDecodeChunk;
+  const long base = ((long)b * p.H + h) * p.nsplit;
+  const float* ws_o = p.ws + base * D;
+  const float* ws_ml = p.ws + (long)p.B * p.H * p.nsplit * D + base * 2;
+
+  // ---- every load first
+  u32x4_t raw = {0, 0, 0, 0};
+  if (tid < 2 * LPR) {  // two rows, LPR lanes each (whole lane groups of wave 0)
     const int r = tid / LPR, c = tid % LPR;
-    const u32x4_t raw = (r == 0) ? *(const u32x4_t*)(p.q + ((long)b * p.H + h) * p.qs + c * 8)
-                                 : *(const u32x4_t*)(p.k_new + ((long)b * p.G + g) * D + c * 8);
+    raw = (r == 0) ? *(const u32x4_t*)(p.q + ((long)b * p.H + h) * p.qs + c * 8)
+                   : *(const u32x4_t*)(p.k_new + ((long)b * p.G + g) * D + c * 8);
+  }
+  float m_t = -INFINITY, l_t = 0.f;  // chunk tid's statistics (chunks >= 256 in the loop below)
+  if (tid < ns) {
+    m_t = ws_ml[tid * 2];
+    l_t = ws_ml[tid * 2 + 1];
+  }
+  const int sub = tid / PPR, e4 = tid % PPR;  // chunk lane, 16-byte piece
+  f32x4_t ov[PF];
+#pragma unroll
+  for (int k = 0; k < PF; ++k) {
+    const int sc = sub + CPP * k;
+    ov[k] = sc < ns ? *(const f32x4_t*)(ws_o + (long)sc * D + e4 * 4) : f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+  float vnew = 0.f;
+  uint16_t graw = 0;
+  if (tid < D) {
+    vnew = bf16_bits_to_f32(p.v_new[((long)b * p.G + g) * D + tid]);
+    if (GATE == 2) graw = p.gate[((long)b * p.H + h) * p.gs + tid];
+    if (GATE == 1) graw = p.gate[((long)b * p.H + h) * p.gs];
+  }
+
+  // ---- q-hat, new k-hat (appended by the group's first head), own score
+  if (tid < 2 * LPR) {
+    const int r = tid / LPR, c = tid % LPR;
     float x[8];
     unpack8(raw, x);
     const float* nw = (r == 0) ? p.wq : p.wk;
@@ -293,88 +328,79 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(const DecodeParams p)
   }
   __syncthreads();
   if (w == 0) {
-    float s = 0.f;
-    for (int e = lane; e < D; e += 64) s += qk[0][e] * qk[1][e];
-    s = sum_xor<64>(s);
-    if (lane == 0) sh_snew = s * p.scale_log2;
+    float sd = 0.f;
+    for (int e = lane; e < D; e += 64) sd += qk[0][e] * qk[1][e];
+    sd = sum_xor<64>(sd);
+    if (lane == 0) sh_snew = sd * p.scale_log2;
   }
   __syncthreads();
   const float snew = sh_snew;
-  const int ns = (L + kDecodeChunk - 1) / kDecodeChunk;
-  const long base = ((long)b * p.H + h) * p.nsplit;
-  const float* ws_o = p.ws + base * D;
-  const float* ws_ml = p.ws + (long)p.B * p.H * p.nsplit * D + base * 2;
-  // global max, then the row sum
-  float mx = snew;
-  for (int s = tid; s < ns; s += 256) mx = fmaxf(mx, ws_ml[s * 2]);
+
+  // ---- global max over the chunks and the own score
+  float mx = fmaxf(snew, m_t);
+  for (int sc = tid + 256; sc < ns; sc += 256) mx = fmaxf(mx, ws_ml[sc * 2]);
   mx = max_xor<64>(mx);
   if (lane == 0) red[w] = mx;
   __syncthreads();
   if (tid == 0) sh_M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
   __syncthreads();
   const float M = sh_M;
+
+  // ---- row sum, then the weighted sum of the chunk outputs, 256 chunks at a time
   float sm = 0.f;
-  for (int s = tid; s < ns; s += 256) sm += ws_ml[s * 2 + 1] * __builtin_amdgcn_exp2f(ws_ml[s * 2] - M);
-  sm = sum_xor<64>(sm);
-  if (lane == 0) red[4 + w] = sm;
-  __syncthreads();
-  if (tid == 0) sh_L = red[4] + red[5] + red[6] + red[7] + __builtin_amdgcn_exp2f(snew - M);
-  // weighted sum of the chunk outputs, SPASS chunks at a time: wave w takes
-  // chunks w*CPW + sub (+ 4*CPW per step), lane (sub, e4) the 16-byte piece e4
-  // of that chunk's row, four steps in flight; waves meet in LDS at the end
-  constexpr int LPC = D / 4;    // lanes per chunk row (4 floats each)
-  constexpr int CPW = 64 / LPC;  // chunks per wave instruction
-  const int sub = lane / LPC, e4 = lane % LPC;
-  f32x4_t acc[4] = {};
-  for (int s0 = 0; s0 < ns; s0 += SPASS) {
+  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+  for (int s0 = 0; s0 < ns; s0 += 256) {
+    if (s0 > 0) __syncthreads();  // the previous pass's weights are read
+    const int sc = s0 + tid;
+    if (sc < ns) {
+      const float ms = s0 == 0 ? m_t : ws_ml[sc * 2];
+      const float ls = s0 == 0 ? l_t : ws_ml[sc * 2 + 1];
+      const float wt = __builtin_amdgcn_exp2f(ms - M);
+      wts[tid] = wt;
+      sm += ls * wt;
+    }
     __syncthreads();
-    if (s0 + tid < ns) wts[tid] = __builtin_amdgcn_exp2f(ws_ml[(s0 + tid) * 2] - M);
-    __syncthreads();
-    const int sn = min(SPASS, ns - s0);
-    const float* src = ws_o + (long)s0 * D + e4 * 4;
-    int s = w * CPW + sub;
-    for (; s + 12 * CPW < sn; s += 16 * CPW) {
+    const int sn = min(256, ns - s0);
+    if (s0 == 0) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const f32x4_t a = *(const f32x4_t*)(src + (long)(s + 4 * CPW * j) * D);
-        const float wt = wts[s + 4 * CPW * j];
+      for (int k = 0; k < PF; ++k) {
+        const int c = sub + CPP * k;
+        if (c < sn) {
+          const float wt = wts[c];
 #pragma unroll
-        for (int c = 0; c < 4; ++c) acc[j][c] += a[c] * wt;
+          for (int q = 0; q < 4; ++q) acc[q] += ov[k][q] * wt;
+        }
       }
     }
-    for (; s < sn; s += 4 * CPW) {
-      const f32x4_t a = *(const f32x4_t*)(src + (long)s * D);
-      const float wt = wts[s];
+    for (int c = sub + CPP * (s0 == 0 ? PF : 0); c < sn; c += CPP) {
+      const f32x4_t a = *(const f32x4_t*)(ws_o + (long)(s0 + c) * D + e4 * 4);
+      const float wt = wts[c];
 #pragma unroll
-      for (int c = 0; c < 4; ++c) acc[0][c] += a[c] * wt;
+      for (int q = 0; q < 4; ++q) acc[q] += a[q] * wt;
     }
   }
-  f32x4_t o4;
-#pragma unroll
-  for (int c = 0; c < 4; ++c) o4[c] = (acc[0][c] + acc[1][c]) + (acc[2][c] + acc[3][c]);
-#pragma unroll
-  for (int m = LPC; m < 64; m <<= 1)
-#pragma unroll
-    for (int c = 0; c < 4; ++c) o4[c] += __shfl_xor(o4[c], m, 64);
-  if (sub == 0) *(f32x4_t*)&ored[w][e4 * 4] = o4;
+  sm = sum_xor<64>(sm);
+  if (lane == 0) red[4 + w] = sm;
+  *(f32x4_t*)&ored[sub][e4 * 4] = acc;
   __syncthreads();
-  if (GATE != kGateExt && tid < D) {
-    const int e = tid;
-    const float o = (ored[0][e] + ored[1][e]) + (ored[2][e] + ored[3][e]);
-    const float vnew = bf16_bits_to_f32(p.v_new[((long)b * p.G + g) * D + e]);
-    float y = (o + vnew * __builtin_amdgcn_exp2f(snew - M)) / sh_L;
-    if (GATE == 2) y *= sigmoid_f32(bf16_bits_to_f32(p.gate[((long)b * p.H + h) * p.gs + e]));
-    if (GATE == 1) y *= sigmoid_f32(bf16_bits_to_f32(p.gate[((long)b * p.H + h) * p.gs]));
-    out[e] = f32_to_bf16_bits(y);
+  if (tid == 0) sh_L = (red[4] + red[5]) + (red[6] + red[7]) + __builtin_amdgcn_exp2f(snew - M);
+  __syncthreads();
+
+  // ---- output
+  const int e = tid;
+  float y = 0.f;
+  if (e < D) {
+    float o = 0.f;
+#pragma unroll
+    for (int c = 0; c < CPP; ++c) o += ored[c][e];
+    y = (o + vnew * __builtin_amdgcn_exp2f(snew - M)) / sh_L;
   }
-  if (GATE == kGateExt) {
-    const int e = tid;
-    float y = 0.f;
+  if (GATE != kGateExt) {
     if (e < D) {
-      const float o = (ored[0][e] + ored[1][e]) + (ored[2][e] + ored[3][e]);
-      const float vnew = bf16_bits_to_f32(p.v_new[((long)b * p.G + g) * D + e]);
-      y = (o + vnew * __builtin_amdgcn_exp2f(snew - M)) / sh_L;
+      if (GATE == 2 || GATE == 1) y *= sigmoid_f32(bf16_bits_to_f32(graw));
+      out[e] = f32_to_bf16_bits(y);
     }
+  } else {
     if (p.ge.onorm_w) {  // per-head RMSNorm of the row over the D threads
       const float ss = sum_xor<64>(y * y);
       if (lane == 0) red[w] = ss;  // red[] was last read before the barrier above
