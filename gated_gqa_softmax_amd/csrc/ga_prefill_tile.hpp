@@ -422,18 +422,6 @@ __device__ __forceinline__ void attn_tile_b(const unsigned char* smem, WaveState
   tile_b_finish<D, NS, BUF, HALF, CINIT>(smem, ws, tile_b_qk<D, NS, BUF, HALF, CINIT>(smem, ws), need_mask, lim);
 }
 
-// Largest |w[e]| over the d weights, the same value in every lane (0 for a
-// null pointer). Each lane reads d/64 of them.
-template <int D>
-__device__ __forceinline__ float max_abs_weight(const float* w) {
-  if (!w) return 0.f;
-  const int lane = threadIdx.x & 63;
-  float m = 0.f;
-#pragma unroll
-  for (int e = lane; e < D; e += 64) m = fmaxf(m, fabsf(w[e]));
-  return max_xor<64>(m);
-}
-
 // Largest log2-domain score bound a row may have before the bounded tiles'
 // probabilities 2^(s - c) could leave the normal fp32 range (the row's
 // largest one is at least 2^(-2c)).

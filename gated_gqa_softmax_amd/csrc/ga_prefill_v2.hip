@@ -229,13 +229,7 @@ __global__ __launch_bounds__(512) void prefill_v2_kernel(const PrefillParams p) 
   }
 
 
-  // ---- score bound (see attn_tile_b): with both norm weights every score
-  // s * log2(e) is at most scale * |q_hat| * sqrt(d) max|w_k| (2% margin for
-  // the bf16 roundings and the sin/cos error); bounded rows fold the scale
-  // into q_hat. Workgroup-uniform: it depends on the weights only.
   const float sl2 = p.scale_log2;
-  const float kb_norm = max_abs_weight<D>(p.wk) * sqrtf((float)D) * 1.02f;
-  const bool bounded = !LSE && p.wq && p.wk && sl2 * sqrtf((float)D) * max_abs_weight<D>(p.wq) * kb_norm <= kMaxScoreBound;
 
   // ---- Q prologue: RMSNorm + RoPE of 128 rows into LDS ------------------------
   // Four adjacent lanes per row, each holding QE = D/4 elements in 16-byte
@@ -309,6 +303,13 @@ __global__ __launch_bounds__(512) void prefill_v2_kernel(const PrefillParams p) 
       qw[2 * i + 1] = *(const f32x4_t*)(p.wq + 8 * qchunk(i) + 4);
     }
   }
+  // the k-norm weights, for the score bound (loaded with the rest, not as a
+  // dependent chain before them)
+  float wkv[D / 64];
+  if (p.wk) {
+#pragma unroll
+    for (int e = 0; e < D / 64; ++e) wkv[e] = p.wk[lane + 64 * e];
+  }
 
   // table: (cos, sin) per (token of the two blocks, pair index); pair t of
   // token tt sits at t ^ (tt & 7) (half % 8 == 0) so the quarter-0 lanes of
@@ -326,6 +327,28 @@ __global__ __launch_bounds__(512) void prefill_v2_kernel(const PrefillParams p) 
       }
     }
   }
+
+  // ---- score bound (see attn_tile_b): with both norm weights every score
+  // s * log2(e) is at most scale * |q_hat| * sqrt(d) max|w_k| (2% margin for
+  // the bf16 roundings and the sin/cos error); bounded rows fold the scale
+  // into q_hat. Workgroup-uniform: it depends on the weights only (a quad's
+  // four lanes hold all D weights of q between them).
+  float mq = 0.f, mk = 0.f;
+  if (p.wq) {
+#pragma unroll
+    for (int i = 0; i < 2 * QC; ++i)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) mq = fmaxf(mq, fabsf(qw[i][jj]));
+    mq = fmaxf(mq, __shfl_xor(mq, 1, 64));
+    mq = fmaxf(mq, __shfl_xor(mq, 2, 64));
+  }
+  if (p.wk) {
+#pragma unroll
+    for (int e = 0; e < D / 64; ++e) mk = fmaxf(mk, fabsf(wkv[e]));
+    mk = max_xor<64>(mk);
+  }
+  const float kb_norm = mk * sqrtf((float)D) * 1.02f;
+  const bool bounded = !LSE && p.wq && p.wk && sl2 * sqrtf((float)D) * mq * kb_norm <= kMaxScoreBound;
 
   float x[QE];
 #pragma unroll

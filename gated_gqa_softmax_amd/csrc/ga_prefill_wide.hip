@@ -152,6 +152,24 @@ __device__ __forceinline__ void wide_loop_p(unsigned char* smem, WaveState<D>& w
   }
 }
 
+// RoPE of a row held in the MFMA operand layout: x[kk][j] is element
+// 16kk + 8hi + j; pair (t, t + 16 HK) for the 16 HK pairs, with the
+// frequencies of pairs 16kk + 8hi + j in fr[kk][j].
+template <int NK, int HK>
+__device__ __forceinline__ void rope_rows(float (&x)[NK][8], const double (&fr)[NK / 2][8], int pos) {
+  static_assert(HK <= NK / 2, "rotated pairs");
+#pragma unroll
+  for (int kk = 0; kk < HK; ++kk)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      float c, s;
+      rope_cos_sin(pos, fr[kk][j], &c, &s);
+      const float a = x[kk][j], e = x[kk + HK][j];
+      x[kk][j] = a * c - e * s;
+      x[kk + HK][j] = e * c + a * s;
+    }
+}
+
 template <int D, int GATE>
 __global__ __launch_bounds__(512) void prefill_wide_kernel(const PrefillParams p) {
   typedef WideShape<D> S;
@@ -208,28 +226,16 @@ __global__ __launch_bounds__(512) void prefill_wide_kernel(const PrefillParams p
   if (nst > 0) stage_issue<D, S::NSTAGE, 0>(smem, krs, vrs, koff, voff, w, 0, kv_row_bytes);
   if (nst > 1) stage_issue<D, S::NSTAGE, 1>(smem, krs, vrs, koff, voff, w, 1, kv_row_bytes);
 
-  // ---- score bound: with both norm weights, |s| * log2(e) <= scale * d *
-  // max|w_q| * max|w_k| (RMS-normed rows have norm sqrt(d) before their
-  // weights, RoPE keeps norms; 2% margin for the bf16 roundings of q_hat and
-  // k_hat and the sin/cos error). Workgroup-uniform: it depends on the
-  // weights only.
-  const float sl2 = p.scale_log2;
-  const float kb_norm = max_abs_weight<D>(p.wk) * sqrtf((float)D) * 1.02f;  // bound on |k_hat|
-  const bool bounded = p.wq && p.wk && sl2 * sqrtf((float)D) * max_abs_weight<D>(p.wq) * kb_norm <= kMaxScoreBound;
-  // the running-max loop keeps three stages in flight, the pipelined one two;
-  // the pipelined one starts from an all-masked tile over V buffer NSTAGE - 1,
-  // zeroed here (it is first loaded in step 1, after step 0's barrier)
-  if (!bounded && nst > 2) stage_issue<D, S::NSTAGE, 2>(smem, krs, vrs, koff, voff, w, 2, kv_row_bytes);
-  if (bounded) {
-    u32x4_t* zv = (u32x4_t*)(smem + S::VBASE + (S::NSTAGE - 1) * S::TILE_BYTES);
-    for (int i = threadIdx.x; i < S::TILE_BYTES / 16; i += 512) zv[i] = u32x4_t{0, 0, 0, 0};
-  }
-
   // ---- q_hat of this lane's row, straight into the MFMA operand layout -------
   // Lane (l32, hi) holds elements 16kk + 8hi + [0, 8) of row l32 for every kk.
   // Bounded rows fold the softmax scale (log2 domain) into q_hat and start
   // their score accumulators at -c, c = |q_hat| * (bound on |k_hat|).
+  // Every global load of the prologue (q, both norm weights, the position,
+  // the RoPE frequencies) is issued before any of them is waited for: as a
+  // chain of dependent loads they took most of the prologue.
   WaveState<D> ws;
+  const float sl2 = p.scale_log2;
+  bool bounded;
   {
     constexpr int NK = D / 16;
     const int half = p.half;
@@ -247,10 +253,49 @@ __global__ __launch_bounds__(512) void prefill_wide_kernel(const PrefillParams p
         wv[kk][1] = *(const f32x4_t*)(p.wq + kk * 16 + hi * 8 + 4);
       }
     }
+    float wkv[D / 64];
+    if (p.wk) {
+#pragma unroll
+      for (int e = 0; e < D / 64; ++e) wkv[e] = p.wk[lane + 64 * e];
+    }
+    double fr[NK / 2][8];
+#pragma unroll
+    for (int kk = 0; kk < NK / 2; ++kk)
+      if (kk * 16 < half) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) fr[kk][j] = p.inv_freq[kk * 16 + hi * 8 + j];
+      }
     const int pos = p.positions ? p.positions[(long)b * n + tq] : tq;
+
+    // score bound: with both norm weights, |s| * log2(e) <= scale * d *
+    // max|w_q| * max|w_k| (RMS-normed rows have norm sqrt(d) before their
+    // weights, RoPE keeps norms; 2% margin for the bf16 roundings of q_hat and
+    // k_hat and the sin/cos error). Workgroup-uniform: it depends on the
+    // weights only.
+    float mq = 0.f, mk = 0.f;
+    if (p.wq) {
+#pragma unroll
+      for (int kk = 0; kk < NK; ++kk)
+#pragma unroll
+        for (int c2 = 0; c2 < 2; ++c2)
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) mq = fmaxf(mq, fabsf(wv[kk][c2][jj]));
+      mq = fmaxf(mq, swap_half(mq));  // the other half of the columns
+    }
+    if (p.wk) {
+#pragma unroll
+      for (int e = 0; e < D / 64; ++e) mk = fmaxf(mk, fabsf(wkv[e]));
+      mk = max_xor<64>(mk);
+    }
+    const float kb_norm = mk * sqrtf((float)D) * 1.02f;  // bound on |k_hat|
+    bounded = p.wq && p.wk && sl2 * sqrtf((float)D) * mq * kb_norm <= kMaxScoreBound;
+
     float x[NK][8];
 #pragma unroll
     for (int kk = 0; kk < NK; ++kk) unpack8(raw[kk], x[kk]);
+    // RMSNorm (bounded rows: times the softmax scale); c from the row's norm
+    // here, which RoPE keeps
+    float c = 0.f;
     if (p.wq) {
       float ss = 0.f;
 #pragma unroll
@@ -258,51 +303,38 @@ __global__ __launch_bounds__(512) void prefill_wide_kernel(const PrefillParams p
 #pragma unroll
         for (int j = 0; j < 8; ++j) ss += x[kk][j] * x[kk][j];
       ss += swap_half(ss);
-      const float inv = rsqrtf(ss * (1.0f / D) + p.eps);
-#pragma unroll
-      for (int kk = 0; kk < NK; ++kk)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) x[kk][j] *= inv * wv[kk][j >> 2][j & 3];
-    }
-    // RoPE: pair (t, t + half) with t = 16kk + 8hi + j, kk < half / 16
-#pragma unroll
-    for (int kk = 0; kk < NK / 2; ++kk) {
-      if (kk * 16 < half) {
-        const int kp = kk + (half >> 4);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          float c, s;
-          rope_cos_sin(pos, p.inv_freq[kk * 16 + hi * 8 + j], &c, &s);
-          float a = x[kk][j], e = 0.f;
-          // kp is lane-uniform; select its chunk without dynamic indexing
-#pragma unroll
-          for (int q2 = 0; q2 < NK; ++q2)
-            if (q2 == kp) e = x[q2][j];
-          const float ra = a * c - e * s, re = e * c + a * s;
-          x[kk][j] = ra;
-#pragma unroll
-          for (int q2 = 0; q2 < NK; ++q2)
-            if (q2 == kp) x[q2][j] = re;
-        }
-      }
-    }
-    float c = 0.f;
-    if (bounded) {
-      float ss = 0.f;
+      const float inv = rsqrtf(ss * (1.0f / D) + p.eps) * (bounded ? sl2 : 1.0f);
+      float s2 = 0.f;
 #pragma unroll
       for (int kk = 0; kk < NK; ++kk)
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-          x[kk][j] *= sl2;
-          ss += x[kk][j] * x[kk][j];
+          x[kk][j] *= inv * wv[kk][j >> 2][j & 3];
+          s2 += x[kk][j] * x[kk][j];
         }
-      ss += swap_half(ss);
-      c = sqrtf(ss) * kb_norm;
+      if (bounded) c = sqrtf(s2 + swap_half(s2)) * kb_norm;
+    }
+    // RoPE: pair (t, t + half) with t = 16kk + 8hi + j, kk < half / 16 (the
+    // pairing is fixed at compile time for each half / 16)
+    switch (half >> 4) {
+      case 1: rope_rows<NK, 1>(x, fr, pos); break;
+      case 2: rope_rows<NK, 2>(x, fr, pos); break;
+      case 3: rope_rows<NK, 3>(x, fr, pos); break;
+      case 4: rope_rows<NK, 4>(x, fr, pos); break;
+      default: break;
     }
 #pragma unroll
     for (int i = 0; i < 16; ++i) ws.cinit[i] = -c;
 #pragma unroll
     for (int kk = 0; kk < NK; ++kk) ws.set_qf(kk, __builtin_bit_cast(bf16x8_t, pack8(x[kk])));
+  }
+  // the running-max loop keeps three stages in flight, the pipelined one two;
+  // the pipelined one starts from an all-masked tile over V buffer NSTAGE - 1,
+  // zeroed here (it is first loaded in step 1, after step 0's barrier)
+  if (!bounded && nst > 2) stage_issue<D, S::NSTAGE, 2>(smem, krs, vrs, koff, voff, w, 2, kv_row_bytes);
+  if (bounded) {
+    u32x4_t* zv = (u32x4_t*)(smem + S::VBASE + (S::NSTAGE - 1) * S::TILE_BYTES);
+    for (int i = threadIdx.x; i < S::TILE_BYTES / 16; i += 512) zv[i] = u32x4_t{0, 0, 0, 0};
   }
 #pragma unroll
   for (int mb = 0; mb < D / 32; ++mb)
