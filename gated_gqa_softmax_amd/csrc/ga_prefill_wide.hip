@@ -119,36 +119,56 @@ __device__ __forceinline__ void wide_step_p(unsigned char* smem, WaveState<D>& w
   clim = l1;
 }
 
+// Stage st's loads into ring buffer st % kWideStages (a run-time index).
+template <int D>
+__device__ __forceinline__ void wide_issue_rt(unsigned char* smem, i32x4_t krs, i32x4_t vrs, int koff, int voff, int w,
+                                              int st, int kv_row_bytes) {
+  switch (st % kWideStages) {
+    case 0: stage_issue<D, kWideStages, 0>(smem, krs, vrs, koff, voff, w, st, kv_row_bytes); break;
+    case 1: stage_issue<D, kWideStages, 1>(smem, krs, vrs, koff, voff, w, st, kv_row_bytes); break;
+    case 2: stage_issue<D, kWideStages, 2>(smem, krs, vrs, koff, voff, w, st, kv_row_bytes); break;
+    default: stage_issue<D, kWideStages, 3>(smem, krs, vrs, koff, voff, w, st, kv_row_bytes); break;
+  }
+}
+
+// The wave computes stages [0, my_nst) (the later ones hold no key its rows
+// see), then only takes its part in the loads and barriers of the rest.
 template <int D>
 __device__ __forceinline__ void wide_loop_p(unsigned char* smem, WaveState<D>& ws, i32x4_t krs, i32x4_t vrs, int koff,
-                                            int voff, int w, int nst, int kv_row_bytes, int wave_min_tok,
+                                            int voff, int w, int nst, int my_nst, int kv_row_bytes, int wave_min_tok,
                                             int my_lim_tok, int n, int hi) {
   f32x16_t cs;
 #pragma unroll
   for (int i = 0; i < 16; ++i) cs[i] = -INFINITY;
   bool cmask = false;
   int clim = 0;
-  for (int st0 = 0; st0 < nst; st0 += kWideStages) {
+  for (int st0 = 0; st0 < my_nst; st0 += kWideStages) {
     wide_step_p<D, 0>(smem, ws, cs, cmask, clim, krs, vrs, koff, voff, w, st0, nst, kv_row_bytes, wave_min_tok,
                       my_lim_tok, n, hi);
-    if (st0 + 1 < nst)
+    if (st0 + 1 < my_nst)
       wide_step_p<D, 1>(smem, ws, cs, cmask, clim, krs, vrs, koff, voff, w, st0 + 1, nst, kv_row_bytes,
                         wave_min_tok, my_lim_tok, n, hi);
-    if (st0 + 2 < nst)
+    if (st0 + 2 < my_nst)
       wide_step_p<D, 2>(smem, ws, cs, cmask, clim, krs, vrs, koff, voff, w, st0 + 2, nst, kv_row_bytes,
                         wave_min_tok, my_lim_tok, n, hi);
-    if (st0 + 3 < nst)
+    if (st0 + 3 < my_nst)
       wide_step_p<D, 3>(smem, ws, cs, cmask, clim, krs, vrs, koff, voff, w, st0 + 3, nst, kv_row_bytes,
                         wave_min_tok, my_lim_tok, n, hi);
   }
-  // the last pending tile (its stage's buffer is never reloaded)
+  // the last pending tile: its stage's buffer is reloaded two steps later, so
+  // not before every wave has passed the next barrier
   typedef WideShape<D> S;
   constexpr int NS = S::NSTAGE;
-  switch ((nst - 1) % NS) {
+  switch ((my_nst - 1) % NS) {
     case 0: tile_b_finish<D, NS, 0, 1>(smem, ws, cs, cmask, clim); break;
     case 1: tile_b_finish<D, NS, 1, 1>(smem, ws, cs, cmask, clim); break;
     case 2: tile_b_finish<D, NS, 2, 1>(smem, ws, cs, cmask, clim); break;
     default: tile_b_finish<D, NS, 3, 1>(smem, ws, cs, cmask, clim); break;
+  }
+  for (int st = my_nst; st < nst; ++st) {
+    wait_stage<2 * S::LOADS_PER_WAVE>(min(1, nst - 1 - st));
+    lds_barrier();
+    if (st + 2 < nst) wide_issue_rt<D>(smem, krs, vrs, koff, voff, w, st + 2, kv_row_bytes);
   }
 }
 
@@ -193,8 +213,11 @@ __global__ __launch_bounds__(512) void prefill_wide_kernel(const PrefillParams p
   const int kend = min(n, blk * TB + TB);
   const int nst = (kend + S::ST - 1) / S::ST;
 
-  // this lane's query row (head-major inside the block)
-  const int my_r = w * 32 + l32;
+  // this lane's query row (head-major inside the block). The two waves of a
+  // SIMD (w and w + 4) take complementary row slots (wr and 7 - wr's mirror),
+  // so the causal diagonal's short rows are spread over the SIMDs.
+  const int wr = (w < 4) ? w : 11 - w;
+  const int my_r = wr * 32 + l32;
   const int my_hh = my_r / TB;
   const int my_tt = my_r - my_hh * TB;
   const int my_tok0 = blk * TB + my_tt;
@@ -355,11 +378,14 @@ __global__ __launch_bounds__(512) void prefill_wide_kernel(const PrefillParams p
   }
 
   // ---- main loop ---------------------------------------------------------------
-  if (bounded)
-    wide_loop_p<D>(smem, ws, krs, vrs, koff, voff, w, nst, kv_row_bytes, wave_min_tok, my_lim_tok, n, hi);
-  else
+  if (bounded) {
+    // stages up to the one holding the wave's last row (at least one)
+    const int my_nst = min(nst, max(1, wave_max_tok / S::ST + 1));
+    wide_loop_p<D>(smem, ws, krs, vrs, koff, voff, w, nst, my_nst, kv_row_bytes, wave_min_tok, my_lim_tok, n, hi);
+  } else {
     wide_loop<D, false>(smem, ws, krs, vrs, koff, voff, w, nst, kv_row_bytes, wave_min_tok, wave_max_tok,
                         my_lim_tok, n, sl2, hi);
+  }
 
   // ---- epilogue: normalise, gate, store ----------------------------------------
   // The wave's 32 rows, RPI rows per instruction and LPR lanes of 8 elements
@@ -374,7 +400,7 @@ __global__ __launch_bounds__(512) void prefill_wide_kernel(const PrefillParams p
   uint16_t ghead[NIT];
 #pragma unroll
   for (int it = 0; it < NIT; ++it) {
-    const int r = w * 32 + it * RPI + rsub;
+    const int r = wr * 32 + it * RPI + rsub;
     const int hh = r / TB;
     const int tt = r - hh * TB;
     const int tok = blk * TB + tt;
