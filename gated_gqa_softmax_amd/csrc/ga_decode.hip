@@ -27,33 +27,37 @@
 
 namespace ga {
 
-// Work item t of the partials grid: the t-th (sequence, chunk) pair among the
-// chunks that hold keys, sequences in order, chunks in order within each.
+// Work item t of the partials grid: first every whole chunk (sequences in
+// order, chunks in order within each), then the last, partial chunk of each
+// sequence that has one, so that the grid's last workgroups are short ones and
+// the tail of the launch, where the compute units run out of work, is short.
 // Lengths outside [0, max_len] count as empty. Wave-uniform; false when t is
 // past the last chunk.
 template <int C>
 __device__ __forceinline__ bool locate_chunk(const int32_t* lens, int B, int max_len, int t, int lane, int& b,
                                              int& split, int& L) {
-  int before = 0;  // chunks of the sequences before this 64-sequence window
-  for (int base = 0; base < B; base += 64) {
-    int len = base + lane < B ? lens[base + lane] : 0;
-    if (len < 0 || len > max_len) len = 0;
-    const int cnt = (len + C - 1) / C;
-    int incl = cnt;  // inclusive prefix sum over the window's lanes
+  int before = 0;  // chunks of the passes and sequences before this 64-sequence window
+  for (int pass = 0; pass < 2; ++pass) {
+    for (int base = 0; base < B; base += 64) {
+      int len = base + lane < B ? lens[base + lane] : 0;
+      if (len < 0 || len > max_len) len = 0;
+      const int cnt = pass == 0 ? len / C : (len % C != 0 ? 1 : 0);
+      int incl = cnt;  // inclusive prefix sum over the window's lanes
 #pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const int y = __shfl_up(incl, off, 64);
-      if (lane >= off) incl += y;
+      for (int off = 1; off < 64; off <<= 1) {
+        const int y = __shfl_up(incl, off, 64);
+        if (lane >= off) incl += y;
+      }
+      const unsigned long long hit = __ballot(before + incl > t);
+      if (hit) {
+        const int j = __builtin_ctzll(hit);
+        b = base + j;
+        L = __shfl(len, j, 64);
+        split = pass == 0 ? t - (before + __shfl(incl, j, 64) - __shfl(cnt, j, 64)) : L / C;
+        return true;
+      }
+      before += __shfl(incl, 63, 64);
     }
-    const unsigned long long hit = __ballot(before + incl > t);
-    if (hit) {
-      const int j = __builtin_ctzll(hit);
-      b = base + j;
-      L = __shfl(len, j, 64);
-      split = t - (before + __shfl(incl, j, 64) - __shfl(cnt, j, 64));
-      return true;
-    }
-    before += __shfl(incl, 63, 64);
   }
   return false;
 }
@@ -75,29 +79,13 @@ __global__ __launch_bounds__(256) void decode_partials_kernel(const DecodeParams
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   // consecutive workgroups take the KV heads of one chunk, so the heads'
   // halves of each cache row are read at the same time; the chunks that hold
-  // keys come first, sequence by sequence, and the grid's surplus (sized for
-  // every sequence at max_len) exits at the end
+  // keys come first (whole ones, then the partial ones: locate_chunk), and
+  // the grid's surplus (sized for every sequence at max_len) exits at the end
   const int g = blockIdx.x % p.G;
   int b, split, L;
   if (!locate_chunk<C>(p.cache_lens, p.B, p.max_len, (int)(blockIdx.x / p.G), lane, b, split, L)) return;
   const int start = split * C;
 
-  // q-hat of the group's heads at position L (bf16, the MFMA operand precision)
-  for (int idx = tid; idx < 16 * LPR; idx += 256) {
-    const int r = idx / LPR, c = idx % LPR;
-    u32x4_t raw = {0, 0, 0, 0};
-    if (r < GRP) raw = *(const u32x4_t*)(p.q + ((long)b * p.H + g * GRP + r) * p.qs + c * 8);
-    float x[8];
-    unpack8(raw, x);
-    norm_rope_chunk<D>(x, c, p.wq ? p.wq + c * 8 : nullptr, p.eps, p.rot, L, p.inv_freq, nullptr);
-    *(u32x4_t*)(Qs + r * SQ + c * 8) = pack8(x);
-  }
-  __syncthreads();
-
-  const int l16 = lane & 15, q4 = lane >> 4;
-  bf16x8_t qf[D / 32];
-#pragma unroll
-  for (int c = 0; c < D / 32; ++c) qf[c] = *(const bf16x8_t*)(Qs + l16 * SQ + c * 32 + q4 * 8);
   const long row = (long)p.G * D;
   const uint16_t* Kc = p.k_cache + (long)b * p.cache_bstride + (long)g * D;
   const uint16_t* Vc = p.v_cache + (long)b * p.cache_bstride + (long)g * D;
@@ -108,6 +96,32 @@ __global__ __launch_bounds__(256) void decode_partials_kernel(const DecodeParams
   const int ngroups = kend > kbeg ? (kend - kbeg + 63) / 64 : 0;
   const float sl2 = p.scale_log2;
   const int dc = lane % LPR, ks = lane / LPR;
+  const int l16 = lane & 15, q4 = lane >> 4;
+
+  // ---- every load of the prologue, then the first group's K and V rows, go
+  // out before q-hat is computed (as a chain of dependent loads the prologue
+  // took about a quarter of a workgroup's life). Lane (r, c) of pass i holds
+  // elements [8c, 8c + 8) of q row RP i + r; rows >= GRP are zeros.
+  constexpr int RP = 256 / LPR;                  // rows per pass
+  constexpr int NQP = (GRP + RP - 1) / RP;       // passes over the group's rows
+  const int qr = tid / LPR, qc = tid % LPR;
+  u32x4_t qraw[NQP];
+#pragma unroll
+  for (int i = 0; i < NQP; ++i) {
+    qraw[i] = u32x4_t{0, 0, 0, 0};
+    if (RP * i + qr < GRP) qraw[i] = *(const u32x4_t*)(p.q + ((long)b * p.H + g * GRP + RP * i + qr) * p.qs + qc * 8);
+  }
+  f32x4_t qw0 = {0.f, 0.f, 0.f, 0.f}, qw1 = qw0;
+  if (p.wq) {
+    qw0 = *(const f32x4_t*)(p.wq + qc * 8);
+    qw1 = *(const f32x4_t*)(p.wq + qc * 8 + 4);
+  }
+  const int half = p.rot >> 1;
+  const bool first = qc * 8 < half, rotated = qc * 8 < p.rot;
+  const int t0 = rotated ? (first ? qc * 8 : qc * 8 - half) : 0;  // pairs t0 .. t0 + 7 (rot % 16 == 0)
+  double fr[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) fr[j] = p.inv_freq[rotated ? t0 + j : 0];
 
   float m_lane = kNegBig;  // reference max of head l16 (same in the 4 lanes of that head)
   float l_part = 0.f;      // this lane's share of head l16's row sum
@@ -133,6 +147,46 @@ __global__ __launch_bounds__(256) void decode_partials_kernel(const DecodeParams
       vr[t] = *(const u32x4_t*)(Vc + vkey * row + dc * 8);
     }
   }
+
+  // q-hat of the group's heads at position L (bf16, the MFMA operand
+  // precision): RMSNorm, then RoPE with the partner chunk c +- rot/16
+#pragma unroll
+  for (int i = 0; i < NQP; ++i) {
+    float x[8];
+    unpack8(qraw[i], x);
+    if (p.wq) {
+      float ss = 0.f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) ss += x[j] * x[j];
+      ss = group_sum<LPR>(ss);
+      const float inv = rsqrtf(ss * (1.0f / D) + p.eps);
+      const float w8[8] = {qw0[0], qw0[1], qw0[2], qw0[3], qw1[0], qw1[1], qw1[2], qw1[3]};
+#pragma unroll
+      for (int j = 0; j < 8; ++j) x[j] = x[j] * inv * w8[j];
+    }
+    if (p.rot > 0) {
+      const int src = first ? lane + half / 8 : lane - half / 8;
+      float xp[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) xp[j] = __shfl(x[j], rotated ? src : lane, 64);
+      if (rotated) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          float cs, sn;
+          rope_cos_sin(L, fr[j], &cs, &sn);
+          x[j] = first ? (x[j] * cs - xp[j] * sn) : (x[j] * cs + xp[j] * sn);
+        }
+      }
+    }
+    *(u32x4_t*)(Qs + (RP * i + qr) * SQ + qc * 8) = pack8(x);
+  }
+  for (int idx = tid + 256 * NQP; idx < 16 * LPR; idx += 256)  // rows past the passes: zeros
+    *(u32x4_t*)(Qs + (idx / LPR) * SQ + (idx % LPR) * 8) = u32x4_t{0, 0, 0, 0};
+  __syncthreads();
+  bf16x8_t qf[D / 32];
+#pragma unroll
+  for (int c = 0; c < D / 32; ++c) qf[c] = *(const bf16x8_t*)(Qs + l16 * SQ + c * 32 + q4 * 8);
+
   for (int gi = 0; gi < ngroups; ++gi) {
     const int k0 = kbeg + gi * 64;
     // scores of this group: S^T[key][head], v_mfma_f32_16x16x32_bf16 over d
