@@ -119,7 +119,7 @@ struct DecodeParams {
   double inv_freq[kMaxHalfRot];
 };
 
-constexpr int kDecodeChunk = 512;  // keys per decode split
+constexpr int kDecodeChunk = 768;  // keys per decode split
 
 // Backward of the prefill (bf16). Row-major workspace copies: y [B,n,H,d]
 // (ungated attention output), dy [B,n,H,d] (gradient of y); lse, dsum

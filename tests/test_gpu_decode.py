@@ -67,6 +67,17 @@ def test_decode_small(w):
         assert np.array_equal(host(vc[b, L]), x["v_new"][b].astype(np.float64))
 
 
+def test_decode_split_boundaries():
+    """Cache lengths on both sides of one, two and three key chunks of the split."""
+    from gated_gqa_softmax_amd import _lib
+    ck = int(_lib.load().ga_decode_split_keys())
+    lens = [ck - 1, ck, ck + 1, 2 * ck, 2 * ck + 1, 3 * ck - 1]
+    w = _decode_case("split_boundaries", lens, 8, 2, 256, 64, "elementwise", seed=208)
+    print(f"[decode] split boundaries at {ck}-key chunks: {lens}", flush=True)
+    x, out, want, khn, kc, vc = _run(w, lens=np.array(lens, dtype=np.int32))
+    assert_close(host(out), want, w, w.name)
+
+
 def test_decode_full_workload():
     w = inputs.WORKLOADS["decode_64seq"]
     print("[decode] decode_64seq full", flush=True)
