@@ -249,7 +249,10 @@ template <int D, int NS, int BUF, int HALF>
 __device__ __forceinline__ bf16x8_t tile_kread(const unsigned char* smem, int kb, int kk) {
   typedef TileShape<D, NS> S;
   int a = kb ^ ((kk & 7) << 5);
-  asm volatile("" : "+v"(a));
+  // d = 256: opaque per read, so that the eight swizzled addresses are not
+  // kept live across the loop (no room beside two waves per SIMD); d < 256:
+  // they are, which saves an address operation per read
+  if (D == 256) asm volatile("" : "+v"(a));
   return *(const bf16x8_t*)(smem + a + (BUF * S::TILE_BYTES + HALF * 32 * S::ROW_BYTES + ((kk >> 3) << 8)));
 }
 
@@ -258,7 +261,7 @@ __device__ __forceinline__ bf16x8_t tile_vread(const unsigned char* smem, int vb
   typedef TileShape<D, NS> S;
   const int ks = t / (D / 32), mb = t % (D / 32);
   int a = vb ^ ((mb & 3) << 6);
-  asm volatile("" : "+v"(a));
+  if (D == 256) asm volatile("" : "+v"(a));  // (as in tile_kread)
   const unsigned char* a1 =
       smem + a + (BUF * S::TILE_BYTES + HALF * 32 * S::ROW_BYTES + ((mb & 4) << 6) + ks * 16 * S::ROW_BYTES);
   const i16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)a1);
@@ -273,7 +276,7 @@ __device__ __forceinline__ f32x16_t tile_b_qk(const unsigned char* smem, const W
   constexpr int NK = D / 16;
   constexpr int KPF = (D == 256) ? 3 : 4;
   int kb = ws.kbase;
-  asm volatile("" : "+v"(kb));
+  if (D == 256) asm volatile("" : "+v"(kb));  // (see tile_kread)
   bf16x8_t ka[NK];
   f32x16_t s;
 #pragma unroll
@@ -302,7 +305,7 @@ __device__ __forceinline__ void tile_b_finish(const unsigned char* smem, WaveSta
   constexpr int NV = D / 16;
   constexpr int VPF = (D == 256) ? 2 : 3;
   int vb = ws.vbase;
-  asm volatile("" : "+v"(vb));
+  if (D == 256) asm volatile("" : "+v"(vb));
   bf16x8_t va[NV];
 #pragma unroll
   for (int t = 0; t < VPF; ++t) va[t] = tile_vread<D, NS, BUF, HALF>(smem, vb, t);
@@ -377,7 +380,7 @@ __device__ __forceinline__ f32x16_t tile_b_pipe(const unsigned char* smem, WaveS
     for (int i = 0; i < 16; ++i) s[i] = ((i >> 2) * 8 + (i & 3) <= lim) ? s[i] : -INFINITY;
   }
   int kb = ws.kbase;
-  asm volatile("" : "+v"(kb));
+  if (D == 256) asm volatile("" : "+v"(kb));  // (see tile_kread)
   bf16x8_t ka[NK];
   f32x16_t sn;
   u32x4_t pk[2];
@@ -404,7 +407,7 @@ __device__ __forceinline__ f32x16_t tile_b_pipe(const unsigned char* smem, WaveS
   }
   ws.l_run = l;
   int vb = ws.vbase;
-  asm volatile("" : "+v"(vb));
+  if (D == 256) asm volatile("" : "+v"(vb));
   bf16x8_t va[NV];
 #pragma unroll
   for (int t = 0; t < VPF; ++t) va[t] = tile_vread<D, NS, B, H>(smem, vb, t);
