@@ -6,6 +6,8 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <atomic>
+
 #include "../../include/ga.h"
 #include "ga_internal.hpp"
 
@@ -369,6 +371,22 @@ ga_status check_chunk_common(const ga_attn_desc* desc, int32_t n, const void* k_
   return GA_OK;
 }
 
+// Compute units of the current device (the chunk kernel's work plan), queried
+// once per device.
+int device_cus() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+  if (dev < 64) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+  if (dev < 64) cache[dev].store(cus, std::memory_order_relaxed);
+  return cus;
+}
+
 ga_status chunk_attn_impl(const ga_attn_desc* desc, int32_t n, const void* q, const void* k_cache,
                           const void* v_cache, int32_t cap, const int32_t* cache_lens, const int32_t* chunk_lens,
                           int32_t max_cache_len, const void* gate, const float* q_norm_w, const float* k_norm_w,
@@ -392,6 +410,7 @@ ga_status chunk_attn_impl(const ga_attn_desc* desc, int32_t n, const void* q, co
     pp.key_base = cache_lens;
     pp.row_lens = chunk_lens;
     pp.max_base = max_cache_len;
+    pp.ncu = device_cus();
     pp.k_bstride = (long)cap * G * d;
     pp.v_bstride = pp.k_bstride;
     pp.qs = q_stride(desc);

@@ -59,6 +59,7 @@ struct PrefillParams {
   const int* key_base;  // [B] or null (= 0)
   const int* row_lens;  // [B] or null (= n)
   int max_base;         // key_base values outside [0, max_base] skip the sequence
+  int ncu;              // compute units of the device (chunk work plan)
   long k_bstride, v_bstride;
   // elements between the rows of consecutive heads of q and of the gate (a
   // token's rows follow each other: token stride = H * stride)

@@ -132,6 +132,153 @@ __device__ __forceinline__ void rope_quarter(float* x, const float2* cs, int sw)
 // Stages (64 keys each) that the queries of unit u (blocks 2u and 2u + 1) see.
 __device__ __forceinline__ int v2_unit_stages(int u, int TB, int n) { return (min(n, (u + 1) * 2 * TB) + 63) / 64; }
 
+// ---- chunk against a cache: work plan -----------------------------------------
+// In a chunk, a sequence's rows all see its L_b cached keys, so a sequence with
+// a long cache costs more per workgroup than one without, and with one
+// workgroup per compute unit the longest sequence sets the kernel time. The
+// plan gives such sequences one block per workgroup ("singles": twice the
+// workgroups, each ~56 % of a mirrored pair's time) and keeps mirrored pairs
+// for the rest, choosing how many sequences to split by an estimate of the
+// longest-first schedule that the in-order dispatch carries out: the largest
+// of (the costliest workgroup, the mean load per compute unit, the two
+// workgroup classes that meet on one compute unit when there are more
+// workgroups than units). Classes are then laid out costliest first, items
+// of a class in decreasing cost with the KV head minor. The per-sequence
+// lengths sit one per lane (at most kPlanMaxSeqs sequences; larger batches
+// keep the plain mirrored mapping); wave w scores splitting the w costliest
+// sequences, the scores meet in LDS, and every wave derives the same item.
+//
+// Cost model of one workgroup, in hundredths of a 64-key stage seen by one
+// block alone (measured at d = 256: 1.07 us per such stage, 1.9 us per stage
+// both blocks see, ~12 us of q prologue and gated epilogue).
+constexpr float kPlanStage1 = 100.f, kPlanStage2 = 178.f, kPlanFixed = 1120.f;
+constexpr int kPlanMaxSeqs = 64;
+constexpr int kPlanMaxSplit = 7;  // sequences considered for splitting (one candidate count per wave)
+
+struct ChunkItem {
+  int b, g, blk_light, blk_heavy;  // b < 0: no work for this workgroup
+  int L0, rows;                    // the sequence's cached keys and real chunk rows
+};
+
+// Sum and max of x over lanes [0, B), in lane order (the same bits in every wave).
+__device__ __forceinline__ float plan_sum(float x, int B) {
+  float s = 0.f;
+  for (int i = 0; i < B; ++i) s += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), i));
+  return s;
+}
+__device__ __forceinline__ float plan_max(float x, int B) {
+  float m = 0.f;
+  for (int i = 0; i < B; ++i) m = fmaxf(m, __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), i)));
+  return m;
+}
+
+// Start of lane j's class when classes are ordered by decreasing key
+// (ties by lane), each holding cnt items.
+__device__ __forceinline__ int plan_start(float key, int cnt, int B) {
+  const int lane = threadIdx.x & 63;
+  int start = 0;
+  for (int i = 0; i < B; ++i) {
+    const float ki = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(key), i));
+    const int ci = __builtin_amdgcn_readlane(cnt, i);
+    start += ((ki > key) | ((ki == key) & (i < lane))) ? ci : 0;  // branch-free
+  }
+  return start;
+}
+
+// Value of x at the lane whose class [start, start + cnt) holds position pos (0 if none).
+__device__ __forceinline__ float plan_at(float x, int start, int cnt, int pos) {
+  const unsigned long long m = __ballot(pos >= start && pos < start + cnt);
+  return m ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), __builtin_ctzll(m))) : 0.f;
+}
+
+// Every wave of the workgroup calls this (it holds a barrier); est_x: 8 floats of LDS.
+__device__ ChunkItem chunk_plan(const PrefillParams& p, int u, int w, float* est_x) {
+  const int lane = threadIdx.x & 63;
+  const int TB = p.TB;
+  const int B = p.B;
+  ChunkItem it{-1, 0, -1, -1, 0, 0};
+  if (B > kPlanMaxSeqs) {
+    // plain mirrored mapping (pair-major)
+    const int nBG = B * p.G;
+    const int pair = u / nBG;
+    if (pair >= (p.nblk + 1) / 2) return it;
+    it.b = (u % nBG) / p.G;
+    it.g = u % p.G;
+    it.blk_heavy = p.nblk - 1 - pair;
+    it.blk_light = (pair < it.blk_heavy) ? pair : -1;
+    it.L0 = p.key_base[it.b];
+    it.rows = p.row_lens ? min(p.row_lens[it.b], p.n) : p.n;
+    return it;
+  }
+  int L = 0, rows = 0;
+  if (lane < B) {
+    // both loads in flight together (the second reads key_base again when
+    // there are no row counts)
+    const int* rl = p.row_lens ? p.row_lens : p.key_base;
+    L = p.key_base[lane];
+    const int r = rl[lane];
+    rows = p.row_lens ? min(r, p.n) : p.n;
+  }
+  const bool valid = lane < B && L >= 0 && L <= p.max_base && rows > 0;
+  const int nbk = valid ? (rows + TB - 1) / TB : 0;               // blocks with real rows
+  const int s_all = valid ? (L + rows + 63) / 64 : 0;             // stages of the last block
+  const int s_first = valid ? (L + min(rows, TB) + 63) / 64 : 0;  // stages of block 0
+  // mirrored pairs (i, nbk - 1 - i): the first pair's cost stands for the class
+  const float c_pair = kPlanFixed + (nbk > 1 ? kPlanStage2 * s_first + kPlanStage1 * (s_all - s_first)
+                                             : kPlanStage1 * s_all);
+  const int n_pair = valid ? p.G * ((nbk + 1) / 2) : 0;
+  // singles: block nbk - 1 down to 0
+  const float c_single_max = kPlanFixed + kPlanStage1 * s_all;
+  const float c_single_mean = kPlanFixed + kPlanStage1 * ((float)L + 0.5f * (float)(rows + TB)) * (1.f / 64.f);
+  const int n_single = valid ? p.G * nbk : 0;
+
+  // splitting order: decreasing pair cost; wave w scores splitting the first w
+  const int rank = plan_start(valid ? c_pair : -1.f, 1, B);
+  const int kmax = min((int)__popcll(__ballot(valid)), kPlanMaxSplit);
+  if (w <= kmax) {
+    const bool single = valid && rank < w;
+    const int cnt = single ? n_single : n_pair;
+    const float cmean = single ? c_single_mean : c_pair;
+    const float items = plan_sum((float)cnt, B);
+    float est = fmaxf(plan_max(valid ? (single ? c_single_max : c_pair) : 0.f, B),
+                      plan_sum((float)cnt * cmean, B) / (float)max(p.ncu, 1));
+    if (items > (float)p.ncu) {
+      // the unit that took the cheapest of the first ncu workgroups also takes workgroup ncu
+      const int start = plan_start(valid ? cmean : -1.f, cnt, B);
+      est = fmaxf(est, plan_at(cmean, start, cnt, p.ncu - 1) + plan_at(cmean, start, cnt, p.ncu));
+    }
+    if (lane == 0) est_x[w] = est;
+  }
+  __syncthreads();
+  float e[kPlanMaxSplit + 1];
+#pragma unroll
+  for (int k = 0; k <= kPlanMaxSplit; ++k) e[k] = est_x[k];
+  int best_k = 0;
+  float best = e[0];
+#pragma unroll
+  for (int k = 1; k <= kPlanMaxSplit; ++k)
+    if (k <= kmax && e[k] < best) {
+      best = e[k];
+      best_k = k;
+    }
+  const bool single = valid && rank < best_k;
+  const int cnt = single ? n_single : n_pair;
+  const int start = plan_start(valid ? (single ? c_single_max : c_pair) : -1.f, cnt, B);
+  const unsigned long long m = __ballot(cnt > 0 && u >= start && u < start + cnt);
+  if (!m) return it;
+  const int j = __builtin_ctzll(m);
+  const int i = u - __builtin_amdgcn_readlane(start, j);
+  const int idx = i / p.G;
+  const int nbj = __builtin_amdgcn_readlane(nbk, j);
+  it.b = j;
+  it.g = i - idx * p.G;
+  it.L0 = __builtin_amdgcn_readlane(L, j);
+  it.rows = __builtin_amdgcn_readlane(rows, j);
+  it.blk_heavy = nbj - 1 - idx;
+  if (!__builtin_amdgcn_readlane((int)single, j)) it.blk_light = (idx < it.blk_heavy) ? idx : -1;
+  return it;
+}
+
 // CHUNK: a chunk against a cache (per-sequence key offsets and real-row counts
 // from p.key_base / p.row_lens); a separate instantiation, so the
 // whole-sequence kernel carries none of it.
@@ -144,18 +291,40 @@ __global__ __launch_bounds__(512) void prefill_v2_kernel(const PrefillParams p) 
   __shared__ float ml_x[4][64][2];
   __shared__ float lse_x[4][32];  // LSE: log2-domain log-sum-exp of each row
   __shared__ float c_x[128];      // bounded rows: the score bound c of each row
+  __shared__ float plan_x[8];     // chunk work plan: one estimate per candidate
 
   const int w = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);  // wave index (uniform)
   // wave -> (row group, phase): each SIMD (w % 4) gets one light and one heavy wave
   const int rg = (w < 4) ? w : ((w + 2) & 3);
   const int phase = (w < 4) ? 0 : 1;
 
-  const int nBG = p.B * p.G;
-  const int u = blockIdx.x;
-  const int pair = u / nBG;
-  const int bg = u % nBG;
-  const int b = bg / p.G;
-  const int g = bg % p.G;
+  // ---- work of this workgroup -------------------------------------------------
+  // Two blocks: a light block in row groups 0-1 and a heavy one in row groups
+  // 2-3, with all the stages they see. A whole sequence pairs block `pair`
+  // with its mirror nblk-1-pair; a chunk takes its blocks from the work plan.
+  int b, g, blk_light, blk_heavy;  // blk_light -1: no light block
+  // Chunk against a cache: the n query rows are tokens L0 + i of the sequence,
+  // rows i < nb are real, and keys [0, L0 + nb) are in the cache. (0 and n
+  // for a whole-sequence prefill.)
+  int L0 = 0, nb = p.n;
+  if (CHUNK) {
+    const ChunkItem item = chunk_plan(p, blockIdx.x, w, plan_x);
+    if (item.b < 0) return;
+    b = item.b;
+    g = item.g;
+    blk_light = item.blk_light;
+    blk_heavy = item.blk_heavy;
+    L0 = item.L0;
+    nb = item.rows;
+  } else {
+    const int nBG = p.B * p.G;
+    const int pair = blockIdx.x / nBG;
+    const int bg = blockIdx.x % nBG;
+    b = bg / p.G;
+    g = bg % p.G;
+    blk_heavy = p.nblk - 1 - pair;
+    blk_light = (pair < blk_heavy) ? pair : -1;  // odd middle
+  }
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -164,22 +333,11 @@ __global__ __launch_bounds__(512) void prefill_v2_kernel(const PrefillParams p) 
   const int TB = p.TB;
   const int n = p.n;
   const int grp = p.grp;
-  // Chunk against a cache: the n query rows are tokens L0 + i of the sequence,
-  // rows i < nb are real, and keys [0, L0 + nb) are in the cache. (0 and n
-  // for a whole-sequence prefill.)
-  const int L0 = CHUNK ? p.key_base[b] : 0;
-  const int nb = (CHUNK && p.row_lens) ? min(p.row_lens[b], n) : n;
   const int nH = p.H;
   const int nG = p.G;
-  const int nblk = p.nblk;
   const long k_bstride = p.k_bstride;
   const long v_bstride = p.v_bstride;
 
-  // ---- work of this workgroup -------------------------------------------------
-  // Two blocks: the light block `pair` in row groups 0-1 and its mirror
-  // nblk-1-pair in row groups 2-3, with all the stages they see.
-  const int blk_heavy = nblk - 1 - pair;
-  const int blk_light = (pair < blk_heavy) ? pair : -1;  // -1: no light block (odd middle)
   if (CHUNK) {
     if (L0 < 0 || L0 > p.max_base || nb <= 0) return;  // sequence skipped (whole workgroup)
     if ((blk_light < 0 || blk_light * TB >= nb) && (blk_heavy < 0 || blk_heavy * TB >= nb)) return;  // no real row
@@ -584,8 +742,8 @@ static void launch_v2_gate(const PrefillParams& p, int gate_mode, long grid, hip
 
 template <int D>
 static hipError_t launch_v2_d(const PrefillParams& p, int gate_mode, hipStream_t s) {
-  const int npairs = (p.nblk + 1) / 2;
-  const long grid = (long)p.B * p.G * npairs;
+  // a chunk's plan has at most one workgroup per block; the surplus exits
+  const long grid = (long)p.B * p.G * (p.key_base ? p.nblk : (p.nblk + 1) / 2);
   if (grid <= 0) return hipSuccess;
   if (p.key_base)
     launch_v2_gate<D, true>(p, gate_mode, grid, s);

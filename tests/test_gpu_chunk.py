@@ -196,6 +196,12 @@ SKEW_CASES = [
     _case("skew_d256_elementwise", 3, 256, 8, 2, 256, 64, "elementwise", [0, 6000, 100], [256, 200, 17], seed=320),
     _case("skew_d128_headwise", 4, 128, 16, 8, 128, 32, "headwise", [4000, 0, 2500, 64], seed=321),
     _case("skew_d256_nogate", 2, 64, 8, 2, 256, 32, "none", [3000, 1], seed=322),
+    # more workgroups than compute units: the plan's second-round estimate
+    _case("many_items_d128", 8, 512, 16, 8, 128, 32, "headwise", [4000, 0, 1000, 3000, 200, 2500, 50, 3500],
+          [512, 512, 300, 512, 1, 512, 512, 77], seed=324),
+    # more sequences than the plan takes (one per lane): the plain mirrored mapping
+    _case("many_seqs_d128", 70, 40, 4, 2, 128, 32, "elementwise", [(37 * b) % 300 for b in range(70)],
+          [40 - (b % 7) * 6 for b in range(70)], seed=325),
 ]
 
 
