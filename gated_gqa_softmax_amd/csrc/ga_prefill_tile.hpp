@@ -241,10 +241,37 @@ __device__ __forceinline__ void attn_tile(const unsigned char* smem, WaveState<D
 // With CINIT the QK chain starts from ws.cinit = -c, so the scores come out
 // as s - c; otherwise (d = 256, where the 16 registers of ws.cinit do not fit
 // beside two waves per SIMD) ws.m_run = -c is added before the exp.
-// p = 2^(s - c) needs one exp each; the row sum adds the bf16-rounded
-// probabilities (the PV operands) two at a time with v_dot2c_f32_bf16.
+// p = 2^(s - c) needs one exp each; the row sum is RowSum's.
 // The tile is two halves, tile_b_qk (the QK MFMAs) and tile_b_finish
 // (softmax and PV), so a wave may run them in different stages.
+// Lane-partial row sum of a bounded tile's probabilities. At d < 256 the
+// fp32 probabilities are added in four independent chains (plain adds hide
+// under the MFMAs; a chain of v_dot2c_f32_bf16 measured 1.4-2.1 % slower
+// there). At d = 256, where the register budget is the limit, the bf16 PV
+// operands are added two at a time with v_dot2c_f32_bf16 into one chain
+// (the four-chain form measured 0.8-2 % slower there).
+template <int D, bool FP32 = (D < 256)>
+struct RowSum {
+  float a[4];
+  __device__ __forceinline__ explicit RowSum(float l) : a{l, 0.f, 0.f, 0.f} {}
+  // pair k of the tile: probabilities e0, e1 and their bf16 pair w
+  __device__ __forceinline__ void add(int k, float e0, float e1, uint32_t w) {
+    a[(2 * k) & 3] += e0;
+    a[(2 * k + 1) & 3] += e1;
+  }
+  __device__ __forceinline__ float total() const { return (a[0] + a[1]) + (a[2] + a[3]); }
+};
+template <int D>
+struct RowSum<D, false> {
+  float l;
+  __device__ __forceinline__ explicit RowSum(float l0) : l(l0) {}
+  __device__ __forceinline__ void add(int, float, float, uint32_t w) {
+    const bf16x2_t one2 = {(__bf16)1.0f, (__bf16)1.0f};
+    l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w), one2, l, false);
+  }
+  __device__ __forceinline__ float total() const { return l; }
+};
+
 template <int D, int NS, int BUF, int HALF>
 __device__ __forceinline__ bf16x8_t tile_kread(const unsigned char* smem, int kb, int kk) {
   typedef TileShape<D, NS> S;
@@ -319,30 +346,19 @@ __device__ __forceinline__ void tile_b_finish(const unsigned char* smem, WaveSta
     for (int i = 0; i < 16; ++i) s[i] = ((i >> 2) * 8 + (i & 3) <= lim) ? s[i] : -INFINITY;
   }
   bf16x8_t pb[2];
+  RowSum<D> rs(ws.l_run);
 #pragma unroll
   for (int ks = 0; ks < 2; ++ks) {
     u32x4_t pk;
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      pk[j] = pack_bf16x2(__builtin_amdgcn_exp2f(s[ks * 8 + 2 * j]), __builtin_amdgcn_exp2f(s[ks * 8 + 2 * j + 1]));
+    for (int j = 0; j < 4; ++j) {
+      const float e0 = __builtin_amdgcn_exp2f(s[ks * 8 + 2 * j]), e1 = __builtin_amdgcn_exp2f(s[ks * 8 + 2 * j + 1]);
+      pk[j] = pack_bf16x2(e0, e1);
+      rs.add(j, e0, e1, pk[j]);
+    }
     pb[ks] = __builtin_bit_cast(bf16x8_t, pk);
   }
-  {
-    const bf16x2_t one2 = {(__bf16)1.0f, (__bf16)1.0f};
-    float l = ws.l_run;
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const u32x4_t pk = __builtin_bit_cast(u32x4_t, pb[ks]);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        // (the element goes through a scalar: a bit cast of the subscript
-        // itself compiled to a read of element 0)
-        const uint32_t wj = pk[j];
-        l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, wj), one2, l, false);
-      }
-    }
-    ws.l_run = l;
-  }
+  ws.l_run = rs.total();
 #pragma unroll
   for (int t = 0; t < NV; ++t) {
     if (t + VPF < NV) va[t + VPF] = tile_vread<D, NS, BUF, HALF>(smem, vb, t + VPF);
@@ -384,8 +400,7 @@ __device__ __forceinline__ f32x16_t tile_b_pipe(const unsigned char* smem, WaveS
   bf16x8_t ka[NK];
   f32x16_t sn;
   u32x4_t pk[2];
-  float l = ws.l_run;
-  const bf16x2_t one2 = {(__bf16)1.0f, (__bf16)1.0f};
+  RowSum<D> rs(ws.l_run);
 #pragma unroll
   for (int kk = 0; kk < KPF; ++kk) ka[kk] = tile_kread<D, NS, BN, HN>(smem, kb, kk);
 #pragma unroll
@@ -399,13 +414,14 @@ __device__ __forceinline__ f32x16_t tile_b_pipe(const unsigned char* smem, WaveS
     for (int j = 0; j < PPM; ++j) {
       const int k = kk * PPM + j;
       if (k < 8) {
-        const uint32_t w = pack_bf16x2(__builtin_amdgcn_exp2f(s[2 * k]), __builtin_amdgcn_exp2f(s[2 * k + 1]));
+        const float e0 = __builtin_amdgcn_exp2f(s[2 * k]), e1 = __builtin_amdgcn_exp2f(s[2 * k + 1]);
+        const uint32_t w = pack_bf16x2(e0, e1);
         pk[k >> 2][k & 3] = w;
-        l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w), one2, l, false);
+        rs.add(k, e0, e1, w);
       }
     }
   }
-  ws.l_run = l;
+  ws.l_run = rs.total();
   int vb = ws.vbase;
   if (D == 256) asm volatile("" : "+v"(vb));
   bf16x8_t va[NV];
