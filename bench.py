@@ -482,7 +482,7 @@ def time_chunk(torch, api, inputs, accounting, steps, warmup):
                    "rot_dim": w.rot_dim, "gate": w.gate_mode},
         "roofline": {"bound": "mfma", "kernel": kernel, "achieved": achieved, "peak": MI355X_BF16_DENSE_TFLOPS,
                      "unit": "TFLOP/s", "frac": achieved / MI355X_BF16_DENSE_TFLOPS, "kernel_ms": res["kernel_ms"],
-                     "algorithmic_flops": flops},
+                     "traffic": measured_traffic(kernel, w.name), "algorithmic_flops": flops},
     }
 
 
