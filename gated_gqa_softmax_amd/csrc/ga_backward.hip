@@ -25,6 +25,7 @@
 // 8 + 4(l/32) + 0..3 of each 16-token step.
 #include <cstdlib>
 #include <cstring>
+#include <type_traits>
 
 #include "ga_common.hpp"
 #include "ga_internal.hpp"
@@ -523,27 +524,33 @@ __global__ __launch_bounds__(256, 2) void bwd_dkv_kernel(const BwdParams p) {
   }
 }
 
-// ---- per-head dk-hat and dv, staged: the query tiles stream through LDS ------------------
+// ---- per-head dk-hat and dv, staged and pipelined over query tiles ---------------------
 // The same products as bwd_dkv_kernel. A workgroup takes one query head and a
 // mirrored pair of 64-key super blocks (m and M - 1 - m, two 32-key blocks
-// each). Wave w holds key block w & 1 of the super block; the waves split the
-// work by role: role 0 (w < 2) holds k-hat, computes S, P and dV over all D
-// dims; role 1 holds v, computes dP, takes P from its partner (wave w ^ 2)
-// through LDS, and computes dS and dK over all D dims. The query tile's
-// operands (row-blocked q-hat and dy, KK pieces each, their column-blocked
-// pieces over all D dims, 2 DB each, and the rows' log-sum-exp and rowsum(dy
-// y)) go HBM -> LDS with direct loads one tile ahead, one copy for the four
-// waves. No tracked load is left outstanding inside the tile loop, so no
-// compiler-placed wait drains the next tile's loads early.
+// each). Wave w holds key block w & 1 of the super block and a role: role 0
+// (w < 2) holds k-hat and computes S, P and dV over all D dims; role 1 holds
+// v, computes dP, takes P from its partner (wave w ^ 2) through LDS, and
+// computes dS and dK over all D dims. The two MFMA phases of consecutive
+// query tiles overlap: the MFMAs that use tile t's P (dV += dy^T P) or dS
+// (dK += q-hat^T dS) run interleaved with the same wave's S or dP chain of
+// tile t + 1, so the exponentials, the P exchange and the dS arithmetic sit
+// between two MFMA phases once per tile. The query tiles' operands go HBM ->
+// LDS with direct loads in two rings of two slots, one copy for the four
+// waves: the row-blocked q-hat and dy pieces that the chains read, and the
+// column-blocked q-hat and dy pieces with the rows' log-sum-exp and rowsum(dy
+// y) that the products read. A tile's loads go out one per MFMA pair of the
+// previous tile (a burst of them right after the barrier stalls the one wave
+// of each SIMD at issue); the columns are waited for at the tile's first
+// barrier, the rows before its second.
 template <int D>
-__global__ __launch_bounds__(256) void bwd_dkv_staged_kernel(const BwdParams p) {
+__global__ __launch_bounds__(256) void bwd_dkv_pipe_kernel(const BwdParams p) {
   constexpr int KK = D / 16, DB = D / 32;
-  constexpr int NP = 2 * KK + 4 * DB;  // 1 KiB pieces per stage
-  constexpr int NPW = NP / 4;          // 16-byte direct loads per wave per stage
-  constexpr int NS = 2;                // stages in the ring
-  static_assert(KK % 4 == 0 && DB % 2 == 0 && NPW + 1 < 32, "stage split over the four waves");
-  __shared__ __attribute__((aligned(16))) unsigned char stg[NS * NP * 1024];
-  __shared__ __attribute__((aligned(16))) float stat[NS][128];  // [lse of 32 rows x2 | dsum of 32 rows x2]
+  constexpr int NR = 2 * KK, NC = 4 * DB;    // 1 KiB pieces per tile: rows, columns
+  constexpr int NRW = NR / 4, NCW = NC / 4;  // 16-byte direct loads per wave per tile
+  static_assert(KK % 4 == 0 && DB % 2 == 0 && KK == 2 * DB, "pieces split over the four waves");
+  __shared__ __attribute__((aligned(16))) unsigned char rows_lds[2][NR * 1024];
+  __shared__ __attribute__((aligned(16))) unsigned char cols_lds[2][NC * 1024];
+  __shared__ __attribute__((aligned(16))) float stat[2][128];      // [lse of 32 rows x2 | dsum of 32 rows x2]
   __shared__ __attribute__((aligned(16))) float pxch[2][16 * 64];  // P of key block kbw, role 0 -> role 1
   const int lane = threadIdx.x & 63, hi = lane >> 5, l32 = lane & 31;
   const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
@@ -561,38 +568,62 @@ __global__ __launch_bounds__(256) void bwd_dkv_staged_kernel(const BwdParams p) 
   const i32x4_t ycs = buffer_desc(p.dy_cb + (long)bh * p.npad * D, slice);
   const uint32_t nstat = (uint32_t)((long)p.B * p.n * p.H * 4);
   const i32x4_t lrs = buffer_desc(p.lse, nstat), srs = buffer_desc(p.dsum, nstat);
-  const uint32_t stg0 = lds_addr(stg);
-  // stage piece j: q-hat rows (j < KK), dy rows (KK <= j < 2 KK), then the
-  // column-blocked q-hat and dy pieces (dim block jj / 2, 16-query half jj % 2)
-  auto issue = [&](int qt, int buf) {
-    const uint32_t base = stg0 + (uint32_t)(buf * NP * 1024);
+  // row piece j: q-hat rows (j < KK), then dy rows
+  auto issue_rows = [&](int qt, int slot) {
+    const uint32_t base = lds_addr(rows_lds[slot]);
+#pragma unroll
+    for (int i = 0; i < NRW; ++i) {
+      const int j = w + 4 * i;
+      if (i < KK / 4)
+        buffer_load_lds16(qrs, base + j * 1024, (qt * KK + j) * 1024 + lane * 16);
+      else
+        buffer_load_lds16(yrs, base + j * 1024, (qt * KK + j - KK) * 1024 + lane * 16);
+    }
+  };
+  // column piece j: q-hat (j < 2 DB), then dy; dim block jj / 2, 16-query half jj % 2
+  auto issue_cols = [&](int qt, int slot) {
     if (w < 2) {  // lanes l and l + 32: row qt * 32 + l (clamped to the last row)
       const int so = ((b * p.n + min(qt * 32 + l32, p.n - 1)) * p.H + h) * 4;
-      buffer_load_lds4(w == 0 ? lrs : srs, lds_addr(stat[buf]) + w * 256, so);
+      buffer_load_lds4(w == 0 ? lrs : srs, lds_addr(stat[slot]) + w * 256, so);
     }
+    const uint32_t base = lds_addr(cols_lds[slot]);
 #pragma unroll
-    for (int i = 0; i < NPW; ++i) {
+    for (int i = 0; i < NCW; ++i) {
       const int j = w + 4 * i;
-      if (i < KK / 4) {
-        buffer_load_lds16(qrs, base + j * 1024, (qt * KK + j) * 1024 + lane * 16);
-      } else if (i < KK / 2) {
-        buffer_load_lds16(yrs, base + j * 1024, (qt * KK + j - KK) * 1024 + lane * 16);
-      } else if (i < KK / 2 + DB / 2) {
-        const int jj = j - 2 * KK;
-        buffer_load_lds16(qcs, base + j * 1024, ((jj >> 1) * TS + qt * 2 + (jj & 1)) * 1024 + lane * 16);
-      } else {
-        const int jj = j - 2 * KK - 2 * DB;
-        buffer_load_lds16(ycs, base + j * 1024, ((jj >> 1) * TS + qt * 2 + (jj & 1)) * 1024 + lane * 16);
-      }
+      const int jj = (i < DB / 2) ? j : j - 2 * DB;
+      buffer_load_lds16((i < DB / 2) ? qcs : ycs, base + j * 1024, ((jj >> 1) * TS + qt * 2 + (jj & 1)) * 1024 + lane * 16);
     }
+  };
+  // single loads of the two rings (load i of this wave), for spreading a
+  // tile's loads over the MFMAs: a burst of them right after the barrier
+  // stalls the one wave of each SIMD at issue
+  auto load_row = [&](int qt, int slot, int i) {
+    const int j = w + 4 * i;
+    const uint32_t base = lds_addr(rows_lds[slot]);
+    if (i < KK / 4)
+      buffer_load_lds16(qrs, base + j * 1024, (qt * KK + j) * 1024 + lane * 16);
+    else
+      buffer_load_lds16(yrs, base + j * 1024, (qt * KK + j - KK) * 1024 + lane * 16);
+  };
+  auto load_col = [&](int qt, int slot, int i) {
+    if (i == 0 && w < 2) {
+      const int so = ((b * p.n + min(qt * 32 + l32, p.n - 1)) * p.H + h) * 4;
+      buffer_load_lds4(w == 0 ? lrs : srs, lds_addr(stat[slot]) + w * 256, so);
+    }
+    const int j = w + 4 * i;
+    const int jj = (i < DB / 2) ? j : j - 2 * DB;
+    buffer_load_lds16((i < DB / 2) ? qcs : ycs, lds_addr(cols_lds[slot]) + j * 1024,
+                      ((jj >> 1) * TS + qt * 2 + (jj & 1)) * 1024 + lane * 16);
   };
   for (int half = 0; half < 2; ++half) {
     const int sbk = half == 0 ? spair : M - 1 - spair;  // heavy super block first
     if (half == 1 && sbk == spair) break;               // (odd middle super block: one only)
     const int kb = 2 * sbk + kbw;                       // < NB: npad is a multiple of 64
-    const int qt0 = 2 * sbk, T = nkb - qt0;             // query tiles [qt0, nkb)
-    lds_barrier();  // every wave is done with the previous block's stages
-    issue(qt0, 0);
+    const int qt0 = 2 * sbk, T = nkb - qt0;             // query tiles [qt0, nkb), T >= 1
+    lds_barrier();  // every wave is done with the previous block's buffers
+    issue_rows(qt0, 0);
+    issue_cols(qt0, 0);
+    if (T > 1) issue_rows(qt0 + 1, 1);
     // role 0: k-hat pieces of the block (S = Q K^T), role 1: v pieces (dP = dy V^T)
     bf16x8_t bo[KK];
     const long kpiece = (bg * NB + kb) * KK;
@@ -605,32 +636,31 @@ __global__ __launch_bounds__(256) void bwd_dkv_staged_kernel(const BwdParams p) 
     f32x16_t acc[DB];  // role 0: dV^T, role 1: dK^T, all D dims
 #pragma unroll
     for (int mb = 0; mb < DB; ++mb) acc[mb] = f32x16_t{};
-    for (int t = 0; t < T; ++t) {
-      const int qt = qt0 + t, q0 = qt * 32;
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      lds_barrier();  // all of stage t is in LDS; every wave is past tile t - 1
-      if (t + 1 < T) issue(qt + 1, (t + 1) & 1);
-      const int buf = t & 1;
-      const unsigned char* sb = stg + buf * (NP * 1024) + lane * 16;
-      f32x16_t x = f32x16_t{};  // role 0: S, role 1: dP
-      lds_one_chain<KK, 4>(sb + role * KK * 1024, bo, x);
-      // the first column-blocked operands do not depend on P or dS; piece u:
-      // dim block u / 2, 16-query half u % 2 of dy (role 0) or q-hat (role 1)
-      constexpr int NC = 2 * DB, CPF = 4;
-      const unsigned char* cbase = sb + (2 * KK + (role ? 0 : 2 * DB)) * 1024;
-      bf16x8_t ca[NC];
-#pragma unroll
-      for (int u = 0; u < CPF; ++u) ca[u] = *(const bf16x8_t*)(cbase + u * 1024);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    lds_barrier();  // tile qt0's rows and columns and tile qt0 + 1's rows are in LDS
+    f32x16_t x = f32x16_t{};  // role 0: S, role 1: dP of the current tile
+    lds_one_chain<KK, 4>(rows_lds[0] + lane * 16 + role * KK * 1024, bo, x);
+    // one tile's step: wait, refill both rings, P (role 0) / dS (role 1), then
+    // tile t's products, with the chain of tile t + 1 between them when NEXT
+    auto step = [&](int t, auto next_tag) {
+      constexpr bool NEXT = decltype(next_tag)::value;
+      const int q0 = (qt0 + t) * 32;
+      // outstanding: tile t's columns and statistics, then tile t + 1's rows
+      // (loaded during the previous step's MFMAs); the rows are waited for
+      // before the second barrier
+      if (NEXT)
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NRW) : "memory");
+      else
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      lds_barrier();  // tile t's columns are in; every wave is past tile t - 1
+      const bool more_rows = t + 2 < T;  // (the loads go out during the MFMAs below)
       // rows 8 (i / 4) + 4 hi + i % 4 of slot i
-      const float* st = stat[buf];
-      f32x4_t lse4[4], dsum4[4];
-#pragma unroll
-      for (int ib = 0; ib < 4; ++ib) {
-        lse4[ib] = *(const f32x4_t*)(st + ib * 8 + hi * 4);
-        dsum4[ib] = *(const f32x4_t*)(st + 64 + ib * 8 + hi * 4);
-      }
+      const float* st = stat[t & 1];
       f32x16_t pm;
       if (role == 0) {
+        f32x4_t lse4[4];
+#pragma unroll
+        for (int ib = 0; ib < 4; ++ib) lse4[ib] = *(const f32x4_t*)(st + ib * 8 + hi * 4);
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int query = q0 + (i >> 2) * 8 + hi * 4 + (i & 3);
@@ -639,21 +669,62 @@ __global__ __launch_bounds__(256) void bwd_dkv_staged_kernel(const BwdParams p) 
           pxch[kbw][i * 64 + lane] = pm[i];
         }
       }
-      lds_barrier();  // P written (the previous tile's reads ended before this tile's stage barrier)
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      lds_barrier();  // P written (its reads of tile t - 1 ended before this tile's first barrier); tile t + 1's rows are in
       if (role == 1) {
+        f32x4_t dsum4[4];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float pv = pxch[kbw][i * 64 + lane];
-          pm[i] = pv * (x[i] - dsum4[i >> 2][i & 3]);  // dS
-        }
+        for (int ib = 0; ib < 4; ++ib) dsum4[ib] = *(const f32x4_t*)(st + 64 + ib * 8 + hi * 4);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) pm[i] = pxch[kbw][i * 64 + lane] * (x[i] - dsum4[i >> 2][i & 3]);  // dS
       }
       const bf16x8_t o0 = pack_operand(pm, 0), o1 = pack_operand(pm, 1);
+      // column piece u: dim block u / 2, 16-query half u % 2 of dy (role 0) or q-hat (role 1)
+      const unsigned char* cb = cols_lds[t & 1] + lane * 16 + (role ? 0 : 2 * DB) * 1024;
+      constexpr int PF = 2;
+      if constexpr (NEXT) {
+        // the chain of tile t + 1 (row pieces) interleaved with tile t's products
+        const unsigned char* rb = rows_lds[(t + 1) & 1] + lane * 16 + role * KK * 1024;
+        bf16x8_t ra[KK], ca[KK];
 #pragma unroll
-      for (int u = 0; u < NC; ++u) {
-        if (u + CPF < NC) ca[u + CPF] = *(const bf16x8_t*)(cbase + (u + CPF) * 1024);
-        acc[u >> 1] = mfma32(ca[u], (u & 1) ? o1 : o0, acc[u >> 1]);
+        for (int u = 0; u < PF; ++u) {
+          ra[u] = *(const bf16x8_t*)(rb + u * 1024);
+          ca[u] = *(const bf16x8_t*)(cb + u * 1024);
+        }
+#pragma unroll
+        for (int u = 0; u < KK; ++u) {
+          if (u + PF < KK) {
+            ra[u + PF] = *(const bf16x8_t*)(rb + (u + PF) * 1024);
+            ca[u + PF] = *(const bf16x8_t*)(cb + (u + PF) * 1024);
+          }
+          x = mfma32(ra[u], bo[u], u == 0 ? f32x16_t{} : x);
+          acc[u >> 1] = mfma32(ca[u], (u & 1) ? o1 : o0, acc[u >> 1]);
+          // tile t + 1's columns, then tile t + 2's rows: one load per MFMA pair
+          if (u < NCW) load_col(qt0 + t + 1, (t + 1) & 1, u);
+          else if (u - NCW < NRW && more_rows) load_row(qt0 + t + 2, t & 1, u - NCW);
+        }
+        static_assert(NCW + NRW <= KK, "one load per MFMA pair");
+        // keep that order: two reads ahead per MFMA pair
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 * PF, 0);
+#pragma unroll
+        for (int u = 0; u < KK - PF; ++u) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 2 * PF, 0);
+      } else {
+        bf16x8_t ca[KK];
+#pragma unroll
+        for (int u = 0; u < PF; ++u) ca[u] = *(const bf16x8_t*)(cb + u * 1024);
+#pragma unroll
+        for (int u = 0; u < KK; ++u) {
+          if (u + PF < KK) ca[u + PF] = *(const bf16x8_t*)(cb + (u + PF) * 1024);
+          acc[u >> 1] = mfma32(ca[u], (u & 1) ? o1 : o0, acc[u >> 1]);
+        }
       }
-    }
+    };
+    for (int t = 0; t + 1 < T; ++t) step(t, std::true_type{});
+    step(T - 1, std::false_type{});
     if (key < p.n) {
       const long ko_ = (((long)b * p.n + key) * p.H + h) * D;
       float* dst = role ? p.dkp : p.dvp;
@@ -866,7 +937,7 @@ static hipError_t launch_dkv_d(const BwdParams& p, hipStream_t s) {
       const long M = ((p.n + 31) / 32 + 1) / 2;  // 64-key super blocks
       const long wgs = (long)p.B * p.H * ((M + 1) / 2);
       if (wgs == 0) return hipSuccess;
-      hipLaunchKernelGGL((bwd_dkv_staged_kernel<D>), dim3((unsigned)wgs), dim3(256), 0, s, p);
+      hipLaunchKernelGGL((bwd_dkv_pipe_kernel<D>), dim3((unsigned)wgs), dim3(256), 0, s, p);
       return hipGetLastError();
     }
   }
