@@ -333,6 +333,40 @@ def prefill(q, k, v, gate, *, gate_mode: str, q_norm_w, k_norm_w, positions,
     return out.reshape(B, n, H * d)
 
 
+def prefill_row_lse(q, k, *, q_norm_w, k_norm_w, positions, rms_eps: float = 1e-6,
+                    rope_base: float = 10000.0, rot_dim: int = 0, scale: Optional[float] = None,
+                    rows: Optional[Sequence[tuple]] = None, dtype=np.float64) -> np.ndarray:
+    """Log2 of the normalising sum of each causal softmax row.
+
+    lse[b,i,h] = log2 sum_{j <= i} exp(s_ij), s_ij = (q_hat_i . k_hat_j) * scale,
+    the denominator of softmax(QK^T/sqrt(d) + M) ("Transformer by Hand · 6.
+    Gated attention", "The formula"), so a_ij = exp(s_ij) / 2^lse[b,i,h].
+    Evaluated in the stable form m + log sum exp(s - m) with m the row max
+    ("Attention, worked all the way through", "Why scaling and stable softmax
+    matter"), then divided by ln 2. Returns [B,n,H], or with ``rows`` (a list
+    of (b, i, h)) the values of those rows only.
+    """
+    for name, x in (("q", q), ("k", k)):
+        _check_finite(name, x)
+    q = np.asarray(q)
+    B, n, H, d = q.shape
+    G = np.asarray(k).shape[2]
+    if H % G:
+        raise ValueError("n_q_heads must be a multiple of n_kv_heads")
+    sc = _default_scale(d, scale)
+    kh = prefill_keys(k, k_norm_w, positions, rms_eps=rms_eps, rope_base=rope_base,
+                      rot_dim=rot_dim, dtype=dtype)
+    want = [(b, i, h) for b in range(B) for i in range(n) for h in range(H)] if rows is None else list(rows)
+    out = np.empty(len(want), dtype=dtype)
+    for t, (b, i, h) in enumerate(want):
+        qh = rope(rms_norm(q[b, i:i + 1, h:h + 1], q_norm_w, rms_eps, dtype),
+                  np.asarray(positions)[b, i:i + 1], rot_dim, rope_base, dtype)[0, 0]   # [T=1, 1 head, d]
+        s = (kh[b, :i + 1, kv_group(h, H, G)] @ qh) * dtype(sc)       # keys j <= i
+        m = np.max(s)
+        out[t] = (m + np.log(np.sum(np.exp(s - m)))) / math.log(2.0)
+    return out.reshape(B, n, H) if rows is None else out
+
+
 def prefill_rows(q, k, v, gate, rows: Sequence[tuple], *, gate_mode: str, q_norm_w, k_norm_w,
                  positions, rms_eps: float = 1e-6, rope_base: float = 10000.0, rot_dim: int = 0,
                  scale: Optional[float] = None, dtype=np.float64,
