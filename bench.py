@@ -602,6 +602,33 @@ def time_backward(torch, api, inputs, accounting, wname, steps, warmup):
     step_ms, step_s = timed_ms(torch, whole, stream, steps, 5)
     flops = accounting.causal_backward_flops(w.batch, w.n_q_heads, w.head_dim, w.seq_len)
     achieved = flops / (step_ms * 1e-3) / 1e12
+
+    # the training pair: the forward keeps each row's log-sum-exp, the backward reuses it
+    fws = torch.empty(api.ga_prefill_lse_workspace_bytes(d, w.seq_len), dtype=torch.uint8, device="cuda")
+    out = torch.empty((w.batch, w.seq_len, w.n_q_heads * w.head_dim), dtype=et, device="cuda")
+    lse = torch.empty((w.batch, w.seq_len, w.n_q_heads), dtype=torch.float32, device="cuda")
+
+    def fwd_lse():
+        api.ga_prefill_lse(d, q, k, v, gate=gate, q_norm_w=wq, k_norm_w=wk, positions=pos, out=out, lse=lse,
+                           workspace=fws, stream=stream)
+
+    def bwd_lse():
+        api.ga_prefill_backward(d, q, k, v, dout, gate=gate, q_norm_w=wq, k_norm_w=wk, positions=pos, workspace=ws,
+                                stream=stream, grads=grads, out=out, lse=lse)
+
+    fwd_lse()
+    ramp(torch, bwd_lse)
+    lse_ms, lse_s = timed_ms(torch, bwd_lse, stream, steps, 5)
+    ramp(torch, fwd_lse)
+    fwd_ms, fwd_s = timed_ms(torch, fwd_lse, stream, steps, 5)
+    saved = {
+        "backward_ms": lse_ms, "backward_samples_ms": lse_s,
+        "backward_tflops": flops / (lse_ms * 1e-3) / 1e12,
+        "backward_frac": flops / (lse_ms * 1e-3) / 1e12 / MI355X_BF16_DENSE_TFLOPS,
+        "forward_ms": fwd_ms, "forward_samples_ms": fwd_s,
+        "note": "ga_prefill_lse (out and row log-sum-exp; running-max softmax) then ga_prefill_backward_lse "
+                "(no recomputed forward attention); whole calls back to back, median of 5 samples",
+    }
     return {
         "metric": "prefill backward TFLOP/s",
         "value": achieved,
@@ -615,6 +642,7 @@ def time_backward(torch, api, inputs, accounting, wname, steps, warmup):
         "roofline": {"bound": "mfma", "kernel": "ga_prefill_backward (whole call: all its kernels)",
                      "achieved": achieved, "peak": MI355X_BF16_DENSE_TFLOPS, "unit": "TFLOP/s",
                      "frac": achieved / MI355X_BF16_DENSE_TFLOPS, "kernel_ms": step_ms, "algorithmic_flops": flops},
+        "saved_lse": saved,
     }
 
 

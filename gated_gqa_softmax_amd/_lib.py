@@ -76,6 +76,10 @@ SIGNATURES = {
     "ga_prefill_chunk_kernel": (ctypes.c_char_p, [_D, _I, _I]),
     "ga_prefill_backward_workspace_bytes": (_S, [_D, _I]),
     "ga_prefill_backward": (_I, [_D, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _S, _P]),
+    "ga_prefill_lse_workspace_bytes": (_S, [_D, _I]),
+    "ga_prefill_lse": (_I, [_D, _I, _P, _P, _P, _P, _P, _P, _P, _P, _S, _P, _P, _P]),
+    "ga_prefill_backward_lse": (_I, [_D, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                     _S, _P]),
     "ga_decode_split_keys": (_I, []),
     "ga_decode_workspace_bytes": (_S, [_D, _I]),
     "ga_decode": (_I, [_D, _P, _P, _P, _P, _P, _P, _P, _P, _I, _P, _I, _P, _S, _P, _P]),

@@ -451,21 +451,59 @@ def ga_prefill_backward_workspace_bytes(desc: AttnDesc, seq_len: int) -> int:
     return int(_lib.load().ga_prefill_backward_workspace_bytes(ctypes.byref(desc), seq_len))
 
 
-def ga_prefill_backward(desc: AttnDesc, q, k, v, dout, gate=None, q_norm_w=None, k_norm_w=None, positions=None,
-                        workspace=None, stream=None, weight_grads=True, grads: Optional[dict] = None) -> dict:
-    """Gradients of sum(dout * ga_prefill(...)): dict with dq, dk, dv, dgate
-    (None without a gate) and dq_norm_w, dk_norm_w (None without that norm
-    weight, or with weight_grads=False). ``grads`` may hold preallocated
-    output tensors under the same keys."""
+def _gate_shape(desc: AttnDesc, qshape):
+    if desc.gate_mode == _lib.GA_GATE_NONE:
+        return None
+    return qshape if desc.gate_mode == _lib.GA_GATE_ELEMENTWISE else qshape[:3]
+
+
+def ga_prefill_lse_workspace_bytes(desc: AttnDesc, seq_len: int) -> int:
+    return int(_lib.load().ga_prefill_lse_workspace_bytes(ctypes.byref(desc), seq_len))
+
+
+def ga_prefill_lse(desc: AttnDesc, q, k, v, gate=None, q_norm_w=None, k_norm_w=None, positions=None, out=None,
+                   lse=None, workspace=None, stream=None):
+    """Training forward: (out [B,n,H*d], lse [B,n,H] float32), lse the log2
+    of each causal softmax row's normalising sum, for ga_prefill_backward_lse."""
     lib = _lib.load()
     et = _elem_dtype(desc)
     B, n = desc.batch, _seq(q)[1]
     H, G, hd = desc.n_q_heads, desc.n_kv_heads, desc.head_dim
     qshape, kshape = (B, n, H, hd), (B, n, G, hd)
-    if desc.gate_mode == _lib.GA_GATE_NONE:
-        gshape = None
-    else:
-        gshape = qshape if desc.gate_mode == _lib.GA_GATE_ELEMENTWISE else (B, n, H)
+    gshape = _gate_shape(desc, qshape)
+    if out is None:
+        out = torch.empty((B, n, H * hd), dtype=et, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, n, H), dtype=torch.float32, device=q.device)
+    ws, wp, wb = _workspace_arg(workspace, ga_prefill_lse_workspace_bytes(desc, n), q.device)
+    st = lib.ga_prefill_lse(ctypes.byref(desc), n, _tensor(q, "q", qshape, et), _tensor(k, "k", kshape, et),
+                            _tensor(v, "v", kshape, et),
+                            _tensor(gate, "gate", gshape, et) if gshape is not None else None,
+                            _norm_w(q_norm_w, "q_norm_w", desc), _norm_w(k_norm_w, "k_norm_w", desc),
+                            _tensor(positions, "positions", (B, n), torch.int32, required=False), wp, wb,
+                            _tensor(out, "out", (B, n, H * hd), et), _tensor(lse, "lse", (B, n, H), torch.float32),
+                            _stream(stream))
+    _check(st, "ga_prefill_lse")
+    return out, lse
+
+
+def ga_prefill_backward(desc: AttnDesc, q, k, v, dout, gate=None, q_norm_w=None, k_norm_w=None, positions=None,
+                        workspace=None, stream=None, weight_grads=True, grads: Optional[dict] = None,
+                        out=None, lse=None) -> dict:
+    """Gradients of sum(dout * ga_prefill(...)): dict with dq, dk, dv, dgate
+    (None without a gate) and dq_norm_w, dk_norm_w (None without that norm
+    weight, or with weight_grads=False). ``grads`` may hold preallocated
+    output tensors under the same keys. With ``out`` and ``lse`` from
+    ga_prefill_lse on the same inputs, ga_prefill_backward_lse runs instead
+    (no recomputation of the forward attention)."""
+    lib = _lib.load()
+    et = _elem_dtype(desc)
+    B, n = desc.batch, _seq(q)[1]
+    H, G, hd = desc.n_q_heads, desc.n_kv_heads, desc.head_dim
+    qshape, kshape = (B, n, H, hd), (B, n, G, hd)
+    gshape = _gate_shape(desc, qshape)
+    if (out is None) != (lse is None):
+        raise ValueError("out and lse go together")
     grads = grads or {}
     dq = grads.get("dq", None)
     dq = torch.empty(qshape, dtype=et, device=q.device) if dq is None else dq
@@ -483,17 +521,20 @@ def ga_prefill_backward(desc: AttnDesc, q, k, v, dout, gate=None, q_norm_w=None,
     if dwk is None and k_norm_w is not None and weight_grads:
         dwk = torch.empty_like(k_norm_w)
     ws, wp, wb = _workspace_arg(workspace, ga_prefill_backward_workspace_bytes(desc, n), q.device)
-    st = lib.ga_prefill_backward(ctypes.byref(desc), n, _tensor(q, "q", qshape, et), _tensor(k, "k", kshape, et),
-                                 _tensor(v, "v", kshape, et),
-                                 _tensor(gate, "gate", gshape, et) if gshape is not None else None,
-                                 _norm_w(q_norm_w, "q_norm_w", desc), _norm_w(k_norm_w, "k_norm_w", desc),
-                                 _tensor(positions, "positions", (B, n), torch.int32, required=False),
-                                 _tensor(dout, "dout", (B, n, H * hd), et), _tensor(dq, "dq", qshape, et),
-                                 _tensor(dk, "dk", kshape, et), _tensor(dv, "dv", kshape, et),
-                                 _tensor(dgate, "dgate", gshape, et) if gshape is not None else None,
-                                 _norm_w(dwq, "dq_norm_w", desc), _norm_w(dwk, "dk_norm_w", desc), wp, wb,
-                                 _stream(stream))
-    _check(st, "ga_prefill_backward")
+    front = (ctypes.byref(desc), n, _tensor(q, "q", qshape, et), _tensor(k, "k", kshape, et),
+              _tensor(v, "v", kshape, et), _tensor(gate, "gate", gshape, et) if gshape is not None else None,
+              _norm_w(q_norm_w, "q_norm_w", desc), _norm_w(k_norm_w, "k_norm_w", desc),
+              _tensor(positions, "positions", (B, n), torch.int32, required=False))
+    rest = (_tensor(dout, "dout", (B, n, H * hd), et), _tensor(dq, "dq", qshape, et), _tensor(dk, "dk", kshape, et),
+            _tensor(dv, "dv", kshape, et), _tensor(dgate, "dgate", gshape, et) if gshape is not None else None,
+            _norm_w(dwq, "dq_norm_w", desc), _norm_w(dwk, "dk_norm_w", desc), wp, wb, _stream(stream))
+    if lse is None:
+        st = lib.ga_prefill_backward(*front, *rest)
+        _check(st, "ga_prefill_backward")
+    else:
+        st = lib.ga_prefill_backward_lse(*front, _tensor(out, "out", (B, n, H * hd), et),
+                                         _tensor(lse, "lse", (B, n, H), torch.float32), *rest)
+        _check(st, "ga_prefill_backward_lse")
     return dict(dq=dq, dk=dk, dv=dv, dgate=dgate, dq_norm_w=dwq, dk_norm_w=dwk)
 
 

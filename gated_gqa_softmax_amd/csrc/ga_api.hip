@@ -583,16 +583,66 @@ size_t ga_prefill_backward_workspace_bytes(const ga_attn_desc* desc, int32_t seq
   return bwd_layout(desc, seq_len).total;
 }
 
-ga_status ga_prefill_backward(const ga_attn_desc* desc, int32_t seq_len, const void* q, const void* k, const void* v,
-                              const void* gate, const float* q_norm_w, const float* k_norm_w,
-                              const int32_t* positions, const void* dout, void* dq, void* dk, void* dv, void* dgate,
-                              float* dq_norm_w, float* dk_norm_w, void* workspace, size_t workspace_bytes,
-                              void* stream) {
+}  // extern "C"
+
+namespace {
+
+// q-hat and k-hat (bf16, as the MFMA operands of the backward) into qh [B,n,H,d] and kh [B,n,G,d].
+ga_status prep_qk_hat(const ga_attn_desc* desc, int32_t n, const void* q, const void* k, const float* q_norm_w,
+                      const float* k_norm_w, const int32_t* positions, uint16_t* qh, uint16_t* kh, hipStream_t s) {
   ga_status st;
-  if ((st = check_desc(desc)) != GA_OK) return st;
-  if (seq_len < 0) return fail(GA_ERR_BAD_SHAPE, "seq_len %d < 0", seq_len);
-  if ((st = check_bwd_desc(desc)) != GA_OK) return st;
-  if (desc->batch == 0 || seq_len == 0) return ok();
+  if ((st = prefill_keys_impl(desc, n, k, nullptr, k_norm_w, positions, kh, nullptr, n, s)) != GA_OK) return st;
+  ga_attn_desc dq_desc = *desc;
+  dq_desc.n_kv_heads = desc->n_q_heads;  // the key-preparation kernel over the H query rows of each token
+  return prefill_keys_impl(&dq_desc, n, q, nullptr, q_norm_w, positions, qh, nullptr, n, s);
+}
+
+// Attention of q-hat against k-hat (no norm and no RoPE left to apply) with
+// a running-max softmax, writing the output (gated by ``gate`` under
+// gate_mode; y itself for GA_GATE_NONE) and the log2-domain log-sum-exp of
+// every row, from the same operands and in the same arithmetic the backward
+// kernels recompute the probabilities with.
+ga_status attention_stats(const ga_attn_desc* desc, int32_t n, const uint16_t* qh, const uint16_t* kh, const void* v,
+                          const void* gate, int gate_mode, void* out, float* lse, hipStream_t s) {
+  ga_status st;
+  const int B = desc->batch, H = desc->n_q_heads, G = desc->n_kv_heads, D = desc->head_dim;
+  PrefillParams pp;
+  memset(&pp, 0, sizeof(pp));
+  pp.q = qh;
+  pp.khat = kh;
+  pp.v = (const uint16_t*)v;
+  pp.gate = (const uint16_t*)gate;
+  pp.out = (uint16_t*)out;
+  pp.lse = lse;
+  pp.k_bstride = (long)n * G * D;
+  pp.v_bstride = pp.k_bstride;
+  pp.qs = D;
+  pp.gs = gate_mode == GA_GATE_HEADWISE ? 1 : D;
+  pp.B = B;
+  pp.n = n;
+  pp.H = H;
+  pp.G = G;
+  pp.grp = H / G;
+  // the mirrored kernel where it serves the shape, else the simple one
+  ga_attn_desc sd = *desc;
+  sd.rot_dim = 0;
+  sd.gate_mode = gate_mode;
+  const bool mirror = prefill_v2_ok(&sd, n, n) && (long long)B * n * H < (1LL << 31);
+  pp.TB = (mirror ? 64 : 128) / pp.grp;
+  pp.nblk = (n + pp.TB - 1) / pp.TB;
+  pp.use_table = 1;
+  pp.scale_log2 = scale_of(desc) * 1.4426950408889634f;
+  if ((long long)pp.B * G * pp.nblk > 0x7fffffffLL) return fail(GA_ERR_UNSUPPORTED, "grid too large");
+  const hipError_t e = mirror ? launch_prefill_v2(pp, D, gate_mode, s) : launch_prefill_mfma(pp, D, gate_mode, s);
+  if ((st = hip_status(e, "attention-with-statistics launch")) != GA_OK) return st;
+  return GA_OK;
+}
+
+// Arguments shared by ga_prefill_backward and ga_prefill_backward_lse.
+ga_status check_bwd_args(const ga_attn_desc* desc, int32_t seq_len, const void* q, const void* k, const void* v,
+                         const void* gate, const float* q_norm_w, const float* k_norm_w, const void* dout,
+                         void* dq, void* dk, void* dv, void* dgate) {
+  ga_status st;
   const char* names[] = {"q", "k", "v", "dout", "dq", "dk", "dv"};
   const void* ptrs[] = {q, k, v, dout, dq, dk, dv};
   for (int i = 0; i < 7; ++i)
@@ -601,12 +651,29 @@ ga_status ga_prefill_backward(const ga_attn_desc* desc, int32_t seq_len, const v
   if (desc->gate_mode != GA_GATE_NONE && (st = check_gate(dgate, desc)) != GA_OK) return st;
   if ((st = check_norm_w(q_norm_w, "q_norm_w")) != GA_OK) return st;
   if ((st = check_norm_w(k_norm_w, "k_norm_w")) != GA_OK) return st;
+  const long long rows = (long long)desc->batch * seq_len * desc->n_q_heads;
+  if (rows >= (1LL << 31)) return fail(GA_ERR_UNSUPPORTED, "backward: B*n*H must stay below 2^31");
+  return GA_OK;
+}
+
+ga_status check_lse(const float* lse) {
+  if (!lse) return fail(GA_ERR_NULL_ARG, "lse is NULL");
+  if (!aligned(lse, 4)) return fail(GA_ERR_MISALIGNED, "lse is not 4-byte aligned");
+  return GA_OK;
+}
+
+// The backward after the argument checks. fwd_out / fwd_lse: the output and
+// row statistics of ga_prefill_lse (both NULL: recompute them here).
+ga_status backward_impl(const ga_attn_desc* desc, int32_t seq_len, const void* q, const void* k, const void* v,
+                        const void* gate, const float* q_norm_w, const float* k_norm_w, const int32_t* positions,
+                        const void* fwd_out, const float* fwd_lse, const void* dout, void* dq, void* dk, void* dv,
+                        void* dgate, float* dq_norm_w, float* dk_norm_w, void* workspace, size_t workspace_bytes,
+                        void* stream) {
+  ga_status st;
   const BwdLayout L = bwd_layout(desc, seq_len);
   if (!workspace || workspace_bytes < L.total)
     return fail(GA_ERR_WORKSPACE, "workspace %zu bytes < %zu required", workspace ? workspace_bytes : 0, L.total);
   if (!aligned(workspace, 256)) return fail(GA_ERR_MISALIGNED, "workspace is not 256-byte aligned");
-  const long long rows = (long long)desc->batch * seq_len * desc->n_q_heads;
-  if (rows >= (1LL << 31)) return fail(GA_ERR_UNSUPPORTED, "backward: B*n*H must stay below 2^31");
   hipStream_t s = (hipStream_t)stream;
   char* ws = (char*)workspace;
   const int B = desc->batch, n = seq_len, H = desc->n_q_heads, G = desc->n_kv_heads, D = desc->head_dim;
@@ -627,46 +694,9 @@ ga_status ga_prefill_backward(const ga_attn_desc* desc, int32_t seq_len, const v
   float* dkp = (float*)(ws + L.dkp);
   float* dvp = (float*)(ws + L.dvp);
 
-  // q-hat and k-hat (bf16, as the forward's MFMA operands)
-  if ((st = prefill_keys_impl(desc, n, k, nullptr, k_norm_w, positions, kh, nullptr, n, s)) != GA_OK) return st;
-  {
-    ga_attn_desc dq_desc = *desc;
-    dq_desc.n_kv_heads = H;  // the key-preparation kernel over the H query rows of each token
-    if ((st = prefill_keys_impl(&dq_desc, n, q, nullptr, q_norm_w, positions, qh, nullptr, n, s)) != GA_OK)
-      return st;
-  }
-  // the forward's ungated output y and the log-sum-exp of each row, from
-  // q-hat and k-hat (no norm and no RoPE left to apply)
-  {
-    PrefillParams pp;
-    memset(&pp, 0, sizeof(pp));
-    pp.q = qh;
-    pp.khat = kh;
-    pp.v = (const uint16_t*)v;
-    pp.out = y;
-    pp.lse = lse;
-    pp.k_bstride = (long)n * G * D;
-    pp.v_bstride = pp.k_bstride;
-    pp.qs = D;
-    pp.gs = D;
-    pp.B = B;
-    pp.n = n;
-    pp.H = H;
-    pp.G = G;
-    pp.grp = H / G;
-    // the mirrored kernel where it serves the shape (no RoPE left to apply), else the simple one
-    ga_attn_desc sd = *desc;
-    sd.rot_dim = 0;
-    sd.gate_mode = GA_GATE_NONE;
-    const bool mirror = prefill_v2_ok(&sd, n, n) && (long long)B * n * H < (1LL << 31);
-    pp.TB = (mirror ? 64 : 128) / pp.grp;
-    pp.nblk = (n + pp.TB - 1) / pp.TB;
-    pp.use_table = 1;
-    pp.scale_log2 = scale_of(desc) * 1.4426950408889634f;
-    if ((long long)pp.B * G * pp.nblk > 0x7fffffffLL) return fail(GA_ERR_UNSUPPORTED, "grid too large");
-    const hipError_t e = mirror ? launch_prefill_v2(pp, D, GA_GATE_NONE, s) : launch_prefill_mfma(pp, D, GA_GATE_NONE, s);
-    if ((st = hip_status(e, "backward forward-stats launch")) != GA_OK) return st;
-  }
+  if ((st = prep_qk_hat(desc, n, q, k, q_norm_w, k_norm_w, positions, qh, kh, s)) != GA_OK) return st;
+  // the forward's ungated output y and the log-sum-exp of each row, unless the caller kept them
+  if (!fwd_lse && (st = attention_stats(desc, n, qh, kh, v, nullptr, GA_GATE_NONE, y, lse, s)) != GA_OK) return st;
   BwdParams bp;
   memset(&bp, 0, sizeof(bp));
   bp.q_rb = q_rb;
@@ -676,10 +706,11 @@ ga_status ga_prefill_backward(const ga_attn_desc* desc, int32_t seq_len, const v
   bp.v_rb = v_rb;
   bp.dy_rb = dy_rb;
   bp.dy_cb = dy_cb;
-  bp.y = y;
+  bp.y = fwd_lse ? (const uint16_t*)fwd_out : y;
+  bp.y_is_out = fwd_lse != nullptr;
   bp.dout = (const uint16_t*)dout;
   bp.gate = (const uint16_t*)gate;
-  bp.lse = lse;
+  bp.lse = fwd_lse ? fwd_lse : lse;
   bp.dsum = dsum;
   bp.dy_out = dyb;
   bp.dsum_out = dsum;
@@ -733,6 +764,79 @@ ga_status ga_prefill_backward(const ga_attn_desc* desc, int32_t seq_len, const v
   return hip_status(launch_bwd_dv_sum(dvp, (uint16_t*)dv, B, n, H, G, D, s), "backward dv launch");
 }
 
+}  // namespace
+
+extern "C" {
+
+ga_status ga_prefill_backward(const ga_attn_desc* desc, int32_t seq_len, const void* q, const void* k, const void* v,
+                              const void* gate, const float* q_norm_w, const float* k_norm_w,
+                              const int32_t* positions, const void* dout, void* dq, void* dk, void* dv, void* dgate,
+                              float* dq_norm_w, float* dk_norm_w, void* workspace, size_t workspace_bytes,
+                              void* stream) {
+  ga_status st;
+  if ((st = check_desc(desc)) != GA_OK) return st;
+  if (seq_len < 0) return fail(GA_ERR_BAD_SHAPE, "seq_len %d < 0", seq_len);
+  if ((st = check_bwd_desc(desc)) != GA_OK) return st;
+  if (desc->batch == 0 || seq_len == 0) return ok();
+  if ((st = check_bwd_args(desc, seq_len, q, k, v, gate, q_norm_w, k_norm_w, dout, dq, dk, dv, dgate)) != GA_OK)
+    return st;
+  return backward_impl(desc, seq_len, q, k, v, gate, q_norm_w, k_norm_w, positions, nullptr, nullptr, dout, dq, dk,
+                       dv, dgate, dq_norm_w, dk_norm_w, workspace, workspace_bytes, stream);
+}
+
+ga_status ga_prefill_backward_lse(const ga_attn_desc* desc, int32_t seq_len, const void* q, const void* k,
+                                  const void* v, const void* gate, const float* q_norm_w, const float* k_norm_w,
+                                  const int32_t* positions, const void* out, const float* lse, const void* dout,
+                                  void* dq, void* dk, void* dv, void* dgate, float* dq_norm_w, float* dk_norm_w,
+                                  void* workspace, size_t workspace_bytes, void* stream) {
+  ga_status st;
+  if ((st = check_desc(desc)) != GA_OK) return st;
+  if (seq_len < 0) return fail(GA_ERR_BAD_SHAPE, "seq_len %d < 0", seq_len);
+  if ((st = check_bwd_desc(desc)) != GA_OK) return st;
+  if (desc->batch == 0 || seq_len == 0) return ok();
+  if ((st = check_bwd_args(desc, seq_len, q, k, v, gate, q_norm_w, k_norm_w, dout, dq, dk, dv, dgate)) != GA_OK)
+    return st;
+  if ((st = check_tensor(out, "out", desc)) != GA_OK || (st = check_lse(lse)) != GA_OK) return st;
+  return backward_impl(desc, seq_len, q, k, v, gate, q_norm_w, k_norm_w, positions, out, lse, dout, dq, dk, dv,
+                       dgate, dq_norm_w, dk_norm_w, workspace, workspace_bytes, stream);
+}
+
+size_t ga_prefill_lse_workspace_bytes(const ga_attn_desc* desc, int32_t seq_len) {
+  if (check_desc(desc) != GA_OK || seq_len < 0) return 0;
+  const size_t B = (size_t)desc->batch, H = (size_t)desc->n_q_heads, G = (size_t)desc->n_kv_heads;
+  const size_t D = (size_t)desc->head_dim, n = (size_t)seq_len;
+  return round_up(B * n * H * D * 2, 256) + round_up(B * n * G * D * 2, 256);
+}
+
+ga_status ga_prefill_lse(const ga_attn_desc* desc, int32_t seq_len, const void* q, const void* k, const void* v,
+                         const void* gate, const float* q_norm_w, const float* k_norm_w, const int32_t* positions,
+                         void* workspace, size_t workspace_bytes, void* out, float* lse, void* stream) {
+  ga_status st;
+  if ((st = check_desc(desc)) != GA_OK) return st;
+  if (seq_len < 0) return fail(GA_ERR_BAD_SHAPE, "seq_len %d < 0", seq_len);
+  if ((st = check_bwd_desc(desc)) != GA_OK) return st;
+  if (desc->batch == 0 || seq_len == 0) return ok();
+  const char* names[] = {"q", "k", "v", "out"};
+  const void* ptrs[] = {q, k, v, out};
+  for (int i = 0; i < 4; ++i)
+    if ((st = check_tensor(ptrs[i], names[i], desc)) != GA_OK) return st;
+  if ((st = check_gate(gate, desc)) != GA_OK) return st;
+  if ((st = check_norm_w(q_norm_w, "q_norm_w")) != GA_OK) return st;
+  if ((st = check_norm_w(k_norm_w, "k_norm_w")) != GA_OK) return st;
+  if ((st = check_lse(lse)) != GA_OK) return st;
+  if ((long long)desc->batch * seq_len * desc->n_q_heads >= (1LL << 31))
+    return fail(GA_ERR_UNSUPPORTED, "B*n*H must stay below 2^31");
+  const size_t need = ga_prefill_lse_workspace_bytes(desc, seq_len);
+  if (!workspace || workspace_bytes < need)
+    return fail(GA_ERR_WORKSPACE, "workspace %zu bytes < %zu required", workspace ? workspace_bytes : 0, need);
+  if (!aligned(workspace, 256)) return fail(GA_ERR_MISALIGNED, "workspace is not 256-byte aligned");
+  hipStream_t s = (hipStream_t)stream;
+  uint16_t* qh = (uint16_t*)workspace;
+  uint16_t* kh = (uint16_t*)((char*)workspace + round_up((size_t)desc->batch * seq_len * desc->n_q_heads *
+                                                             desc->head_dim * 2, 256));
+  if ((st = prep_qk_hat(desc, seq_len, q, k, q_norm_w, k_norm_w, positions, qh, kh, s)) != GA_OK) return st;
+  return attention_stats(desc, seq_len, qh, kh, v, gate, desc->gate_mode, out, lse, s);
+}
 
 const char* ga_prefill_attention_kernel(const ga_attn_desc* desc, int32_t seq_len) {
   if (check_desc(desc) != GA_OK || seq_len < 0) return "invalid";
@@ -1062,6 +1166,6 @@ int32_t ga_fast_path(int32_t dtype, int32_t head_dim, int32_t rot_dim, int32_t g
   return (prefill_fast(&d) ? 1 : 0) | (decode_fast(&d, 0) ? 2 : 0);
 }
 
-int32_t ga_version(void) { return 5; }
+int32_t ga_version(void) { return 6; }
 
 }  // extern "C"

@@ -57,7 +57,10 @@ __device__ __forceinline__ bf16x8_t pack_operand(const f32x16_t& x, int half) {
 }  // namespace
 
 // ---- gate backward, dy and rowsum(dy * y): one wave per (b, i, h) row -------------
-template <int D, int GATE>
+// FROM_OUT: p.y holds the forward's gated output o = y * g instead of y, so
+// with g = sigmoid(z): dz = dout * o * (1 - g) and rowsum(dy * y) =
+// rowsum(dout * o), with no division by g (which may round to 0).
+template <int D, int GATE, bool FROM_OUT = false>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(const BwdParams p) {
   constexpr int EPL = D / 64;  // elements per lane
   const int lane = threadIdx.x & 63;
@@ -77,18 +80,21 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const BwdParams p) {
 #pragma unroll
     for (int m = 0; m < EPL; ++m) dyy += go[m] * y[m];
     dyy = sum_xor<64>(dyy);
-    if (lane == 0) p.dgate[row] = f32_to_bf16_bits(dyy * gh * (1.f - gh));
+    if (lane == 0) p.dgate[row] = f32_to_bf16_bits(FROM_OUT ? dyy * (1.f - gh) : dyy * gh * (1.f - gh));
   }
   float ds = 0.f;
 #pragma unroll
   for (int m = 0; m < EPL; ++m) {
     const float g = GATE == 2 ? sigmoid_f32(z[m]) : gh;
-    if (GATE == 2) p.dgate[base + m] = f32_to_bf16_bits(go[m] * y[m] * g * (1.f - g));
+    if (GATE == 2) p.dgate[base + m] = f32_to_bf16_bits(FROM_OUT ? go[m] * y[m] * (1.f - g) : go[m] * y[m] * g * (1.f - g));
     const uint16_t dyb = f32_to_bf16_bits(GATE == 0 ? go[m] : go[m] * g);
     p.dy_out[base + m] = dyb;
-    ds += bf16_bits_to_f32(dyb) * y[m];  // the rounded dy the products use
+    if (!FROM_OUT || GATE == 0)
+      ds += bf16_bits_to_f32(dyb) * y[m];  // the rounded dy the products use
+    else if (GATE == 2)
+      ds += go[m] * y[m];
   }
-  ds = sum_xor<64>(ds);
+  ds = (FROM_OUT && GATE == 1) ? dyy : sum_xor<64>(ds);  // dyy is summed over the row already
   if (lane == 0) p.dsum_out[row] = ds;
 }
 
@@ -862,10 +868,12 @@ static hipError_t launch_pre_d(const BwdParams& p, hipStream_t s) {
   const long rows = (long)p.B * p.n * p.H;
   const unsigned grid = (unsigned)((rows + 3) / 4);
   if (rows == 0) return hipSuccess;
-  switch (p.gate_mode) {
+  switch (p.gate_mode + 3 * (p.y_is_out && p.gate_mode != 0)) {
     case 0: hipLaunchKernelGGL((bwd_pre_kernel<D, 0>), dim3(grid), dim3(256), 0, s, p); break;
     case 1: hipLaunchKernelGGL((bwd_pre_kernel<D, 1>), dim3(grid), dim3(256), 0, s, p); break;
-    default: hipLaunchKernelGGL((bwd_pre_kernel<D, 2>), dim3(grid), dim3(256), 0, s, p); break;
+    case 2: hipLaunchKernelGGL((bwd_pre_kernel<D, 2>), dim3(grid), dim3(256), 0, s, p); break;
+    case 4: hipLaunchKernelGGL((bwd_pre_kernel<D, 1, true>), dim3(grid), dim3(256), 0, s, p); break;
+    default: hipLaunchKernelGGL((bwd_pre_kernel<D, 2, true>), dim3(grid), dim3(256), 0, s, p); break;
   }
   return hipGetLastError();
 }

@@ -68,7 +68,8 @@ struct PrefillParams {
   int B, n, H, G, grp, TB, nblk, rot, half, use_table;
   float eps, scale_log2;
   // log2-domain log-sum-exp of each output row (b, token, head), for the
-  // backward pass (simple kernel; mirrored kernel without a gate); null otherwise
+  // backward pass (simple and mirrored kernels, running-max softmax, the
+  // method's gate only); null otherwise
   float* lse;
   double inv_freq[kMaxHalfRot];
 };
@@ -123,7 +124,7 @@ struct DecodeParams {
 constexpr int kDecodeChunk = 768;  // keys per decode split
 
 // Backward of the prefill (bf16). Row-major workspace copies: y [B,n,H,d]
-// (ungated attention output), dy [B,n,H,d] (gradient of y); lse, dsum
+// (ungated attention output; or, with y_is_out, the caller's gated output), dy [B,n,H,d] (gradient of y); lse, dsum
 // [B,n,H] fp32 (log2-domain log-sum-exp of each score row; rowsum(dy * y)).
 // MFMA-operand copies (bf16, zero past n, npad tokens): row-blocked
 // ("rb": 32 tokens x 16 dims per 1 KiB piece, lane l holding token l%32,
@@ -153,6 +154,7 @@ struct BwdParams {
   float* dvp;
   int B, n, npad, H, G, grp, gate_mode;
   int plain;            // 1: the register-operand dq and dK/dV kernels for every shape
+  int y_is_out;         // pre kernel: y holds the forward's gated output (see bwd_pre_kernel)
   float scale, scale_log2;
 };
 

@@ -747,8 +747,13 @@ static hipError_t launch_v2_d(const PrefillParams& p, int gate_mode, hipStream_t
   if (grid <= 0) return hipSuccess;
   if (p.key_base)
     launch_v2_gate<D, true>(p, gate_mode, grid, s);
-  else if (p.lse)  // ungated output with the row statistics, for the backward pass
-    hipLaunchKernelGGL((prefill_v2_kernel<D, 0, false, true>), dim3((unsigned)grid), dim3(512), 0, s, p);
+  else if (p.lse)  // with the row statistics for the backward pass (running-max softmax, method's gate only)
+    switch (gate_mode) {
+      case 0: hipLaunchKernelGGL((prefill_v2_kernel<D, 0, false, true>), dim3((unsigned)grid), dim3(512), 0, s, p); break;
+      case 1: hipLaunchKernelGGL((prefill_v2_kernel<D, 1, false, true>), dim3((unsigned)grid), dim3(512), 0, s, p); break;
+      case 2: hipLaunchKernelGGL((prefill_v2_kernel<D, 2, false, true>), dim3((unsigned)grid), dim3(512), 0, s, p); break;
+      default: return hipErrorInvalidValue;
+    }
   else
     launch_v2_gate<D>(p, gate_mode, grid, s);
   return hipGetLastError();

@@ -385,6 +385,50 @@ ga_status ga_prefill_backward(const ga_attn_desc* desc, int32_t seq_len,
                               float* dq_norm_w, float* dk_norm_w,
                               void* workspace, size_t workspace_bytes, void* stream);
 
+/* ---- training pair with saved row statistics ------------------------------ */
+
+/* Workspace ga_prefill_lse needs (256-byte aligned): bf16 q-hat [B,n,H,d]
+ * and k-hat [B,n,G,d], each rounded up to 256 bytes. Depends on its
+ * arguments only. */
+size_t ga_prefill_lse_workspace_bytes(const ga_attn_desc* desc, int32_t seq_len);
+
+/* Forward for training: out as ga_prefill computes it (no KV cache), plus
+ * the statistic of each softmax row that the backward would otherwise
+ * recompute: lse[b,i,h] = log2 of sum over keys j <= i of
+ * exp2(s_ij * scale * log2 e), s_ij = q_hat_i . k_hat_j (the normalising
+ * sum of the causal softmax in "Transformer by Hand · 6. Gated attention",
+ * "The formula", kept in log2 form). The probabilities are then
+ * P_ij = exp2(s_ij * scale * log2 e - lse_i).
+ * q-hat and k-hat are rounded to bf16 in the workspace before the
+ * attention, exactly as ga_prefill_backward rounds them, and the softmax
+ * takes a running row max (not the bounded form of ga_prefill_attention),
+ * so lse matches what the backward kernels recompute the probabilities
+ * from. out can differ from ga_prefill's by bf16 roundings.
+ *  q, k, v, gate, q_norm_w, k_norm_w, positions: as for ga_prefill.
+ *  workspace     ga_prefill_lse_workspace_bytes bytes, 256-byte aligned.
+ *  out           [B,n,H*d] bf16.
+ *  lse           [B,n,H] float32, 4-byte aligned, written.
+ * Serves the shapes ga_prefill_backward serves (GA_ERR_UNSUPPORTED otherwise). */
+ga_status ga_prefill_lse(const ga_attn_desc* desc, int32_t seq_len,
+                         const void* q, const void* k, const void* v, const void* gate,
+                         const float* q_norm_w, const float* k_norm_w, const int32_t* positions,
+                         void* workspace, size_t workspace_bytes, void* out, float* lse, void* stream);
+
+/* ga_prefill_backward given the out and lse that ga_prefill_lse wrote for
+ * the same inputs: it skips the recomputation of the forward attention.
+ * The gate's gradient and the row sums rowsum(dy * y) come from out:
+ * dz = dout * out * (1 - g) and rowsum(dout * out), which equal the
+ * definitions (dout * y * g(1 - g); dy = dout * g) for out = y * g.
+ * Other arguments, the workspace (ga_prefill_backward_workspace_bytes bytes)
+ * and the outputs as for ga_prefill_backward. out and lse are read only. */
+ga_status ga_prefill_backward_lse(const ga_attn_desc* desc, int32_t seq_len,
+                                  const void* q, const void* k, const void* v, const void* gate,
+                                  const float* q_norm_w, const float* k_norm_w, const int32_t* positions,
+                                  const void* out, const float* lse,
+                                  const void* dout, void* dq, void* dk, void* dv, void* dgate,
+                                  float* dq_norm_w, float* dk_norm_w,
+                                  void* workspace, size_t workspace_bytes, void* stream);
+
 /* ---- misc --------------------------------------------------------------- */
 
 const char* ga_status_string(ga_status status);
@@ -397,8 +441,9 @@ const char* ga_last_error(void);
  * fp32 or bf16); ga_decode_partials/ga_decode_merge need bit 1. The bits
  * are for dense q and gate (see ga_attn_desc for wider head strides). */
 int32_t ga_fast_path(int32_t dtype, int32_t head_dim, int32_t rot_dim, int32_t group);
-/* ABI version: 5 (ga_attn_desc with head strides, gate variants, the output
- * norm and the kernel-choice fields; k_norm_w in ga_prefill_chunk_attention). */
+/* ABI version: 6 (ga_attn_desc with head strides, gate variants, the output
+ * norm and the kernel-choice fields; k_norm_w in ga_prefill_chunk_attention;
+ * the ga_prefill_lse / ga_prefill_backward_lse pair). */
 int32_t ga_version(void);
 
 #ifdef __cplusplus

@@ -36,7 +36,7 @@ def test_library_exports_every_declared_entry_point():
     assert declared == set(_lib.SIGNATURES), declared ^ set(_lib.SIGNATURES)
     for name in declared:
         assert getattr(lib, name) is not None
-    assert lib.ga_version() == 5
+    assert lib.ga_version() == 6
     assert ctypes.sizeof(AttnDesc) == 80
 
 
@@ -311,6 +311,44 @@ def test_backward_rejects_bad_arguments():
     # empty inputs are a no-op, even without buffers
     assert call(n=0, q=None, ws=None, ws_bytes=0) == _lib.GA_OK
     assert call(desc=_desc(batch=0), q=None, ws=None, ws_bytes=0) == _lib.GA_OK
+
+
+def test_training_pair_rejects_bad_arguments():
+    """ga_prefill_lse and ga_prefill_backward_lse: the backward's shape rules,
+    the statistics buffer, the output the backward reads, the workspace."""
+    lib = _lib_or_build()
+    d = _desc(batch=1)
+    need = lib.ga_prefill_lse_workspace_bytes(ctypes.byref(d), 64)
+    # bf16 q-hat [1,64,H,d] and k-hat [1,64,G,d], each rounded to 256 bytes
+    assert need == 64 * d.n_q_heads * d.head_dim * 2 + 64 * d.n_kv_heads * d.head_dim * 2
+    bneed = lib.ga_prefill_backward_workspace_bytes(ctypes.byref(d), 64)
+
+    def fwd(desc=d, n=64, q=A16, gate=A16, ws=A16, ws_bytes=1 << 40, out=A16, lse=A16):
+        return lib.ga_prefill_lse(ctypes.byref(desc), n, q, A16, A16, gate, None, None, None, ws, ws_bytes, out, lse,
+                                  None)
+
+    def bwd(desc=d, n=64, out=A16, lse=A16, ws_bytes=1 << 40, dq=A16):
+        return lib.ga_prefill_backward_lse(ctypes.byref(desc), n, A16, A16, A16, A16, None, None, None, out, lse,
+                                           A16, dq, A16, A16, A16, None, None, A16, ws_bytes, None)
+
+    assert fwd(n=-1) == _lib.GA_ERR_BAD_SHAPE
+    assert fwd(q=None) == _lib.GA_ERR_NULL_ARG
+    assert fwd(gate=None) == _lib.GA_ERR_NULL_ARG
+    assert fwd(out=None) == _lib.GA_ERR_NULL_ARG
+    assert fwd(lse=None) == _lib.GA_ERR_NULL_ARG
+    assert fwd(lse=A16 + 2) == _lib.GA_ERR_MISALIGNED
+    assert fwd(ws_bytes=need - 256) == _lib.GA_ERR_WORKSPACE
+    assert fwd(ws=A16 + 16) == _lib.GA_ERR_MISALIGNED
+    assert fwd(desc=_desc(dtype=_lib.GA_F32)) == _lib.GA_ERR_UNSUPPORTED
+    assert fwd(desc=_desc(gate_act=_lib.GA_ACT_SILU)) == _lib.GA_ERR_UNSUPPORTED
+    assert fwd(n=0, q=None, ws=None, ws_bytes=0, out=None, lse=None) == _lib.GA_OK
+    assert bwd(out=None) == _lib.GA_ERR_NULL_ARG
+    assert bwd(lse=None) == _lib.GA_ERR_NULL_ARG
+    assert bwd(lse=A16 + 1) == _lib.GA_ERR_MISALIGNED
+    assert bwd(dq=MIS) == _lib.GA_ERR_MISALIGNED
+    assert bwd(ws_bytes=bneed - 256) == _lib.GA_ERR_WORKSPACE
+    assert bwd(desc=_desc(head_dim=96, rot_dim=16)) == _lib.GA_ERR_UNSUPPORTED
+    assert bwd(n=0, out=None, lse=None) == _lib.GA_OK
 
 
 def test_noalloc_decode_rejects_oversized_steps_before_any_launch():
