@@ -256,17 +256,19 @@ ga_status prefill_keys_impl(const ga_attn_desc* desc, int32_t n, const void* k, 
 }
 
 // k_norm_w: the weights k_hat was normed with, or null when unknown (then no
-// score bound is used).
+// score bound is used). lse: also write each row's log2 log-sum-exp (the
+// mirrored and simple kernels only; running-max softmax), or null.
 ga_status prefill_attn_impl(const ga_attn_desc* desc, int32_t n, const void* q, const void* k_hat,
                             int32_t k_cap, const void* v, int32_t v_cap, const void* gate,
                             const float* q_norm_w, const float* k_norm_w, const int32_t* positions, void* out,
-                            hipStream_t stream) {
+                            hipStream_t stream, float* lse = nullptr) {
   const int H = desc->n_q_heads, G = desc->n_kv_heads, d = desc->head_dim;
   const int grp = H / G;
   const PrefillKernel choice = prefill_choice(desc, n, k_cap, v_cap);
   const bool wide = choice == PK_WIDE;
   const bool v2 = choice == PK_MIRROR;
   const bool v1 = choice == PK_SIMPLE;
+  if (lse && !(v2 || v1)) return fail(GA_ERR_UNSUPPORTED, "row statistics need the mirrored or simple kernel");
   if (wide || v2 || v1) {
     PrefillParams pp;
     memset(&pp, 0, sizeof(pp));
@@ -278,6 +280,7 @@ ga_status prefill_attn_impl(const ga_attn_desc* desc, int32_t n, const void* q, 
     pp.wk = k_norm_w;
     pp.positions = positions;
     pp.out = (uint16_t*)out;
+    pp.lse = lse;
     pp.k_bstride = (long)k_cap * G * d;
     pp.v_bstride = (long)v_cap * G * d;
     pp.qs = q_stride(desc);
@@ -834,6 +837,19 @@ ga_status ga_prefill_lse(const ga_attn_desc* desc, int32_t seq_len, const void* 
   uint16_t* qh = (uint16_t*)workspace;
   uint16_t* kh = (uint16_t*)((char*)workspace + round_up((size_t)desc->batch * seq_len * desc->n_q_heads *
                                                              desc->head_dim * 2, 256));
+  // The fused kernels norm and rotate q themselves (rounding q-hat to bf16 as
+  // the backward's key preparation does, up to the last bit of an fp32
+  // result on either side) where one serves the shape with RoPE; otherwise
+  // q-hat is prepared here too and the attention runs without norm or RoPE.
+  ga_attn_desc fd = *desc;
+  fd.kernel = GA_KERNEL_MIRROR;
+  if (prefill_choice(&fd, seq_len, seq_len, seq_len) != PK_MIRROR) fd.kernel = GA_KERNEL_SIMPLE;
+  if (prefill_choice(&fd, seq_len, seq_len, seq_len) != PK_INVALID) {
+    if ((st = prefill_keys_impl(desc, seq_len, k, nullptr, k_norm_w, positions, kh, nullptr, seq_len, s)) != GA_OK)
+      return st;
+    return prefill_attn_impl(&fd, seq_len, q, kh, seq_len, v, seq_len, gate, q_norm_w, k_norm_w, positions, out, s,
+                             lse);
+  }
   if ((st = prep_qk_hat(desc, seq_len, q, k, q_norm_w, k_norm_w, positions, qh, kh, s)) != GA_OK) return st;
   return attention_stats(desc, seq_len, qh, kh, v, gate, desc->gate_mode, out, lse, s);
 }

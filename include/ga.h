@@ -399,11 +399,14 @@ size_t ga_prefill_lse_workspace_bytes(const ga_attn_desc* desc, int32_t seq_len)
  * sum of the causal softmax in "Transformer by Hand · 6. Gated attention",
  * "The formula", kept in log2 form). The probabilities are then
  * P_ij = exp2(s_ij * scale * log2 e - lse_i).
- * q-hat and k-hat are rounded to bf16 in the workspace before the
- * attention, exactly as ga_prefill_backward rounds them, and the softmax
- * takes a running row max (not the bounded form of ga_prefill_attention),
- * so lse matches what the backward kernels recompute the probabilities
- * from. out can differ from ga_prefill's by bf16 roundings.
+ * k-hat goes to the workspace in bf16 exactly as ga_prefill_backward
+ * prepares it; the attention kernel norms and rotates q itself and rounds
+ * q-hat to bf16 likewise (where no fused kernel serves the shape, q-hat is
+ * prepared in the workspace too). The softmax takes a running row max (not
+ * the bounded form of ga_prefill_attention), so lse matches the scores the
+ * backward kernels recompute the probabilities from, up to the last bit of
+ * an fp32 norm result rounding differently on either side. out can differ
+ * from ga_prefill's by bf16 roundings.
  *  q, k, v, gate, q_norm_w, k_norm_w, positions: as for ga_prefill.
  *  workspace     ga_prefill_lse_workspace_bytes bytes, 256-byte aligned.
  *  out           [B,n,H*d] bf16.
