@@ -44,6 +44,8 @@ CASES = [
     _case("d256_g2_head_staged", 1, 130, 4, 2, 256, 64, "headwise", seed=611),
     # group 3 at d = 256: the staged dq cannot pair its dim slices, so the register-operand dq runs
     _case("d256_g3_elem_plain_dq", 1, 90, 6, 2, 256, 64, "elementwise", seed=612),
+    # a RoPE width that is not a multiple of 16
+    _case("d128_rot24_elem", 1, 50, 4, 2, 128, 24, "elementwise", seed=615),
 ]
 
 # The register-operand kernels, forced everywhere by their switches

@@ -31,6 +31,9 @@ CASES = [
     _case("d256_g3_elem", 1, 90, 6, 2, 256, 64, "elementwise", seed=704),
     _case("d128_g8_head", 1, 200, 8, 1, 128, 32, "headwise", seed=706),
     _case("d128_g2_elem_long", 1, 300, 4, 2, 128, 32, "elementwise", seed=707),
+    # RoPE widths neither fused kernel serves (rot % 16 != 0): q-hat is prepared in the workspace
+    _case("d128_rot24_elem_prepared_q", 1, 50, 4, 2, 128, 24, "elementwise", seed=708),
+    _case("d64_rot8_head_prepared_q", 2, 37, 4, 2, 64, 8, "headwise", seed=709),
 ]
 
 
