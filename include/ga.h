@@ -376,7 +376,8 @@ size_t ga_prefill_backward_workspace_bytes(const ga_attn_desc* desc, int32_t seq
  * Serves bf16, d in {64, 128, 256}, group <= 128, the method's gate
  * (GA_ERR_UNSUPPORTED for gate variants, the output norm, head strides other
  * than dense, fp32). The forward's softmax statistics are recomputed inside
- * the call from q-hat and k-hat, so nothing from the forward call is needed.
+ * the call from q-hat and k-hat, so nothing from the forward call is needed
+ * (ga_prefill_backward_lse takes them from ga_prefill_lse instead).
  * Deterministic: no atomics, fixed summation orders. */
 ga_status ga_prefill_backward(const ga_attn_desc* desc, int32_t seq_len,
                               const void* q, const void* k, const void* v, const void* gate,
